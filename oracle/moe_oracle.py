@@ -1,0 +1,282 @@
+"""CPU oracle for the forward pass of one top-k routed Mixture-of-Experts FFN layer.
+
+TEST INFRASTRUCTURE. Only the test suite, the smoke check and the CPU-baseline leg of the
+benchmark may import this module. The product path (the HIP library and its binding) never
+imports, links or calls it, and this module imports nothing from the product path: it is plain,
+slow, obviously-correct NumPy, written from the pages listed below, in float64 on inputs that are
+widened exactly (a bfloat16 value held in a float32 array is exact, and float32 -> float64 is
+exact).
+
+Pages (cited by title and section; nothing here copies their code):
+  [tirogla]  "Mixture of experts (MoE)" -- tirogla.com/machine-learning/mixture-of-experts.html
+             ("How it works" steps 1-6; "Code": route, dispatch, aux_loss, z_loss, combine, main;
+             "Complexity and constants"; "Implementation notes").
+  [dinesh]   "DL S077 - Mixture of Experts (MoE) Intuition" -- dineshblog.com/blog/session-dl-077-moe
+             (1.1 What an "expert" is; 2 Top-k gating, step by step; 3.1 The auxiliary loss;
+             3.2 Why not just enforce balance?; 4 The parameter-count arithmetic).
+  [starphix] "Mixture of Experts (MoE)" -- learn.starphix.com ... ModelArchitectures/Mixture-of-Experts.md
+             (Key Equations; Top-k Gating; Expert Architectures: Shared + Specialized).
+  [vanos]    "Mixture of Experts (MoE)" -- vanos001.github.io/placement_prep/llm/moe
+             (Load Balancing Loss).
+
+Readings taken where the pages are silent or disagree (each one is also listed with its reason in
+the design notes of this repository):
+  * W_r is [d, E] and logits = x . W_r ([tirogla] How it works); no biases except an explicit
+    per-expert logit bias input.
+  * Ranking is always on the float32 logits, descending, equal logits to the lower expert index
+    first (the stable sort of [tirogla] Code `route`); -0.0 == +0.0; -inf ranks last; NaN rejected.
+  * Sigmoid gating: g = sigmoid(L_e) / sum over the selected sigmoid(L_s), no extra scale
+    ([tirogla] How it works, step 1).
+  * f_e = (assignments to e before capacity) / (T*k); P_e = mean over tokens of the full softmax;
+    L_aux = alpha * E * sum_e f_e * P_e ([tirogla] step 6 and Code `aux_loss`).  The full softmax
+    is used for P in every gating mode.
+  * z = beta * mean over tokens of logsumexp(row)^2 ([tirogla] step 6; Code `z_loss`).
+  * Capacity C counts assignments per expert; C <= 0 or None means unlimited; overflow is dropped
+    in assignment order a = t*k + s, earlier tokens first ([tirogla] Code `dispatch`).
+  * y excludes the residual; a dropped assignment contributes 0 ([tirogla] step 5).
+  * A shared expert is added to every token with weight 1 ([starphix] Shared + Specialized).
+  * token(a) = floor(a / k) for assignment a = t*k + s ([tirogla] Code `combine`).
+
+Pins: every function here is checked by the CPU tests against page-printed values (the worked
+top-2 example of [dinesh] section 2), closed forms, invariants stated on the pages, library
+routines on special cases and brute force on tiny inputs.  The exact float32 bits of gates and y
+on the GPU are compared only within tolerances.  Parity unpinned beyond self-consistency: the
+sigmoid-mode P_e reading and the Zipf logit-bias input recipe (conventions, no page value).
+"""
+
+import math
+
+import numpy as np
+
+# Gating modes (values follow the C header's enum so that test code can pass either).
+SOFTMAX_TOPK = 0   # softmax over the k selected logits (Mixtral)
+SOFTMAX_ALL = 1    # softmax over all E logits, keep the selected probabilities (Switch / GShard)
+SIGMOID_TOPK = 2   # sigmoid affinities renormalised over the selected experts (DeepSeek-V3)
+
+
+def _f64(a):
+    return np.asarray(a, dtype=np.float64)
+
+
+def router_logits(x, w_r, bias=None):
+    """Router scores, [tirogla] How it works step 1 (Score) and [dinesh] 1.2 What the router computes.
+
+    logits[t, e] = sum_j x[t, j] * W_r[j, e] (+ bias[e]); x [T, d], W_r [d, E].  Computed in float64
+    on the given values and rounded once to float32 (logits are always float32: [tirogla]
+    Implementation notes ask for float32 router math).
+    """
+    L = _f64(x) @ _f64(w_r)
+    if bias is not None:
+        L = L + _f64(bias)[None, :]
+    return L.astype(np.float32)
+
+
+def select_topk(logits, k):
+    """Top-k experts per token, [tirogla] How it works step 2 (Select) and Code `route`.
+
+    Each row is ordered by a stable descending sort on its float32 logits (equal logits keep the
+    lower expert index first) and the first k are kept, in that order.  Returns int32 [T, k].
+    """
+    L = np.asarray(logits, dtype=np.float32)
+    if L.ndim != 2:
+        raise ValueError("logits must be [T, E]")
+    T, E = L.shape
+    if not 1 <= k <= E:
+        raise ValueError("need 1 <= k <= E")
+    if np.isnan(L).any():
+        raise ValueError("NaN logit: ranking is undefined")
+    idx = np.empty((T, k), dtype=np.int32)
+    for t in range(T):
+        row = [float(v) for v in L[t]]        # python floats: -0.0 == 0.0, -inf sorts last
+        order = sorted(range(E), key=lambda e: (-row[e], e))
+        idx[t] = order[:k]
+    return idx
+
+
+def row_softmax_lse(logits):
+    """Full-row softmax p[t, :] and logsumexp lse[t], [tirogla] Code `route` (probs) and `z_loss`.
+
+    Shifted by the row maximum m: p = exp(L - m) / sum exp(L - m), lse = m + ln sum exp(L - m).
+    """
+    L = _f64(logits)
+    m = L.max(axis=1, keepdims=True)
+    ex = np.exp(L - m)
+    s = ex.sum(axis=1, keepdims=True)
+    return ex / s, m[:, 0] + np.log(s[:, 0])
+
+
+def gate_weights(logits, idx, mode):
+    """Mixture weights of the selected experts, [tirogla] How it works step 1 and Code `route`.
+
+    SOFTMAX_TOPK: exp(L_e - m) / sum over selected exp(L_s - m)  ([dinesh] section 2; [starphix]
+                  Top-k Gating).
+    SOFTMAX_ALL:  exp(L_e - m) / sum over all j exp(L_j - m)      (Switch / GShard).
+    SIGMOID_TOPK: sigmoid(L_e) / sum over selected sigmoid(L_s)    (DeepSeek-V3).
+    m is the full-row maximum.  float64 [T, k].
+    """
+    L = _f64(logits)
+    T, E = L.shape
+    k = idx.shape[1]
+    g = np.empty((T, k), dtype=np.float64)
+    with np.errstate(over="ignore"):
+        for t in range(T):
+            row = L[t]
+            sel = row[idx[t]]
+            m = row.max()
+            if mode == SOFTMAX_TOPK:
+                w = np.exp(sel - m)
+                g[t] = w / w.sum()
+            elif mode == SOFTMAX_ALL:
+                g[t] = np.exp(sel - m) / np.exp(row - m).sum()
+            elif mode == SIGMOID_TOPK:
+                s = 1.0 / (1.0 + np.exp(-sel))
+                g[t] = s / s.sum()
+            else:
+                raise ValueError("unknown gating mode %r" % (mode,))
+    return g
+
+
+def dispatch(idx, E, capacity=None):
+    """Counting sort of assignments by expert with capacity, [tirogla] How it works step 3 and
+    Code `dispatch`; capacity as in [dinesh] 3.2.
+
+    Assignments a = t*k + s are visited in increasing a, so earlier tokens have priority.  Each expert
+    keeps its first `capacity` assignments; later ones are dropped.  Returns
+      counts   int32 [E]    assignments per expert before capacity,
+      offsets  int32 [E+1]  exclusive prefix sum of the kept counts,
+      perm     int32 [n_kept] kept assignment ids, expert-major, increasing a within an expert,
+      inv      int32 [T*k]  position of a in perm, or -1 when a was dropped,
+      n_dropped int.
+    capacity None or <= 0 means unlimited.
+    """
+    flat = np.asarray(idx).reshape(-1)
+    A = flat.size
+    cap = A if (capacity is None or capacity <= 0) else int(capacity)
+    counts = [0] * E
+    lists = [[] for _ in range(E)]
+    n_dropped = 0
+    for a in range(A):
+        e = int(flat[a])
+        counts[e] += 1
+        if len(lists[e]) < cap:
+            lists[e].append(a)
+        else:
+            n_dropped += 1
+    offsets = [0]
+    for e in range(E):
+        offsets.append(offsets[-1] + len(lists[e]))
+    perm = np.array([a for e in range(E) for a in lists[e]], dtype=np.int32)
+    inv = np.full(A, -1, dtype=np.int32)
+    inv[perm] = np.arange(perm.size, dtype=np.int32)
+    return (np.array(counts, dtype=np.int32), np.array(offsets, dtype=np.int32), perm, inv,
+            n_dropped)
+
+
+def silu(z):
+    """silu(z) = z * sigmoid(z) = z / (1 + exp(-z))."""
+    with np.errstate(over="ignore"):
+        return z / (1.0 + np.exp(-z))
+
+
+def swiglu_ffn(X, w1, w3, w2):
+    """SwiGLU expert, [dinesh] 1.1 What an "expert" is: w2(silu(x w1) * (x w3)).
+
+    X [n, d]; w1, w3 [d, d_ff] (w1 is the gate branch, w3 the up branch); w2 [d_ff, d].  float64.
+    """
+    X = _f64(X)
+    return (silu(X @ _f64(w1)) * (X @ _f64(w3))) @ _f64(w2)
+
+
+def expert_rows(x, perm, offsets, k, w1, w3, w2):
+    """Each expert on its contiguous batch, [tirogla] How it works step 4 (Compute).
+
+    Row r of the result is expert e's output for token perm[r] // k, where
+    offsets[e] <= r < offsets[e+1].  float64 [offsets[E], d].
+    """
+    x = np.asarray(x)
+    E = len(offsets) - 1
+    out = np.zeros((int(offsets[E]), x.shape[1]), dtype=np.float64)
+    for e in range(E):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if hi > lo:
+            tok = np.asarray(perm[lo:hi]) // k
+            out[lo:hi] = swiglu_ffn(x[tok], w1[e], w3[e], w2[e])
+    return out
+
+
+def combine(out_rows, inv, gate, T, k, shared_out=None):
+    """Gate-weighted combine, [tirogla] How it works step 5 and Code `combine`.
+
+    y[t] = sum over slots s with inv[t*k+s] >= 0 of gate[t, s] * out_rows[inv[t*k+s]]; dropped
+    assignments add nothing and the residual is not included.  With a shared expert, its output is
+    added with weight 1 ([starphix] Shared + Specialized).  float64 [T, d].
+    """
+    out_rows = _f64(out_rows)
+    d = out_rows.shape[1] if out_rows.ndim == 2 and out_rows.shape[0] else (
+        shared_out.shape[1] if shared_out is not None else 0)
+    inv = np.asarray(inv).reshape(T, k)
+    g = _f64(gate).reshape(T, k)
+    y = np.zeros((T, d), dtype=np.float64)
+    for s in range(k):
+        keep = inv[:, s] >= 0
+        y[keep] += g[keep, s, None] * out_rows[inv[keep, s]]
+    if shared_out is not None:
+        y += _f64(shared_out)
+    return y
+
+
+def aux_loss(counts, prob_sum, T, E, k, alpha):
+    """Load-balancing loss, [tirogla] How it works step 6 and Code `aux_loss`:
+    alpha * E * sum_e f_e * P_e with f_e = counts_e / (T*k) and P_e = prob_sum_e / T."""
+    f = _f64(counts) / float(T * k)
+    P = _f64(prob_sum) / float(T)
+    return alpha * E * float(np.sum(f * P))
+
+
+def z_loss(lse_sq_sum, T, beta):
+    """Router z-loss, [tirogla] How it works step 6 and Code `z_loss`: beta * mean_t lse_t^2."""
+    return beta * float(lse_sq_sum) / float(T)
+
+
+def forward(x, w_r, w1, w3, w2, k, mode, capacity=None, bias=None, shared=None,
+            alpha=0.01, beta=1e-3, logits=None):
+    """The whole layer, steps in the order of [tirogla] How it works (Score, Select, Dispatch,
+    Compute, Combine, Balance).
+
+    x [T, d]; w_r [d, E]; w1, w3 [E, d, d_ff]; w2 [E, d_ff, d]; shared = (w1s, w3s, w2s) or None.
+    `logits` (float32 [T, E]) replaces the router product when given.
+    Returns a dict of every intermediate (float64 except the integer dispatch outputs).
+    """
+    x = np.asarray(x)
+    T = x.shape[0]
+    if logits is None:
+        logits = router_logits(x, w_r, bias)
+    logits = np.asarray(logits, dtype=np.float32)
+    E = logits.shape[1]
+    idx = select_topk(logits, k)
+    gate = gate_weights(logits, idx, mode)
+    p, lse = row_softmax_lse(logits)
+    counts, offsets, perm, inv, n_dropped = dispatch(idx, E, capacity)
+    rows = expert_rows(x, perm, offsets, k, w1, w3, w2)
+    shared_out = None
+    if shared is not None:
+        shared_out = swiglu_ffn(x, *shared)
+    y = combine(rows, inv, gate, T, k, shared_out)
+    prob_sum = p.sum(axis=0)
+    lse_sq_sum = float(np.sum(lse * lse))
+    return dict(logits=logits, topk_idx=idx, topk_gate=gate, probs=p, lse=lse,
+                prob_sum=prob_sum, lse_sq_sum=lse_sq_sum, counts=counts, offsets=offsets,
+                perm=perm, inv=inv, n_dropped=n_dropped, expert_out=rows, shared_out=shared_out,
+                y=y, aux=aux_loss(counts, prob_sum, T, E, k, alpha),
+                z=z_loss(lse_sq_sum, T, beta))
+
+
+def capacity_from_factor(cf, T, k, E):
+    """Capacity in assignments per expert, ceil(cf * T * k / E) ([tirogla] Code `main`)."""
+    return int(math.ceil(cf * T * k / E))
+
+
+def routed_flops(T, d, E, d_ff, n_kept, T_shared=0):
+    """Algorithmic FLOPs of the layer: router 2*T*d*E ([tirogla] Complexity and constants) plus
+    2*3*d*d_ff per expert row (three d x d_ff matrices per expert, [dinesh] section 4)."""
+    return 2 * T * d * E + 6 * d * d_ff * (n_kept + T_shared)
