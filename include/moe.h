@@ -1,0 +1,165 @@
+/*
+ * libmoe -- forward pass of one top-k routed Mixture-of-Experts FFN layer on one AMD MI355X
+ * (CDNA4, gfx950), as hand-written HIP kernels behind a plain C ABI.
+ *
+ * The method follows the page "Mixture of experts (MoE)" (tirogla.com/machine-learning/
+ * mixture-of-experts.html), section "How it works": Score (router product and gating), Select
+ * (top-k), Dispatch (counting sort by expert, at most C per expert), Compute (each expert's FFN on
+ * its contiguous batch, as one grouped GEMM), Combine (gate-weighted sum, dropped assignments add
+ * nothing) and Balance (load-balancing loss and router z-loss).  The expert is the SwiGLU MLP of
+ * "DL S077 - Mixture of Experts (MoE) Intuition" (dineshblog.com), section 1.1.
+ *
+ * Conventions shared by every entry point
+ *   - Every pointer is a DEVICE pointer (memory the caller allocated on the current HIP device),
+ *     unless stated otherwise.  The caller owns every buffer, including the workspace; the
+ *     library never allocates, frees or synchronises.  Buffers must stay valid until the work
+ *     enqueued on `stream` has finished.
+ *   - `stream` is a hipStream_t passed as void*; NULL means the default stream.  Every call only
+ *     enqueues kernels on that stream and returns.
+ *   - Outputs are fully overwritten (no accumulate-into semantics) and must not alias inputs.
+ *   - Integers are int32, row-major everywhere.  T tokens, d model width, E routed experts, k
+ *     experts per token, d_ff expert width; assignment a = t*k + s for slot s of token t.
+ *   - Errors are reported before anything is enqueued: MOE_ERR_ARG for a NULL required pointer or
+ *     a size out of range (T < 1, d < 1, d_ff < 1, E < 1, k < 1, k > E), MOE_ERR_UNSUPPORTED for
+ *     E > 1024, k > 32, or d / d_ff not a multiple of 8 (16-byte vector loads), MOE_ERR_WORKSPACE
+ *     when ws_bytes is below what moe_workspace_bytes() returns.  MOE_ERR_DEVICE means a kernel
+ *     launch failed (hipGetLastError after the launch).
+ *   - Sizes are limited so that T*k*max(d, d_ff) fits in int32 element counts.
+ */
+#ifndef LIBMOE_MOE_H
+#define LIBMOE_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_ARG = 1,
+  MOE_ERR_UNSUPPORTED = 2,
+  MOE_ERR_WORKSPACE = 3,
+  MOE_ERR_DEVICE = 4
+} moe_status;
+
+/* Element type of x, W_r, the expert weights, expert outputs and y.  Accumulation is always fp32
+ * and router logits are always fp32 (the tirogla page, Implementation notes: compute the router in
+ * fp32 because small logit differences decide routing). */
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+/* Gating (the tirogla page, How it works, step 1). */
+typedef enum {
+  MOE_GATE_SOFTMAX_TOPK = 0, /* softmax over the k selected logits (Mixtral)                       */
+  MOE_GATE_SOFTMAX_ALL = 1,  /* softmax over all E logits, keep the selected probabilities (Switch) */
+  MOE_GATE_SIGMOID_TOPK = 2  /* sigmoid affinities renormalised over the k selected (DeepSeek-V3)   */
+} moe_gating;
+
+/* moe_route flag: skip the router product and read `logits` as an input. */
+#define MOE_ROUTE_LOGITS_IN 0x1u
+
+/* Workspace bytes that cover every call below for this layer shape (max over the calls). */
+size_t moe_workspace_bytes(int T, int d, int d_ff, int E, int k, moe_dtype dt);
+
+/* Human-readable name of a status code (static string, host memory). */
+const char* moe_status_str(moe_status s);
+
+/*
+ * moe_route -- Score and Select (the tirogla page, How it works steps 1-2, and its Code `route`;
+ * the worked top-2 example of the dineshblog page, section 2).
+ *
+ *   logits[t,e] = sum_j x[t,j] * w_r[j,e] + logit_bias[e]      (fp32 accumulate)
+ *   topk_idx[t,0..k)  the k largest logits of row t, in descending order; equal logits go to the
+ *                     lower expert index first; -0.0 equals +0.0; -inf ranks last.
+ *   topk_gate[t,s]    SOFTMAX_TOPK: exp(L_e - m) / sum_sel exp(L_s - m), m = row max
+ *                     SOFTMAX_ALL:  exp(L_e - m) / sum_all exp(L_j - m)
+ *                     SIGMOID_TOPK: sigmoid(L_e) / sum_sel sigmoid(L_s)
+ *   prob_sum[e]       sum over tokens of the full-row softmax p[t,e] (the P_e numerator of the
+ *                     load-balancing loss, in every gating mode)
+ *   lse_sq_sum[0]     sum over tokens of logsumexp(row t)^2 (the z-loss numerator)
+ *
+ * x [T,d] and w_r [d,E] in dtype `dt`; logit_bias [E] fp32 or NULL; logits [T,E] fp32 (output, or
+ * input with MOE_ROUTE_LOGITS_IN, in which case x and w_r may be NULL and logit_bias must be
+ * NULL); topk_idx [T,k] int32; topk_gate [T,k] fp32; prob_sum [E] fp32; lse_sq_sum [1] fp32.
+ * prob_sum and lse_sq_sum may be NULL.  Non-finite logits violate the precondition: routing is then
+ * unspecified but memory-safe (indices stay in [0,E) and distinct within a row).
+ * Results are bitwise deterministic run to run.
+ */
+moe_status moe_route(const void* x, const void* w_r, const float* logit_bias, int T, int d, int E,
+                     int k, moe_dtype dt, moe_gating gating, unsigned flags, float* logits,
+                     int32_t* topk_idx, float* topk_gate, float* prob_sum, float* lse_sq_sum,
+                     void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * moe_dispatch -- Dispatch (the tirogla page, How it works step 3 and Code `dispatch`; capacity and
+ * token dropping as in the dineshblog page, section 3.2).  A stable counting sort of the T*k
+ * assignments by expert; each expert keeps its first `capacity` assignments in increasing
+ * assignment order a = t*k + s, later ones are dropped.
+ *
+ *   counts[e]        assignments to e before capacity                      int32 [E]
+ *   offsets[e]       exclusive prefix sum of kept_e = min(counts[e], C)     int32 [E+1]
+ *   perm[r]          for offsets[e] <= r < offsets[e+1]: expert e's kept assignment ids in
+ *                    increasing order; entries at r >= offsets[E] are unspecified  int32 [T*k]
+ *   inv[a]           the r with perm[r] = a, or -1 when a was dropped       int32 [T*k]
+ *   n_dropped[0]     T*k - offsets[E]                                       int32 [1]
+ *
+ * topk_idx [T,k] with entries in [0,E).  An out-of-range entry (checked on the device) is not counted
+ * in counts, gets inv = -1 and is included in n_dropped.  capacity <= 0 means unlimited.
+ * Deterministic.
+ */
+moe_status moe_dispatch(const int32_t* topk_idx, int T, int E, int k, int capacity,
+                        int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv,
+                        int32_t* n_dropped, void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * moe_expert_ffn -- Compute (the tirogla page, How it works step 4: every expert runs its FFN on its
+ * contiguous batch, as one grouped GEMM).  The expert is SwiGLU (the dineshblog page, section 1.1):
+ *
+ *   h   = silu(x_t . w1_e) * (x_t . w3_e)      silu(z) = z / (1 + exp(-z))
+ *   out[r] = h . w2_e                          for every row r in [offsets[e], offsets[e+1])
+ *
+ * where token t = perm[r] / k.  Rows are those of moe_dispatch: out is in perm order, and only rows
+ * r < offsets[E] are written.  With perm == NULL the call is one dense group over the T tokens
+ * (row r = token r; E must be 1 and offsets may be NULL): this is how a shared, always-on expert
+ * runs (the starphix page, Expert Architectures: Shared + Specialized).
+ *
+ * x [T,d]; w1, w3 [E][d][d_ff]; w2 [E][d_ff][d]; out [T*k][d] (routed) or [T][d] (perm NULL); all in
+ * dtype `dt`.  h is kept in the workspace in dtype `dt` (bf16 layers round h to bf16 before the
+ * down projection; accumulation is fp32).
+ */
+moe_status moe_expert_ffn(const void* x, const int32_t* perm, const int32_t* offsets, int T, int d,
+                          int d_ff, int E, int k, const void* w1, const void* w3, const void* w2,
+                          moe_dtype dt, void* out, void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * moe_combine -- Combine (the tirogla page, How it works step 5 and Code `combine`):
+ *
+ *   y[t] = sum over s with inv[t*k+s] >= 0 of topk_gate[t,s] * expert_out[inv[t*k+s]]
+ *          (+ shared_out[t] with weight 1 when shared_out is not NULL)
+ *
+ * Dropped assignments add nothing; the residual is not included (a token whose assignments were
+ * all dropped gets y = 0, or its shared output).  Sums in fp32, rounds y once to dtype `dt`.
+ * expert_out [T*k][d]; inv [T*k]; topk_gate [T,k] fp32; shared_out [T][d] or NULL; y [T][d].
+ */
+moe_status moe_combine(const void* expert_out, const int32_t* inv, const float* topk_gate, int T,
+                       int d, int k, moe_dtype dt, const void* shared_out, void* y, void* stream);
+
+/*
+ * moe_aux_loss -- Balance (the tirogla page, How it works step 6 and Code `aux_loss`, `z_loss`):
+ *
+ *   aux[0] = alpha * E * sum_e f_e * P_e,  f_e = counts[e] / (T*k),  P_e = prob_sum[e] / T
+ *   z[0]   = beta * lse_sq_sum[0] / T
+ *
+ * counts from moe_dispatch (before capacity); prob_sum and lse_sq_sum from moe_route.  aux and z
+ * are fp32 [1] each.  Equals alpha exactly in real arithmetic when either f or P is uniform.
+ */
+moe_status moe_aux_loss(const int32_t* counts, const float* prob_sum, const float* lse_sq_sum,
+                        int T, int E, int k, float alpha, float beta, float* aux, float* z,
+                        void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBMOE_MOE_H */

@@ -1,0 +1,112 @@
+// Combine and loss reduction.
+//   combine: y[t] = sum_s gate[t,s] * out[inv[t*k+s]] (+ shared[t]); the page "Mixture of experts
+//            (MoE)" (tirogla), How it works step 5 and Code `combine`.
+//   losses:  aux = alpha * E * sum_e (counts_e / (T*k)) * (prob_sum_e / T); z = beta * lse2 / T;
+//            the same page, How it works step 6 and Code `aux_loss`, `z_loss`.
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+// One block per token row; each thread owns 16-byte column chunks.  Gathers the token's k expert
+// rows through inv, sums in fp32 in slot order and writes y once.
+template <bool BF16>
+__global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ expert_out,
+                                                      const int32_t* __restrict__ inv,
+                                                      const float* __restrict__ gate, int T, int d,
+                                                      int k, const void* __restrict__ shared_out,
+                                                      void* __restrict__ y) {
+  __shared__ int32_t s_pos[32];
+  __shared__ float s_g[32];
+  const int t = blockIdx.x;
+  if (threadIdx.x < k) {
+    s_pos[threadIdx.x] = inv[(size_t)t * k + threadIdx.x];
+    s_g[threadIdx.x] = gate[(size_t)t * k + threadIdx.x];
+  }
+  __syncthreads();
+  constexpr int VEC = BF16 ? 8 : 4;  // elements per 16-byte chunk
+  const int nchunk = d / VEC;
+  for (int c = threadIdx.x; c < nchunk; c += blockDim.x) {
+    float acc[VEC];
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) acc[i] = 0.f;
+    for (int s = 0; s < k; ++s) {
+      const int pos = s_pos[s];
+      if (pos < 0) continue;
+      const float g = s_g[s];
+      float v[VEC];
+      if constexpr (BF16) {
+        unpack8(*reinterpret_cast<const u32x4*>((const uint16_t*)expert_out + (size_t)pos * d + c * 8), v);
+      } else {
+        const f32x4 q = *reinterpret_cast<const f32x4*>((const float*)expert_out + (size_t)pos * d + c * 4);
+        v[0] = q[0]; v[1] = q[1]; v[2] = q[2]; v[3] = q[3];
+      }
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) acc[i] = fmaf(g, v[i], acc[i]);
+    }
+    if (shared_out) {
+      float v[VEC];
+      if constexpr (BF16) {
+        unpack8(*reinterpret_cast<const u32x4*>((const uint16_t*)shared_out + (size_t)t * d + c * 8), v);
+      } else {
+        const f32x4 q = *reinterpret_cast<const f32x4*>((const float*)shared_out + (size_t)t * d + c * 4);
+        v[0] = q[0]; v[1] = q[1]; v[2] = q[2]; v[3] = q[3];
+      }
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) acc[i] += v[i];
+    }
+    if constexpr (BF16) {
+      u32x4 o;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(acc[2 * i], acc[2 * i + 1]);
+      *reinterpret_cast<u32x4*>((uint16_t*)y + (size_t)t * d + c * 8) = o;
+    } else {
+      f32x4 o = {acc[0], acc[1], acc[2], acc[3]};
+      *reinterpret_cast<f32x4*>((float*)y + (size_t)t * d + c * 4) = o;
+    }
+  }
+}
+
+void launch_combine(const void* expert_out, const int32_t* inv, const float* gate, int T, int d,
+                    int k, bool bf16, const void* shared_out, void* y, hipStream_t s) {
+  const int vec = bf16 ? 8 : 4;
+  int threads = 64;
+  while (threads < 256 && threads * vec < d) threads *= 2;
+  if (bf16)
+    hipLaunchKernelGGL(combine_kernel<true>, dim3(T), dim3(threads), 0, s, expert_out, inv, gate, T,
+                       d, k, shared_out, y);
+  else
+    hipLaunchKernelGGL(combine_kernel<false>, dim3(T), dim3(threads), 0, s, expert_out, inv, gate,
+                       T, d, k, shared_out, y);
+}
+
+// One block; fixed-order fp64 reduction over the experts so the result is deterministic.
+__global__ __launch_bounds__(256) void aux_loss_kernel(const int32_t* __restrict__ counts,
+                                                       const float* __restrict__ prob_sum,
+                                                       const float* __restrict__ lse_sq_sum, int T,
+                                                       int E, int k, float alpha, float beta,
+                                                       float* __restrict__ aux,
+                                                       float* __restrict__ z) {
+  __shared__ double part[256];
+  double s = 0.0;
+  for (int e = threadIdx.x; e < E; e += 256) s += (double)counts[e] * (double)prob_sum[e];
+  part[threadIdx.x] = s;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if (threadIdx.x < o) part[threadIdx.x] += part[threadIdx.x + o];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    const double TT = (double)T;
+    aux[0] = (float)((double)alpha * (double)E * part[0] / ((double)k * TT * TT));
+    z[0] = (float)((double)beta * (double)lse_sq_sum[0] / TT);
+  }
+}
+
+void launch_aux_loss(const int32_t* counts, const float* prob_sum, const float* lse_sq_sum, int T,
+                     int E, int k, float alpha, float beta, float* aux, float* z, hipStream_t s) {
+  hipLaunchKernelGGL(aux_loss_kernel, dim3(1), dim3(256), 0, s, counts, prob_sum, lse_sq_sum, T, E,
+                     k, alpha, beta, aux, z);
+}
+
+}  // namespace moe

@@ -1,0 +1,112 @@
+// Grouped-GEMM launch parameters and the device-side tile scheduler shared by the GEMM kernels.
+//
+// A grouped GEMM here is: for every group g (an expert) and every row r in [offsets[g],
+// offsets[g+1]), C[r, :] = A[src(r), :] . B_g (+ epilogue), with B_g = B + g * b_gstride a [K][N]
+// row-major matrix (N contiguous, the layout the weights are given in).  src(r) = gather[r] /
+// gather_div when a gather list is given (token of assignment perm[r]), else r.  The group sizes
+// live on the device (they come out of the dispatch kernels), so the grid is sized for an upper
+// bound and every block finds its tile from `offsets` itself; blocks past the real tile count exit.
+#pragma once
+
+#include "common.h"
+
+namespace moe {
+
+struct GemmParams {
+  const void* A;            // [rows][K], element type of the kernel
+  const int32_t* gather;    // NULL: A row r; else A row gather[r] / gather_div
+  int gather_div;
+  const int32_t* offsets;   // [G+1] on the device, or NULL for one group of M rows
+  int G;
+  int M;                    // rows of the single group (offsets == NULL)
+  int N, K;
+  const void* B0;           // [G][K][N]
+  const void* B1;           // second matrix for the fused SwiGLU epilogue (same layout) or NULL
+  long long b_gstride;      // elements between consecutive groups' B
+  void* C;                  // output rows, [rows][ldc]
+  int ldc;
+  const float* bias;        // fp32 [N] added by the fp32 epilogue, or NULL
+};
+
+enum { EPI_SWIGLU = 0, EPI_STORE = 1, EPI_STORE_F32_BIAS = 2 };
+
+struct TileCoord {
+  int g;        // group
+  int row0;     // first output row of the tile (global row index)
+  int row_end;  // end of the group's rows
+  int n_tile;   // column tile index
+};
+
+// Map block `bid` to a tile.  Tiles are ordered group by group; inside a group n-tile by n-tile,
+// with the m-tiles of one n-tile consecutive (they share the same B tile).  Consecutive tiles are
+// placed on the same XCD (blocks are handed to the 8 XCDs round-robin), so the m-tiles sharing a
+// B tile also share that XCD's L2.  Returns false when bid is past the real tile count.
+template <int BM>
+__device__ __forceinline__ bool find_tile(const GemmParams& p, int NT, int bid, TileCoord& tc) {
+  const int lane = __lane_id();
+  int total;
+  if (p.offsets == nullptr) {
+    const int tm = (p.M + BM - 1) / BM;
+    total = tm * NT;
+    if (bid >= total) return false;
+    const int q = total >> 3, r = total & 7, x = bid & 7, i = bid >> 3;
+    const int t = (x < r) ? x * (q + 1) + i : r * (q + 1) + (x - r) * q + i;
+    tc.g = 0;
+    tc.row0 = (t % tm) * BM;
+    tc.n_tile = t / tm;
+    tc.row_end = p.M;
+    return true;
+  }
+  // Per-lane slice of the groups; wave-wide inclusive scan of the tile counts.
+  const int per = (p.G + 63) >> 6;
+  const int g0 = min(p.G, lane * per), g1 = min(p.G, g0 + per);
+  int mine = 0;
+  for (int g = g0; g < g1; ++g) {
+    const int n = p.offsets[g + 1] - p.offsets[g];
+    mine += ((n + BM - 1) / BM) * NT;
+  }
+  int incl = mine;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int u = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += u;
+  }
+  total = __shfl(incl, 63, 64);
+  if (bid >= total) return false;
+  const int q = total >> 3, r = total & 7, x = bid & 7, i = bid >> 3;
+  const int t = (x < r) ? x * (q + 1) + i : r * (q + 1) + (x - r) * q + i;
+  const int excl = incl - mine;
+  const uint64_t own = __ballot(t >= excl && t < incl);
+  const int owner = __ffsll((long long)own) - 1;
+  int g_found = 0, base = 0;
+  if (lane == owner) {
+    base = excl;
+    for (int g = g0; g < g1; ++g) {
+      const int n = p.offsets[g + 1] - p.offsets[g];
+      const int c = ((n + BM - 1) / BM) * NT;
+      if (t < base + c) {
+        g_found = g;
+        break;
+      }
+      base += c;
+    }
+  }
+  g_found = __shfl(g_found, owner, 64);
+  base = __shfl(base, owner, 64);
+  const int rs = p.offsets[g_found], re = p.offsets[g_found + 1];
+  const int tm = (re - rs + BM - 1) / BM;
+  const int local = t - base;
+  tc.g = g_found;
+  tc.row0 = rs + (local % tm) * BM;
+  tc.row_end = re;
+  tc.n_tile = local / tm;
+  return true;
+}
+
+// Host-side upper bound on the number of tiles (for the grid size).
+inline int tiles_upper_bound(int rows_max, int G, bool grouped, int BM, int NT) {
+  const int tm = (rows_max + BM - 1) / BM + (grouped ? G : 0);
+  return tm * NT;
+}
+
+}  // namespace moe

@@ -1,0 +1,37 @@
+// Host-side launchers of the libmoe kernels (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+struct GemmParams;
+
+// route.hip
+void launch_router_small_e(const void* x, const void* w_r, const float* bias, int T, int d, int E,
+                           bool bf16, float* logits, hipStream_t s);
+void launch_gate_topk(const float* logits, int T, int E, int k, int mode, int32_t* topk_idx,
+                      float* topk_gate, float* part_p, float* part_l, float* prob_sum,
+                      float* lse_sq_sum, hipStream_t s);
+size_t route_workspace_bytes(int T, int E);
+int gate_rows_per_block(int T);
+
+// dispatch.hip
+size_t dispatch_workspace_bytes(int A, int E);
+void launch_dispatch(const int32_t* topk_idx, int A, int E, int capacity, int32_t* counts,
+                     int32_t* offsets, int32_t* perm, int32_t* inv, int32_t* n_dropped,
+                     int32_t* hist, hipStream_t s);
+
+// gemm_bf16.hip / gemm_f32.hip
+hipError_t launch_gemm_bf16(const GemmParams& p, int rows_max, int epi, hipStream_t s);
+hipError_t launch_gemm_f32(const GemmParams& p, int rows_max, int epi, hipStream_t s);
+
+// combine.hip
+void launch_combine(const void* expert_out, const int32_t* inv, const float* gate, int T, int d,
+                    int k, bool bf16, const void* shared_out, void* y, hipStream_t s);
+void launch_aux_loss(const int32_t* counts, const float* prob_sum, const float* lse_sq_sum, int T,
+                     int E, int k, float alpha, float beta, float* aux, float* z, hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,98 @@
+"""One MoE layer forward on the GPU through libmoe: buffers plus the five C entry points in order.
+
+Score+Select (moe_route) -> Dispatch (moe_dispatch) -> Compute (moe_expert_ffn, routed experts and
+the shared expert when there is one) -> Combine (moe_combine) -> Balance (moe_aux_loss), the step
+order of the page "Mixture of experts (MoE)" (tirogla), How it works.  PyTorch only allocates the
+device buffers and provides the stream; every step runs in the HIP library.
+"""
+
+import dataclasses
+
+import torch
+
+from . import libmoe as lm
+from .synth import GATING_CODE
+
+
+@dataclasses.dataclass
+class MoEBuffers:
+    logits: torch.Tensor
+    topk_idx: torch.Tensor
+    topk_gate: torch.Tensor
+    prob_sum: torch.Tensor
+    lse_sq_sum: torch.Tensor
+    counts: torch.Tensor
+    offsets: torch.Tensor
+    perm: torch.Tensor
+    inv: torch.Tensor
+    n_dropped: torch.Tensor
+    expert_out: torch.Tensor
+    shared_out: torch.Tensor
+    y: torch.Tensor
+    aux: torch.Tensor
+    z: torch.Tensor
+    workspace: torch.Tensor
+
+
+def alloc_buffers(cfg, device="cuda"):
+    dev = torch.device(device)
+    dt = torch.float32 if cfg.dtype == "fp32" else torch.bfloat16
+    code = lm.MOE_F32 if cfg.dtype == "fp32" else lm.MOE_BF16
+    T, d, E, k, f = cfg.T, cfg.d, cfg.E, cfg.k, cfg.d_ff
+    A = T * k
+    i32 = dict(dtype=torch.int32, device=dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    ws = lm.workspace_bytes(T, d, f, E, k, code)
+    return MoEBuffers(
+        logits=torch.empty((T, E), **f32), topk_idx=torch.empty((T, k), **i32),
+        topk_gate=torch.empty((T, k), **f32), prob_sum=torch.empty(E, **f32),
+        lse_sq_sum=torch.empty(1, **f32), counts=torch.empty(E, **i32),
+        offsets=torch.empty(E + 1, **i32), perm=torch.empty(A, **i32), inv=torch.empty(A, **i32),
+        n_dropped=torch.empty(1, **i32), expert_out=torch.empty((A, d), dtype=dt, device=dev),
+        shared_out=torch.empty((T, d), dtype=dt, device=dev) if cfg.n_shared else None,
+        y=torch.empty((T, d), dtype=dt, device=dev), aux=torch.empty(1, **f32),
+        z=torch.empty(1, **f32), workspace=torch.empty(ws, dtype=torch.uint8, device=dev))
+
+
+def route(cfg, inp, b, logits_in=False, stream=None):
+    code = lm.MOE_F32 if cfg.dtype == "fp32" else lm.MOE_BF16
+    lm.route(None if logits_in else inp.x, None if logits_in else inp.w_r,
+             None if logits_in else inp.bias, cfg.T, cfg.d, cfg.E, cfg.k, code,
+             GATING_CODE[cfg.gating], lm.ROUTE_LOGITS_IN if logits_in else 0, b.logits,
+             b.topk_idx, b.topk_gate, b.prob_sum, b.lse_sq_sum, b.workspace, stream)
+
+
+def dispatch(cfg, b, stream=None):
+    lm.dispatch(b.topk_idx, cfg.T, cfg.E, cfg.k, cfg.capacity, b.counts, b.offsets, b.perm, b.inv,
+                b.n_dropped, b.workspace, stream)
+
+
+def experts(cfg, inp, b, stream=None):
+    code = lm.MOE_F32 if cfg.dtype == "fp32" else lm.MOE_BF16
+    lm.expert_ffn(inp.x, b.perm, b.offsets, cfg.T, cfg.d, cfg.d_ff, cfg.E, cfg.k, inp.w1, inp.w3,
+                  inp.w2, code, b.expert_out, b.workspace, stream)
+    if cfg.n_shared:
+        w1s, w3s, w2s = inp.shared
+        lm.expert_ffn(inp.x, None, None, cfg.T, cfg.d, cfg.d_ff, 1, 1, w1s, w3s, w2s, code,
+                      b.shared_out, b.workspace, stream)
+
+
+def combine(cfg, b, stream=None):
+    code = lm.MOE_F32 if cfg.dtype == "fp32" else lm.MOE_BF16
+    lm.combine(b.expert_out, b.inv, b.topk_gate, cfg.T, cfg.d, cfg.k, code, b.shared_out, b.y,
+               stream)
+
+
+def losses(cfg, b, stream=None):
+    lm.aux_loss(b.counts, b.prob_sum, b.lse_sq_sum, cfg.T, cfg.E, cfg.k, cfg.alpha, cfg.beta,
+                b.aux, b.z, stream)
+
+
+def forward(cfg, inp, b, stream=None, logits_in=False):
+    """The whole hot path on one stream; no host synchronisation inside."""
+    route(cfg, inp, b, logits_in, stream)
+    dispatch(cfg, b, stream)
+    experts(cfg, inp, b, stream)
+    combine(cfg, b, stream)
+    losses(cfg, b, stream)
+    return b

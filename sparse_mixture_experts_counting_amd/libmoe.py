@@ -1,0 +1,123 @@
+"""ctypes binding of libmoe (the C ABI in include/moe.h).
+
+Argument marshalling only: every function takes device tensors (or None), passes their data
+pointers and the current HIP stream to the C entry point of the same name, and raises MoEError on a
+non-zero status.  Nothing here computes any part of the layer.  Loading fails loudly when the
+library has not been built (``python -m sparse_mixture_experts_counting_amd.build``).
+"""
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "_lib", "libmoe.so")
+
+MOE_F32, MOE_BF16 = 0, 1
+GATE_SOFTMAX_TOPK, GATE_SOFTMAX_ALL, GATE_SIGMOID_TOPK = 0, 1, 2
+ROUTE_LOGITS_IN = 0x1
+STATUS = {0: "MOE_OK", 1: "MOE_ERR_ARG", 2: "MOE_ERR_UNSUPPORTED", 3: "MOE_ERR_WORKSPACE",
+          4: "MOE_ERR_DEVICE"}
+
+EXPORTS = ("moe_workspace_bytes", "moe_status_str", "moe_route", "moe_dispatch", "moe_expert_ffn",
+           "moe_combine", "moe_aux_loss")
+
+
+class MoEError(RuntimeError):
+    def __init__(self, fn, status, msg):
+        super().__init__("%s failed: %s" % (fn, msg))
+        self.status = status
+
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError("libmoe.so is not built at %s; run "
+                      "`python -m sparse_mixture_experts_counting_amd.build`" % LIB_PATH)
+_lib = ctypes.CDLL(LIB_PATH)
+
+_p, _i, _u, _sz, _f = ctypes.c_void_p, ctypes.c_int, ctypes.c_uint, ctypes.c_size_t, ctypes.c_float
+_lib.moe_workspace_bytes.argtypes = [_i, _i, _i, _i, _i, _i]
+_lib.moe_workspace_bytes.restype = _sz
+_lib.moe_status_str.argtypes = [_i]
+_lib.moe_status_str.restype = ctypes.c_char_p
+_lib.moe_route.argtypes = [_p, _p, _p, _i, _i, _i, _i, _i, _i, _u, _p, _p, _p, _p, _p, _p, _sz, _p]
+_lib.moe_dispatch.argtypes = [_p, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _sz, _p]
+_lib.moe_expert_ffn.argtypes = [_p, _p, _p, _i, _i, _i, _i, _i, _p, _p, _p, _i, _p, _p, _sz, _p]
+_lib.moe_combine.argtypes = [_p, _p, _p, _i, _i, _i, _i, _p, _p, _p]
+_lib.moe_aux_loss.argtypes = [_p, _p, _p, _i, _i, _i, _f, _f, _p, _p, _p]
+for _n in ("moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_aux_loss"):
+    getattr(_lib, _n).restype = _i
+
+
+def lib():
+    return _lib
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _nbytes(t):
+    return 0 if t is None else t.numel() * t.element_size()
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(fn, status):
+    if status != 0:
+        raise MoEError(fn, status, _lib.moe_status_str(status).decode())
+
+
+def dtype_code(t):
+    if t.dtype == torch.bfloat16:
+        return MOE_BF16
+    if t.dtype == torch.float32:
+        return MOE_F32
+    raise TypeError("unsupported layer dtype %s" % t.dtype)
+
+
+def workspace_bytes(T, d, d_ff, E, k, dt):
+    return int(_lib.moe_workspace_bytes(T, d, d_ff, E, k, dt))
+
+
+def route(x, w_r, logit_bias, T, d, E, k, dt, gating, flags, logits, topk_idx, topk_gate,
+          prob_sum, lse_sq_sum, workspace, stream=None):
+    _check("moe_route", _lib.moe_route(
+        _ptr(x), _ptr(w_r), _ptr(logit_bias), T, d, E, k, dt, gating, flags, _ptr(logits),
+        _ptr(topk_idx), _ptr(topk_gate), _ptr(prob_sum), _ptr(lse_sq_sum), _ptr(workspace),
+        _nbytes(workspace), _stream(stream)))
+
+
+def dispatch(topk_idx, T, E, k, capacity, counts, offsets, perm, inv, n_dropped, workspace,
+             stream=None):
+    _check("moe_dispatch", _lib.moe_dispatch(
+        _ptr(topk_idx), T, E, k, capacity, _ptr(counts), _ptr(offsets), _ptr(perm), _ptr(inv),
+        _ptr(n_dropped), _ptr(workspace), _nbytes(workspace), _stream(stream)))
+
+
+def expert_ffn(x, perm, offsets, T, d, d_ff, E, k, w1, w3, w2, dt, out, workspace, stream=None):
+    _check("moe_expert_ffn", _lib.moe_expert_ffn(
+        _ptr(x), _ptr(perm), _ptr(offsets), T, d, d_ff, E, k, _ptr(w1), _ptr(w3), _ptr(w2), dt,
+        _ptr(out), _ptr(workspace), _nbytes(workspace), _stream(stream)))
+
+
+def combine(expert_out, inv, topk_gate, T, d, k, dt, shared_out, y, stream=None):
+    _check("moe_combine", _lib.moe_combine(
+        _ptr(expert_out), _ptr(inv), _ptr(topk_gate), T, d, k, dt, _ptr(shared_out), _ptr(y),
+        _stream(stream)))
+
+
+def aux_loss(counts, prob_sum, lse_sq_sum, T, E, k, alpha, beta, aux, z, stream=None):
+    _check("moe_aux_loss", _lib.moe_aux_loss(
+        _ptr(counts), _ptr(prob_sum), _ptr(lse_sq_sum), T, E, k, float(alpha), float(beta),
+        _ptr(aux), _ptr(z), _stream(stream)))

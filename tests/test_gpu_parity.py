@@ -1,0 +1,240 @@
+"""GPU parity of the libmoe hot path against the CPU oracle (needs an MI355X).
+
+Every call goes through the C ABI (ctypes binding).  Routing, dispatch and drop sets are compared
+bit-exactly; y, gates and losses within the tolerances stated in tests/parity.py.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import moe_oracle as O
+import parity as P
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def M():
+    from sparse_mixture_experts_counting_amd import build
+    import os
+    if not os.path.exists(build.LIB):
+        build.build()
+    from sparse_mixture_experts_counting_amd import layer, libmoe, synth
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    return dict(layer=layer, lm=libmoe, synth=synth)
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+# ------------------------------------------------------------------------ routing from given logits
+
+
+def _adversarial_logits(T, E, rng):
+    L = rng.normal(0, 2, size=(T, E)).astype(np.float32)
+    L[0] = 1.0                                              # all equal
+    if T > 1:
+        L[1] = rng.integers(-2, 3, size=E).astype(np.float32)   # many ties
+    if T > 2:
+        L[2] = 0.0
+        L[2, ::2] = -0.0                                    # signed zeros
+    if T > 3:
+        L[3] = -np.inf
+        L[3, E // 2] = 0.5                                  # one finite entry
+        if E > 3:
+            L[3, 1] = 0.25
+    if T > 4:
+        L[4] = rng.normal(0, 1, size=E).astype(np.float32) * 1e30   # huge magnitudes
+        L[4, 0] = 5.0e30
+    if T > 5:
+        L[5] = -1e30
+        L[5, E - 1] = 3.0                                   # masked logits
+        L[5, 0] = 2.0
+    if T > 6:
+        L[6] = np.float32(1e-40) * rng.integers(-3, 4, size=E)   # denormals
+    return L
+
+
+@pytest.mark.parametrize("E,k", [(1, 1), (4, 2), (8, 2), (8, 8), (13, 5), (64, 6), (65, 3),
+                                 (256, 8), (300, 32), (1024, 4)])
+@pytest.mark.parametrize("mode", ["softmax_topk", "softmax_all", "sigmoid_topk"])
+def test_route_from_given_logits(M, E, k, mode):
+    _say("route LOGITS_IN E=%d k=%d mode=%s" % (E, k, mode))
+    rng = np.random.default_rng(E * 100 + k)
+    T = 37
+    L = _adversarial_logits(T, E, rng)
+    cfg = M["synth"].tiny_config(T, 8, E, k, 8, "fp32", mode)
+    b = M["layer"].alloc_buffers(cfg)
+    b.logits.copy_(torch.from_numpy(L))
+    M["layer"].route(cfg, None, b, logits_in=True)
+    torch.cuda.synchronize()
+    want = O.select_topk(L, k)
+    np.testing.assert_array_equal(P.npi(b.topk_idx), want)
+    # Gates, probabilities and lse on the finite, well-conditioned rows (rows 0..2 and 7..).
+    rows = [t for t in range(T) if t in (0, 1, 2) or t >= 7]
+    g_ref = O.gate_weights(L[rows], want[rows], P.GATE_CODE[mode])
+    np.testing.assert_allclose(P.np32(b.topk_gate)[rows], g_ref, atol=1e-6, rtol=0)
+    if mode != "softmax_all":
+        assert np.all(np.abs(P.np32(b.topk_gate)[rows].sum(axis=1) - 1.0) < 1e-5)
+    p, lse = O.row_softmax_lse(L[rows])
+    # prob_sum / lse over all rows include the adversarial ones; compare a second, clean call.
+    Lc = L[rows]
+    cfg2 = M["synth"].tiny_config(len(rows), 8, E, k, 8, "fp32", mode)
+    b2 = M["layer"].alloc_buffers(cfg2)
+    b2.logits.copy_(torch.from_numpy(Lc))
+    M["layer"].route(cfg2, None, b2, logits_in=True)
+    torch.cuda.synchronize()
+    np.testing.assert_allclose(P.np32(b2.prob_sum), p.sum(axis=0), rtol=1e-5, atol=1e-6)
+    assert abs(float(P.np32(b2.lse_sq_sum)[0]) - float(np.sum(lse * lse))) <= 1e-5 * max(
+        1.0, float(np.sum(lse * lse)))
+
+
+# ------------------------------------------------------------------------ dispatch from given top-k
+
+
+@pytest.mark.parametrize("T,E,k,C", [(1, 1, 1, 0), (5, 3, 2, 1), (300, 8, 2, 40), (2048, 8, 1, 256),
+                                     (4096, 8, 2, 0), (3000, 64, 6, 200), (8192, 256, 8, 0),
+                                     (1500, 1024, 3, 2), (777, 17, 4, 0), (2500, 4, 1, 100)])
+def test_dispatch_from_given_topk(M, T, E, k, C):
+    _say("dispatch T=%d E=%d k=%d C=%d" % (T, E, k, C))
+    rng = np.random.default_rng(T + E + k + C)
+    # Skewed seeded logits so that some experts overflow.
+    L = (rng.normal(size=(T, E)) - 0.3 * np.log1p(np.arange(E))[None, :]).astype(np.float32)
+    idx = O.select_topk(L, k)
+    ref = dict(zip(("counts", "offsets", "perm", "inv", "n_dropped"), O.dispatch(idx, E, C)))
+    cfg = M["synth"].tiny_config(T, 8, E, k, 8, "fp32", capacity=C)
+    b = M["layer"].alloc_buffers(cfg)
+    b.topk_idx.copy_(torch.from_numpy(idx))
+    M["layer"].dispatch(cfg, b)
+    torch.cuda.synchronize()
+    P.check_dispatch_exact(b, ref)
+
+
+def test_dispatch_collapse(M):
+    """Every token prefers expert 0: counts [T, 0, ...], C kept, T - C dropped."""
+    T, E, C = 5000, 8, 320
+    idx = np.zeros((T, 1), np.int32)
+    cfg = M["synth"].tiny_config(T, 8, E, 1, 8, "bf16", capacity=C)
+    b = M["layer"].alloc_buffers(cfg)
+    b.topk_idx.copy_(torch.from_numpy(idx))
+    M["layer"].dispatch(cfg, b)
+    torch.cuda.synchronize()
+    assert P.npi(b.counts).tolist() == [T] + [0] * (E - 1)
+    assert P.npi(b.offsets).tolist() == [0] + [C] * E
+    assert int(P.npi(b.n_dropped)[0]) == T - C
+    assert P.npi(b.perm)[:C].tolist() == list(range(C))
+
+
+# ------------------------------------------------------------------------ whole layer
+
+
+def run_and_compare(M, cfg, inp, seed_note=""):
+    b = M["layer"].alloc_buffers(cfg)
+    M["layer"].forward(cfg, inp, b)
+    torch.cuda.synchronize()
+    h = P.host_inputs(inp)
+    mode = P.GATE_CODE[cfg.gating]
+    bound, exact = P.logit_error_bound(h["x"], h["w_r"], h["bias"])
+    gl = P.np32(b.logits)
+    assert np.all(np.abs(gl - exact) <= bound), "router logits outside the rounding bound"
+    ref = O.forward(h["x"], h["w_r"], h["w1"], h["w3"], h["w2"], cfg.k, mode,
+                    capacity=cfg.capacity, bias=h["bias"], shared=h["shared"], alpha=cfg.alpha,
+                    beta=cfg.beta)
+    flips = P.certify_routing(P.npi(b.topk_idx), ref["topk_idx"], exact, bound)
+    _say("  %s: flips=%d drops=%d" % (cfg.name, len(flips), ref["n_dropped"]))
+    if not flips:
+        P.check_dispatch_exact(b, ref)
+        err = P.rel_err(P.np32(b.y), ref["y"])
+        assert err <= P.y_tol(cfg), "y relative error %.3e" % err
+        np.testing.assert_allclose(P.np32(b.topk_gate), ref["topk_gate"], atol=1e-6, rtol=0)
+        P.check_losses(cfg, b, ref)
+    else:
+        keep = np.setdiff1d(np.arange(cfg.T), flips)
+        if cfg.capacity <= 0:
+            err = P.rel_err(P.np32(b.y)[keep], ref["y"][keep])
+            assert err <= P.y_tol(cfg)
+    return b, ref
+
+
+@pytest.mark.parametrize("name", ["tiny_fp32", "switch_top1", "switch_top1_c256"])
+def test_layer_small_workloads(M, name):
+    _say("layer", name)
+    cfg = M["synth"].CONFIGS[name]
+    inp = M["synth"].make_inputs(cfg, seed=0, device="cpu")
+    inp = _to_cuda(inp)
+    b, ref = run_and_compare(M, cfg, inp)
+    if name == "switch_top1_c256":
+        assert ref["n_dropped"] > 0
+
+
+def _to_cuda(inp):
+    import dataclasses
+    kw = {}
+    for f in dataclasses.fields(inp):
+        v = getattr(inp, f.name)
+        if isinstance(v, torch.Tensor):
+            v = v.cuda()
+        elif isinstance(v, tuple):
+            v = tuple(t.cuda() for t in v)
+        kw[f.name] = v
+    return type(inp)(**kw)
+
+
+SWEEP = [
+    # T, d, E, k, d_ff, dtype, gating, C, shared, zipf
+    (1, 8, 1, 1, 8, "bf16", "softmax_topk", 0, 0, 0.0),
+    (3, 24, 4, 2, 40, "bf16", "softmax_all", 0, 0, 0.0),
+    (257, 136, 8, 2, 264, "bf16", "softmax_topk", 0, 0, 0.0),
+    (257, 136, 8, 2, 264, "fp32", "sigmoid_topk", 70, 0, 0.0),
+    (300, 64, 17, 3, 72, "bf16", "sigmoid_topk", 0, 0, 0.0),
+    (129, 520, 24, 4, 200, "bf16", "softmax_topk", 30, 0, 0.0),
+    (64, 256, 64, 6, 128, "bf16", "sigmoid_topk", 0, 1, 1.1),
+    (700, 72, 3, 1, 48, "fp32", "softmax_all", 200, 0, 0.0),
+    (513, 328, 16, 2, 296, "bf16", "softmax_topk", 0, 1, 0.0),
+    (200, 16, 256, 8, 24, "bf16", "sigmoid_topk", 0, 1, 1.1),
+]
+
+
+@pytest.mark.parametrize("case", SWEEP, ids=lambda c: "T%d_d%d_E%d_k%d_f%d_%s_%s_C%d_s%d" % c[:9])
+def test_layer_property_sweep(M, case):
+    T, d, E, k, f, dt, g, C, sh, zipf = case
+    _say("sweep", case)
+    cfg = M["synth"].tiny_config(T, d, E, k, f, dt, g, capacity=C, n_shared=sh, zipf_s=zipf)
+    inp = _to_cuda(M["synth"].make_inputs(cfg, seed=1, device="cpu"))
+    run_and_compare(M, cfg, inp)
+
+
+def test_determinism(M):
+    _say("determinism")
+    cfg = M["synth"].tiny_config(1000, 256, 16, 4, 512, "bf16", "sigmoid_topk", capacity=300,
+                                 n_shared=1, zipf_s=1.1)
+    inp = _to_cuda(M["synth"].make_inputs(cfg, seed=3, device="cpu"))
+    outs = []
+    for _ in range(2):
+        b = M["layer"].alloc_buffers(cfg)
+        M["layer"].forward(cfg, inp, b)
+        torch.cuda.synchronize()
+        outs.append(b)
+    for name in ("logits", "topk_idx", "topk_gate", "prob_sum", "lse_sq_sum", "counts", "offsets",
+                 "inv", "n_dropped", "y", "aux", "z"):
+        a, c = getattr(outs[0], name), getattr(outs[1], name)
+        assert torch.equal(a.view(torch.uint8) if a.dtype == torch.bfloat16 else a,
+                           c.view(torch.uint8) if c.dtype == torch.bfloat16 else c), name
+
+
+def test_error_codes_on_device(M):
+    """Workspace too small and unsupported shapes are refused before any launch."""
+    lm = M["lm"]
+    cfg = M["synth"].tiny_config(16, 16, 4, 2, 16, "bf16")
+    b = M["layer"].alloc_buffers(cfg)
+    small = torch.empty(8, dtype=torch.uint8, device="cuda")
+    with pytest.raises(lm.MoEError) as ei:
+        lm.dispatch(b.topk_idx, 16, 4, 2, 0, b.counts, b.offsets, b.perm, b.inv, b.n_dropped, small)
+    assert ei.value.status == 3
+    x = torch.zeros((16, 12), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(lm.MoEError) as ei:
+        lm.expert_ffn(x, b.perm, b.offsets, 16, 12, 16, 4, 2, x, x, x, lm.MOE_BF16, b.expert_out,
+                      b.workspace)
+    assert ei.value.status == 2
