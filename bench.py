@@ -1,0 +1,236 @@
+#!/usr/bin/env python3
+"""Benchmark of one top-k routed MoE FFN layer forward on one MI355X.
+
+A step is one pass of the whole hot path over one batch of synthetic tokens: router product and
+gating (moe_route), counting-sort dispatch (moe_dispatch), the SwiGLU up projection and the down
+projection of every expert as grouped GEMMs (moe_expert_up / moe_expert_down; plus the shared
+expert when the workload has one), the gate-weighted combine (moe_combine) and the loss reduction
+(moe_aux_loss).  Inputs are resident in HBM before timing starts.
+
+Prints ONE JSON line: tokens/s of the layer, per-stage kernel times from HIP events recorded on the
+stream the kernels run on, the roofline of the dominant kernel (the fused up projection + SwiGLU
+grouped GEMM) against the bf16 matrix-core peak, and the CPU oracle timed on a bounded sample.
+
+    python bench.py [--steps K] [--warmup W] [--workload mixtral_prefill]
+"""
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 matrix-core peak
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E peak
+DOMINANT = "expert_up"        # fused up projection + SwiGLU grouped GEMM
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_%s.json")
+KERNEL_SRC = os.path.join(ROOT, "sparse_mixture_experts_counting_amd", "csrc", "gemm_bf16.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash():
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def load_traffic(workload):
+    """HBM bytes per launch of the dominant kernel from the committed PMC summary, if it was taken
+    on the current kernel source; else None."""
+    path = TRAFFIC_FILE % workload
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(cfg, inp, n_tokens):
+    """The CPU oracle (float64 NumPy, as it stands) on the first n_tokens tokens of the same
+    workload.  Returns tokens/s, BLAS threads used and a description of the sample."""
+    import numpy as np
+    from oracle import moe_oracle as O
+    from threadpoolctl import threadpool_info
+
+    n = min(n_tokens, cfg.T)
+    f = lambda t: t.detach().float().cpu().numpy()
+    x = f(inp.x[:n])
+    w_r = f(inp.w_r)
+    bias = None if inp.bias is None else f(inp.bias)
+    mode = {"softmax_topk": 0, "softmax_all": 1, "sigmoid_topk": 2}[cfg.gating]
+    # Host copies of the experts this sample touches (copying is not part of the timed work).
+    idx = O.select_topk(O.router_logits(x, w_r, bias), cfg.k)
+    used = sorted(set(idx.reshape(-1).tolist()))
+    w1 = {e: f(inp.w1[e]) for e in used}
+    w3 = {e: f(inp.w3[e]) for e in used}
+    w2 = {e: f(inp.w2[e]) for e in used}
+    shared = tuple(f(w) for w in inp.shared) if inp.shared is not None else None
+    cap = cfg.capacity
+    if cap > 0:   # same capacity factor on the smaller batch
+        cap = max(1, int(math.ceil(cap * n / cfg.T)))
+    t0 = time.perf_counter()
+    O.forward(x, w_r, w1, w3, w2, cfg.k, mode, capacity=cap, bias=bias, shared=shared,
+              alpha=cfg.alpha, beta=cfg.beta)
+    dt = time.perf_counter() - t0
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()
+                   if p.get("user_api") == "blas"] or [1])
+    sample = ("first %d of %d tokens of %s, all steps of the layer, float64 NumPy oracle "
+              "(%d experts touched)" % (n, cfg.T, cfg.name, len(used)))
+    return n / dt, threads, sample, dt
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="mixtral_prefill")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=3072)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print("bench.py: this build measures one GPU only; --gpus %d is not supported "
+              "(run with --gpus 1)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from sparse_mixture_experts_counting_amd import build as B
+    if not os.path.exists(B.LIB):
+        B.build()
+    from sparse_mixture_experts_counting_amd import layer, libmoe as lm, synth
+
+    cfg = synth.CONFIGS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log("bench: workload %s, generating inputs on the device" % cfg.name)
+    inp = synth.make_inputs(cfg, seed=args.seed, device=dev)
+    buf = layer.alloc_buffers(cfg, dev)
+    code = lm.MOE_F32 if cfg.dtype == "fp32" else lm.MOE_BF16
+    stream = torch.cuda.current_stream(dev)
+    h = buf.workspace   # h lives in the workspace between the two expert GEMMs
+
+    stages = ["route", "dispatch", "expert_up", "expert_down", "shared_up", "shared_down",
+              "combine", "aux_loss"]
+    if not cfg.n_shared:
+        stages = [s for s in stages if not s.startswith("shared")]
+
+    def step(ev=None):
+        def mark(i):
+            if ev is not None:
+                ev[i].record(stream)
+        mark(0)
+        layer.route(cfg, inp, buf)
+        mark(1)
+        layer.dispatch(cfg, buf)
+        mark(2)
+        lm.expert_up(inp.x, buf.perm, buf.offsets, cfg.T, cfg.d, cfg.d_ff, cfg.E, cfg.k, inp.w1,
+                     inp.w3, code, h)
+        mark(3)
+        lm.expert_down(h, buf.offsets, cfg.T, cfg.d, cfg.d_ff, cfg.E, cfg.k, inp.w2, code,
+                       buf.expert_out)
+        mark(4)
+        i = 4
+        if cfg.n_shared:
+            w1s, w3s, w2s = inp.shared
+            lm.expert_up(inp.x, None, None, cfg.T, cfg.d, cfg.d_ff, 1, 1, w1s, w3s, code, h)
+            mark(5)
+            lm.expert_down(h, None, cfg.T, cfg.d, cfg.d_ff, 1, 1, w2s, code, buf.shared_out)
+            mark(6)
+            i = 6
+        layer.combine(cfg, buf)
+        mark(i + 1)
+        layer.losses(cfg, buf)
+        mark(i + 2)
+
+    # A plain copy of known size, untimed: the byte-counter calibration for PMC runs.
+    calib_src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
+    calib_dst = torch.empty_like(calib_src)
+    calib_dst.copy_(calib_src)
+    del calib_src, calib_dst
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize(dev)
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)]
+              for _ in range(args.steps)]
+    torch.cuda.synchronize(dev)
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(events[s])
+    torch.cuda.synchronize(dev)
+    wall = time.perf_counter() - t0
+
+    stage_ms = {}
+    for j, name in enumerate(stages):
+        stage_ms[name] = sum(events[s][j].elapsed_time(events[s][j + 1])
+                             for s in range(args.steps)) / args.steps
+    gpu_ms = sum(events[s][0].elapsed_time(events[s][-1]) for s in range(args.steps)) / args.steps
+    ms_per_step = wall * 1e3 / args.steps
+
+    counts = buf.counts.cpu().tolist()
+    n_kept = int(buf.offsets[-1].item())
+    n_dropped = int(buf.n_dropped.item())
+    touched = sum(1 for c in counts if c > 0)
+    T, d, E, k, f = cfg.T, cfg.d, cfg.E, cfg.k, cfg.d_ff
+    sb = 4 if cfg.dtype == "fp32" else 2
+    up_flops = 4.0 * d * f * n_kept
+    down_flops = 2.0 * d * f * n_kept
+    layer_flops = 2.0 * T * d * E + 6.0 * d * f * (n_kept + T * cfg.n_shared)
+    layer_bytes = sb * (3.0 * d * f * (touched + cfg.n_shared) + 2.0 * T * d + d * E)
+    up_ms = stage_ms["expert_up"]
+    achieved = up_flops / (up_ms * 1e-3) / 1e12
+    traffic = load_traffic(cfg.name)
+    gg_ms = stage_ms["expert_up"] + stage_ms["expert_down"]
+    result = {
+        "metric": "MoE layer tokens/s at 1 GPU; expert grouped-GEMM % bf16 MFMA peak",
+        "value": T / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if cfg.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded randn inputs and random-init expert weights of the workload's "
+                "shapes, drawn on the device)",
+        "config": {"workload": cfg.name, "T": T, "d": d, "E": E, "k": k, "d_ff": f,
+                   "gating": cfg.gating, "capacity": cfg.capacity or None,
+                   "shared_experts": cfg.n_shared, "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "mfma", "kernel": "moe_expert_up (gemm_bf16 SwiGLU)",
+                     "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic},
+        "grouped_gemm": {"ms": gg_ms, "tflops": (up_flops + down_flops) / (gg_ms * 1e-3) / 1e12,
+                         "frac_bf16_peak": (up_flops + down_flops) / (gg_ms * 1e-3) / 1e12
+                         / PEAK_BF16_TFLOPS},
+        "layer": {"gpu_event_ms": gpu_ms, "tflops": layer_flops / (ms_per_step * 1e-3) / 1e12,
+                  "hbm_gbs_algorithmic": layer_bytes / (ms_per_step * 1e-3) / 1e9,
+                  "algorithmic_flops": layer_flops, "algorithmic_bytes": layer_bytes,
+                  "kept_assignments": n_kept, "dropped": n_dropped, "experts_touched": touched},
+        "stage_ms": stage_ms,
+    }
+    del h
+    if not args.no_cpu_baseline:
+        log("bench: timing the CPU oracle on a sample")
+        v, threads, sample, secs = cpu_baseline(cfg, inp, args.cpu_sample_tokens)
+        result["cpu_baseline"] = {"value": v, "unit": "tokens/s", "cores": threads,
+                                  "kind": "oracle", "sample": sample, "seconds": secs}
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -133,6 +133,23 @@ moe_status moe_expert_ffn(const void* x, const int32_t* perm, const int32_t* off
                           moe_dtype dt, void* out, void* workspace, size_t ws_bytes, void* stream);
 
 /*
+ * moe_expert_up / moe_expert_down -- the two halves of moe_expert_ffn, for callers that keep h
+ * themselves (to overlap the shared expert with the routed ones, or to time each half):
+ *
+ *   moe_expert_up:   h[r]   = silu(x_t . w1_e) * (x_t . w3_e)   h [rows][d_ff] in dtype `dt`
+ *   moe_expert_down: out[r] = h[r] . w2_e                       out [rows][d]
+ *
+ * Same row convention as moe_expert_ffn (rows r < offsets[E], t = perm[r] / k); with perm == NULL
+ * (up) or offsets == NULL (down) the call is one dense group over T rows and E must be 1.  h must
+ * hold T*k rows (routed) or T rows (dense).  Same errors as moe_expert_ffn (no workspace).
+ */
+moe_status moe_expert_up(const void* x, const int32_t* perm, const int32_t* offsets, int T, int d,
+                         int d_ff, int E, int k, const void* w1, const void* w3, moe_dtype dt,
+                         void* h, void* stream);
+moe_status moe_expert_down(const void* h, const int32_t* offsets, int T, int d, int d_ff, int E,
+                           int k, const void* w2, moe_dtype dt, void* out, void* stream);
+
+/*
  * moe_combine -- Combine (the tirogla page, How it works step 5 and Code `combine`):
  *
  *   y[t] = sum over s with inv[t*k+s] >= 0 of topk_gate[t,s] * expert_out[inv[t*k+s]]

@@ -131,27 +131,26 @@ moe_status moe_dispatch(const int32_t* topk_idx, int T, int E, int k, int capaci
   return launched();
 }
 
-moe_status moe_expert_ffn(const void* x, const int32_t* perm, const int32_t* offsets, int T, int d,
-                          int d_ff, int E, int k, const void* w1, const void* w3, const void* w2,
-                          moe_dtype dt, void* out, void* workspace, size_t ws_bytes,
-                          void* stream) {
+static moe_status check_ffn_args(const void* x, const void* wa, const void* wb, const void* out,
+                                 bool grouped, const int32_t* offsets, int T, int d, int d_ff,
+                                 int E, int k, moe_dtype dt) {
   if (T < 1 || d < 1 || d_ff < 1 || E < 1 || k < 1) return MOE_ERR_ARG;
-  if (!x || !w1 || !w3 || !w2 || !out || !workspace || !dtype_ok(dt)) return MOE_ERR_ARG;
-  if (perm && (!offsets || k > E)) return MOE_ERR_ARG;
-  if (!perm && E != 1) return MOE_ERR_ARG;
-  if (!aligned16(x) || !aligned16(w1) || !aligned16(w3) || !aligned16(w2) || !aligned16(out) ||
-      !aligned16(workspace))
-    return MOE_ERR_ARG;
+  if (!x || !wa || !wb || !out || !dtype_ok(dt)) return MOE_ERR_ARG;
+  if (grouped && (!offsets || k > E)) return MOE_ERR_ARG;
+  if (!grouped && E != 1) return MOE_ERR_ARG;
+  if (!aligned16(x) || !aligned16(wa) || !aligned16(wb) || !aligned16(out)) return MOE_ERR_ARG;
   if (E > kMaxE || k > kMaxK) return MOE_ERR_UNSUPPORTED;
   if ((d % 8) != 0 || (d_ff % 8) != 0) return MOE_ERR_UNSUPPORTED;
-  const int rows_max = perm ? T * k : T;
-  if (!fits_i32((long long)T * k) || !fits_i32((long long)rows_max * d) ||
-      !fits_i32((long long)rows_max * d_ff) || !fits_i32((long long)T * d))
+  const long long rows_max = grouped ? (long long)T * k : T;
+  if (!fits_i32((long long)T * k) || !fits_i32(rows_max * d) || !fits_i32(rows_max * d_ff) ||
+      !fits_i32((long long)T * d))
     return MOE_ERR_UNSUPPORTED;
-  if (ws_bytes < ffn_workspace_bytes(rows_max, d_ff, dt)) return MOE_ERR_WORKSPACE;
-  hipStream_t s = (hipStream_t)stream;
-  const bool bf16 = dt == MOE_BF16;
+  return MOE_OK;
+}
 
+static hipError_t run_up(const void* x, const int32_t* perm, const int32_t* offsets, int T, int d,
+                         int d_ff, int E, int k, const void* w1, const void* w3, bool bf16, void* h,
+                         hipStream_t s) {
   moe::GemmParams up{};
   up.A = x;
   up.gather = perm;
@@ -164,18 +163,20 @@ moe_status moe_expert_ffn(const void* x, const int32_t* perm, const int32_t* off
   up.B0 = w1;
   up.B1 = w3;
   up.b_gstride = (long long)d * d_ff;
-  up.C = workspace;
+  up.C = h;
   up.ldc = d_ff;
-  hipError_t e = bf16 ? moe::launch_gemm_bf16(up, rows_max, moe::EPI_SWIGLU, s)
-                      : moe::launch_gemm_f32(up, rows_max, moe::EPI_SWIGLU, s);
-  if (e != hipSuccess) return MOE_ERR_DEVICE;
+  const int rows_max = perm ? T * k : T;
+  return bf16 ? moe::launch_gemm_bf16(up, rows_max, moe::EPI_SWIGLU, s)
+              : moe::launch_gemm_f32(up, rows_max, moe::EPI_SWIGLU, s);
+}
 
+static hipError_t run_down(const void* h, const int32_t* offsets, int T, int d, int d_ff, int E,
+                           int k, const void* w2, bool bf16, void* out, hipStream_t s) {
   moe::GemmParams dn{};
-  dn.A = workspace;
-  dn.gather = nullptr;
+  dn.A = h;
   dn.gather_div = 1;
-  dn.offsets = up.offsets;
-  dn.G = up.G;
+  dn.offsets = offsets;
+  dn.G = offsets ? E : 1;
   dn.M = T;
   dn.N = d;
   dn.K = d_ff;
@@ -183,10 +184,46 @@ moe_status moe_expert_ffn(const void* x, const int32_t* perm, const int32_t* off
   dn.b_gstride = (long long)d_ff * d;
   dn.C = out;
   dn.ldc = d;
-  e = bf16 ? moe::launch_gemm_bf16(dn, rows_max, moe::EPI_STORE, s)
-           : moe::launch_gemm_f32(dn, rows_max, moe::EPI_STORE, s);
+  const int rows_max = offsets ? T * k : T;
+  return bf16 ? moe::launch_gemm_bf16(dn, rows_max, moe::EPI_STORE, s)
+              : moe::launch_gemm_f32(dn, rows_max, moe::EPI_STORE, s);
+}
+
+moe_status moe_expert_ffn(const void* x, const int32_t* perm, const int32_t* offsets, int T, int d,
+                          int d_ff, int E, int k, const void* w1, const void* w3, const void* w2,
+                          moe_dtype dt, void* out, void* workspace, size_t ws_bytes,
+                          void* stream) {
+  moe_status st = check_ffn_args(x, w1, w3, out, perm != nullptr, offsets, T, d, d_ff, E, k, dt);
+  if (st != MOE_OK) return st;
+  if (!w2 || !aligned16(w2) || !workspace || !aligned16(workspace)) return MOE_ERR_ARG;
+  const int rows_max = perm ? T * k : T;
+  if (ws_bytes < ffn_workspace_bytes(rows_max, d_ff, dt)) return MOE_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  const bool bf16 = dt == MOE_BF16;
+  hipError_t e = run_up(x, perm, offsets, T, d, d_ff, E, k, w1, w3, bf16, workspace, s);
+  if (e != hipSuccess) return MOE_ERR_DEVICE;
+  e = run_down(workspace, perm ? offsets : nullptr, T, d, d_ff, E, k, w2, bf16, out, s);
   if (e != hipSuccess) return MOE_ERR_DEVICE;
   return launched();
+}
+
+moe_status moe_expert_up(const void* x, const int32_t* perm, const int32_t* offsets, int T, int d,
+                         int d_ff, int E, int k, const void* w1, const void* w3, moe_dtype dt,
+                         void* h, void* stream) {
+  moe_status st = check_ffn_args(x, w1, w3, h, perm != nullptr, offsets, T, d, d_ff, E, k, dt);
+  if (st != MOE_OK) return st;
+  hipError_t e = run_up(x, perm, offsets, T, d, d_ff, E, k, w1, w3, dt == MOE_BF16, h,
+                        (hipStream_t)stream);
+  return e != hipSuccess ? MOE_ERR_DEVICE : launched();
+}
+
+moe_status moe_expert_down(const void* h, const int32_t* offsets, int T, int d, int d_ff, int E,
+                           int k, const void* w2, moe_dtype dt, void* out, void* stream) {
+  moe_status st = check_ffn_args(h, w2, w2, out, offsets != nullptr, offsets, T, d, d_ff, E, k, dt);
+  if (st != MOE_OK) return st;
+  hipError_t e = run_down(h, offsets, T, d, d_ff, E, k, w2, dt == MOE_BF16, out,
+                          (hipStream_t)stream);
+  return e != hipSuccess ? MOE_ERR_DEVICE : launched();
 }
 
 moe_status moe_combine(const void* expert_out, const int32_t* inv, const float* topk_gate, int T,

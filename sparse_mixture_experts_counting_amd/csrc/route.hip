@@ -284,22 +284,27 @@ __global__ __launch_bounds__(256) void gate_topk_kernel(const float* __restrict_
   }
 }
 
+// Sum the per-block partials in a fixed order: one wave per expert (lanes stride over the blocks,
+// then a fixed butterfly), the lse partials by the extra wave E.  Deterministic.
 __global__ __launch_bounds__(256) void route_finalize_kernel(const float* __restrict__ part_p,
                                                              const float* __restrict__ part_l,
                                                              int nblk, int E,
                                                              float* __restrict__ prob_sum,
                                                              float* __restrict__ lse_sq_sum) {
-  if (prob_sum) {
-    for (int e = threadIdx.x; e < E; e += blockDim.x) {
-      float s = 0.f;
-      for (int b = 0; b < nblk; ++b) s += part_p[(size_t)b * E + e];
-      prob_sum[e] = s;
-    }
-  }
-  if (lse_sq_sum && threadIdx.x == 0) {
-    float s = 0.f;
-    for (int b = 0; b < nblk; ++b) s += part_l[b];
-    lse_sq_sum[0] = s;
+  const int lane = threadIdx.x & 63;
+  const int item = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (item > E) return;
+  float s = 0.f;
+  if (item < E) {
+    if (!prob_sum) return;
+    for (int b = lane; b < nblk; b += 64) s += part_p[(size_t)b * E + item];
+    s = wave_sum(s);
+    if (lane == 0) prob_sum[item] = s;
+  } else {
+    if (!lse_sq_sum) return;
+    for (int b = lane; b < nblk; b += 64) s += part_l[b];
+    s = wave_sum(s);
+    if (lane == 0) lse_sq_sum[0] = s;
   }
 }
 
@@ -327,8 +332,8 @@ void launch_gate_topk(const float* logits, int T, int E, int k, int mode, int32_
   else MOE_GATE(16);
 #undef MOE_GATE
   if (pp)
-    hipLaunchKernelGGL(route_finalize_kernel, dim3(1), dim3(256), 0, s, part_p, part_l, nblk, E,
-                       prob_sum, lse_sq_sum);
+    hipLaunchKernelGGL(route_finalize_kernel, dim3((E + 1 + 3) / 4), dim3(256), 0, s, part_p,
+                       part_l, nblk, E, prob_sum, lse_sq_sum);
 }
 
 size_t route_workspace_bytes(int T, int E) {

@@ -21,7 +21,7 @@ STATUS = {0: "MOE_OK", 1: "MOE_ERR_ARG", 2: "MOE_ERR_UNSUPPORTED", 3: "MOE_ERR_W
           4: "MOE_ERR_DEVICE"}
 
 EXPORTS = ("moe_workspace_bytes", "moe_status_str", "moe_route", "moe_dispatch", "moe_expert_ffn",
-           "moe_combine", "moe_aux_loss")
+           "moe_expert_up", "moe_expert_down", "moe_combine", "moe_aux_loss")
 
 
 class MoEError(RuntimeError):
@@ -43,9 +43,12 @@ _lib.moe_status_str.restype = ctypes.c_char_p
 _lib.moe_route.argtypes = [_p, _p, _p, _i, _i, _i, _i, _i, _i, _u, _p, _p, _p, _p, _p, _p, _sz, _p]
 _lib.moe_dispatch.argtypes = [_p, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _sz, _p]
 _lib.moe_expert_ffn.argtypes = [_p, _p, _p, _i, _i, _i, _i, _i, _p, _p, _p, _i, _p, _p, _sz, _p]
+_lib.moe_expert_up.argtypes = [_p, _p, _p, _i, _i, _i, _i, _i, _p, _p, _i, _p, _p]
+_lib.moe_expert_down.argtypes = [_p, _p, _i, _i, _i, _i, _i, _p, _i, _p, _p]
 _lib.moe_combine.argtypes = [_p, _p, _p, _i, _i, _i, _i, _p, _p, _p]
 _lib.moe_aux_loss.argtypes = [_p, _p, _p, _i, _i, _i, _f, _f, _p, _p, _p]
-for _n in ("moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_aux_loss"):
+for _n in ("moe_route", "moe_dispatch", "moe_expert_ffn", "moe_expert_up", "moe_expert_down",
+           "moe_combine", "moe_aux_loss"):
     getattr(_lib, _n).restype = _i
 
 
@@ -109,6 +112,17 @@ def expert_ffn(x, perm, offsets, T, d, d_ff, E, k, w1, w3, w2, dt, out, workspac
     _check("moe_expert_ffn", _lib.moe_expert_ffn(
         _ptr(x), _ptr(perm), _ptr(offsets), T, d, d_ff, E, k, _ptr(w1), _ptr(w3), _ptr(w2), dt,
         _ptr(out), _ptr(workspace), _nbytes(workspace), _stream(stream)))
+
+
+def expert_up(x, perm, offsets, T, d, d_ff, E, k, w1, w3, dt, h, stream=None):
+    _check("moe_expert_up", _lib.moe_expert_up(
+        _ptr(x), _ptr(perm), _ptr(offsets), T, d, d_ff, E, k, _ptr(w1), _ptr(w3), dt, _ptr(h),
+        _stream(stream)))
+
+
+def expert_down(h, offsets, T, d, d_ff, E, k, w2, dt, out, stream=None):
+    _check("moe_expert_down", _lib.moe_expert_down(
+        _ptr(h), _ptr(offsets), T, d, d_ff, E, k, _ptr(w2), dt, _ptr(out), _stream(stream)))
 
 
 def combine(expert_out, inv, topk_gate, T, d, k, dt, shared_out, y, stream=None):

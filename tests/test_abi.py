@@ -28,7 +28,8 @@ def _declared():
 def test_every_declared_symbol_is_exported(lm):
     names = _declared()
     assert set(names) == {"moe_workspace_bytes", "moe_status_str", "moe_route", "moe_dispatch",
-                          "moe_expert_ffn", "moe_combine", "moe_aux_loss"}
+                          "moe_expert_ffn", "moe_expert_up", "moe_expert_down", "moe_combine",
+                          "moe_aux_loss"}
     lib = ctypes.CDLL(lm.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
