@@ -6,13 +6,15 @@
 // Tiling: a 256-thread block (4 waves, WGM x WGN) computes a BM x BN tile of C (for NMAT = 2 two
 // B matrices share the tile: w1 and w3 of the SwiGLU expert, and the epilogue forms
 // silu(x.w1) * (x.w3) in registers, so the gate and up products never leave the chip).  K is walked
-// in steps of 64 through LDS:
+// in steps of 64 through a double-buffered LDS:
 //   A (activation rows, K contiguous) is gathered row by row (token of each assignment) with
 //     16-byte loads and stored as [BM][64+8] bf16;
 //   B (weights [K][N], N contiguous) is loaded as 8x8 bf16 blocks (eight 16-byte rows), transposed
 //     in registers and stored K-contiguous as [BN][64+8], so both MFMA operands are read from LDS
 //     with one 16-byte read per lane.
-// The next K step is fetched into registers while the current one is multiplied.
+// Pipeline, one barrier per K step: at the top of step kt the registers hold tile kt+1 (loaded one
+// step earlier); they are written to the idle LDS buffer, the loads of tile kt+2 are issued, and the
+// MFMAs run on tile kt from the other buffer.
 #include "common.h"
 #include "gemm_common.h"
 #include "kernels.h"
@@ -37,67 +39,83 @@ __device__ __forceinline__ void transpose8x8(const u32x4 (&in)[8], u32x4 (&out)[
   }
 }
 
-template <int BM, int BN, int NMAT, int WGM, int WGN, int EPI>
+template <int BM, int BN, int NMAT>
+constexpr size_t gemm_stage_elems() {
+  return (size_t)(BM + NMAT * BN) * kLDK;
+}
+
+template <int BM, int BN, int NMAT, int WGM, int WGN, int EPI, bool KFULL>
 __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(const GemmParams p) {
   constexpr int WM = BM / WGM, WN = BN / WGN;
   constexpr int TM = WM / 32, TN = WN / 32;
   constexpr int A_CHUNKS = BM * (kBK / 8) / 256;             // 16-byte A chunks per thread
   constexpr int B_BLOCKS = NMAT * (kBK / 8) * (BN / 8) / 256;  // 8x8 B blocks per thread
+  constexpr int STAGE = (int)gemm_stage_elems<BM, BN, NMAT>();
   static_assert(WGM * WGN == 4, "4 waves");
+  static_assert(BN % 64 == 0, "the B matrix of a wave's blocks must be uniform");
   static_assert(A_CHUNKS >= 1 && B_BLOCKS >= 1, "tile too small for 256 threads");
   static_assert(BM * (kBK / 8) % 256 == 0 && NMAT * (kBK / 8) * (BN / 8) % 256 == 0, "tiling");
 
   extern __shared__ __align__(16) uint16_t smem[];
-  uint16_t* As = smem;
-  uint16_t* Bs = smem + BM * kLDK;
 
   const int NT = (p.N + BN - 1) / BN;
   TileCoord tc;
   if (!find_tile<BM>(p, NT, blockIdx.x, tc)) return;
+  tc.g = __builtin_amdgcn_readfirstlane(tc.g);
+  tc.row0 = __builtin_amdgcn_readfirstlane(tc.row0);
+  tc.row_end = __builtin_amdgcn_readfirstlane(tc.row_end);
+  tc.n_tile = __builtin_amdgcn_readfirstlane(tc.n_tile);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm0 = (wave % WGM) * WM;
   const int wn0 = (wave / WGM) * WN;
   const int n_base = tc.n_tile * BN;
   const int K = p.K, N = p.N;
 
-  const uint16_t* Ab = (const uint16_t*)p.A;
-  const uint16_t* B0 = (const uint16_t*)p.B0 + (size_t)tc.g * p.b_gstride;
-  const uint16_t* B1 = NMAT == 2 ? (const uint16_t*)p.B1 + (size_t)tc.g * p.b_gstride : nullptr;
+  // Buffer descriptors: 32-bit offsets, and loads past the end of a matrix return zeros.
+  const __amdgpu_buffer_rsrc_t rA =
+      __builtin_amdgcn_make_buffer_rsrc((void*)p.A, (short)0, p.a_rows * K * 2, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rB0 = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)((const uint16_t*)p.B0 + (size_t)tc.g * p.b_gstride), (short)0, K * N * 2, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rB1 =
+      NMAT == 2 ? __builtin_amdgcn_make_buffer_rsrc(
+                      (void*)((const uint16_t*)p.B1 + (size_t)tc.g * p.b_gstride), (short)0,
+                      K * N * 2, 0x00020000)
+                : rB0;
 
-  // A rows handled by this thread (fixed for the whole K loop).
-  const uint16_t* a_src[A_CHUNKS];
+  // A rows handled by this thread (fixed for the whole K loop).  Rows past the group's end load a
+  // valid row of the group instead; they only feed accumulator rows that are never stored.
+  uint32_t a_off[A_CHUNKS];
   int a_kc[A_CHUNKS];
-  bool a_ok[A_CHUNKS];
 #pragma unroll
   for (int i = 0; i < A_CHUNKS; ++i) {
     const int c = tid + 256 * i;
     const int row = c >> 3;
     a_kc[i] = (c & 7) * 8;
-    const int grow = tc.row0 + row;
-    a_ok[i] = grow < tc.row_end;
-    int src = grow;
-    if (a_ok[i] && p.gather) src = p.gather[grow] / p.gather_div;
-    a_src[i] = Ab + (size_t)(a_ok[i] ? src : 0) * K;
+    const int grow = min(tc.row0 + row, tc.row_end - 1);
+    const int src = p.gather ? p.gather[grow] / p.gather_div : grow;
+    a_off[i] = (uint32_t)(src * K + a_kc[i]) * 2u;
   }
-  // B blocks handled by this thread.
-  const uint16_t* b_src[B_BLOCKS];
-  int b_kb[B_BLOCKS], b_lds[B_BLOCKS];
-  bool b_ok[B_BLOCKS];
+  // B blocks handled by this thread: rows kb*8..kb*8+7 of the K step, columns col..col+7.
+  // Columns past N read the next row's values (or zeros past the end); they only feed output
+  // columns that are never stored.
+  uint32_t b_off[B_BLOCKS];
+  int b_kb[B_BLOCKS], b_lds[B_BLOCKS], b_mat[B_BLOCKS];
 #pragma unroll
   for (int i = 0; i < B_BLOCKS; ++i) {
-    const int b = tid + 256 * i;
-    const int mat = b / (8 * (BN / 8));
-    const int rem = b % (8 * (BN / 8));
+    // 8 * (BN / 8) = BN blocks per matrix; BN % 64 == 0 keeps the matrix index wave-uniform.
+    const int mat = (wave * 64 + 256 * i) / BN;
+    const int rem = (tid + 256 * i) % BN;
     const int kb = rem & 7, nb = rem >> 3;
     const int col = n_base + nb * 8;
-    b_ok[i] = col < N;
+    b_mat[i] = mat;
     b_kb[i] = kb * 8;
-    b_src[i] = (mat == 0 ? B0 : B1) + (b_ok[i] ? col : 0);
-    b_lds[i] = (mat * BN + nb * 8) * kLDK + kb * 8;
+    b_off[i] = (uint32_t)(kb * 8 * N + col) * 2u;
+    b_lds[i] = BM * kLDK + (mat * BN + nb * 8) * kLDK + kb * 8;
   }
+  const uint32_t row_bytes = (uint32_t)N * 2u;
 
   u32x4 a_reg[A_CHUNKS];
   u32x4 b_reg[B_BLOCKS][8];
@@ -106,32 +124,36 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(const GemmParams p) {
   auto load_tile = [&](int k0) {
 #pragma unroll
     for (int i = 0; i < A_CHUNKS; ++i) {
-      const int k = k0 + a_kc[i];
-      a_reg[i] = (a_ok[i] && k < K) ? *reinterpret_cast<const u32x4*>(a_src[i] + k) : zero;
+      if (KFULL || k0 + a_kc[i] < K)
+        a_reg[i] = __builtin_amdgcn_raw_buffer_load_b128(rA, a_off[i] + (uint32_t)k0 * 2u, 0, 0);
+      else
+        a_reg[i] = zero;
     }
 #pragma unroll
     for (int i = 0; i < B_BLOCKS; ++i) {
+      const uint32_t base = b_off[i] + (uint32_t)k0 * row_bytes;
 #pragma unroll
       for (int r = 0; r < 8; ++r) {
-        const int k = k0 + b_kb[i] + r;
-        b_reg[i][r] = (b_ok[i] && k < K)
-                          ? *reinterpret_cast<const u32x4*>(b_src[i] + (size_t)k * N)
-                          : zero;
+        if (KFULL || k0 + b_kb[i] + r < K)
+          b_reg[i][r] = __builtin_amdgcn_raw_buffer_load_b128(b_mat[i] == 0 ? rB0 : rB1,
+                                                              base + r * row_bytes, 0, 0);
+        else
+          b_reg[i][r] = zero;
       }
     }
   };
-  auto store_tile = [&]() {
+  auto store_tile = [&](uint16_t* buf) {
 #pragma unroll
     for (int i = 0; i < A_CHUNKS; ++i) {
       const int c = tid + 256 * i;
-      *reinterpret_cast<u32x4*>(As + (c >> 3) * kLDK + a_kc[i]) = a_reg[i];
+      *reinterpret_cast<u32x4*>(buf + (c >> 3) * kLDK + a_kc[i]) = a_reg[i];
     }
 #pragma unroll
     for (int i = 0; i < B_BLOCKS; ++i) {
       u32x4 t[8];
       transpose8x8(b_reg[i], t);
 #pragma unroll
-      for (int n = 0; n < 8; ++n) *reinterpret_cast<u32x4*>(Bs + b_lds[i] + n * kLDK) = t[n];
+      for (int n = 0; n < 8; ++n) *reinterpret_cast<u32x4*>(buf + b_lds[i] + n * kLDK) = t[n];
     }
   };
 
@@ -145,14 +167,26 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(const GemmParams p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[m][i][j][r] = 0.f;
 
+  // Number of this wave's 32-row sub-tiles that hold at least one row of the group.
+  const int rows_left = tc.row_end - (tc.row0 + wm0);
+  const int tm_live = __builtin_amdgcn_readfirstlane(
+      rows_left <= 0 ? 0 : (rows_left >= WM ? TM : (rows_left + 31) / 32));
+
   const int KT = (K + kBK - 1) / kBK;
   load_tile(0);
-  store_tile();
+  store_tile(smem);
+  if (KT > 1) load_tile(kBK);
   __syncthreads();
   const int lrow = lane & 31;
   const int lk = (lane >> 5) * 8;
   for (int kt = 0; kt < KT; ++kt) {
-    if (kt + 1 < KT) load_tile((kt + 1) * kBK);
+    const uint16_t* cur = smem + (kt & 1) * STAGE;
+    if (kt + 1 < KT) {
+      store_tile(smem + ((kt + 1) & 1) * STAGE);
+      if (kt + 2 < KT) load_tile((kt + 2) * kBK);
+    }
+    const uint16_t* As = cur;
+    const uint16_t* Bs = cur + BM * kLDK;
 #pragma unroll
     for (int ks = 0; ks < kBK / 16; ++ks) {
       bf16x8 af[TM];
@@ -167,25 +201,23 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(const GemmParams p) {
           bfr[m][j] = *reinterpret_cast<const bf16x8*>(
               Bs + (m * BN + wn0 + j * 32 + lrow) * kLDK + ks * 16 + lk);
 #pragma unroll
-      for (int m = 0; m < NMAT; ++m)
+      for (int i = 0; i < TM; ++i) {
 #pragma unroll
-        for (int i = 0; i < TM; ++i)
+        for (int m = 0; m < NMAT; ++m)
 #pragma unroll
           for (int j = 0; j < TN; ++j)
-            acc[m][i][j] =
-                __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[m][j], acc[m][i][j], 0, 0, 0);
+            acc[m][i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[m][j],
+                                                                   acc[m][i][j], 0, 0, 0);
+      }
     }
     __syncthreads();
-    if (kt + 1 < KT) {
-      store_tile();
-      __syncthreads();
-    }
   }
 
   // Epilogue.  Accumulator register r of a 32x32 tile holds row 8*(r/4) + 4*(lane/32) + r%4 and
   // column lane%32.
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
+    if (i >= tm_live) continue;
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
       const int col = n_base + wn0 + j * 32 + (lane & 31);
@@ -210,10 +242,10 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(const GemmParams p) {
   }
 }
 
-template <int BM, int BN, int NMAT, int WGM, int WGN, int EPI>
-static hipError_t launch_gemm_bf16_t(const GemmParams& p, int rows_max, hipStream_t s) {
-  auto kern = gemm_bf16_kernel<BM, BN, NMAT, WGM, WGN, EPI>;
-  const size_t lds = (size_t)(BM + NMAT * BN) * kLDK * sizeof(uint16_t);
+template <int BM, int BN, int NMAT, int WGM, int WGN, int EPI, bool KFULL>
+static hipError_t launch_gemm_bf16_k(const GemmParams& p, int rows_max, hipStream_t s) {
+  auto kern = gemm_bf16_kernel<BM, BN, NMAT, WGM, WGN, EPI, KFULL>;
+  const size_t lds = 2 * gemm_stage_elems<BM, BN, NMAT>() * sizeof(uint16_t);
   static bool attr_set = false;  // the attribute is per function; setting it twice is harmless
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute((const void*)kern,
@@ -228,7 +260,16 @@ static hipError_t launch_gemm_bf16_t(const GemmParams& p, int rows_max, hipStrea
   return hipGetLastError();
 }
 
+template <int BM, int BN, int NMAT, int WGM, int WGN, int EPI>
+static hipError_t launch_gemm_bf16_t(const GemmParams& p, int rows_max, hipStream_t s) {
+  if (p.K % kBK == 0) return launch_gemm_bf16_k<BM, BN, NMAT, WGM, WGN, EPI, true>(p, rows_max, s);
+  return launch_gemm_bf16_k<BM, BN, NMAT, WGM, WGN, EPI, false>(p, rows_max, s);
+}
+
 hipError_t launch_gemm_bf16(const GemmParams& p, int rows_max, int epi, hipStream_t s) {
+  // K a multiple of 64: the direct-to-LDS kernel (gemm_bf16_lds.hip); else the general one below.
+  const hipError_t e = launch_gemm_bf16_lds(p, rows_max, epi, s);
+  if (e != hipErrorNotSupported) return e;
   switch (epi) {
     case EPI_SWIGLU:
       return launch_gemm_bf16_t<256, 128, 2, 2, 2, EPI_SWIGLU>(p, rows_max, s);

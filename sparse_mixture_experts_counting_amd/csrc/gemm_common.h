@@ -13,7 +13,8 @@
 namespace moe {
 
 struct GemmParams {
-  const void* A;            // [rows][K], element type of the kernel
+  const void* A;            // [a_rows][K], element type of the kernel
+  int a_rows;               // rows of A (bounds of the gathered reads)
   const int32_t* gather;    // NULL: A row r; else A row gather[r] / gather_div
   int gather_div;
   const int32_t* offsets;   // [G+1] on the device, or NULL for one group of M rows

@@ -89,6 +89,7 @@ moe_status moe_route(const void* x, const void* w_r, const float* logit_bias, in
     } else if (E % 8 == 0) {
       moe::GemmParams p{};
       p.A = x;
+      p.a_rows = T;
       p.M = T;
       p.N = E;
       p.K = d;
@@ -153,6 +154,7 @@ static hipError_t run_up(const void* x, const int32_t* perm, const int32_t* offs
                          hipStream_t s) {
   moe::GemmParams up{};
   up.A = x;
+  up.a_rows = T;
   up.gather = perm;
   up.gather_div = k;
   up.offsets = perm ? offsets : nullptr;
@@ -174,6 +176,7 @@ static hipError_t run_down(const void* h, const int32_t* offsets, int T, int d, 
                            int k, const void* w2, bool bf16, void* out, hipStream_t s) {
   moe::GemmParams dn{};
   dn.A = h;
+  dn.a_rows = offsets ? T * k : T;
   dn.gather_div = 1;
   dn.offsets = offsets;
   dn.G = offsets ? E : 1;

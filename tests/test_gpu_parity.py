@@ -194,6 +194,12 @@ SWEEP = [
     (700, 72, 3, 1, 48, "fp32", "softmax_all", 200, 0, 0.0),
     (513, 328, 16, 2, 296, "bf16", "softmax_topk", 0, 1, 0.0),
     (200, 16, 256, 8, 24, "bf16", "sigmoid_topk", 0, 1, 1.1),
+    # K a multiple of 64: the direct-to-LDS matrix-core kernel (N below, at and above one tile)
+    (300, 128, 8, 2, 192, "bf16", "softmax_topk", 0, 0, 0.0),
+    (257, 64, 5, 2, 64, "bf16", "softmax_all", 90, 0, 0.0),
+    (300, 128, 256, 8, 64, "bf16", "sigmoid_topk", 0, 1, 1.1),
+    (600, 256, 8, 2, 640, "bf16", "softmax_topk", 0, 1, 0.0),
+    (1030, 192, 4, 1, 384, "bf16", "softmax_topk", 0, 0, 0.0),
 ]
 
 
