@@ -54,8 +54,8 @@ __device__ __forceinline__ void barrier_no_fence() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-template <int BM, int BN, int NMAT, int BK, int STAGES, int EPI>
-__global__ __launch_bounds__(256, 1) void gemm_bf16_lds_kernel(const GemmParams p) {
+template <int BM, int BN, int NMAT, int BK, int STAGES, int MINB, int EPI>
+__global__ __launch_bounds__(256, MINB) void gemm_bf16_lds_kernel(const GemmParams p) {
   constexpr int WM = BM / 2, WN = BN / 2;          // 2 x 2 waves
   constexpr int TM = WM / 32, TN = WN / 32;
   constexpr int KS = BK / 16;                      // 16-wide k slices per step
@@ -292,9 +292,9 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_lds_kernel(const GemmParams 
   }
 }
 
-template <int BM, int BN, int NMAT, int BK, int STAGES, int EPI>
+template <int BM, int BN, int NMAT, int BK, int STAGES, int MINB, int EPI>
 static hipError_t launch_lds_t(const GemmParams& p, int rows_max, hipStream_t s) {
-  auto kern = gemm_bf16_lds_kernel<BM, BN, NMAT, BK, STAGES, EPI>;
+  auto kern = gemm_bf16_lds_kernel<BM, BN, NMAT, BK, STAGES, MINB, EPI>;
   const size_t lds = (size_t)STAGES * lds_stage_bytes<BM, BN, NMAT, BK>();
   static bool attr_set = false;
   if (!attr_set) {
@@ -316,11 +316,11 @@ hipError_t launch_gemm_bf16_lds(const GemmParams& p, int rows_max, int epi, hipS
   if (p.K % 64 != 0 || p.N < 8) return hipErrorNotSupported;
   switch (epi) {
     case EPI_SWIGLU:
-      return launch_lds_t<256, 128, 2, 32, 2, EPI_SWIGLU>(p, rows_max, s);
+      return launch_lds_t<128, 128, 2, 32, 2, 2, EPI_SWIGLU>(p, rows_max, s);
     case EPI_STORE:
-      return launch_lds_t<256, 256, 1, 32, 2, EPI_STORE>(p, rows_max, s);
+      return launch_lds_t<128, 256, 1, 32, 2, 2, EPI_STORE>(p, rows_max, s);
     default:
-      return launch_lds_t<128, 256, 1, 32, 2, EPI_STORE_F32_BIAS>(p, rows_max, s);
+      return launch_lds_t<128, 256, 1, 32, 2, 1, EPI_STORE_F32_BIAS>(p, rows_max, s);
   }
 }
 
