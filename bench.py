@@ -118,7 +118,9 @@ def main():
     buf = layer.alloc_buffers(cfg, dev)
     code = lm.MOE_F32 if cfg.dtype == "fp32" else lm.MOE_BF16
     stream = torch.cuda.current_stream(dev)
-    h = buf.workspace   # h lives in the workspace between the two expert GEMMs
+    # h between the two expert GEMMs (the workspace holds their split-K scratch, if any)
+    h = torch.empty((cfg.T * cfg.k, cfg.d_ff), dtype=synth.torch_dtype(cfg), device=dev)
+    ws = buf.workspace
 
     stages = ["route", "dispatch", "expert_up", "expert_down", "shared_up", "shared_down",
               "combine", "aux_loss"]
@@ -135,17 +137,17 @@ def main():
         layer.dispatch(cfg, buf)
         mark(2)
         lm.expert_up(inp.x, buf.perm, buf.offsets, cfg.T, cfg.d, cfg.d_ff, cfg.E, cfg.k, inp.w1,
-                     inp.w3, code, h)
+                     inp.w3, code, h, ws)
         mark(3)
         lm.expert_down(h, buf.offsets, cfg.T, cfg.d, cfg.d_ff, cfg.E, cfg.k, inp.w2, code,
-                       buf.expert_out)
+                       buf.expert_out, ws)
         mark(4)
         i = 4
         if cfg.n_shared:
             w1s, w3s, w2s = inp.shared
-            lm.expert_up(inp.x, None, None, cfg.T, cfg.d, cfg.d_ff, 1, 1, w1s, w3s, code, h)
+            lm.expert_up(inp.x, None, None, cfg.T, cfg.d, cfg.d_ff, 1, 1, w1s, w3s, code, h, ws)
             mark(5)
-            lm.expert_down(h, None, cfg.T, cfg.d, cfg.d_ff, 1, 1, w2s, code, buf.shared_out)
+            lm.expert_down(h, None, cfg.T, cfg.d, cfg.d_ff, 1, 1, w2s, code, buf.shared_out, ws)
             mark(6)
             i = 6
         layer.combine(cfg, buf)

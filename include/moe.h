@@ -126,7 +126,9 @@ moe_status moe_dispatch(const int32_t* topk_idx, int T, int E, int k, int capaci
  *
  * x [T,d]; w1, w3 [E][d][d_ff]; w2 [E][d_ff][d]; out [T*k][d] (routed) or [T][d] (perm NULL); all in
  * dtype `dt`.  h is kept in the workspace in dtype `dt` (bf16 layers round h to bf16 before the
- * down projection; accumulation is fp32).
+ * down projection; accumulation is fp32).  For few rows per expert the K dimension is split over
+ * several blocks whose fp32 partial sums (also in the workspace) are added in a fixed order, so
+ * results are deterministic.
  */
 moe_status moe_expert_ffn(const void* x, const int32_t* perm, const int32_t* offsets, int T, int d,
                           int d_ff, int E, int k, const void* w1, const void* w3, const void* w2,
@@ -141,13 +143,16 @@ moe_status moe_expert_ffn(const void* x, const int32_t* perm, const int32_t* off
  *
  * Same row convention as moe_expert_ffn (rows r < offsets[E], t = perm[r] / k); with perm == NULL
  * (up) or offsets == NULL (down) the call is one dense group over T rows and E must be 1.  h must
- * hold T*k rows (routed) or T rows (dense).  Same errors as moe_expert_ffn (no workspace).
+ * hold T*k rows (routed) or T rows (dense).  The workspace (sized by moe_workspace_bytes) holds
+ * split-K partial sums when few rows leave the GPU under-filled (decode-sized batches); the
+ * result does not depend on the split.  Same errors as moe_expert_ffn.
  */
 moe_status moe_expert_up(const void* x, const int32_t* perm, const int32_t* offsets, int T, int d,
                          int d_ff, int E, int k, const void* w1, const void* w3, moe_dtype dt,
-                         void* h, void* stream);
+                         void* h, void* workspace, size_t ws_bytes, void* stream);
 moe_status moe_expert_down(const void* h, const int32_t* offsets, int T, int d, int d_ff, int E,
-                           int k, const void* w2, moe_dtype dt, void* out, void* stream);
+                           int k, const void* w2, moe_dtype dt, void* out, void* workspace,
+                           size_t ws_bytes, void* stream);
 
 /*
  * moe_combine -- Combine (the tirogla page, How it works step 5 and Code `combine`):

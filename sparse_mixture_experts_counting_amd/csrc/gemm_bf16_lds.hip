@@ -25,6 +25,7 @@
 #include "gemm_common.h"
 #include "kernels.h"
 
+#include <algorithm>
 #include <type_traits>
 
 namespace moe {
@@ -77,7 +78,9 @@ __global__ __launch_bounds__(256, MINB) void gemm_bf16_lds_kernel(const GemmPara
 
   const int NT = (p.N + BN - 1) / BN;
   TileCoord tc;
-  if (!find_tile<BM>(p, NT, blockIdx.x, tc)) return;
+  // Split-K: consecutive blocks take the K chunks of one tile.
+  const int kc = blockIdx.x % p.ksplit;
+  if (!find_tile<BM>(p, NT, blockIdx.x / p.ksplit, tc)) return;
   tc.g = __builtin_amdgcn_readfirstlane(tc.g);
   tc.row0 = __builtin_amdgcn_readfirstlane(tc.row0);
   tc.row_end = __builtin_amdgcn_readfirstlane(tc.row_end);
@@ -225,13 +228,15 @@ __global__ __launch_bounds__(256, MINB) void gemm_bf16_lds_kernel(const GemmPara
   // The loop body is branch-free (branches inside it make the register allocator move the
   // accumulators between register files): prefetches past the last K step re-read the last step
   // (in bounds, never used), and KT is even so the two-step unroll is exact.
-  const int KT = K / BK;
-  const int k_last = (KT - 1) * BK;
+  const int Kc = K / p.ksplit;                        // this block's K chunk
+  const int kbeg = kc * Kc;
+  const int KT = Kc / BK;
+  const int k_last = kbeg + (KT - 1) * BK;
   // Prologue: step 0 into LDS stage 0, steps 1 and 2 in the registers.
-  load_regs(0, 0);
-  load_regs(1, min(BK, k_last));
+  load_regs(0, kbeg);
+  load_regs(1, min(kbeg + BK, k_last));
   store_regs(0, 0);
-  load_regs(0, min(2 * BK, k_last));
+  load_regs(0, min(kbeg + 2 * BK, k_last));
   __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
   barrier_no_fence();
   read_frags(0, 0, 0);
@@ -242,7 +247,7 @@ __global__ __launch_bounds__(256, MINB) void gemm_bf16_lds_kernel(const GemmPara
     constexpr int nx = R() == 1 ? STAGE : 0;
     // Step kt+1 (register set R) into the idle stage, then refill that set with step kt+3.
     store_regs(R(), nx);
-    load_regs(R(), min((kt + 3) * BK, k_last));
+    load_regs(R(), min(kbeg + (kt + 3) * BK, k_last));
 #pragma unroll
     for (int ks = 0; ks < KS - 1; ++ks) {
       read_frags(st, ks + 1, (ks + 1) & 1);
@@ -276,7 +281,11 @@ __global__ __launch_bounds__(256, MINB) void gemm_bf16_lds_kernel(const GemmPara
       for (int r = 0; r < 16; ++r) {
         const int row = tc.row0 + wm0 + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
         if (row >= tc.row_end) continue;
-        if constexpr (EPI == EPI_SWIGLU) {
+        if (p.ksplit > 1) {   // fp32 partial sums; splitk_finish_kernel applies the epilogue
+#pragma unroll
+          for (int m = 0; m < NMAT; ++m)
+            p.part[((size_t)(kc * NMAT + m) * p.part_rows + row) * N + col] = acc[m][i][j][r];
+        } else if constexpr (EPI == EPI_SWIGLU) {
           const float g = acc[0][i][j][r];
           const float u = acc[NMAT - 1][i][j][r];
           const float hv = g / (1.0f + expf(-g)) * u;
@@ -292,6 +301,49 @@ __global__ __launch_bounds__(256, MINB) void gemm_bf16_lds_kernel(const GemmPara
   }
 }
 
+// Sum the K-chunk partials of every valid row in a fixed order and apply the epilogue.
+// Rows past the valid count (offsets[G], or M for a single group) are untouched.
+template <int NMAT, int EPI>
+__global__ __launch_bounds__(256) void splitk_finish_kernel(const GemmParams p) {
+  const int rows = p.offsets ? p.offsets[p.G] : p.M;
+  const int nv = p.N / 8;                              // 8 columns per thread
+  const size_t total = (size_t)rows * nv;
+  for (size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x; idx < total;
+       idx += (size_t)gridDim.x * 256) {
+    const int row = (int)(idx / nv), c0 = (int)(idx % nv) * 8;
+    float s[NMAT][8];
+#pragma unroll
+    for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+      for (int q = 0; q < 8; ++q) s[m][q] = 0.f;
+    for (int kc = 0; kc < p.ksplit; ++kc) {
+#pragma unroll
+      for (int m = 0; m < NMAT; ++m) {
+        const f32x4* src = reinterpret_cast<const f32x4*>(
+            p.part + ((size_t)(kc * NMAT + m) * p.part_rows + row) * p.N + c0);
+        const f32x4 a = src[0], b = src[1];
+        s[m][0] += a[0]; s[m][1] += a[1]; s[m][2] += a[2]; s[m][3] += a[3];
+        s[m][4] += b[0]; s[m][5] += b[1]; s[m][6] += b[2]; s[m][7] += b[3];
+      }
+    }
+    u32x4 o;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      float v0, v1;
+      if constexpr (EPI == EPI_SWIGLU) {
+        const float g0 = s[0][2 * q], g1 = s[0][2 * q + 1];
+        v0 = g0 / (1.0f + expf(-g0)) * s[NMAT - 1][2 * q];
+        v1 = g1 / (1.0f + expf(-g1)) * s[NMAT - 1][2 * q + 1];
+      } else {
+        v0 = s[0][2 * q];
+        v1 = s[0][2 * q + 1];
+      }
+      o[q] = pack_bf16x2(v0, v1);
+    }
+    *reinterpret_cast<u32x4*>((uint16_t*)p.C + (size_t)row * p.ldc + c0) = o;
+  }
+}
+
 template <int BM, int BN, int NMAT, int BK, int STAGES, int MINB, int EPI>
 static hipError_t launch_lds_t(const GemmParams& p, int rows_max, hipStream_t s) {
   auto kern = gemm_bf16_lds_kernel<BM, BN, NMAT, BK, STAGES, MINB, EPI>;
@@ -304,16 +356,44 @@ static hipError_t launch_lds_t(const GemmParams& p, int rows_max, hipStream_t s)
     attr_set = true;
   }
   const int NT = (p.N + BN - 1) / BN;
-  const int grid = tiles_upper_bound(rows_max, p.G, p.offsets != nullptr, BM, NT);
+  const int grid = tiles_upper_bound(rows_max, p.G, p.offsets != nullptr, BM, NT) * p.ksplit;
   if (grid <= 0) return hipSuccess;
   hipLaunchKernelGGL(kern, dim3(grid), dim3(256), lds, s, p);
+  if (p.ksplit > 1) {
+    const size_t items = (size_t)rows_max * (p.N / 8);
+    const int fgrid = (int)std::min<size_t>((items + 255) / 256, 4096);
+    hipLaunchKernelGGL((splitk_finish_kernel<NMAT, EPI>), dim3(fgrid), dim3(256), 0, s, p);
+  }
   return hipGetLastError();
+}
+
+// K chunks for the expert GEMMs: when the tile grid would leave CUs idle (few rows, e.g. decode),
+// split K so that about 1024 blocks run, keeping every chunk a whole number of 64-deep steps.
+static int splitk_factor(int rows_max, int G, bool grouped, int N, int K, int epi) {
+  if (epi == EPI_STORE_F32_BIAS || K % 64 != 0) return 1;
+  const int BM = 128, BN = (epi == EPI_SWIGLU) ? 128 : 256;
+  const int mt = grouped ? std::min(G, rows_max) + rows_max / BM : (rows_max + BM - 1) / BM;
+  const long long tiles = (long long)mt * ((N + BN - 1) / BN);
+  int ks = 1;
+  while (ks < 16 && tiles * ks * 2 <= 1024 && (K / 64) % (ks * 2) == 0) ks *= 2;
+  return ks;
+}
+
+size_t gemm_bf16_partial_bytes(int rows_max, int G, bool grouped, int N, int K, int epi) {
+  const int ks = splitk_factor(rows_max, G, grouped, N, K, epi);
+  if (ks == 1) return 0;
+  const int nmat = epi == EPI_SWIGLU ? 2 : 1;
+  return (size_t)ks * nmat * rows_max * N * sizeof(float);
 }
 
 // Returns hipErrorNotSupported when the shape needs the general kernel (K not a multiple of 64:
 // an even number of 32-deep steps).
-hipError_t launch_gemm_bf16_lds(const GemmParams& p, int rows_max, int epi, hipStream_t s) {
-  if (p.K % 64 != 0 || p.N < 8) return hipErrorNotSupported;
+hipError_t launch_gemm_bf16_lds(const GemmParams& p_in, int rows_max, int epi, hipStream_t s) {
+  if (p_in.K % 64 != 0 || p_in.N < 8) return hipErrorNotSupported;
+  GemmParams p = p_in;
+  p.ksplit = splitk_factor(rows_max, p.G, p.offsets != nullptr, p.N, p.K, epi);
+  p.part_rows = rows_max;
+  if (p.ksplit > 1 && p.part == nullptr) p.ksplit = 1;   // no scratch given: no split
   switch (epi) {
     case EPI_SWIGLU:
       return launch_lds_t<128, 128, 2, 32, 2, 2, EPI_SWIGLU>(p, rows_max, s);

@@ -27,6 +27,9 @@ struct GemmParams {
   void* C;                  // output rows, [rows][ldc]
   int ldc;
   const float* bias;        // fp32 [N] added by the fp32 epilogue, or NULL
+  float* part;              // split-K scratch: [ksplit][NMAT][part_rows][N] fp32, or NULL
+  int ksplit;               // K chunks (set by the launcher; 1 = no split)
+  int part_rows;
 };
 
 enum { EPI_SWIGLU = 0, EPI_STORE = 1, EPI_STORE_F32_BIAS = 2 };

@@ -28,8 +28,22 @@ moe_status launched(hipError_t e = hipSuccess) {
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_DEVICE;
 }
 
-size_t ffn_workspace_bytes(int rows, int d_ff, moe_dtype dt) {
+// Split-K scratch of the two expert GEMMs (bf16 matrix-core path only; they run one after the
+// other, so one region serves both).
+size_t ffn_partial_bytes(int rows, bool grouped, int G, int d, int d_ff, moe_dtype dt) {
+  if (dt != MOE_BF16) return 0;
+  const size_t up = moe::gemm_bf16_partial_bytes(rows, G, grouped, d_ff, d, moe::EPI_SWIGLU);
+  const size_t dn = moe::gemm_bf16_partial_bytes(rows, G, grouped, d, d_ff, moe::EPI_STORE);
+  return align_up(up > dn ? up : dn);
+}
+
+size_t h_bytes(int rows, int d_ff, moe_dtype dt) {
   return align_up((size_t)rows * d_ff * elem_bytes(dt));
+}
+
+// moe_expert_ffn workspace: h, then the split-K scratch.
+size_t ffn_workspace_bytes(int rows, bool grouped, int G, int d, int d_ff, moe_dtype dt) {
+  return h_bytes(rows, d_ff, dt) + ffn_partial_bytes(rows, grouped, G, d, d_ff, dt);
 }
 
 }  // namespace
@@ -51,7 +65,9 @@ size_t moe_workspace_bytes(int T, int d, int d_ff, int E, int k, moe_dtype dt) {
   if (T < 1 || E < 1 || k < 1 || d_ff < 1 || d < 1) return 0;
   size_t r = align_up(moe::route_workspace_bytes(T, E));
   size_t q = align_up(moe::dispatch_workspace_bytes(T * k, E));
-  size_t f = ffn_workspace_bytes(T * k, d_ff, dt);
+  size_t f = ffn_workspace_bytes(T * k, true, E, d, d_ff, dt);
+  const size_t fs = ffn_workspace_bytes(T, false, 1, d, d_ff, dt);   // shared / dense expert
+  f = f > fs ? f : fs;
   size_t m = r > q ? r : q;
   return m > f ? m : f;
 }
@@ -151,7 +167,7 @@ static moe_status check_ffn_args(const void* x, const void* wa, const void* wb, 
 
 static hipError_t run_up(const void* x, const int32_t* perm, const int32_t* offsets, int T, int d,
                          int d_ff, int E, int k, const void* w1, const void* w3, bool bf16, void* h,
-                         hipStream_t s) {
+                         void* part, hipStream_t s) {
   moe::GemmParams up{};
   up.A = x;
   up.a_rows = T;
@@ -167,13 +183,14 @@ static hipError_t run_up(const void* x, const int32_t* perm, const int32_t* offs
   up.b_gstride = (long long)d * d_ff;
   up.C = h;
   up.ldc = d_ff;
+  up.part = (float*)part;
   const int rows_max = perm ? T * k : T;
   return bf16 ? moe::launch_gemm_bf16(up, rows_max, moe::EPI_SWIGLU, s)
               : moe::launch_gemm_f32(up, rows_max, moe::EPI_SWIGLU, s);
 }
 
 static hipError_t run_down(const void* h, const int32_t* offsets, int T, int d, int d_ff, int E,
-                           int k, const void* w2, bool bf16, void* out, hipStream_t s) {
+                           int k, const void* w2, bool bf16, void* out, void* part, hipStream_t s) {
   moe::GemmParams dn{};
   dn.A = h;
   dn.a_rows = offsets ? T * k : T;
@@ -187,6 +204,7 @@ static hipError_t run_down(const void* h, const int32_t* offsets, int T, int d, 
   dn.b_gstride = (long long)d_ff * d;
   dn.C = out;
   dn.ldc = d;
+  dn.part = (float*)part;
   const int rows_max = offsets ? T * k : T;
   return bf16 ? moe::launch_gemm_bf16(dn, rows_max, moe::EPI_STORE, s)
               : moe::launch_gemm_f32(dn, rows_max, moe::EPI_STORE, s);
@@ -200,32 +218,43 @@ moe_status moe_expert_ffn(const void* x, const int32_t* perm, const int32_t* off
   if (st != MOE_OK) return st;
   if (!w2 || !aligned16(w2) || !workspace || !aligned16(workspace)) return MOE_ERR_ARG;
   const int rows_max = perm ? T * k : T;
-  if (ws_bytes < ffn_workspace_bytes(rows_max, d_ff, dt)) return MOE_ERR_WORKSPACE;
+  const bool grouped = perm != nullptr;
+  if (ws_bytes < ffn_workspace_bytes(rows_max, grouped, E, d, d_ff, dt)) return MOE_ERR_WORKSPACE;
   hipStream_t s = (hipStream_t)stream;
   const bool bf16 = dt == MOE_BF16;
-  hipError_t e = run_up(x, perm, offsets, T, d, d_ff, E, k, w1, w3, bf16, workspace, s);
+  void* part = (char*)workspace + h_bytes(rows_max, d_ff, dt);
+  hipError_t e = run_up(x, perm, offsets, T, d, d_ff, E, k, w1, w3, bf16, workspace, part, s);
   if (e != hipSuccess) return MOE_ERR_DEVICE;
-  e = run_down(workspace, perm ? offsets : nullptr, T, d, d_ff, E, k, w2, bf16, out, s);
+  e = run_down(workspace, perm ? offsets : nullptr, T, d, d_ff, E, k, w2, bf16, out, part, s);
   if (e != hipSuccess) return MOE_ERR_DEVICE;
   return launched();
 }
 
 moe_status moe_expert_up(const void* x, const int32_t* perm, const int32_t* offsets, int T, int d,
                          int d_ff, int E, int k, const void* w1, const void* w3, moe_dtype dt,
-                         void* h, void* stream) {
+                         void* h, void* workspace, size_t ws_bytes, void* stream) {
   moe_status st = check_ffn_args(x, w1, w3, h, perm != nullptr, offsets, T, d, d_ff, E, k, dt);
   if (st != MOE_OK) return st;
+  const int rows_max = perm ? T * k : T;
+  const size_t need = ffn_partial_bytes(rows_max, perm != nullptr, E, d, d_ff, dt);
+  if (need && (!workspace || !aligned16(workspace))) return MOE_ERR_ARG;
+  if (ws_bytes < need) return MOE_ERR_WORKSPACE;
   hipError_t e = run_up(x, perm, offsets, T, d, d_ff, E, k, w1, w3, dt == MOE_BF16, h,
-                        (hipStream_t)stream);
+                        need ? workspace : nullptr, (hipStream_t)stream);
   return e != hipSuccess ? MOE_ERR_DEVICE : launched();
 }
 
 moe_status moe_expert_down(const void* h, const int32_t* offsets, int T, int d, int d_ff, int E,
-                           int k, const void* w2, moe_dtype dt, void* out, void* stream) {
+                           int k, const void* w2, moe_dtype dt, void* out, void* workspace,
+                           size_t ws_bytes, void* stream) {
   moe_status st = check_ffn_args(h, w2, w2, out, offsets != nullptr, offsets, T, d, d_ff, E, k, dt);
   if (st != MOE_OK) return st;
+  const int rows_max = offsets ? T * k : T;
+  const size_t need = ffn_partial_bytes(rows_max, offsets != nullptr, E, d, d_ff, dt);
+  if (need && (!workspace || !aligned16(workspace))) return MOE_ERR_ARG;
+  if (ws_bytes < need) return MOE_ERR_WORKSPACE;
   hipError_t e = run_down(h, offsets, T, d, d_ff, E, k, w2, dt == MOE_BF16, out,
-                          (hipStream_t)stream);
+                          need ? workspace : nullptr, (hipStream_t)stream);
   return e != hipSuccess ? MOE_ERR_DEVICE : launched();
 }
 

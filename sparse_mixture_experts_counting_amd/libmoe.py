@@ -43,8 +43,8 @@ _lib.moe_status_str.restype = ctypes.c_char_p
 _lib.moe_route.argtypes = [_p, _p, _p, _i, _i, _i, _i, _i, _i, _u, _p, _p, _p, _p, _p, _p, _sz, _p]
 _lib.moe_dispatch.argtypes = [_p, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _sz, _p]
 _lib.moe_expert_ffn.argtypes = [_p, _p, _p, _i, _i, _i, _i, _i, _p, _p, _p, _i, _p, _p, _sz, _p]
-_lib.moe_expert_up.argtypes = [_p, _p, _p, _i, _i, _i, _i, _i, _p, _p, _i, _p, _p]
-_lib.moe_expert_down.argtypes = [_p, _p, _i, _i, _i, _i, _i, _p, _i, _p, _p]
+_lib.moe_expert_up.argtypes = [_p, _p, _p, _i, _i, _i, _i, _i, _p, _p, _i, _p, _p, _sz, _p]
+_lib.moe_expert_down.argtypes = [_p, _p, _i, _i, _i, _i, _i, _p, _i, _p, _p, _sz, _p]
 _lib.moe_combine.argtypes = [_p, _p, _p, _i, _i, _i, _i, _p, _p, _p]
 _lib.moe_aux_loss.argtypes = [_p, _p, _p, _i, _i, _i, _f, _f, _p, _p, _p]
 for _n in ("moe_route", "moe_dispatch", "moe_expert_ffn", "moe_expert_up", "moe_expert_down",
@@ -114,15 +114,16 @@ def expert_ffn(x, perm, offsets, T, d, d_ff, E, k, w1, w3, w2, dt, out, workspac
         _ptr(out), _ptr(workspace), _nbytes(workspace), _stream(stream)))
 
 
-def expert_up(x, perm, offsets, T, d, d_ff, E, k, w1, w3, dt, h, stream=None):
+def expert_up(x, perm, offsets, T, d, d_ff, E, k, w1, w3, dt, h, workspace, stream=None):
     _check("moe_expert_up", _lib.moe_expert_up(
         _ptr(x), _ptr(perm), _ptr(offsets), T, d, d_ff, E, k, _ptr(w1), _ptr(w3), dt, _ptr(h),
-        _stream(stream)))
+        _ptr(workspace), _nbytes(workspace), _stream(stream)))
 
 
-def expert_down(h, offsets, T, d, d_ff, E, k, w2, dt, out, stream=None):
+def expert_down(h, offsets, T, d, d_ff, E, k, w2, dt, out, workspace, stream=None):
     _check("moe_expert_down", _lib.moe_expert_down(
-        _ptr(h), _ptr(offsets), T, d, d_ff, E, k, _ptr(w2), dt, _ptr(out), _stream(stream)))
+        _ptr(h), _ptr(offsets), T, d, d_ff, E, k, _ptr(w2), dt, _ptr(out), _ptr(workspace),
+        _nbytes(workspace), _stream(stream)))
 
 
 def combine(expert_out, inv, topk_gate, T, d, k, dt, shared_out, y, stream=None):

@@ -200,6 +200,10 @@ SWEEP = [
     (300, 128, 256, 8, 64, "bf16", "sigmoid_topk", 0, 1, 1.1),
     (600, 256, 8, 2, 640, "bf16", "softmax_topk", 0, 1, 0.0),
     (1030, 192, 4, 1, 384, "bf16", "softmax_topk", 0, 0, 0.0),
+    # few rows per expert: split-K partial sums (routed and dense shared expert)
+    (16, 256, 4, 2, 512, "bf16", "softmax_topk", 0, 1, 0.0),
+    (32, 128, 8, 2, 256, "bf16", "sigmoid_topk", 0, 1, 0.0),
+    (7, 512, 3, 2, 1024, "bf16", "softmax_all", 3, 0, 0.0),
 ]
 
 
