@@ -69,7 +69,7 @@ const char* moe_status_str(moe_status s);
  * moe_route -- Score and Select (the tirogla page, How it works steps 1-2, and its Code `route`;
  * the worked top-2 example of the dineshblog page, section 2).
  *
- *   logits[t,e] = sum_j x[t,j] * w_r[j,e] + logit_bias[e]      (fp32 accumulate)
+ *   logits[t,e] = sum_j x[t,j] * w_r[e,j] + logit_bias[e]      (fp32 accumulate)
  *   topk_idx[t,0..k)  the k largest logits of row t, in descending order; equal logits go to the
  *                     lower expert index first; -0.0 equals +0.0; -inf ranks last.
  *   topk_gate[t,s]    SOFTMAX_TOPK: exp(L_e - m) / sum_sel exp(L_s - m), m = row max
@@ -79,7 +79,8 @@ const char* moe_status_str(moe_status s);
  *                     load-balancing loss, in every gating mode)
  *   lse_sq_sum[0]     sum over tokens of logsumexp(row t)^2 (the z-loss numerator)
  *
- * x [T,d] and w_r [d,E] in dtype `dt`; logit_bias [E] fp32 or NULL; logits [T,E] fp32 (output, or
+ * x [T,d] and w_r [E,d] (the [out][in] weight of the bias-free linear layer that the dineshblog
+ * page, section 1.2, declares as the router) in dtype `dt`; logit_bias [E] fp32 or NULL; logits [T,E] fp32 (output, or
  * input with MOE_ROUTE_LOGITS_IN, in which case x and w_r may be NULL and logit_bias must be
  * NULL); topk_idx [T,k] int32; topk_gate [T,k] fp32; prob_sum [E] fp32; lse_sq_sum [1] fp32.
  * prob_sum and lse_sq_sum may be NULL.  Non-finite logits violate the precondition: routing is then
@@ -116,16 +117,18 @@ moe_status moe_dispatch(const int32_t* topk_idx, int T, int E, int k, int capaci
  * moe_expert_ffn -- Compute (the tirogla page, How it works step 4: every expert runs its FFN on its
  * contiguous batch, as one grouped GEMM).  The expert is SwiGLU (the dineshblog page, section 1.1):
  *
- *   h   = silu(x_t . w1_e) * (x_t . w3_e)      silu(z) = z / (1 + exp(-z))
- *   out[r] = h . w2_e                          for every row r in [offsets[e], offsets[e+1])
+ *   h[n]   = silu(sum_j x[t,j] w1[e][n][j]) * (sum_j x[t,j] w3[e][n][j])   silu(z) = z/(1+exp(-z))
+ *   out[r][i] = sum_n h[n] w2[e][i][n]          for every row r in [offsets[e], offsets[e+1])
  *
  * where token t = perm[r] / k.  Rows are those of moe_dispatch: out is in perm order, and only rows
  * r < offsets[E] are written.  With perm == NULL the call is one dense group over the T tokens
  * (row r = token r; E must be 1 and offsets may be NULL): this is how a shared, always-on expert
  * runs (the starphix page, Expert Architectures: Shared + Specialized).
  *
- * x [T,d]; w1, w3 [E][d][d_ff]; w2 [E][d_ff][d]; out [T*k][d] (routed) or [T][d] (perm NULL); all in
- * dtype `dt`.  h is kept in the workspace in dtype `dt` (bf16 layers round h to bf16 before the
+ * x [T,d]; w1, w3 [E][d_ff][d]; w2 [E][d][d_ff]: each expert's matrices in the [out][in] layout of
+ * the bias-free linear layers that the dineshblog page, section 1.1, declares, so both GEMM
+ * operands are contiguous along the reduced dimension; out [T*k][d] (routed) or [T][d] (perm
+ * NULL); all in dtype `dt`.  d and d_ff must be multiples of 8.  h is kept in the workspace in dtype `dt` (bf16 layers round h to bf16 before the
  * down projection; accumulation is fp32).  For few rows per expert the K dimension is split over
  * several blocks whose fp32 partial sums (also in the workspace) are added in a fixed order, so
  * results are deterministic.

@@ -61,11 +61,12 @@ def _f64(a):
 def router_logits(x, w_r, bias=None):
     """Router scores, [tirogla] How it works step 1 (Score) and [dinesh] 1.2 What the router computes.
 
-    logits[t, e] = sum_j x[t, j] * W_r[j, e] (+ bias[e]); x [T, d], W_r [d, E].  Computed in float64
+    logits[t, e] = sum_j x[t, j] * W_r[e, j] (+ bias[e]); x [T, d], W_r [E, d] (the [out][in]
+    weight of the bias-free linear layer that [dinesh] 1.2 declares as the router).  Computed in float64
     on the given values and rounded once to float32 (logits are always float32: [tirogla]
     Implementation notes ask for float32 router math).
     """
-    L = _f64(x) @ _f64(w_r)
+    L = _f64(x) @ _f64(w_r).T
     if bias is not None:
         L = L + _f64(bias)[None, :]
     return L.astype(np.float32)
@@ -179,12 +180,14 @@ def silu(z):
 
 
 def swiglu_ffn(X, w1, w3, w2):
-    """SwiGLU expert, [dinesh] 1.1 What an "expert" is: w2(silu(x w1) * (x w3)).
+    """SwiGLU expert, [dinesh] 1.1 What an "expert" is: w2(silu(w1(x)) * w3(x)), each w a linear
+    layer without bias, applied as x -> x W^T.
 
-    X [n, d]; w1, w3 [d, d_ff] (w1 is the gate branch, w3 the up branch); w2 [d_ff, d].  float64.
+    X [n, d]; w1, w3 [d_ff, d] (w1 is the gate branch, w3 the up branch); w2 [d, d_ff]: the
+    [out][in] weights of those layers.  float64.
     """
     X = _f64(X)
-    return (silu(X @ _f64(w1)) * (X @ _f64(w3))) @ _f64(w2)
+    return (silu(X @ _f64(w1).T) * (X @ _f64(w3).T)) @ _f64(w2).T
 
 
 def expert_rows(x, perm, offsets, k, w1, w3, w2):
@@ -243,7 +246,7 @@ def forward(x, w_r, w1, w3, w2, k, mode, capacity=None, bias=None, shared=None,
     """The whole layer, steps in the order of [tirogla] How it works (Score, Select, Dispatch,
     Compute, Combine, Balance).
 
-    x [T, d]; w_r [d, E]; w1, w3 [E, d, d_ff]; w2 [E, d_ff, d]; shared = (w1s, w3s, w2s) or None.
+    x [T, d]; w_r [E, d]; w1, w3 [E, d_ff, d]; w2 [E, d, d_ff]; shared = (w1s, w3s, w2s) or None.
     `logits` (float32 [T, E]) replaces the router product when given.
     Returns a dict of every intermediate (float64 except the integer dispatch outputs).
     """

@@ -2,65 +2,98 @@
 //
 // Used for the expert FFN (the page "Mixture of experts (MoE)" (tirogla), How it works step 4: one
 // grouped GEMM over the experts' contiguous batches) and for the router product when E is large.
+// C[r, n] = sum_k A[src(r), k] * B_g[n, k]: both operands are K-contiguous (activation rows, and
+// weights in the [out][in] layout of a linear layer), so both travel the same way.
 //
-// Tiling: a 256-thread block (4 waves, WGM x WGN) computes a BM x BN tile of C (for NMAT = 2 two
-// B matrices share the tile: w1 and w3 of the SwiGLU expert, and the epilogue forms
-// silu(x.w1) * (x.w3) in registers, so the gate and up products never leave the chip).  K is walked
-// in steps of 64 through a double-buffered LDS:
-//   A (activation rows, K contiguous) is gathered row by row (token of each assignment) with
-//     16-byte loads and stored as [BM][64+8] bf16;
-//   B (weights [K][N], N contiguous) is loaded as 8x8 bf16 blocks (eight 16-byte rows), transposed
-//     in registers and stored K-contiguous as [BN][64+8], so both MFMA operands are read from LDS
-//     with one 16-byte read per lane.
-// Pipeline, one barrier per K step: at the top of step kt the registers hold tile kt+1 (loaded one
-// step earlier); they are written to the idle LDS buffer, the loads of tile kt+2 are issued, and the
-// MFMAs run on tile kt from the other buffer.
+// Tiling: a block of WGM x WGN waves computes a BM-row tile of C over BN columns (256 x 256 with
+// 8 waves and one block per CU for large groups, 128 x 256 with 4 waves and two blocks per CU
+// otherwise); for the SwiGLU up projection two weight matrices (w1 and w3) of 128 columns each
+// share the tile and the epilogue forms silu(x.w1) * (x.w3) in registers, so the gate and up
+// products never leave the chip.  Each wave owns a 64 x 128 block of accumulators.  K is walked in
+// steps of 32.
+//
+// LDS: every operand row holds the step's 32 bf16 (64 bytes, four 16-byte units) with unit u of
+// row r stored at u ^ swz(r).  Each operand read of the matrix instruction is one ds_read_b128 per
+// lane (32 rows x 2 units per wave), and the swizzle puts 16 consecutive rows read at one unit in
+// 16 distinct 4-bank groups; stores are 4-lane quads filling one row, so 16 lanes write 256
+// contiguous bytes.  Global loads are quads reading one row's 64 contiguous bytes.
+//
+// Pipeline: two LDS stages and two register sets.  At the top of step kt the registers holding
+// step kt+1 go to the idle stage and are refilled with step kt+3, so a load has two steps of work
+// to land; one barrier per step, issued without the memory fence of __syncthreads so that it does
+// not drain the loads in flight; the operand reads of the next 16-wide k slice are issued before
+// the matrix instructions of the current one.  The loop body is branch-free: when K divides into
+// an even number of steps, prefetches past the end re-read the last step; otherwise (TAIL) each
+// 16-byte load past the end of its K range is sent out of the buffer's range, which reads zeros.
+//
+// Split-K: when the tile grid would leave CUs idle (few rows per expert, e.g. decode), blocks also
+// split K; each writes fp32 partials and splitk_finish_kernel sums them in a fixed order and
+// applies the epilogue (results do not depend on the split).
 #include "common.h"
 #include "gemm_common.h"
 #include "kernels.h"
 
+#include <algorithm>
+#include <type_traits>
+
 namespace moe {
 
-static constexpr int kBK = 64;
-static constexpr int kLDK = kBK + 8;  // padded LDS row (144 bytes): conflict-free 16-byte reads
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4_t;
+typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8_t;
 
-// Transpose an 8x8 block of bf16: in[r] holds row r (8 values along n); out[n] gets column n
-// (8 values along r).
-__device__ __forceinline__ void transpose8x8(const u32x4 (&in)[8], u32x4 (&out)[8]) {
-#pragma unroll
-  for (int n = 0; n < 8; ++n) {
-    const int w = n >> 1;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint32_t lo = in[2 * j][w];
-      const uint32_t hi = in[2 * j + 1][w];
-      out[n][j] = (n & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
-    }
-  }
+// Physical 16-byte unit of logical unit u in LDS row r is u ^ swz(r).  Both forms depend on r % 32
+// only, keep 16 consecutive rows read at one unit in distinct 4-bank groups (with 64 banks; and 8
+// rows with 32 banks), and leave a row's units inside the row.
+template <int BK>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (BK == 32)
+    return ((r >> 2) ^ (r >> 1)) & 3;   // 64-byte rows: four units
+  else
+    return (r ^ ((r >> 3) & 3)) & 7;    // 128-byte rows: eight units
 }
 
-template <int BM, int BN, int NMAT>
-constexpr size_t gemm_stage_elems() {
-  return (size_t)(BM + NMAT * BN) * kLDK;
+template <int BM, int BN, int NMAT, int BK>
+constexpr int stage_bytes() {
+  return (BM + NMAT * BN) * BK * 2;
 }
 
-template <int BM, int BN, int NMAT, int WGM, int WGN, int EPI, bool KFULL>
-__global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(const GemmParams p) {
-  constexpr int WM = BM / WGM, WN = BN / WGN;
+constexpr int waitcnt_lgkm0() {                    // s_waitcnt lgkmcnt(0), other counters free
+  return 15 | (3 << 14) | (7 << 4) | (0 << 8);
+}
+
+__device__ __forceinline__ void barrier_no_fence() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+template <int BM, int BN, int NMAT, int WGM, int WGN, int BK, int MINB, int EPI, bool TAIL>
+__global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_bf16_kernel(const GemmParams p) {
+  constexpr int NTHR = 64 * WGM * WGN;
+  constexpr int WM = BM / WGM, WN = BN / WGN;       // WGM x WGN waves
   constexpr int TM = WM / 32, TN = WN / 32;
-  constexpr int A_CHUNKS = BM * (kBK / 8) / 256;             // 16-byte A chunks per thread
-  constexpr int B_BLOCKS = NMAT * (kBK / 8) * (BN / 8) / 256;  // 8x8 B blocks per thread
-  constexpr int STAGE = (int)gemm_stage_elems<BM, BN, NMAT>();
-  static_assert(WGM * WGN == 4, "4 waves");
-  static_assert(BN % 64 == 0, "the B matrix of a wave's blocks must be uniform");
-  static_assert(A_CHUNKS >= 1 && B_BLOCKS >= 1, "tile too small for 256 threads");
-  static_assert(BM * (kBK / 8) % 256 == 0 && NMAT * (kBK / 8) * (BN / 8) % 256 == 0, "tiling");
+  constexpr int KS = BK / 16;                       // 16-wide k slices per step
+  constexpr int RB = BK * 2;                        // LDS bytes per operand row per step
+  constexpr int UPR = BK / 8;                       // 16-byte units per row per step
+  constexpr int A_UNITS = BM * UPR / NTHR;          // units per thread per step
+  constexpr int B_UNITS = NMAT * BN * UPR / NTHR;
+  constexpr int ROWS_PER_LOAD = NTHR / UPR;         // operand rows covered by one load per thread
+  // Register sets: with 32-deep steps a load is issued two steps ahead (two sets), with 64-deep
+  // steps one step ahead (one set, the same number of registers).
+  constexpr int NSETS = BK == 32 ? 2 : 1;
+  constexpr int STAGE = stage_bytes<BM, BN, NMAT, BK>();
+  constexpr int B_OFF = BM * RB;                    // B rows follow the A rows in a stage
+  static_assert(BK == 32 || BK == 64, "K step");
+  static_assert(A_UNITS * NTHR == BM * UPR && B_UNITS * NTHR == NMAT * BN * UPR, "even split");
+  static_assert(BN % ROWS_PER_LOAD == 0, "a load stays inside one weight matrix");
+  static_assert(TM * 32 == WM && TN * 32 == WN, "32 x 32 matrix-instruction tiles");
 
-  extern __shared__ __align__(16) uint16_t smem[];
+  extern __shared__ __align__(16) uint8_t smem[];
 
   const int NT = (p.N + BN - 1) / BN;
   TileCoord tc;
-  if (!find_tile<BM>(p, NT, blockIdx.x, tc)) return;
+  const int kc = blockIdx.x % p.ksplit;
+  if (!find_tile<BM>(p, NT, blockIdx.x / p.ksplit, tc)) return;
   tc.g = __builtin_amdgcn_readfirstlane(tc.g);
   tc.row0 = __builtin_amdgcn_readfirstlane(tc.row0);
   tc.row_end = __builtin_amdgcn_readfirstlane(tc.row_end);
@@ -74,88 +107,84 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(const GemmParams p) {
   const int n_base = tc.n_tile * BN;
   const int K = p.K, N = p.N;
 
-  // Buffer descriptors: 32-bit offsets, and loads past the end of a matrix return zeros.
+  // Buffer descriptors: 32-bit offsets, and loads at or past num_records return zeros.
+  const uint32_t a_bytes = (uint32_t)p.a_rows * (uint32_t)K * 2u;
+  const uint32_t b_bytes = (uint32_t)N * (uint32_t)K * 2u;
   const __amdgpu_buffer_rsrc_t rA =
-      __builtin_amdgcn_make_buffer_rsrc((void*)p.A, (short)0, p.a_rows * K * 2, 0x00020000);
+      __builtin_amdgcn_make_buffer_rsrc((void*)p.A, (short)0, a_bytes, 0x00020000);
   const __amdgpu_buffer_rsrc_t rB0 = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)((const uint16_t*)p.B0 + (size_t)tc.g * p.b_gstride), (short)0, K * N * 2, 0x00020000);
+      (void*)((const uint16_t*)p.B0 + (size_t)tc.g * p.b_gstride), (short)0, b_bytes, 0x00020000);
   const __amdgpu_buffer_rsrc_t rB1 =
       NMAT == 2 ? __builtin_amdgcn_make_buffer_rsrc(
                       (void*)((const uint16_t*)p.B1 + (size_t)tc.g * p.b_gstride), (short)0,
-                      K * N * 2, 0x00020000)
+                      b_bytes, 0x00020000)
                 : rB0;
 
-  // A rows handled by this thread (fixed for the whole K loop).  Rows past the group's end load a
-  // valid row of the group instead; they only feed accumulator rows that are never stored.
-  uint32_t a_off[A_CHUNKS];
-  int a_kc[A_CHUNKS];
+  // Unit c = tid + NTHR i of an operand is row c / UPR, unit c % UPR (UPR consecutive lanes read
+  // one row's step of K, 64 or 128 contiguous bytes).  A rows past the group's end and B rows past
+  // N read a valid row instead; they only feed accumulators that are never stored.
+  uint32_t a_voff[A_UNITS], b_voff[B_UNITS];
+  int a_lds[A_UNITS], b_lds[B_UNITS];
+  const int u = tid % UPR;
 #pragma unroll
-  for (int i = 0; i < A_CHUNKS; ++i) {
-    const int c = tid + 256 * i;
-    const int row = c >> 3;
-    a_kc[i] = (c & 7) * 8;
+  for (int i = 0; i < A_UNITS; ++i) {
+    const int row = tid / UPR + ROWS_PER_LOAD * i;
     const int grow = min(tc.row0 + row, tc.row_end - 1);
     const int src = p.gather ? p.gather[grow] / p.gather_div : grow;
-    a_off[i] = (uint32_t)(src * K + a_kc[i]) * 2u;
+    a_voff[i] = ((uint32_t)src * (uint32_t)K + 8u * u) * 2u;
+    a_lds[i] = row * RB + ((u ^ swz<BK>(row)) << 4);
   }
-  // B blocks handled by this thread: rows kb*8..kb*8+7 of the K step, columns col..col+7.
-  // Columns past N read the next row's values (or zeros past the end); they only feed output
-  // columns that are never stored.
-  uint32_t b_off[B_BLOCKS];
-  int b_kb[B_BLOCKS], b_lds[B_BLOCKS], b_mat[B_BLOCKS];
 #pragma unroll
-  for (int i = 0; i < B_BLOCKS; ++i) {
-    // 8 * (BN / 8) = BN blocks per matrix; BN % 64 == 0 keeps the matrix index wave-uniform.
-    const int mat = (wave * 64 + 256 * i) / BN;
-    const int rem = (tid + 256 * i) % BN;
-    const int kb = rem & 7, nb = rem >> 3;
-    const int col = n_base + nb * 8;
-    b_mat[i] = mat;
-    b_kb[i] = kb * 8;
-    b_off[i] = (uint32_t)(kb * 8 * N + col) * 2u;
-    b_lds[i] = BM * kLDK + (mat * BN + nb * 8) * kLDK + kb * 8;
+  for (int i = 0; i < B_UNITS; ++i) {
+    const int brow = tid / UPR + ROWS_PER_LOAD * i;   // row of the stage's B block
+    const int n = min(n_base + brow % BN, N - 1);
+    b_voff[i] = ((uint32_t)n * (uint32_t)K + 8u * u) * 2u;
+    b_lds[i] = B_OFF + brow * RB + ((u ^ swz<BK>(brow)) << 4);
   }
-  const uint32_t row_bytes = (uint32_t)N * 2u;
 
-  u32x4 a_reg[A_CHUNKS];
-  u32x4 b_reg[B_BLOCKS][8];
-  const u32x4 zero = {0u, 0u, 0u, 0u};
+  const int Kc = K / p.ksplit;
+  const int kbeg = kc * Kc;
+  const int kend = kbeg + Kc;
+  const int KT = (Kc + BK - 1) / BK;
+  const int k_last = kbeg + (KT - 1) * BK;
 
-  auto load_tile = [&](int k0) {
+  u32x4 a_reg[NSETS][A_UNITS];
+  u32x4 b_reg[NSETS][B_UNITS];
+  auto load_regs = [&](int set, int k0) {
+    if constexpr (!TAIL) k0 = min(k0, k_last);
+    const uint32_t koff = (uint32_t)k0 * 2u;
+    const bool in_range = !TAIL || (k0 + 8 * u < kend);
 #pragma unroll
-    for (int i = 0; i < A_CHUNKS; ++i) {
-      if (KFULL || k0 + a_kc[i] < K)
-        a_reg[i] = __builtin_amdgcn_raw_buffer_load_b128(rA, a_off[i] + (uint32_t)k0 * 2u, 0, 0);
-      else
-        a_reg[i] = zero;
-    }
+    for (int i = 0; i < A_UNITS; ++i)
+      a_reg[set][i] =
+          __builtin_amdgcn_raw_buffer_load_b128(rA, in_range ? a_voff[i] + koff : a_bytes, 0, 0);
 #pragma unroll
-    for (int i = 0; i < B_BLOCKS; ++i) {
-      const uint32_t base = b_off[i] + (uint32_t)k0 * row_bytes;
-#pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        if (KFULL || k0 + b_kb[i] + r < K)
-          b_reg[i][r] = __builtin_amdgcn_raw_buffer_load_b128(b_mat[i] == 0 ? rB0 : rB1,
-                                                              base + r * row_bytes, 0, 0);
-        else
-          b_reg[i][r] = zero;
-      }
+    for (int i = 0; i < B_UNITS; ++i) {
+      const bool second = NMAT == 2 && (ROWS_PER_LOAD * i) / BN == 1;   // static per i
+      b_reg[set][i] = __builtin_amdgcn_raw_buffer_load_b128(
+          second ? rB1 : rB0, in_range ? b_voff[i] + koff : b_bytes, 0, 0);
     }
   };
-  auto store_tile = [&](uint16_t* buf) {
+  auto store_regs = [&](int set, int stage_off) {
 #pragma unroll
-    for (int i = 0; i < A_CHUNKS; ++i) {
-      const int c = tid + 256 * i;
-      *reinterpret_cast<u32x4*>(buf + (c >> 3) * kLDK + a_kc[i]) = a_reg[i];
-    }
+    for (int i = 0; i < A_UNITS; ++i)
+      *(lds_u32x4_t*)(smem + stage_off + a_lds[i]) = a_reg[set][i];
 #pragma unroll
-    for (int i = 0; i < B_BLOCKS; ++i) {
-      u32x4 t[8];
-      transpose8x8(b_reg[i], t);
-#pragma unroll
-      for (int n = 0; n < 8; ++n) *reinterpret_cast<u32x4*>(buf + b_lds[i] + n * kLDK) = t[n];
-    }
+    for (int i = 0; i < B_UNITS; ++i)
+      *(lds_u32x4_t*)(smem + stage_off + b_lds[i]) = b_reg[set][i];
   };
+
+  // Operand reads: lane l takes row (or weight row) l % 32 of a 32-row block and k 8 (l / 32) .. +7
+  // of the 16-wide slice ks, i.e. logical unit 2 ks + l / 32, stored at unit (l / 32 ^ swz) ^ 2 ks.
+  // Block bases are multiples of 32 rows, so the swizzle depends on l % 32 only.
+  const int l32 = lane & 31, h = lane >> 5;
+  const int su = (h ^ swz<BK>(l32)) << 4;
+  int a_rd[KS], b_rd[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    a_rd[ks] = (wm0 + l32) * RB + (su ^ (ks << 5));
+    b_rd[ks] = B_OFF + (wn0 + l32) * RB + (su ^ (ks << 5));
+  }
 
   f32x16 acc[NMAT][TM][TN];
 #pragma unroll
@@ -167,70 +196,84 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(const GemmParams p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[m][i][j][r] = 0.f;
 
-  // Number of this wave's 32-row sub-tiles that hold at least one row of the group.
-  const int rows_left = tc.row_end - (tc.row0 + wm0);
-  const int tm_live = __builtin_amdgcn_readfirstlane(
-      rows_left <= 0 ? 0 : (rows_left >= WM ? TM : (rows_left + 31) / 32));
-
-  const int KT = (K + kBK - 1) / kBK;
-  load_tile(0);
-  store_tile(smem);
-  if (KT > 1) load_tile(kBK);
-  __syncthreads();
-  const int lrow = lane & 31;
-  const int lk = (lane >> 5) * 8;
-  for (int kt = 0; kt < KT; ++kt) {
-    const uint16_t* cur = smem + (kt & 1) * STAGE;
-    if (kt + 1 < KT) {
-      store_tile(smem + ((kt + 1) & 1) * STAGE);
-      if (kt + 2 < KT) load_tile((kt + 2) * kBK);
-    }
-    const uint16_t* As = cur;
-    const uint16_t* Bs = cur + BM * kLDK;
+  bf16x8 af[2][TM];
+  bf16x8 bfr[2][NMAT][TN];
+  auto read_frags = [&](int stage_off, int ks, int buf) {
 #pragma unroll
-    for (int ks = 0; ks < kBK / 16; ++ks) {
-      bf16x8 af[TM];
-      bf16x8 bfr[NMAT][TN];
+    for (int i = 0; i < TM; ++i)
+      af[buf][i] = *(const lds_bf16x8_t*)(smem + stage_off + a_rd[ks] + i * 32 * RB);
 #pragma unroll
-      for (int i = 0; i < TM; ++i)
-        af[i] = *reinterpret_cast<const bf16x8*>(As + (wm0 + i * 32 + lrow) * kLDK + ks * 16 + lk);
+    for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        bfr[buf][m][j] =
+            *(const lds_bf16x8_t*)(smem + stage_off + b_rd[ks] + (m * BN + j * 32) * RB);
+  };
+  auto mfmas = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
 #pragma unroll
       for (int m = 0; m < NMAT; ++m)
 #pragma unroll
         for (int j = 0; j < TN; ++j)
-          bfr[m][j] = *reinterpret_cast<const bf16x8*>(
-              Bs + (m * BN + wn0 + j * 32 + lrow) * kLDK + ks * 16 + lk);
+          acc[m][i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[buf][i], bfr[buf][m][j],
+                                                                 acc[m][i][j], 0, 0, 0);
+  };
+
+  load_regs(0, kbeg);
+  if constexpr (NSETS == 2) load_regs(1, kbeg + BK);
+  store_regs(0, 0);
+  load_regs(0, kbeg + NSETS * BK);
+  __builtin_amdgcn_s_waitcnt(waitcnt_lgkm0());
+  barrier_no_fence();
+  read_frags(0, 0, 0);
+  // One K step; S is true when kt is even (reads stage 0, fills stage 1).
+  auto step = [&](int kt, auto S) {
+    constexpr int st = decltype(S)::value ? 0 : STAGE;
+    constexpr int nx = decltype(S)::value ? STAGE : 0;
+    constexpr int set = (NSETS == 2 && decltype(S)::value) ? 1 : 0;
+    store_regs(set, nx);                                // step kt+1 into the idle stage
+    load_regs(set, kbeg + (kt + 1 + NSETS) * BK);       // and a later step into its registers
 #pragma unroll
-      for (int i = 0; i < TM; ++i) {
-#pragma unroll
-        for (int m = 0; m < NMAT; ++m)
-#pragma unroll
-          for (int j = 0; j < TN; ++j)
-            acc[m][i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[m][j],
-                                                                   acc[m][i][j], 0, 0, 0);
-      }
+    for (int ks = 0; ks < KS - 1; ++ks) {
+      read_frags(st, ks + 1, (ks + 1) & 1);
+      __builtin_amdgcn_sched_barrier(0);
+      mfmas(ks & 1);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    __syncthreads();
+    __builtin_amdgcn_s_waitcnt(waitcnt_lgkm0());
+    barrier_no_fence();
+    read_frags(nx, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    mfmas((KS - 1) & 1);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // An odd step count runs one extra step; then K is ragged (TAIL) and the extra step reads zeros.
+  for (int kt = 0; kt < KT; kt += 2) {
+    step(kt, std::true_type());
+    step(kt + 1, std::false_type());
   }
 
-  // Epilogue.  Accumulator register r of a 32x32 tile holds row 8*(r/4) + 4*(lane/32) + r%4 and
-  // column lane%32.
+  // Epilogue.  Accumulator register r of a 32x32 tile holds row 8 (r / 4) + 4 (lane / 32) + r % 4
+  // and column lane % 32.
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
-    if (i >= tm_live) continue;
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
-      const int col = n_base + wn0 + j * 32 + (lane & 31);
+      const int col = n_base + wn0 + j * 32 + l32;
       if (col >= N) continue;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int row = tc.row0 + wm0 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        const int row = tc.row0 + wm0 + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
         if (row >= tc.row_end) continue;
-        if constexpr (EPI == EPI_SWIGLU) {
+        if (p.ksplit > 1) {   // fp32 partial sums; splitk_finish_kernel applies the epilogue
+#pragma unroll
+          for (int m = 0; m < NMAT; ++m)
+            p.part[((size_t)(kc * NMAT + m) * p.part_rows + row) * N + col] = acc[m][i][j][r];
+        } else if constexpr (EPI == EPI_SWIGLU) {
           const float g = acc[0][i][j][r];
-          const float u = acc[NMAT - 1][i][j][r];
-          const float h = g / (1.0f + expf(-g)) * u;
-          ((uint16_t*)p.C)[(size_t)row * p.ldc + col] = f32_to_bf16(h);
+          const float v = acc[NMAT - 1][i][j][r];
+          ((uint16_t*)p.C)[(size_t)row * p.ldc + col] = f32_to_bf16(g / (1.0f + expf(-g)) * v);
         } else if constexpr (EPI == EPI_STORE) {
           ((uint16_t*)p.C)[(size_t)row * p.ldc + col] = f32_to_bf16(acc[0][i][j][r]);
         } else {
@@ -242,11 +285,54 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(const GemmParams p) {
   }
 }
 
-template <int BM, int BN, int NMAT, int WGM, int WGN, int EPI, bool KFULL>
-static hipError_t launch_gemm_bf16_k(const GemmParams& p, int rows_max, hipStream_t s) {
-  auto kern = gemm_bf16_kernel<BM, BN, NMAT, WGM, WGN, EPI, KFULL>;
-  const size_t lds = 2 * gemm_stage_elems<BM, BN, NMAT>() * sizeof(uint16_t);
-  static bool attr_set = false;  // the attribute is per function; setting it twice is harmless
+// Sum the K-chunk partials of every valid row in a fixed order and apply the epilogue.
+// Rows past the valid count (offsets[G], or M for a single group) are untouched.
+template <int NMAT, int EPI>
+__global__ __launch_bounds__(256) void splitk_finish_kernel(const GemmParams p) {
+  const int rows = p.offsets ? p.offsets[p.G] : p.M;
+  const int nv = p.N / 8;                              // 8 columns per thread
+  const size_t total = (size_t)rows * nv;
+  for (size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x; idx < total;
+       idx += (size_t)gridDim.x * 256) {
+    const int row = (int)(idx / nv), c0 = (int)(idx % nv) * 8;
+    float s[NMAT][8];
+#pragma unroll
+    for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+      for (int q = 0; q < 8; ++q) s[m][q] = 0.f;
+    for (int kc = 0; kc < p.ksplit; ++kc) {
+#pragma unroll
+      for (int m = 0; m < NMAT; ++m) {
+        const f32x4* src = reinterpret_cast<const f32x4*>(
+            p.part + ((size_t)(kc * NMAT + m) * p.part_rows + row) * p.N + c0);
+        const f32x4 a = src[0], b = src[1];
+        s[m][0] += a[0]; s[m][1] += a[1]; s[m][2] += a[2]; s[m][3] += a[3];
+        s[m][4] += b[0]; s[m][5] += b[1]; s[m][6] += b[2]; s[m][7] += b[3];
+      }
+    }
+    u32x4 o;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      float v0, v1;
+      if constexpr (EPI == EPI_SWIGLU) {
+        const float g0 = s[0][2 * q], g1 = s[0][2 * q + 1];
+        v0 = g0 / (1.0f + expf(-g0)) * s[NMAT - 1][2 * q];
+        v1 = g1 / (1.0f + expf(-g1)) * s[NMAT - 1][2 * q + 1];
+      } else {
+        v0 = s[0][2 * q];
+        v1 = s[0][2 * q + 1];
+      }
+      o[q] = pack_bf16x2(v0, v1);
+    }
+    *reinterpret_cast<u32x4*>((uint16_t*)p.C + (size_t)row * p.ldc + c0) = o;
+  }
+}
+
+template <int BM, int BN, int NMAT, int WGM, int WGN, int BK, int MINB, int EPI, bool TAIL>
+static hipError_t launch_t(const GemmParams& p, int rows_max, hipStream_t s) {
+  auto kern = gemm_bf16_kernel<BM, BN, NMAT, WGM, WGN, BK, MINB, EPI, TAIL>;
+  const size_t lds = 2 * (size_t)stage_bytes<BM, BN, NMAT, BK>();
+  static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute((const void*)kern,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -254,30 +340,85 @@ static hipError_t launch_gemm_bf16_k(const GemmParams& p, int rows_max, hipStrea
     attr_set = true;
   }
   const int NT = (p.N + BN - 1) / BN;
-  const int grid = tiles_upper_bound(rows_max, p.G, p.offsets != nullptr, BM, NT);
+  const int grid = tiles_upper_bound(rows_max, p.G, p.offsets != nullptr, BM, NT) * p.ksplit;
   if (grid <= 0) return hipSuccess;
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(256), lds, s, p);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * WGM * WGN), lds, s, p);
   return hipGetLastError();
 }
 
-template <int BM, int BN, int NMAT, int WGM, int WGN, int EPI>
-static hipError_t launch_gemm_bf16_t(const GemmParams& p, int rows_max, hipStream_t s) {
-  if (p.K % kBK == 0) return launch_gemm_bf16_k<BM, BN, NMAT, WGM, WGN, EPI, true>(p, rows_max, s);
-  return launch_gemm_bf16_k<BM, BN, NMAT, WGM, WGN, EPI, false>(p, rows_max, s);
+template <int BM, int BN, int NMAT, int WGM, int WGN, int BK, int MINB, int EPI>
+static hipError_t launch_tail_or_not(const GemmParams& p, int rows_max, hipStream_t s) {
+  const bool even_steps = (p.K / p.ksplit) % (2 * BK) == 0;
+  return even_steps ? launch_t<BM, BN, NMAT, WGM, WGN, BK, MINB, EPI, false>(p, rows_max, s)
+                    : launch_t<BM, BN, NMAT, WGM, WGN, BK, MINB, EPI, true>(p, rows_max, s);
 }
 
-hipError_t launch_gemm_bf16(const GemmParams& p, int rows_max, int epi, hipStream_t s) {
-  // K a multiple of 64: the direct-to-LDS kernel (gemm_bf16_lds.hip); else the general one below.
-  const hipError_t e = launch_gemm_bf16_lds(p, rows_max, epi, s);
-  if (e != hipErrorNotSupported) return e;
+static void launch_splitk_finish(const GemmParams& p, int rows_max, int epi, hipStream_t s) {
+  const size_t items = (size_t)rows_max * (p.N / 8);
+  const int fgrid = (int)std::min<size_t>((items + 255) / 256, 4096);
+  if (fgrid <= 0) return;
+  if (epi == EPI_SWIGLU)
+    hipLaunchKernelGGL((splitk_finish_kernel<2, EPI_SWIGLU>), dim3(fgrid), dim3(256), 0, s, p);
+  else
+    hipLaunchKernelGGL((splitk_finish_kernel<1, EPI_STORE>), dim3(fgrid), dim3(256), 0, s, p);
+}
+
+// 256-row tiles (8 waves, one block per CU) when the groups are large enough to fill them: they
+// load a third fewer operand bytes per flop than 128-row tiles.  Smaller groups (fine-grained
+// experts, decode) keep 128-row tiles so that ragged group ends waste less.
+static bool use_big_tiles(int rows_max, int G, bool grouped, int epi) {
+  if (epi == EPI_STORE_F32_BIAS) return false;
+  return rows_max >= 512 * (grouped ? std::max(G, 1) : 1);
+}
+
+// K chunks for the expert GEMMs: when the tile grid would leave CUs idle (few rows, e.g. decode),
+// split K so that about 1024 blocks run, keeping every chunk a whole number of 64-deep steps.
+static int splitk_factor(int rows_max, int G, bool grouped, int N, int K, int epi) {
+  if (epi == EPI_STORE_F32_BIAS || K % 64 != 0 || N % 8 != 0) return 1;
+  if (use_big_tiles(rows_max, G, grouped, epi)) return 1;
+  const int BM = 128, BN = (epi == EPI_SWIGLU) ? 128 : 256;
+  const int mt = grouped ? std::min(G, rows_max) + rows_max / BM : (rows_max + BM - 1) / BM;
+  const long long tiles = (long long)mt * ((N + BN - 1) / BN);
+  int ks = 1;
+  while (ks < 16 && tiles * ks * 2 <= 1024 && (K / 64) % (ks * 2) == 0) ks *= 2;
+  return ks;
+}
+
+size_t gemm_bf16_partial_bytes(int rows_max, int G, bool grouped, int N, int K, int epi) {
+  const int ks = splitk_factor(rows_max, G, grouped, N, K, epi);
+  if (ks == 1) return 0;
+  const int nmat = epi == EPI_SWIGLU ? 2 : 1;
+  return (size_t)ks * nmat * rows_max * N * sizeof(float);
+}
+
+// Needs K a multiple of 8 (16-byte rows) and every operand under 2 GiB (32-bit buffer offsets).
+hipError_t launch_gemm_bf16(const GemmParams& p_in, int rows_max, int epi, hipStream_t s) {
+  if (p_in.K % 8 != 0 || p_in.N < 1 || p_in.K < 8) return hipErrorNotSupported;
+  if ((long long)p_in.a_rows * p_in.K * 2 >= (1ll << 31) ||
+      (long long)p_in.N * p_in.K * 2 >= (1ll << 31))
+    return hipErrorNotSupported;
+  GemmParams p = p_in;
+  const bool grouped = p.offsets != nullptr;
+  p.ksplit = splitk_factor(rows_max, p.G, grouped, p.N, p.K, epi);
+  p.part_rows = rows_max;
+  if (p.ksplit > 1 && p.part == nullptr) p.ksplit = 1;   // no scratch given: no split
+  const bool big = use_big_tiles(rows_max, p.G, grouped, epi);
+  hipError_t e;
   switch (epi) {
     case EPI_SWIGLU:
-      return launch_gemm_bf16_t<256, 128, 2, 2, 2, EPI_SWIGLU>(p, rows_max, s);
+      e = big ? launch_tail_or_not<256, 128, 2, 4, 2, 64, 1, EPI_SWIGLU>(p, rows_max, s)
+              : launch_tail_or_not<128, 128, 2, 2, 2, 32, 2, EPI_SWIGLU>(p, rows_max, s);
+      break;
     case EPI_STORE:
-      return launch_gemm_bf16_t<256, 256, 1, 2, 2, EPI_STORE>(p, rows_max, s);
+      e = big ? launch_tail_or_not<256, 256, 1, 4, 2, 64, 1, EPI_STORE>(p, rows_max, s)
+              : launch_tail_or_not<128, 256, 1, 2, 2, 32, 2, EPI_STORE>(p, rows_max, s);
+      break;
     default:
-      return launch_gemm_bf16_t<64, 256, 1, 2, 2, EPI_STORE_F32_BIAS>(p, rows_max, s);
+      e = launch_tail_or_not<128, 256, 1, 2, 2, 32, 1, EPI_STORE_F32_BIAS>(p, rows_max, s);
   }
+  if (e != hipSuccess) return e;
+  if (p.ksplit > 1) launch_splitk_finish(p, rows_max, epi, s);
+  return hipGetLastError();
 }
 
 }  // namespace moe

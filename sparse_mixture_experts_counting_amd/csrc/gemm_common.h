@@ -1,8 +1,9 @@
 // Grouped-GEMM launch parameters and the device-side tile scheduler shared by the GEMM kernels.
 //
 // A grouped GEMM here is: for every group g (an expert) and every row r in [offsets[g],
-// offsets[g+1]), C[r, :] = A[src(r), :] . B_g (+ epilogue), with B_g = B + g * b_gstride a [K][N]
-// row-major matrix (N contiguous, the layout the weights are given in).  src(r) = gather[r] /
+// offsets[g+1]), C[r, n] = sum_k A[src(r), k] B_g[n, k] (+ epilogue), with B_g = B + g * b_gstride
+// an [N][K] row-major matrix (K contiguous: the [out][in] layout of a linear layer's weight, the
+// layout the weights are given in).  src(r) = gather[r] /
 // gather_div when a gather list is given (token of assignment perm[r]), else r.  The group sizes
 // live on the device (they come out of the dispatch kernels), so the grid is sized for an upper
 // bound and every block finds its tile from `offsets` itself; blocks past the real tile count exit.
@@ -21,7 +22,7 @@ struct GemmParams {
   int G;
   int M;                    // rows of the single group (offsets == NULL)
   int N, K;
-  const void* B0;           // [G][K][N]
+  const void* B0;           // [G][N][K]
   const void* B1;           // second matrix for the fused SwiGLU epilogue (same layout) or NULL
   long long b_gstride;      // elements between consecutive groups' B
   void* C;                  // output rows, [rows][ldc]

@@ -1,6 +1,7 @@
 // fp32 grouped GEMM on the vector ALUs (the fp32 layer dtype; small shapes).  Same grouped-GEMM
-// contract and epilogues as the bf16 matrix-core kernel: C[r, :] = A[src(r), :] . B_g, with the
-// SwiGLU epilogue silu(x.w1) * (x.w3) fused for the expert up projection.
+// contract and epilogues as the bf16 matrix-core kernel: C[r, n] = sum_k A[src(r), k] B_g[n, k]
+// (weights [N][K], the [out][in] layout of a linear layer), with the SwiGLU epilogue
+// silu(x.w1) * (x.w3) fused for the expert up projection.  K must be a multiple of 4.
 #include "common.h"
 #include "gemm_common.h"
 #include "kernels.h"
@@ -30,8 +31,8 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const GemmParams p) {
   int src = grow;
   if (a_ok && p.gather) src = p.gather[grow] / p.gather_div;
   const float* a_ptr = A + (size_t)(a_ok ? src : 0) * K;
-  // B loader: k row tid/16, 4 consecutive n.
-  const int b_k = tid >> 4, b_n = (tid & 15) * 4;
+  // B loader: weight row (output column) tid/4, 4 consecutive k.
+  const int b_n = tid >> 2, b_k = (tid & 3) * 4;
   const bool b_ok = n_base + b_n < N;
 
   float acc[NMAT][4][4];
@@ -51,8 +52,9 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const GemmParams p) {
     for (int m = 0; m < NMAT; ++m) {
       f32x4 bv = {0.f, 0.f, 0.f, 0.f};
       if (b_ok && k0 + b_k < K)
-        bv = *reinterpret_cast<const f32x4*>(Bm[m] + (size_t)(k0 + b_k) * N + n_base + b_n);
-      *reinterpret_cast<f32x4*>(&Bs[m][b_k][b_n]) = bv;
+        bv = *reinterpret_cast<const f32x4*>(Bm[m] + (size_t)(n_base + b_n) * K + k0 + b_k);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) Bs[m][b_k + q][b_n] = bv[q];
     }
     __syncthreads();
 #pragma unroll

@@ -26,7 +26,6 @@ void launch_dispatch(const int32_t* topk_idx, int A, int E, int capacity, int32_
 
 // gemm_bf16.hip / gemm_f32.hip
 hipError_t launch_gemm_bf16(const GemmParams& p, int rows_max, int epi, hipStream_t s);
-hipError_t launch_gemm_bf16_lds(const GemmParams& p, int rows_max, int epi, hipStream_t s);
 size_t gemm_bf16_partial_bytes(int rows_max, int G, bool grouped, int N, int K, int epi);
 hipError_t launch_gemm_f32(const GemmParams& p, int rows_max, int epi, hipStream_t s);
 

@@ -9,9 +9,10 @@
 namespace moe {
 
 // ---------------------------------------------------------------------------------------------
-// Router product for E <= 16 experts: logits[t, e] = sum_j x[t, j] w_r[j, e] (+ bias[e]).
-// Memory bound on x; one wave handles TPW tokens, lanes stride over 8-wide slices of d, and each
-// lane reads the matching 8 x E slab of W_r (contiguous in the [d][E] layout, 16-byte aligned).
+// Router product for E <= 16 experts: logits[t, e] = sum_j x[t, j] w_r[e, j] (+ bias[e]), W_r in
+// the [E][d] layout of a linear layer.  Memory bound on x; one wave handles TPW tokens, lanes
+// stride over 8-wide slices of d, and each lane reads the matching 8 values of every W_r row
+// (16-byte aligned: d is a multiple of 8).
 // ---------------------------------------------------------------------------------------------
 template <typename TIn, int E, int TPW>
 __global__ __launch_bounds__(256) void router_small_e_kernel(const TIn* __restrict__ x,
@@ -30,20 +31,16 @@ __global__ __launch_bounds__(256) void router_small_e_kernel(const TIn* __restri
 
   const int nchunk = d >> 3;
   for (int c = lane; c < nchunk; c += 64) {
-    float w[8 * E];
-    if constexpr (sizeof(TIn) == 2) {
-      const u32x4* src = reinterpret_cast<const u32x4*>(w_r + (size_t)c * 8 * E);
+    float w[E][8];
 #pragma unroll
-      for (int v = 0; v < E; ++v) {  // 8*E bf16 = E 16-byte words
-        u32x4 q = src[v];
-        unpack8(q, &w[8 * v]);
-      }
-    } else {
-      const f32x4* src = reinterpret_cast<const f32x4*>(w_r + (size_t)c * 8 * E);
-#pragma unroll
-      for (int v = 0; v < 2 * E; ++v) {
-        f32x4 q = src[v];
-        w[4 * v] = q[0]; w[4 * v + 1] = q[1]; w[4 * v + 2] = q[2]; w[4 * v + 3] = q[3];
+    for (int e = 0; e < E; ++e) {
+      if constexpr (sizeof(TIn) == 2) {
+        unpack8(*reinterpret_cast<const u32x4*>(w_r + (size_t)e * d + c * 8), w[e]);
+      } else {
+        const f32x4* src = reinterpret_cast<const f32x4*>(w_r + (size_t)e * d + c * 8);
+        const f32x4 a = src[0], b = src[1];
+        w[e][0] = a[0]; w[e][1] = a[1]; w[e][2] = a[2]; w[e][3] = a[3];
+        w[e][4] = b[0]; w[e][5] = b[1]; w[e][6] = b[2]; w[e][7] = b[3];
       }
     }
 #pragma unroll
@@ -63,7 +60,7 @@ __global__ __launch_bounds__(256) void router_small_e_kernel(const TIn* __restri
 #pragma unroll
         for (int kk = 0; kk < 8; ++kk)
 #pragma unroll
-          for (int e = 0; e < E; ++e) acc[i][e] = fmaf(xv[kk], w[kk * E + e], acc[i][e]);
+          for (int e = 0; e < E; ++e) acc[i][e] = fmaf(xv[kk], w[e][kk], acc[i][e]);
       }
     }
   }
@@ -141,9 +138,9 @@ __global__ __launch_bounds__(256) void router_generic_kernel(const TIn* __restri
       for (int j = 0; j < n; ++j) {
         float w;
         if constexpr (sizeof(TIn) == 2)
-          w = bf16_to_f32(w_r[(size_t)(j0 + j) * E + e]);
+          w = bf16_to_f32(w_r[(size_t)e * d + j0 + j]);
         else
-          w = w_r[(size_t)(j0 + j) * E + e];
+          w = w_r[(size_t)e * d + j0 + j];
         acc = fmaf(xs[j], w, acc);
       }
     }

@@ -17,9 +17,11 @@ top-8 in its section 8.2; Switch top-1 with capacity factor 1.25 in "Mixture of 
                      1 shared expert, Zipf(s=1.1) logit bias
   mixtral_decode     T=32   d=4096 E=8   k=2 d_ff=14336 bf16 softmax_topk no capacity
 
-Draw order for one seed: x = randn(T, d); W_r = randn(d, E) / sqrt(d) (times router_scale); for each
-expert e: w1[e] = randn(d, d_ff) / sqrt(d), w3[e] = randn(d, d_ff) / sqrt(d),
-w2[e] = randn(d_ff, d) / sqrt(d_ff); then the shared expert's w1, w3, w2 the same way.  Each tensor is
+Weights are held [out][in], as linear layers store them (the expert and router modules of the
+"DL S077" page, sections 1.1 and 1.2, are bias-free linear layers).  Draw order for one seed:
+x = randn(T, d); W_r = randn(E, d) / sqrt(d) (times router_scale); for each expert e:
+w1[e] = randn(d_ff, d) / sqrt(d), w3[e] = randn(d_ff, d) / sqrt(d), w2[e] = randn(d, d_ff) / sqrt(d_ff);
+then the shared expert's w1, w3, w2 the same way.  Each tensor is
 cast to the layer dtype right after it is drawn (bfloat16 round-to-nearest-even).  On device "cpu"
 the draws come from torch's CPU generator; on a GPU device from torch's device generator (much faster
 for the multi-GB workloads; a different but equally deterministic stream).
@@ -88,11 +90,11 @@ def zipf_logit_bias(E, s):
 class MoEInputs:
     cfg: MoEConfig
     x: torch.Tensor          # [T, d]
-    w_r: torch.Tensor        # [d, E]
-    w1: torch.Tensor         # [E, d, d_ff]
-    w3: torch.Tensor         # [E, d, d_ff]
-    w2: torch.Tensor         # [E, d_ff, d]
-    shared: tuple = None     # (w1s [d, d_ff], w3s [d, d_ff], w2s [d_ff, d]) or None
+    w_r: torch.Tensor        # [E, d]      (all weights: [out][in], as linear layers hold them)
+    w1: torch.Tensor         # [E, d_ff, d]
+    w3: torch.Tensor         # [E, d_ff, d]
+    w2: torch.Tensor         # [E, d, d_ff]
+    shared: tuple = None     # (w1s [d_ff, d], w3s [d_ff, d], w2s [d, d_ff]) or None
     bias: torch.Tensor = None  # float32 [E] or None
 
 
@@ -111,20 +113,20 @@ def make_inputs(cfg, seed=0, device="cpu"):
         return t.to(dt)
 
     x = draw((T, d), 1.0)
-    w_r = draw((d, E), cfg.router_scale / math.sqrt(d))
-    w1 = torch.empty((E, d, d_ff), dtype=dt, device=dev)
-    w3 = torch.empty((E, d, d_ff), dtype=dt, device=dev)
-    w2 = torch.empty((E, d_ff, d), dtype=dt, device=dev)
+    w_r = draw((E, d), cfg.router_scale / math.sqrt(d))
+    w1 = torch.empty((E, d_ff, d), dtype=dt, device=dev)
+    w3 = torch.empty((E, d_ff, d), dtype=dt, device=dev)
+    w2 = torch.empty((E, d, d_ff), dtype=dt, device=dev)
     for e in range(E):
-        w1[e] = draw((d, d_ff), 1.0 / math.sqrt(d))
-        w3[e] = draw((d, d_ff), 1.0 / math.sqrt(d))
-        w2[e] = draw((d_ff, d), 1.0 / math.sqrt(d_ff))
+        w1[e] = draw((d_ff, d), 1.0 / math.sqrt(d))
+        w3[e] = draw((d_ff, d), 1.0 / math.sqrt(d))
+        w2[e] = draw((d, d_ff), 1.0 / math.sqrt(d_ff))
     shared = None
     if cfg.n_shared:
         if cfg.n_shared != 1:
             raise ValueError("one shared expert supported")
-        shared = (draw((d, d_ff), 1.0 / math.sqrt(d)), draw((d, d_ff), 1.0 / math.sqrt(d)),
-                  draw((d_ff, d), 1.0 / math.sqrt(d_ff)))
+        shared = (draw((d_ff, d), 1.0 / math.sqrt(d)), draw((d_ff, d), 1.0 / math.sqrt(d)),
+                  draw((d, d_ff), 1.0 / math.sqrt(d_ff)))
     bias = None
     if cfg.zipf_s:
         bias = torch.from_numpy(zipf_logit_bias(E, cfg.zipf_s)).to(dev)

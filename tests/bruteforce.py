@@ -56,14 +56,15 @@ def gates_alt(logits, idx, mode):
 
 
 def swiglu_loops(xrow, w1, w3, w2):
-    """One token through a SwiGLU expert with explicit loops over every index."""
-    d, d_ff = w1.shape
+    """One token through a SwiGLU expert with explicit loops over every index.  The weights are
+    the [out][in] matrices of bias-free linear layers: w1, w3 [d_ff][d], w2 [d][d_ff]."""
+    d_ff, d = w1.shape
     h = np.zeros(d_ff)
     for f in range(d_ff):
-        g = sum(xrow[j] * w1[j, f] for j in range(d))
-        u = sum(xrow[j] * w3[j, f] for j in range(d))
+        g = sum(xrow[j] * w1[f, j] for j in range(d))
+        u = sum(xrow[j] * w3[f, j] for j in range(d))
         h[f] = g / (1.0 + np.exp(-g)) * u
-    return np.array([sum(h[f] * w2[f, c] for f in range(d_ff)) for c in range(w2.shape[1])])
+    return np.array([sum(w2[c, f] * h[f] for f in range(d_ff)) for c in range(w2.shape[0])])
 
 
 def dense_then_mask(x, logits, w1, w3, w2, k, mode, capacity, shared=None):
@@ -74,12 +75,12 @@ def dense_then_mask(x, logits, w1, w3, w2, k, mode, capacity, shared=None):
     idx = rank_select(logits, k)
     g = gates_alt(logits, idx, mode)
     keep = keep_mask(idx, capacity).reshape(T, k)
-    dense = np.zeros((E, T, w2.shape[2]))
+    dense = np.zeros((E, T, w2.shape[1]))
     for e in range(E):
         for t in range(T):
             dense[e, t] = swiglu_loops(x[t], np.asarray(w1[e], np.float64),
                                        np.asarray(w3[e], np.float64), np.asarray(w2[e], np.float64))
-    y = np.zeros((T, w2.shape[2]))
+    y = np.zeros((T, w2.shape[1]))
     for t in range(T):
         for s in range(k):
             if keep[t, s]:

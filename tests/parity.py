@@ -41,8 +41,8 @@ def logit_error_bound(x, w_r, bias=None):
     d = x.shape[1]
     g = d * U32 / (1 - d * U32)
     ax = np.abs(np.asarray(x, np.float64))
-    aw = np.abs(np.asarray(w_r, np.float64))
-    exact = np.asarray(x, np.float64) @ np.asarray(w_r, np.float64)
+    aw = np.abs(np.asarray(w_r, np.float64)).T          # w_r is [E, d]
+    exact = np.asarray(x, np.float64) @ np.asarray(w_r, np.float64).T
     if bias is not None:
         exact = exact + np.asarray(bias, np.float64)[None, :]
     return (g + U32) * (ax @ aw) + 4 * U32 * np.abs(exact) + 1e-30, exact

@@ -194,7 +194,7 @@ SWEEP = [
     (700, 72, 3, 1, 48, "fp32", "softmax_all", 200, 0, 0.0),
     (513, 328, 16, 2, 296, "bf16", "softmax_topk", 0, 1, 0.0),
     (200, 16, 256, 8, 24, "bf16", "sigmoid_topk", 0, 1, 1.1),
-    # K a multiple of 64: the direct-to-LDS matrix-core kernel (N below, at and above one tile)
+    # K a multiple of 64: even step count, no ragged K (N below, at and above one tile)
     (300, 128, 8, 2, 192, "bf16", "softmax_topk", 0, 0, 0.0),
     (257, 64, 5, 2, 64, "bf16", "softmax_all", 90, 0, 0.0),
     (300, 128, 256, 8, 64, "bf16", "sigmoid_topk", 0, 1, 1.1),
@@ -204,6 +204,9 @@ SWEEP = [
     (16, 256, 4, 2, 512, "bf16", "softmax_topk", 0, 1, 0.0),
     (32, 128, 8, 2, 256, "bf16", "sigmoid_topk", 0, 1, 0.0),
     (7, 512, 3, 2, 1024, "bf16", "softmax_all", 3, 0, 0.0),
+    # at least 512 rows per expert: 256-row tiles (8 waves), ragged and even K, N past one tile
+    (2600, 136, 2, 2, 264, "bf16", "softmax_all", 0, 0, 0.0),
+    (2048, 128, 2, 1, 320, "bf16", "softmax_topk", 0, 1, 0.0),
 ]
 
 

@@ -280,9 +280,9 @@ def test_single_expert_is_dense_swiglu():
     rng = np.random.default_rng(7)
     T, d, f = 5, 6, 10
     x = rng.normal(size=(T, d))
-    w1, w3 = rng.normal(size=(1, d, f)), rng.normal(size=(1, d, f))
-    w2 = rng.normal(size=(1, f, d))
-    out = O.forward(x, rng.normal(size=(d, 1)), w1, w3, w2, 1, O.SOFTMAX_TOPK)
+    w1, w3 = rng.normal(size=(1, f, d)), rng.normal(size=(1, f, d))
+    w2 = rng.normal(size=(1, d, f))
+    out = O.forward(x, rng.normal(size=(1, d)), w1, w3, w2, 1, O.SOFTMAX_TOPK)
     ref = np.stack([bf.swiglu_loops(x[t], w1[0], w3[0], w2[0]) for t in range(T)])
     np.testing.assert_allclose(out["y"], ref, rtol=1e-12, atol=1e-12)
     assert np.all(out["topk_gate"] == 1.0)
@@ -317,11 +317,11 @@ def test_layer_matches_dense_evaluate_then_mask(mode, C, shared):
     rng = np.random.default_rng(10 + mode)
     T, d, E, k, f = 9, 5, 4, 2, 6
     x = rng.normal(size=(T, d)).astype(np.float32)
-    w_r = rng.normal(size=(d, E)).astype(np.float32)
-    w1 = rng.normal(size=(E, d, f)) / 2
-    w3 = rng.normal(size=(E, d, f)) / 2
-    w2 = rng.normal(size=(E, f, d)) / 2
-    sh = (rng.normal(size=(d, f)), rng.normal(size=(d, f)), rng.normal(size=(f, d))) if shared else None
+    w_r = rng.normal(size=(E, d)).astype(np.float32)
+    w1 = rng.normal(size=(E, f, d)) / 2
+    w3 = rng.normal(size=(E, f, d)) / 2
+    w2 = rng.normal(size=(E, d, f)) / 2
+    sh = (rng.normal(size=(f, d)), rng.normal(size=(f, d)), rng.normal(size=(d, f))) if shared else None
     out = O.forward(x, w_r, w1, w3, w2, k, mode, capacity=C, shared=sh)
     y, idx, keep = bf.dense_then_mask(x, out["logits"], w1, w3, w2, k, mode, C, sh)
     np.testing.assert_array_equal(out["topk_idx"], idx)
@@ -338,10 +338,10 @@ def test_router_logits_rounding():
     """Logits are the float64 product rounded once to float32."""
     rng = np.random.default_rng(11)
     x = rng.normal(size=(4, 300)).astype(np.float32)
-    w = rng.normal(size=(300, 5)).astype(np.float32)
+    w = rng.normal(size=(5, 300)).astype(np.float32)
     L = O.router_logits(x, w)
     assert L.dtype == np.float32
-    exact = np.array([[math.fsum(float(a) * float(b) for a, b in zip(x[t], w[:, e]))
+    exact = np.array([[math.fsum(float(a) * float(b) for a, b in zip(x[t], w[e]))
                        for e in range(5)] for t in range(4)])
     np.testing.assert_array_equal(L, exact.astype(np.float32))
 
