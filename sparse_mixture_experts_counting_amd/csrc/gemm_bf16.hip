@@ -38,6 +38,7 @@
 
 namespace moe {
 
+typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4_t;
 typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8_t;
 
@@ -60,6 +61,9 @@ constexpr int stage_bytes() {
 constexpr int waitcnt_lgkm0() {                    // s_waitcnt lgkmcnt(0), other counters free
   return 15 | (3 << 14) | (7 << 4) | (0 << 8);
 }
+constexpr int waitcnt_vm0_lgkm0() {                // s_waitcnt vmcnt(0) lgkmcnt(0)
+  return 0 | (0 << 14) | (7 << 4) | (0 << 8);
+}
 
 __device__ __forceinline__ void barrier_no_fence() {
   __builtin_amdgcn_sched_barrier(0);
@@ -67,7 +71,7 @@ __device__ __forceinline__ void barrier_no_fence() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-template <int BM, int BN, int NMAT, int WGM, int WGN, int BK, int MINB, int EPI, bool TAIL>
+template <int BM, int BN, int NMAT, int WGM, int WGN, int BK, bool DMA, int MINB, int EPI, bool TAIL>
 __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_bf16_kernel(const GemmParams p) {
   constexpr int NTHR = 64 * WGM * WGN;
   constexpr int WM = BM / WGM, WN = BN / WGN;       // WGM x WGN waves
@@ -87,6 +91,14 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_bf16_kernel(const G
   static_assert(A_UNITS * NTHR == BM * UPR && B_UNITS * NTHR == NMAT * BN * UPR, "even split");
   static_assert(BN % ROWS_PER_LOAD == 0, "a load stays inside one weight matrix");
   static_assert(TM * 32 == WM && TN * 32 == WN, "32 x 32 matrix-instruction tiles");
+  // Direct-to-LDS loads: one wave-wide 16-byte load fills 1 KB of LDS (lane l at byte 16 l), i.e.
+  // DROWS rows of a stage; block b of a stage is loaded by wave b % NW.
+  constexpr int NW = WGM * WGN;
+  constexpr int DROWS = 1024 / RB;
+  constexpr int DPW = (BM + NMAT * BN) / (DROWS * NW);   // direct loads per wave per step
+  constexpr int DPW_A = BM / (DROWS * NW);                // the first DPW_A of them are A rows
+  static_assert(!DMA || (DPW_A * DROWS * NW == BM && DPW * DROWS * NW == BM + NMAT * BN &&
+                         BN % (DROWS * NW) == 0), "direct loads split evenly");
 
   extern __shared__ __align__(16) uint8_t smem[];
 
@@ -142,14 +154,33 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_bf16_kernel(const G
     b_lds[i] = B_OFF + brow * RB + ((u ^ swz<BK>(brow)) << 4);
   }
 
+  // Direct loads: lane l of the load for stage block b = wave + NW j covers stage row
+  // DROWS b + l / UPR at physical unit l % UPR, so it fetches the logical unit stored there.
+  uint32_t d_voff[DMA ? DPW : 1];
+  if constexpr (DMA) {
+#pragma unroll
+    for (int j = 0; j < DPW; ++j) {
+      const int srow = (wave + NW * j) * DROWS + lane / UPR;
+      const int uu = (lane % UPR) ^ swz<BK>(srow);
+      if (j < DPW_A) {
+        const int grow = min(tc.row0 + srow, tc.row_end - 1);
+        const int src = p.gather ? p.gather[grow] / p.gather_div : grow;
+        d_voff[j] = ((uint32_t)src * (uint32_t)K + 8u * uu) * 2u;
+      } else {
+        const int n = min(n_base + (srow - BM) % BN, N - 1);
+        d_voff[j] = ((uint32_t)n * (uint32_t)K + 8u * uu) * 2u;
+      }
+    }
+  }
+
   const int Kc = K / p.ksplit;
   const int kbeg = kc * Kc;
   const int kend = kbeg + Kc;
   const int KT = (Kc + BK - 1) / BK;
   const int k_last = kbeg + (KT - 1) * BK;
 
-  u32x4 a_reg[NSETS][A_UNITS];
-  u32x4 b_reg[NSETS][B_UNITS];
+  u32x4 a_reg[DMA ? 1 : NSETS][DMA ? 1 : A_UNITS];
+  u32x4 b_reg[DMA ? 1 : NSETS][DMA ? 1 : B_UNITS];
   auto load_regs = [&](int set, int k0) {
     if constexpr (!TAIL) k0 = min(k0, k_last);
     const uint32_t koff = (uint32_t)k0 * 2u;
@@ -163,6 +194,24 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_bf16_kernel(const G
       const bool second = NMAT == 2 && (ROWS_PER_LOAD * i) / BN == 1;   // static per i
       b_reg[set][i] = __builtin_amdgcn_raw_buffer_load_b128(
           second ? rB1 : rB0, in_range ? b_voff[i] + koff : b_bytes, 0, 0);
+    }
+  };
+  auto issue_dma = [&](int stage_off, int k0) {
+    if constexpr (!TAIL) k0 = min(k0, k_last);
+    const uint32_t koff = (uint32_t)k0 * 2u;
+#pragma unroll
+    for (int j = 0; j < DPW; ++j) {
+      const bool is_a = j < DPW_A;
+      const bool second = NMAT == 2 && !is_a && ((j - DPW_A) * DROWS * NW) / BN == 1;
+      uint32_t voff = d_voff[j] + koff;
+      if constexpr (TAIL) {
+        const int srow = (wave + NW * j) * DROWS + lane / UPR;
+        if (k0 + 8 * ((lane % UPR) ^ swz<BK>(srow)) >= kend) voff = is_a ? a_bytes : b_bytes;
+      }
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(is_a ? rA : (second ? rB1 : rB0),
+                                               (lds_void_t*)(smem + stage_off +
+                                                             (wave + NW * j) * 1024),
+                                               16, (int)voff, 0, 0, 0);
     }
   };
   auto store_regs = [&](int set, int stage_off) {
@@ -220,11 +269,16 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_bf16_kernel(const G
                                                                  acc[m][i][j], 0, 0, 0);
   };
 
-  load_regs(0, kbeg);
-  if constexpr (NSETS == 2) load_regs(1, kbeg + BK);
-  store_regs(0, 0);
-  load_regs(0, kbeg + NSETS * BK);
-  __builtin_amdgcn_s_waitcnt(waitcnt_lgkm0());
+  if constexpr (DMA) {
+    issue_dma(0, kbeg);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm0_lgkm0());
+  } else {
+    load_regs(0, kbeg);
+    if constexpr (NSETS == 2) load_regs(1, kbeg + BK);
+    store_regs(0, 0);
+    load_regs(0, kbeg + NSETS * BK);
+    __builtin_amdgcn_s_waitcnt(waitcnt_lgkm0());
+  }
   barrier_no_fence();
   read_frags(0, 0, 0);
   // One K step; S is true when kt is even (reads stage 0, fills stage 1).
@@ -232,8 +286,12 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_bf16_kernel(const G
     constexpr int st = decltype(S)::value ? 0 : STAGE;
     constexpr int nx = decltype(S)::value ? STAGE : 0;
     constexpr int set = (NSETS == 2 && decltype(S)::value) ? 1 : 0;
-    store_regs(set, nx);                                // step kt+1 into the idle stage
-    load_regs(set, kbeg + (kt + 1 + NSETS) * BK);       // and a later step into its registers
+    if constexpr (DMA) {
+      issue_dma(nx, kbeg + (kt + 1) * BK);              // step kt+1 straight into the idle stage
+    } else {
+      store_regs(set, nx);                              // step kt+1 into the idle stage
+      load_regs(set, kbeg + (kt + 1 + NSETS) * BK);     // and a later step into its registers
+    }
 #pragma unroll
     for (int ks = 0; ks < KS - 1; ++ks) {
       read_frags(st, ks + 1, (ks + 1) & 1);
@@ -241,7 +299,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_bf16_kernel(const G
       mfmas(ks & 1);
       __builtin_amdgcn_sched_barrier(0);
     }
-    __builtin_amdgcn_s_waitcnt(waitcnt_lgkm0());
+    __builtin_amdgcn_s_waitcnt(DMA ? waitcnt_vm0_lgkm0() : waitcnt_lgkm0());
     barrier_no_fence();
     read_frags(nx, 0, 0);
     __builtin_amdgcn_sched_barrier(0);
@@ -328,9 +386,9 @@ __global__ __launch_bounds__(256) void splitk_finish_kernel(const GemmParams p) 
   }
 }
 
-template <int BM, int BN, int NMAT, int WGM, int WGN, int BK, int MINB, int EPI, bool TAIL>
+template <int BM, int BN, int NMAT, int WGM, int WGN, int BK, bool DMA, int MINB, int EPI, bool TAIL>
 static hipError_t launch_t(const GemmParams& p, int rows_max, hipStream_t s) {
-  auto kern = gemm_bf16_kernel<BM, BN, NMAT, WGM, WGN, BK, MINB, EPI, TAIL>;
+  auto kern = gemm_bf16_kernel<BM, BN, NMAT, WGM, WGN, BK, DMA, MINB, EPI, TAIL>;
   const size_t lds = 2 * (size_t)stage_bytes<BM, BN, NMAT, BK>();
   static bool attr_set = false;
   if (!attr_set) {
@@ -346,11 +404,11 @@ static hipError_t launch_t(const GemmParams& p, int rows_max, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int BM, int BN, int NMAT, int WGM, int WGN, int BK, int MINB, int EPI>
+template <int BM, int BN, int NMAT, int WGM, int WGN, int BK, bool DMA, int MINB, int EPI>
 static hipError_t launch_tail_or_not(const GemmParams& p, int rows_max, hipStream_t s) {
   const bool even_steps = (p.K / p.ksplit) % (2 * BK) == 0;
-  return even_steps ? launch_t<BM, BN, NMAT, WGM, WGN, BK, MINB, EPI, false>(p, rows_max, s)
-                    : launch_t<BM, BN, NMAT, WGM, WGN, BK, MINB, EPI, true>(p, rows_max, s);
+  return even_steps ? launch_t<BM, BN, NMAT, WGM, WGN, BK, DMA, MINB, EPI, false>(p, rows_max, s)
+                    : launch_t<BM, BN, NMAT, WGM, WGN, BK, DMA, MINB, EPI, true>(p, rows_max, s);
 }
 
 static void launch_splitk_finish(const GemmParams& p, int rows_max, int epi, hipStream_t s) {
@@ -406,15 +464,15 @@ hipError_t launch_gemm_bf16(const GemmParams& p_in, int rows_max, int epi, hipSt
   hipError_t e;
   switch (epi) {
     case EPI_SWIGLU:
-      e = big ? launch_tail_or_not<256, 128, 2, 4, 2, 64, 1, EPI_SWIGLU>(p, rows_max, s)
-              : launch_tail_or_not<128, 128, 2, 2, 2, 32, 2, EPI_SWIGLU>(p, rows_max, s);
+      e = big ? launch_tail_or_not<256, 128, 2, 4, 2, 64, true, 1, EPI_SWIGLU>(p, rows_max, s)
+              : launch_tail_or_not<128, 128, 2, 2, 2, 32, false, 2, EPI_SWIGLU>(p, rows_max, s);
       break;
     case EPI_STORE:
-      e = big ? launch_tail_or_not<256, 256, 1, 4, 2, 64, 1, EPI_STORE>(p, rows_max, s)
-              : launch_tail_or_not<128, 256, 1, 2, 2, 32, 2, EPI_STORE>(p, rows_max, s);
+      e = big ? launch_tail_or_not<256, 256, 1, 4, 2, 64, true, 1, EPI_STORE>(p, rows_max, s)
+              : launch_tail_or_not<128, 256, 1, 2, 2, 32, false, 2, EPI_STORE>(p, rows_max, s);
       break;
     default:
-      e = launch_tail_or_not<128, 256, 1, 2, 2, 32, 1, EPI_STORE_F32_BIAS>(p, rows_max, s);
+      e = launch_tail_or_not<128, 256, 1, 2, 2, 32, false, 1, EPI_STORE_F32_BIAS>(p, rows_max, s);
   }
   if (e != hipSuccess) return e;
   if (p.ksplit > 1) launch_splitk_finish(p, rows_max, epi, s);
