@@ -147,8 +147,10 @@ moe_status moe_expert_ffn(const void* x, const int32_t* perm, const int32_t* off
  * Same row convention as moe_expert_ffn (rows r < offsets[E], t = perm[r] / k); with perm == NULL
  * (up) or offsets == NULL (down) the call is one dense group over T rows and E must be 1.  h must
  * hold T*k rows (routed) or T rows (dense).  The workspace (sized by moe_workspace_bytes) holds
- * split-K partial sums when few rows leave the GPU under-filled (decode-sized batches); the
- * result does not depend on the split.  Same errors as moe_expert_ffn.
+ * fp32 partial sums of K-split tiles: every tile when few rows leave the GPU under-filled
+ * (decode-sized batches), else the tiles of a last, partial round of tiles.  Partials are added in
+ * a fixed order, so the result does not depend on the split.  The workspace may be NULL: the
+ * GEMMs then run unsplit (same result).  Same errors as moe_expert_ffn.
  */
 moe_status moe_expert_up(const void* x, const int32_t* perm, const int32_t* offsets, int T, int d,
                          int d_ff, int E, int k, const void* w1, const void* w3, moe_dtype dt,

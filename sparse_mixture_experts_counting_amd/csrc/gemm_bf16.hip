@@ -61,8 +61,10 @@ constexpr int stage_bytes() {
 constexpr int waitcnt_lgkm0() {                    // s_waitcnt lgkmcnt(0), other counters free
   return 15 | (3 << 14) | (7 << 4) | (0 << 8);
 }
-constexpr int waitcnt_vm0_lgkm0() {                // s_waitcnt vmcnt(0) lgkmcnt(0)
-  return 0 | (0 << 14) | (7 << 4) | (0 << 8);
+template <int VM>
+constexpr int waitcnt_vm_lgkm0() {                 // s_waitcnt vmcnt(VM) lgkmcnt(0)
+  static_assert(VM >= 0 && VM < 64, "vmcnt range");
+  return (VM & 15) | ((VM >> 4) << 14) | (7 << 4) | (0 << 8);
 }
 
 __device__ __forceinline__ void barrier_no_fence() {
@@ -71,7 +73,31 @@ __device__ __forceinline__ void barrier_no_fence() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-template <int BM, int BN, int NMAT, int WGM, int WGN, int BK, bool DMA, int MINB, int EPI, bool TAIL>
+// Splitting the last round of tiles.  With `slots` blocks resident at once, total tiles run in
+// total / slots whole rounds and one partial round of `rem` tiles that would leave the rest of the
+// GPU idle; those tiles are split into q K chunks (q a power of two up to 8 with rem * q <= slots,
+// chunks a whole number of 64-deep steps), and tail_finish_kernel adds the chunks' fp32 partials in
+// a fixed order.  q == 1 runs every tile whole.
+struct TailPlan {
+  int full;   // tiles run whole (a multiple of slots, or all of them)
+  int rem;    // tiles split
+  int q;      // K chunks per split tile
+};
+
+__device__ __forceinline__ TailPlan tail_plan(int total, int slots, int K) {
+  TailPlan tp{total, 0, 1};
+  if (slots <= 0 || K % 64 != 0) return tp;
+  const int full = total / slots * slots, rem = total - full;
+  int q = 1;
+  while (q < 8 && rem * q * 2 <= slots && (K / 64) % (q * 2) == 0) q *= 2;
+  if (rem == 0 || q == 1) return tp;
+  tp.full = full;
+  tp.rem = rem;
+  tp.q = q;
+  return tp;
+}
+
+template <int BM, int BN, int NMAT, int WGM, int WGN, int BK, int NST, int MINB, int EPI, bool TAIL>
 __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_bf16_kernel(const GemmParams p) {
   constexpr int NTHR = 64 * WGM * WGN;
   constexpr int WM = BM / WGM, WN = BN / WGN;       // WGM x WGN waves
@@ -91,8 +117,10 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_bf16_kernel(const G
   static_assert(A_UNITS * NTHR == BM * UPR && B_UNITS * NTHR == NMAT * BN * UPR, "even split");
   static_assert(BN % ROWS_PER_LOAD == 0, "a load stays inside one weight matrix");
   static_assert(TM * 32 == WM && TN * 32 == WN, "32 x 32 matrix-instruction tiles");
-  // Direct-to-LDS loads: one wave-wide 16-byte load fills 1 KB of LDS (lane l at byte 16 l), i.e.
-  // DROWS rows of a stage; block b of a stage is loaded by wave b % NW.
+  // Direct-to-LDS loads (NST > 0 stages; NST == 0 stages through registers): one wave-wide
+  // 16-byte load fills 1 KB of LDS (lane l at byte 16 l), i.e. DROWS rows of a stage; block b of a
+  // stage is loaded by wave b % NW.
+  constexpr bool DMA = NST > 0;
   constexpr int NW = WGM * WGN;
   constexpr int DROWS = 1024 / RB;
   constexpr int DPW = (BM + NMAT * BN) / (DROWS * NW);   // direct loads per wave per step
@@ -104,8 +132,26 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_bf16_kernel(const G
 
   const int NT = (p.N + BN - 1) / BN;
   TileCoord tc;
-  const int kc = blockIdx.x % p.ksplit;
-  if (!find_tile<BM>(p, NT, blockIdx.x / p.ksplit, tc)) return;
+  const TileScan ts = scan_tiles<BM>(p, NT);
+  int kc = 0, nsplit = p.ksplit, rtile = -1;
+  if (p.ksplit > 1) {                       // every tile split over K
+    kc = blockIdx.x % p.ksplit;
+    const int bid = blockIdx.x / p.ksplit;
+    if (bid >= ts.total) return;
+    tile_at<BM>(p, NT, ts, xcd_order(bid, ts.total), tc);
+  } else {                                  // whole rounds as is, the last partial round split
+    const TailPlan tp = tail_plan(ts.total, p.slots, p.K);
+    if ((int)blockIdx.x < tp.full) {
+      tile_at<BM>(p, NT, ts, xcd_order(blockIdx.x, tp.full), tc);
+    } else {
+      const int w = blockIdx.x - tp.full;
+      rtile = w / tp.q;
+      kc = w % tp.q;
+      nsplit = tp.q;
+      if (rtile >= tp.rem) return;
+      tile_at<BM>(p, NT, ts, tp.full + rtile, tc);
+    }
+  }
   tc.g = __builtin_amdgcn_readfirstlane(tc.g);
   tc.row0 = __builtin_amdgcn_readfirstlane(tc.row0);
   tc.row_end = __builtin_amdgcn_readfirstlane(tc.row_end);
@@ -157,11 +203,13 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_bf16_kernel(const G
   // Direct loads: lane l of the load for stage block b = wave + NW j covers stage row
   // DROWS b + l / UPR at physical unit l % UPR, so it fetches the logical unit stored there.
   uint32_t d_voff[DMA ? DPW : 1];
+  int d_kmax[DMA ? DPW : 1];            // the load reads zeros for steps starting at k0 >= d_kmax
   if constexpr (DMA) {
 #pragma unroll
     for (int j = 0; j < DPW; ++j) {
       const int srow = (wave + NW * j) * DROWS + lane / UPR;
       const int uu = (lane % UPR) ^ swz<BK>(srow);
+      d_kmax[j] = 0;   // set below, once the K range is known
       if (j < DPW_A) {
         const int grow = min(tc.row0 + srow, tc.row_end - 1);
         const int src = p.gather ? p.gather[grow] / p.gather_div : grow;
@@ -173,11 +221,18 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_bf16_kernel(const G
     }
   }
 
-  const int Kc = K / p.ksplit;
+  const int Kc = K / nsplit;
   const int kbeg = kc * Kc;
   const int kend = kbeg + Kc;
   const int KT = (Kc + BK - 1) / BK;
   const int k_last = kbeg + (KT - 1) * BK;
+  if constexpr (DMA) {
+#pragma unroll
+    for (int j = 0; j < DPW; ++j) {
+      const int srow = (wave + NW * j) * DROWS + lane / UPR;
+      d_kmax[j] = kend - 8 * ((lane % UPR) ^ swz<BK>(srow));
+    }
+  }
 
   u32x4 a_reg[DMA ? 1 : NSETS][DMA ? 1 : A_UNITS];
   u32x4 b_reg[DMA ? 1 : NSETS][DMA ? 1 : B_UNITS];
@@ -196,18 +251,16 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_bf16_kernel(const G
           second ? rB1 : rB0, in_range ? b_voff[i] + koff : b_bytes, 0, 0);
     }
   };
+  // Direct loads of the step starting at k0 into the stage at stage_off.  Units at or past the end
+  // of this block's K range (a ragged K, or a step past the last one) are sent out of the buffer's
+  // range: they read zeros and touch no memory.
   auto issue_dma = [&](int stage_off, int k0) {
-    if constexpr (!TAIL) k0 = min(k0, k_last);
     const uint32_t koff = (uint32_t)k0 * 2u;
 #pragma unroll
     for (int j = 0; j < DPW; ++j) {
       const bool is_a = j < DPW_A;
       const bool second = NMAT == 2 && !is_a && ((j - DPW_A) * DROWS * NW) / BN == 1;
-      uint32_t voff = d_voff[j] + koff;
-      if constexpr (TAIL) {
-        const int srow = (wave + NW * j) * DROWS + lane / UPR;
-        if (k0 + 8 * ((lane % UPR) ^ swz<BK>(srow)) >= kend) voff = is_a ? a_bytes : b_bytes;
-      }
+      const uint32_t voff = k0 < d_kmax[j] ? d_voff[j] + koff : (is_a ? a_bytes : b_bytes);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(is_a ? rA : (second ? rB1 : rB0),
                                                (lds_void_t*)(smem + stage_off +
                                                              (wave + NW * j) * 1024),
@@ -270,46 +323,67 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_bf16_kernel(const G
   };
 
   if constexpr (DMA) {
-    issue_dma(0, kbeg);
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm0_lgkm0());
+    // NST-stage ring: the loads of step kt+NST-1 go into the stage that step kt-1 used, so a load
+    // has NST-1 steps to land; the barrier that ends step kt waits only for step kt+1's loads.
+#pragma unroll
+    for (int s = 0; s < NST - 1; ++s) issue_dma(s * STAGE, kbeg + s * BK);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0<DPW * (NST - 2)>());
+    barrier_no_fence();
+    read_frags(0, 0, 0);
+    int st = 0;                                   // stage of step kt
+    for (int kt = 0; kt < KT; ++kt) {
+      const int nx = st + 1 == NST ? 0 : st + 1;
+      const int fr = st == 0 ? NST - 1 : st - 1;
+      issue_dma(fr * STAGE, kbeg + (kt + NST - 1) * BK);
+#pragma unroll
+      for (int ks = 0; ks < KS - 1; ++ks) {
+        read_frags(st * STAGE, ks + 1, (ks + 1) & 1);
+        __builtin_amdgcn_sched_barrier(0);
+        mfmas(ks & 1);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0<DPW * (NST - 2)>());
+      barrier_no_fence();
+      read_frags(nx * STAGE, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      mfmas((KS - 1) & 1);
+      __builtin_amdgcn_sched_barrier(0);
+      st = nx;
+    }
   } else {
     load_regs(0, kbeg);
     if constexpr (NSETS == 2) load_regs(1, kbeg + BK);
     store_regs(0, 0);
     load_regs(0, kbeg + NSETS * BK);
     __builtin_amdgcn_s_waitcnt(waitcnt_lgkm0());
-  }
-  barrier_no_fence();
-  read_frags(0, 0, 0);
-  // One K step; S is true when kt is even (reads stage 0, fills stage 1).
-  auto step = [&](int kt, auto S) {
-    constexpr int st = decltype(S)::value ? 0 : STAGE;
-    constexpr int nx = decltype(S)::value ? STAGE : 0;
-    constexpr int set = (NSETS == 2 && decltype(S)::value) ? 1 : 0;
-    if constexpr (DMA) {
-      issue_dma(nx, kbeg + (kt + 1) * BK);              // step kt+1 straight into the idle stage
-    } else {
+    barrier_no_fence();
+    read_frags(0, 0, 0);
+    // One K step; S is true when kt is even (reads stage 0, fills stage 1).
+    auto step = [&](int kt, auto S) {
+      constexpr int st = decltype(S)::value ? 0 : STAGE;
+      constexpr int nx = decltype(S)::value ? STAGE : 0;
+      constexpr int set = (NSETS == 2 && decltype(S)::value) ? 1 : 0;
       store_regs(set, nx);                              // step kt+1 into the idle stage
       load_regs(set, kbeg + (kt + 1 + NSETS) * BK);     // and a later step into its registers
-    }
 #pragma unroll
-    for (int ks = 0; ks < KS - 1; ++ks) {
-      read_frags(st, ks + 1, (ks + 1) & 1);
+      for (int ks = 0; ks < KS - 1; ++ks) {
+        read_frags(st, ks + 1, (ks + 1) & 1);
+        __builtin_amdgcn_sched_barrier(0);
+        mfmas(ks & 1);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      __builtin_amdgcn_s_waitcnt(waitcnt_lgkm0());
+      barrier_no_fence();
+      read_frags(nx, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
-      mfmas(ks & 1);
+      mfmas((KS - 1) & 1);
       __builtin_amdgcn_sched_barrier(0);
+    };
+    // An odd step count runs one extra step; then K is ragged (TAIL) and it reads zeros.
+    for (int kt = 0; kt < KT; kt += 2) {
+      step(kt, std::true_type());
+      step(kt + 1, std::false_type());
     }
-    __builtin_amdgcn_s_waitcnt(DMA ? waitcnt_vm0_lgkm0() : waitcnt_lgkm0());
-    barrier_no_fence();
-    read_frags(nx, 0, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    mfmas((KS - 1) & 1);
-    __builtin_amdgcn_sched_barrier(0);
-  };
-  // An odd step count runs one extra step; then K is ragged (TAIL) and the extra step reads zeros.
-  for (int kt = 0; kt < KT; kt += 2) {
-    step(kt, std::true_type());
-    step(kt + 1, std::false_type());
   }
 
   // Epilogue.  Accumulator register r of a 32x32 tile holds row 8 (r / 4) + 4 (lane / 32) + r % 4
@@ -328,6 +402,11 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_bf16_kernel(const G
 #pragma unroll
           for (int m = 0; m < NMAT; ++m)
             p.part[((size_t)(kc * NMAT + m) * p.part_rows + row) * N + col] = acc[m][i][j][r];
+        } else if (rtile >= 0) {   // tile-local fp32 partials; tail_finish_kernel sums them
+#pragma unroll
+          for (int m = 0; m < NMAT; ++m)
+            p.part[(((size_t)rtile * nsplit + kc) * NMAT + m) * (BM * BN) + (row - tc.row0) * BN +
+                   (col - n_base)] = acc[m][i][j][r];
         } else if constexpr (EPI == EPI_SWIGLU) {
           const float g = acc[0][i][j][r];
           const float v = acc[NMAT - 1][i][j][r];
@@ -386,10 +465,71 @@ __global__ __launch_bounds__(256) void splitk_finish_kernel(const GemmParams p) 
   }
 }
 
-template <int BM, int BN, int NMAT, int WGM, int WGN, int BK, bool DMA, int MINB, int EPI, bool TAIL>
+// Block r finishes split tile r of the last round: sums its q chunks' partials in chunk order and
+// applies the epilogue (8 columns per item).
+template <int BM, int BN, int NMAT, int EPI>
+__global__ __launch_bounds__(256) void tail_finish_kernel(const GemmParams p) {
+  const int NT = (p.N + BN - 1) / BN;
+  const TileScan ts = scan_tiles<BM>(p, NT);
+  const TailPlan tp = tail_plan(ts.total, p.slots, p.K);
+  if ((int)blockIdx.x >= tp.rem) return;
+  TileCoord tc;
+  tile_at<BM>(p, NT, ts, tp.full + blockIdx.x, tc);
+  const int n_base = tc.n_tile * BN;
+  const float* base = p.part + (size_t)blockIdx.x * tp.q * NMAT * (BM * BN);
+  for (int e = threadIdx.x; e < BM * BN / 8; e += 256) {
+    const int lr = e / (BN / 8), lc = (e % (BN / 8)) * 8;
+    const int row = tc.row0 + lr, col = n_base + lc;
+    if (row >= tc.row_end || col >= p.N) continue;
+    float s[NMAT][8];
+#pragma unroll
+    for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+      for (int c = 0; c < 8; ++c) s[m][c] = 0.f;
+    for (int kc = 0; kc < tp.q; ++kc) {
+#pragma unroll
+      for (int m = 0; m < NMAT; ++m) {
+        const f32x4* src = reinterpret_cast<const f32x4*>(
+            base + (size_t)(kc * NMAT + m) * (BM * BN) + lr * BN + lc);
+        const f32x4 a = src[0], b = src[1];
+        s[m][0] += a[0]; s[m][1] += a[1]; s[m][2] += a[2]; s[m][3] += a[3];
+        s[m][4] += b[0]; s[m][5] += b[1]; s[m][6] += b[2]; s[m][7] += b[3];
+      }
+    }
+    u32x4 o;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      float v0, v1;
+      if constexpr (EPI == EPI_SWIGLU) {
+        const float g0 = s[0][2 * c], g1 = s[0][2 * c + 1];
+        v0 = g0 / (1.0f + expf(-g0)) * s[NMAT - 1][2 * c];
+        v1 = g1 / (1.0f + expf(-g1)) * s[NMAT - 1][2 * c + 1];
+      } else {
+        v0 = s[0][2 * c];
+        v1 = s[0][2 * c + 1];
+      }
+      o[c] = pack_bf16x2(v0, v1);
+    }
+    *reinterpret_cast<u32x4*>((uint16_t*)p.C + (size_t)row * p.ldc + col) = o;
+  }
+}
+
+static int device_cus() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) n = 0;
+    cus[dev] = n > 0 ? n : -1;
+  }
+  return cus[dev] > 0 ? cus[dev] : 0;
+}
+
+template <int BM, int BN, int NMAT, int WGM, int WGN, int BK, int NST, int MINB, int EPI, bool TAIL>
 static hipError_t launch_t(const GemmParams& p, int rows_max, hipStream_t s) {
-  auto kern = gemm_bf16_kernel<BM, BN, NMAT, WGM, WGN, BK, DMA, MINB, EPI, TAIL>;
-  const size_t lds = 2 * (size_t)stage_bytes<BM, BN, NMAT, BK>();
+  auto kern = gemm_bf16_kernel<BM, BN, NMAT, WGM, WGN, BK, NST, MINB, EPI, TAIL>;
+  const size_t lds = (NST > 0 ? NST : 2) * (size_t)stage_bytes<BM, BN, NMAT, BK>();
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute((const void*)kern,
@@ -397,18 +537,31 @@ static hipError_t launch_t(const GemmParams& p, int rows_max, hipStream_t s) {
     if (e != hipSuccess) return e;
     attr_set = true;
   }
+  GemmParams q = p;
+  // The last partial round of tiles is split over K when the epilogue allows it (bf16 output, 8
+  // columns per finishing item) and the caller gave scratch for the partials.
+  const bool tail = p.ksplit == 1 && p.part != nullptr && EPI != EPI_STORE_F32_BIAS &&
+                    p.N % 8 == 0 && p.K % 64 == 0;
+  q.slots = tail ? device_cus() * MINB : 0;
   const int NT = (p.N + BN - 1) / BN;
-  const int grid = tiles_upper_bound(rows_max, p.G, p.offsets != nullptr, BM, NT) * p.ksplit;
-  if (grid <= 0) return hipSuccess;
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * WGM * WGN), lds, s, p);
+  const int tiles = tiles_upper_bound(rows_max, p.G, p.offsets != nullptr, BM, NT);
+  const int grid = tiles * p.ksplit + q.slots;
+  if (tiles <= 0) return hipSuccess;
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * WGM * WGN), lds, s, q);
+  if (q.slots > 0) {
+    if constexpr (EPI != EPI_STORE_F32_BIAS)
+      hipLaunchKernelGGL((tail_finish_kernel<BM, BN, NMAT, EPI>), dim3(q.slots), dim3(256), 0, s,
+                         q);
+  }
   return hipGetLastError();
 }
 
-template <int BM, int BN, int NMAT, int WGM, int WGN, int BK, bool DMA, int MINB, int EPI>
+template <int BM, int BN, int NMAT, int WGM, int WGN, int BK, int NST, int MINB, int EPI>
 static hipError_t launch_tail_or_not(const GemmParams& p, int rows_max, hipStream_t s) {
-  const bool even_steps = (p.K / p.ksplit) % (2 * BK) == 0;
-  return even_steps ? launch_t<BM, BN, NMAT, WGM, WGN, BK, DMA, MINB, EPI, false>(p, rows_max, s)
-                    : launch_t<BM, BN, NMAT, WGM, WGN, BK, DMA, MINB, EPI, true>(p, rows_max, s);
+  // The direct-load path handles any K range; the register path needs an even step count.
+  const bool even_steps = NST > 0 || (p.K / p.ksplit) % (2 * BK) == 0;
+  return even_steps ? launch_t<BM, BN, NMAT, WGM, WGN, BK, NST, MINB, EPI, false>(p, rows_max, s)
+                    : launch_t<BM, BN, NMAT, WGM, WGN, BK, NST, MINB, EPI, true>(p, rows_max, s);
 }
 
 static void launch_splitk_finish(const GemmParams& p, int rows_max, int epi, hipStream_t s) {
@@ -442,11 +595,18 @@ static int splitk_factor(int rows_max, int G, bool grouped, int N, int K, int ep
   return ks;
 }
 
+// Scratch for the fp32 partial sums: every tile split (few rows), or the split tiles of the last
+// round (at most one round of blocks, each a BM x BN tile of NMAT partials; 256 KB per CU for
+// every tile configuration used here).
 size_t gemm_bf16_partial_bytes(int rows_max, int G, bool grouped, int N, int K, int epi) {
-  const int ks = splitk_factor(rows_max, G, grouped, N, K, epi);
-  if (ks == 1) return 0;
+  if (epi == EPI_STORE_F32_BIAS) return 0;
   const int nmat = epi == EPI_SWIGLU ? 2 : 1;
-  return (size_t)ks * nmat * rows_max * N * sizeof(float);
+  const int ks = splitk_factor(rows_max, G, grouped, N, K, epi);
+  if (ks > 1) return (size_t)ks * nmat * rows_max * N * sizeof(float);
+  if (N % 8 != 0 || K % 64 != 0) return 0;
+  const bool big = use_big_tiles(rows_max, G, grouped, epi);
+  const int BM = big ? 256 : 128, BN = epi == EPI_SWIGLU ? 128 : 256, minb = big ? 1 : 2;
+  return (size_t)device_cus() * minb * nmat * BM * BN * sizeof(float);
 }
 
 // Needs K a multiple of 8 (16-byte rows) and every operand under 2 GiB (32-bit buffer offsets).
@@ -464,15 +624,15 @@ hipError_t launch_gemm_bf16(const GemmParams& p_in, int rows_max, int epi, hipSt
   hipError_t e;
   switch (epi) {
     case EPI_SWIGLU:
-      e = big ? launch_tail_or_not<256, 128, 2, 4, 2, 64, true, 1, EPI_SWIGLU>(p, rows_max, s)
-              : launch_tail_or_not<128, 128, 2, 2, 2, 32, false, 2, EPI_SWIGLU>(p, rows_max, s);
+      e = big ? launch_tail_or_not<256, 128, 2, 4, 2, 64, 2, 1, EPI_SWIGLU>(p, rows_max, s)
+              : launch_tail_or_not<128, 128, 2, 2, 2, 32, 0, 2, EPI_SWIGLU>(p, rows_max, s);
       break;
     case EPI_STORE:
-      e = big ? launch_tail_or_not<256, 256, 1, 4, 2, 64, true, 1, EPI_STORE>(p, rows_max, s)
-              : launch_tail_or_not<128, 256, 1, 2, 2, 32, false, 2, EPI_STORE>(p, rows_max, s);
+      e = big ? launch_tail_or_not<256, 256, 1, 4, 2, 64, 2, 1, EPI_STORE>(p, rows_max, s)
+              : launch_tail_or_not<128, 256, 1, 2, 2, 32, 0, 2, EPI_STORE>(p, rows_max, s);
       break;
     default:
-      e = launch_tail_or_not<128, 256, 1, 2, 2, 32, false, 1, EPI_STORE_F32_BIAS>(p, rows_max, s);
+      e = launch_tail_or_not<128, 256, 1, 2, 2, 32, 0, 1, EPI_STORE_F32_BIAS>(p, rows_max, s);
   }
   if (e != hipSuccess) return e;
   if (p.ksplit > 1) launch_splitk_finish(p, rows_max, epi, s);

@@ -31,6 +31,8 @@ struct GemmParams {
   float* part;              // split-K scratch: [ksplit][NMAT][part_rows][N] fp32, or NULL
   int ksplit;               // K chunks (set by the launcher; 1 = no split)
   int part_rows;
+  int slots;                // blocks resident at once; > 0 enables splitting the last partial
+                            // round of tiles over K (set by the launcher)
 };
 
 enum { EPI_SWIGLU = 0, EPI_STORE = 1, EPI_STORE_F32_BIAS = 2 };
@@ -42,31 +44,30 @@ struct TileCoord {
   int n_tile;   // column tile index
 };
 
-// Map block `bid` to a tile.  Tiles are ordered group by group; inside a group n-tile by n-tile,
-// with the m-tiles of one n-tile consecutive (they share the same B tile).  Consecutive tiles are
-// placed on the same XCD (blocks are handed to the 8 XCDs round-robin), so the m-tiles sharing a
-// B tile also share that XCD's L2.  Returns false when bid is past the real tile count.
+// Tile bookkeeping.  Tiles are ordered group by group; inside a group n-tile by n-tile, with the
+// m-tiles of one n-tile consecutive (they share the same B tile).  scan_tiles counts them (each lane
+// of the wave takes a slice of the groups), tile_at maps a tile index to its coordinates.
+struct TileScan {
+  int total;    // number of tiles
+  int g0, g1;   // this lane's groups [g0, g1)
+  int mine;     // tiles in this lane's groups
+  int incl;     // tiles up to and including this lane's groups
+};
+
 template <int BM>
-__device__ __forceinline__ bool find_tile(const GemmParams& p, int NT, int bid, TileCoord& tc) {
-  const int lane = __lane_id();
-  int total;
+__device__ __forceinline__ TileScan scan_tiles(const GemmParams& p, int NT) {
+  TileScan s;
   if (p.offsets == nullptr) {
-    const int tm = (p.M + BM - 1) / BM;
-    total = tm * NT;
-    if (bid >= total) return false;
-    const int q = total >> 3, r = total & 7, x = bid & 7, i = bid >> 3;
-    const int t = (x < r) ? x * (q + 1) + i : r * (q + 1) + (x - r) * q + i;
-    tc.g = 0;
-    tc.row0 = (t % tm) * BM;
-    tc.n_tile = t / tm;
-    tc.row_end = p.M;
-    return true;
+    s.total = ((p.M + BM - 1) / BM) * NT;
+    s.g0 = s.g1 = s.mine = s.incl = 0;
+    return s;
   }
-  // Per-lane slice of the groups; wave-wide inclusive scan of the tile counts.
+  const int lane = __lane_id();
   const int per = (p.G + 63) >> 6;
-  const int g0 = min(p.G, lane * per), g1 = min(p.G, g0 + per);
+  s.g0 = min(p.G, lane * per);
+  s.g1 = min(p.G, s.g0 + per);
   int mine = 0;
-  for (int g = g0; g < g1; ++g) {
+  for (int g = s.g0; g < s.g1; ++g) {
     const int n = p.offsets[g + 1] - p.offsets[g];
     mine += ((n + BM - 1) / BM) * NT;
   }
@@ -76,17 +77,32 @@ __device__ __forceinline__ bool find_tile(const GemmParams& p, int NT, int bid, 
     const int u = __shfl_up(incl, o, 64);
     if (lane >= o) incl += u;
   }
-  total = __shfl(incl, 63, 64);
-  if (bid >= total) return false;
-  const int q = total >> 3, r = total & 7, x = bid & 7, i = bid >> 3;
-  const int t = (x < r) ? x * (q + 1) + i : r * (q + 1) + (x - r) * q + i;
-  const int excl = incl - mine;
-  const uint64_t own = __ballot(t >= excl && t < incl);
+  s.mine = mine;
+  s.incl = incl;
+  s.total = __shfl(incl, 63, 64);
+  return s;
+}
+
+// Tile t (< s.total) -> coordinates.  Wave-uniform t.
+template <int BM>
+__device__ __forceinline__ void tile_at(const GemmParams& p, int NT, const TileScan& s, int t,
+                                        TileCoord& tc) {
+  if (p.offsets == nullptr) {
+    const int tm = (p.M + BM - 1) / BM;
+    tc.g = 0;
+    tc.row0 = (t % tm) * BM;
+    tc.n_tile = t / tm;
+    tc.row_end = p.M;
+    return;
+  }
+  const int lane = __lane_id();
+  const int excl = s.incl - s.mine;
+  const uint64_t own = __ballot(t >= excl && t < s.incl);
   const int owner = __ffsll((long long)own) - 1;
   int g_found = 0, base = 0;
   if (lane == owner) {
     base = excl;
-    for (int g = g0; g < g1; ++g) {
+    for (int g = s.g0; g < s.g1; ++g) {
       const int n = p.offsets[g + 1] - p.offsets[g];
       const int c = ((n + BM - 1) / BM) * NT;
       if (t < base + c) {
@@ -105,6 +121,21 @@ __device__ __forceinline__ bool find_tile(const GemmParams& p, int NT, int bid, 
   tc.row0 = rs + (local % tm) * BM;
   tc.row_end = re;
   tc.n_tile = local / tm;
+}
+
+// Blocks are handed to the 8 XCDs round-robin (block b to XCD b % 8).  Give each XCD a contiguous
+// run of the n tile indices, so that the m-tiles sharing a B tile also share that XCD's L2.
+__device__ __forceinline__ int xcd_order(int bid, int n) {
+  const int q = n >> 3, r = n & 7, x = bid & 7, i = bid >> 3;
+  return (x < r) ? x * (q + 1) + i : r * (q + 1) + (x - r) * q + i;
+}
+
+// Map block `bid` to a tile in XCD order.  Returns false when bid is past the real tile count.
+template <int BM>
+__device__ __forceinline__ bool find_tile(const GemmParams& p, int NT, int bid, TileCoord& tc) {
+  const TileScan s = scan_tiles<BM>(p, NT);
+  if (bid >= s.total) return false;
+  tile_at<BM>(p, NT, s, xcd_order(bid, s.total), tc);
   return true;
 }
 

@@ -237,8 +237,8 @@ moe_status moe_expert_up(const void* x, const int32_t* perm, const int32_t* offs
   if (st != MOE_OK) return st;
   const int rows_max = perm ? T * k : T;
   const size_t need = ffn_partial_bytes(rows_max, perm != nullptr, E, d, d_ff, dt);
-  if (need && (!workspace || !aligned16(workspace))) return MOE_ERR_ARG;
-  if (ws_bytes < need) return MOE_ERR_WORKSPACE;
+  if (workspace && !aligned16(workspace)) return MOE_ERR_ARG;
+  if (workspace && ws_bytes < need) return MOE_ERR_WORKSPACE;
   hipError_t e = run_up(x, perm, offsets, T, d, d_ff, E, k, w1, w3, dt == MOE_BF16, h,
                         need ? workspace : nullptr, (hipStream_t)stream);
   return e != hipSuccess ? MOE_ERR_DEVICE : launched();
@@ -251,8 +251,8 @@ moe_status moe_expert_down(const void* h, const int32_t* offsets, int T, int d, 
   if (st != MOE_OK) return st;
   const int rows_max = offsets ? T * k : T;
   const size_t need = ffn_partial_bytes(rows_max, offsets != nullptr, E, d, d_ff, dt);
-  if (need && (!workspace || !aligned16(workspace))) return MOE_ERR_ARG;
-  if (ws_bytes < need) return MOE_ERR_WORKSPACE;
+  if (workspace && !aligned16(workspace)) return MOE_ERR_ARG;
+  if (workspace && ws_bytes < need) return MOE_ERR_WORKSPACE;
   hipError_t e = run_down(h, offsets, T, d, d_ff, E, k, w2, dt == MOE_BF16, out,
                           need ? workspace : nullptr, (hipStream_t)stream);
   return e != hipSuccess ? MOE_ERR_DEVICE : launched();

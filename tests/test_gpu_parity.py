@@ -207,6 +207,9 @@ SWEEP = [
     # at least 512 rows per expert: 256-row tiles (8 waves), ragged and even K, N past one tile
     (2600, 136, 2, 2, 264, "bf16", "softmax_all", 0, 0, 0.0),
     (2048, 128, 2, 1, 320, "bf16", "softmax_topk", 0, 1, 0.0),
+    # more tiles than one round of blocks: whole rounds plus a K-split last round
+    (2048, 512, 8, 2, 2048, "bf16", "softmax_topk", 0, 0, 0.0),
+    (2048, 256, 64, 2, 1024, "bf16", "sigmoid_topk", 0, 0, 0.0),
 ]
 
 
