@@ -160,8 +160,12 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_bf16_kernel(const G
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm0 = (wave % WGM) * WM;
-  const int wn0 = (wave / WGM) * WN;
+  // N-fastest wave layout: waves w and w + 4, which share a SIMD, own different row slices, so a
+  // tile whose valid rows end in its first half (a group's ragged last tile) keeps every SIMD's
+  // matrix core busy with only one of its two waves.
+  const int wm0 = (wave / WGN) * WM;
+  const int wn0 = (wave % WGN) * WN;
+  static_assert(WGM * WGN <= 4 || WGN == 2, "row slices spread over the SIMDs");
   const int n_base = tc.n_tile * BN;
   const int K = p.K, N = p.N;
 
@@ -322,69 +326,95 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_bf16_kernel(const G
                                                                  acc[m][i][j], 0, 0, 0);
   };
 
+  // A wave whose row slice lies wholly past the group's end only takes its share of the loads and
+  // the barriers (the loop is instantiated twice, so that neither copy branches inside).
+  const bool active = tc.row0 + wm0 < tc.row_end;
   if constexpr (DMA) {
     // NST-stage ring: the loads of step kt+NST-1 go into the stage that step kt-1 used, so a load
     // has NST-1 steps to land; the barrier that ends step kt waits only for step kt+1's loads.
+    auto run = [&](auto MATH) {
+      constexpr bool math = decltype(MATH)::value;
 #pragma unroll
-    for (int s = 0; s < NST - 1; ++s) issue_dma(s * STAGE, kbeg + s * BK);
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0<DPW * (NST - 2)>());
-    barrier_no_fence();
-    read_frags(0, 0, 0);
-    int st = 0;                                   // stage of step kt
-    for (int kt = 0; kt < KT; ++kt) {
-      const int nx = st + 1 == NST ? 0 : st + 1;
-      const int fr = st == 0 ? NST - 1 : st - 1;
-      issue_dma(fr * STAGE, kbeg + (kt + NST - 1) * BK);
-#pragma unroll
-      for (int ks = 0; ks < KS - 1; ++ks) {
-        read_frags(st * STAGE, ks + 1, (ks + 1) & 1);
-        __builtin_amdgcn_sched_barrier(0);
-        mfmas(ks & 1);
-        __builtin_amdgcn_sched_barrier(0);
-      }
+      for (int s = 0; s < NST - 1; ++s) issue_dma(s * STAGE, kbeg + s * BK);
       __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0<DPW * (NST - 2)>());
       barrier_no_fence();
-      read_frags(nx * STAGE, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
-      mfmas((KS - 1) & 1);
-      __builtin_amdgcn_sched_barrier(0);
-      st = nx;
-    }
-  } else {
-    load_regs(0, kbeg);
-    if constexpr (NSETS == 2) load_regs(1, kbeg + BK);
-    store_regs(0, 0);
-    load_regs(0, kbeg + NSETS * BK);
-    __builtin_amdgcn_s_waitcnt(waitcnt_lgkm0());
-    barrier_no_fence();
-    read_frags(0, 0, 0);
-    // One K step; S is true when kt is even (reads stage 0, fills stage 1).
-    auto step = [&](int kt, auto S) {
-      constexpr int st = decltype(S)::value ? 0 : STAGE;
-      constexpr int nx = decltype(S)::value ? STAGE : 0;
-      constexpr int set = (NSETS == 2 && decltype(S)::value) ? 1 : 0;
-      store_regs(set, nx);                              // step kt+1 into the idle stage
-      load_regs(set, kbeg + (kt + 1 + NSETS) * BK);     // and a later step into its registers
+      if constexpr (math) read_frags(0, 0, 0);
+      int st = 0;                                   // stage of step kt
+      for (int kt = 0; kt < KT; ++kt) {
+        const int nx = st + 1 == NST ? 0 : st + 1;
+        const int fr = st == 0 ? NST - 1 : st - 1;
+        issue_dma(fr * STAGE, kbeg + (kt + NST - 1) * BK);
+        if constexpr (math) {
 #pragma unroll
-      for (int ks = 0; ks < KS - 1; ++ks) {
-        read_frags(st, ks + 1, (ks + 1) & 1);
-        __builtin_amdgcn_sched_barrier(0);
-        mfmas(ks & 1);
-        __builtin_amdgcn_sched_barrier(0);
+          for (int ks = 0; ks < KS - 1; ++ks) {
+            read_frags(st * STAGE, ks + 1, (ks + 1) & 1);
+            __builtin_amdgcn_sched_barrier(0);
+            mfmas(ks & 1);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0<DPW * (NST - 2)>());
+        barrier_no_fence();
+        if constexpr (math) {
+          read_frags(nx * STAGE, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+          mfmas((KS - 1) & 1);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        st = nx;
       }
+    };
+    if (active)
+      run(std::true_type());
+    else
+      run(std::false_type());
+  } else {
+    auto run = [&](auto MATH) {
+      constexpr bool math = decltype(MATH)::value;
+      load_regs(0, kbeg);
+      if constexpr (NSETS == 2) load_regs(1, kbeg + BK);
+      store_regs(0, 0);
+      load_regs(0, kbeg + NSETS * BK);
       __builtin_amdgcn_s_waitcnt(waitcnt_lgkm0());
       barrier_no_fence();
-      read_frags(nx, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
-      mfmas((KS - 1) & 1);
-      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (math) read_frags(0, 0, 0);
+      // One K step; S is true when kt is even (reads stage 0, fills stage 1).
+      auto step = [&](int kt, auto S) {
+        constexpr int st = decltype(S)::value ? 0 : STAGE;
+        constexpr int nx = decltype(S)::value ? STAGE : 0;
+        constexpr int set = (NSETS == 2 && decltype(S)::value) ? 1 : 0;
+        store_regs(set, nx);                              // step kt+1 into the idle stage
+        load_regs(set, kbeg + (kt + 1 + NSETS) * BK);     // and a later step into its registers
+        if constexpr (math) {
+#pragma unroll
+          for (int ks = 0; ks < KS - 1; ++ks) {
+            read_frags(st, ks + 1, (ks + 1) & 1);
+            __builtin_amdgcn_sched_barrier(0);
+            mfmas(ks & 1);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+        __builtin_amdgcn_s_waitcnt(waitcnt_lgkm0());
+        barrier_no_fence();
+        if constexpr (math) {
+          read_frags(nx, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+          mfmas((KS - 1) & 1);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      };
+      // An odd step count runs one extra step; then K is ragged (TAIL) and it reads zeros.
+      for (int kt = 0; kt < KT; kt += 2) {
+        step(kt, std::true_type());
+        step(kt + 1, std::false_type());
+      }
     };
-    // An odd step count runs one extra step; then K is ragged (TAIL) and it reads zeros.
-    for (int kt = 0; kt < KT; kt += 2) {
-      step(kt, std::true_type());
-      step(kt + 1, std::false_type());
-    }
+    if (active)
+      run(std::true_type());
+    else
+      run(std::false_type());
   }
+  if (!active) return;
 
   // Epilogue.  Accumulator register r of a 32x32 tile holds row 8 (r / 4) + 4 (lane / 32) + r % 4
   // and column lane % 32.
@@ -465,19 +495,23 @@ __global__ __launch_bounds__(256) void splitk_finish_kernel(const GemmParams p) 
   }
 }
 
-// Block r finishes split tile r of the last round: sums its q chunks' partials in chunk order and
-// applies the epilogue (8 columns per item).
+// Blocks kFinishSplit r .. +kFinishSplit-1 finish split tile r of the last round, a slice of rows
+// each: they sum the q chunks' partials in chunk order and apply the epilogue (8 columns per item).
+static constexpr int kFinishSplit = 8;
+
 template <int BM, int BN, int NMAT, int EPI>
 __global__ __launch_bounds__(256) void tail_finish_kernel(const GemmParams p) {
   const int NT = (p.N + BN - 1) / BN;
   const TileScan ts = scan_tiles<BM>(p, NT);
   const TailPlan tp = tail_plan(ts.total, p.slots, p.K);
-  if ((int)blockIdx.x >= tp.rem) return;
+  const int r = blockIdx.x / kFinishSplit, slice = blockIdx.x % kFinishSplit;
+  if (r >= tp.rem) return;
   TileCoord tc;
-  tile_at<BM>(p, NT, ts, tp.full + blockIdx.x, tc);
+  tile_at<BM>(p, NT, ts, tp.full + r, tc);
   const int n_base = tc.n_tile * BN;
-  const float* base = p.part + (size_t)blockIdx.x * tp.q * NMAT * (BM * BN);
-  for (int e = threadIdx.x; e < BM * BN / 8; e += 256) {
+  const float* base = p.part + (size_t)r * tp.q * NMAT * (BM * BN);
+  constexpr int ITEMS = BM * BN / 8 / kFinishSplit;
+  for (int e = slice * ITEMS + threadIdx.x; e < (slice + 1) * ITEMS; e += 256) {
     const int lr = e / (BN / 8), lc = (e % (BN / 8)) * 8;
     const int row = tc.row0 + lr, col = n_base + lc;
     if (row >= tc.row_end || col >= p.N) continue;
@@ -550,8 +584,8 @@ static hipError_t launch_t(const GemmParams& p, int rows_max, hipStream_t s) {
   hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * WGM * WGN), lds, s, q);
   if (q.slots > 0) {
     if constexpr (EPI != EPI_STORE_F32_BIAS)
-      hipLaunchKernelGGL((tail_finish_kernel<BM, BN, NMAT, EPI>), dim3(q.slots), dim3(256), 0, s,
-                         q);
+      hipLaunchKernelGGL((tail_finish_kernel<BM, BN, NMAT, EPI>), dim3(q.slots * kFinishSplit),
+                         dim3(256), 0, s, q);
   }
   return hipGetLastError();
 }
