@@ -613,20 +613,48 @@ static void launch_splitk_finish(const GemmParams& p, int rows_max, int epi, hip
 // experts, decode) keep 128-row tiles so that ragged group ends waste less.
 static bool use_big_tiles(int rows_max, int G, bool grouped, int epi) {
   if (epi == EPI_STORE_F32_BIAS) return false;
-  return rows_max >= 512 * (grouped ? std::max(G, 1) : 1);
+  return rows_max >= 256 * (grouped ? std::max(G, 1) : 1);
 }
 
-// K chunks for the expert GEMMs: when the tile grid would leave CUs idle (few rows, e.g. decode),
-// split K so that about 1024 blocks run, keeping every chunk a whole number of 64-deep steps.
+// K chunks for the expert GEMMs when the tiles alone would fill less than two rounds of the
+// resident blocks (few rows per expert, e.g. decode).  Compute-bound shapes take the smallest
+// power-of-two split (chunks a
+// whole number of 64-deep steps) whose work items fill at least one round with the rounds at
+// least 90% busy on average, else the split that keeps them busiest (or, when no split fills a
+// round, the largest).
 static int splitk_factor(int rows_max, int G, bool grouped, int N, int K, int epi) {
   if (epi == EPI_STORE_F32_BIAS || K % 64 != 0 || N % 8 != 0) return 1;
   if (use_big_tiles(rows_max, G, grouped, epi)) return 1;
   const int BM = 128, BN = (epi == EPI_SWIGLU) ? 128 : 256;
   const int mt = grouped ? std::min(G, rows_max) + rows_max / BM : (rows_max + BM - 1) / BM;
   const long long tiles = (long long)mt * ((N + BN - 1) / BN);
-  int ks = 1;
-  while (ks < 16 && tiles * ks * 2 <= 1024 && (K / 64) % (ks * 2) == 0) ks *= 2;
-  return ks;
+  const int cus = device_cus();
+  const long long slots = 2ll * (cus > 0 ? cus : 256);   // two 128-row blocks per CU
+  if (tiles >= 2 * slots) return 1;
+  // Fewer rows than a tile per group: weight streaming, bound by HBM; any full round keeps HBM
+  // busy, so split only as far as one round needs (fewer partial sums to add).
+  if ((grouped ? rows_max / std::max(G, 1) : rows_max) < BM) {
+    int ks = 1;
+    while (ks < 16 && tiles * ks < slots && (K / 64) % (ks * 2) == 0) ks *= 2;
+    return ks;
+  }
+  auto busy = [&](long long items) {                    // mean occupancy of the rounds
+    const long long rounds = (items + slots - 1) / slots;
+    return (double)items / (double)(rounds * slots);
+  };
+  int best = 1, largest = 1;
+  double best_busy = tiles >= slots ? busy(tiles) : 0.0;
+  for (int ks = 1; ks <= 16 && (K / 64) % ks == 0; ks *= 2) {
+    const long long items = tiles * ks;
+    largest = ks;
+    if (items < slots) continue;
+    if (busy(items) >= 0.9) return ks;
+    if (busy(items) > best_busy + 0.02) {
+      best = ks;
+      best_busy = busy(items);
+    }
+  }
+  return best_busy > 0.0 ? best : largest;   // no split fills a round: split the most
 }
 
 // Scratch for the fp32 partial sums: every tile split (few rows), or the split tiles of the last
