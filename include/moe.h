@@ -79,10 +79,11 @@ const char* moe_status_str(moe_status s);
  *                     load-balancing loss, in every gating mode)
  *   lse_sq_sum[0]     sum over tokens of logsumexp(row t)^2 (the z-loss numerator)
  *
- * x [T,d] and w_r [E,d] (the [out][in] weight of the bias-free linear layer that the dineshblog
- * page, section 1.2, declares as the router) in dtype `dt`; logit_bias [E] fp32 or NULL; logits [T,E] fp32 (output, or
- * input with MOE_ROUTE_LOGITS_IN, in which case x and w_r may be NULL and logit_bias must be
- * NULL); topk_idx [T,k] int32; topk_gate [T,k] fp32; prob_sum [E] fp32; lse_sq_sum [1] fp32.
+ * x [T,d] row-major and w_r the d x E router matrix stored column-major (w_r[e*d + j] holds
+ * element (j, e): the [out][in] weight of the bias-free linear layer that the dineshblog page,
+ * section 1.2, declares as the router), both in dtype `dt`; logit_bias [E] fp32 or NULL; logits
+ * [T,E] fp32 (output, or input with MOE_ROUTE_LOGITS_IN, in which case x and w_r may be NULL and
+ * logit_bias must be NULL); topk_idx [T,k] int32; topk_gate [T,k] fp32; prob_sum [E] fp32; lse_sq_sum [1] fp32.
  * prob_sum and lse_sq_sum may be NULL.  Non-finite logits violate the precondition: routing is then
  * unspecified but memory-safe (indices stay in [0,E) and distinct within a row).
  * Results are bitwise deterministic run to run.
@@ -125,11 +126,13 @@ moe_status moe_dispatch(const int32_t* topk_idx, int T, int E, int k, int capaci
  * (row r = token r; E must be 1 and offsets may be NULL): this is how a shared, always-on expert
  * runs (the starphix page, Expert Architectures: Shared + Specialized).
  *
- * x [T,d]; w1, w3 [E][d_ff][d]; w2 [E][d][d_ff]: each expert's matrices in the [out][in] layout of
- * the bias-free linear layers that the dineshblog page, section 1.1, declares, so both GEMM
- * operands are contiguous along the reduced dimension; out [T*k][d] (routed) or [T][d] (perm
- * NULL); all in dtype `dt`.  d and d_ff must be multiples of 8.  h is kept in the workspace in dtype `dt` (bf16 layers round h to bf16 before the
- * down projection; accumulation is fp32).  For few rows per expert the K dimension is split over
+ * x [T,d] row-major.  Expert e's matrices have the pages' shapes, w1 and w3 d x d_ff and w2
+ * d_ff x d, each stored column-major: w1[(e*d_ff + n)*d + j] holds element (j, n) of w1_e, and
+ * w2[(e*d + i)*d_ff + n] element (n, i) of w2_e.  That is the [out][in] weight layout of the
+ * bias-free linear layers that the dineshblog page, section 1.1, declares, and it keeps both GEMM
+ * operands contiguous along the reduced dimension.  out [T*k][d] (routed) or [T][d] (perm NULL);
+ * all in dtype `dt`.  d and d_ff must be multiples of 8.  h is kept in the workspace in dtype `dt`
+ * (bf16 layers round h to bf16 before the down projection; accumulation is fp32).  For few rows per expert the K dimension is split over
  * several blocks whose fp32 partial sums (also in the workspace) are added in a fixed order, so
  * results are deterministic.
  */

@@ -1,0 +1,109 @@
+"""Summaries of rocprofv3 output for the committed profiles.
+
+    python -m sparse_mixture_experts_counting_amd.profsum stats KERNEL_STATS_CSV TITLE COMMAND
+        Markdown table of per-kernel calls and durations (microseconds) from a
+        `rocprofv3 --kernel-trace --stats` run.
+
+    python -m sparse_mixture_experts_counting_amd.profsum traffic FETCH_CSV WRITE_CSV WORKLOAD KERNEL \
+            OUT_JSON COMMAND
+        HBM bytes per launch of the kernels whose name contains KERNEL, from two
+        `rocprofv3 --pmc FETCH_SIZE` / `--pmc WRITE_SIZE` runs (KiB per dispatch), each scaled by
+        what the same counter reads for the benchmark's untimed 256 MiB device copy (the
+        calibration).  Writes OUT_JSON (read by bench.py) and prints a Markdown summary.
+"""
+
+import collections
+import csv
+import hashlib
+import json
+import os
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+KERNEL_SRC = os.path.join(ROOT, "sparse_mixture_experts_counting_amd", "csrc", "gemm_bf16.hip")
+CALIB_BYTES = 256 << 20          # the benchmark's calibration copy (bytes read and written)
+
+
+def source_hash():
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def stats(path, title, command):
+    rows = list(csv.DictReader(open(path)))
+    out = ["# Kernel time: %s" % title, "", "Command (run from /tmp with TMPDIR=/tmp on one MI355X; "
+           "repository at $R):", "", "    " + command, "",
+           "| kernel | calls | avg us | min us | max us | % of GPU time |", "|---|---|---|---|---|---|"]
+    for r in rows:
+        name = r["Name"].split("(")[0]
+        out.append("| `%s` | %s | %.1f | %.1f | %.1f | %.2f |" % (
+            name, r["Calls"], float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
+            float(r["MaxNs"]) / 1e3, float(r["Percentage"])))
+    return "\n".join(out) + "\n"
+
+
+def _per_kernel(path):
+    vals = collections.defaultdict(list)
+    for r in csv.DictReader(open(path)):
+        vals[r["Kernel_Name"]].append(float(r["Counter_Value"]))
+    return vals
+
+
+def traffic(fetch_csv, write_csv, workload, kernel, out_json, command):
+    fetch, write = _per_kernel(fetch_csv), _per_kernel(write_csv)
+
+    def calib(vals):   # the largest copy: the benchmark's 256 MiB calibration copy
+        best = max((max(v) for k, v in vals.items() if "copyBuffer" in k or "copy_kernel" in k),
+                   default=0.0)
+        if best <= 0:
+            raise SystemExit("no copy kernel found for the calibration")
+        return CALIB_BYTES / (best * 1024.0), best
+
+    f_scale, f_cal = calib(fetch)
+    w_scale, w_cal = calib(write)
+    # KERNEL may name several kernels joined by '+' (one operation's kernels); their averages add.
+    picked = []
+    for part in kernel.split("+"):
+        names = [k for k in fetch if part in k]
+        if not names:
+            raise SystemExit("kernel %r not in %s" % (part, fetch_csv))
+        picked.append(names[0])
+    fk = sum(sum(fetch[n]) / len(fetch[n]) for n in picked)
+    wk = sum(sum(write.get(n, [0.0])) / max(1, len(write.get(n, []))) for n in picked)
+    hbm = fk * 1024.0 * f_scale + wk * 1024.0 * w_scale
+    rec = {"workload": workload, "kernel": " + ".join(n.split("(")[0] for n in picked),
+           "kernel_source_sha256_16": source_hash(),
+           "fetch_kib_per_launch": fk, "write_kib_per_launch": wk,
+           "calibration": {"bytes": CALIB_BYTES, "fetch_kib": f_cal, "write_kib": w_cal,
+                           "fetch_scale": f_scale, "write_scale": w_scale},
+           "hbm_bytes_per_launch": hbm, "command": command}
+    with open(out_json, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    md = ["# HBM traffic: %s, `%s`" % (workload, rec["kernel"]), "",
+          "Commands (run from /tmp with TMPDIR=/tmp on one MI355X; repository at $R):", "",
+          "    " + command.replace("COUNTER", "FETCH_SIZE"),
+          "    " + command.replace("COUNTER", "WRITE_SIZE"), "",
+          "| quantity | value |", "|---|---|",
+          "| FETCH_SIZE per launch | %.0f KiB |" % fk,
+          "| WRITE_SIZE per launch | %.0f KiB |" % wk,
+          "| 256 MiB calibration copy: FETCH_SIZE / WRITE_SIZE | %.0f / %.0f KiB |" % (f_cal, w_cal),
+          "| scale applied (fetch, write) | %.4f, %.4f |" % (f_scale, w_scale),
+          "| HBM bytes per launch | %.3f GB |" % (hbm / 1e9),
+          "| kernel source sha256[:16] | %s |" % rec["kernel_source_sha256_16"]]
+    return "\n".join(md) + "\n"
+
+
+def main(argv):
+    if len(argv) >= 4 and argv[0] == "stats":
+        sys.stdout.write(stats(argv[1], argv[2], " ".join(argv[3:])))
+    elif len(argv) >= 7 and argv[0] == "traffic":
+        sys.stdout.write(traffic(argv[1], argv[2], argv[3], argv[4], argv[5], " ".join(argv[6:])))
+    else:
+        sys.stderr.write(__doc__)
+        return 2
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main(sys.argv[1:]))
