@@ -53,6 +53,12 @@ __device__ __forceinline__ int swz(int r) {
     return (r ^ ((r >> 3) & 3)) & 7;    // 128-byte rows: eight units
 }
 
+// silu(g) = g / (1 + e^-g) with the hardware base-2 exponential and reciprocal (about 1 ulp each;
+// the result is rounded to bf16).  Saturates to g for large g and to -0 for very negative g.
+__device__ __forceinline__ float silu(float g) {
+  return g * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * g));
+}
+
 template <int BM, int BN, int NMAT, int BK>
 constexpr int stage_bytes() {
   return (BM + NMAT * BN) * BK * 2;
@@ -418,6 +424,41 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_bf16_kernel(const G
 
   // Epilogue.  Accumulator register r of a 32x32 tile holds row 8 (r / 4) + 4 (lane / 32) + r % 4
   // and column lane % 32.
+  const bool partial = p.ksplit > 1 || rtile >= 0;
+  if (EPI != EPI_STORE_F32_BIAS && !partial && N % 2 == 0 && p.ldc % 2 == 0) {
+    // bf16 output, two columns per 4-byte store: lanes 2c and 2c+1 swap one value of each pair of
+    // rows (a DPP quad permute), so the even lane holds row a and the odd lane row b of columns
+    // (2c, 2c+1).
+    const bool odd = lane & 1;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int col0 = n_base + wn0 + j * 32 + (l32 & ~1);
+        float v[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          if constexpr (EPI == EPI_SWIGLU)
+            v[r] = silu(acc[0][i][j][r]) * acc[NMAT - 1][i][j][r];
+          else
+            v[r] = acc[0][i][j][r];
+        }
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+          const float send = odd ? v[r] : v[r + 1];
+          const float got = __builtin_bit_cast(
+              float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, send), 0xB1, 0xF, 0xF, false));
+          const int rr = odd ? r + 1 : r;
+          const int row = tc.row0 + wm0 + i * 32 + 8 * (rr >> 2) + 4 * h + (rr & 3);
+          if (row < tc.row_end && col0 < N) {
+            const uint32_t packed = odd ? pack_bf16x2(got, v[r + 1]) : pack_bf16x2(v[r], got);
+            *(uint32_t*)((uint16_t*)p.C + (size_t)row * p.ldc + col0) = packed;
+          }
+        }
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
 #pragma unroll
@@ -440,7 +481,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_bf16_kernel(const G
         } else if constexpr (EPI == EPI_SWIGLU) {
           const float g = acc[0][i][j][r];
           const float v = acc[NMAT - 1][i][j][r];
-          ((uint16_t*)p.C)[(size_t)row * p.ldc + col] = f32_to_bf16(g / (1.0f + expf(-g)) * v);
+          ((uint16_t*)p.C)[(size_t)row * p.ldc + col] = f32_to_bf16(silu(g) * v);
         } else if constexpr (EPI == EPI_STORE) {
           ((uint16_t*)p.C)[(size_t)row * p.ldc + col] = f32_to_bf16(acc[0][i][j][r]);
         } else {
@@ -483,8 +524,8 @@ __global__ __launch_bounds__(256) void splitk_finish_kernel(const GemmParams p) 
       float v0, v1;
       if constexpr (EPI == EPI_SWIGLU) {
         const float g0 = s[0][2 * q], g1 = s[0][2 * q + 1];
-        v0 = g0 / (1.0f + expf(-g0)) * s[NMAT - 1][2 * q];
-        v1 = g1 / (1.0f + expf(-g1)) * s[NMAT - 1][2 * q + 1];
+        v0 = silu(g0) * s[NMAT - 1][2 * q];
+        v1 = silu(g1) * s[NMAT - 1][2 * q + 1];
       } else {
         v0 = s[0][2 * q];
         v1 = s[0][2 * q + 1];
@@ -536,8 +577,8 @@ __global__ __launch_bounds__(256) void tail_finish_kernel(const GemmParams p) {
       float v0, v1;
       if constexpr (EPI == EPI_SWIGLU) {
         const float g0 = s[0][2 * c], g1 = s[0][2 * c + 1];
-        v0 = g0 / (1.0f + expf(-g0)) * s[NMAT - 1][2 * c];
-        v1 = g1 / (1.0f + expf(-g1)) * s[NMAT - 1][2 * c + 1];
+        v0 = silu(g0) * s[NMAT - 1][2 * c];
+        v1 = silu(g1) * s[NMAT - 1][2 * c + 1];
       } else {
         v0 = s[0][2 * c];
         v1 = s[0][2 * c + 1];
