@@ -34,6 +34,7 @@
 #include "kernels.h"
 
 #include <algorithm>
+#include <climits>
 #include <type_traits>
 
 namespace moe {
@@ -240,7 +241,10 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_bf16_kernel(const G
 #pragma unroll
     for (int j = 0; j < DPW; ++j) {
       const int srow = (wave + NW * j) * DROWS + lane / UPR;
-      d_kmax[j] = kend - 8 * ((lane % UPR) ^ swz<BK>(srow));
+      // Rows past the group's end (A) or past N (B) feed only results that are never stored:
+      // they read zeros without touching memory.
+      const bool live = j < DPW_A ? tc.row0 + srow < tc.row_end : n_base + (srow - BM) % BN < N;
+      d_kmax[j] = live ? kend - 8 * ((lane % UPR) ^ swz<BK>(srow)) : INT_MIN;
     }
   }
 
@@ -728,11 +732,11 @@ hipError_t launch_gemm_bf16(const GemmParams& p_in, int rows_max, int epi, hipSt
   switch (epi) {
     case EPI_SWIGLU:
       e = big ? launch_tail_or_not<256, 128, 2, 4, 2, 64, 2, 1, EPI_SWIGLU>(p, rows_max, s)
-              : launch_tail_or_not<128, 128, 2, 2, 2, 32, 0, 2, EPI_SWIGLU>(p, rows_max, s);
+              : launch_tail_or_not<128, 128, 2, 2, 2, 32, 3, 2, EPI_SWIGLU>(p, rows_max, s);
       break;
     case EPI_STORE:
       e = big ? launch_tail_or_not<256, 256, 1, 4, 2, 64, 2, 1, EPI_STORE>(p, rows_max, s)
-              : launch_tail_or_not<128, 256, 1, 2, 2, 32, 0, 2, EPI_STORE>(p, rows_max, s);
+              : launch_tail_or_not<128, 256, 1, 2, 2, 32, 3, 2, EPI_STORE>(p, rows_max, s);
       break;
     default:
       e = launch_tail_or_not<128, 256, 1, 2, 2, 32, 0, 1, EPI_STORE_F32_BIAS>(p, rows_max, s);
