@@ -10,82 +10,92 @@ namespace moe {
 
 // ---------------------------------------------------------------------------------------------
 // Router product for E <= 16 experts: logits[t, e] = sum_j x[t, j] w_r[e, j] (+ bias[e]), W_r in
-// the [E][d] layout of a linear layer.  Memory bound on x; one wave handles TPW tokens, lanes
-// stride over 8-wide slices of d, and each lane reads the matching 8 values of every W_r row
-// (16-byte aligned: d is a multiple of 8).
+// the [E][d] layout of a linear layer.  Memory bound on x.  A block of 4 waves takes TPB = 64 / EP
+// tokens (EP = E rounded up to a power of two, at least 4), so that its TPB x EP (token, expert)
+// sums are one per lane; the waves split d in four, and lanes stride over 8-wide slices of their
+// quarter (16-byte loads of x and of every W_r row; d is a multiple of 8).  Each lane's 64 partial
+// sums are reduced across the wave by a butterfly that halves the values a lane carries at every
+// step (63 lane exchanges in all), leaving lane l with the total of sum l; the four waves' totals
+// are added in a fixed order.
 // ---------------------------------------------------------------------------------------------
-template <typename TIn, int E, int TPW>
+template <int E>
+constexpr int pow2_at_least() {      // at least 4, so that a block takes at most 16 tokens
+  return E <= 4 ? 4 : E <= 8 ? 8 : 16;
+}
+
+template <typename TIn>
+__device__ __forceinline__ void load8(const TIn* p, float* f) {
+  if constexpr (sizeof(TIn) == 2) {
+    unpack8(*reinterpret_cast<const u32x4*>(p), f);
+  } else {
+    const f32x4 a = reinterpret_cast<const f32x4*>(p)[0], b = reinterpret_cast<const f32x4*>(p)[1];
+    f[0] = a[0]; f[1] = a[1]; f[2] = a[2]; f[3] = a[3];
+    f[4] = b[0]; f[5] = b[1]; f[6] = b[2]; f[7] = b[3];
+  }
+}
+
+template <typename TIn, int E>
 __global__ __launch_bounds__(256) void router_small_e_kernel(const TIn* __restrict__ x,
                                                              const TIn* __restrict__ w_r,
                                                              const float* __restrict__ bias, int T,
                                                              int d, float* __restrict__ logits) {
+  constexpr int EP = pow2_at_least<E>();
+  constexpr int TPB = 64 / EP;
+  __shared__ float part[4][64];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int t0 = (blockIdx.x * 4 + wave) * TPW;
-  if (t0 >= T) return;
-  float acc[TPW][E];
+  const int t0 = blockIdx.x * TPB;
+  float v[64];                                   // v[i * EP + e]: token t0 + i, expert e
 #pragma unroll
-  for (int i = 0; i < TPW; ++i)
-#pragma unroll
-    for (int e = 0; e < E; ++e) acc[i][e] = 0.f;
+  for (int q = 0; q < 64; ++q) v[q] = 0.f;
 
   const int nchunk = d >> 3;
-  for (int c = lane; c < nchunk; c += 64) {
+  const int per = (nchunk + 3) >> 2;
+  const int c_end = min(nchunk, (wave + 1) * per);
+  for (int c = wave * per + lane; c < c_end; c += 64) {
     float w[E][8];
 #pragma unroll
-    for (int e = 0; e < E; ++e) {
-      if constexpr (sizeof(TIn) == 2) {
-        unpack8(*reinterpret_cast<const u32x4*>(w_r + (size_t)e * d + c * 8), w[e]);
-      } else {
-        const f32x4* src = reinterpret_cast<const f32x4*>(w_r + (size_t)e * d + c * 8);
-        const f32x4 a = src[0], b = src[1];
-        w[e][0] = a[0]; w[e][1] = a[1]; w[e][2] = a[2]; w[e][3] = a[3];
-        w[e][4] = b[0]; w[e][5] = b[1]; w[e][6] = b[2]; w[e][7] = b[3];
-      }
-    }
+    for (int e = 0; e < E; ++e) load8(w_r + (size_t)e * d + c * 8, w[e]);
 #pragma unroll
-    for (int i = 0; i < TPW; ++i) {
+    for (int i = 0; i < TPB; ++i) {
       const int t = t0 + i;
       if (t < T) {
         float xv[8];
-        if constexpr (sizeof(TIn) == 2) {
-          u32x4 q = *reinterpret_cast<const u32x4*>(x + (size_t)t * d + c * 8);
-          unpack8(q, xv);
-        } else {
-          const f32x4* p = reinterpret_cast<const f32x4*>(x + (size_t)t * d + c * 8);
-          f32x4 a = p[0], b = p[1];
-          xv[0] = a[0]; xv[1] = a[1]; xv[2] = a[2]; xv[3] = a[3];
-          xv[4] = b[0]; xv[5] = b[1]; xv[6] = b[2]; xv[7] = b[3];
-        }
+        load8(x + (size_t)t * d + c * 8, xv);
 #pragma unroll
         for (int kk = 0; kk < 8; ++kk)
 #pragma unroll
-          for (int e = 0; e < E; ++e) acc[i][e] = fmaf(xv[kk], w[e][kk], acc[i][e]);
+          for (int e = 0; e < E; ++e) v[i * EP + e] = fmaf(xv[kk], w[e][kk], v[i * EP + e]);
       }
     }
   }
+  // Butterfly: at offset o a lane keeps the half of its 2 o values selected by bit o of its lane
+  // id and adds the partner's copy of that half.
 #pragma unroll
-  for (int i = 0; i < TPW; ++i)
+  for (int o = 32; o >= 1; o >>= 1) {
+    const bool upper = lane & o;
 #pragma unroll
-    for (int e = 0; e < E; ++e) acc[i][e] = wave_sum(acc[i][e]);
-  if (lane == 0) {
-#pragma unroll
-    for (int i = 0; i < TPW; ++i) {
-      const int t = t0 + i;
-      if (t < T) {
-#pragma unroll
-        for (int e = 0; e < E; ++e) logits[(size_t)t * E + e] = acc[i][e] + (bias ? bias[e] : 0.f);
-      }
+    for (int q = 0; q < o; ++q) {
+      const float send = upper ? v[q] : v[o + q];
+      const float keep = upper ? v[o + q] : v[q];
+      v[q] = keep + __shfl_xor(send, o, 64);
     }
+  }
+  part[wave][lane] = v[0];
+  __syncthreads();
+  if (wave == 0) {
+    const float sum = ((part[0][lane] + part[1][lane]) + part[2][lane]) + part[3][lane];
+    const int t = t0 + lane / EP, e = lane % EP;
+    if (t < T && e < E) logits[(size_t)t * E + e] = sum + (bias ? bias[e] : 0.f);
   }
 }
 
 template <typename TIn, int E>
 static void launch_router_small_e_t(const void* x, const void* w_r, const float* bias, int T,
                                     int d, float* logits, hipStream_t s) {
-  constexpr int TPW = 4;
-  const int blocks = (T + 4 * TPW - 1) / (4 * TPW);
-  hipLaunchKernelGGL((router_small_e_kernel<TIn, E, TPW>), dim3(blocks), dim3(256), 0, s,
+  constexpr int TPB = 64 / pow2_at_least<E>();
+  const int blocks = (T + TPB - 1) / TPB;
+  hipLaunchKernelGGL((router_small_e_kernel<TIn, E>), dim3(blocks), dim3(256), 0, s,
                      (const TIn*)x, (const TIn*)w_r, bias, T, d, logits);
 }
 
