@@ -54,14 +54,15 @@ def load_traffic(workload):
     return t.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(cfg, inp, n_tokens):
+def cpu_baseline(cfg, inp, n_tokens, repeats):
     """The CPU oracle (float64 NumPy, as it stands) on the first n_tokens tokens of the same
-    workload.  Returns tokens/s, BLAS threads used and a description of the sample."""
+    workload (all of them when n_tokens <= 0), run `repeats` times.  Returns tokens/s, BLAS
+    threads used, a description of the sample and the seconds spent."""
     import numpy as np
     from oracle import moe_oracle as O
     from threadpoolctl import threadpool_info
 
-    n = min(n_tokens, cfg.T)
+    n = cfg.T if n_tokens <= 0 else min(n_tokens, cfg.T)
     f = lambda t: t.detach().float().cpu().numpy()
     x = f(inp.x[:n])
     w_r = f(inp.w_r)
@@ -78,14 +79,15 @@ def cpu_baseline(cfg, inp, n_tokens):
     if cap > 0:   # same capacity factor on the smaller batch
         cap = max(1, int(math.ceil(cap * n / cfg.T)))
     t0 = time.perf_counter()
-    O.forward(x, w_r, w1, w3, w2, cfg.k, mode, capacity=cap, bias=bias, shared=shared,
-              alpha=cfg.alpha, beta=cfg.beta)
+    for _ in range(repeats):
+        O.forward(x, w_r, w1, w3, w2, cfg.k, mode, capacity=cap, bias=bias, shared=shared,
+                  alpha=cfg.alpha, beta=cfg.beta)
     dt = time.perf_counter() - t0
     threads = max([p.get("num_threads", 1) for p in threadpool_info()
                    if p.get("user_api") == "blas"] or [1])
     sample = ("first %d of %d tokens of %s, all steps of the layer, float64 NumPy oracle "
-              "(%d experts touched)" % (n, cfg.T, cfg.name, len(used)))
-    return n / dt, threads, sample, dt
+              "(%d experts touched), %d runs" % (n, cfg.T, cfg.name, len(used), repeats))
+    return n * repeats / dt, threads, sample, dt
 
 
 def main():
@@ -95,7 +97,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="mixtral_prefill")
     ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--cpu-sample-tokens", type=int, default=3072)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=0,
+                    help="tokens of the workload the CPU oracle runs on (0: all)")
+    ap.add_argument("--cpu-repeats", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
 
@@ -211,7 +215,8 @@ def main():
         "config": {"workload": cfg.name, "T": T, "d": d, "E": E, "k": k, "d_ff": f,
                    "gating": cfg.gating, "capacity": cfg.capacity or None,
                    "shared_experts": cfg.n_shared, "parallelism": "none (1 GPU)"},
-        "roofline": {"bound": "mfma", "kernel": "moe_expert_up (gemm_bf16 SwiGLU)",
+        "roofline": {"bound": "mfma",
+                     "kernel": "moe_expert_up: gemm_bf16_kernel (SwiGLU epilogue) + tail_finish_kernel",
                      "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic},
         "grouped_gemm": {"ms": gg_ms, "tflops": (up_flops + down_flops) / (gg_ms * 1e-3) / 1e12,
@@ -226,7 +231,7 @@ def main():
     del h
     if not args.no_cpu_baseline:
         log("bench: timing the CPU oracle on a sample")
-        v, threads, sample, secs = cpu_baseline(cfg, inp, args.cpu_sample_tokens)
+        v, threads, sample, secs = cpu_baseline(cfg, inp, args.cpu_sample_tokens, args.cpu_repeats)
         result["cpu_baseline"] = {"value": v, "unit": "tokens/s", "cores": threads,
                                   "kind": "oracle", "sample": sample, "seconds": secs}
     else:

@@ -29,13 +29,28 @@ def source_hash():
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
+def short_name(name):
+    """Kernel name without its argument list (the last parenthesised group that ends the name)."""
+    name = name.strip()
+    if not name.endswith(")"):
+        return name
+    depth = 0
+    for i in range(len(name) - 1, -1, -1):
+        depth += {")": 1, "(": -1}.get(name[i], 0)
+        if depth == 0:
+            return name[:i].rstrip() or name
+    return name
+
+
 def stats(path, title, command):
     rows = list(csv.DictReader(open(path)))
     out = ["# Kernel time: %s" % title, "", "Command (run from /tmp with TMPDIR=/tmp on one MI355X; "
            "repository at $R):", "", "    " + command, "",
            "| kernel | calls | avg us | min us | max us | % of GPU time |", "|---|---|---|---|---|---|"]
     for r in rows:
-        name = r["Name"].split("(")[0]
+        name = short_name(r["Name"])
+        if len(name) > 100:
+            name = name[:97] + "..."
         out.append("| `%s` | %s | %.1f | %.1f | %.1f | %.2f |" % (
             name, r["Calls"], float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
             float(r["MaxNs"]) / 1e3, float(r["Percentage"])))
@@ -71,7 +86,7 @@ def traffic(fetch_csv, write_csv, workload, kernel, out_json, command):
     fk = sum(sum(fetch[n]) / len(fetch[n]) for n in picked)
     wk = sum(sum(write.get(n, [0.0])) / max(1, len(write.get(n, []))) for n in picked)
     hbm = fk * 1024.0 * f_scale + wk * 1024.0 * w_scale
-    rec = {"workload": workload, "kernel": " + ".join(n.split("(")[0] for n in picked),
+    rec = {"workload": workload, "kernel": " + ".join(short_name(n) for n in picked),
            "kernel_source_sha256_16": source_hash(),
            "fetch_kib_per_launch": fk, "write_kib_per_launch": wk,
            "calibration": {"bytes": CALIB_BYTES, "fetch_kib": f_cal, "write_kib": w_cal,
