@@ -132,9 +132,9 @@ moe_status moe_dispatch(const int32_t* topk_idx, int T, int E, int k, int capaci
  * bias-free linear layers that the dineshblog page, section 1.1, declares, and it keeps both GEMM
  * operands contiguous along the reduced dimension.  out [T*k][d] (routed) or [T][d] (perm NULL);
  * all in dtype `dt`.  d and d_ff must be multiples of 8.  h is kept in the workspace in dtype `dt`
- * (bf16 layers round h to bf16 before the down projection; accumulation is fp32).  For few rows per expert the K dimension is split over
- * several blocks whose fp32 partial sums (also in the workspace) are added in a fixed order, so
- * results are deterministic.
+ * (bf16 layers round h to bf16 before the down projection; accumulation is fp32).  When the tiles
+ * would leave the GPU under-filled, K is split over several blocks whose fp32 partial sums (also in
+ * the workspace) are added in a fixed order, so results are bitwise deterministic run to run.
  */
 moe_status moe_expert_ffn(const void* x, const int32_t* perm, const int32_t* offsets, int T, int d,
                           int d_ff, int E, int k, const void* w1, const void* w3, const void* w2,
@@ -152,8 +152,9 @@ moe_status moe_expert_ffn(const void* x, const int32_t* perm, const int32_t* off
  * hold T*k rows (routed) or T rows (dense).  The workspace (sized by moe_workspace_bytes) holds
  * fp32 partial sums of K-split tiles: every tile when few rows leave the GPU under-filled
  * (decode-sized batches), else the tiles of a last, partial round of tiles.  Partials are added in
- * a fixed order, so the result does not depend on the split.  The workspace may be NULL: the
- * GEMMs then run unsplit (same result).  Same errors as moe_expert_ffn.
+ * a fixed order, so results are bitwise deterministic run to run; a split changes only the order of
+ * the fp32 sums.  The workspace may be NULL: the GEMMs then run unsplit (equal up to that rounding
+ * order).  Same errors as moe_expert_ffn.
  */
 moe_status moe_expert_up(const void* x, const int32_t* perm, const int32_t* offsets, int T, int d,
                          int d_ff, int E, int k, const void* w1, const void* w3, moe_dtype dt,
@@ -187,6 +188,20 @@ moe_status moe_combine(const void* expert_out, const int32_t* inv, const float* 
 moe_status moe_aux_loss(const int32_t* counts, const float* prob_sum, const float* lse_sq_sum,
                         int T, int E, int k, float alpha, float beta, float* aux, float* z,
                         void* stream);
+
+/*
+ * moe_transpose -- weight layout conversion, outside the per-call path.  For b < batch:
+ *
+ *   dst[b][c][r] = src[b][r][c]      src [batch][rows][cols], dst [batch][cols][rows], dtype `dt`
+ *
+ * i.e. the column-major storage of a row-major rows x cols matrix.  Weights held row-major in the
+ * pages' shapes (w1, w3: d x d_ff; w2: d_ff x d; W_r: d x E) become the arrays moe_route and
+ * moe_expert_ffn take: call it once when the weights are loaded.  src and dst must not overlap.
+ * Enqueues on `stream`; MOE_ERR_ARG for null pointers or non-positive sizes, MOE_ERR_UNSUPPORTED
+ * when batch*rows*cols does not fit in 64-bit or a grid dimension exceeds 65535 blocks.
+ */
+moe_status moe_transpose(const void* src, int batch, int rows, int cols, moe_dtype dt, void* dst,
+                         void* stream);
 
 #ifdef __cplusplus
 }

@@ -35,4 +35,8 @@ void launch_combine(const void* expert_out, const int32_t* inv, const float* gat
 void launch_aux_loss(const int32_t* counts, const float* prob_sum, const float* lse_sq_sum, int T,
                      int E, int k, float alpha, float beta, float* aux, float* z, hipStream_t s);
 
+// transpose.hip
+void launch_transpose(const void* src, int batch, int rows, int cols, int elem_bytes, void* dst,
+                      hipStream_t s);
+
 }  // namespace moe

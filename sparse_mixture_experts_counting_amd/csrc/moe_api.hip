@@ -284,4 +284,14 @@ moe_status moe_aux_loss(const int32_t* counts, const float* prob_sum, const floa
   return launched();
 }
 
+moe_status moe_transpose(const void* src, int batch, int rows, int cols, moe_dtype dt, void* dst,
+                         void* stream) {
+  if (!src || !dst || batch < 1 || rows < 1 || cols < 1 || !dtype_ok(dt)) return MOE_ERR_ARG;
+  if ((rows + 63) / 64 > 65535 || batch > 65535) return MOE_ERR_UNSUPPORTED;
+  const long long elems = (long long)batch * rows * cols;
+  if (elems / batch / rows != cols) return MOE_ERR_UNSUPPORTED;
+  moe::launch_transpose(src, batch, rows, cols, (int)elem_bytes(dt), dst, (hipStream_t)stream);
+  return launched();
+}
+
 }  // extern "C"

@@ -21,7 +21,7 @@ STATUS = {0: "MOE_OK", 1: "MOE_ERR_ARG", 2: "MOE_ERR_UNSUPPORTED", 3: "MOE_ERR_W
           4: "MOE_ERR_DEVICE"}
 
 EXPORTS = ("moe_workspace_bytes", "moe_status_str", "moe_route", "moe_dispatch", "moe_expert_ffn",
-           "moe_expert_up", "moe_expert_down", "moe_combine", "moe_aux_loss")
+           "moe_expert_up", "moe_expert_down", "moe_combine", "moe_aux_loss", "moe_transpose")
 
 
 class MoEError(RuntimeError):
@@ -47,8 +47,9 @@ _lib.moe_expert_up.argtypes = [_p, _p, _p, _i, _i, _i, _i, _i, _p, _p, _i, _p, _
 _lib.moe_expert_down.argtypes = [_p, _p, _i, _i, _i, _i, _i, _p, _i, _p, _p, _sz, _p]
 _lib.moe_combine.argtypes = [_p, _p, _p, _i, _i, _i, _i, _p, _p, _p]
 _lib.moe_aux_loss.argtypes = [_p, _p, _p, _i, _i, _i, _f, _f, _p, _p, _p]
+_lib.moe_transpose.argtypes = [_p, _i, _i, _i, _i, _p, _p]
 for _n in ("moe_route", "moe_dispatch", "moe_expert_ffn", "moe_expert_up", "moe_expert_down",
-           "moe_combine", "moe_aux_loss"):
+           "moe_combine", "moe_aux_loss", "moe_transpose"):
     getattr(_lib, _n).restype = _i
 
 
@@ -136,3 +137,9 @@ def aux_loss(counts, prob_sum, lse_sq_sum, T, E, k, alpha, beta, aux, z, stream=
     _check("moe_aux_loss", _lib.moe_aux_loss(
         _ptr(counts), _ptr(prob_sum), _ptr(lse_sq_sum), T, E, k, float(alpha), float(beta),
         _ptr(aux), _ptr(z), _stream(stream)))
+
+
+def transpose(src, batch, rows, cols, dt, dst, stream=None):
+    """dst[b][c][r] = src[b][r][c] (weight layout conversion, at load time)."""
+    _check("moe_transpose", _lib.moe_transpose(_ptr(src), batch, rows, cols, dt, _ptr(dst),
+                                               _stream(stream)))

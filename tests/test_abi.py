@@ -29,7 +29,7 @@ def test_every_declared_symbol_is_exported(lm):
     names = _declared()
     assert set(names) == {"moe_workspace_bytes", "moe_status_str", "moe_route", "moe_dispatch",
                           "moe_expert_ffn", "moe_expert_up", "moe_expert_down", "moe_combine",
-                          "moe_aux_loss"}
+                          "moe_aux_loss", "moe_transpose"}
     lib = ctypes.CDLL(lm.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -115,3 +115,14 @@ def test_combine_and_loss_argument_errors(lm):
     f = ctypes.c_float
     assert L.moe_aux_loss(FAKE, FAKE, FAKE, 0, 4, 2, f(0.01), f(1e-3), FAKE, FAKE, None) == 1
     assert L.moe_aux_loss(FAKE, None, FAKE, 4, 4, 2, f(0.01), f(1e-3), FAKE, FAKE, None) == 1
+
+
+def test_transpose_argument_errors(lm):
+    L = lm.lib()
+    assert L.moe_transpose(None, 1, 4, 4, 1, FAKE, None) == 1
+    assert L.moe_transpose(FAKE, 1, 4, 4, 1, None, None) == 1
+    assert L.moe_transpose(FAKE, 0, 4, 4, 1, FAKE, None) == 1
+    assert L.moe_transpose(FAKE, 1, 4, -1, 1, FAKE, None) == 1
+    assert L.moe_transpose(FAKE, 1, 4, 4, 7, FAKE, None) == 1
+    assert L.moe_transpose(FAKE, 70000, 4, 4, 1, FAKE, None) == 2
+    assert L.moe_transpose(FAKE, 1, 64 * 65536, 4, 1, FAKE, None) == 2

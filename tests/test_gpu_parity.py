@@ -254,3 +254,47 @@ def test_error_codes_on_device(M):
         lm.expert_ffn(x, b.perm, b.offsets, 16, 12, 16, 4, 2, x, x, x, lm.MOE_BF16, b.expert_out,
                       b.workspace)
     assert ei.value.status == 2
+
+
+@pytest.mark.parametrize("batch,rows,cols", [(1, 8, 8), (3, 37, 100), (2, 130, 70), (1, 4096, 14)])
+@pytest.mark.parametrize("dt", ["bf16", "fp32"])
+def test_transpose_exact(M, batch, rows, cols, dt):
+    """moe_transpose gives the column-major storage of each row-major matrix, bit for bit."""
+    _say("transpose", batch, rows, cols, dt)
+    lm = M["lm"]
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+    g = torch.Generator().manual_seed(rows * 131 + cols)
+    src = torch.randn((batch, rows, cols), generator=g).to(tdt).cuda()
+    dst = torch.full((batch, cols, rows), float("nan"), dtype=tdt, device="cuda")
+    lm.transpose(src, batch, rows, cols, lm.MOE_BF16 if dt == "bf16" else lm.MOE_F32, dst)
+    torch.cuda.synchronize()
+    ref = src.transpose(1, 2).contiguous()
+    assert torch.equal(dst.view(torch.uint8) if dt == "bf16" else dst.view(torch.int32),
+                       ref.view(torch.uint8) if dt == "bf16" else ref.view(torch.int32))
+
+
+def test_expert_halves_split_and_unsplit(M):
+    """moe_expert_up/down with the workspace (K-split tiles) and without (unsplit) agree to within
+    fp32 summation order, and each is bitwise repeatable."""
+    _say("expert halves with and without workspace")
+    lm, synth, layer = M["lm"], M["synth"], M["layer"]
+    cfg = synth.tiny_config(300, 128, 8, 2, 192, "bf16")
+    inp = _to_cuda(synth.make_inputs(cfg, seed=5, device="cpu"))
+    b = layer.alloc_buffers(cfg)
+    layer.route(cfg, inp, b)
+    layer.dispatch(cfg, b)
+    rows = cfg.T * cfg.k
+    outs = {}
+    for name, ws in (("split", b.workspace), ("split_again", b.workspace), ("unsplit", None)):
+        h = torch.empty((rows, cfg.d_ff), dtype=torch.bfloat16, device="cuda")
+        out = torch.empty((rows, cfg.d), dtype=torch.bfloat16, device="cuda")
+        lm.expert_up(inp.x, b.perm, b.offsets, cfg.T, cfg.d, cfg.d_ff, cfg.E, cfg.k, inp.w1,
+                     inp.w3, lm.MOE_BF16, h, ws)
+        lm.expert_down(h, b.offsets, cfg.T, cfg.d, cfg.d_ff, cfg.E, cfg.k, inp.w2, lm.MOE_BF16,
+                       out, ws)
+        torch.cuda.synchronize()
+        outs[name] = out[: int(b.offsets[-1].item())].float()
+    assert torch.equal(outs["split"], outs["split_again"])
+    ref = outs["unsplit"]
+    err = (outs["split"] - ref).abs().max().item() / max(ref.abs().max().item(), 1e-30)
+    assert err <= 2e-2, err
