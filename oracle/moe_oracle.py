@@ -12,8 +12,9 @@ Pages (cited by title and section; nothing here copies their code):
              ("How it works" steps 1-6; "Code": route, dispatch, aux_loss, z_loss, combine, main;
              "Complexity and constants"; "Implementation notes").
   [dinesh]   "DL S077 - Mixture of Experts (MoE) Intuition" -- dineshblog.com/blog/session-dl-077-moe
-             (1.1 What an "expert" is; 2 Top-k gating, step by step; 3.1 The auxiliary loss;
-             3.2 Why not just enforce balance?; 4 The parameter-count arithmetic).
+             (1.1 What an "expert" is; 1.2 What the router computes; 2 Top-k gating, step by
+             step; 3.1 The auxiliary loss; 3.2 Why not just enforce balance?; 4 The
+             parameter-count arithmetic; 8.2 DeepSeek-V2 -> V3 -> R1).
   [starphix] "Mixture of Experts (MoE)" -- learn.starphix.com ... ModelArchitectures/Mixture-of-Experts.md
              (Key Equations; Top-k Gating; Expert Architectures: Shared + Specialized).
   [vanos]    "Mixture of Experts (MoE)" -- vanos001.github.io/placement_prep/llm/moe
@@ -21,7 +22,8 @@ Pages (cited by title and section; nothing here copies their code):
 
 Readings taken where the pages are silent or disagree (each one is also listed with its reason in
 the design notes of this repository):
-  * W_r is [d, E] and logits = x . W_r ([tirogla] How it works); no biases except an explicit
+  * W_r is the d x E matrix of [tirogla] How it works, held as its [E, d] transpose (the weight of
+    the bias-free linear router of [dinesh] 1.2), logits = x . W_r; no biases except an explicit
     per-expert logit bias input.
   * Ranking is always on the float32 logits, descending, equal logits to the lower expert index
     first (the stable sort of [tirogla] Code `route`); -0.0 == +0.0; -inf ranks last; NaN rejected.
@@ -36,6 +38,12 @@ the design notes of this repository):
   * y excludes the residual; a dropped assignment contributes 0 ([tirogla] step 5).
   * A shared expert is added to every token with weight 1 ([starphix] Shared + Specialized).
   * token(a) = floor(a / k) for assignment a = t*k + s ([tirogla] Code `combine`).
+  * Aux-loss-free balancing ([tirogla] Implementation notes; [dinesh] 8.2): a per-expert selection
+    bias is added (float32) to the logits used for ranking only; gates, P and z use the logits.
+    After a step each bias moves by a fixed `rate` towards balance: +rate when the expert's load is
+    below the mean T*k/E, -rate above it, 0 at it.  [dinesh] 9 mentions an exponential moving
+    average of relative load instead; the fixed-size nudge is the plainer reading of "nudge it up
+    or down by load" and is the one built.
 
 Pins: every function here is checked by the CPU tests against page-printed values (the worked
 top-2 example of [dinesh] section 2), closed forms, invariants stated on the pages, library
@@ -72,13 +80,19 @@ def router_logits(x, w_r, bias=None):
     return L.astype(np.float32)
 
 
-def select_topk(logits, k):
+def select_topk(logits, k, select_bias=None):
     """Top-k experts per token, [tirogla] How it works step 2 (Select) and Code `route`.
 
     Each row is ordered by a stable descending sort on its float32 logits (equal logits keep the
     lower expert index first) and the first k are kept, in that order.  Returns int32 [T, k].
+
+    select_bias (float32 [E] or None): aux-loss-free balancing ([tirogla] Implementation notes;
+    [dinesh] 8.2): the ranking uses the float32 sum logit + select_bias[e]; the gates do not (see
+    gate_weights, which takes the logits alone).
     """
     L = np.asarray(logits, dtype=np.float32)
+    if select_bias is not None:
+        L = L + np.asarray(select_bias, dtype=np.float32)[None, :]   # one float32 rounding
     if L.ndim != 2:
         raise ValueError("logits must be [T, E]")
     T, E = L.shape
@@ -242,12 +256,13 @@ def z_loss(lse_sq_sum, T, beta):
 
 
 def forward(x, w_r, w1, w3, w2, k, mode, capacity=None, bias=None, shared=None,
-            alpha=0.01, beta=1e-3, logits=None):
+            alpha=0.01, beta=1e-3, logits=None, select_bias=None):
     """The whole layer, steps in the order of [tirogla] How it works (Score, Select, Dispatch,
     Compute, Combine, Balance).
 
     x [T, d]; w_r [E, d]; w1, w3 [E, d_ff, d]; w2 [E, d, d_ff]; shared = (w1s, w3s, w2s) or None.
-    `logits` (float32 [T, E]) replaces the router product when given.
+    `logits` (float32 [T, E]) replaces the router product when given; `select_bias` (float32 [E])
+    biases the ranking only (aux-loss-free balancing).
     Returns a dict of every intermediate (float64 except the integer dispatch outputs).
     """
     x = np.asarray(x)
@@ -256,7 +271,7 @@ def forward(x, w_r, w1, w3, w2, k, mode, capacity=None, bias=None, shared=None,
         logits = router_logits(x, w_r, bias)
     logits = np.asarray(logits, dtype=np.float32)
     E = logits.shape[1]
-    idx = select_topk(logits, k)
+    idx = select_topk(logits, k, select_bias)
     gate = gate_weights(logits, idx, mode)
     p, lse = row_softmax_lse(logits)
     counts, offsets, perm, inv, n_dropped = dispatch(idx, E, capacity)
@@ -272,6 +287,19 @@ def forward(x, w_r, w1, w3, w2, k, mode, capacity=None, bias=None, shared=None,
                 perm=perm, inv=inv, n_dropped=n_dropped, expert_out=rows, shared_out=shared_out,
                 y=y, aux=aux_loss(counts, prob_sum, T, E, k, alpha),
                 z=z_loss(lse_sq_sum, T, beta))
+
+
+def update_select_bias(select_bias, counts, T, E, k, rate):
+    """One aux-loss-free balancing step ([tirogla] Implementation notes: nudge each expert's
+    selection bias up or down after each step by its load; [dinesh] 8.2: up when the expert is
+    under-used, down when over-used).  Reading: the nudge has a fixed size `rate` and the sign of
+    (mean load - load), the mean load being T*k/E assignments (counts before capacity):
+
+        b_e <- b_e + rate * sign(T*k - E*counts_e)        (float32, one rounding)
+    """
+    c = np.asarray(counts, dtype=np.int64)
+    sgn = np.sign(np.int64(T) * np.int64(k) - np.int64(E) * c).astype(np.float32)
+    return (np.asarray(select_bias, dtype=np.float32) + np.float32(rate) * sgn).astype(np.float32)
 
 
 def capacity_from_factor(cf, T, k, E):

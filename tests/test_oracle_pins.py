@@ -356,3 +356,73 @@ def test_flop_accounting_matches_page_parameter_counts():
     assert round(E * per_expert / 1e9, 2) == g["params_all_experts_billions"]
     assert round(d * E / 1e3) == g["router_params_thousands"]
     assert O.routed_flops(1, d, E, f, 1) - 2 * d * E == 2 * per_expert
+
+
+# ------------------------------------------------------------ aux-loss-free balancing (selection bias)
+
+
+def test_select_bias_zero_is_plain_selection():
+    rng = np.random.default_rng(21)
+    L = rng.normal(size=(50, 12)).astype(np.float32)
+    for k in (1, 3, 12):
+        np.testing.assert_array_equal(O.select_topk(L, k, np.zeros(12, np.float32)),
+                                      O.select_topk(L, k))
+
+
+@pytest.mark.parametrize("k", [1, 2, 5])
+def test_select_bias_ranks_on_biased_scores_bruteforce(k):
+    """Selection with a bias equals rank-counting selection on the float32 scores logit + bias."""
+    rng = np.random.default_rng(22 + k)
+    L = rng.normal(size=(40, 9)).astype(np.float32)
+    L[3, :] = 0.25                                   # ties broken by the biases, then by index
+    b = rng.normal(0, 0.5, size=9).astype(np.float32)
+    b[4] = b[5]
+    scores = (L + b[None, :]).astype(np.float32)
+    np.testing.assert_array_equal(O.select_topk(L, k, b), bf.rank_select(scores, k))
+
+
+@pytest.mark.parametrize("mode", [0, 1, 2])
+def test_select_bias_steers_selection_but_not_gates(mode):
+    """A large bias forces its expert into every top-k; the gates are still those of the logits
+    (gates_alt evaluates them from the logits alone), not of the biased scores."""
+    rng = np.random.default_rng(30 + mode)
+    T, E, k = 25, 6, 2
+    L = rng.normal(size=(T, E)).astype(np.float32)
+    b = np.zeros(E, np.float32)
+    b[5] = 1e4
+    idx = O.select_topk(L, k, b)
+    assert np.all(idx[:, 0] == 5)
+    np.testing.assert_array_equal(idx[:, 1], O.select_topk(L[:, :5], 1)[:, 0])
+    g = O.gate_weights(L, idx, mode)
+    np.testing.assert_allclose(g, bf.gates_alt(L, idx, mode), rtol=1e-12, atol=1e-15)
+    if mode != 1:
+        g_biased = O.gate_weights((L + b).astype(np.float32), idx, mode)
+        assert np.abs(g - g_biased).max() > 1e-3
+
+
+def test_update_select_bias_closed_form():
+    """Counts (5, 3, 0, 4) with T*k = 12 over E = 4 experts: mean load 3, so the nudges are
+    (-1, 0, +1, -1) times the rate."""
+    b = O.update_select_bias(np.float32([0.5, -1.0, 0.0, 2.0]), np.int32([5, 3, 0, 4]), T=6, E=4,
+                             k=2, rate=0.25)
+    assert b.dtype == np.float32
+    np.testing.assert_array_equal(b, np.float32([0.25, -1.0, 0.25, 1.75]))
+
+
+def test_select_bias_updates_balance_a_skewed_router():
+    """Repeated select -> count -> nudge on a router that prefers expert 0 evens out the loads
+    (the direction of the nudge: a sign error would make the skew worse)."""
+    rng = np.random.default_rng(40)
+    T, E, k = 256, 8, 2
+    pref = np.float32([1.5, 1.0, 0.5, 0.0, 0.0, -0.5, -1.0, -1.5])
+    L = (rng.normal(size=(T, E)) * 0.5 + pref[None, :]).astype(np.float32)
+    b = np.zeros(E, np.float32)
+    counts0 = np.bincount(O.select_topk(L, k).reshape(-1), minlength=E)
+    for _ in range(300):
+        counts = np.bincount(O.select_topk(L, k, b).reshape(-1), minlength=E)
+        b = O.update_select_bias(b, counts, T, E, k, rate=0.01)
+    counts = np.bincount(O.select_topk(L, k, b).reshape(-1), minlength=E)
+    mean = T * k / E
+    assert counts0.max() > 2 * mean
+    assert counts.max() < 1.25 * mean and counts.min() > 0.75 * mean
+    assert b[0] < 0 < b[7]
