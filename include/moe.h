@@ -70,9 +70,13 @@ const char* moe_status_str(moe_status s);
  * the worked top-2 example of the dineshblog page, section 2).
  *
  *   logits[t,e] = sum_j x[t,j] * w_r[e,j] + logit_bias[e]      (fp32 accumulate)
- *   topk_idx[t,0..k)  the k largest logits of row t, in descending order; equal logits go to the
- *                     lower expert index first; -0.0 equals +0.0; -inf ranks last.
- *   topk_gate[t,s]    SOFTMAX_TOPK: exp(L_e - m) / sum_sel exp(L_s - m), m = row max
+ *   topk_idx[t,0..k)  the k largest scores of row t, in descending order; equal scores go to the
+ *                     lower expert index first; -0.0 equals +0.0; -inf ranks last.  The score is
+ *                     the logit, or logit + select_bias[e] (one fp32 add) when select_bias is
+ *                     given: aux-loss-free balancing, which biases the selection only (the tirogla
+ *                     page, Implementation notes; the dineshblog page, section 8.2).
+ *   topk_gate[t,s]    from the logits, never the selection bias:
+ *                     SOFTMAX_TOPK: exp(L_e - m) / sum_sel exp(L_s - m), m = row max
  *                     SOFTMAX_ALL:  exp(L_e - m) / sum_all exp(L_j - m)
  *                     SIGMOID_TOPK: sigmoid(L_e) / sum_sel sigmoid(L_s)
  *   prob_sum[e]       sum over tokens of the full-row softmax p[t,e] (the P_e numerator of the
@@ -81,17 +85,20 @@ const char* moe_status_str(moe_status s);
  *
  * x [T,d] row-major and w_r the d x E router matrix stored column-major (w_r[e*d + j] holds
  * element (j, e): the [out][in] weight of the bias-free linear layer that the dineshblog page,
- * section 1.2, declares as the router), both in dtype `dt`; logit_bias [E] fp32 or NULL; logits
- * [T,E] fp32 (output, or input with MOE_ROUTE_LOGITS_IN, in which case x and w_r may be NULL and
- * logit_bias must be NULL); topk_idx [T,k] int32; topk_gate [T,k] fp32; prob_sum [E] fp32; lse_sq_sum [1] fp32.
+ * section 1.2, declares as the router), both in dtype `dt`; logit_bias [E] fp32 or NULL (added to
+ * the logits, so seen by selection, gates, P and z); select_bias [E] fp32 or NULL (selection
+ * only); logits [T,E] fp32 (output, or input with MOE_ROUTE_LOGITS_IN, in which case x and w_r may
+ * be NULL and logit_bias must be NULL); topk_idx [T,k] int32; topk_gate [T,k] fp32; prob_sum [E]
+ * fp32; lse_sq_sum [1] fp32.
  * prob_sum and lse_sq_sum may be NULL.  Non-finite logits violate the precondition: routing is then
  * unspecified but memory-safe (indices stay in [0,E) and distinct within a row).
  * Results are bitwise deterministic run to run.
  */
-moe_status moe_route(const void* x, const void* w_r, const float* logit_bias, int T, int d, int E,
-                     int k, moe_dtype dt, moe_gating gating, unsigned flags, float* logits,
-                     int32_t* topk_idx, float* topk_gate, float* prob_sum, float* lse_sq_sum,
-                     void* workspace, size_t ws_bytes, void* stream);
+moe_status moe_route(const void* x, const void* w_r, const float* logit_bias,
+                     const float* select_bias, int T, int d, int E, int k, moe_dtype dt,
+                     moe_gating gating, unsigned flags, float* logits, int32_t* topk_idx,
+                     float* topk_gate, float* prob_sum, float* lse_sq_sum, void* workspace,
+                     size_t ws_bytes, void* stream);
 
 /*
  * moe_dispatch -- Dispatch (the tirogla page, How it works step 3 and Code `dispatch`; capacity and
@@ -188,6 +195,19 @@ moe_status moe_combine(const void* expert_out, const int32_t* inv, const float* 
 moe_status moe_aux_loss(const int32_t* counts, const float* prob_sum, const float* lse_sq_sum,
                         int T, int E, int k, float alpha, float beta, float* aux, float* z,
                         void* stream);
+
+/*
+ * moe_update_select_bias -- one aux-loss-free balancing step after a layer call (the tirogla page,
+ * Implementation notes: nudge each selection bias up or down after each step by load; the
+ * dineshblog page, section 8.2: up when the expert is under-used, down when over-used):
+ *
+ *   select_bias[e] += rate * sign(T*k - E*counts[e])      in place, fp32
+ *
+ * i.e. a fixed-size step towards the mean load T*k/E (counts from moe_dispatch, before capacity).
+ * counts [E] int32, select_bias [E] fp32, device memory.
+ */
+moe_status moe_update_select_bias(const int32_t* counts, int T, int E, int k, float rate,
+                                  float* select_bias, void* stream);
 
 /*
  * moe_transpose -- weight layout conversion, outside the per-call path.  For b < batch:

@@ -109,4 +109,23 @@ void launch_aux_loss(const int32_t* counts, const float* prob_sum, const float* 
                      k, alpha, beta, aux, z);
 }
 
+// Aux-loss-free balancing step: b_e += rate * sign(T*k - E*counts_e) (integer comparison of the
+// load with the mean load T*k/E; one float32 add).  The tirogla page, Implementation notes; the
+// DL S077 page, 8.2.
+__global__ __launch_bounds__(256) void update_select_bias_kernel(const int32_t* __restrict__ counts,
+                                                                 int T, int E, int k, float rate,
+                                                                 float* __restrict__ bias) {
+  const int e = blockIdx.x * 256 + threadIdx.x;
+  if (e >= E) return;
+  const long long diff = (long long)T * k - (long long)E * counts[e];
+  const float sgn = diff > 0 ? 1.0f : (diff < 0 ? -1.0f : 0.0f);
+  bias[e] = bias[e] + rate * sgn;
+}
+
+void launch_update_select_bias(const int32_t* counts, int T, int E, int k, float rate,
+                               float* select_bias, hipStream_t s) {
+  hipLaunchKernelGGL(update_select_bias_kernel, dim3((E + 255) / 256), dim3(256), 0, s, counts, T,
+                     E, k, rate, select_bias);
+}
+
 }  // namespace moe

@@ -12,9 +12,9 @@ struct GemmParams;
 // route.hip
 void launch_router_small_e(const void* x, const void* w_r, const float* bias, int T, int d, int E,
                            bool bf16, float* logits, hipStream_t s);
-void launch_gate_topk(const float* logits, int T, int E, int k, int mode, int32_t* topk_idx,
-                      float* topk_gate, float* part_p, float* part_l, float* prob_sum,
-                      float* lse_sq_sum, hipStream_t s);
+void launch_gate_topk(const float* logits, const float* select_bias, int T, int E, int k, int mode,
+                      int32_t* topk_idx, float* topk_gate, float* part_p, float* part_l,
+                      float* prob_sum, float* lse_sq_sum, hipStream_t s);
 size_t route_workspace_bytes(int T, int E);
 int gate_rows_per_block(int T);
 
@@ -32,6 +32,8 @@ hipError_t launch_gemm_f32(const GemmParams& p, int rows_max, int epi, hipStream
 // combine.hip
 void launch_combine(const void* expert_out, const int32_t* inv, const float* gate, int T, int d,
                     int k, bool bf16, const void* shared_out, void* y, hipStream_t s);
+void launch_update_select_bias(const int32_t* counts, int T, int E, int k, float rate,
+                                float* select_bias, hipStream_t s);
 void launch_aux_loss(const int32_t* counts, const float* prob_sum, const float* lse_sq_sum, int T,
                      int E, int k, float alpha, float beta, float* aux, float* z, hipStream_t s);
 

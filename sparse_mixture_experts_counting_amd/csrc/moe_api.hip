@@ -72,10 +72,11 @@ size_t moe_workspace_bytes(int T, int d, int d_ff, int E, int k, moe_dtype dt) {
   return m > f ? m : f;
 }
 
-moe_status moe_route(const void* x, const void* w_r, const float* logit_bias, int T, int d, int E,
-                     int k, moe_dtype dt, moe_gating gating, unsigned flags, float* logits,
-                     int32_t* topk_idx, float* topk_gate, float* prob_sum, float* lse_sq_sum,
-                     void* workspace, size_t ws_bytes, void* stream) {
+moe_status moe_route(const void* x, const void* w_r, const float* logit_bias,
+                     const float* select_bias, int T, int d, int E, int k, moe_dtype dt,
+                     moe_gating gating, unsigned flags, float* logits, int32_t* topk_idx,
+                     float* topk_gate, float* prob_sum, float* lse_sq_sum, void* workspace,
+                     size_t ws_bytes, void* stream) {
   const bool logits_in = (flags & MOE_ROUTE_LOGITS_IN) != 0;
   if (T < 1 || E < 1 || k < 1 || k > E) return MOE_ERR_ARG;
   if (flags & ~MOE_ROUTE_LOGITS_IN) return MOE_ERR_ARG;
@@ -129,8 +130,8 @@ moe_status moe_route(const void* x, const void* w_r, const float* logit_bias, in
     part_p = (float*)workspace;
     part_l = part_p + nblk * E;
   }
-  moe::launch_gate_topk(logits, T, E, k, (int)gating, topk_idx, topk_gate, part_p, part_l,
-                        prob_sum, lse_sq_sum, s);
+  moe::launch_gate_topk(logits, select_bias, T, E, k, (int)gating, topk_idx, topk_gate, part_p,
+                        part_l, prob_sum, lse_sq_sum, s);
   return launched();
 }
 
@@ -270,6 +271,14 @@ moe_status moe_combine(const void* expert_out, const int32_t* inv, const float* 
     return MOE_ERR_UNSUPPORTED;
   moe::launch_combine(expert_out, inv, topk_gate, T, d, k, dt == MOE_BF16, shared_out, y,
                       (hipStream_t)stream);
+  return launched();
+}
+
+moe_status moe_update_select_bias(const int32_t* counts, int T, int E, int k, float rate,
+                                  float* select_bias, void* stream) {
+  if (T < 1 || E < 1 || k < 1 || !counts || !select_bias) return MOE_ERR_ARG;
+  if (E > kMaxE || k > kMaxK) return MOE_ERR_UNSUPPORTED;
+  moe::launch_update_select_bias(counts, T, E, k, rate, select_bias, (hipStream_t)stream);
   return launched();
 }
 

@@ -171,8 +171,10 @@ void launch_router_generic(const void* x, const void* w_r, const float* bias, in
 
 // ---------------------------------------------------------------------------------------------
 // Gating + top-k.  One wave per token row; lane l holds experts l, l+64, ... (EPL of them).
-// Selection ranks on an integer key built from the float32 logit so that -0.0 == +0.0 and equal
-// logits go to the lower expert index: key = (order-preserving bits of the logit) << 32 | ~e.
+// Selection ranks on an integer key built from the float32 score so that -0.0 == +0.0 and equal
+// scores go to the lower expert index: key = (order-preserving bits of the score) << 32 | ~e.  The
+// score is the logit, or logit + select_bias[e] (one float32 add) for aux-loss-free balancing; the
+// gates, P and the z-loss always use the logit.
 // ---------------------------------------------------------------------------------------------
 __device__ __forceinline__ uint32_t ordered_bits(float v) {
   uint32_t u = __float_as_uint(v);
@@ -188,8 +190,10 @@ __device__ __forceinline__ float log_sigmoid(float v) {
 }
 
 template <int EPL>
-__global__ __launch_bounds__(256) void gate_topk_kernel(const float* __restrict__ logits, int T,
-                                                        int E, int k, int mode, int rows_per_block,
+__global__ __launch_bounds__(256) void gate_topk_kernel(const float* __restrict__ logits,
+                                                        const float* __restrict__ select_bias,
+                                                        int T, int E, int k, int mode,
+                                                        int rows_per_block,
                                                         int32_t* __restrict__ topk_idx,
                                                         float* __restrict__ topk_gate,
                                                         float* __restrict__ part_p,
@@ -215,7 +219,8 @@ __global__ __launch_bounds__(256) void gate_topk_kernel(const float* __restrict_
       const int e = lane + 64 * i;
       if (e < E) {
         v[i] = row[e];
-        key[i] = ((uint64_t)ordered_bits(v[i]) << 32) | (uint32_t)(~e);
+        const float score = select_bias ? v[i] + select_bias[e] : v[i];
+        key[i] = ((uint64_t)ordered_bits(score) << 32) | (uint32_t)(~e);
       } else {
         v[i] = -INFINITY;
         key[i] = 0ull;
@@ -240,26 +245,26 @@ __global__ __launch_bounds__(256) void gate_topk_kernel(const float* __restrict_
     const float lse = m + logf(s);
     acc_l += lse * lse;
 
-    // Top-k by repeated wave arg-max over the keys.
+    // Top-k by repeated wave arg-max over the keys.  v0 is the largest selected logit (the first
+    // one selected when there is no selection bias), the shift that keeps the gates finite.
     int my_e = 0;
-    float my_v = 0.f;
-    float v0 = 0.f;
+    float my_v = -INFINITY;
     for (int j = 0; j < k; ++j) {
       uint64_t best = key[0];
 #pragma unroll
       for (int i = 1; i < EPL; ++i) best = key[i] > best ? key[i] : best;
       best = wave_max_u64(best);
       const int e_j = (int)(~(uint32_t)best);
-      const float v_j = from_ordered_bits((uint32_t)(best >> 32));
+      const float v_j = select_bias ? row[e_j] : from_ordered_bits((uint32_t)(best >> 32));
 #pragma unroll
       for (int i = 0; i < EPL; ++i)
         if (lane + 64 * i == e_j) key[i] = 0ull;
-      if (j == 0) v0 = v_j;
       if (lane == j) {
         my_e = e_j;
         my_v = v_j;
       }
     }
+    const float v0 = wave_max(my_v);
     float w = 0.f;
     if (lane < k) {
       if (mode == 0)
@@ -322,16 +327,16 @@ int gate_rows_per_block(int T) {
   return 8;
 }
 
-void launch_gate_topk(const float* logits, int T, int E, int k, int mode, int32_t* topk_idx,
-                      float* topk_gate, float* part_p, float* part_l, float* prob_sum,
-                      float* lse_sq_sum, hipStream_t s) {
+void launch_gate_topk(const float* logits, const float* select_bias, int T, int E, int k, int mode,
+                      int32_t* topk_idx, float* topk_gate, float* part_p, float* part_l,
+                      float* prob_sum, float* lse_sq_sum, hipStream_t s) {
   const int rpb = gate_rows_per_block(T);
   const int nblk = (T + rpb - 1) / rpb;
   float* pp = (prob_sum || lse_sq_sum) ? part_p : nullptr;
   const int epl = (E + 63) / 64;
 #define MOE_GATE(n)                                                                          \
-  hipLaunchKernelGGL((gate_topk_kernel<n>), dim3(nblk), dim3(256), 0, s, logits, T, E, k, mode, \
-                     rpb, topk_idx, topk_gate, pp, part_l)
+  hipLaunchKernelGGL((gate_topk_kernel<n>), dim3(nblk), dim3(256), 0, s, logits, select_bias, T, \
+                     E, k, mode, rpb, topk_idx, topk_gate, pp, part_l)
   if (epl <= 1) MOE_GATE(1);
   else if (epl <= 2) MOE_GATE(2);
   else if (epl <= 4) MOE_GATE(4);

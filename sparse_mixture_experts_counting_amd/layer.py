@@ -59,7 +59,8 @@ def route(cfg, inp, b, logits_in=False, stream=None):
     lm.route(None if logits_in else inp.x, None if logits_in else inp.w_r,
              None if logits_in else inp.bias, cfg.T, cfg.d, cfg.E, cfg.k, code,
              GATING_CODE[cfg.gating], lm.ROUTE_LOGITS_IN if logits_in else 0, b.logits,
-             b.topk_idx, b.topk_gate, b.prob_sum, b.lse_sq_sum, b.workspace, stream)
+             b.topk_idx, b.topk_gate, b.prob_sum, b.lse_sq_sum, b.workspace, stream,
+             select_bias=getattr(inp, "select_bias", None))
 
 
 def dispatch(cfg, b, stream=None):

@@ -21,7 +21,8 @@ STATUS = {0: "MOE_OK", 1: "MOE_ERR_ARG", 2: "MOE_ERR_UNSUPPORTED", 3: "MOE_ERR_W
           4: "MOE_ERR_DEVICE"}
 
 EXPORTS = ("moe_workspace_bytes", "moe_status_str", "moe_route", "moe_dispatch", "moe_expert_ffn",
-           "moe_expert_up", "moe_expert_down", "moe_combine", "moe_aux_loss", "moe_transpose")
+           "moe_expert_up", "moe_expert_down", "moe_combine", "moe_aux_loss",
+           "moe_update_select_bias", "moe_transpose")
 
 
 class MoEError(RuntimeError):
@@ -40,7 +41,8 @@ _lib.moe_workspace_bytes.argtypes = [_i, _i, _i, _i, _i, _i]
 _lib.moe_workspace_bytes.restype = _sz
 _lib.moe_status_str.argtypes = [_i]
 _lib.moe_status_str.restype = ctypes.c_char_p
-_lib.moe_route.argtypes = [_p, _p, _p, _i, _i, _i, _i, _i, _i, _u, _p, _p, _p, _p, _p, _p, _sz, _p]
+_lib.moe_route.argtypes = [_p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _u, _p, _p, _p, _p, _p, _p, _sz,
+                          _p]
 _lib.moe_dispatch.argtypes = [_p, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _sz, _p]
 _lib.moe_expert_ffn.argtypes = [_p, _p, _p, _i, _i, _i, _i, _i, _p, _p, _p, _i, _p, _p, _sz, _p]
 _lib.moe_expert_up.argtypes = [_p, _p, _p, _i, _i, _i, _i, _i, _p, _p, _i, _p, _p, _sz, _p]
@@ -48,8 +50,9 @@ _lib.moe_expert_down.argtypes = [_p, _p, _i, _i, _i, _i, _i, _p, _i, _p, _p, _sz
 _lib.moe_combine.argtypes = [_p, _p, _p, _i, _i, _i, _i, _p, _p, _p]
 _lib.moe_aux_loss.argtypes = [_p, _p, _p, _i, _i, _i, _f, _f, _p, _p, _p]
 _lib.moe_transpose.argtypes = [_p, _i, _i, _i, _i, _p, _p]
+_lib.moe_update_select_bias.argtypes = [_p, _i, _i, _i, _f, _p, _p]
 for _n in ("moe_route", "moe_dispatch", "moe_expert_ffn", "moe_expert_up", "moe_expert_down",
-           "moe_combine", "moe_aux_loss", "moe_transpose"):
+           "moe_combine", "moe_aux_loss", "moe_transpose", "moe_update_select_bias"):
     getattr(_lib, _n).restype = _i
 
 
@@ -95,9 +98,10 @@ def workspace_bytes(T, d, d_ff, E, k, dt):
 
 
 def route(x, w_r, logit_bias, T, d, E, k, dt, gating, flags, logits, topk_idx, topk_gate,
-          prob_sum, lse_sq_sum, workspace, stream=None):
+          prob_sum, lse_sq_sum, workspace, stream=None, select_bias=None):
     _check("moe_route", _lib.moe_route(
-        _ptr(x), _ptr(w_r), _ptr(logit_bias), T, d, E, k, dt, gating, flags, _ptr(logits),
+        _ptr(x), _ptr(w_r), _ptr(logit_bias), _ptr(select_bias), T, d, E, k, dt, gating, flags,
+        _ptr(logits),
         _ptr(topk_idx), _ptr(topk_gate), _ptr(prob_sum), _ptr(lse_sq_sum), _ptr(workspace),
         _nbytes(workspace), _stream(stream)))
 
@@ -143,3 +147,9 @@ def transpose(src, batch, rows, cols, dt, dst, stream=None):
     """dst[b][c][r] = src[b][r][c] (weight layout conversion, at load time)."""
     _check("moe_transpose", _lib.moe_transpose(_ptr(src), batch, rows, cols, dt, _ptr(dst),
                                                _stream(stream)))
+
+
+def update_select_bias(counts, T, E, k, rate, select_bias, stream=None):
+    """select_bias[e] += rate * sign(T*k - E*counts[e]) (aux-loss-free balancing step)."""
+    _check("moe_update_select_bias", _lib.moe_update_select_bias(
+        _ptr(counts), T, E, k, float(rate), _ptr(select_bias), _stream(stream)))

@@ -96,6 +96,7 @@ class MoEInputs:
     w2: torch.Tensor         # [E, d, d_ff]
     shared: tuple = None     # (w1s [d_ff, d], w3s [d_ff, d], w2s [d, d_ff]) or None
     bias: torch.Tensor = None  # float32 [E] or None
+    select_bias: torch.Tensor = None  # float32 [E] or None: biases expert selection only
 
 
 def make_inputs(cfg, seed=0, device="cpu"):

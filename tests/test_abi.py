@@ -29,7 +29,7 @@ def test_every_declared_symbol_is_exported(lm):
     names = _declared()
     assert set(names) == {"moe_workspace_bytes", "moe_status_str", "moe_route", "moe_dispatch",
                           "moe_expert_ffn", "moe_expert_up", "moe_expert_down", "moe_combine",
-                          "moe_aux_loss", "moe_transpose"}
+                          "moe_aux_loss", "moe_update_select_bias", "moe_transpose"}
     lib = ctypes.CDLL(lm.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -53,7 +53,8 @@ FAKE = 1 << 20   # never dereferenced: every call below fails its host-side chec
 
 def test_route_argument_errors(lm):
     L = lm.lib()
-    args = lambda **kw: [kw.get("x", FAKE), kw.get("w", FAKE), kw.get("bias", None), kw.get("T", 4),
+    args = lambda **kw: [kw.get("x", FAKE), kw.get("w", FAKE), kw.get("bias", None),
+                         kw.get("sbias", None), kw.get("T", 4),
                          kw.get("d", 8), kw.get("E", 4), kw.get("k", 2), kw.get("dt", 1),
                          kw.get("g", 0), kw.get("flags", 0), kw.get("logits", FAKE), FAKE, FAKE,
                          kw.get("ps", None), None, kw.get("ws", None), kw.get("wsb", 0), None]
@@ -126,3 +127,13 @@ def test_transpose_argument_errors(lm):
     assert L.moe_transpose(FAKE, 1, 4, 4, 7, FAKE, None) == 1
     assert L.moe_transpose(FAKE, 70000, 4, 4, 1, FAKE, None) == 2
     assert L.moe_transpose(FAKE, 1, 64 * 65536, 4, 1, FAKE, None) == 2
+
+
+def test_update_select_bias_argument_errors(lm):
+    L = lm.lib()
+    f = ctypes.c_float
+    assert L.moe_update_select_bias(None, 4, 4, 2, f(0.01), FAKE, None) == 1
+    assert L.moe_update_select_bias(FAKE, 4, 4, 2, f(0.01), None, None) == 1
+    assert L.moe_update_select_bias(FAKE, 0, 4, 2, f(0.01), FAKE, None) == 1
+    assert L.moe_update_select_bias(FAKE, 4, 0, 2, f(0.01), FAKE, None) == 1
+    assert L.moe_update_select_bias(FAKE, 4, 2000, 2, f(0.01), FAKE, None) == 2

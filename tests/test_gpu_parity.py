@@ -139,10 +139,16 @@ def run_and_compare(M, cfg, inp, seed_note=""):
     bound, exact = P.logit_error_bound(h["x"], h["w_r"], h["bias"])
     gl = P.np32(b.logits)
     assert np.all(np.abs(gl - exact) <= bound), "router logits outside the rounding bound"
+    sb = None if getattr(inp, "select_bias", None) is None else P.np32(inp.select_bias)
     ref = O.forward(h["x"], h["w_r"], h["w1"], h["w3"], h["w2"], cfg.k, mode,
                     capacity=cfg.capacity, bias=h["bias"], shared=h["shared"], alpha=cfg.alpha,
-                    beta=cfg.beta)
-    flips = P.certify_routing(P.npi(b.topk_idx), ref["topk_idx"], exact, bound)
+                    beta=cfg.beta, select_bias=sb)
+    if sb is None:
+        flips = P.certify_routing(P.npi(b.topk_idx), ref["topk_idx"], exact, bound)
+    else:   # ranking scores logit + bias, each side rounded once more in float32
+        scores = exact + sb.astype(np.float64)[None, :]
+        sbound = bound + 4 * P.U32 * (np.abs(exact) + np.abs(sb)[None, :])
+        flips = P.certify_routing(P.npi(b.topk_idx), ref["topk_idx"], scores, sbound)
     _say("  %s: flips=%d drops=%d" % (cfg.name, len(flips), ref["n_dropped"]))
     if not flips:
         P.check_dispatch_exact(b, ref)
@@ -298,3 +304,59 @@ def test_expert_halves_split_and_unsplit(M):
     ref = outs["unsplit"]
     err = (outs["split"] - ref).abs().max().item() / max(ref.abs().max().item(), 1e-30)
     assert err <= 2e-2, err
+
+
+# ------------------------------------------------------------ aux-loss-free balancing (selection bias)
+
+
+@pytest.mark.parametrize("E,k", [(4, 2), (8, 2), (64, 6), (256, 8), (1000, 3)])
+@pytest.mark.parametrize("mode", ["softmax_topk", "softmax_all", "sigmoid_topk"])
+def test_route_select_bias_from_given_logits(M, E, k, mode):
+    """Ranking on logit + select_bias bit-exact; gates from the logits alone."""
+    import types
+    _say("route select_bias E=%d k=%d mode=%s" % (E, k, mode))
+    rng = np.random.default_rng(E * 7 + k)
+    T = 41
+    L = rng.normal(0, 2, size=(T, E)).astype(np.float32)
+    L[0] = 1.0
+    sb = rng.normal(0, 1.0, size=E).astype(np.float32)
+    sb[: E // 4] = 0.0                                  # ties among biased scores in row 0
+    cfg = M["synth"].tiny_config(T, 8, E, k, 8, "fp32", mode)
+    b = M["layer"].alloc_buffers(cfg)
+    b.logits.copy_(torch.from_numpy(L))
+    inp = types.SimpleNamespace(select_bias=torch.from_numpy(sb).cuda())
+    M["layer"].route(cfg, inp, b, logits_in=True)
+    torch.cuda.synchronize()
+    want = O.select_topk(L, k, sb)
+    np.testing.assert_array_equal(P.npi(b.topk_idx), want)
+    g_ref = O.gate_weights(L, want, P.GATE_CODE[mode])
+    np.testing.assert_allclose(P.np32(b.topk_gate), g_ref, atol=1e-6, rtol=0)
+    assert not np.array_equal(want, O.select_topk(L, k)), "the bias should change some choices"
+
+
+def test_update_select_bias_exact(M):
+    _say("update select bias")
+    lm = M["lm"]
+    rng = np.random.default_rng(99)
+    for T, E, k in [(64, 8, 2), (8192, 256, 8), (5, 3, 1)]:
+        counts = rng.multinomial(T * k, np.ones(E) / E).astype(np.int32)
+        counts[0] = T * k // E if (T * k) % E == 0 else counts[0]   # an expert exactly at the mean
+        b0 = rng.normal(0, 0.1, size=E).astype(np.float32)
+        dev_b = torch.from_numpy(b0.copy()).cuda()
+        lm.update_select_bias(torch.from_numpy(counts).cuda(), T, E, k, 1e-3, dev_b)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(P.np32(dev_b), O.update_select_bias(b0, counts, T, E, k,
+                                                                          1e-3))
+
+
+@pytest.mark.parametrize("mode", ["softmax_topk", "sigmoid_topk"])
+def test_layer_with_select_bias(M, mode):
+    """A whole layer whose expert selection is biased; routing, dispatch, gates, y and losses
+    against the oracle given the same bias."""
+    import dataclasses
+    _say("layer with select bias", mode)
+    cfg = M["synth"].tiny_config(300, 128, 16, 2, 192, "bf16", mode)
+    inp = M["synth"].make_inputs(cfg, seed=12, device="cpu")
+    sb = torch.from_numpy(np.random.default_rng(5).normal(0, 0.5, size=16).astype(np.float32))
+    inp = _to_cuda(dataclasses.replace(inp, select_bias=sb))
+    run_and_compare(M, cfg, inp)
