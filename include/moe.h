@@ -198,8 +198,9 @@ moe_status moe_aux_loss(const int32_t* counts, const float* prob_sum, const floa
 
 /*
  * moe_update_select_bias -- one aux-loss-free balancing step after a layer call (the tirogla page,
- * Implementation notes: nudge each selection bias up or down after each step by load; the
- * dineshblog page, section 8.2: up when the expert is under-used, down when over-used):
+ * Implementation notes, where each bias moves after every step in the direction its expert's load
+ * calls for; the dineshblog page, section 8.2, where it rises for experts that get too few tokens
+ * and falls for those that get too many):
  *
  *   select_bias[e] += rate * sign(T*k - E*counts[e])      in place, fp32
  *

@@ -42,8 +42,8 @@ the design notes of this repository):
     bias is added (float32) to the logits used for ranking only; gates, P and z use the logits.
     After a step each bias moves by a fixed `rate` towards balance: +rate when the expert's load is
     below the mean T*k/E, -rate above it, 0 at it.  [dinesh] 9 mentions an exponential moving
-    average of relative load instead; the fixed-size nudge is the plainer reading of "nudge it up
-    or down by load" and is the one built.
+    average of relative load instead; a fixed-size step whose direction comes from the load is the
+    plainer reading of [tirogla] and is the one built.
 
 Pins: every function here is checked by the CPU tests against page-printed values (the worked
 top-2 example of [dinesh] section 2), closed forms, invariants stated on the pages, library
@@ -290,9 +290,10 @@ def forward(x, w_r, w1, w3, w2, k, mode, capacity=None, bias=None, shared=None,
 
 
 def update_select_bias(select_bias, counts, T, E, k, rate):
-    """One aux-loss-free balancing step ([tirogla] Implementation notes: nudge each expert's
-    selection bias up or down after each step by its load; [dinesh] 8.2: up when the expert is
-    under-used, down when over-used).  Reading: the nudge has a fixed size `rate` and the sign of
+    """One aux-loss-free balancing step ([tirogla] Implementation notes: after every step each
+    expert's selection bias moves in a direction set by its load; [dinesh] 8.2: it rises for an
+    expert that receives too few tokens and falls for one that receives too many).  Reading: the
+    step has a fixed size `rate` and the sign of
     (mean load - load), the mean load being T*k/E assignments (counts before capacity):
 
         b_e <- b_e + rate * sign(T*k - E*counts_e)        (float32, one rounding)
