@@ -210,6 +210,9 @@ SWEEP = [
     (16, 256, 4, 2, 512, "bf16", "softmax_topk", 0, 1, 0.0),
     (32, 128, 8, 2, 256, "bf16", "sigmoid_topk", 0, 1, 0.0),
     (7, 512, 3, 2, 1024, "bf16", "softmax_all", 3, 0, 0.0),
+    # decode-sized groups (weight-streaming kernel): N not a multiple of 32, groups past 32 rows
+    (24, 192, 8, 2, 200, "bf16", "softmax_topk", 0, 1, 0.0),
+    (128, 128, 32, 2, 192, "bf16", "softmax_topk", 0, 0, 1.2),
     # at least 512 rows per expert: 256-row tiles (8 waves), ragged and even K, N past one tile
     (2600, 136, 2, 2, 264, "bf16", "softmax_all", 0, 0, 0.0),
     (2048, 128, 2, 1, 320, "bf16", "softmax_topk", 0, 1, 0.0),
