@@ -1,4 +1,4 @@
-"""CPU oracle for the forward pass of one top-k routed Mixture-of-Experts FFN layer.
+"""CPU oracle for the forward and backward passes of one top-k routed Mixture-of-Experts FFN layer.
 
 TEST INFRASTRUCTURE. Only the test suite, the smoke check and the CPU-baseline leg of the
 benchmark may import this module. The product path (the HIP library and its binding) never
@@ -19,6 +19,8 @@ Pages (cited by title and section; nothing here copies their code):
              (Key Equations; Top-k Gating; Expert Architectures: Shared + Specialized).
   [vanos]    "Mixture of Experts (MoE)" -- vanos001.github.io/placement_prep/llm/moe
              (Load Balancing Loss).
+  [chipfoundry] "Mixture of Experts (MoE) architecture" glossary entry -- chipfoundryservices.com
+             (MoE Architecture Components: the router is trained end to end by gradient descent).
 
 Readings taken where the pages are silent or disagree (each one is also listed with its reason in
 the design notes of this repository):
@@ -66,7 +68,7 @@ def _f64(a):
     return np.asarray(a, dtype=np.float64)
 
 
-def router_logits(x, w_r, bias=None):
+def router_logits(x, w_r, bias=None, exact=False):
     """Router scores, [tirogla] How it works step 1 (Score) and [dinesh] 1.2 What the router computes.
 
     logits[t, e] = sum_j x[t, j] * W_r[e, j] (+ bias[e]); x [T, d], W_r [E, d] (the [out][in]
@@ -77,7 +79,7 @@ def router_logits(x, w_r, bias=None):
     L = _f64(x) @ _f64(w_r).T
     if bias is not None:
         L = L + _f64(bias)[None, :]
-    return L.astype(np.float32)
+    return L if exact else L.astype(np.float32)
 
 
 def select_topk(logits, k, select_bias=None):
@@ -256,20 +258,21 @@ def z_loss(lse_sq_sum, T, beta):
 
 
 def forward(x, w_r, w1, w3, w2, k, mode, capacity=None, bias=None, shared=None,
-            alpha=0.01, beta=1e-3, logits=None, select_bias=None):
+            alpha=0.01, beta=1e-3, logits=None, select_bias=None, exact_logits=False):
     """The whole layer, steps in the order of [tirogla] How it works (Score, Select, Dispatch,
     Compute, Combine, Balance).
 
     x [T, d]; w_r [E, d]; w1, w3 [E, d_ff, d]; w2 [E, d, d_ff]; shared = (w1s, w3s, w2s) or None.
     `logits` (float32 [T, E]) replaces the router product when given; `select_bias` (float32 [E])
-    biases the ranking only (aux-loss-free balancing).
+    biases the ranking only (aux-loss-free balancing).  exact_logits keeps the router product in
+    float64 instead of rounding it to float32 (for finite-difference checks of the gradients).
     Returns a dict of every intermediate (float64 except the integer dispatch outputs).
     """
     x = np.asarray(x)
     T = x.shape[0]
     if logits is None:
-        logits = router_logits(x, w_r, bias)
-    logits = np.asarray(logits, dtype=np.float32)
+        logits = router_logits(x, w_r, bias, exact=exact_logits)
+    logits = np.asarray(logits, dtype=np.float64 if exact_logits else np.float32)
     E = logits.shape[1]
     idx = select_topk(logits, k, select_bias)
     gate = gate_weights(logits, idx, mode)
@@ -287,6 +290,172 @@ def forward(x, w_r, w1, w3, w2, k, mode, capacity=None, bias=None, shared=None,
                 perm=perm, inv=inv, n_dropped=n_dropped, expert_out=rows, shared_out=shared_out,
                 y=y, aux=aux_loss(counts, prob_sum, T, E, k, alpha),
                 z=z_loss(lse_sq_sum, T, beta))
+
+
+# ------------------------------------------------------------------------------------------------
+# Backward pass.  The objective is J = <dy, y> + L_aux + z: a task loss whose gradient with respect
+# to the layer output is dy, plus the two router losses of [tirogla] How it works step 6 (the total
+# loss of [vanos] Load Balancing Loss adds the balancing term to the task loss; the router is
+# trained end to end by gradient descent, [chipfoundry] MoE Architecture Components).  f_e is a
+# count and carries no gradient ([tirogla] step 6 says so); P_e and lse do.  The selection (which
+# experts, which assignments are dropped) is piecewise constant in the logits and carries none
+# either, so a selection bias only changes which experts the gradient flows through ([dinesh] 8.2:
+# the bias acts on routing decisions, not on the gradient path).  Each function below is the chain
+# rule of one forward step, run in the reverse order of the steps.
+# ------------------------------------------------------------------------------------------------
+
+
+def combine_backward(dy, out_rows, inv, gate, T, k):
+    """Gradient of Combine ([tirogla] How it works step 5): for a kept assignment a = t*k + s with
+    row r = inv[a],  d_out[r] = gate[t, s] * dy[t]  and  d_gate[t, s] = <dy[t], out_rows[r]>;
+    a dropped assignment gets d_gate = 0.  The shared expert's output enters y with weight 1, so
+    its output gradient is dy itself.  float64 ([n_kept, d], [T, k])."""
+    dy = _f64(dy)
+    out_rows = _f64(out_rows)
+    inv = np.asarray(inv).reshape(T, k)
+    g = _f64(gate).reshape(T, k)
+    d_out = np.zeros(out_rows.shape, dtype=np.float64)
+    d_gate = np.zeros((T, k), dtype=np.float64)
+    for s in range(k):
+        keep = inv[:, s] >= 0
+        rows = inv[keep, s]
+        d_out[rows] = g[keep, s, None] * dy[keep]
+        d_gate[keep, s] = np.sum(dy[keep] * out_rows[rows], axis=1)
+    return d_out, d_gate
+
+
+def silu_grad(z):
+    """d/dz silu(z) = sigmoid(z) * (1 + z * (1 - sigmoid(z)))."""
+    with np.errstate(over="ignore"):
+        sg = 1.0 / (1.0 + np.exp(-z))
+    return sg * (1.0 + z * (1.0 - sg))
+
+
+def swiglu_ffn_backward(X, w1, w3, w2, dO):
+    """Gradient of the SwiGLU expert of [dinesh] 1.1, O = H w2^T with H = silu(A) * B, A = X w1^T,
+    B = X w3^T:
+        dw2 = dO^T H,  dH = dO w2,  dA = dH * B * silu'(A),  dB = dH * silu(A),
+        dw1 = dA^T X,  dw3 = dB^T X,  dX = dA w1 + dB w3.
+    Shapes as swiglu_ffn; returns (dX, dw1, dw3, dw2), float64."""
+    X = _f64(X)
+    w1, w3, w2, dO = _f64(w1), _f64(w3), _f64(w2), _f64(dO)
+    A = X @ w1.T
+    B = X @ w3.T
+    H = silu(A) * B
+    dH = dO @ w2
+    dA = dH * B * silu_grad(A)
+    dB = dH * silu(A)
+    return dA @ w1 + dB @ w3, dA.T @ X, dB.T @ X, dO.T @ H
+
+
+def expert_rows_backward(x, perm, offsets, k, w1, w3, w2, d_out):
+    """Gradient of Compute ([tirogla] How it works step 4) given d_out for every kept row.
+    Returns dx_rows [n_kept, d] (row r: the input gradient of expert e's batch row, before the
+    rows of one token are added), dx [T, d] (those rows added per token), and dw1, dw3 [E, d_ff, d],
+    dw2 [E, d, d_ff] (experts with no rows get zeros).  float64."""
+    x = _f64(x)
+    E = len(offsets) - 1
+    dx = np.zeros_like(x)
+    dx_rows = np.zeros((int(offsets[E]), x.shape[1]), dtype=np.float64)
+    dw1 = np.zeros(np.shape(w1), dtype=np.float64)
+    dw3 = np.zeros(np.shape(w3), dtype=np.float64)
+    dw2 = np.zeros(np.shape(w2), dtype=np.float64)
+    for e in range(E):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if hi > lo:
+            tok = np.asarray(perm[lo:hi]) // k
+            dX, dw1[e], dw3[e], dw2[e] = swiglu_ffn_backward(x[tok], w1[e], w3[e], w2[e],
+                                                             d_out[lo:hi])
+            dx_rows[lo:hi] = dX
+            np.add.at(dx, tok, dX)
+    return dx_rows, dx, dw1, dw3, dw2
+
+
+def gate_backward(logits, idx, mode, d_gate):
+    """Gradient of the gates (gate_weights) with respect to the logits, per row t:
+    SOFTMAX_TOPK: dL[e_s] = g_s (dg_s - sum_s' g_s' dg_s')        (softmax over the selected)
+    SOFTMAX_ALL:  dL[j]   = p_j (dp_j - sum_i p_i dp_i), dp = dg on the selected, 0 elsewhere
+    SIGMOID_TOPK: dL[e_s] = sigmoid'(L_e_s) (dg_s - sum_s' g_s' dg_s') / sum_s' sigmoid(L_e_s')
+    float64 [T, E]; zero on experts that the gate does not depend on."""
+    L = _f64(logits)
+    T, E = L.shape
+    dg_all = _f64(d_gate)
+    dL = np.zeros((T, E), dtype=np.float64)
+    with np.errstate(over="ignore"):
+        for t in range(T):
+            row, sel, dg = L[t], np.asarray(idx[t]), dg_all[t]
+            m = row.max()
+            if mode == SOFTMAX_TOPK:
+                w = np.exp(row[sel] - m)
+                g = w / w.sum()
+                dL[t, sel] += g * (dg - np.sum(g * dg))
+            elif mode == SOFTMAX_ALL:
+                p = np.exp(row - m)
+                p /= p.sum()
+                dp = np.zeros(E)
+                dp[sel] = dg
+                dL[t] += p * (dp - np.sum(p * dp))
+            elif mode == SIGMOID_TOPK:
+                sg = 1.0 / (1.0 + np.exp(-row[sel]))
+                S = sg.sum()
+                g = sg / S
+                dL[t, sel] += sg * (1.0 - sg) * (dg - np.sum(g * dg)) / S
+            else:
+                raise ValueError("unknown gating mode %r" % (mode,))
+    return dL
+
+
+def balance_backward(logits, counts, T, E, k, alpha, beta):
+    """Gradient of L_aux + z with respect to the logits ([tirogla] step 6): with f fixed,
+    dL_aux/dp[t, e] = alpha * E * f_e / T =: c_e, so dL[t, j] = p_tj (c_j - sum_e p_te c_e);
+    dz/dL[t, j] = 2 * beta * lse_t * p_tj / T.  float64 [T, E]."""
+    p, lse = row_softmax_lse(logits)
+    c = alpha * E * (_f64(counts) / float(T * k)) / float(T)
+    dL = p * (c[None, :] - np.sum(p * c[None, :], axis=1, keepdims=True))
+    return dL + (2.0 * beta / float(T)) * lse[:, None] * p
+
+
+def router_backward(x, w_r, d_logits):
+    """Gradient of the router product logits = x W_r^T (+ bias): dW_r = dL^T x, dx = dL W_r.
+    float64 ([E, d], [T, d])."""
+    dL = _f64(d_logits)
+    return dL.T @ _f64(x), dL @ _f64(w_r)
+
+
+def backward(x, w_r, w1, w3, w2, dy, k, mode, capacity=None, bias=None, shared=None,
+             alpha=0.01, beta=1e-3, select_bias=None, exact_logits=False):
+    """Gradient of J = <dy, y> + L_aux + z with respect to x, W_r and every expert weight, the
+    steps of forward() chained in reverse (Combine, Compute, gates and Balance, Score).
+    Returns a dict: the forward dict as `fw`, d_out [n_kept, d], d_gate [T, k], dx_rows
+    [n_kept, d], d_logits [T, E], dx [T, d], dw_r [E, d], dw1, dw3 [E, d_ff, d], dw2 [E, d, d_ff],
+    and dshared = (dw1s, dw3s, dw2s) or None.  float64."""
+    x = np.asarray(x)
+    T = x.shape[0]
+    fw = forward(x, w_r, w1, w3, w2, k, mode, capacity=capacity, bias=bias, shared=shared,
+                 alpha=alpha, beta=beta, select_bias=select_bias, exact_logits=exact_logits)
+    E = fw["logits"].shape[1]
+    d_out, d_gate = combine_backward(dy, fw["expert_out"], fw["inv"], fw["topk_gate"], T, k)
+    dx_rows, dx, dw1, dw3, dw2 = expert_rows_backward(x, fw["perm"], fw["offsets"], k, w1, w3,
+                                                      w2, d_out)
+    d_logits = (gate_backward(fw["logits"], fw["topk_idx"], mode, d_gate) +
+                balance_backward(fw["logits"], fw["counts"], T, E, k, alpha, beta))
+    dw_r, dx_router = router_backward(x, w_r, d_logits)
+    dx = dx + dx_router
+    dshared = None
+    if shared is not None:
+        dxs, dw1s, dw3s, dw2s = swiglu_ffn_backward(x, *shared, dy)
+        dx = dx + dxs
+        dshared = (dw1s, dw3s, dw2s)
+    return dict(fw=fw, d_out=d_out, d_gate=d_gate, dx_rows=dx_rows, d_logits=d_logits, dx=dx,
+                dw_r=dw_r, dw1=dw1, dw3=dw3, dw2=dw2, dshared=dshared)
+
+
+def objective(x, w_r, w1, w3, w2, dy, k, mode, capacity=None, bias=None, shared=None,
+              alpha=0.01, beta=1e-3, select_bias=None):
+    """J = <dy, y> + L_aux + z from forward() with float64 logits (what backward() differentiates)."""
+    fw = forward(x, w_r, w1, w3, w2, k, mode, capacity=capacity, bias=bias, shared=shared,
+                 alpha=alpha, beta=beta, select_bias=select_bias, exact_logits=True)
+    return float(np.sum(_f64(dy) * fw["y"])) + fw["aux"] + fw["z"]
 
 
 def update_select_bias(select_bias, counts, T, E, k, rate):
