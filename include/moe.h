@@ -1,6 +1,6 @@
 /*
- * libmoe -- forward pass of one top-k routed Mixture-of-Experts FFN layer on one AMD MI355X
- * (CDNA4, gfx950), as hand-written HIP kernels behind a plain C ABI.
+ * libmoe -- forward and backward passes of one top-k routed Mixture-of-Experts FFN layer on one
+ * AMD MI355X (CDNA4, gfx950), as hand-written HIP kernels behind a plain C ABI.
  *
  * The method follows the page "Mixture of experts (MoE)" (tirogla.com/machine-learning/
  * mixture-of-experts.html), section "How it works": Score (router product and gating), Select
@@ -178,7 +178,9 @@ moe_status moe_expert_down(const void* h, const int32_t* offsets, int T, int d, 
  *
  * Dropped assignments add nothing; the residual is not included (a token whose assignments were
  * all dropped gets y = 0, or its shared output).  Sums in fp32, rounds y once to dtype `dt`.
- * expert_out [T*k][d]; inv [T*k]; topk_gate [T,k] fp32; shared_out [T][d] or NULL; y [T][d].
+ * expert_out [T*k][d]; inv [T*k]; topk_gate [T,k] fp32, or NULL for weight 1 on every slot (the
+ * backward pass adds each token's input-gradient rows this way); shared_out [T][d] or NULL;
+ * y [T][d].
  */
 moe_status moe_combine(const void* expert_out, const int32_t* inv, const float* topk_gate, int T,
                        int d, int k, moe_dtype dt, const void* shared_out, void* y, void* stream);
@@ -223,6 +225,88 @@ moe_status moe_update_select_bias(const int32_t* counts, int T, int E, int k, fl
  */
 moe_status moe_transpose(const void* src, int batch, int rows, int cols, moe_dtype dt, void* dst,
                          void* stream);
+
+/*
+ * Backward pass.  The objective is J = <dy, y> + aux + z: a task loss whose gradient with respect
+ * to y is dy [T][d], plus the two router losses of moe_aux_loss (the tirogla page, How it works
+ * step 6: f_e is a count and carries no gradient, P_e and the logsumexp do; the vanos001 page,
+ * Load Balancing Loss, adds the balancing term to the task loss).  The selection (top-k, capacity
+ * drops, a selection bias) carries no gradient; it only decides which experts the gradient flows
+ * through.  Chain, in the reverse order of the forward steps (every buffer from the forward call
+ * is an input):
+ *
+ *   moe_combine_backward(dy, expert_out, inv, topk_gate)   -> d_out [T*k][d], d_gate [T,k]
+ *   moe_expert_backward(x, perm, offsets, w1, w3, w2, d_out) -> dx_rows [T*k][d], dw1, dw3, dw2
+ *   moe_expert_backward(x, NULL, NULL, w1s, w3s, w2s, dy)  -> dxs [T][d], dw1s, dw3s, dw2s
+ *                                                              (shared expert, gate weight 1)
+ *   moe_route_backward(..., d_gate, counts, dx_add = dxs)   -> d_logits [T,E], dw_r [E][d], dx_r
+ *   moe_combine(dx_rows, inv, NULL, ..., shared_out = dx_r) -> dx [T][d]
+ *
+ * bf16 layers only (MOE_ERR_UNSUPPORTED for MOE_F32 where noted); weight gradients are fp32,
+ * activation gradients in the layer dtype, accumulation fp32.  Results are bitwise deterministic
+ * run to run.  Same argument conventions and errors as the forward calls.
+ */
+
+/* Workspace bytes that cover every backward call below for this layer shape (0 for MOE_F32). */
+size_t moe_backward_workspace_bytes(int T, int d, int d_ff, int E, int k, moe_dtype dt);
+
+/*
+ * moe_combine_backward -- gradient of Combine: for a kept assignment a = t*k+s with row
+ * r = inv[a],
+ *
+ *   d_out[r]    = topk_gate[t,s] * dy[t]          bf16 [T*k][d] (rows r < offsets[E] written)
+ *   d_gate[t,s] = sum_i dy[t,i] * expert_out[r,i]  fp32 [T,k], 0 for a dropped assignment
+ *
+ * dy [T][d], expert_out [T*k][d] (the forward expert rows), inv [T*k], topk_gate [T,k] fp32.
+ * MOE_F32 is unsupported.
+ */
+moe_status moe_combine_backward(const void* dy, const void* expert_out, const int32_t* inv,
+                                const float* topk_gate, int T, int d, int k, moe_dtype dt,
+                                void* d_out, float* d_gate, void* stream);
+
+/*
+ * moe_expert_backward -- gradient of Compute for the SwiGLU experts of moe_expert_ffn, given the
+ * gradient d_out of every expert row.  With a = x_t w1_e^T, b = x_t w3_e^T, h = silu(a) * b:
+ *
+ *   dh      = d_out[r] w2_e                      (recomputing a and b from x, w1, w3)
+ *   da      = dh * b * silu'(a),  db = dh * silu(a)
+ *   dx_rows[r] = da w1_e + db w3_e               [T*k][d] dtype, one row per expert row r
+ *   dw1[e]  = sum_r da_r^T x_t,  dw3[e] = sum_r db_r^T x_t,  dw2[e] = sum_r d_out[r]^T h_r
+ *
+ * Same row convention, weight storage and dense (perm == NULL, E == 1) mode as moe_expert_ffn;
+ * dw1, dw3 [E][d_ff][d] and dw2 [E][d][d_ff] fp32 in that same storage (experts with no rows get
+ * zeros).  Rows of dx_rows past offsets[E] are not written.  Intermediates (dh, h, da, db) are
+ * rounded to bf16.  The workspace (moe_backward_workspace_bytes) holds transposed copies of the
+ * weights and activations (about 3 E d d_ff + 8 T k (d + d_ff) bytes).  MOE_F32 is unsupported.
+ */
+moe_status moe_expert_backward(const void* x, const int32_t* perm, const int32_t* offsets, int T,
+                               int d, int d_ff, int E, int k, const void* w1, const void* w3,
+                               const void* w2, const void* d_out, moe_dtype dt, void* dx_rows,
+                               float* dw1, float* dw3, float* dw2, void* workspace,
+                               size_t ws_bytes, void* stream);
+
+/*
+ * moe_route_backward -- gradient of Score and of the two router losses:
+ *
+ *   d_logits[t,.] = (gating function's derivative) applied to d_gate[t,.]
+ *                   + p_t (c - <p_t, c>),  c_e = alpha * E * counts[e] / (T*k) / T   (aux)
+ *                   + 2 * beta * lse_t * p_t / T                                   (z)
+ *   dw_r[e][j]   = sum_t d_logits[t,e] x[t,j]                  fp32 [E][d] (w_r's storage)
+ *   dx[t][j]     = sum_e d_logits[t,e] w_r[e][j] (+ dx_add[t][j])        dtype [T][d]
+ *
+ * where p_t is the full softmax of logits row t and lse_t its logsumexp; the gating derivatives
+ * are those of the forward gates (softmax over the selected, softmax over all, or sigmoids
+ * renormalised over the selected).  logits [T,E] fp32, topk_idx, topk_gate from moe_route; d_gate
+ * from moe_combine_backward; counts from moe_dispatch (may be NULL when alpha == 0); dx_add [T][d]
+ * or NULL.  d_logits [T,E] fp32 is an output.  fp32 sums throughout; dw_r is added over token
+ * chunks in a fixed order.
+ */
+moe_status moe_route_backward(const void* x, const void* w_r, const float* logits,
+                              const int32_t* topk_idx, const float* topk_gate,
+                              const float* d_gate, const int32_t* counts, int T, int d, int E,
+                              int k, moe_dtype dt, moe_gating gating, float alpha, float beta,
+                              const void* dx_add, float* d_logits, float* dw_r, void* dx,
+                              void* workspace, size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -423,16 +423,18 @@ def router_backward(x, w_r, d_logits):
 
 
 def backward(x, w_r, w1, w3, w2, dy, k, mode, capacity=None, bias=None, shared=None,
-             alpha=0.01, beta=1e-3, select_bias=None, exact_logits=False):
+             alpha=0.01, beta=1e-3, select_bias=None, exact_logits=False, logits=None):
     """Gradient of J = <dy, y> + L_aux + z with respect to x, W_r and every expert weight, the
     steps of forward() chained in reverse (Combine, Compute, gates and Balance, Score).
     Returns a dict: the forward dict as `fw`, d_out [n_kept, d], d_gate [T, k], dx_rows
     [n_kept, d], d_logits [T, E], dx [T, d], dw_r [E, d], dw1, dw3 [E, d_ff, d], dw2 [E, d, d_ff],
-    and dshared = (dw1s, dw3s, dw2s) or None.  float64."""
+    and dshared = (dw1s, dw3s, dw2s) or None.  `logits` (float32 [T, E]) replaces the router
+    product as in forward(); the router gradient still flows through the product.  float64."""
     x = np.asarray(x)
     T = x.shape[0]
     fw = forward(x, w_r, w1, w3, w2, k, mode, capacity=capacity, bias=bias, shared=shared,
-                 alpha=alpha, beta=beta, select_bias=select_bias, exact_logits=exact_logits)
+                 alpha=alpha, beta=beta, select_bias=select_bias, exact_logits=exact_logits,
+                 logits=logits)
     E = fw["logits"].shape[1]
     d_out, d_gate = combine_backward(dy, fw["expert_out"], fw["inv"], fw["topk_gate"], T, k)
     dx_rows, dx, dw1, dw3, dw2 = expert_rows_backward(x, fw["perm"], fw["offsets"], k, w1, w3,

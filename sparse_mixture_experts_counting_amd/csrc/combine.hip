@@ -21,7 +21,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ e
   const int t = blockIdx.x;
   if (threadIdx.x < k) {
     s_pos[threadIdx.x] = inv[(size_t)t * k + threadIdx.x];
-    s_g[threadIdx.x] = gate[(size_t)t * k + threadIdx.x];
+    s_g[threadIdx.x] = gate ? gate[(size_t)t * k + threadIdx.x] : 1.0f;
   }
   __syncthreads();
   constexpr int VEC = BF16 ? 8 : 4;  // elements per 16-byte chunk

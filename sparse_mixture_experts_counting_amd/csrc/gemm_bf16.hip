@@ -139,14 +139,29 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_bf16_kernel(const G
 
   const int NT = (p.N + BN - 1) / BN;
   TileCoord tc;
-  const TileScan ts = scan_tiles<BM>(p, NT);
   int kc = 0, nsplit = p.ksplit, rtile = -1;
-  if (p.ksplit > 1) {                       // every tile split over K
+  int kg_beg = 0, kg_len = 0;               // K-grouped mode: this group's reduction columns
+  if (p.kgrouped) {                         // tiles: group-major, m-tiles of an n-tile adjacent
+    const int MT = (p.M + BM - 1) / BM;
+    const int per = MT * NT;
+    if ((int)blockIdx.x >= p.G * per) return;
+    const int t = xcd_order(blockIdx.x, p.G * per);
+    tc.g = t / per;
+    const int local = t - tc.g * per;
+    tc.row0 = (local % MT) * BM;
+    tc.row_end = p.M;
+    tc.n_tile = local / MT;
+    const int o0 = p.offsets[tc.g];
+    kg_beg = __builtin_amdgcn_readfirstlane(kpad(o0, tc.g));
+    kg_len = __builtin_amdgcn_readfirstlane(p.offsets[tc.g + 1] - o0);
+  } else if (p.ksplit > 1) {                // every tile split over K
+    const TileScan ts = scan_tiles<BM>(p, NT);
     kc = blockIdx.x % p.ksplit;
     const int bid = blockIdx.x / p.ksplit;
     if (bid >= ts.total) return;
     tile_at<BM>(p, NT, ts, xcd_order(bid, ts.total), tc);
   } else {                                  // whole rounds as is, the last partial round split
+    const TileScan ts = scan_tiles<BM>(p, NT);
     const TailPlan tp = tail_plan(ts.total, p.slots, p.K);
     if ((int)blockIdx.x < tp.full) {
       tile_at<BM>(p, NT, ts, xcd_order(blockIdx.x, tp.full), tc);
@@ -177,8 +192,9 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_bf16_kernel(const G
   const int K = p.K, N = p.N;
 
   // Buffer descriptors: 32-bit offsets, and loads at or past num_records return zeros.
-  const uint32_t a_bytes = (uint32_t)p.a_rows * (uint32_t)K * 2u;
-  const uint32_t b_bytes = (uint32_t)N * (uint32_t)K * 2u;
+  const int lda = p.lda ? p.lda : K, ldb = p.ldb ? p.ldb : K;
+  const uint32_t a_bytes = (uint32_t)p.a_rows * (uint32_t)lda * 2u;
+  const uint32_t b_bytes = (uint32_t)N * (uint32_t)ldb * 2u;
   const __amdgpu_buffer_rsrc_t rA =
       __builtin_amdgcn_make_buffer_rsrc((void*)p.A, (short)0, a_bytes, 0x00020000);
   const __amdgpu_buffer_rsrc_t rB0 = __builtin_amdgcn_make_buffer_rsrc(
@@ -200,14 +216,14 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_bf16_kernel(const G
     const int row = tid / UPR + ROWS_PER_LOAD * i;
     const int grow = min(tc.row0 + row, tc.row_end - 1);
     const int src = p.gather ? p.gather[grow] / p.gather_div : grow;
-    a_voff[i] = ((uint32_t)src * (uint32_t)K + 8u * u) * 2u;
+    a_voff[i] = ((uint32_t)src * (uint32_t)lda + 8u * u) * 2u;
     a_lds[i] = row * RB + ((u ^ swz<BK>(row)) << 4);
   }
 #pragma unroll
   for (int i = 0; i < B_UNITS; ++i) {
     const int brow = tid / UPR + ROWS_PER_LOAD * i;   // row of the stage's B block
     const int n = min(n_base + brow % BN, N - 1);
-    b_voff[i] = ((uint32_t)n * (uint32_t)K + 8u * u) * 2u;
+    b_voff[i] = ((uint32_t)n * (uint32_t)ldb + 8u * u) * 2u;
     b_lds[i] = B_OFF + brow * RB + ((u ^ swz<BK>(brow)) << 4);
   }
 
@@ -224,16 +240,16 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_bf16_kernel(const G
       if (j < DPW_A) {
         const int grow = min(tc.row0 + srow, tc.row_end - 1);
         const int src = p.gather ? p.gather[grow] / p.gather_div : grow;
-        d_voff[j] = ((uint32_t)src * (uint32_t)K + 8u * uu) * 2u;
+        d_voff[j] = ((uint32_t)src * (uint32_t)lda + 8u * uu) * 2u;
       } else {
         const int n = min(n_base + (srow - BM) % BN, N - 1);
-        d_voff[j] = ((uint32_t)n * (uint32_t)K + 8u * uu) * 2u;
+        d_voff[j] = ((uint32_t)n * (uint32_t)ldb + 8u * uu) * 2u;
       }
     }
   }
 
-  const int Kc = K / nsplit;
-  const int kbeg = kc * Kc;
+  const int Kc = p.kgrouped ? kg_len : K / nsplit;
+  const int kbeg = p.kgrouped ? kg_beg : kc * Kc;
   const int kend = kbeg + Kc;
   const int KT = (Kc + BK - 1) / BK;
   const int k_last = kbeg + (KT - 1) * BK;
@@ -429,6 +445,34 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_bf16_kernel(const G
   // Epilogue.  Accumulator register r of a 32x32 tile holds row 8 (r / 4) + 4 (lane / 32) + r % 4
   // and column lane % 32.
   const bool partial = p.ksplit > 1 || rtile >= 0;
+  void* const Cg = p.kgrouped ? (void*)((char*)p.C + (size_t)tc.g * p.c_gstride *
+                                                         (EPI == EPI_STORE_F32_BIAS ? 4 : 2))
+                              : p.C;
+  if constexpr (EPI == EPI_SWIGLU_BWD) {   // never split (the launcher passes no workspace)
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int col = n_base + wn0 + j * 32 + l32;
+        if (col >= N) continue;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = tc.row0 + wm0 + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+          if (row >= tc.row_end) continue;
+          const float a = acc[0][i][j][r], b = acc[NMAT - 1][i][j][r];
+          const size_t o = (size_t)row * N + col;
+          const float dh = bf16_to_f32(((const uint16_t*)p.D)[o]);
+          const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * a));
+          const float sa = a * sg;
+          ((uint16_t*)p.H)[o] = f32_to_bf16(sa * b);
+          uint16_t* dab = (uint16_t*)p.C + (size_t)row * p.ldc + col;
+          dab[0] = f32_to_bf16(dh * b * (sg * (1.0f + a * (1.0f - sg))));
+          dab[N] = f32_to_bf16(dh * sa);
+        }
+      }
+    }
+    return;
+  }
   if (EPI != EPI_STORE_F32_BIAS && !partial && N % 2 == 0 && p.ldc % 2 == 0) {
     // bf16 output, two columns per 4-byte store: lanes 2c and 2c+1 swap one value of each pair of
     // rows (a DPP quad permute), so the even lane holds row a and the odd lane row b of columns
@@ -456,7 +500,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_bf16_kernel(const G
           const int row = tc.row0 + wm0 + i * 32 + 8 * (rr >> 2) + 4 * h + (rr & 3);
           if (row < tc.row_end && col0 < N) {
             const uint32_t packed = odd ? pack_bf16x2(got, v[r + 1]) : pack_bf16x2(v[r], got);
-            *(uint32_t*)((uint16_t*)p.C + (size_t)row * p.ldc + col0) = packed;
+            *(uint32_t*)((uint16_t*)Cg + (size_t)row * p.ldc + col0) = packed;
           }
         }
       }
@@ -485,11 +529,11 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_bf16_kernel(const G
         } else if constexpr (EPI == EPI_SWIGLU) {
           const float g = acc[0][i][j][r];
           const float v = acc[NMAT - 1][i][j][r];
-          ((uint16_t*)p.C)[(size_t)row * p.ldc + col] = f32_to_bf16(silu(g) * v);
+          ((uint16_t*)Cg)[(size_t)row * p.ldc + col] = f32_to_bf16(silu(g) * v);
         } else if constexpr (EPI == EPI_STORE) {
-          ((uint16_t*)p.C)[(size_t)row * p.ldc + col] = f32_to_bf16(acc[0][i][j][r]);
+          ((uint16_t*)Cg)[(size_t)row * p.ldc + col] = f32_to_bf16(acc[0][i][j][r]);
         } else {
-          ((float*)p.C)[(size_t)row * p.ldc + col] =
+          ((float*)Cg)[(size_t)row * p.ldc + col] =
               acc[0][i][j][r] + (p.bias ? p.bias[col] : 0.f);
         }
       }
@@ -620,15 +664,16 @@ static hipError_t launch_t(const GemmParams& p, int rows_max, hipStream_t s) {
   // The last partial round of tiles is split over K when the epilogue allows it (bf16 output, 8
   // columns per finishing item) and the caller gave scratch for the partials.
   const bool tail = p.ksplit == 1 && p.part != nullptr && EPI != EPI_STORE_F32_BIAS &&
-                    p.N % 8 == 0 && p.K % 64 == 0;
+                    EPI != EPI_SWIGLU_BWD && !p.kgrouped && p.N % 8 == 0 && p.K % 64 == 0;
   q.slots = tail ? device_cus() * MINB : 0;
   const int NT = (p.N + BN - 1) / BN;
-  const int tiles = tiles_upper_bound(rows_max, p.G, p.offsets != nullptr, BM, NT);
+  const int tiles = p.kgrouped ? p.G * ((p.M + BM - 1) / BM) * NT
+                               : tiles_upper_bound(rows_max, p.G, p.offsets != nullptr, BM, NT);
   const int grid = tiles * p.ksplit + q.slots;
   if (tiles <= 0) return hipSuccess;
   hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * WGM * WGN), lds, s, q);
   if (q.slots > 0) {
-    if constexpr (EPI != EPI_STORE_F32_BIAS)
+    if constexpr (EPI != EPI_STORE_F32_BIAS && EPI != EPI_SWIGLU_BWD)
       hipLaunchKernelGGL((tail_finish_kernel<BM, BN, NMAT, EPI>), dim3(q.slots * kFinishSplit),
                          dim3(256), 0, s, q);
   }
@@ -716,14 +761,23 @@ size_t gemm_bf16_partial_bytes(int rows_max, int G, bool grouped, int N, int K, 
   return (size_t)device_cus() * minb * nmat * BM * BN * sizeof(float);
 }
 
-// Needs K a multiple of 8 (16-byte rows) and every operand under 2 GiB (32-bit buffer offsets).
+// Needs K (and the row strides) a multiple of 8 (16-byte rows) and every operand under 2 GiB
+// (32-bit buffer offsets).
 hipError_t launch_gemm_bf16(const GemmParams& p_in, int rows_max, int epi, hipStream_t s) {
-  if (p_in.K % 8 != 0 || p_in.N < 1 || p_in.K < 8) return hipErrorNotSupported;
-  if ((long long)p_in.a_rows * p_in.K * 2 >= (1ll << 31) ||
-      (long long)p_in.N * p_in.K * 2 >= (1ll << 31))
+  const int lda = p_in.lda ? p_in.lda : p_in.K, ldb = p_in.ldb ? p_in.ldb : p_in.K;
+  if (p_in.K % 8 != 0 || lda % 8 != 0 || ldb % 8 != 0 || p_in.N < 1 || p_in.K < 8)
+    return hipErrorNotSupported;
+  if ((long long)p_in.a_rows * lda * 2 >= (1ll << 31) || (long long)p_in.N * ldb * 2 >= (1ll << 31))
     return hipErrorNotSupported;
   GemmParams p = p_in;
   const bool grouped = p.offsets != nullptr;
+  if (p.kgrouped) {             // weight gradients: fp32 out, 256 x 256 tiles, no split
+    if (!grouped || epi != EPI_STORE_F32_BIAS || p.gather) return hipErrorNotSupported;
+    p.ksplit = 1;
+    p.part = nullptr;
+    return launch_t<256, 256, 1, 4, 2, 64, 2, 1, EPI_STORE_F32_BIAS, false>(p, 0, s);
+  }
+  if (epi == EPI_SWIGLU_BWD) p.part = nullptr;   // its epilogue runs on whole sums only
   p.ksplit = splitk_factor(rows_max, p.G, grouped, p.N, p.K, epi);
   p.part_rows = rows_max;
   if (p.ksplit > 1 && p.part == nullptr) p.ksplit = 1;   // no scratch given: no split
@@ -737,6 +791,10 @@ hipError_t launch_gemm_bf16(const GemmParams& p_in, int rows_max, int epi, hipSt
     case EPI_STORE:
       e = big ? launch_tail_or_not<256, 256, 1, 4, 2, 64, 2, 1, EPI_STORE>(p, rows_max, s)
               : launch_tail_or_not<128, 256, 1, 2, 2, 32, 3, 2, EPI_STORE>(p, rows_max, s);
+      break;
+    case EPI_SWIGLU_BWD:
+      e = big ? launch_tail_or_not<256, 128, 2, 4, 2, 64, 2, 1, EPI_SWIGLU_BWD>(p, rows_max, s)
+              : launch_tail_or_not<128, 128, 2, 2, 2, 32, 3, 2, EPI_SWIGLU_BWD>(p, rows_max, s);
       break;
     default:
       e = launch_tail_or_not<128, 256, 1, 2, 2, 32, 0, 1, EPI_STORE_F32_BIAS>(p, rows_max, s);

@@ -33,9 +33,28 @@ struct GemmParams {
   int part_rows;
   int slots;                // blocks resident at once; > 0 enables splitting the last partial
                             // round of tiles over K (set by the launcher)
+  int lda, ldb;             // row strides of A and B in elements (0: K)
+  // K-grouped mode (kgrouped = 1): the groups split the reduction instead of the rows.  Group g
+  // reduces over columns [kpad(g), kpad(g) + offsets[g+1] - offsets[g]) of A [M][lda] and
+  // B [N][ldb] (kpad as below) and writes its own C at C + g * c_gstride; every group has all M
+  // rows.  No gather, no split.
+  int kgrouped;
+  long long c_gstride;
+  // SwiGLU-backward epilogue (EPI_SWIGLU_BWD, two matrices: a = A B0^T, b = A B1^T): reads
+  // D = dh [rows][N], writes H = silu(a) * b [rows][N] and C [rows][ldc] with da in columns
+  // [0, N) and db in [N, 2N): da = dh * b * silu'(a), db = dh * silu(a).  All bf16.
+  const void* D;
+  void* H;
 };
 
-enum { EPI_SWIGLU = 0, EPI_STORE = 1, EPI_STORE_F32_BIAS = 2 };
+enum { EPI_SWIGLU = 0, EPI_STORE = 1, EPI_STORE_F32_BIAS = 2, EPI_SWIGLU_BWD = 3 };
+
+// Padded start of group g's columns in a K-grouped operand: each group starts on a multiple of 8
+// (16-byte loads never straddle two groups) and the layout depends on offsets[g] alone.  The
+// padded width of G groups holding R rows is kpad(R, G).
+__host__ __device__ __forceinline__ int kpad(int row_offset, int g) {
+  return ((row_offset + 7) & ~7) + 8 * g;
+}
 
 struct TileCoord {
   int g;        // group

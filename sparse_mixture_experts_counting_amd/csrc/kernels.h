@@ -40,5 +40,24 @@ void launch_aux_loss(const int32_t* counts, const float* prob_sum, const float* 
 // transpose.hip
 void launch_transpose(const void* src, int batch, int rows, int cols, int elem_bytes, void* dst,
                       hipStream_t s);
+void launch_transpose_ld(const void* src, int batch, int rows, int cols, int elem_bytes,
+                         void* dst, int ldd, long long dst_bstride, hipStream_t s);
+void launch_transpose_grouped(const void* src, int src_rows, const int32_t* gather,
+                              int gather_div, const int32_t* offsets, int G, int rows_max,
+                              int cols, void* dst, int ldd, hipStream_t s);
+
+// backward.hip
+void launch_combine_backward(const void* dy, const void* out, const int32_t* inv,
+                             const float* gate, int T, int d, int k, void* d_out, float* d_gate,
+                             hipStream_t s);
+void launch_gate_backward(const float* logits, const int32_t* topk_idx, const float* topk_gate,
+                          const float* d_gate, const int32_t* counts, int T, int E, int k, int mode,
+                          float alpha, float beta, float* d_logits, hipStream_t s);
+int router_wgrad_chunks(int T);
+void launch_router_wgrad(const void* x, bool bf16, const float* dL, int T, int d, int E,
+                         float* part, float* dw, hipStream_t s);
+void launch_router_xgrad(const float* dL, const void* w_r, bool bf16, int T, int d, int E,
+                         const void* add, void* dx, hipStream_t s);
+void launch_dense_offsets(int32_t* o, int T, hipStream_t s);
 
 }  // namespace moe

@@ -46,6 +46,38 @@ size_t ffn_workspace_bytes(int rows, bool grouped, int G, int d, int d_ff, moe_d
   return h_bytes(rows, d_ff, dt) + ffn_partial_bytes(rows, grouped, G, d, d_ff, dt);
 }
 
+// moe_expert_backward workspace (bf16): the transposed weights, the row-major intermediates, the
+// group-padded transposed operands of the weight-gradient products, two ints of dense offsets and
+// the split-K scratch of the input-gradient products, in this order.
+struct BwdLayout {
+  size_t w2t, w13t, dh, h, dab, doT, hT, dabT, xgT, offs, part, total;
+};
+BwdLayout bwd_layout(int rows, bool grouped, int G, int d, int d_ff) {
+  const size_t P = (size_t)moe::kpad(rows, G);
+  BwdLayout L;
+  size_t o = 0;
+  auto take = [&](size_t bytes) { const size_t at = o; o += align_up(bytes); return at; };
+  L.w2t = take((size_t)G * d_ff * d * 2);
+  L.w13t = take((size_t)G * d * 2 * d_ff * 2);
+  L.dh = take((size_t)rows * d_ff * 2);
+  L.h = take((size_t)rows * d_ff * 2);
+  L.dab = take((size_t)rows * 2 * d_ff * 2);
+  L.doT = take((size_t)d * P * 2);
+  L.hT = take((size_t)d_ff * P * 2);
+  L.dabT = take((size_t)2 * d_ff * P * 2);
+  L.xgT = take((size_t)d * P * 2);
+  L.offs = take(16);
+  const size_t p1 = moe::gemm_bf16_partial_bytes(rows, G, grouped, d_ff, d, moe::EPI_STORE);
+  const size_t p2 = moe::gemm_bf16_partial_bytes(rows, G, grouped, d, 2 * d_ff, moe::EPI_STORE);
+  L.part = take(p1 > p2 ? p1 : p2);
+  L.total = o;
+  return L;
+}
+
+size_t route_bwd_bytes(int T, int d, int E) {
+  return align_up((size_t)moe::router_wgrad_chunks(T) * E * d * sizeof(float));
+}
+
 }  // namespace
 
 extern "C" {
@@ -262,7 +294,7 @@ moe_status moe_expert_down(const void* h, const int32_t* offsets, int T, int d, 
 moe_status moe_combine(const void* expert_out, const int32_t* inv, const float* topk_gate, int T,
                        int d, int k, moe_dtype dt, const void* shared_out, void* y, void* stream) {
   if (T < 1 || d < 1 || k < 1) return MOE_ERR_ARG;
-  if (!expert_out || !inv || !topk_gate || !y || !dtype_ok(dt)) return MOE_ERR_ARG;
+  if (!expert_out || !inv || !y || !dtype_ok(dt)) return MOE_ERR_ARG;
   if (!aligned16(expert_out) || !aligned16(y) || (shared_out && !aligned16(shared_out)))
     return MOE_ERR_ARG;
   if (k > kMaxK) return MOE_ERR_UNSUPPORTED;
@@ -300,6 +332,141 @@ moe_status moe_transpose(const void* src, int batch, int rows, int cols, moe_dty
   const long long elems = (long long)batch * rows * cols;
   if (elems / batch / rows != cols) return MOE_ERR_UNSUPPORTED;
   moe::launch_transpose(src, batch, rows, cols, (int)elem_bytes(dt), dst, (hipStream_t)stream);
+  return launched();
+}
+
+size_t moe_backward_workspace_bytes(int T, int d, int d_ff, int E, int k, moe_dtype dt) {
+  if (T < 1 || E < 1 || k < 1 || d_ff < 1 || d < 1 || dt != MOE_BF16) return 0;
+  const size_t a = bwd_layout(T * k, true, E, d, d_ff).total;
+  const size_t b = bwd_layout(T, false, 1, d, d_ff).total;   // shared / dense expert
+  const size_t c = route_bwd_bytes(T, d, E);
+  const size_t m = a > b ? a : b;
+  return m > c ? m : c;
+}
+
+moe_status moe_combine_backward(const void* dy, const void* expert_out, const int32_t* inv,
+                                const float* topk_gate, int T, int d, int k, moe_dtype dt,
+                                void* d_out, float* d_gate, void* stream) {
+  if (T < 1 || d < 1 || k < 1) return MOE_ERR_ARG;
+  if (!dy || !expert_out || !inv || !topk_gate || !d_out || !d_gate || !dtype_ok(dt))
+    return MOE_ERR_ARG;
+  if (!aligned16(dy) || !aligned16(expert_out) || !aligned16(d_out)) return MOE_ERR_ARG;
+  if (dt != MOE_BF16 || k > kMaxK || (d % 8) != 0) return MOE_ERR_UNSUPPORTED;
+  if (!fits_i32((long long)T * k) || !fits_i32((long long)T * k * (long long)d))
+    return MOE_ERR_UNSUPPORTED;
+  moe::launch_combine_backward(dy, expert_out, inv, topk_gate, T, d, k, d_out, d_gate,
+                               (hipStream_t)stream);
+  return launched();
+}
+
+moe_status moe_expert_backward(const void* x, const int32_t* perm, const int32_t* offsets, int T,
+                               int d, int d_ff, int E, int k, const void* w1, const void* w3,
+                               const void* w2, const void* d_out, moe_dtype dt, void* dx_rows,
+                               float* dw1, float* dw3, float* dw2, void* workspace,
+                               size_t ws_bytes, void* stream) {
+  const bool grouped = perm != nullptr;
+  moe_status st = check_ffn_args(x, w1, w3, dx_rows, grouped, offsets, T, d, d_ff, E, k, dt);
+  if (st != MOE_OK) return st;
+  if (!w2 || !d_out || !dw1 || !dw3 || !dw2 || !workspace) return MOE_ERR_ARG;
+  if (!aligned16(w2) || !aligned16(d_out) || !aligned16(dw1) || !aligned16(dw3) ||
+      !aligned16(dw2) || !aligned16(workspace))
+    return MOE_ERR_ARG;
+  if (dt != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  const int G = grouped ? E : 1;
+  const int rows = grouped ? T * k : T;
+  const int P = moe::kpad(rows, G);
+  if (!fits_i32((long long)rows * 2 * d_ff) || !fits_i32((long long)2 * d_ff * P) ||
+      !fits_i32((long long)d * P) || !fits_i32((long long)G * d * 2 * d_ff))
+    return MOE_ERR_UNSUPPORTED;
+  const BwdLayout L = bwd_layout(rows, grouped, G, d, d_ff);
+  if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  void *w2t = ws + L.w2t, *w13t = ws + L.w13t, *dh = ws + L.dh, *h = ws + L.h, *dab = ws + L.dab;
+  void *doT = ws + L.doT, *hT = ws + L.hT, *dabT = ws + L.dabT, *xgT = ws + L.xgT;
+  int32_t* offs = grouped ? (int32_t*)offsets : (int32_t*)(ws + L.offs);
+  float* part = (float*)(ws + L.part);
+  if (!grouped) moe::launch_dense_offsets(offs, T, s);
+
+  // Weights as the input-gradient products read them: w2T[e][n][i] = w2[e][i][n], and
+  // w13T[e][i] = (w1[e][.][i], w3[e][.][i]) side by side (K = 2 d_ff).
+  moe::launch_transpose_ld(w2, G, d, d_ff, 2, w2t, d, (long long)d_ff * d, s);
+  moe::launch_transpose_ld(w1, G, d_ff, d, 2, w13t, 2 * d_ff, (long long)d * 2 * d_ff, s);
+  moe::launch_transpose_ld(w3, G, d_ff, d, 2, (uint16_t*)w13t + d_ff, 2 * d_ff,
+                           (long long)d * 2 * d_ff, s);
+  hipError_t e;
+  {   // dh = d_out w2 (rows of each expert)
+    moe::GemmParams q{};
+    q.A = d_out; q.a_rows = rows; q.gather_div = 1;
+    q.offsets = grouped ? offsets : nullptr; q.G = G; q.M = T;
+    q.N = d_ff; q.K = d; q.B0 = w2t; q.b_gstride = (long long)d_ff * d;
+    q.C = dh; q.ldc = d_ff; q.part = part;
+    if ((e = moe::launch_gemm_bf16(q, rows, moe::EPI_STORE, s)) != hipSuccess) return MOE_ERR_DEVICE;
+  }
+  {   // a, b recomputed; h, da, db from dh
+    moe::GemmParams q{};
+    q.A = x; q.a_rows = T; q.gather = perm; q.gather_div = k;
+    q.offsets = grouped ? offsets : nullptr; q.G = G; q.M = T;
+    q.N = d_ff; q.K = d; q.B0 = w1; q.B1 = w3; q.b_gstride = (long long)d * d_ff;
+    q.C = dab; q.ldc = 2 * d_ff; q.D = dh; q.H = h;
+    if ((e = moe::launch_gemm_bf16(q, rows, moe::EPI_SWIGLU_BWD, s)) != hipSuccess)
+      return MOE_ERR_DEVICE;
+  }
+  {   // dx_rows = da w1 + db w3
+    moe::GemmParams q{};
+    q.A = dab; q.a_rows = rows; q.gather_div = 1;
+    q.offsets = grouped ? offsets : nullptr; q.G = G; q.M = T;
+    q.N = d; q.K = 2 * d_ff; q.B0 = w13t; q.b_gstride = (long long)d * 2 * d_ff;
+    q.C = dx_rows; q.ldc = d; q.part = part;
+    if ((e = moe::launch_gemm_bf16(q, rows, moe::EPI_STORE, s)) != hipSuccess) return MOE_ERR_DEVICE;
+  }
+  // Operands of the weight gradients, reduced over each expert's rows.
+  const int32_t* toffs = grouped ? offsets : nullptr;
+  moe::launch_transpose_grouped(d_out, rows, nullptr, 1, toffs, G, rows, d, doT, P, s);
+  moe::launch_transpose_grouped(h, rows, nullptr, 1, toffs, G, rows, d_ff, hT, P, s);
+  moe::launch_transpose_grouped(dab, rows, nullptr, 1, toffs, G, rows, 2 * d_ff, dabT, P, s);
+  moe::launch_transpose_grouped(x, T, perm, k, toffs, G, rows, d, xgT, P, s);
+  struct WG { const void* A; int M; const void* B; int N; float* C; };
+  const WG wg[3] = {{doT, d, hT, d_ff, dw2},                                   // dw2 = d_out^T h
+                    {dabT, d_ff, xgT, d, dw1},                                 // dw1 = da^T x
+                    {(uint16_t*)dabT + (size_t)d_ff * P, d_ff, xgT, d, dw3}};  // dw3 = db^T x
+  for (const WG& w : wg) {
+    moe::GemmParams q{};
+    q.A = w.A; q.a_rows = w.M; q.lda = P; q.gather_div = 1;
+    q.offsets = offs; q.G = G; q.M = w.M; q.N = w.N; q.K = P;
+    q.B0 = w.B; q.ldb = P; q.C = w.C; q.ldc = w.N;
+    q.kgrouped = 1; q.c_gstride = (long long)w.M * w.N;
+    if ((e = moe::launch_gemm_bf16(q, rows, moe::EPI_STORE_F32_BIAS, s)) != hipSuccess)
+      return MOE_ERR_DEVICE;
+  }
+  return launched();
+}
+
+moe_status moe_route_backward(const void* x, const void* w_r, const float* logits,
+                              const int32_t* topk_idx, const float* topk_gate,
+                              const float* d_gate, const int32_t* counts, int T, int d, int E,
+                              int k, moe_dtype dt, moe_gating gating, float alpha, float beta,
+                              const void* dx_add, float* d_logits, float* dw_r, void* dx,
+                              void* workspace, size_t ws_bytes, void* stream) {
+  if (T < 1 || d < 1 || E < 1 || k < 1 || k > E) return MOE_ERR_ARG;
+  if (!x || !w_r || !logits || !topk_idx || !topk_gate || !d_gate || !d_logits || !dw_r || !dx ||
+      !workspace || !dtype_ok(dt))
+    return MOE_ERR_ARG;
+  if (gating < MOE_GATE_SOFTMAX_TOPK || gating > MOE_GATE_SIGMOID_TOPK) return MOE_ERR_ARG;
+  if (!counts && alpha != 0.0f) return MOE_ERR_ARG;
+  if (!aligned16(x) || !aligned16(w_r) || !aligned16(dx) || (dx_add && !aligned16(dx_add)))
+    return MOE_ERR_ARG;
+  if (E > kMaxE || k > kMaxK || (d % 8) != 0) return MOE_ERR_UNSUPPORTED;
+  if (!fits_i32((long long)T * E) || !fits_i32((long long)T * d) ||
+      !fits_i32((long long)E * d * 16))
+    return MOE_ERR_UNSUPPORTED;
+  if (ws_bytes < route_bwd_bytes(T, d, E)) return MOE_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  const bool bf16 = dt == MOE_BF16;
+  moe::launch_gate_backward(logits, topk_idx, topk_gate, d_gate, alpha != 0.0f ? counts : nullptr,
+                            T, E, k, (int)gating, alpha, beta, d_logits, s);
+  moe::launch_router_wgrad(x, bf16, d_logits, T, d, E, (float*)workspace, dw_r, s);
+  moe::launch_router_xgrad(d_logits, w_r, bf16, T, d, E, dx_add, dx, s);
   return launched();
 }
 

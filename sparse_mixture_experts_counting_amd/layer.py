@@ -1,4 +1,5 @@
-"""One MoE layer forward on the GPU through libmoe: buffers plus the five C entry points in order.
+"""One MoE layer forward (and backward) on the GPU through libmoe: buffers plus the C entry points
+in order.
 
 Score+Select (moe_route) -> Dispatch (moe_dispatch) -> Compute (moe_expert_ffn, routed experts and
 the shared expert when there is one) -> Combine (moe_combine) -> Balance (moe_aux_loss), the step
@@ -97,3 +98,63 @@ def forward(cfg, inp, b, stream=None, logits_in=False):
     combine(cfg, b, stream)
     losses(cfg, b, stream)
     return b
+
+
+@dataclasses.dataclass
+class MoEGrads:
+    d_out: torch.Tensor       # [T*k, d] gradient of each expert row
+    d_gate: torch.Tensor      # [T, k] fp32
+    dx_rows: torch.Tensor     # [T*k, d] input gradient of each expert row
+    d_logits: torch.Tensor    # [T, E] fp32
+    dx_route: torch.Tensor    # [T, d] router (+ shared expert) part of dx
+    dx: torch.Tensor          # [T, d]
+    dw_r: torch.Tensor        # [E, d] fp32
+    dw1: torch.Tensor         # [E, d_ff, d] fp32
+    dw3: torch.Tensor
+    dw2: torch.Tensor         # [E, d, d_ff] fp32
+    dshared: tuple            # (dw1s, dw3s, dw2s) fp32 or None
+    dx_shared: torch.Tensor   # [T, d] or None
+    workspace: torch.Tensor
+
+
+def alloc_grads(cfg, device="cuda"):
+    dev = torch.device(device)
+    if cfg.dtype != "bf16":
+        raise ValueError("the backward pass runs bf16 layers only")
+    T, d, E, k, f = cfg.T, cfg.d, cfg.E, cfg.k, cfg.d_ff
+    bf = dict(dtype=torch.bfloat16, device=dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    ws = lm.backward_workspace_bytes(T, d, f, E, k, lm.MOE_BF16)
+    shared = None
+    if cfg.n_shared:
+        shared = (torch.empty((f, d), **f32), torch.empty((f, d), **f32),
+                  torch.empty((d, f), **f32))
+    return MoEGrads(
+        d_out=torch.empty((T * k, d), **bf), d_gate=torch.empty((T, k), **f32),
+        dx_rows=torch.empty((T * k, d), **bf), d_logits=torch.empty((T, E), **f32),
+        dx_route=torch.empty((T, d), **bf), dx=torch.empty((T, d), **bf),
+        dw_r=torch.empty((E, d), **f32), dw1=torch.empty((E, f, d), **f32),
+        dw3=torch.empty((E, f, d), **f32), dw2=torch.empty((E, d, f), **f32), dshared=shared,
+        dx_shared=torch.empty((T, d), **bf) if cfg.n_shared else None,
+        workspace=torch.empty(ws, dtype=torch.uint8, device=dev))
+
+
+def backward(cfg, inp, b, dy, g, stream=None):
+    """Gradient of <dy, y> + aux + z after forward(cfg, inp, b): the steps in reverse order
+    (Combine, Compute of the routed and shared experts, Score and Balance), then the input
+    gradient rows added per token.  No host synchronisation inside."""
+    T, d, f, E, k = cfg.T, cfg.d, cfg.d_ff, cfg.E, cfg.k
+    bf = lm.MOE_BF16
+    lm.combine_backward(dy, b.expert_out, b.inv, b.topk_gate, T, d, k, bf, g.d_out, g.d_gate,
+                        stream)
+    lm.expert_backward(inp.x, b.perm, b.offsets, T, d, f, E, k, inp.w1, inp.w3, inp.w2, g.d_out,
+                       bf, g.dx_rows, g.dw1, g.dw3, g.dw2, g.workspace, stream)
+    if cfg.n_shared:
+        w1s, w3s, w2s = inp.shared
+        lm.expert_backward(inp.x, None, None, T, d, f, 1, 1, w1s, w3s, w2s, dy, bf, g.dx_shared,
+                           *g.dshared, g.workspace, stream)
+    lm.route_backward(inp.x, inp.w_r, b.logits, b.topk_idx, b.topk_gate, g.d_gate, b.counts, T, d,
+                      E, k, bf, GATING_CODE[cfg.gating], cfg.alpha, cfg.beta, g.dx_shared,
+                      g.d_logits, g.dw_r, g.dx_route, g.workspace, stream)
+    lm.combine(g.dx_rows, b.inv, None, T, d, k, bf, g.dx_route, g.dx, stream)
+    return g

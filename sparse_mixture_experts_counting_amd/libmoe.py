@@ -22,7 +22,8 @@ STATUS = {0: "MOE_OK", 1: "MOE_ERR_ARG", 2: "MOE_ERR_UNSUPPORTED", 3: "MOE_ERR_W
 
 EXPORTS = ("moe_workspace_bytes", "moe_status_str", "moe_route", "moe_dispatch", "moe_expert_ffn",
            "moe_expert_up", "moe_expert_down", "moe_combine", "moe_aux_loss",
-           "moe_update_select_bias", "moe_transpose")
+           "moe_update_select_bias", "moe_transpose", "moe_backward_workspace_bytes",
+           "moe_combine_backward", "moe_expert_backward", "moe_route_backward")
 
 
 class MoEError(RuntimeError):
@@ -51,8 +52,16 @@ _lib.moe_combine.argtypes = [_p, _p, _p, _i, _i, _i, _i, _p, _p, _p]
 _lib.moe_aux_loss.argtypes = [_p, _p, _p, _i, _i, _i, _f, _f, _p, _p, _p]
 _lib.moe_transpose.argtypes = [_p, _i, _i, _i, _i, _p, _p]
 _lib.moe_update_select_bias.argtypes = [_p, _i, _i, _i, _f, _p, _p]
+_lib.moe_backward_workspace_bytes.argtypes = [_i, _i, _i, _i, _i, _i]
+_lib.moe_backward_workspace_bytes.restype = _sz
+_lib.moe_combine_backward.argtypes = [_p, _p, _p, _p, _i, _i, _i, _i, _p, _p, _p]
+_lib.moe_expert_backward.argtypes = [_p, _p, _p, _i, _i, _i, _i, _i, _p, _p, _p, _p, _i, _p, _p,
+                                     _p, _p, _p, _sz, _p]
+_lib.moe_route_backward.argtypes = [_p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _f, _f,
+                                    _p, _p, _p, _p, _p, _sz, _p]
 for _n in ("moe_route", "moe_dispatch", "moe_expert_ffn", "moe_expert_up", "moe_expert_down",
-           "moe_combine", "moe_aux_loss", "moe_transpose", "moe_update_select_bias"):
+           "moe_combine", "moe_aux_loss", "moe_transpose", "moe_update_select_bias",
+           "moe_combine_backward", "moe_expert_backward", "moe_route_backward"):
     getattr(_lib, _n).restype = _i
 
 
@@ -153,3 +162,30 @@ def update_select_bias(counts, T, E, k, rate, select_bias, stream=None):
     """select_bias[e] += rate * sign(T*k - E*counts[e]) (aux-loss-free balancing step)."""
     _check("moe_update_select_bias", _lib.moe_update_select_bias(
         _ptr(counts), T, E, k, float(rate), _ptr(select_bias), _stream(stream)))
+
+
+def backward_workspace_bytes(T, d, d_ff, E, k, dt):
+    return int(_lib.moe_backward_workspace_bytes(T, d, d_ff, E, k, dt))
+
+
+def combine_backward(dy, expert_out, inv, topk_gate, T, d, k, dt, d_out, d_gate, stream=None):
+    _check("moe_combine_backward", _lib.moe_combine_backward(
+        _ptr(dy), _ptr(expert_out), _ptr(inv), _ptr(topk_gate), T, d, k, dt, _ptr(d_out),
+        _ptr(d_gate), _stream(stream)))
+
+
+def expert_backward(x, perm, offsets, T, d, d_ff, E, k, w1, w3, w2, d_out, dt, dx_rows, dw1, dw3,
+                    dw2, workspace, stream=None):
+    _check("moe_expert_backward", _lib.moe_expert_backward(
+        _ptr(x), _ptr(perm), _ptr(offsets), T, d, d_ff, E, k, _ptr(w1), _ptr(w3), _ptr(w2),
+        _ptr(d_out), dt, _ptr(dx_rows), _ptr(dw1), _ptr(dw3), _ptr(dw2), _ptr(workspace),
+        _nbytes(workspace), _stream(stream)))
+
+
+def route_backward(x, w_r, logits, topk_idx, topk_gate, d_gate, counts, T, d, E, k, dt, gating,
+                   alpha, beta, dx_add, d_logits, dw_r, dx, workspace, stream=None):
+    _check("moe_route_backward", _lib.moe_route_backward(
+        _ptr(x), _ptr(w_r), _ptr(logits), _ptr(topk_idx), _ptr(topk_gate), _ptr(d_gate),
+        _ptr(counts), T, d, E, k, dt, gating, float(alpha), float(beta), _ptr(dx_add),
+        _ptr(d_logits), _ptr(dw_r), _ptr(dx), _ptr(workspace), _nbytes(workspace),
+        _stream(stream)))

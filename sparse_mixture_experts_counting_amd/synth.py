@@ -148,3 +148,12 @@ def p5_main_logits():
     i = np.arange(64 * 8, dtype=np.uint64)
     v = ((i * np.uint64(2654435761)) >> np.uint64(7)) % np.uint64(1000)
     return (v.astype(np.float32) / np.float32(250.0)).reshape(64, 8)
+
+
+def make_dy(cfg, seed=0, device="cpu"):
+    """Upstream gradient of the layer output for the backward pass: standard normal [T, d] in the
+    layer dtype, from its own generator (seed + 1000003) so the forward inputs are unchanged."""
+    gen = torch.Generator(device=torch.device(device))
+    gen.manual_seed(seed + 1000003)
+    dt = torch.float32 if cfg.dtype == "fp32" else torch.bfloat16
+    return torch.randn((cfg.T, cfg.d), generator=gen, device=torch.device(device)).to(dt)

@@ -29,7 +29,9 @@ def test_every_declared_symbol_is_exported(lm):
     names = _declared()
     assert set(names) == {"moe_workspace_bytes", "moe_status_str", "moe_route", "moe_dispatch",
                           "moe_expert_ffn", "moe_expert_up", "moe_expert_down", "moe_combine",
-                          "moe_aux_loss", "moe_update_select_bias", "moe_transpose"}
+                          "moe_aux_loss", "moe_update_select_bias", "moe_transpose",
+                          "moe_backward_workspace_bytes", "moe_combine_backward",
+                          "moe_expert_backward", "moe_route_backward"}
     lib = ctypes.CDLL(lm.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -137,3 +139,57 @@ def test_update_select_bias_argument_errors(lm):
     assert L.moe_update_select_bias(FAKE, 0, 4, 2, f(0.01), FAKE, None) == 1
     assert L.moe_update_select_bias(FAKE, 4, 0, 2, f(0.01), FAKE, None) == 1
     assert L.moe_update_select_bias(FAKE, 4, 2000, 2, f(0.01), FAKE, None) == 2
+
+
+def test_backward_workspace_bytes(lm):
+    T, d, f, E, k = 4096, 4096, 14336, 8, 2
+    ws = lm.backward_workspace_bytes(T, d, f, E, k, lm.MOE_BF16)
+    assert ws >= 3 * E * d * f * 2                 # transposed copies of the three weights
+    assert ws >= T * k * 4 * f * 2                  # dh, h, da and db of every expert row
+    assert lm.backward_workspace_bytes(T, d, f, E, k, lm.MOE_F32) == 0
+    assert lm.backward_workspace_bytes(0, d, f, E, k, lm.MOE_BF16) == 0
+
+
+def test_combine_backward_argument_errors(lm):
+    L = lm.lib()
+    args = lambda **kw: [kw.get("dy", FAKE), FAKE, FAKE, FAKE, kw.get("T", 4), kw.get("d", 16),
+                         kw.get("k", 2), kw.get("dt", 1), FAKE, kw.get("dg", FAKE), None]
+    assert L.moe_combine_backward(*args(T=0)) == 1
+    assert L.moe_combine_backward(*args(dy=None)) == 1
+    assert L.moe_combine_backward(*args(dg=None)) == 1
+    assert L.moe_combine_backward(*args(dy=FAKE + 2)) == 1
+    assert L.moe_combine_backward(*args(dt=0)) == 2                  # fp32 layers: unsupported
+    assert L.moe_combine_backward(*args(d=12)) == 2
+    assert L.moe_combine_backward(*args(k=33)) == 2
+
+
+def test_expert_backward_argument_errors(lm):
+    L = lm.lib()
+    args = lambda **kw: [FAKE, kw.get("perm", FAKE), kw.get("offs", FAKE), kw.get("T", 4),
+                         kw.get("d", 16), kw.get("f", 32), kw.get("E", 4), kw.get("k", 2), FAKE,
+                         FAKE, FAKE, kw.get("dout", FAKE), kw.get("dt", 1), FAKE, FAKE, FAKE,
+                         kw.get("dw2", FAKE), kw.get("ws", FAKE), kw.get("wsb", 1 << 40), None]
+    assert L.moe_expert_backward(*args(T=0)) == 1
+    assert L.moe_expert_backward(*args(offs=None)) == 1               # routed rows need offsets
+    assert L.moe_expert_backward(*args(perm=None)) == 1               # dense mode needs E == 1
+    assert L.moe_expert_backward(*args(dout=None)) == 1
+    assert L.moe_expert_backward(*args(dw2=None)) == 1
+    assert L.moe_expert_backward(*args(ws=None)) == 1
+    assert L.moe_expert_backward(*args(dt=0)) == 2
+    assert L.moe_expert_backward(*args(f=36)) == 2
+    assert L.moe_expert_backward(*args(wsb=16)) == 3
+
+
+def test_route_backward_argument_errors(lm):
+    L = lm.lib()
+    args = lambda **kw: [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, kw.get("counts", FAKE),
+                         kw.get("T", 4), kw.get("d", 16), kw.get("E", 4), kw.get("k", 2),
+                         kw.get("dt", 1), kw.get("g", 0), kw.get("alpha", 0.01), 0.001, None,
+                         FAKE, FAKE, FAKE, FAKE, kw.get("wsb", 1 << 40), None]
+    assert L.moe_route_backward(*args(T=0)) == 1
+    assert L.moe_route_backward(*args(k=5)) == 1
+    assert L.moe_route_backward(*args(g=3)) == 1
+    assert L.moe_route_backward(*args(counts=None)) == 1              # aux term needs counts
+    assert L.moe_route_backward(*args(E=2000, k=2)) == 2
+    assert L.moe_route_backward(*args(d=12)) == 2
+    assert L.moe_route_backward(*args(wsb=16)) == 3
