@@ -12,6 +12,12 @@ stream the kernels run on, the roofline of the dominant kernel (the fused up pro
 grouped GEMM) against the bf16 matrix-core peak, and the CPU oracle timed on a bounded sample.
 
     python bench.py [--steps K] [--warmup W] [--workload mixtral_prefill]
+
+With --pass train a step is the forward followed by the backward pass of the layer (gradients of
+<dy, y> + aux + z for x, the router and every expert weight: moe_combine_backward,
+moe_expert_backward for the routed and shared experts, moe_route_backward, and moe_combine adding
+each token's input-gradient rows); that line reports training-step tokens/s and the roofline of
+the expert backward.
 """
 
 import argparse
@@ -101,6 +107,7 @@ def main():
                     help="tokens of the workload the CPU oracle runs on (0: all)")
     ap.add_argument("--cpu-repeats", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--pass", dest="mode", choices=("forward", "train"), default="forward")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -117,6 +124,8 @@ def main():
     cfg = synth.CONFIGS[args.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.mode == "train":
+        return train_bench(args, cfg, dev, torch, layer, lm, synth)
     log("bench: workload %s, generating inputs on the device" % cfg.name)
     inp = synth.make_inputs(cfg, seed=args.seed, device=dev)
     buf = layer.alloc_buffers(cfg, dev)
@@ -232,6 +241,127 @@ def main():
     if not args.no_cpu_baseline:
         log("bench: timing the CPU oracle on a sample")
         v, threads, sample, secs = cpu_baseline(cfg, inp, args.cpu_sample_tokens, args.cpu_repeats)
+        result["cpu_baseline"] = {"value": v, "unit": "tokens/s", "cores": threads,
+                                  "kind": "oracle", "sample": sample, "seconds": secs}
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline_train(cfg, inp, dy, n_tokens, repeats):
+    """The CPU oracle's forward + backward (float64 NumPy, as it stands) on the first n_tokens
+    tokens, `repeats` times.  Returns tokens/s, BLAS threads, the sample and the seconds spent."""
+    from oracle import moe_oracle as O
+    from threadpoolctl import threadpool_info
+
+    n = min(n_tokens, cfg.T)
+    f = lambda t: t.detach().float().cpu().numpy()
+    x, w_r, dyh = f(inp.x[:n]), f(inp.w_r), f(dy[:n]).astype("float64")
+    bias = None if inp.bias is None else f(inp.bias)
+    mode = {"softmax_topk": 0, "softmax_all": 1, "sigmoid_topk": 2}[cfg.gating]
+    w1, w3, w2 = f(inp.w1), f(inp.w3), f(inp.w2)
+    shared = tuple(f(w) for w in inp.shared) if inp.shared is not None else None
+    t0 = time.perf_counter()
+    for _ in range(repeats):
+        O.backward(x, w_r, w1, w3, w2, dyh, cfg.k, mode, capacity=cfg.capacity or None,
+                   bias=bias, shared=shared, alpha=cfg.alpha, beta=cfg.beta)
+    secs = time.perf_counter() - t0
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()
+                   if p.get("user_api") == "blas"] or [1])
+    sample = ("first %d of %d tokens of %s, forward + backward, float64 NumPy oracle, %d runs"
+              % (n, cfg.T, cfg.name, repeats))
+    return n * repeats / secs, threads, sample, secs
+
+
+def train_bench(args, cfg, dev, torch, layer, lm, synth):
+    if cfg.dtype != "bf16":
+        print("bench.py: the backward pass runs bf16 layers only", file=sys.stderr)
+        sys.exit(2)
+    log("bench: workload %s (forward + backward), generating inputs on the device" % cfg.name)
+    inp = synth.make_inputs(cfg, seed=args.seed, device=dev)
+    dy = synth.make_dy(cfg, seed=args.seed, device=dev)
+    buf = layer.alloc_buffers(cfg, dev)
+    g = layer.alloc_grads(cfg, dev)
+    stream = torch.cuda.current_stream(dev)
+    T, d, E, k, f = cfg.T, cfg.d, cfg.E, cfg.k, cfg.d_ff
+    bf = lm.MOE_BF16
+    from sparse_mixture_experts_counting_amd.synth import GATING_CODE
+    stages = ["forward", "combine_bwd", "expert_bwd", "shared_bwd", "route_bwd", "dx_combine"]
+    if not cfg.n_shared:
+        stages.remove("shared_bwd")
+
+    def step(ev=None):
+        def mark(i):
+            if ev is not None:
+                ev[i].record(stream)
+        mark(0)
+        layer.forward(cfg, inp, buf)
+        mark(1)
+        lm.combine_backward(dy, buf.expert_out, buf.inv, buf.topk_gate, T, d, k, bf, g.d_out,
+                            g.d_gate)
+        mark(2)
+        lm.expert_backward(inp.x, buf.perm, buf.offsets, T, d, f, E, k, inp.w1, inp.w3, inp.w2,
+                           g.d_out, bf, g.dx_rows, g.dw1, g.dw3, g.dw2, g.workspace)
+        mark(3)
+        i = 3
+        if cfg.n_shared:
+            w1s, w3s, w2s = inp.shared
+            lm.expert_backward(inp.x, None, None, T, d, f, 1, 1, w1s, w3s, w2s, dy, bf,
+                               g.dx_shared, *g.dshared, g.workspace)
+            i += 1
+            mark(i)
+        lm.route_backward(inp.x, inp.w_r, buf.logits, buf.topk_idx, buf.topk_gate, g.d_gate,
+                          buf.counts, T, d, E, k, bf, GATING_CODE[cfg.gating], cfg.alpha,
+                          cfg.beta, g.dx_shared, g.d_logits, g.dw_r, g.dx_route, g.workspace)
+        mark(i + 1)
+        lm.combine(g.dx_rows, buf.inv, None, T, d, k, bf, g.dx_route, g.dx)
+        mark(i + 2)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize(dev)
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)]
+              for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(events[s])
+    torch.cuda.synchronize(dev)
+    wall = time.perf_counter() - t0
+    stage_ms = {name: sum(events[s][j].elapsed_time(events[s][j + 1])
+                          for s in range(args.steps)) / args.steps
+                for j, name in enumerate(stages)}
+    ms_per_step = wall * 1e3 / args.steps
+    n_kept = int(buf.offsets[-1].item())
+    # Algorithmic FLOPs of the expert backward: dh (2 d d_ff per row), dx (4), dw1 + dw3 (4),
+    # dw2 (2); the recomputed up projection (4 more) is not counted.
+    bwd_flops = 12.0 * d * f * n_kept
+    achieved = bwd_flops / (stage_ms["expert_bwd"] * 1e-3) / 1e12
+    fwd_flops = 2.0 * T * d * E + 6.0 * d * f * (n_kept + T * cfg.n_shared)
+    train_flops = fwd_flops + 2.0 * 2 * T * d * E + 12.0 * d * f * (n_kept + T * cfg.n_shared)
+    result = {
+        "metric": "MoE layer training step (forward + backward) tokens/s at 1 GPU",
+        "value": T / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded randn inputs, upstream gradient and random-init expert "
+                "weights of the workload's shapes, drawn on the device)",
+        "config": {"workload": cfg.name, "pass": "forward+backward", "T": T, "d": d, "E": E,
+                   "k": k, "d_ff": f, "gating": cfg.gating, "capacity": cfg.capacity or None,
+                   "shared_experts": cfg.n_shared, "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "mfma",
+                     "kernel": "moe_expert_backward (routed): 6 grouped GEMMs + transposes",
+                     "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None},
+        "layer": {"algorithmic_flops": train_flops,
+                  "tflops": train_flops / (ms_per_step * 1e-3) / 1e12,
+                  "kept_assignments": n_kept},
+        "stage_ms": stage_ms,
+    }
+    if not args.no_cpu_baseline:
+        log("bench: timing the CPU oracle (forward + backward) on a sample")
+        n = args.cpu_sample_tokens if args.cpu_sample_tokens > 0 else 256
+        v, threads, sample, secs = cpu_baseline_train(cfg, inp, dy, n, args.cpu_repeats)
         result["cpu_baseline"] = {"value": v, "unit": "tokens/s", "cores": threads,
                                   "kind": "oracle", "sample": sample, "seconds": secs}
     else:

@@ -54,6 +54,12 @@ __device__ __forceinline__ int swz(int r) {
     return (r ^ ((r >> 3) & 3)) & 7;    // 128-byte rows: eight units
 }
 
+// Value of the other lane of an adjacent pair (lanes 2c and 2c + 1 swap: a DPP quad permute).
+__device__ __forceinline__ float swap_pair(float x) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, false));
+}
+
 // silu(g) = g / (1 + e^-g) with the hardware base-2 exponential and reciprocal (about 1 ulp each;
 // the result is rounded to bf16).  Saturates to g for large g and to -0 for very negative g.
 __device__ __forceinline__ float silu(float g) {
@@ -141,16 +147,26 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_bf16_kernel(const G
   TileCoord tc;
   int kc = 0, nsplit = p.ksplit, rtile = -1;
   int kg_beg = 0, kg_len = 0;               // K-grouped mode: this group's reduction columns
-  if (p.kgrouped) {                         // tiles: group-major, m-tiles of an n-tile adjacent
+  if (p.kgrouped) {
+    // Tiles group-major; inside a group, bands of 8 m-tiles walked n-tile by n-tile.  Blocks take
+    // tiles in index order, so block b's XCD (b % 8) always gets the same m-tile of a band and
+    // keeps that A tile in its L2 across the n-tiles.  (A tile's work grows with its group's row
+    // count, so contiguous runs of tiles per XCD would load the XCDs unevenly under skewed
+    // routing.)
     const int MT = (p.M + BM - 1) / BM;
     const int per = MT * NT;
     if ((int)blockIdx.x >= p.G * per) return;
-    const int t = xcd_order(blockIdx.x, p.G * per);
+    const int t = blockIdx.x;
     tc.g = t / per;
     const int local = t - tc.g * per;
-    tc.row0 = (local % MT) * BM;
+    constexpr int GM = 8;
+    const int band = local / (GM * NT);
+    const int m_first = band * GM;
+    const int gm = min(MT - m_first, GM);
+    const int in = local - band * GM * NT;
+    tc.row0 = (m_first + in % gm) * BM;
     tc.row_end = p.M;
-    tc.n_tile = local / MT;
+    tc.n_tile = in / gm;
     const int o0 = p.offsets[tc.g];
     kg_beg = __builtin_amdgcn_readfirstlane(kpad(o0, tc.g));
     kg_len = __builtin_amdgcn_readfirstlane(p.offsets[tc.g + 1] - o0);
@@ -449,6 +465,50 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_bf16_kernel(const G
                                                          (EPI == EPI_STORE_F32_BIAS ? 4 : 2))
                               : p.C;
   if constexpr (EPI == EPI_SWIGLU_BWD) {   // never split (the launcher passes no workspace)
+    if (N % 2 == 0 && p.ldc % 2 == 0) {
+      // Two columns per lane as in the bf16 store below: after the pair exchange the even lane
+      // holds row a and the odd lane row b of columns (2c, 2c+1); dh is read and h, da, db are
+      // written 4 bytes at a time.
+      const bool odd = lane & 1;
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          const int col0 = n_base + wn0 + j * 32 + (l32 & ~1);
+#pragma unroll
+          for (int r = 0; r < 16; r += 2) {
+            const float ga = swap_pair(odd ? acc[0][i][j][r] : acc[0][i][j][r + 1]);
+            const float gb = swap_pair(odd ? acc[NMAT - 1][i][j][r] : acc[NMAT - 1][i][j][r + 1]);
+            const int rr = odd ? r + 1 : r;
+            const int row = tc.row0 + wm0 + i * 32 + 8 * (rr >> 2) + 4 * h + (rr & 3);
+            if (row >= tc.row_end || col0 >= N) continue;
+            float a[2], b[2];
+            a[0] = odd ? ga : acc[0][i][j][r];
+            a[1] = odd ? acc[0][i][j][r + 1] : ga;
+            b[0] = odd ? gb : acc[NMAT - 1][i][j][r];
+            b[1] = odd ? acc[NMAT - 1][i][j][r + 1] : gb;
+            const size_t o = (size_t)row * N + col0;
+            const uint32_t dhw = *(const uint32_t*)((const uint16_t*)p.D + o);
+            float hv[2], da[2], db[2];
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+              const float dh = q ? bf16_hi(dhw) : bf16_lo(dhw);
+              const float sg =
+                  __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * a[q]));
+              const float sa = a[q] * sg;
+              hv[q] = sa * b[q];
+              da[q] = dh * b[q] * (sg * (1.0f + a[q] * (1.0f - sg)));
+              db[q] = dh * sa;
+            }
+            *(uint32_t*)((uint16_t*)p.H + o) = pack_bf16x2(hv[0], hv[1]);
+            uint16_t* dab = (uint16_t*)p.C + (size_t)row * p.ldc + col0;
+            *(uint32_t*)dab = pack_bf16x2(da[0], da[1]);
+            *(uint32_t*)(dab + N) = pack_bf16x2(db[0], db[1]);
+          }
+        }
+      }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
 #pragma unroll

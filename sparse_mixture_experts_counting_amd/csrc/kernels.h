@@ -42,6 +42,8 @@ void launch_transpose(const void* src, int batch, int rows, int cols, int elem_b
                       hipStream_t s);
 void launch_transpose_ld(const void* src, int batch, int rows, int cols, int elem_bytes,
                          void* dst, int ldd, long long dst_bstride, hipStream_t s);
+void launch_transpose16(const void* src, int batch, int rows, int cols, void* dst, int ldd,
+                        long long dst_bstride, hipStream_t s);
 void launch_transpose_grouped(const void* src, int src_rows, const int32_t* gather,
                               int gather_div, const int32_t* offsets, int G, int rows_max,
                               int cols, void* dst, int ldd, hipStream_t s);

@@ -375,8 +375,9 @@ moe_status moe_expert_backward(const void* x, const int32_t* perm, const int32_t
   const int G = grouped ? E : 1;
   const int rows = grouped ? T * k : T;
   const int P = moe::kpad(rows, G);
+  // 32-bit element offsets inside one operand (the GEMMs offset each group's weights in 64 bits)
   if (!fits_i32((long long)rows * 2 * d_ff) || !fits_i32((long long)2 * d_ff * P) ||
-      !fits_i32((long long)d * P) || !fits_i32((long long)G * d * 2 * d_ff))
+      !fits_i32((long long)d * P) || !fits_i32((long long)d * 2 * d_ff))
     return MOE_ERR_UNSUPPORTED;
   const BwdLayout L = bwd_layout(rows, grouped, G, d, d_ff);
   if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
@@ -390,10 +391,10 @@ moe_status moe_expert_backward(const void* x, const int32_t* perm, const int32_t
 
   // Weights as the input-gradient products read them: w2T[e][n][i] = w2[e][i][n], and
   // w13T[e][i] = (w1[e][.][i], w3[e][.][i]) side by side (K = 2 d_ff).
-  moe::launch_transpose_ld(w2, G, d, d_ff, 2, w2t, d, (long long)d_ff * d, s);
-  moe::launch_transpose_ld(w1, G, d_ff, d, 2, w13t, 2 * d_ff, (long long)d * 2 * d_ff, s);
-  moe::launch_transpose_ld(w3, G, d_ff, d, 2, (uint16_t*)w13t + d_ff, 2 * d_ff,
-                           (long long)d * 2 * d_ff, s);
+  moe::launch_transpose16(w2, G, d, d_ff, w2t, d, (long long)d_ff * d, s);
+  moe::launch_transpose16(w1, G, d_ff, d, w13t, 2 * d_ff, (long long)d * 2 * d_ff, s);
+  moe::launch_transpose16(w3, G, d_ff, d, (uint16_t*)w13t + d_ff, 2 * d_ff,
+                          (long long)d * 2 * d_ff, s);
   hipError_t e;
   {   // dh = d_out w2 (rows of each expert)
     moe::GemmParams q{};
