@@ -1,4 +1,5 @@
-"""CPU oracle for the forward and backward passes of one top-k routed Mixture-of-Experts FFN layer.
+"""CPU oracle for the forward and backward passes of one top-k routed Mixture-of-Experts FFN layer,
+and for its Expert Choice routing variant.
 
 TEST INFRASTRUCTURE. Only the test suite, the smoke check and the CPU-baseline leg of the
 benchmark may import this module. The product path (the HIP library and its binding) never
@@ -16,7 +17,8 @@ Pages (cited by title and section; nothing here copies their code):
              step; 3.1 The auxiliary loss; 3.2 Why not just enforce balance?; 4 The
              parameter-count arithmetic; 8.2 DeepSeek-V2 -> V3 -> R1).
   [starphix] "Mixture of Experts (MoE)" -- learn.starphix.com ... ModelArchitectures/Mixture-of-Experts.md
-             (Key Equations; Top-k Gating; Expert Architectures: Shared + Specialized).
+             (Key Equations; Top-k Gating; Router Variants; Expert Architectures: Shared +
+             Specialized).
   [vanos]    "Mixture of Experts (MoE)" -- vanos001.github.io/placement_prep/llm/moe
              (Load Balancing Loss).
   [chipfoundry] "Mixture of Experts (MoE) architecture" glossary entry -- chipfoundryservices.com
@@ -458,6 +460,69 @@ def objective(x, w_r, w1, w3, w2, dy, k, mode, capacity=None, bias=None, shared=
     fw = forward(x, w_r, w1, w3, w2, k, mode, capacity=capacity, bias=bias, shared=shared,
                  alpha=alpha, beta=beta, select_bias=select_bias, exact_logits=True)
     return float(np.sum(_f64(dy) * fw["y"])) + fw["aux"] + fw["z"]
+
+
+# ------------------------------------------------------------------------------------------------
+# Expert Choice routing ([starphix] Router Variants: experts choose tokens, perfect load balance;
+# [chipfoundry] Routing Strategies and Variants: experts select their top tokens instead of tokens
+# selecting experts, which balances the load by construction and needs no balancing loss).
+# Readings: the score of (token t, expert e) is the router's softmax over experts p[t, e] (the router
+# is a linear layer followed by a softmax, [chipfoundry] MoE Architecture Components); expert e keeps
+# the C tokens with the largest p[:, e], equal scores to the lower token index; the pick's weight in
+# y is p[t, e] itself; a token no expert picks gets y = 0 (the residual is outside the layer); an
+# expert's rows are listed in increasing token order.
+# ------------------------------------------------------------------------------------------------
+
+
+def expert_choice(scores, C):
+    """Per expert, the C tokens with the largest score (ties to the lower token index), listed in
+    increasing token order.  scores [T, E] (any float type; compared as given).  Returns
+      offsets int32 [E+1] (e * min(C, T)), perm int32 [E * min(C, T)] token ids,
+      gate float64 [E * min(C, T)] = scores[perm[r], e], slot int32 [T, E] row of each pick or -1."""
+    S = np.asarray(scores)
+    T, E = S.shape
+    c = min(int(C), T)
+    perm = np.empty(E * c, dtype=np.int32)
+    gate = np.empty(E * c, dtype=np.float64)
+    slot = np.full((T, E), -1, dtype=np.int32)
+    for e in range(E):
+        col = S[:, e]
+        # rank: larger score first, then lower token index
+        order = sorted(range(T), key=lambda t: (-float(col[t]), t))
+        chosen = sorted(order[:c])
+        for i, t in enumerate(chosen):
+            perm[e * c + i] = t
+            gate[e * c + i] = float(col[t])
+            slot[t, e] = e * c + i
+    offsets = np.arange(E + 1, dtype=np.int32) * c
+    return offsets, perm, gate, slot
+
+
+def forward_expert_choice(x, w_r, w1, w3, w2, C, bias=None, shared=None, logits=None,
+                          scores=None):
+    """The layer under Expert Choice: router logits, p = softmax over experts, per-expert top-C
+    selection, each expert's SwiGLU FFN on its C tokens, y_t = sum over the experts that picked t of
+    p[t, e] * FFN_e(x_t) (+ the shared expert).  `scores` (float32 [T, E]) replaces p when given (the
+    selection is then taken on those values).  Returns a dict of the intermediates (float64)."""
+    x = np.asarray(x)
+    T = x.shape[0]
+    if logits is None:
+        logits = router_logits(x, w_r, bias)
+    p, lse = row_softmax_lse(logits)
+    S = p if scores is None else np.asarray(scores)
+    offsets, perm, gate, slot = expert_choice(S, C)
+    E = S.shape[1]
+    rows = expert_rows(x, perm, offsets, 1, w1, w3, w2)
+    y = np.zeros((T, x.shape[1]), dtype=np.float64)
+    for e in range(E):
+        for r in range(int(offsets[e]), int(offsets[e + 1])):
+            y[perm[r]] += gate[r] * rows[r]
+    shared_out = None
+    if shared is not None:
+        shared_out = swiglu_ffn(x, *shared)
+        y += shared_out
+    return dict(logits=logits, probs=p, scores=S, offsets=offsets, perm=perm, gate=gate,
+                slot=slot, expert_out=rows, shared_out=shared_out, y=y)
 
 
 def update_select_bias(select_bias, counts, T, E, k, rate):

@@ -426,3 +426,60 @@ def test_select_bias_updates_balance_a_skewed_router():
     assert counts0.max() > 2 * mean
     assert counts.max() < 1.25 * mean and counts.min() > 0.75 * mean
     assert b[0] < 0 < b[7]
+
+
+# ---------------------------------------------------------------- expert choice
+
+
+def _ec_bruteforce_selected(S, C):
+    """Token t is picked by expert e iff fewer than C tokens beat it (higher score, or equal score
+    and lower index): counting, no sort."""
+    T, E = S.shape
+    c = min(C, T)
+    sel = np.zeros((T, E), dtype=bool)
+    for e in range(E):
+        for t in range(T):
+            better = sum(1 for u in range(T) if S[u, e] > S[t, e] or (S[u, e] == S[t, e] and u < t))
+            sel[t, e] = better < c
+    return sel
+
+
+@pytest.mark.parametrize("T,E,C", [(9, 3, 4), (16, 5, 16), (7, 4, 20), (12, 2, 1)])
+def test_expert_choice_selection_bruteforce(T, E, C):
+    rng = np.random.default_rng(T * 31 + E)
+    S = rng.integers(0, 4, size=(T, E)).astype(np.float32) / 4    # many ties
+    offsets, perm, gate, slot = O.expert_choice(S, C)
+    sel = _ec_bruteforce_selected(S, C)
+    c = min(C, T)
+    assert offsets.tolist() == [e * c for e in range(E + 1)]
+    for e in range(E):
+        rows = perm[e * c:(e + 1) * c]
+        assert rows.tolist() == sorted(rows.tolist())                  # token order
+        assert set(rows.tolist()) == set(np.nonzero(sel[:, e])[0].tolist())
+        np.testing.assert_array_equal(gate[e * c:(e + 1) * c], S[rows, e])
+    for t in range(T):
+        for e in range(E):
+            assert (slot[t, e] >= 0) == sel[t, e]
+            if slot[t, e] >= 0:
+                assert perm[slot[t, e]] == t
+
+
+def test_expert_choice_perfect_balance_and_full_capacity_is_soft_moe():
+    # every expert gets exactly C rows; with C = T each token is picked by every expert, so y is
+    # the probability-weighted sum of every expert's output (evaluated densely here)
+    rng = np.random.default_rng(11)
+    T, d, E, f = 6, 5, 3, 7
+    x = rng.standard_normal((T, d))
+    w_r = rng.standard_normal((E, d))
+    w1, w3 = rng.standard_normal((E, f, d)), rng.standard_normal((E, f, d))
+    w2 = rng.standard_normal((E, d, f))
+    out = O.forward_expert_choice(x, w_r, w1, w3, w2, C=3)
+    assert np.all(np.diff(out["offsets"]) == 3)
+    full = O.forward_expert_choice(x, w_r, w1, w3, w2, C=T)
+    p = full["probs"]
+    want = sum(p[:, e, None] * np.array([bf.swiglu_loops(x[t], w1[e], w3[e], w2[e])
+                                         for t in range(T)]) for e in range(E))
+    np.testing.assert_allclose(full["y"], want, rtol=1e-10, atol=1e-10)
+    # a token nobody picks gets y = 0
+    unpicked = np.nonzero(np.all(out["slot"] < 0, axis=1))[0]
+    assert np.all(out["y"][unpicked] == 0)
