@@ -59,6 +59,9 @@ typedef enum {
 /* moe_route flag: skip the router product and read `logits` as an input. */
 #define MOE_ROUTE_LOGITS_IN 0x1u
 
+/* moe_expert_choice flag: `scores` is an input (the selection is taken on those values). */
+#define MOE_EC_SCORES_IN 0x1u
+
 /* Workspace bytes that cover every call below for this layer shape (max over the calls). */
 size_t moe_workspace_bytes(int T, int d, int d_ff, int E, int k, moe_dtype dt);
 
@@ -180,7 +183,8 @@ moe_status moe_expert_down(const void* h, const int32_t* offsets, int T, int d, 
  * all dropped gets y = 0, or its shared output).  Sums in fp32, rounds y once to dtype `dt`.
  * expert_out [T*k][d]; inv [T*k]; topk_gate [T,k] fp32, or NULL for weight 1 on every slot (the
  * backward pass adds each token's input-gradient rows this way); shared_out [T][d] or NULL;
- * y [T][d].
+ * y [T][d].  k may be up to 1024 here (the expert-choice layout passes k = E, inv = slot and
+ * topk_gate = scores; see moe_expert_choice).
  */
 moe_status moe_combine(const void* expert_out, const int32_t* inv, const float* topk_gate, int T,
                        int d, int k, moe_dtype dt, const void* shared_out, void* y, void* stream);
@@ -225,6 +229,43 @@ moe_status moe_update_select_bias(const int32_t* counts, int T, int E, int k, fl
  */
 moe_status moe_transpose(const void* src, int batch, int rows, int cols, moe_dtype dt, void* dst,
                          void* stream);
+
+/*
+ * moe_expert_choice -- Expert Choice routing (the starphix page, Router Variants: experts choose
+ * tokens, with perfect load balance; the chipfoundry glossary entry on MoE, Routing Strategies and
+ * Variants: experts select their top tokens instead of tokens selecting experts, no balancing
+ * loss needed).  With p the router's softmax over experts and c = min(C, T):
+ *
+ *   scores[t,e]   = p[t,e] = exp(L[t,e] - m_t) / sum_j exp(L[t,j] - m_t)   fp32 [T,E] (output, or
+ *                   input with MOE_EC_SCORES_IN, in which case logits may be NULL)
+ *   expert e keeps the c tokens with the largest scores[.,e]; equal scores go to the lower token
+ *   index (-0.0 equals +0.0); its rows are listed in increasing token order:
+ *   offsets[e]    = e*c                                   int32 [E+1]
+ *   perm[e*c + i] = the i-th kept token of expert e       int32 [E*c]
+ *   gate[e*c + i] = scores[perm[e*c+i], e]                fp32 [E*c]
+ *   slot[t*E + e] = the row of (t, e), or -1 when e did not keep t          int32 [T*E]
+ *
+ * logits [T,E] fp32 from moe_route (its top-k outputs are not used).  The layer then runs
+ *   moe_expert_ffn_gathered(x, perm, offsets, ..., rows_max = E*c, ...) -> out [E*c][d]
+ *   moe_combine(out, slot, scores, T, d, k = E, ...)   y[t] = sum over e keeping t of p[t,e] out[row]
+ * (E <= 1024).  A token that no expert keeps gets y = 0 (or its shared output).  No workspace.
+ * Deterministic: the selection is exact on the fp32 scores.
+ */
+moe_status moe_expert_choice(const float* logits, int T, int E, int C, unsigned flags,
+                             float* scores, int32_t* offsets, int32_t* perm, float* gate,
+                             int32_t* slot, void* stream);
+
+/*
+ * moe_expert_ffn_gathered -- moe_expert_ffn on explicit rows: row r of expert e
+ * (offsets[e] <= r < offsets[e+1], offsets[E] <= rows_max) reads x row rows[r] (a token index in
+ * [0, T)).  out [rows_max][d]; the workspace is moe_gathered_workspace_bytes(rows_max, ...).
+ * Otherwise as moe_expert_ffn (weights, dtype, split-K determinism, errors).
+ */
+size_t moe_gathered_workspace_bytes(int rows_max, int d, int d_ff, int E, moe_dtype dt);
+moe_status moe_expert_ffn_gathered(const void* x, const int32_t* rows, const int32_t* offsets,
+                                   int T, int d, int d_ff, int E, int rows_max, const void* w1,
+                                   const void* w3, const void* w2, moe_dtype dt, void* out,
+                                   void* workspace, size_t ws_bytes, void* stream);
 
 /*
  * Backward pass.  The objective is J = <dy, y> + aux + z: a task loss whose gradient with respect

@@ -8,7 +8,8 @@
 
 namespace moe {
 
-// One block per token row; each thread owns 16-byte column chunks.  Gathers the token's k expert
+// One block per token row; each thread owns 16-byte column chunks.  k is at most kCombineMaxK (the
+// expert-choice layout passes one slot per expert).  Gathers the token's k expert
 // rows through inv, sums in fp32 in slot order and writes y once.
 template <bool BF16>
 __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ expert_out,
@@ -16,12 +17,12 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ e
                                                       const float* __restrict__ gate, int T, int d,
                                                       int k, const void* __restrict__ shared_out,
                                                       void* __restrict__ y) {
-  __shared__ int32_t s_pos[32];
-  __shared__ float s_g[32];
+  __shared__ int32_t s_pos[kCombineMaxK];
+  __shared__ float s_g[kCombineMaxK];
   const int t = blockIdx.x;
-  if (threadIdx.x < k) {
-    s_pos[threadIdx.x] = inv[(size_t)t * k + threadIdx.x];
-    s_g[threadIdx.x] = gate ? gate[(size_t)t * k + threadIdx.x] : 1.0f;
+  for (int i = threadIdx.x; i < k; i += blockDim.x) {
+    s_pos[i] = inv[(size_t)t * k + i];
+    s_g[i] = gate ? gate[(size_t)t * k + i] : 1.0f;
   }
   __syncthreads();
   constexpr int VEC = BF16 ? 8 : 4;  // elements per 16-byte chunk

@@ -30,6 +30,7 @@ size_t gemm_bf16_partial_bytes(int rows_max, int G, bool grouped, int N, int K, 
 hipError_t launch_gemm_f32(const GemmParams& p, int rows_max, int epi, hipStream_t s);
 
 // combine.hip
+constexpr int kCombineMaxK = 1024;
 void launch_combine(const void* expert_out, const int32_t* inv, const float* gate, int T, int d,
                     int k, bool bf16, const void* shared_out, void* y, hipStream_t s);
 void launch_update_select_bias(const int32_t* counts, int T, int E, int k, float rate,
@@ -61,5 +62,10 @@ void launch_router_wgrad(const void* x, bool bf16, const float* dL, int T, int d
 void launch_router_xgrad(const float* dL, const void* w_r, bool bf16, int T, int d, int E,
                          const void* add, void* dx, hipStream_t s);
 void launch_dense_offsets(int32_t* o, int T, hipStream_t s);
+
+// expert_choice.hip
+void launch_expert_choice(const float* logits, int T, int E, int C, bool scores_in, float* scores,
+                          int32_t* offsets, int32_t* perm, float* gate, int32_t* slot,
+                          hipStream_t s);
 
 }  // namespace moe

@@ -198,14 +198,17 @@ static moe_status check_ffn_args(const void* x, const void* wa, const void* wb, 
   return MOE_OK;
 }
 
-static hipError_t run_up(const void* x, const int32_t* perm, const int32_t* offsets, int T, int d,
-                         int d_ff, int E, int k, const void* w1, const void* w3, bool bf16, void* h,
-                         void* part, hipStream_t s) {
+// Rows r of expert e are [offsets[e], offsets[e+1]); row r reads x row perm[r] / gather_div; at most
+// rows_max rows (perm == NULL: one dense group of T rows).
+static hipError_t run_up_rows(const void* x, const int32_t* perm, int gather_div,
+                              const int32_t* offsets, int T, int d, int d_ff, int E, int rows_max,
+                              const void* w1, const void* w3, bool bf16, void* h, void* part,
+                              hipStream_t s) {
   moe::GemmParams up{};
   up.A = x;
   up.a_rows = T;
   up.gather = perm;
-  up.gather_div = k;
+  up.gather_div = gather_div;
   up.offsets = perm ? offsets : nullptr;
   up.G = perm ? E : 1;
   up.M = T;
@@ -217,16 +220,23 @@ static hipError_t run_up(const void* x, const int32_t* perm, const int32_t* offs
   up.C = h;
   up.ldc = d_ff;
   up.part = (float*)part;
-  const int rows_max = perm ? T * k : T;
   return bf16 ? moe::launch_gemm_bf16(up, rows_max, moe::EPI_SWIGLU, s)
               : moe::launch_gemm_f32(up, rows_max, moe::EPI_SWIGLU, s);
 }
 
-static hipError_t run_down(const void* h, const int32_t* offsets, int T, int d, int d_ff, int E,
-                           int k, const void* w2, bool bf16, void* out, void* part, hipStream_t s) {
+static hipError_t run_up(const void* x, const int32_t* perm, const int32_t* offsets, int T, int d,
+                         int d_ff, int E, int k, const void* w1, const void* w3, bool bf16, void* h,
+                         void* part, hipStream_t s) {
+  return run_up_rows(x, perm, k, offsets, T, d, d_ff, E, perm ? T * k : T, w1, w3, bf16, h, part,
+                     s);
+}
+
+static hipError_t run_down_rows(const void* h, const int32_t* offsets, int T, int d, int d_ff,
+                                int E, int rows_max, const void* w2, bool bf16, void* out,
+                                void* part, hipStream_t s) {
   moe::GemmParams dn{};
   dn.A = h;
-  dn.a_rows = offsets ? T * k : T;
+  dn.a_rows = rows_max;
   dn.gather_div = 1;
   dn.offsets = offsets;
   dn.G = offsets ? E : 1;
@@ -238,9 +248,13 @@ static hipError_t run_down(const void* h, const int32_t* offsets, int T, int d, 
   dn.C = out;
   dn.ldc = d;
   dn.part = (float*)part;
-  const int rows_max = offsets ? T * k : T;
   return bf16 ? moe::launch_gemm_bf16(dn, rows_max, moe::EPI_STORE, s)
               : moe::launch_gemm_f32(dn, rows_max, moe::EPI_STORE, s);
+}
+
+static hipError_t run_down(const void* h, const int32_t* offsets, int T, int d, int d_ff, int E,
+                           int k, const void* w2, bool bf16, void* out, void* part, hipStream_t s) {
+  return run_down_rows(h, offsets, T, d, d_ff, E, offsets ? T * k : T, w2, bf16, out, part, s);
 }
 
 moe_status moe_expert_ffn(const void* x, const int32_t* perm, const int32_t* offsets, int T, int d,
@@ -297,7 +311,7 @@ moe_status moe_combine(const void* expert_out, const int32_t* inv, const float* 
   if (!expert_out || !inv || !y || !dtype_ok(dt)) return MOE_ERR_ARG;
   if (!aligned16(expert_out) || !aligned16(y) || (shared_out && !aligned16(shared_out)))
     return MOE_ERR_ARG;
-  if (k > kMaxK) return MOE_ERR_UNSUPPORTED;
+  if (k > moe::kCombineMaxK) return MOE_ERR_UNSUPPORTED;
   if ((d % 8) != 0) return MOE_ERR_UNSUPPORTED;
   if (!fits_i32((long long)T * k) || !fits_i32((long long)T * k * (long long)d))
     return MOE_ERR_UNSUPPORTED;
@@ -332,6 +346,53 @@ moe_status moe_transpose(const void* src, int batch, int rows, int cols, moe_dty
   const long long elems = (long long)batch * rows * cols;
   if (elems / batch / rows != cols) return MOE_ERR_UNSUPPORTED;
   moe::launch_transpose(src, batch, rows, cols, (int)elem_bytes(dt), dst, (hipStream_t)stream);
+  return launched();
+}
+
+size_t moe_gathered_workspace_bytes(int rows_max, int d, int d_ff, int E, moe_dtype dt) {
+  if (rows_max < 1 || d < 1 || d_ff < 1 || E < 1) return 0;
+  return ffn_workspace_bytes(rows_max, true, E, d, d_ff, dt);
+}
+
+moe_status moe_expert_ffn_gathered(const void* x, const int32_t* rows, const int32_t* offsets,
+                                   int T, int d, int d_ff, int E, int rows_max, const void* w1,
+                                   const void* w3, const void* w2, moe_dtype dt, void* out,
+                                   void* workspace, size_t ws_bytes, void* stream) {
+  if (T < 1 || d < 1 || d_ff < 1 || E < 1 || rows_max < 1) return MOE_ERR_ARG;
+  if (!x || !rows || !offsets || !w1 || !w3 || !w2 || !out || !workspace || !dtype_ok(dt))
+    return MOE_ERR_ARG;
+  if (!aligned16(x) || !aligned16(w1) || !aligned16(w3) || !aligned16(w2) || !aligned16(out) ||
+      !aligned16(workspace))
+    return MOE_ERR_ARG;
+  if (E > kMaxE) return MOE_ERR_UNSUPPORTED;
+  if ((d % 8) != 0 || (d_ff % 8) != 0) return MOE_ERR_UNSUPPORTED;
+  if (!fits_i32((long long)rows_max * d) || !fits_i32((long long)rows_max * d_ff) ||
+      !fits_i32((long long)T * d))
+    return MOE_ERR_UNSUPPORTED;
+  if (ws_bytes < ffn_workspace_bytes(rows_max, true, E, d, d_ff, dt)) return MOE_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  const bool bf16 = dt == MOE_BF16;
+  void* part = (char*)workspace + h_bytes(rows_max, d_ff, dt);
+  hipError_t e = run_up_rows(x, rows, 1, offsets, T, d, d_ff, E, rows_max, w1, w3, bf16,
+                             workspace, part, s);
+  if (e != hipSuccess) return MOE_ERR_DEVICE;
+  e = run_down_rows(workspace, offsets, T, d, d_ff, E, rows_max, w2, bf16, out, part, s);
+  if (e != hipSuccess) return MOE_ERR_DEVICE;
+  return launched();
+}
+
+moe_status moe_expert_choice(const float* logits, int T, int E, int C, unsigned flags,
+                             float* scores, int32_t* offsets, int32_t* perm, float* gate,
+                             int32_t* slot, void* stream) {
+  const bool scores_in = (flags & MOE_EC_SCORES_IN) != 0;
+  if (T < 1 || E < 1 || C < 1 || (flags & ~MOE_EC_SCORES_IN)) return MOE_ERR_ARG;
+  if (!scores || !offsets || !perm || !gate || !slot || (!scores_in && !logits))
+    return MOE_ERR_ARG;
+  if (E > kMaxE) return MOE_ERR_UNSUPPORTED;
+  const long long c = C < T ? C : T;
+  if (!fits_i32((long long)T * E) || !fits_i32(c * E)) return MOE_ERR_UNSUPPORTED;
+  moe::launch_expert_choice(logits, T, E, C, scores_in, scores, offsets, perm, gate, slot,
+                            (hipStream_t)stream);
   return launched();
 }
 

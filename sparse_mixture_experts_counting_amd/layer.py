@@ -158,3 +158,64 @@ def backward(cfg, inp, b, dy, g, stream=None):
                       g.d_logits, g.dw_r, g.dx_route, g.workspace, stream)
     lm.combine(g.dx_rows, b.inv, None, T, d, k, bf, g.dx_route, g.dx, stream)
     return g
+
+
+@dataclasses.dataclass
+class ECBuffers:
+    logits: torch.Tensor      # [T, E] fp32
+    topk_idx: torch.Tensor    # [T, 1] (moe_route output, unused by expert choice)
+    topk_gate: torch.Tensor
+    scores: torch.Tensor      # [T, E] fp32 router probabilities
+    offsets: torch.Tensor     # [E + 1]
+    perm: torch.Tensor        # [E * c] token of each expert row
+    gate: torch.Tensor        # [E * c] fp32
+    slot: torch.Tensor        # [T, E] row of each pick or -1
+    expert_out: torch.Tensor  # [E * c, d]
+    shared_out: torch.Tensor
+    y: torch.Tensor
+    workspace: torch.Tensor
+
+
+def ec_rows(cfg):
+    """Expert rows under Expert Choice: each expert keeps c = min(C, T) tokens."""
+    return cfg.E * min(cfg.capacity, cfg.T)
+
+
+def alloc_ec_buffers(cfg, device="cuda"):
+    dev = torch.device(device)
+    dt = torch.float32 if cfg.dtype == "fp32" else torch.bfloat16
+    code = lm.MOE_F32 if cfg.dtype == "fp32" else lm.MOE_BF16
+    T, d, E, f = cfg.T, cfg.d, cfg.E, cfg.d_ff
+    R = ec_rows(cfg)
+    i32 = dict(dtype=torch.int32, device=dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    ws = max(lm.gathered_workspace_bytes(R, d, f, E, code), lm.workspace_bytes(T, d, f, E, 1, code))
+    return ECBuffers(
+        logits=torch.empty((T, E), **f32), topk_idx=torch.empty((T, 1), **i32),
+        topk_gate=torch.empty((T, 1), **f32), scores=torch.empty((T, E), **f32),
+        offsets=torch.empty(E + 1, **i32), perm=torch.empty(R, **i32), gate=torch.empty(R, **f32),
+        slot=torch.empty((T, E), **i32), expert_out=torch.empty((R, d), dtype=dt, device=dev),
+        shared_out=torch.empty((T, d), dtype=dt, device=dev) if cfg.n_shared else None,
+        y=torch.empty((T, d), dtype=dt, device=dev),
+        workspace=torch.empty(ws, dtype=torch.uint8, device=dev))
+
+
+def forward_expert_choice(cfg, inp, b, stream=None):
+    """The layer under Expert Choice routing (cfg.capacity = tokens per expert): router logits
+    (moe_route, k = 1, its top-k unused), per-expert top-C selection (moe_expert_choice), the
+    experts on their rows (moe_expert_ffn_gathered, plus the shared expert), and the combine with
+    one slot per expert (moe_combine, k = E)."""
+    code = lm.MOE_F32 if cfg.dtype == "fp32" else lm.MOE_BF16
+    T, d, E, f = cfg.T, cfg.d, cfg.E, cfg.d_ff
+    lm.route(inp.x, inp.w_r, inp.bias, T, d, E, 1, code, 0, 0, b.logits, b.topk_idx, b.topk_gate,
+             None, None, None, stream)
+    lm.expert_choice(b.logits, T, E, cfg.capacity, 0, b.scores, b.offsets, b.perm, b.gate, b.slot,
+                     stream)
+    lm.expert_ffn_gathered(inp.x, b.perm, b.offsets, T, d, f, E, ec_rows(cfg), inp.w1, inp.w3,
+                           inp.w2, code, b.expert_out, b.workspace, stream)
+    if cfg.n_shared:
+        w1s, w3s, w2s = inp.shared
+        lm.expert_ffn(inp.x, None, None, T, d, f, 1, 1, w1s, w3s, w2s, code, b.shared_out,
+                      b.workspace, stream)
+    lm.combine(b.expert_out, b.slot, b.scores, T, d, E, code, b.shared_out, b.y, stream)
+    return b

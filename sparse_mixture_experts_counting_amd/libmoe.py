@@ -17,13 +17,15 @@ LIB_PATH = os.path.join(_PKG, "_lib", "libmoe.so")
 MOE_F32, MOE_BF16 = 0, 1
 GATE_SOFTMAX_TOPK, GATE_SOFTMAX_ALL, GATE_SIGMOID_TOPK = 0, 1, 2
 ROUTE_LOGITS_IN = 0x1
+EC_SCORES_IN = 0x1
 STATUS = {0: "MOE_OK", 1: "MOE_ERR_ARG", 2: "MOE_ERR_UNSUPPORTED", 3: "MOE_ERR_WORKSPACE",
           4: "MOE_ERR_DEVICE"}
 
 EXPORTS = ("moe_workspace_bytes", "moe_status_str", "moe_route", "moe_dispatch", "moe_expert_ffn",
            "moe_expert_up", "moe_expert_down", "moe_combine", "moe_aux_loss",
            "moe_update_select_bias", "moe_transpose", "moe_backward_workspace_bytes",
-           "moe_combine_backward", "moe_expert_backward", "moe_route_backward")
+           "moe_combine_backward", "moe_expert_backward", "moe_route_backward",
+           "moe_expert_choice", "moe_gathered_workspace_bytes", "moe_expert_ffn_gathered")
 
 
 class MoEError(RuntimeError):
@@ -59,10 +61,20 @@ _lib.moe_expert_backward.argtypes = [_p, _p, _p, _i, _i, _i, _i, _i, _p, _p, _p,
                                      _p, _p, _p, _sz, _p]
 _lib.moe_route_backward.argtypes = [_p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _f, _f,
                                     _p, _p, _p, _p, _p, _sz, _p]
+_lib.moe_expert_choice.argtypes = [_p, _i, _i, _i, _u, _p, _p, _p, _p, _p, _p]
+_lib.moe_gathered_workspace_bytes.argtypes = [_i, _i, _i, _i, _i]
+_lib.moe_gathered_workspace_bytes.restype = _sz
+_lib.moe_expert_ffn_gathered.argtypes = [_p, _p, _p, _i, _i, _i, _i, _i, _p, _p, _p, _i, _p, _p,
+                                         _sz, _p]
 for _n in ("moe_route", "moe_dispatch", "moe_expert_ffn", "moe_expert_up", "moe_expert_down",
            "moe_combine", "moe_aux_loss", "moe_transpose", "moe_update_select_bias",
-           "moe_combine_backward", "moe_expert_backward", "moe_route_backward"):
+           "moe_combine_backward", "moe_expert_backward", "moe_route_backward",
+           "moe_expert_choice", "moe_expert_ffn_gathered"):
     getattr(_lib, _n).restype = _i
+# Every exported entry point has its argument types declared (a missing declaration would pass
+# 64-bit pointers and sizes as C ints).
+for _n in EXPORTS:
+    assert getattr(_lib, _n).argtypes is not None, _n
 
 
 def lib():
@@ -189,3 +201,20 @@ def route_backward(x, w_r, logits, topk_idx, topk_gate, d_gate, counts, T, d, E,
         _ptr(counts), T, d, E, k, dt, gating, float(alpha), float(beta), _ptr(dx_add),
         _ptr(d_logits), _ptr(dw_r), _ptr(dx), _ptr(workspace), _nbytes(workspace),
         _stream(stream)))
+
+
+def expert_choice(logits, T, E, C, flags, scores, offsets, perm, gate, slot, stream=None):
+    _check("moe_expert_choice", _lib.moe_expert_choice(
+        _ptr(logits), T, E, C, flags, _ptr(scores), _ptr(offsets), _ptr(perm), _ptr(gate),
+        _ptr(slot), _stream(stream)))
+
+
+def gathered_workspace_bytes(rows_max, d, d_ff, E, dt):
+    return int(_lib.moe_gathered_workspace_bytes(rows_max, d, d_ff, E, dt))
+
+
+def expert_ffn_gathered(x, rows, offsets, T, d, d_ff, E, rows_max, w1, w3, w2, dt, out, workspace,
+                        stream=None):
+    _check("moe_expert_ffn_gathered", _lib.moe_expert_ffn_gathered(
+        _ptr(x), _ptr(rows), _ptr(offsets), T, d, d_ff, E, rows_max, _ptr(w1), _ptr(w3), _ptr(w2),
+        dt, _ptr(out), _ptr(workspace), _nbytes(workspace), _stream(stream)))

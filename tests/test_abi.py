@@ -31,7 +31,8 @@ def test_every_declared_symbol_is_exported(lm):
                           "moe_expert_ffn", "moe_expert_up", "moe_expert_down", "moe_combine",
                           "moe_aux_loss", "moe_update_select_bias", "moe_transpose",
                           "moe_backward_workspace_bytes", "moe_combine_backward",
-                          "moe_expert_backward", "moe_route_backward"}
+                          "moe_expert_backward", "moe_route_backward", "moe_expert_choice",
+                          "moe_gathered_workspace_bytes", "moe_expert_ffn_gathered"}
     lib = ctypes.CDLL(lm.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -113,7 +114,7 @@ def test_combine_and_loss_argument_errors(lm):
     L = lm.lib()
     assert L.moe_combine(FAKE, FAKE, FAKE, 0, 8, 2, 1, None, FAKE, None) == 1
     assert L.moe_combine(FAKE, FAKE, FAKE, 4, 12, 2, 1, None, FAKE, None) == 2
-    assert L.moe_combine(FAKE, FAKE, FAKE, 4, 8, 40, 1, None, FAKE, None) == 2
+    assert L.moe_combine(FAKE, FAKE, FAKE, 4, 8, 2000, 1, None, FAKE, None) == 2   # k > 1024
     assert L.moe_combine(None, FAKE, FAKE, 4, 8, 2, 1, None, FAKE, None) == 1
     f = ctypes.c_float
     assert L.moe_aux_loss(FAKE, FAKE, FAKE, 0, 4, 2, f(0.01), f(1e-3), FAKE, FAKE, None) == 1
@@ -193,3 +194,24 @@ def test_route_backward_argument_errors(lm):
     assert L.moe_route_backward(*args(E=2000, k=2)) == 2
     assert L.moe_route_backward(*args(d=12)) == 2
     assert L.moe_route_backward(*args(wsb=16)) == 3
+
+
+def test_expert_choice_argument_errors(lm):
+    L = lm.lib()
+    args = lambda **kw: [kw.get("logits", FAKE), kw.get("T", 8), kw.get("E", 4), kw.get("C", 2),
+                         kw.get("flags", 0), kw.get("scores", FAKE), FAKE, FAKE, FAKE,
+                         kw.get("slot", FAKE), None]
+    assert L.moe_expert_choice(*args(T=0)) == 1
+    assert L.moe_expert_choice(*args(C=0)) == 1
+    assert L.moe_expert_choice(*args(flags=2)) == 1
+    assert L.moe_expert_choice(*args(logits=None)) == 1            # scores are computed from it
+    assert L.moe_expert_choice(*args(scores=None)) == 1
+    assert L.moe_expert_choice(*args(slot=None)) == 1
+    assert L.moe_expert_choice(*args(E=2000)) == 2
+    g = lambda **kw: [FAKE, FAKE, FAKE, 8, kw.get("d", 16), 32, 4, kw.get("rows", 16), FAKE, FAKE,
+                      FAKE, 1, FAKE, kw.get("ws", FAKE), kw.get("wsb", 1 << 40), None]
+    assert L.moe_expert_ffn_gathered(*g(rows=0)) == 1
+    assert L.moe_expert_ffn_gathered(*g(ws=None)) == 1
+    assert L.moe_expert_ffn_gathered(*g(d=12)) == 2
+    assert L.moe_expert_ffn_gathered(*g(wsb=16)) == 3
+    assert lm.gathered_workspace_bytes(16, 16, 32, 4, lm.MOE_BF16) >= 16 * 32 * 2
