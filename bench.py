@@ -17,7 +17,8 @@ With --pass train a step is the forward followed by the backward pass of the lay
 <dy, y> + aux + z for x, the router and every expert weight: moe_combine_backward,
 moe_expert_backward for the routed and shared experts, moe_route_backward, and moe_combine adding
 each token's input-gradient rows); that line reports training-step tokens/s and the roofline of
-the expert backward.
+the expert backward.  With --routing expert_choice the forward runs under Expert Choice routing
+(moe_expert_choice, C = T*k/E tokens per expert) and reports its own line.
 """
 
 import argparse
@@ -108,6 +109,8 @@ def main():
     ap.add_argument("--cpu-repeats", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--pass", dest="mode", choices=("forward", "train"), default="forward")
+    ap.add_argument("--routing", choices=("topk", "expert_choice"), default="topk",
+                    help="expert_choice: each expert takes C = T*k/E tokens (same expert work)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -126,6 +129,8 @@ def main():
     torch.cuda.set_device(dev)
     if args.mode == "train":
         return train_bench(args, cfg, dev, torch, layer, lm, synth)
+    if args.routing == "expert_choice":
+        return expert_choice_bench(args, cfg, dev, torch, layer, lm, synth)
     log("bench: workload %s, generating inputs on the device" % cfg.name)
     inp = synth.make_inputs(cfg, seed=args.seed, device=dev)
     buf = layer.alloc_buffers(cfg, dev)
@@ -245,6 +250,104 @@ def main():
                                   "kind": "oracle", "sample": sample, "seconds": secs}
     else:
         result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+def expert_choice_bench(args, cfg, dev, torch, layer, lm, synth):
+    """The layer under Expert Choice routing with C = T*k/E tokens per expert (the same number of
+    expert rows as the top-k workload)."""
+    C = cfg.T * cfg.k // cfg.E
+    cfg = cfg.replace(capacity=C, name=cfg.name + "_expert_choice")
+    log("bench: workload %s (expert choice, C = %d), generating inputs on the device" % (cfg.name, C))
+    inp = synth.make_inputs(cfg, seed=args.seed, device=dev)
+    b = layer.alloc_ec_buffers(cfg, dev)
+    stream = torch.cuda.current_stream(dev)
+    T, d, E, f = cfg.T, cfg.d, cfg.E, cfg.d_ff
+    code = lm.MOE_F32 if cfg.dtype == "fp32" else lm.MOE_BF16
+    R = layer.ec_rows(cfg)
+    stages = ["route", "select", "experts", "shared", "combine"]
+    if not cfg.n_shared:
+        stages.remove("shared")
+
+    def step(ev=None):
+        def mark(i):
+            if ev is not None:
+                ev[i].record(stream)
+        mark(0)
+        lm.route(inp.x, inp.w_r, inp.bias, T, d, E, 1, code, 0, 0, b.logits, b.topk_idx,
+                 b.topk_gate, None, None, None)
+        mark(1)
+        lm.expert_choice(b.logits, T, E, C, 0, b.scores, b.offsets, b.perm, b.gate, b.slot)
+        mark(2)
+        lm.expert_ffn_gathered(inp.x, b.perm, b.offsets, T, d, f, E, R, inp.w1, inp.w3, inp.w2,
+                               code, b.expert_out, b.workspace)
+        mark(3)
+        i = 3
+        if cfg.n_shared:
+            w1s, w3s, w2s = inp.shared
+            lm.expert_ffn(inp.x, None, None, T, d, f, 1, 1, w1s, w3s, w2s, code, b.shared_out,
+                          b.workspace)
+            i += 1
+            mark(i)
+        lm.combine(b.expert_out, b.slot, b.scores, T, d, E, code, b.shared_out, b.y)
+        mark(i + 1)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize(dev)
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)]
+              for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for s_ in range(args.steps):
+        step(events[s_])
+    torch.cuda.synchronize(dev)
+    wall = time.perf_counter() - t0
+    stage_ms = {name: sum(events[s_][j].elapsed_time(events[s_][j + 1])
+                          for s_ in range(args.steps)) / args.steps
+                for j, name in enumerate(stages)}
+    ms_per_step = wall * 1e3 / args.steps
+    exp_flops = 6.0 * d * f * R
+    achieved = exp_flops / (stage_ms["experts"] * 1e-3) / 1e12
+    kept_by = torch.bincount(b.perm.long(), minlength=T)
+    result = {
+        "metric": "MoE layer tokens/s at 1 GPU, Expert Choice routing",
+        "value": T / (ms_per_step * 1e-3), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if cfg.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded randn inputs and random-init expert weights of the workload's "
+                "shapes, drawn on the device)",
+        "config": {"workload": cfg.name, "routing": "expert_choice", "T": T, "d": d, "E": E,
+                   "C": C, "d_ff": f, "shared_experts": cfg.n_shared,
+                   "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "mfma",
+                     "kernel": "moe_expert_ffn_gathered: up (SwiGLU) + down grouped GEMMs",
+                     "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None},
+        "routing": {"expert_rows": R, "tokens_kept_by_no_expert": int((kept_by == 0).sum()),
+                    "max_experts_per_token": int(kept_by.max())},
+        "stage_ms": stage_ms,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        from oracle import moe_oracle as O
+        from threadpoolctl import threadpool_info
+        n = args.cpu_sample_tokens if args.cpu_sample_tokens > 0 else 512
+        fl = lambda t: t.detach().float().cpu().numpy()
+        x, w_r = fl(inp.x[:n]), fl(inp.w_r)
+        w1, w3, w2 = fl(inp.w1), fl(inp.w3), fl(inp.w2)
+        c_s = max(1, n * cfg.k // E)
+        t1 = time.perf_counter()
+        for _ in range(args.cpu_repeats):
+            O.forward_expert_choice(x, w_r, w1, w3, w2, c_s)
+        secs = time.perf_counter() - t1
+        threads = max([q.get("num_threads", 1) for q in threadpool_info()
+                       if q.get("user_api") == "blas"] or [1])
+        result["cpu_baseline"] = {
+            "value": n * args.cpu_repeats / secs, "unit": "tokens/s", "cores": threads,
+            "kind": "oracle", "seconds": secs,
+            "sample": "first %d of %d tokens, expert choice with C = %d, float64 NumPy oracle, "
+                      "%d runs" % (n, T, c_s, args.cpu_repeats)}
     print(json.dumps(result), flush=True)
 
 

@@ -313,8 +313,8 @@ moe_status moe_combine(const void* expert_out, const int32_t* inv, const float* 
     return MOE_ERR_ARG;
   if (k > moe::kCombineMaxK) return MOE_ERR_UNSUPPORTED;
   if ((d % 8) != 0) return MOE_ERR_UNSUPPORTED;
-  if (!fits_i32((long long)T * k) || !fits_i32((long long)T * k * (long long)d))
-    return MOE_ERR_UNSUPPORTED;
+  // inv is indexed in 32 bits; row offsets into expert_out and y are 64-bit in the kernel
+  if (!fits_i32((long long)T * k) || !fits_i32((long long)T * d)) return MOE_ERR_UNSUPPORTED;
   moe::launch_combine(expert_out, inv, topk_gate, T, d, k, dt == MOE_BF16, shared_out, y,
                       (hipStream_t)stream);
   return launched();
