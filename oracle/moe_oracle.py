@@ -191,6 +191,54 @@ def dispatch(idx, E, capacity=None):
             n_dropped)
 
 
+def dispatch_reroute(logits, idx, E, capacity, select_bias=None):
+    """Overflow routed to the next-best expert instead of dropped ([chipfoundry] MoE Architecture
+    Components, Expert Capacity: tokens past capacity are dropped or sent to their next-best expert;
+    [dinesh] 3.2: or routed to their second choice).  Reading, in two rounds:
+      round 1: dispatch(idx, E, capacity): each expert keeps its first C assignments;
+      round 2: the j-th overflowed slot of token t (slots in order, j = 0, 1, ...) proposes the
+               token's expert of rank k + j in its full ranking (the order of select_topk over all
+               E, so never one of its top k); proposals take the room each expert has left after
+               round 1 (C - kept) in increasing assignment order; a proposal that finds no room, or
+               a slot with no rank k + j (k + j >= E), is dropped.
+    Returns (idx2, offsets, perm, inv, n_dropped): idx2 [T, k] is idx with each overflowed slot
+    replaced by its proposal (kept or not); within an expert the round-1 rows (increasing a) come
+    before the round-2 rows (increasing a)."""
+    idx = np.asarray(idx)
+    T, k = idx.shape
+    A = T * k
+    cap = A if (capacity is None or capacity <= 0) else int(capacity)
+    counts, off1, perm1, inv1, _ = dispatch(idx, E, capacity)
+    order = select_topk(logits, E, select_bias)
+    idx2 = idx.copy()
+    proposal = np.full(A, -1, dtype=np.int64)
+    for t in range(T):
+        j = 0
+        for s in range(k):
+            a = t * k + s
+            if inv1[a] < 0:
+                if k + j < E:
+                    proposal[a] = int(order[t, k + j])
+                    idx2[t, s] = proposal[a]
+                j += 1
+    lists = [list(perm1[off1[e]:off1[e + 1]]) for e in range(E)]
+    room = [cap - len(lists[e]) for e in range(E)]
+    extra = [[] for _ in range(E)]
+    for a in range(A):
+        e = int(proposal[a])
+        if e >= 0 and room[e] > 0:
+            extra[e].append(a)
+            room[e] -= 1
+    offsets = [0]
+    for e in range(E):
+        offsets.append(offsets[-1] + len(lists[e]) + len(extra[e]))
+    perm = np.array([a for e in range(E) for a in lists[e] + extra[e]], dtype=np.int32)
+    inv = np.full(A, -1, dtype=np.int32)
+    inv[perm] = np.arange(perm.size, dtype=np.int32)
+    return (idx2.astype(np.int32), np.array(offsets, dtype=np.int32), perm, inv,
+            int(A - offsets[-1]))
+
+
 def silu(z):
     """silu(z) = z * sigmoid(z) = z / (1 + exp(-z))."""
     with np.errstate(over="ignore"):
@@ -260,7 +308,8 @@ def z_loss(lse_sq_sum, T, beta):
 
 
 def forward(x, w_r, w1, w3, w2, k, mode, capacity=None, bias=None, shared=None,
-            alpha=0.01, beta=1e-3, logits=None, select_bias=None, exact_logits=False):
+            alpha=0.01, beta=1e-3, logits=None, select_bias=None, exact_logits=False,
+            reroute=False):
     """The whole layer, steps in the order of [tirogla] How it works (Score, Select, Dispatch,
     Compute, Combine, Balance).
 
@@ -268,6 +317,9 @@ def forward(x, w_r, w1, w3, w2, k, mode, capacity=None, bias=None, shared=None,
     `logits` (float32 [T, E]) replaces the router product when given; `select_bias` (float32 [E])
     biases the ranking only (aux-loss-free balancing).  exact_logits keeps the router product in
     float64 instead of rounding it to float32 (for finite-difference checks of the gradients).
+    reroute sends overflowed assignments to their next-best expert (dispatch_reroute) instead of
+    dropping them; the gates are then those of the final selection and f still counts the router's
+    first choices before capacity.
     Returns a dict of every intermediate (float64 except the integer dispatch outputs).
     """
     x = np.asarray(x)
@@ -277,9 +329,13 @@ def forward(x, w_r, w1, w3, w2, k, mode, capacity=None, bias=None, shared=None,
     logits = np.asarray(logits, dtype=np.float64 if exact_logits else np.float32)
     E = logits.shape[1]
     idx = select_topk(logits, k, select_bias)
-    gate = gate_weights(logits, idx, mode)
     p, lse = row_softmax_lse(logits)
     counts, offsets, perm, inv, n_dropped = dispatch(idx, E, capacity)
+    first_choice = idx
+    if reroute:
+        idx, offsets, perm, inv, n_dropped = dispatch_reroute(logits, first_choice, E, capacity,
+                                                              select_bias)
+    gate = gate_weights(logits, idx, mode)
     rows = expert_rows(x, perm, offsets, k, w1, w3, w2)
     shared_out = None
     if shared is not None:
@@ -287,7 +343,8 @@ def forward(x, w_r, w1, w3, w2, k, mode, capacity=None, bias=None, shared=None,
     y = combine(rows, inv, gate, T, k, shared_out)
     prob_sum = p.sum(axis=0)
     lse_sq_sum = float(np.sum(lse * lse))
-    return dict(logits=logits, topk_idx=idx, topk_gate=gate, probs=p, lse=lse,
+    return dict(logits=logits, topk_idx=idx, first_choice=first_choice, topk_gate=gate, probs=p,
+                lse=lse,
                 prob_sum=prob_sum, lse_sq_sum=lse_sq_sum, counts=counts, offsets=offsets,
                 perm=perm, inv=inv, n_dropped=n_dropped, expert_out=rows, shared_out=shared_out,
                 y=y, aux=aux_loss(counts, prob_sum, T, E, k, alpha),

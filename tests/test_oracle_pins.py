@@ -483,3 +483,60 @@ def test_expert_choice_perfect_balance_and_full_capacity_is_soft_moe():
     # a token nobody picks gets y = 0
     unpicked = np.nonzero(np.all(out["slot"] < 0, axis=1))[0]
     assert np.all(out["y"][unpicked] == 0)
+
+
+# ---------------------------------------------------------------- overflow rerouting
+
+
+def test_reroute_hand_example():
+    # 4 tokens, 3 experts, k = 1, C = 1; every token ranks expert 0 first.  Expert 0 keeps token
+    # 0; tokens 1-3 overflow and propose their second choice: 1 -> e1, 2 -> e2, 3 -> e1 (e1 is full
+    # by then, so token 3 is dropped).
+    L = np.array([[3, 2, 1], [3, 2, 1], [3, 1, 2], [3, 2, 1]], dtype=np.float32)
+    idx = O.select_topk(L, 1)
+    idx2, offsets, perm, inv, nd = O.dispatch_reroute(L, idx, 3, 1)
+    assert idx2[:, 0].tolist() == [0, 1, 2, 1]
+    assert offsets.tolist() == [0, 1, 2, 3]
+    assert perm.tolist() == [0, 1, 2]
+    assert inv.tolist() == [0, 1, 2, -1]
+    assert nd == 1
+
+
+def test_reroute_top2_uses_ranks_past_k():
+    # k = 2, C = 1, E = 4: token 1 loses both experts and proposes ranks 2 and 3
+    L = np.array([[4, 3, 2, 1], [4, 3, 2, 1]], dtype=np.float32)
+    idx = O.select_topk(L, 2)
+    idx2, offsets, perm, inv, nd = O.dispatch_reroute(L, idx, 4, 1)
+    assert idx2.tolist() == [[0, 1], [2, 3]]
+    assert nd == 0 and offsets.tolist() == [0, 1, 2, 3, 4]
+
+
+@settings(max_examples=60, deadline=None)
+@given(st.integers(1, 12), st.integers(1, 6), st.integers(1, 3), st.integers(1, 5),
+       st.integers(0, 10 ** 6))
+def test_reroute_invariants(T, E, k, C, seed):
+    k = min(k, E)
+    rng = np.random.default_rng(seed)
+    L = rng.integers(-2, 3, size=(T, E)).astype(np.float32)
+    idx = O.select_topk(L, k)
+    _, _, _, inv1, nd1 = O.dispatch(idx, E, C)
+    idx2, offsets, perm, inv, nd = O.dispatch_reroute(L, idx, E, C)
+    kept = np.diff(offsets)
+    assert np.all(kept <= C)                                   # capacity still holds
+    assert nd <= nd1 and nd == T * k - offsets[-1]             # rerouting only recovers
+    order = O.select_topk(L, E)
+    for t in range(T):
+        assert len(set(idx2[t].tolist())) == k                 # distinct experts per token
+        for s in range(k):
+            a = t * k + s
+            if inv1[a] >= 0:                                   # round-1 keeps stay put
+                assert idx2[t, s] == idx[t, s] and inv[a] >= 0
+            else:                                              # proposals come from ranks >= k
+                assert idx2[t, s] == idx[t, s] or idx2[t, s] in order[t, k:].tolist()
+            if inv[a] >= 0:
+                e = idx2[t, s]
+                assert offsets[e] <= inv[a] < offsets[e + 1] and perm[inv[a]] == a
+    # unlimited capacity: nothing overflows, identical to plain dispatch
+    i3, o3, p3, v3, n3 = O.dispatch_reroute(L, idx, E, None)
+    c0, o0, p0, v0, n0 = O.dispatch(idx, E, None)
+    assert np.array_equal(i3, idx) and np.array_equal(o3, o0) and np.array_equal(p3, p0)
