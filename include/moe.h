@@ -231,6 +231,33 @@ moe_status moe_transpose(const void* src, int batch, int rows, int cols, moe_dty
                          void* stream);
 
 /*
+ * moe_reroute -- overflow routed to the next-best expert instead of dropped (the chipfoundry
+ * glossary entry on MoE, Architecture Components, Expert Capacity; the dineshblog page, section
+ * 3.2: or routed to their second choice).  Runs after moe_route and moe_dispatch with capacity C
+ * (its offsets and inv are round 1) and adds round 2: the j-th overflowed slot (slot order) of
+ * token t proposes the token's expert of rank k + j in the ranking of moe_route (same scores,
+ * select_bias included, same tie order); proposals take the room each expert has left after
+ * round 1, in increasing assignment order; a proposal with no room, or a slot with no rank k + j
+ * (k + j >= E), is dropped.
+ *
+ *   topk_idx2 [T,k]   topk_idx with each overflowed slot replaced by its proposal (kept or not)
+ *   topk_gate2 [T,k]  the gating function over topk_idx2 (tokens with no overflow keep topk_gate)
+ *   offsets2 [E+1], perm2 [T*k], inv2 [T*k], n_dropped2 [1]: the dispatch layout of the final
+ *                     assignment, each expert's round-1 rows first, then its round-2 rows, each in
+ *                     increasing assignment order (same conventions as moe_dispatch)
+ *
+ * logits [T,E] fp32 and select_bias [E] (or NULL) as given to moe_route; topk_idx, topk_gate from
+ * moe_route; offsets, inv from moe_dispatch (capacity <= 0: nothing overflows and the outputs repeat
+ * the inputs).  counts from moe_dispatch still feed moe_aux_loss (f counts the router's choices).
+ * Workspace: (2 T k + E) int32 (covered by moe_workspace_bytes).  Deterministic.
+ */
+moe_status moe_reroute(const float* logits, const float* select_bias, const int32_t* topk_idx,
+                       const float* topk_gate, const int32_t* offsets, const int32_t* inv, int T,
+                       int E, int k, int capacity, moe_gating gating, int32_t* topk_idx2,
+                       float* topk_gate2, int32_t* offsets2, int32_t* perm2, int32_t* inv2,
+                       int32_t* n_dropped2, void* workspace, size_t ws_bytes, void* stream);
+
+/*
  * moe_expert_choice -- Expert Choice routing (the starphix page, Router Variants: experts choose
  * tokens, with perfect load balance; the chipfoundry glossary entry on MoE, Routing Strategies and
  * Variants: experts select their top tokens instead of tokens selecting experts, no balancing

@@ -63,6 +63,14 @@ void launch_router_xgrad(const float* dL, const void* w_r, bool bf16, int T, int
                          const void* add, void* dx, hipStream_t s);
 void launch_dense_offsets(int32_t* o, int T, hipStream_t s);
 
+// reroute.hip
+size_t reroute_workspace_bytes(int A, int E);
+void launch_reroute(const float* logits, const float* select_bias, const int32_t* topk_idx,
+                    const float* topk_gate, const int32_t* offsets1, const int32_t* inv1, int T,
+                    int E, int k, int capacity, int mode, int32_t* idx2, float* gate2,
+                    int32_t* offsets2, int32_t* perm2, int32_t* inv2, int32_t* n_dropped,
+                    int32_t* ws, hipStream_t s);
+
 // expert_choice.hip
 void launch_expert_choice(const float* logits, int T, int E, int C, bool scores_in, float* scores,
                           int32_t* offsets, int32_t* perm, float* gate, int32_t* slot,

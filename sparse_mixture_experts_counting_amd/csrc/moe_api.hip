@@ -97,6 +97,8 @@ size_t moe_workspace_bytes(int T, int d, int d_ff, int E, int k, moe_dtype dt) {
   if (T < 1 || E < 1 || k < 1 || d_ff < 1 || d < 1) return 0;
   size_t r = align_up(moe::route_workspace_bytes(T, E));
   size_t q = align_up(moe::dispatch_workspace_bytes(T * k, E));
+  const size_t rr = align_up(moe::reroute_workspace_bytes(T * k, E));
+  q = q > rr ? q : rr;
   size_t f = ffn_workspace_bytes(T * k, true, E, d, d_ff, dt);
   const size_t fs = ffn_workspace_bytes(T, false, 1, d, d_ff, dt);   // shared / dense expert
   f = f > fs ? f : fs;
@@ -378,6 +380,26 @@ moe_status moe_expert_ffn_gathered(const void* x, const int32_t* rows, const int
   if (e != hipSuccess) return MOE_ERR_DEVICE;
   e = run_down_rows(workspace, offsets, T, d, d_ff, E, rows_max, w2, bf16, out, part, s);
   if (e != hipSuccess) return MOE_ERR_DEVICE;
+  return launched();
+}
+
+moe_status moe_reroute(const float* logits, const float* select_bias, const int32_t* topk_idx,
+                       const float* topk_gate, const int32_t* offsets, const int32_t* inv, int T,
+                       int E, int k, int capacity, moe_gating gating, int32_t* topk_idx2,
+                       float* topk_gate2, int32_t* offsets2, int32_t* perm2, int32_t* inv2,
+                       int32_t* n_dropped2, void* workspace, size_t ws_bytes, void* stream) {
+  if (T < 1 || E < 1 || k < 1 || k > E) return MOE_ERR_ARG;
+  if (!logits || !topk_idx || !topk_gate || !offsets || !inv || !topk_idx2 || !topk_gate2 ||
+      !offsets2 || !perm2 || !inv2 || !n_dropped2 || !workspace)
+    return MOE_ERR_ARG;
+  if (gating < MOE_GATE_SOFTMAX_TOPK || gating > MOE_GATE_SIGMOID_TOPK) return MOE_ERR_ARG;
+  if (E > kMaxE || k > kMaxK) return MOE_ERR_UNSUPPORTED;
+  if (!fits_i32((long long)T * E) || !fits_i32((long long)2 * T * k + E))
+    return MOE_ERR_UNSUPPORTED;
+  if (ws_bytes < moe::reroute_workspace_bytes(T * k, E)) return MOE_ERR_WORKSPACE;
+  moe::launch_reroute(logits, select_bias, topk_idx, topk_gate, offsets, inv, T, E, k, capacity,
+                      (int)gating, topk_idx2, topk_gate2, offsets2, perm2, inv2, n_dropped2,
+                      (int32_t*)workspace, (hipStream_t)stream);
   return launched();
 }
 

@@ -219,3 +219,46 @@ def forward_expert_choice(cfg, inp, b, stream=None):
                       b.workspace, stream)
     lm.combine(b.expert_out, b.slot, b.scores, T, d, E, code, b.shared_out, b.y, stream)
     return b
+
+
+@dataclasses.dataclass
+class RerouteBuffers:
+    topk_idx: torch.Tensor    # [T, k] final selection
+    topk_gate: torch.Tensor   # [T, k] gates over it
+    offsets: torch.Tensor
+    perm: torch.Tensor
+    inv: torch.Tensor
+    n_dropped: torch.Tensor
+
+
+def alloc_reroute_buffers(cfg, device="cuda"):
+    dev = torch.device(device)
+    T, E, k = cfg.T, cfg.E, cfg.k
+    i32 = dict(dtype=torch.int32, device=dev)
+    return RerouteBuffers(
+        topk_idx=torch.empty((T, k), **i32),
+        topk_gate=torch.empty((T, k), dtype=torch.float32, device=dev),
+        offsets=torch.empty(E + 1, **i32), perm=torch.empty(T * k, **i32),
+        inv=torch.empty(T * k, **i32), n_dropped=torch.empty(1, **i32))
+
+
+def forward_reroute(cfg, inp, b, r, stream=None):
+    """The layer with overflow sent to the next-best expert: route, capacity dispatch (round 1),
+    moe_reroute (round 2), then the experts, the combine over the final layout and the losses (f
+    from the round-1 counts)."""
+    code = lm.MOE_F32 if cfg.dtype == "fp32" else lm.MOE_BF16
+    route(cfg, inp, b, stream=stream)
+    dispatch(cfg, b, stream)
+    lm.reroute(b.logits, getattr(inp, "select_bias", None), b.topk_idx, b.topk_gate, b.offsets,
+               b.inv, cfg.T, cfg.E, cfg.k, cfg.capacity, GATING_CODE[cfg.gating], r.topk_idx,
+               r.topk_gate, r.offsets, r.perm, r.inv, r.n_dropped, b.workspace, stream)
+    lm.expert_ffn(inp.x, r.perm, r.offsets, cfg.T, cfg.d, cfg.d_ff, cfg.E, cfg.k, inp.w1, inp.w3,
+                  inp.w2, code, b.expert_out, b.workspace, stream)
+    if cfg.n_shared:
+        w1s, w3s, w2s = inp.shared
+        lm.expert_ffn(inp.x, None, None, cfg.T, cfg.d, cfg.d_ff, 1, 1, w1s, w3s, w2s, code,
+                      b.shared_out, b.workspace, stream)
+    lm.combine(b.expert_out, r.inv, r.topk_gate, cfg.T, cfg.d, cfg.k, code, b.shared_out, b.y,
+               stream)
+    losses(cfg, b, stream)
+    return b

@@ -25,7 +25,8 @@ EXPORTS = ("moe_workspace_bytes", "moe_status_str", "moe_route", "moe_dispatch",
            "moe_expert_up", "moe_expert_down", "moe_combine", "moe_aux_loss",
            "moe_update_select_bias", "moe_transpose", "moe_backward_workspace_bytes",
            "moe_combine_backward", "moe_expert_backward", "moe_route_backward",
-           "moe_expert_choice", "moe_gathered_workspace_bytes", "moe_expert_ffn_gathered")
+           "moe_expert_choice", "moe_gathered_workspace_bytes", "moe_expert_ffn_gathered",
+           "moe_reroute")
 
 
 class MoEError(RuntimeError):
@@ -62,6 +63,8 @@ _lib.moe_expert_backward.argtypes = [_p, _p, _p, _i, _i, _i, _i, _i, _p, _p, _p,
 _lib.moe_route_backward.argtypes = [_p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _f, _f,
                                     _p, _p, _p, _p, _p, _sz, _p]
 _lib.moe_expert_choice.argtypes = [_p, _i, _i, _i, _u, _p, _p, _p, _p, _p, _p]
+_lib.moe_reroute.argtypes = [_p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p,
+                             _p, _sz, _p]
 _lib.moe_gathered_workspace_bytes.argtypes = [_i, _i, _i, _i, _i]
 _lib.moe_gathered_workspace_bytes.restype = _sz
 _lib.moe_expert_ffn_gathered.argtypes = [_p, _p, _p, _i, _i, _i, _i, _i, _p, _p, _p, _i, _p, _p,
@@ -69,7 +72,7 @@ _lib.moe_expert_ffn_gathered.argtypes = [_p, _p, _p, _i, _i, _i, _i, _i, _p, _p,
 for _n in ("moe_route", "moe_dispatch", "moe_expert_ffn", "moe_expert_up", "moe_expert_down",
            "moe_combine", "moe_aux_loss", "moe_transpose", "moe_update_select_bias",
            "moe_combine_backward", "moe_expert_backward", "moe_route_backward",
-           "moe_expert_choice", "moe_expert_ffn_gathered"):
+           "moe_expert_choice", "moe_expert_ffn_gathered", "moe_reroute"):
     getattr(_lib, _n).restype = _i
 # Every exported entry point has its argument types declared (a missing declaration would pass
 # 64-bit pointers and sizes as C ints).
@@ -218,3 +221,11 @@ def expert_ffn_gathered(x, rows, offsets, T, d, d_ff, E, rows_max, w1, w3, w2, d
     _check("moe_expert_ffn_gathered", _lib.moe_expert_ffn_gathered(
         _ptr(x), _ptr(rows), _ptr(offsets), T, d, d_ff, E, rows_max, _ptr(w1), _ptr(w3), _ptr(w2),
         dt, _ptr(out), _ptr(workspace), _nbytes(workspace), _stream(stream)))
+
+
+def reroute(logits, select_bias, topk_idx, topk_gate, offsets, inv, T, E, k, capacity, gating,
+            topk_idx2, topk_gate2, offsets2, perm2, inv2, n_dropped2, workspace, stream=None):
+    _check("moe_reroute", _lib.moe_reroute(
+        _ptr(logits), _ptr(select_bias), _ptr(topk_idx), _ptr(topk_gate), _ptr(offsets), _ptr(inv),
+        T, E, k, capacity, gating, _ptr(topk_idx2), _ptr(topk_gate2), _ptr(offsets2), _ptr(perm2),
+        _ptr(inv2), _ptr(n_dropped2), _ptr(workspace), _nbytes(workspace), _stream(stream)))

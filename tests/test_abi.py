@@ -32,7 +32,8 @@ def test_every_declared_symbol_is_exported(lm):
                           "moe_aux_loss", "moe_update_select_bias", "moe_transpose",
                           "moe_backward_workspace_bytes", "moe_combine_backward",
                           "moe_expert_backward", "moe_route_backward", "moe_expert_choice",
-                          "moe_gathered_workspace_bytes", "moe_expert_ffn_gathered"}
+                          "moe_gathered_workspace_bytes", "moe_expert_ffn_gathered",
+                          "moe_reroute"}
     lib = ctypes.CDLL(lm.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -215,3 +216,18 @@ def test_expert_choice_argument_errors(lm):
     assert L.moe_expert_ffn_gathered(*g(d=12)) == 2
     assert L.moe_expert_ffn_gathered(*g(wsb=16)) == 3
     assert lm.gathered_workspace_bytes(16, 16, 32, 4, lm.MOE_BF16) >= 16 * 32 * 2
+
+
+def test_reroute_argument_errors(lm):
+    L = lm.lib()
+    args = lambda **kw: [kw.get("logits", FAKE), None, FAKE, FAKE, FAKE, FAKE, kw.get("T", 8),
+                         kw.get("E", 4), kw.get("k", 2), 3, kw.get("g", 0), FAKE, FAKE, FAKE, FAKE,
+                         FAKE, FAKE, kw.get("ws", FAKE), kw.get("wsb", 1 << 40), None]
+    assert L.moe_reroute(*args(T=0)) == 1
+    assert L.moe_reroute(*args(k=5)) == 1
+    assert L.moe_reroute(*args(g=3)) == 1
+    assert L.moe_reroute(*args(logits=None)) == 1
+    assert L.moe_reroute(*args(ws=None)) == 1
+    assert L.moe_reroute(*args(E=2000)) == 2
+    assert L.moe_reroute(*args(wsb=8)) == 3
+    assert lm.workspace_bytes(8, 16, 16, 4, 2, lm.MOE_BF16) >= (2 * 8 * 2 + 4) * 4
