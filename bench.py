@@ -18,7 +18,8 @@ With --pass train a step is the forward followed by the backward pass of the lay
 moe_expert_backward for the routed and shared experts, moe_route_backward, and moe_combine adding
 each token's input-gradient rows); that line reports training-step tokens/s and the roofline of
 the expert backward.  With --routing expert_choice the forward runs under Expert Choice routing
-(moe_expert_choice, C = T*k/E tokens per expert) and reports its own line.
+(moe_expert_choice, C = T*k/E tokens per expert) and reports its own line; with --routing reroute
+the capacity is C = T*k/E and overflowed assignments go to their next-best expert (moe_reroute).
 """
 
 import argparse
@@ -109,8 +110,9 @@ def main():
     ap.add_argument("--cpu-repeats", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--pass", dest="mode", choices=("forward", "train"), default="forward")
-    ap.add_argument("--routing", choices=("topk", "expert_choice"), default="topk",
-                    help="expert_choice: each expert takes C = T*k/E tokens (same expert work)")
+    ap.add_argument("--routing", choices=("topk", "expert_choice", "reroute"), default="topk",
+                    help="expert_choice: each expert takes C = T*k/E tokens (same expert work); "
+                         "reroute: capacity C = T*k/E with overflow sent to the next-best expert")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -131,6 +133,8 @@ def main():
         return train_bench(args, cfg, dev, torch, layer, lm, synth)
     if args.routing == "expert_choice":
         return expert_choice_bench(args, cfg, dev, torch, layer, lm, synth)
+    if args.routing == "reroute":
+        return reroute_bench(args, cfg, dev, torch, layer, lm, synth)
     log("bench: workload %s, generating inputs on the device" % cfg.name)
     inp = synth.make_inputs(cfg, seed=args.seed, device=dev)
     buf = layer.alloc_buffers(cfg, dev)
@@ -348,6 +352,90 @@ def expert_choice_bench(args, cfg, dev, torch, layer, lm, synth):
             "kind": "oracle", "seconds": secs,
             "sample": "first %d of %d tokens, expert choice with C = %d, float64 NumPy oracle, "
                       "%d runs" % (n, T, c_s, args.cpu_repeats)}
+    print(json.dumps(result), flush=True)
+
+
+def reroute_bench(args, cfg, dev, torch, layer, lm, synth):
+    """Top-k routing with capacity C = T*k/E (capacity factor 1) and overflow sent to the
+    next-best expert (moe_reroute after moe_dispatch)."""
+    C = cfg.T * cfg.k // cfg.E
+    cfg = cfg.replace(capacity=C, name=cfg.name + "_reroute")
+    log("bench: workload %s (capacity %d, overflow rerouted)" % (cfg.name, C))
+    inp = synth.make_inputs(cfg, seed=args.seed, device=dev)
+    b = layer.alloc_buffers(cfg, dev)
+    r = layer.alloc_reroute_buffers(cfg, dev)
+    stream = torch.cuda.current_stream(dev)
+    code = lm.MOE_F32 if cfg.dtype == "fp32" else lm.MOE_BF16
+    from sparse_mixture_experts_counting_amd.synth import GATING_CODE
+    T, d, E, k, f = cfg.T, cfg.d, cfg.E, cfg.k, cfg.d_ff
+    stages = ["route", "dispatch", "reroute", "experts", "shared", "combine", "aux_loss"]
+    if not cfg.n_shared:
+        stages.remove("shared")
+
+    def step(ev=None):
+        def mark(i):
+            if ev is not None:
+                ev[i].record(stream)
+        mark(0)
+        layer.route(cfg, inp, b)
+        mark(1)
+        layer.dispatch(cfg, b)
+        mark(2)
+        lm.reroute(b.logits, None, b.topk_idx, b.topk_gate, b.offsets, b.inv, T, E, k, C,
+                   GATING_CODE[cfg.gating], r.topk_idx, r.topk_gate, r.offsets, r.perm, r.inv,
+                   r.n_dropped, b.workspace)
+        mark(3)
+        lm.expert_ffn(inp.x, r.perm, r.offsets, T, d, f, E, k, inp.w1, inp.w3, inp.w2, code,
+                      b.expert_out, b.workspace)
+        mark(4)
+        i = 4
+        if cfg.n_shared:
+            w1s, w3s, w2s = inp.shared
+            lm.expert_ffn(inp.x, None, None, T, d, f, 1, 1, w1s, w3s, w2s, code, b.shared_out,
+                          b.workspace)
+            i += 1
+            mark(i)
+        lm.combine(b.expert_out, r.inv, r.topk_gate, T, d, k, code, b.shared_out, b.y)
+        mark(i + 1)
+        layer.losses(cfg, b)
+        mark(i + 2)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize(dev)
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)]
+              for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for s_ in range(args.steps):
+        step(events[s_])
+    torch.cuda.synchronize(dev)
+    wall = time.perf_counter() - t0
+    stage_ms = {name: sum(events[s_][j].elapsed_time(events[s_][j + 1])
+                          for s_ in range(args.steps)) / args.steps
+                for j, name in enumerate(stages)}
+    ms_per_step = wall * 1e3 / args.steps
+    kept = int(r.offsets[-1].item())
+    exp_flops = 6.0 * d * f * kept
+    achieved = exp_flops / (stage_ms["experts"] * 1e-3) / 1e12
+    result = {
+        "metric": "MoE layer tokens/s at 1 GPU, capacity factor 1 with overflow rerouted",
+        "value": T / (ms_per_step * 1e-3), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if cfg.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded randn inputs and random-init expert weights of the workload's "
+                "shapes, drawn on the device)",
+        "config": {"workload": cfg.name, "routing": "topk+reroute", "T": T, "d": d, "E": E,
+                   "k": k, "capacity": C, "d_ff": f, "gating": cfg.gating,
+                   "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "mfma", "kernel": "moe_expert_ffn: up (SwiGLU) + down grouped GEMMs",
+                     "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None},
+        "routing": {"dropped_without_reroute": int(b.n_dropped.item()),
+                    "dropped_with_reroute": int(r.n_dropped.item()), "kept": kept},
+        "stage_ms": stage_ms,
+        "cpu_baseline": None,
+    }
     print(json.dumps(result), flush=True)
 
 
