@@ -1,5 +1,5 @@
 """CPU oracle for the forward and backward passes of one top-k routed Mixture-of-Experts FFN layer,
-and for its Expert Choice routing variant.
+its Expert Choice and overflow-rerouting variants, and weight-only quantized experts.
 
 TEST INFRASTRUCTURE. Only the test suite, the smoke check and the CPU-baseline leg of the
 benchmark may import this module. The product path (the HIP library and its binding) never
@@ -18,9 +18,9 @@ Pages (cited by title and section; nothing here copies their code):
              parameter-count arithmetic; 8.2 DeepSeek-V2 -> V3 -> R1).
   [starphix] "Mixture of Experts (MoE)" -- learn.starphix.com ... ModelArchitectures/Mixture-of-Experts.md
              (Key Equations; Top-k Gating; Router Variants; Expert Architectures: Shared +
-             Specialized).
+             Specialized; Inference Optimization: Quantization).
   [vanos]    "Mixture of Experts (MoE)" -- vanos001.github.io/placement_prep/llm/moe
-             (Load Balancing Loss).
+             (Load Balancing Loss; Quantized Experts).
   [chipfoundry] "Mixture of Experts (MoE) architecture" glossary entry -- chipfoundryservices.com
              (MoE Architecture Components: the router is trained end to end by gradient descent).
 
@@ -580,6 +580,53 @@ def forward_expert_choice(x, w_r, w1, w3, w2, C, bias=None, shared=None, logits=
         y += shared_out
     return dict(logits=logits, probs=p, scores=S, offsets=offsets, perm=perm, gate=gate,
                 slot=slot, expert_out=rows, shared_out=shared_out, y=y)
+
+
+# ------------------------------------------------------------------------------------------------
+# Weight-only quantized experts ([starphix] Inference Optimization, Quantization: experts stored
+# in INT8 or INT4 while the router stays 16-bit; [vanos] Quantized Experts: INT4 for a 4x memory
+# cut).  Reading: symmetric quantization with one fp32 scale per output channel (per row of a
+# [out][in] weight): s = max|w_row| / Q with Q = 127 (INT8) or 7 (INT4), q = round-half-even(w / s)
+# in float32 arithmetic, clamped to [-Q, Q]; a zero row has s = 0 and q = 0.  The layer then
+# computes with the dequantized weights s * q (activations and accumulation as in the bf16 layer).
+# ------------------------------------------------------------------------------------------------
+
+
+def quantize_rows(w, bits):
+    """Per-row symmetric quantization of w [..., rows, cols] (float32 values).  Returns
+    (q int8 [..., rows, cols], scale float32 [..., rows])."""
+    Q = {8: 127, 4: 7}[bits]
+    w = np.asarray(w, dtype=np.float32)
+    amax = np.max(np.abs(w), axis=-1)
+    scale = (amax / np.float32(Q)).astype(np.float32)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        r = np.where(scale[..., None] > 0, w / scale[..., None], np.float32(0))
+    q = np.clip(np.rint(r.astype(np.float32)), -Q, Q).astype(np.int8)
+    return q, scale
+
+
+def pack_int4(q):
+    """Two 4-bit two's-complement values per byte along the last axis: column 2j in the low nibble,
+    2j + 1 in the high nibble.  q int8 [..., cols] with cols even -> uint8 [..., cols / 2]."""
+    q = np.asarray(q, dtype=np.int8).astype(np.int16) & 15
+    return (q[..., 0::2] | (q[..., 1::2] << 4)).astype(np.uint8)
+
+
+def unpack_int4(b):
+    """Inverse of pack_int4 (sign-extends each nibble)."""
+    b = np.asarray(b, dtype=np.uint8).astype(np.int16)
+    lo, hi = b & 15, (b >> 4) & 15
+    lo = np.where(lo >= 8, lo - 16, lo)
+    hi = np.where(hi >= 8, hi - 16, hi)
+    out = np.empty(b.shape[:-1] + (2 * b.shape[-1],), dtype=np.int8)
+    out[..., 0::2] = lo
+    out[..., 1::2] = hi
+    return out
+
+
+def dequantize_rows(q, scale):
+    """s * q in float64 (the weights the quantized layer computes with)."""
+    return np.asarray(q, dtype=np.float64) * np.asarray(scale, dtype=np.float64)[..., None]
 
 
 def update_select_bias(select_bias, counts, T, E, k, rate):

@@ -540,3 +540,44 @@ def test_reroute_invariants(T, E, k, C, seed):
     i3, o3, p3, v3, n3 = O.dispatch_reroute(L, idx, E, None)
     c0, o0, p0, v0, n0 = O.dispatch(idx, E, None)
     assert np.array_equal(i3, idx) and np.array_equal(o3, o0) and np.array_equal(p3, p0)
+
+
+# ---------------------------------------------------------------- weight-only quantization
+
+
+@pytest.mark.parametrize("bits,Q", [(8, 127), (4, 7)])
+def test_quantize_rows_bound_and_range(bits, Q):
+    rng = np.random.default_rng(bits)
+    w = (rng.standard_normal((3, 5, 64)) * rng.uniform(0.01, 10, size=(3, 5, 1))).astype(np.float32)
+    w[1, 2] = 0.0                                         # a zero row
+    q, s = O.quantize_rows(w, bits)
+    assert q.dtype == np.int8 and np.all(np.abs(q) <= Q)
+    assert s[1, 2] == 0 and np.all(q[1, 2] == 0)
+    # the largest magnitude of each nonzero row maps to +-Q exactly; every error is at most s/2
+    nz = s > 0
+    assert np.all(np.max(np.abs(q), axis=-1)[nz] == Q)
+    err = np.abs(w.astype(np.float64) - O.dequantize_rows(q, s))
+    assert np.all(err <= s[..., None].astype(np.float64) * (0.5 + 1e-6))
+
+
+def test_quantize_exact_grid_round_trips():
+    # values already on the grid s * q (s a power of two) come back exactly
+    q0 = np.arange(-127, 128, dtype=np.int8)[None, :]
+    w = q0.astype(np.float32) * np.float32(0.125)
+    q, s = O.quantize_rows(w, 8)
+    assert s[0] == np.float32(127 * 0.125 / 127) and np.array_equal(q, q0)
+
+
+def test_quantize_half_way_rounds_to_even():
+    # row max 127 -> s = 1; 2.5 and -0.5 are ties: round half to even
+    w = np.array([[127.0, 2.5, -0.5, 3.5, 1.49]], dtype=np.float32)
+    q, s = O.quantize_rows(w, 8)
+    assert s[0] == 1.0 and q[0].tolist() == [127, 2, 0, 4, 1]
+
+
+def test_int4_pack_round_trip():
+    rng = np.random.default_rng(3)
+    q = rng.integers(-8, 8, size=(4, 6, 32)).astype(np.int8)
+    b = O.pack_int4(q)
+    assert b.shape == (4, 6, 16) and np.array_equal(O.unpack_int4(b), q)
+    assert O.pack_int4(np.array([[-1, 7]], dtype=np.int8)).tolist() == [[0x7F]]
