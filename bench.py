@@ -19,7 +19,8 @@ moe_expert_backward for the routed and shared experts, moe_route_backward, and m
 each token's input-gradient rows); that line reports training-step tokens/s and the roofline of
 the expert backward.  With --routing expert_choice the forward runs under Expert Choice routing
 (moe_expert_choice, C = T*k/E tokens per expert) and reports its own line; with --routing reroute
-the capacity is C = T*k/E and overflowed assignments go to their next-best expert (moe_reroute).
+the capacity is C = T*k/E and overflowed assignments go to their next-best expert (moe_reroute);
+with --weights int8 / int4 the routed experts are weight-only quantized (moe_expert_ffn_q).
 """
 
 import argparse
@@ -110,6 +111,8 @@ def main():
     ap.add_argument("--cpu-repeats", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--pass", dest="mode", choices=("forward", "train"), default="forward")
+    ap.add_argument("--weights", choices=("bf16", "int8", "int4"), default="bf16",
+                    help="int8 / int4: weight-only quantized routed experts (moe_expert_ffn_q)")
     ap.add_argument("--routing", choices=("topk", "expert_choice", "reroute"), default="topk",
                     help="expert_choice: each expert takes C = T*k/E tokens (same expert work); "
                          "reroute: capacity C = T*k/E with overflow sent to the next-best expert")
@@ -131,6 +134,8 @@ def main():
     torch.cuda.set_device(dev)
     if args.mode == "train":
         return train_bench(args, cfg, dev, torch, layer, lm, synth)
+    if args.weights != "bf16":
+        return quant_bench(args, cfg, dev, torch, layer, lm, synth)
     if args.routing == "expert_choice":
         return expert_choice_bench(args, cfg, dev, torch, layer, lm, synth)
     if args.routing == "reroute":
@@ -352,6 +357,81 @@ def expert_choice_bench(args, cfg, dev, torch, layer, lm, synth):
             "kind": "oracle", "seconds": secs,
             "sample": "first %d of %d tokens, expert choice with C = %d, float64 NumPy oracle, "
                       "%d runs" % (n, T, c_s, args.cpu_repeats)}
+    print(json.dumps(result), flush=True)
+
+
+def quant_bench(args, cfg, dev, torch, layer, lm, synth):
+    """The layer with weight-only INT8 / INT4 routed experts (quantized once, untimed)."""
+    bits = 8 if args.weights == "int8" else 4
+    log("bench: workload %s with %s experts" % (cfg.name, args.weights))
+    inp = synth.make_inputs(cfg, seed=args.seed, device=dev)
+    qw = layer.quantize_experts(cfg, inp, bits, dev)
+    b = layer.alloc_buffers(cfg, dev)
+    stream = torch.cuda.current_stream(dev)
+    T, d, E, k, f = cfg.T, cfg.d, cfg.E, cfg.k, cfg.d_ff
+    stages = ["route", "dispatch", "experts", "shared", "combine", "aux_loss"]
+    if not cfg.n_shared:
+        stages.remove("shared")
+
+    def step(ev=None):
+        def mark(i):
+            if ev is not None:
+                ev[i].record(stream)
+        mark(0)
+        layer.route(cfg, inp, b)
+        mark(1)
+        layer.dispatch(cfg, b)
+        mark(2)
+        lm.expert_ffn_q(inp.x, b.perm, b.offsets, T, d, f, E, k, bits, qw.q1, qw.s1, qw.q3, qw.s3,
+                        qw.q2, qw.s2, lm.MOE_BF16, b.expert_out, qw.workspace)
+        mark(3)
+        i = 3
+        if cfg.n_shared:
+            w1s, w3s, w2s = inp.shared
+            lm.expert_ffn(inp.x, None, None, T, d, f, 1, 1, w1s, w3s, w2s, lm.MOE_BF16,
+                          b.shared_out, b.workspace)
+            i += 1
+            mark(i)
+        layer.combine(cfg, b)
+        mark(i + 1)
+        layer.losses(cfg, b)
+        mark(i + 2)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize(dev)
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)]
+              for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for s_ in range(args.steps):
+        step(events[s_])
+    torch.cuda.synchronize(dev)
+    wall = time.perf_counter() - t0
+    stage_ms = {name: sum(events[s_][j].elapsed_time(events[s_][j + 1])
+                          for s_ in range(args.steps)) / args.steps
+                for j, name in enumerate(stages)}
+    ms_per_step = wall * 1e3 / args.steps
+    touched = int((b.counts > 0).sum().item())
+    # Algorithmic bytes of the quantized expert GEMMs: the touched experts' three weight matrices
+    # (bits / 8 bytes per weight) and their fp32 scales.
+    wbytes = touched * (3.0 * d * f * bits / 8 + 4.0 * (2 * f + d))
+    achieved = wbytes / (stage_ms["experts"] * 1e-3) / 1e9
+    result = {
+        "metric": "MoE layer tokens/s at 1 GPU with %s weight-only experts" % args.weights.upper(),
+        "value": T / (ms_per_step * 1e-3), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16 activations, %s weights" % args.weights,
+        "data": "synthetic (seeded randn inputs and random-init expert weights of the workload's "
+                "shapes, drawn on the device, quantized per output channel)",
+        "config": {"workload": cfg.name, "weights": args.weights, "T": T, "d": d, "E": E, "k": k,
+                   "d_ff": f, "gating": cfg.gating, "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "hbm", "kernel": "moe_expert_ffn_q: up (SwiGLU) + down GEMMs",
+                     "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBS, "traffic": None},
+        "stage_ms": stage_ms,
+        "cpu_baseline": None,
+    }
     print(json.dumps(result), flush=True)
 
 

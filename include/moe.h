@@ -295,6 +295,35 @@ moe_status moe_expert_ffn_gathered(const void* x, const int32_t* rows, const int
                                    void* workspace, size_t ws_bytes, void* stream);
 
 /*
+ * Weight-only quantized experts (the starphix page, Inference Optimization, Quantization: experts
+ * in INT8 or INT4 while the router stays 16-bit; the vanos001 page, Quantized Experts).  One fp32
+ * scale per output channel (per row of a stored [out][in] weight matrix):
+ *
+ *   s[row] = max_c |w[row][c]| / Q,  Q = 127 (bits 8) or 7 (bits 4)        (fp32 division)
+ *   q[row][c] = rint(w[row][c] / s[row]) clamped to [-Q, Q]; a zero row has s = 0, q = 0
+ *
+ * moe_quantize_weights converts bf16 weights [batch][rows][cols] (the storage moe_expert_ffn takes:
+ * w1, w3 [E][d_ff][d], w2 [E][d][d_ff]) into q: int8 [batch][rows][cols] (bits 8) or bytes
+ * [batch][rows][cols/2] holding columns 2j (low nibble) and 2j+1 (high nibble) as 4-bit two's
+ * complement (bits 4; cols even), and scale fp32 [batch][rows].  Load time, not per call.
+ *
+ * moe_expert_ffn_q is moe_expert_ffn with the dequantized weights s * q: activations bf16, products
+ * formed exactly from the integer weights, fp32 accumulation, the scale applied to each output;
+ * h rounded to bf16 between the two GEMMs.  q1, q3 with s1, s3 [E][d_ff]; q2 with s2 [E][d].
+ * bf16 layers only; d and d_ff must be multiples of 128.  Its kernels are made for decode-sized
+ * groups (the weight stream bounds them; INT8 halves and INT4 quarters the streamed bytes).
+ * Workspace: moe_q_workspace_bytes.  Deterministic (fixed-order split-K sums).
+ */
+size_t moe_q_workspace_bytes(int T, int d, int d_ff, int E, int k, int bits);
+moe_status moe_quantize_weights(const void* w, int batch, int rows, int cols, moe_dtype dt,
+                                int bits, void* q, float* scale, void* stream);
+moe_status moe_expert_ffn_q(const void* x, const int32_t* perm, const int32_t* offsets, int T,
+                            int d, int d_ff, int E, int k, int bits, const void* q1,
+                            const float* s1, const void* q3, const float* s3, const void* q2,
+                            const float* s2, moe_dtype dt, void* out, void* workspace,
+                            size_t ws_bytes, void* stream);
+
+/*
  * Backward pass.  The objective is J = <dy, y> + aux + z: a task loss whose gradient with respect
  * to y is dy [T][d], plus the two router losses of moe_aux_loss (the tirogla page, How it works
  * step 6: f_e is a count and carries no gradient, P_e and the logsumexp do; the vanos001 page,

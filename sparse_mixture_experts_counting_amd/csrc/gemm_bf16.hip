@@ -758,6 +758,10 @@ static void launch_splitk_finish(const GemmParams& p, int rows_max, int epi, hip
     hipLaunchKernelGGL((splitk_finish_kernel<1, EPI_STORE>), dim3(fgrid), dim3(256), 0, s, p);
 }
 
+void launch_splitk_finish_bf16(const GemmParams& p, int rows_max, int epi, hipStream_t s) {
+  launch_splitk_finish(p, rows_max, epi, s);
+}
+
 // 256-row tiles (8 waves, one block per CU) when the groups are large enough to fill them: they
 // load a third fewer operand bytes per flop than 128-row tiles.  Smaller groups (fine-grained
 // experts, decode) keep 128-row tiles so that ragged group ends waste less.

@@ -28,6 +28,15 @@ void launch_dispatch(const int32_t* topk_idx, int A, int E, int capacity, int32_
 hipError_t launch_gemm_bf16(const GemmParams& p, int rows_max, int epi, hipStream_t s);
 size_t gemm_bf16_partial_bytes(int rows_max, int G, bool grouped, int N, int K, int epi);
 hipError_t launch_gemm_f32(const GemmParams& p, int rows_max, int epi, hipStream_t s);
+void launch_splitk_finish_bf16(const GemmParams& p, int rows_max, int epi, hipStream_t s);
+
+// gemm_q.hip (weight-only INT8 / INT4 experts)
+int gemm_q_split(int rows_max, int G, bool grouped, int N, int K, int bits);
+size_t gemm_q_partial_bytes(int rows_max, int G, bool grouped, int N, int K, int bits, int nmat);
+hipError_t launch_gemm_q(const GemmParams& p, int rows_max, int epi, int bits, const float* s0,
+                         const float* s1, hipStream_t s);
+void launch_quantize_rows(const void* w, long long rows, int cols, int bits, void* q, float* scale,
+                          hipStream_t s);
 
 // combine.hip
 constexpr int kCombineMaxK = 1024;

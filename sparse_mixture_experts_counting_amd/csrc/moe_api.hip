@@ -383,6 +383,68 @@ moe_status moe_expert_ffn_gathered(const void* x, const int32_t* rows, const int
   return launched();
 }
 
+size_t q_workspace_bytes(int rows, bool grouped, int G, int d, int d_ff, int bits) {
+  const size_t up = moe::gemm_q_partial_bytes(rows, G, grouped, d_ff, d, bits, 2);
+  const size_t dn = moe::gemm_q_partial_bytes(rows, G, grouped, d, d_ff, bits, 1);
+  return align_up((size_t)rows * d_ff * 2) + align_up(up > dn ? up : dn);
+}
+
+size_t moe_q_workspace_bytes(int T, int d, int d_ff, int E, int k, int bits) {
+  if (T < 1 || d < 1 || d_ff < 1 || E < 1 || k < 1 || (bits != 8 && bits != 4)) return 0;
+  const size_t a = q_workspace_bytes(T * k, true, E, d, d_ff, bits);
+  const size_t b = q_workspace_bytes(T, false, 1, d, d_ff, bits);
+  return a > b ? a : b;
+}
+
+moe_status moe_quantize_weights(const void* w, int batch, int rows, int cols, moe_dtype dt,
+                                int bits, void* q, float* scale, void* stream) {
+  if (!w || !q || !scale || batch < 1 || rows < 1 || cols < 1) return MOE_ERR_ARG;
+  if (bits != 8 && bits != 4) return MOE_ERR_ARG;
+  if (dt != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (bits == 4 && cols % 2 != 0) return MOE_ERR_UNSUPPORTED;
+  const long long nrows = (long long)batch * rows;
+  if (nrows > 0x7fffffffLL || nrows * cols / rows / batch != cols) return MOE_ERR_UNSUPPORTED;
+  moe::launch_quantize_rows(w, nrows, cols, bits, q, scale, (hipStream_t)stream);
+  return launched();
+}
+
+moe_status moe_expert_ffn_q(const void* x, const int32_t* perm, const int32_t* offsets, int T,
+                            int d, int d_ff, int E, int k, int bits, const void* q1,
+                            const float* s1, const void* q3, const float* s3, const void* q2,
+                            const float* s2, moe_dtype dt, void* out, void* workspace,
+                            size_t ws_bytes, void* stream) {
+  const bool grouped = perm != nullptr;
+  moe_status st = check_ffn_args(x, q1, q3, out, grouped, offsets, T, d, d_ff, E, k, dt);
+  if (st != MOE_OK) return st;
+  if (!q2 || !s1 || !s3 || !s2 || !workspace || !aligned16(q2) || !aligned16(workspace))
+    return MOE_ERR_ARG;
+  if (bits != 8 && bits != 4) return MOE_ERR_ARG;
+  if (dt != MOE_BF16 || d % 128 != 0 || d_ff % 128 != 0) return MOE_ERR_UNSUPPORTED;
+  const int G = grouped ? E : 1;
+  const int rows = grouped ? T * k : T;
+  if (ws_bytes < q_workspace_bytes(rows, grouped, G, d, d_ff, bits)) return MOE_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  void* h = workspace;
+  float* part = (float*)((char*)workspace + align_up((size_t)rows * d_ff * 2));
+  moe::GemmParams up{};
+  up.A = x; up.a_rows = T; up.gather = perm; up.gather_div = k;
+  up.offsets = grouped ? offsets : nullptr; up.G = G; up.M = T;
+  up.N = d_ff; up.K = d; up.B0 = q1; up.B1 = q3;
+  up.b_gstride = (long long)d_ff * d * bits / 8;
+  up.C = h; up.ldc = d_ff; up.part = part;
+  if (moe::launch_gemm_q(up, rows, moe::EPI_SWIGLU, bits, s1, s3, s) != hipSuccess)
+    return MOE_ERR_DEVICE;
+  moe::GemmParams dn{};
+  dn.A = h; dn.a_rows = rows; dn.gather_div = 1;
+  dn.offsets = grouped ? offsets : nullptr; dn.G = G; dn.M = T;
+  dn.N = d; dn.K = d_ff; dn.B0 = q2;
+  dn.b_gstride = (long long)d * d_ff * bits / 8;
+  dn.C = out; dn.ldc = d; dn.part = part;
+  if (moe::launch_gemm_q(dn, rows, moe::EPI_STORE, bits, s2, nullptr, s) != hipSuccess)
+    return MOE_ERR_DEVICE;
+  return launched();
+}
+
 moe_status moe_reroute(const float* logits, const float* select_bias, const int32_t* topk_idx,
                        const float* topk_gate, const int32_t* offsets, const int32_t* inv, int T,
                        int E, int k, int capacity, moe_gating gating, int32_t* topk_idx2,

@@ -262,3 +262,48 @@ def forward_reroute(cfg, inp, b, r, stream=None):
                stream)
     losses(cfg, b, stream)
     return b
+
+
+@dataclasses.dataclass
+class QuantWeights:
+    bits: int
+    q1: torch.Tensor          # int8 [E, d_ff, d] or uint8 [E, d_ff, d / 2]
+    s1: torch.Tensor          # fp32 [E, d_ff]
+    q3: torch.Tensor
+    s3: torch.Tensor
+    q2: torch.Tensor          # [E, d, d_ff] or [E, d, d_ff / 2]
+    s2: torch.Tensor          # fp32 [E, d]
+    workspace: torch.Tensor
+
+
+def quantize_experts(cfg, inp, bits, device="cuda"):
+    """Weight-only INT8 / INT4 copies of the routed experts (moe_quantize_weights), load time."""
+    dev = torch.device(device)
+    E, d, f = cfg.E, cfg.d, cfg.d_ff
+    div = 8 // bits
+    mk = lambda rows, cols: (torch.empty((E, rows, cols // div), dtype=torch.uint8, device=dev),
+                             torch.empty((E, rows), dtype=torch.float32, device=dev))
+    (q1, s1), (q3, s3), (q2, s2) = mk(f, d), mk(f, d), mk(d, f)
+    lm.quantize_weights(inp.w1, E, f, d, lm.MOE_BF16, bits, q1, s1)
+    lm.quantize_weights(inp.w3, E, f, d, lm.MOE_BF16, bits, q3, s3)
+    lm.quantize_weights(inp.w2, E, d, f, lm.MOE_BF16, bits, q2, s2)
+    ws = lm.q_workspace_bytes(cfg.T, d, f, E, cfg.k, bits)
+    return QuantWeights(bits, q1, s1, q3, s3, q2, s2,
+                        torch.empty(ws, dtype=torch.uint8, device=dev))
+
+
+def forward_quantized(cfg, inp, b, qw, stream=None):
+    """The layer with weight-only quantized routed experts (moe_expert_ffn_q); routing, dispatch,
+    the shared expert, combine and losses as in forward()."""
+    route(cfg, inp, b, stream=stream)
+    dispatch(cfg, b, stream)
+    lm.expert_ffn_q(inp.x, b.perm, b.offsets, cfg.T, cfg.d, cfg.d_ff, cfg.E, cfg.k, qw.bits,
+                    qw.q1, qw.s1, qw.q3, qw.s3, qw.q2, qw.s2, lm.MOE_BF16, b.expert_out,
+                    qw.workspace, stream)
+    if cfg.n_shared:
+        w1s, w3s, w2s = inp.shared
+        lm.expert_ffn(inp.x, None, None, cfg.T, cfg.d, cfg.d_ff, 1, 1, w1s, w3s, w2s, lm.MOE_BF16,
+                      b.shared_out, b.workspace, stream)
+    combine(cfg, b, stream)
+    losses(cfg, b, stream)
+    return b

@@ -26,7 +26,7 @@ EXPORTS = ("moe_workspace_bytes", "moe_status_str", "moe_route", "moe_dispatch",
            "moe_update_select_bias", "moe_transpose", "moe_backward_workspace_bytes",
            "moe_combine_backward", "moe_expert_backward", "moe_route_backward",
            "moe_expert_choice", "moe_gathered_workspace_bytes", "moe_expert_ffn_gathered",
-           "moe_reroute")
+           "moe_reroute", "moe_q_workspace_bytes", "moe_quantize_weights", "moe_expert_ffn_q")
 
 
 class MoEError(RuntimeError):
@@ -63,6 +63,11 @@ _lib.moe_expert_backward.argtypes = [_p, _p, _p, _i, _i, _i, _i, _i, _p, _p, _p,
 _lib.moe_route_backward.argtypes = [_p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _f, _f,
                                     _p, _p, _p, _p, _p, _sz, _p]
 _lib.moe_expert_choice.argtypes = [_p, _i, _i, _i, _u, _p, _p, _p, _p, _p, _p]
+_lib.moe_q_workspace_bytes.argtypes = [_i, _i, _i, _i, _i, _i]
+_lib.moe_q_workspace_bytes.restype = _sz
+_lib.moe_quantize_weights.argtypes = [_p, _i, _i, _i, _i, _i, _p, _p, _p]
+_lib.moe_expert_ffn_q.argtypes = [_p, _p, _p, _i, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _i,
+                                  _p, _p, _sz, _p]
 _lib.moe_reroute.argtypes = [_p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p,
                              _p, _sz, _p]
 _lib.moe_gathered_workspace_bytes.argtypes = [_i, _i, _i, _i, _i]
@@ -72,7 +77,8 @@ _lib.moe_expert_ffn_gathered.argtypes = [_p, _p, _p, _i, _i, _i, _i, _i, _p, _p,
 for _n in ("moe_route", "moe_dispatch", "moe_expert_ffn", "moe_expert_up", "moe_expert_down",
            "moe_combine", "moe_aux_loss", "moe_transpose", "moe_update_select_bias",
            "moe_combine_backward", "moe_expert_backward", "moe_route_backward",
-           "moe_expert_choice", "moe_expert_ffn_gathered", "moe_reroute"):
+           "moe_expert_choice", "moe_expert_ffn_gathered", "moe_reroute",
+           "moe_quantize_weights", "moe_expert_ffn_q"):
     getattr(_lib, _n).restype = _i
 # Every exported entry point has its argument types declared (a missing declaration would pass
 # 64-bit pointers and sizes as C ints).
@@ -229,3 +235,21 @@ def reroute(logits, select_bias, topk_idx, topk_gate, offsets, inv, T, E, k, cap
         _ptr(logits), _ptr(select_bias), _ptr(topk_idx), _ptr(topk_gate), _ptr(offsets), _ptr(inv),
         T, E, k, capacity, gating, _ptr(topk_idx2), _ptr(topk_gate2), _ptr(offsets2), _ptr(perm2),
         _ptr(inv2), _ptr(n_dropped2), _ptr(workspace), _nbytes(workspace), _stream(stream)))
+
+
+def q_workspace_bytes(T, d, d_ff, E, k, bits):
+    return int(_lib.moe_q_workspace_bytes(T, d, d_ff, E, k, bits))
+
+
+def quantize_weights(w, batch, rows, cols, dt, bits, q, scale, stream=None):
+    """Per-row symmetric INT8 / INT4 quantization of bf16 weights (load time)."""
+    _check("moe_quantize_weights", _lib.moe_quantize_weights(
+        _ptr(w), batch, rows, cols, dt, bits, _ptr(q), _ptr(scale), _stream(stream)))
+
+
+def expert_ffn_q(x, perm, offsets, T, d, d_ff, E, k, bits, q1, s1, q3, s3, q2, s2, dt, out,
+                 workspace, stream=None):
+    _check("moe_expert_ffn_q", _lib.moe_expert_ffn_q(
+        _ptr(x), _ptr(perm), _ptr(offsets), T, d, d_ff, E, k, bits, _ptr(q1), _ptr(s1), _ptr(q3),
+        _ptr(s3), _ptr(q2), _ptr(s2), dt, _ptr(out), _ptr(workspace), _nbytes(workspace),
+        _stream(stream)))

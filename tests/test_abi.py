@@ -33,7 +33,8 @@ def test_every_declared_symbol_is_exported(lm):
                           "moe_backward_workspace_bytes", "moe_combine_backward",
                           "moe_expert_backward", "moe_route_backward", "moe_expert_choice",
                           "moe_gathered_workspace_bytes", "moe_expert_ffn_gathered",
-                          "moe_reroute"}
+                          "moe_reroute", "moe_q_workspace_bytes", "moe_quantize_weights",
+                          "moe_expert_ffn_q"}
     lib = ctypes.CDLL(lm.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -231,3 +232,19 @@ def test_reroute_argument_errors(lm):
     assert L.moe_reroute(*args(E=2000)) == 2
     assert L.moe_reroute(*args(wsb=8)) == 3
     assert lm.workspace_bytes(8, 16, 16, 4, 2, lm.MOE_BF16) >= (2 * 8 * 2 + 4) * 4
+
+
+def test_quantized_argument_errors(lm):
+    L = lm.lib()
+    assert L.moe_quantize_weights(None, 1, 4, 8, 1, 8, FAKE, FAKE, None) == 1
+    assert L.moe_quantize_weights(FAKE, 1, 4, 8, 1, 5, FAKE, FAKE, None) == 1    # bits
+    assert L.moe_quantize_weights(FAKE, 1, 4, 8, 0, 8, FAKE, FAKE, None) == 2    # fp32 weights
+    assert L.moe_quantize_weights(FAKE, 1, 4, 7, 1, 4, FAKE, FAKE, None) == 2    # odd cols, int4
+    q = lambda **kw: [FAKE, FAKE, FAKE, 8, kw.get("d", 128), kw.get("f", 256), 4, 2,
+                      kw.get("bits", 8), FAKE, FAKE, FAKE, FAKE, FAKE, kw.get("s2", FAKE), 1,
+                      FAKE, FAKE, kw.get("wsb", 1 << 40), None]
+    assert L.moe_expert_ffn_q(*q(bits=3)) == 1
+    assert L.moe_expert_ffn_q(*q(s2=None)) == 1
+    assert L.moe_expert_ffn_q(*q(d=64)) == 2                                     # not 128k
+    assert L.moe_expert_ffn_q(*q(wsb=16)) == 3
+    assert lm.q_workspace_bytes(8, 128, 256, 4, 2, 8) >= 16 * 256 * 2
