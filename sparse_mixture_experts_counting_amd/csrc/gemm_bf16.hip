@@ -533,6 +533,55 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_bf16_kernel(const G
     }
     return;
   }
+  if (EPI == EPI_STORE_F32_BIAS && !partial && N % 4 == 0 && p.ldc % 4 == 0) {
+    // fp32 output, four columns per 16-byte store: the four lanes of a quad hold one column each
+    // of four consecutive rows; two DPP exchanges (lane ^ 1, then lane ^ 2) transpose that 4 x 4
+    // block, so lane 4c + s holds row s of columns 4c .. 4c + 3.  The stores are non-temporal:
+    // the output (the weight gradients, 4 bytes per weight) is not read again by this kernel and
+    // would otherwise push the operand tiles out of the caches.
+    const int s4 = lane & 3;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int col0 = n_base + wn0 + j * 32 + (l32 & ~3);
+        f32x4 bias4 = {0.f, 0.f, 0.f, 0.f};
+        if (p.bias && col0 < N) bias4 = *(const f32x4*)(p.bias + col0);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          float a[4], b[4];
+#pragma unroll
+          for (int t = 0; t < 4; ++t) a[t] = acc[0][i][j][4 * q + t];
+          // Exchange across lane ^ 1: swap bit 0 of the lane with bit 0 of the slot.
+          const bool o1 = s4 & 1;
+          const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(
+                                __builtin_bit_cast(int, o1 ? a[0] : a[1]), 0xB1, 0xF, 0xF, false));
+          const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(
+                                __builtin_bit_cast(int, o1 ? a[2] : a[3]), 0xB1, 0xF, 0xF, false));
+          b[0] = o1 ? r0 : a[0];
+          b[1] = o1 ? a[1] : r0;
+          b[2] = o1 ? r1 : a[2];
+          b[3] = o1 ? a[3] : r1;
+          // Exchange across lane ^ 2: swap bit 1 of the lane with bit 1 of the slot.
+          const bool o2 = s4 & 2;
+          const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(
+                                __builtin_bit_cast(int, o2 ? b[0] : b[2]), 0x4E, 0xF, 0xF, false));
+          const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(
+                                __builtin_bit_cast(int, o2 ? b[1] : b[3]), 0x4E, 0xF, 0xF, false));
+          f32x4 w;
+          w[0] = (o2 ? r2 : b[0]) + bias4[0];
+          w[1] = (o2 ? r3 : b[1]) + bias4[1];
+          w[2] = (o2 ? b[2] : r2) + bias4[2];
+          w[3] = (o2 ? b[3] : r3) + bias4[3];
+          const int row = tc.row0 + wm0 + i * 32 + 8 * q + 4 * h + s4;
+          if (row < tc.row_end && col0 < N) {
+            __builtin_nontemporal_store(w, (f32x4*)((float*)Cg + (size_t)row * p.ldc + col0));
+          }
+        }
+      }
+    }
+    return;
+  }
   if (EPI != EPI_STORE_F32_BIAS && !partial && N % 2 == 0 && p.ldc % 2 == 0) {
     // bf16 output, two columns per 4-byte store: lanes 2c and 2c+1 swap one value of each pair of
     // rows (a DPP quad permute), so the even lane holds row a and the odd lane row b of columns
