@@ -148,18 +148,25 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_bf16_kernel(const G
   int kc = 0, nsplit = p.ksplit, rtile = -1;
   int kg_beg = 0, kg_len = 0;               // K-grouped mode: this group's reduction columns
   if (p.kgrouped) {
-    // Tiles group-major; inside a group, bands of 8 m-tiles walked n-tile by n-tile.  Blocks take
-    // tiles in index order, so block b's XCD (b % 8) always gets the same m-tile of a band and
-    // keeps that A tile in its L2 across the n-tiles.  (A tile's work grows with its group's row
-    // count, so contiguous runs of tiles per XCD would load the XCDs unevenly under skewed
-    // routing.)
+    // Tiles group-major; inside a group, bands of 4 m-tiles walked n-tile by n-tile, so 32
+    // consecutive tiles form a 4 x 8 block that reads 4 A and 8 B tiles.  Blocks are dealt to the
+    // 8 XCDs in turn (block b on XCD b % 8); in each whole round of p.slots blocks, XCD x takes
+    // chunk 8 r + x of p.slots / 8 consecutive tiles, so the CUs sharing an L2 share operand
+    // tiles, while consecutive chunks (a group's work, which grows with its row count) still go
+    // to different XCDs.  The last partial round takes tiles in index order.
     const int MT = (p.M + BM - 1) / BM;
     const int per = MT * NT;
-    if ((int)blockIdx.x >= p.G * per) return;
-    const int t = blockIdx.x;
+    const int total = p.G * per;
+    int t = blockIdx.x;
+    if (t >= total) return;
+    const int round = p.slots >= 8 ? p.slots : 8, chunk = round / 8;
+    if (t < total / round * round) {
+      const int x = t & 7, k = t >> 3;
+      t = ((k / chunk) * 8 + x) * chunk + k % chunk;
+    }
     tc.g = t / per;
     const int local = t - tc.g * per;
-    constexpr int GM = 8;
+    constexpr int GM = 4;
     const int band = local / (GM * NT);
     const int m_first = band * GM;
     const int gm = min(MT - m_first, GM);
@@ -775,13 +782,14 @@ static hipError_t launch_t(const GemmParams& p, int rows_max, hipStream_t s) {
   const bool tail = p.ksplit == 1 && p.part != nullptr && EPI != EPI_STORE_F32_BIAS &&
                     EPI != EPI_SWIGLU_BWD && !p.kgrouped && p.N % 8 == 0 && p.K % 64 == 0;
   q.slots = tail ? device_cus() * MINB : 0;
+  if (p.kgrouped) q.slots = device_cus() / 8 * 8 * MINB;   // blocks per round (tile order only)
   const int NT = (p.N + BN - 1) / BN;
   const int tiles = p.kgrouped ? p.G * ((p.M + BM - 1) / BM) * NT
                                : tiles_upper_bound(rows_max, p.G, p.offsets != nullptr, BM, NT);
-  const int grid = tiles * p.ksplit + q.slots;
+  const int grid = tiles * p.ksplit + (p.kgrouped ? 0 : q.slots);
   if (tiles <= 0) return hipSuccess;
   hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * WGM * WGN), lds, s, q);
-  if (q.slots > 0) {
+  if (q.slots > 0 && !p.kgrouped) {
     if constexpr (EPI != EPI_STORE_F32_BIAS && EPI != EPI_SWIGLU_BWD)
       hipLaunchKernelGGL((tail_finish_kernel<BM, BN, NMAT, EPI>), dim3(q.slots * kFinishSplit),
                          dim3(256), 0, s, q);

@@ -49,11 +49,12 @@ struct GemmParams {
 
 enum { EPI_SWIGLU = 0, EPI_STORE = 1, EPI_STORE_F32_BIAS = 2, EPI_SWIGLU_BWD = 3 };
 
-// Padded start of group g's columns in a K-grouped operand: each group starts on a multiple of 8
-// (16-byte loads never straddle two groups) and the layout depends on offsets[g] alone.  The
-// padded width of G groups holding R rows is kpad(R, G).
+// Padded start of group g's columns in a K-grouped operand: each group starts on a multiple of 64
+// columns, so every 64-deep step of a row is one aligned 128-byte line (a step that straddles two
+// lines costs twice the cache requests), and the layout depends on offsets[g] alone.  The padded
+// width of G groups holding R rows is kpad(R, G).
 __host__ __device__ __forceinline__ int kpad(int row_offset, int g) {
-  return ((row_offset + 7) & ~7) + 8 * g;
+  return ((row_offset + 63) & ~63) + 64 * g;
 }
 
 struct TileCoord {
