@@ -71,6 +71,25 @@ constexpr int stage_bytes() {
   return (BM + NMAT * BN) * BK * 2;
 }
 
+constexpr int kMaxLds = 160 * 1024;                 // LDS per CU (and per block) on gfx950
+
+// With direct loads, a 2-stage ring and one block per CU, the B operand (the weights: the stream
+// whose loads miss the caches) gets a third stage in the LDS the 2-stage ring leaves free, so its
+// loads have two steps to land; A keeps the 2-stage ring.
+template <int BM, int BN, int NMAT, int BK, int NST, int MINB>
+constexpr int b_stages() {
+  return (NST == 2 && MINB == 1 &&
+          NST * BM * BK * 2 + (NST + 1) * NMAT * BN * BK * 2 <= kMaxLds)
+             ? NST + 1
+             : NST;
+}
+
+template <int BM, int BN, int NMAT, int BK, int NST, int MINB>
+constexpr int lds_bytes() {
+  return NST == 0 ? 2 * stage_bytes<BM, BN, NMAT, BK>()
+                  : NST * BM * BK * 2 + b_stages<BM, BN, NMAT, BK, NST, MINB>() * NMAT * BN * BK * 2;
+}
+
 constexpr int waitcnt_lgkm0() {                    // s_waitcnt lgkmcnt(0), other counters free
   return 15 | (3 << 14) | (7 << 4) | (0 << 8);
 }
@@ -307,18 +326,24 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_bf16_kernel(const G
   // Direct loads of the step starting at k0 into the stage at stage_off.  Units at or past the end
   // of this block's K range (a ragged K, or a step past the last one) are sent out of the buffer's
   // range: they read zeros and touch no memory.
-  auto issue_dma = [&](int stage_off, int k0) {
+  // Loads j in [J0, J1) (A blocks first, then B): an A block goes to a_off + its offset in a
+  // stage, a B block to b_off + its offset (b_off is the B stage's address minus B_OFF).
+  auto issue_dma_range = [&](int a_off, int b_off, int k0, auto J0, auto J1) {
     const uint32_t koff = (uint32_t)k0 * 2u;
 #pragma unroll
-    for (int j = 0; j < DPW; ++j) {
+    for (int j = decltype(J0)::value; j < decltype(J1)::value; ++j) {
       const bool is_a = j < DPW_A;
       const bool second = NMAT == 2 && !is_a && ((j - DPW_A) * DROWS * NW) / BN == 1;
       const uint32_t voff = k0 < d_kmax[j] ? d_voff[j] + koff : (is_a ? a_bytes : b_bytes);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(is_a ? rA : (second ? rB1 : rB0),
-                                               (lds_void_t*)(smem + stage_off +
+                                               (lds_void_t*)(smem + (is_a ? a_off : b_off) +
                                                              (wave + NW * j) * 1024),
                                                16, (int)voff, 0, 0, 0);
     }
+  };
+  auto issue_dma = [&](int stage_off, int k0) {
+    issue_dma_range(stage_off, stage_off, k0, std::integral_constant<int, 0>(),
+                    std::integral_constant<int, DPW>());
   };
   auto store_regs = [&](int set, int stage_off) {
 #pragma unroll
@@ -353,17 +378,18 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_bf16_kernel(const G
 
   bf16x8 af[2][TM];
   bf16x8 bfr[2][NMAT][TN];
-  auto read_frags = [&](int stage_off, int ks, int buf) {
+  auto read_frags2 = [&](int a_off, int b_off, int ks, int buf) {
 #pragma unroll
     for (int i = 0; i < TM; ++i)
-      af[buf][i] = *(const lds_bf16x8_t*)(smem + stage_off + a_rd[ks] + i * 32 * RB);
+      af[buf][i] = *(const lds_bf16x8_t*)(smem + a_off + a_rd[ks] + i * 32 * RB);
 #pragma unroll
     for (int m = 0; m < NMAT; ++m)
 #pragma unroll
       for (int j = 0; j < TN; ++j)
         bfr[buf][m][j] =
-            *(const lds_bf16x8_t*)(smem + stage_off + b_rd[ks] + (m * BN + j * 32) * RB);
+            *(const lds_bf16x8_t*)(smem + b_off + b_rd[ks] + (m * BN + j * 32) * RB);
   };
+  auto read_frags = [&](int stage_off, int ks, int buf) { read_frags2(stage_off, stage_off, ks, buf); };
   auto mfmas = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < TM; ++i)
@@ -381,6 +407,54 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_bf16_kernel(const G
   if constexpr (DMA) {
     // NST-stage ring: the loads of step kt+NST-1 go into the stage that step kt-1 used, so a load
     // has NST-1 steps to land; the barrier that ends step kt waits only for step kt+1's loads.
+    constexpr int NSB = b_stages<BM, BN, NMAT, BK, NST, MINB>();
+    constexpr int A_BYTES = BM * RB, B_BYTES = NMAT * BN * RB;
+    // Split rings: A stage s at s * A_BYTES, B stage s at NST * A_BYTES + s * B_BYTES.  In step kt
+    // the loads of A(kt + 1) go out before those of B(kt + 2), so waiting until only the latter
+    // are in flight (vmcnt counts in issue order) leaves A(kt + 1) and B(kt + 1) landed.
+    auto run_split = [&](auto MATH) {
+      constexpr bool math = decltype(MATH)::value;
+      constexpr int DPW_B = DPW - DPW_A;
+      const std::integral_constant<int, 0> j0;
+      const std::integral_constant<int, DPW_A> ja;
+      const std::integral_constant<int, DPW> j1;
+      auto b_at = [&](int sb) { return NST * A_BYTES + sb * B_BYTES - B_OFF; };
+      issue_dma_range(0, 0, kbeg, j0, ja);
+      issue_dma_range(0, b_at(0), kbeg, ja, j1);
+      issue_dma_range(0, b_at(1), kbeg + BK, ja, j1);
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0<DPW_B>());
+      barrier_no_fence();
+      if constexpr (math) read_frags2(0, b_at(0), 0, 0);
+      int sa = 0, sb = 0;                           // stages of step kt
+      for (int kt = 0; kt < KT; ++kt) {
+        const int na = sa ^ 1;
+        const int nb = sb + 1 == NSB ? 0 : sb + 1;
+        const int fb = sb == 0 ? NSB - 1 : sb - 1;  // stage of step kt + 2
+        issue_dma_range(na * A_BYTES, 0, kbeg + (kt + 1) * BK, j0, ja);
+        issue_dma_range(0, b_at(fb), kbeg + (kt + 2) * BK, ja, j1);
+        if constexpr (math) {
+#pragma unroll
+          for (int ks = 0; ks < KS - 1; ++ks) {
+            read_frags2(sa * A_BYTES, b_at(sb), ks + 1, (ks + 1) & 1);
+            __builtin_amdgcn_sched_barrier(0);
+            mfmas(ks & 1);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0<DPW_B>());
+        barrier_no_fence();
+        if constexpr (math) {
+          read_frags2(na * A_BYTES, b_at(nb), 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+          mfmas((KS - 1) & 1);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        sa = na;
+        sb = nb;
+      }
+      // The last step's loads (past the end of K: zeros) land before the block may exit.
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0<0>());
+    };
     auto run = [&](auto MATH) {
       constexpr bool math = decltype(MATH)::value;
 #pragma unroll
@@ -413,10 +487,18 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_bf16_kernel(const G
         st = nx;
       }
     };
-    if (active)
-      run(std::true_type());
-    else
-      run(std::false_type());
+    if constexpr (NSB > NST) {
+      static_assert(NST == 2, "split rings take a 2-stage A ring");
+      if (active)
+        run_split(std::true_type());
+      else
+        run_split(std::false_type());
+    } else {
+      if (active)
+        run(std::true_type());
+      else
+        run(std::false_type());
+    }
   } else {
     auto run = [&](auto MATH) {
       constexpr bool math = decltype(MATH)::value;
@@ -768,7 +850,7 @@ static int device_cus() {
 template <int BM, int BN, int NMAT, int WGM, int WGN, int BK, int NST, int MINB, int EPI, bool TAIL>
 static hipError_t launch_t(const GemmParams& p, int rows_max, hipStream_t s) {
   auto kern = gemm_bf16_kernel<BM, BN, NMAT, WGM, WGN, BK, NST, MINB, EPI, TAIL>;
-  const size_t lds = (NST > 0 ? NST : 2) * (size_t)stage_bytes<BM, BN, NMAT, BK>();
+  const size_t lds = (size_t)lds_bytes<BM, BN, NMAT, BK, NST, MINB>();
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute((const void*)kern,
