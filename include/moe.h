@@ -373,8 +373,10 @@ moe_status moe_combine_backward(const void* dy, const void* expert_out, const in
  * Same row convention, weight storage and dense (perm == NULL, E == 1) mode as moe_expert_ffn;
  * dw1, dw3 [E][d_ff][d] and dw2 [E][d][d_ff] fp32 in that same storage (experts with no rows get
  * zeros).  Rows of dx_rows past offsets[E] are not written.  Intermediates (dh, h, da, db) are
- * rounded to bf16.  The workspace (moe_backward_workspace_bytes) holds transposed copies of the
- * weights and activations (about 3 E d d_ff + 8 T k (d + d_ff) bytes).  MOE_F32 is unsupported.
+ * rounded to bf16.  The workspace (moe_backward_workspace_bytes) holds the intermediates and
+ * transposed copies of the activations (about 8 T k (d + d_ff) bytes); when d_ff is not a
+ * multiple of 64 it also holds transposed copies of the weights (3 E d d_ff bf16 more).  MOE_F32 is
+ * unsupported.
  */
 moe_status moe_expert_backward(const void* x, const int32_t* perm, const int32_t* offsets, int T,
                                int d, int d_ff, int E, int k, const void* w1, const void* w3,

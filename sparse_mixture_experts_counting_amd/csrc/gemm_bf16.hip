@@ -42,6 +42,37 @@ namespace moe {
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4_t;
 typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8_t;
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4_t;
+
+// Transposed-B stages hold K rows of BN columns (2 BN bytes); unit u of row r is stored at
+// u ^ swzT(r).  A transposing read takes 4 consecutive rows of 32 bytes at one unit pair; the
+// swizzle sends those 4 rows (and the two column halves of a wave) to disjoint banks.
+__device__ __forceinline__ int swzT(int r) { return 4 * (r & 3); }
+
+// A raw buffer descriptor (base, stride 0, num_records bytes) held in scalar registers.
+typedef uint32_t desc_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ desc_t make_desc(const void* base, uint32_t num_records) {
+  const uint64_t a = (uint64_t)base;
+  desc_t d;
+  d[0] = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  d[1] = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32) & 0xffffu);
+  d[2] = __builtin_amdgcn_readfirstlane(num_records);
+  d[3] = 0x00020000u;
+  return d;
+}
+
+// One wave-wide 16-byte direct-to-LDS load (lane l to byte lds + 16 l), issued where the compiler
+// does not see it: the transposing LDS reads would otherwise make it wait for every such load in
+// flight (it cannot tell the stages apart) before each of them.  No register is written; the
+// loads are waited for by the explicit vmcnt waits of the main loop.
+__device__ __forceinline__ void dma16(desc_t desc, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               :
+               : "v"(voff), "s"(desc), "s"(lds)
+               : "memory", "m0");
+}
 
 // Physical 16-byte unit of logical unit u in LDS row r is u ^ swz(r).  Both forms depend on r % 32
 // only, keep 16 consecutive rows read at one unit in distinct 4-bank groups (with 64 banks; and 8
@@ -129,7 +160,8 @@ __device__ __forceinline__ TailPlan tail_plan(int total, int slots, int K) {
   return tp;
 }
 
-template <int BM, int BN, int NMAT, int WGM, int WGN, int BK, int NST, int MINB, int EPI, bool TAIL>
+template <int BM, int BN, int NMAT, int WGM, int WGN, int BK, int NST, int MINB, int EPI, bool TAIL,
+          bool BT = false>
 __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_bf16_kernel(const GemmParams p) {
   constexpr int NTHR = 64 * WGM * WGN;
   constexpr int WM = BM / WGM, WN = BN / WGN;       // WGM x WGN waves
@@ -159,6 +191,10 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_bf16_kernel(const G
   constexpr int DPW_A = BM / (DROWS * NW);                // the first DPW_A of them are A rows
   static_assert(!DMA || (DPW_A * DROWS * NW == BM && DPW * DROWS * NW == BM + NMAT * BN &&
                          BN % (DROWS * NW) == 0), "direct loads split evenly");
+  // Transposed B: a stage's B block is BK rows of RBT bytes; one direct load fills RPB rows.
+  constexpr int RBT = BN * 2, UPB = RBT / 16, RPB = 1024 / RBT;
+  static_assert(!BT || (DMA && NMAT == 1 && BN == 256 && EPI == EPI_STORE && BK * RBT == BN * RB),
+                "transposed B: direct loads, one 256-column matrix, bf16 output");
 
   extern __shared__ __align__(16) uint8_t smem[];
 
@@ -229,23 +265,33 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_bf16_kernel(const G
   // matrix core busy with only one of its two waves.
   const int wm0 = (wave / WGN) * WM;
   const int wn0 = (wave % WGN) * WN;
-  static_assert(WGM * WGN <= 4 || WGN == 2, "row slices spread over the SIMDs");
+  static_assert(WGM * WGN <= 4 || (WGN == 2 || WGN == 4), "row slices spread over the SIMDs");
   const int n_base = tc.n_tile * BN;
   const int K = p.K, N = p.N;
 
   // Buffer descriptors: 32-bit offsets, and loads at or past num_records return zeros.
   const int lda = p.lda ? p.lda : K, ldb = p.ldb ? p.ldb : K;
   const uint32_t a_bytes = (uint32_t)p.a_rows * (uint32_t)lda * 2u;
-  const uint32_t b_bytes = (uint32_t)N * (uint32_t)ldb * 2u;
+  // Transposed B: [K][N] with row stride ldb_t; each of the stacked matrices holds bt_k1 rows.
+  const int ldb_t = p.ldb ? p.ldb : N;
+  const uint32_t b_bytes =
+      BT ? (uint32_t)(p.bt_k1 > 0 ? p.bt_k1 : K) * (uint32_t)ldb_t * 2u : (uint32_t)N * (uint32_t)ldb * 2u;
   const __amdgpu_buffer_rsrc_t rA =
       __builtin_amdgcn_make_buffer_rsrc((void*)p.A, (short)0, a_bytes, 0x00020000);
   const __amdgpu_buffer_rsrc_t rB0 = __builtin_amdgcn_make_buffer_rsrc(
       (void*)((const uint16_t*)p.B0 + (size_t)tc.g * p.b_gstride), (short)0, b_bytes, 0x00020000);
   const __amdgpu_buffer_rsrc_t rB1 =
-      NMAT == 2 ? __builtin_amdgcn_make_buffer_rsrc(
+      (NMAT == 2 || BT) ? __builtin_amdgcn_make_buffer_rsrc(
                       (void*)((const uint16_t*)p.B1 + (size_t)tc.g * p.b_gstride), (short)0,
                       b_bytes, 0x00020000)
                 : rB0;
+
+  desc_t dA{}, dB0{}, dB1{};
+  if constexpr (BT) {
+    dA = make_desc(p.A, a_bytes);
+    dB0 = make_desc((const uint16_t*)p.B0 + (size_t)tc.g * p.b_gstride, b_bytes);
+    dB1 = make_desc(p.B1 ? (const uint16_t*)p.B1 + (size_t)tc.g * p.b_gstride : nullptr, b_bytes);
+  }
 
   // Unit c = tid + NTHR i of an operand is row c / UPR, unit c % UPR (UPR consecutive lanes read
   // one row's step of K, 64 or 128 contiguous bytes).  A rows past the group's end and B rows past
@@ -283,6 +329,12 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_bf16_kernel(const G
         const int grow = min(tc.row0 + srow, tc.row_end - 1);
         const int src = p.gather ? p.gather[grow] / p.gather_div : grow;
         d_voff[j] = ((uint32_t)src * (uint32_t)lda + 8u * uu) * 2u;
+      } else if constexpr (BT) {
+        // Row kr of the stage's B block (a K row), physical unit lane % UPB.
+        const int kr = (wave + NW * (j - DPW_A)) * RPB + lane / UPB;
+        const int ub = (lane % UPB) ^ swzT(kr);
+        const int n = min(n_base + 8 * ub, N - 8);
+        d_voff[j] = ((uint32_t)kr * (uint32_t)ldb_t + (uint32_t)n) * 2u;
       } else {
         const int n = min(n_base + (srow - BM) % BN, N - 1);
         d_voff[j] = ((uint32_t)n * (uint32_t)ldb + 8u * uu) * 2u;
@@ -290,8 +342,9 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_bf16_kernel(const G
     }
   }
 
-  const int Kc = p.kgrouped ? kg_len : K / nsplit;
-  const int kbeg = p.kgrouped ? kg_beg : kc * Kc;
+  // Uniform across the block (the compiler cannot always prove it through the tile scan).
+  const int Kc = __builtin_amdgcn_readfirstlane(p.kgrouped ? kg_len : K / nsplit);
+  const int kbeg = __builtin_amdgcn_readfirstlane(p.kgrouped ? kg_beg : kc * Kc);
   const int kend = kbeg + Kc;
   const int KT = (Kc + BK - 1) / BK;
   const int k_last = kbeg + (KT - 1) * BK;
@@ -303,6 +356,13 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_bf16_kernel(const G
       // they read zeros without touching memory.
       const bool live = j < DPW_A ? tc.row0 + srow < tc.row_end : n_base + (srow - BM) % BN < N;
       d_kmax[j] = live ? kend - 8 * ((lane % UPR) ^ swz<BK>(srow)) : INT_MIN;
+      if constexpr (BT) {
+        if (j >= DPW_A) {   // a K row: live while k0 + kr < kend and its 8 columns lie below N
+          const int kr = (wave + NW * (j - DPW_A)) * RPB + lane / UPB;
+          const int ub = (lane % UPB) ^ swzT(kr);
+          d_kmax[j] = n_base + 8 * ub < N ? kend - kr : INT_MIN;
+        }
+      }
     }
   }
 
@@ -333,12 +393,25 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_bf16_kernel(const G
 #pragma unroll
     for (int j = decltype(J0)::value; j < decltype(J1)::value; ++j) {
       const bool is_a = j < DPW_A;
-      const bool second = NMAT == 2 && !is_a && ((j - DPW_A) * DROWS * NW) / BN == 1;
-      const uint32_t voff = k0 < d_kmax[j] ? d_voff[j] + koff : (is_a ? a_bytes : b_bytes);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(is_a ? rA : (second ? rB1 : rB0),
-                                               (lds_void_t*)(smem + (is_a ? a_off : b_off) +
-                                                             (wave + NW * j) * 1024),
-                                               16, (int)voff, 0, 0, 0);
+      bool second = NMAT == 2 && !is_a && ((j - DPW_A) * DROWS * NW) / BN == 1;
+      uint32_t step_off = koff;
+      if constexpr (BT) {
+        if (!is_a) {   // K rows: k0 moves along rows; past bt_k1 they come from B1
+          second = p.bt_k1 > 0 && k0 >= p.bt_k1;
+          step_off = (uint32_t)(second ? k0 - p.bt_k1 : k0) * (uint32_t)ldb_t * 2u;
+        }
+      }
+      const uint32_t voff = k0 < d_kmax[j] ? d_voff[j] + step_off : (is_a ? a_bytes : b_bytes);
+      if constexpr (BT) {
+        dma16(is_a ? dA : (second ? dB1 : dB0), voff,
+              (uint32_t)(size_t)(lds_void_t*)(smem + (is_a ? a_off : b_off) +
+                                              (wave + NW * j) * 1024));
+      } else {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(is_a ? rA : (second ? rB1 : rB0),
+                                                 (lds_void_t*)(smem + (is_a ? a_off : b_off) +
+                                                               (wave + NW * j) * 1024),
+                                                 16, (int)voff, 0, 0, 0);
+      }
     }
   };
   auto issue_dma = [&](int stage_off, int k0) {
@@ -378,16 +451,42 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_bf16_kernel(const G
 
   bf16x8 af[2][TM];
   bf16x8 bfr[2][NMAT][TN];
+  // Transposed B: lane l needs column l % 32 and K 8 (l / 32) .. +7 of a 32-column block.  Two
+  // transposing reads (rows r .. r+3, then r+4 .. r+7) each give a lane 4 K values of one column:
+  // in a group of 16 lanes, lane 4 q + a names row r + q and columns 4 a .. 4 a + 3, and lane s of
+  // the group receives column s of the 4 rows.
+  int bt_rd[BT ? TN : 1];
+  if constexpr (BT) {
+    const int g16 = lane >> 4, s16 = lane & 15, qa = s16 >> 2, aa = s16 & 3;
+    const int kh = g16 >> 1, nh = g16 & 1;
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int n = wn0 + 32 * j + 16 * nh + 4 * aa;
+      const int r = 8 * kh + qa;
+      bt_rd[j] = B_OFF + r * RBT + (((n >> 3) ^ swzT(r)) << 4) + (n & 7) * 2;
+    }
+  }
   auto read_frags2 = [&](int a_off, int b_off, int ks, int buf) {
 #pragma unroll
     for (int i = 0; i < TM; ++i)
       af[buf][i] = *(const lds_bf16x8_t*)(smem + a_off + a_rd[ks] + i * 32 * RB);
+    if constexpr (BT) {
 #pragma unroll
-    for (int m = 0; m < NMAT; ++m)
+      for (int j = 0; j < TN; ++j) {
+        const uint8_t* bp = smem + b_off + bt_rd[j] + ks * 16 * RBT;
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)bp);
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(bp + 4 * RBT));
+        const i16x8 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        bfr[buf][0][j] = __builtin_bit_cast(bf16x8, both);
+      }
+    } else {
 #pragma unroll
-      for (int j = 0; j < TN; ++j)
-        bfr[buf][m][j] =
-            *(const lds_bf16x8_t*)(smem + b_off + b_rd[ks] + (m * BN + j * 32) * RB);
+      for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          bfr[buf][m][j] =
+              *(const lds_bf16x8_t*)(smem + b_off + b_rd[ks] + (m * BN + j * 32) * RB);
+    }
   };
   auto read_frags = [&](int stage_off, int ks, int buf) { read_frags2(stage_off, stage_off, ks, buf); };
   auto mfmas = [&](int buf) {
@@ -847,9 +946,10 @@ static int device_cus() {
   return cus[dev] > 0 ? cus[dev] : 0;
 }
 
-template <int BM, int BN, int NMAT, int WGM, int WGN, int BK, int NST, int MINB, int EPI, bool TAIL>
+template <int BM, int BN, int NMAT, int WGM, int WGN, int BK, int NST, int MINB, int EPI, bool TAIL,
+          bool BT = false>
 static hipError_t launch_t(const GemmParams& p, int rows_max, hipStream_t s) {
-  auto kern = gemm_bf16_kernel<BM, BN, NMAT, WGM, WGN, BK, NST, MINB, EPI, TAIL>;
+  auto kern = gemm_bf16_kernel<BM, BN, NMAT, WGM, WGN, BK, NST, MINB, EPI, TAIL, BT>;
   const size_t lds = (size_t)lds_bytes<BM, BN, NMAT, BK, NST, MINB>();
   static bool attr_set = false;
   if (!attr_set) {
@@ -879,12 +979,14 @@ static hipError_t launch_t(const GemmParams& p, int rows_max, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int BM, int BN, int NMAT, int WGM, int WGN, int BK, int NST, int MINB, int EPI>
+template <int BM, int BN, int NMAT, int WGM, int WGN, int BK, int NST, int MINB, int EPI,
+          bool BT = false>
 static hipError_t launch_tail_or_not(const GemmParams& p, int rows_max, hipStream_t s) {
   // The direct-load path handles any K range; the register path needs an even step count.
   const bool even_steps = NST > 0 || (p.K / p.ksplit) % (2 * BK) == 0;
-  return even_steps ? launch_t<BM, BN, NMAT, WGM, WGN, BK, NST, MINB, EPI, false>(p, rows_max, s)
-                    : launch_t<BM, BN, NMAT, WGM, WGN, BK, NST, MINB, EPI, true>(p, rows_max, s);
+  return even_steps
+             ? launch_t<BM, BN, NMAT, WGM, WGN, BK, NST, MINB, EPI, false, BT>(p, rows_max, s)
+             : launch_t<BM, BN, NMAT, WGM, WGN, BK, NST, MINB, EPI, true, BT>(p, rows_max, s);
 }
 
 static void launch_splitk_finish(const GemmParams& p, int rows_max, int epi, hipStream_t s) {
@@ -967,11 +1069,19 @@ size_t gemm_bf16_partial_bytes(int rows_max, int G, bool grouped, int N, int K, 
 // Needs K (and the row strides) a multiple of 8 (16-byte rows) and every operand under 2 GiB
 // (32-bit buffer offsets).
 hipError_t launch_gemm_bf16(const GemmParams& p_in, int rows_max, int epi, hipStream_t s) {
-  const int lda = p_in.lda ? p_in.lda : p_in.K, ldb = p_in.ldb ? p_in.ldb : p_in.K;
+  const int lda = p_in.lda ? p_in.lda : p_in.K;
+  const int ldb = p_in.ldb ? p_in.ldb : (p_in.bt ? p_in.N : p_in.K);
   if (p_in.K % 8 != 0 || lda % 8 != 0 || ldb % 8 != 0 || p_in.N < 1 || p_in.K < 8)
     return hipErrorNotSupported;
-  if ((long long)p_in.a_rows * lda * 2 >= (1ll << 31) || (long long)p_in.N * ldb * 2 >= (1ll << 31))
+  const long long b_rows = p_in.bt ? (p_in.bt_k1 > 0 ? p_in.bt_k1 : p_in.K) : p_in.N;
+  if ((long long)p_in.a_rows * lda * 2 >= (1ll << 31) || b_rows * ldb * 2 >= (1ll << 31))
     return hipErrorNotSupported;
+  if (p_in.bt) {
+    // Transposed B: bf16 output, N a multiple of 8, the stacked matrices split on a 64-deep step.
+    if (epi != EPI_STORE || p_in.kgrouped || p_in.N % 8 != 0 || ldb < p_in.N ||
+        (p_in.bt_k1 > 0 && (p_in.bt_k1 % 64 != 0 || p_in.bt_k1 >= p_in.K)))
+      return hipErrorNotSupported;
+  }
   GemmParams p = p_in;
   const bool grouped = p.offsets != nullptr;
   if (p.kgrouped) {             // weight gradients: fp32 out, 256 x 256 tiles, no split
@@ -992,8 +1102,12 @@ hipError_t launch_gemm_bf16(const GemmParams& p_in, int rows_max, int epi, hipSt
               : launch_tail_or_not<128, 128, 2, 2, 2, 32, 3, 2, EPI_SWIGLU>(p, rows_max, s);
       break;
     case EPI_STORE:
-      e = big ? launch_tail_or_not<256, 256, 1, 4, 2, 64, 2, 1, EPI_STORE>(p, rows_max, s)
-              : launch_tail_or_not<128, 256, 1, 2, 2, 32, 3, 2, EPI_STORE>(p, rows_max, s);
+      if (p.bt)
+        e = big ? launch_tail_or_not<256, 256, 1, 2, 4, 64, 2, 1, EPI_STORE, true>(p, rows_max, s)
+                : launch_tail_or_not<128, 256, 1, 2, 2, 32, 3, 2, EPI_STORE, true>(p, rows_max, s);
+      else
+        e = big ? launch_tail_or_not<256, 256, 1, 4, 2, 64, 2, 1, EPI_STORE>(p, rows_max, s)
+                : launch_tail_or_not<128, 256, 1, 2, 2, 32, 3, 2, EPI_STORE>(p, rows_max, s);
       break;
     case EPI_SWIGLU_BWD:
       e = big ? launch_tail_or_not<256, 128, 2, 4, 2, 64, 2, 1, EPI_SWIGLU_BWD>(p, rows_max, s)

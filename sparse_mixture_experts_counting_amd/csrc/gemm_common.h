@@ -45,6 +45,12 @@ struct GemmParams {
   // [0, N) and db in [N, 2N): da = dh * b * silu'(a), db = dh * silu(a).  All bf16.
   const void* D;
   void* H;
+  // Transposed B (bt != 0; one matrix, bf16 output): B_g is stored [K][N] (row stride ldb, or N),
+  // i.e. N-contiguous, as a linear layer's weight is for the products that reduce over its output
+  // dimension.  With bt_k1 > 0, rows k < bt_k1 come from B0 and rows k >= bt_k1 from row
+  // k - bt_k1 of B1 (two matrices stacked along K).
+  int bt;
+  int bt_k1;
 };
 
 enum { EPI_SWIGLU = 0, EPI_STORE = 1, EPI_STORE_F32_BIAS = 2, EPI_SWIGLU_BWD = 3 };

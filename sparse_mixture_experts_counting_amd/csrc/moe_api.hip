@@ -46,9 +46,15 @@ size_t ffn_workspace_bytes(int rows, bool grouped, int G, int d, int d_ff, moe_d
   return h_bytes(rows, d_ff, dt) + ffn_partial_bytes(rows, grouped, G, d, d_ff, dt);
 }
 
-// moe_expert_backward workspace (bf16): the transposed weights, the row-major intermediates, the
-// group-padded transposed operands of the weight-gradient products, two ints of dense offsets and
-// the split-K scratch of the input-gradient products, in this order.
+// The input-gradient products read the weights as stored (the GEMM's transposed-B mode) when
+// d_ff is a multiple of 64, so that the stacked w1 / w3 of dx split on a 64-deep step; otherwise
+// they read transposed copies made in the workspace.
+bool bwd_weights_in_place(int d_ff) { return d_ff % 64 == 0; }
+
+// moe_expert_backward workspace (bf16): the transposed weights (only without in-place weights),
+// the row-major intermediates, the group-padded transposed operands of the weight-gradient
+// products, two ints of dense offsets and the split-K scratch of the input-gradient products, in
+// this order.
 struct BwdLayout {
   size_t w2t, w13t, dh, h, dab, doT, hT, dabT, xgT, offs, part, total;
 };
@@ -57,8 +63,9 @@ BwdLayout bwd_layout(int rows, bool grouped, int G, int d, int d_ff) {
   BwdLayout L;
   size_t o = 0;
   auto take = [&](size_t bytes) { const size_t at = o; o += align_up(bytes); return at; };
-  L.w2t = take((size_t)G * d_ff * d * 2);
-  L.w13t = take((size_t)G * d * 2 * d_ff * 2);
+  const bool in_place = bwd_weights_in_place(d_ff);
+  L.w2t = take(in_place ? 0 : (size_t)G * d_ff * d * 2);
+  L.w13t = take(in_place ? 0 : (size_t)G * d * 2 * d_ff * 2);
   L.dh = take((size_t)rows * d_ff * 2);
   L.h = take((size_t)rows * d_ff * 2);
   L.dab = take((size_t)rows * 2 * d_ff * 2);
@@ -534,18 +541,26 @@ moe_status moe_expert_backward(const void* x, const int32_t* perm, const int32_t
   float* part = (float*)(ws + L.part);
   if (!grouped) moe::launch_dense_offsets(offs, T, s);
 
-  // Weights as the input-gradient products read them: w2T[e][n][i] = w2[e][i][n], and
-  // w13T[e][i] = (w1[e][.][i], w3[e][.][i]) side by side (K = 2 d_ff).
-  moe::launch_transpose16(w2, G, d, d_ff, w2t, d, (long long)d_ff * d, s);
-  moe::launch_transpose16(w1, G, d_ff, d, w13t, 2 * d_ff, (long long)d * 2 * d_ff, s);
-  moe::launch_transpose16(w3, G, d_ff, d, (uint16_t*)w13t + d_ff, 2 * d_ff,
-                          (long long)d * 2 * d_ff, s);
+  const bool in_place = bwd_weights_in_place(d_ff);
+  if (!in_place) {
+    // Weights as the input-gradient products read them: w2T[e][n][i] = w2[e][i][n], and
+    // w13T[e][i] = (w1[e][.][i], w3[e][.][i]) side by side (K = 2 d_ff).
+    moe::launch_transpose16(w2, G, d, d_ff, w2t, d, (long long)d_ff * d, s);
+    moe::launch_transpose16(w1, G, d_ff, d, w13t, 2 * d_ff, (long long)d * 2 * d_ff, s);
+    moe::launch_transpose16(w3, G, d_ff, d, (uint16_t*)w13t + d_ff, 2 * d_ff,
+                            (long long)d * 2 * d_ff, s);
+  }
   hipError_t e;
-  {   // dh = d_out w2 (rows of each expert)
+  {   // dh = d_out w2 (rows of each expert); w2[e] is [d][d_ff], i.e. [K][N]
     moe::GemmParams q{};
     q.A = d_out; q.a_rows = rows; q.gather_div = 1;
     q.offsets = grouped ? offsets : nullptr; q.G = G; q.M = T;
-    q.N = d_ff; q.K = d; q.B0 = w2t; q.b_gstride = (long long)d_ff * d;
+    q.N = d_ff; q.K = d; q.b_gstride = (long long)d_ff * d;
+    if (in_place) {
+      q.B0 = w2; q.bt = 1; q.ldb = d_ff;
+    } else {
+      q.B0 = w2t;
+    }
     q.C = dh; q.ldc = d_ff; q.part = part;
     if ((e = moe::launch_gemm_bf16(q, rows, moe::EPI_STORE, s)) != hipSuccess) return MOE_ERR_DEVICE;
   }
@@ -558,11 +573,17 @@ moe_status moe_expert_backward(const void* x, const int32_t* perm, const int32_t
     if ((e = moe::launch_gemm_bf16(q, rows, moe::EPI_SWIGLU_BWD, s)) != hipSuccess)
       return MOE_ERR_DEVICE;
   }
-  {   // dx_rows = da w1 + db w3
+  {   // dx_rows = da w1 + db w3: K = 2 d_ff over [da | db] and w1[e], w3[e] ([d_ff][d]) stacked
     moe::GemmParams q{};
     q.A = dab; q.a_rows = rows; q.gather_div = 1;
     q.offsets = grouped ? offsets : nullptr; q.G = G; q.M = T;
-    q.N = d; q.K = 2 * d_ff; q.B0 = w13t; q.b_gstride = (long long)d * 2 * d_ff;
+    q.N = d; q.K = 2 * d_ff;
+    if (in_place) {
+      q.B0 = w1; q.B1 = w3; q.bt = 1; q.bt_k1 = d_ff; q.ldb = d;
+      q.b_gstride = (long long)d_ff * d;
+    } else {
+      q.B0 = w13t; q.b_gstride = (long long)d * 2 * d_ff;
+    }
     q.C = dx_rows; q.ldc = d; q.part = part;
     if ((e = moe::launch_gemm_bf16(q, rows, moe::EPI_STORE, s)) != hipSuccess) return MOE_ERR_DEVICE;
   }

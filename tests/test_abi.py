@@ -147,8 +147,11 @@ def test_update_select_bias_argument_errors(lm):
 def test_backward_workspace_bytes(lm):
     T, d, f, E, k = 4096, 4096, 14336, 8, 2
     ws = lm.backward_workspace_bytes(T, d, f, E, k, lm.MOE_BF16)
-    assert ws >= 3 * E * d * f * 2                 # transposed copies of the three weights
     assert ws >= T * k * 4 * f * 2                  # dh, h, da and db of every expert row
+    assert ws < 3 * E * d * f * 2                   # d_ff % 64 == 0: weights read in place
+    f2 = f + 8                                      # otherwise transposed copies of the weights
+    ws2 = lm.backward_workspace_bytes(T, d, f2, E, k, lm.MOE_BF16)
+    assert ws2 >= 3 * E * d * f2 * 2 + T * k * 4 * f2 * 2
     assert lm.backward_workspace_bytes(T, d, f, E, k, lm.MOE_F32) == 0
     assert lm.backward_workspace_bytes(0, d, f, E, k, lm.MOE_BF16) == 0
 

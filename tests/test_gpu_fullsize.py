@@ -93,3 +93,73 @@ def test_full_size_workload(M, name):
     err = P.rel_err(y_gpu, y_ref)
     print("  y rel err %.3e on %d tokens" % (err, len(tokens)), flush=True)
     assert err <= P.y_tol(cfg)
+
+
+BWD_TOL = 2e-2   # the GPU rounds dh, h, da and db to bf16 (as the small-size backward tests)
+
+
+@pytest.mark.parametrize("name", ["mixtral_decode", "mixtral_prefill", "deepseek_fine"])
+def test_full_size_expert_backward(M, name):
+    """moe_expert_backward at the full sizes, as the training benchmark runs it: the input
+    gradient of sampled expert rows (full d_ff) and sampled rows / columns of the weight gradients
+    of a few experts (all their rows; SwiGLU acts per d_ff index, so restricting d_ff is exact),
+    against the oracle fed the GPU's own d_out.  Experts without rows get zero gradients."""
+    print("full-size backward", name, flush=True)
+    cfg = M["synth"].CONFIGS[name]
+    inp = M["synth"].make_inputs(cfg, seed=0, device="cuda")
+    b = M["layer"].alloc_buffers(cfg)
+    M["layer"].forward(cfg, inp, b)
+    dy = M["synth"].make_dy(cfg, seed=0, device="cuda")
+    g = M["layer"].alloc_grads(cfg)
+    M["layer"].backward(cfg, inp, b, dy, g)
+    torch.cuda.synchronize()
+    k = cfg.k
+    offsets, perm = P.npi(b.offsets), P.npi(b.perm)
+    counts = np.diff(offsets)
+    n_kept = int(offsets[-1])
+    rng = np.random.default_rng(11)
+
+    def rows_of(rr):
+        rr = np.asarray(sorted(rr))
+        return rr, torch.as_tensor(rr, device="cuda")
+
+    # Input gradient of sampled expert rows.
+    rows = set([0, n_kept - 1]) | set(rng.choice(n_kept, size=10, replace=False).tolist())
+    by_e = {}
+    for r in rows:
+        by_e.setdefault(int(np.searchsorted(offsets, r, side="right") - 1), []).append(r)
+    got, want = [], []
+    for e, rr in sorted(by_e.items()):
+        rr, rr_d = rows_of(rr)
+        tok = torch.as_tensor(perm[rr] // k, device="cuda")
+        dX, _, _, _ = O.swiglu_ffn_backward(P.np32(inp.x[tok]), P.np32(inp.w1[e]),
+                                            P.np32(inp.w3[e]), P.np32(inp.w2[e]),
+                                            P.np32(g.d_out[rr_d]))
+        got.append(P.np32(g.dx_rows[rr_d]))
+        want.append(dX)
+    err = P.rel_err(np.concatenate(got), np.concatenate(want))
+    print("  dx_rows rel err %.3e on %d rows" % (err, len(rows)), flush=True)
+    assert err <= BWD_TOL
+
+    # Weight gradients: rows f of dw1 / dw3 and columns f of dw2 for a few experts.
+    live = np.nonzero(counts > 0)[0]
+    experts = sorted(set([int(live[np.argmax(counts[live])]), int(live[np.argmin(counts[live])]),
+                          int(rng.choice(live))]))
+    fs = np.sort(rng.choice(cfg.d_ff, size=6, replace=False))
+    fs_d = torch.as_tensor(fs, device="cuda")
+    for e in experts:
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        tok = torch.as_tensor(perm[lo:hi] // k, device="cuda")
+        _, w1s, w3s, w2s = O.swiglu_ffn_backward(
+            P.np32(inp.x[tok]), P.np32(inp.w1[e][fs_d]), P.np32(inp.w3[e][fs_d]),
+            P.np32(inp.w2[e][:, fs_d]), P.np32(g.d_out[lo:hi]))
+        errs = (P.rel_err(P.np32(g.dw1[e][fs_d]), w1s), P.rel_err(P.np32(g.dw3[e][fs_d]), w3s),
+                P.rel_err(P.np32(g.dw2[e][:, fs_d]), w2s))
+        print("  expert %d (%d rows): dw1 %.2e dw3 %.2e dw2 %.2e" % ((e, hi - lo) + errs),
+              flush=True)
+        assert max(errs) <= BWD_TOL
+    empty = np.nonzero(counts == 0)[0]
+    if len(empty):
+        ed = torch.as_tensor(empty, device="cuda")
+        for t in (g.dw1, g.dw3, g.dw2):
+            assert bool((t[ed] == 0).all())
