@@ -35,6 +35,7 @@
 
 #include <algorithm>
 #include <climits>
+#include <mutex>
 #include <type_traits>
 
 namespace moe {
@@ -946,6 +947,41 @@ static int device_cus() {
   return cus[dev] > 0 ? cus[dev] : 0;
 }
 
+// A second stream per device for work that runs beside the caller's stream (created on first use,
+// default priority), and the two events that fork it from and join it back to the caller's stream.
+struct SideStream {
+  hipStream_t stream = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+  bool failed = false;
+};
+static std::mutex g_side_mutex;
+static SideStream g_side[64];
+
+// Queues side(side_stream) after the work already queued on s, then main(s), then makes s wait for
+// the side work.  Returns false (queueing nothing) when no side stream could be made.
+template <typename FS, typename FM>
+static bool run_beside(hipStream_t s, FS&& side, FM&& main, hipError_t& err) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return false;
+  std::lock_guard<std::mutex> lock(g_side_mutex);
+  SideStream& ss = g_side[dev];
+  if (!ss.stream && !ss.failed) {
+    if (hipStreamCreateWithFlags(&ss.stream, hipStreamNonBlocking) != hipSuccess ||
+        hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&ss.join, hipEventDisableTiming) != hipSuccess)
+      ss.failed = true;
+  }
+  if (ss.failed) return false;
+  if ((err = hipEventRecord(ss.fork, s)) != hipSuccess) return true;
+  if ((err = hipStreamWaitEvent(ss.stream, ss.fork, 0)) != hipSuccess) return true;
+  err = side(ss.stream);
+  const hipError_t e1 = hipEventRecord(ss.join, ss.stream);
+  const hipError_t e2 = main(s);
+  const hipError_t e3 = hipStreamWaitEvent(s, ss.join, 0);
+  if (err == hipSuccess) err = e1 != hipSuccess ? e1 : (e2 != hipSuccess ? e2 : e3);
+  return true;
+}
+
 template <int BM, int BN, int NMAT, int WGM, int WGN, int BK, int NST, int MINB, int EPI, bool TAIL,
           bool BT = false>
 static hipError_t launch_t(const GemmParams& p, int rows_max, hipStream_t s) {
@@ -1066,6 +1102,27 @@ size_t gemm_bf16_partial_bytes(int rows_max, int G, bool grouped, int N, int K, 
   return (size_t)device_cus() * minb * nmat * BM * BN * sizeof(float);
 }
 
+// The tile configuration of each epilogue: 256-row tiles (8 waves, one block per CU) or 128-row
+// tiles (4 waves, two blocks per CU).
+static hipError_t launch_cfg(const GemmParams& p, int rows_max, int epi, bool big, hipStream_t s) {
+  switch (epi) {
+    case EPI_SWIGLU:
+      return big ? launch_tail_or_not<256, 128, 2, 4, 2, 64, 2, 1, EPI_SWIGLU>(p, rows_max, s)
+                 : launch_tail_or_not<128, 128, 2, 2, 2, 32, 3, 2, EPI_SWIGLU>(p, rows_max, s);
+    case EPI_STORE:
+      if (p.bt)
+        return big ? launch_tail_or_not<256, 256, 1, 2, 4, 64, 2, 1, EPI_STORE, true>(p, rows_max, s)
+                   : launch_tail_or_not<128, 256, 1, 2, 2, 32, 3, 2, EPI_STORE, true>(p, rows_max, s);
+      return big ? launch_tail_or_not<256, 256, 1, 4, 2, 64, 2, 1, EPI_STORE>(p, rows_max, s)
+                 : launch_tail_or_not<128, 256, 1, 2, 2, 32, 3, 2, EPI_STORE>(p, rows_max, s);
+    case EPI_SWIGLU_BWD:
+      return big ? launch_tail_or_not<256, 128, 2, 4, 2, 64, 2, 1, EPI_SWIGLU_BWD>(p, rows_max, s)
+                 : launch_tail_or_not<128, 128, 2, 2, 2, 32, 3, 2, EPI_SWIGLU_BWD>(p, rows_max, s);
+    default:
+      return launch_tail_or_not<128, 256, 1, 2, 2, 32, 0, 1, EPI_STORE_F32_BIAS>(p, rows_max, s);
+  }
+}
+
 // Needs K (and the row strides) a multiple of 8 (16-byte rows) and every operand under 2 GiB
 // (32-bit buffer offsets).
 hipError_t launch_gemm_bf16(const GemmParams& p_in, int rows_max, int epi, hipStream_t s) {
@@ -1096,25 +1153,31 @@ hipError_t launch_gemm_bf16(const GemmParams& p_in, int rows_max, int epi, hipSt
   if (p.ksplit > 1 && p.part == nullptr) p.ksplit = 1;   // no scratch given: no split
   const bool big = use_big_tiles(rows_max, p.G, grouped, epi);
   hipError_t e;
-  switch (epi) {
-    case EPI_SWIGLU:
-      e = big ? launch_tail_or_not<256, 128, 2, 4, 2, 64, 2, 1, EPI_SWIGLU>(p, rows_max, s)
-              : launch_tail_or_not<128, 128, 2, 2, 2, 32, 3, 2, EPI_SWIGLU>(p, rows_max, s);
-      break;
-    case EPI_STORE:
-      if (p.bt)
-        e = big ? launch_tail_or_not<256, 256, 1, 2, 4, 64, 2, 1, EPI_STORE, true>(p, rows_max, s)
-                : launch_tail_or_not<128, 256, 1, 2, 2, 32, 3, 2, EPI_STORE, true>(p, rows_max, s);
-      else
-        e = big ? launch_tail_or_not<256, 256, 1, 4, 2, 64, 2, 1, EPI_STORE>(p, rows_max, s)
-                : launch_tail_or_not<128, 256, 1, 2, 2, 32, 3, 2, EPI_STORE>(p, rows_max, s);
-      break;
-    case EPI_SWIGLU_BWD:
-      e = big ? launch_tail_or_not<256, 128, 2, 4, 2, 64, 2, 1, EPI_SWIGLU_BWD>(p, rows_max, s)
-              : launch_tail_or_not<128, 128, 2, 2, 2, 32, 3, 2, EPI_SWIGLU_BWD>(p, rows_max, s);
-      break;
-    default:
-      e = launch_tail_or_not<128, 256, 1, 2, 2, 32, 0, 1, EPI_STORE_F32_BIAS>(p, rows_max, s);
+  if (big && grouped && p.ksplit == 1 && epi != EPI_STORE_F32_BIAS &&
+      (long long)rows_max < 512ll * p.G) {
+    // Groups of a few hundred rows on average (fine-grained experts, skewed routing): the rows of
+    // every group that fill whole 256-row tiles run in 256-row tiles, the rest (under 256 rows
+    // per group) in 128-row tiles, two blocks per CU, where a short group wastes less.  The short
+    // tiles of the many small groups are bound by streaming those experts' weights, the tall ones
+    // by the matrix cores, so the two launches run side by side on two streams.  Only the tall
+    // launch splits its last round over K (the scratch is not shared).
+    GemmParams p1 = p, p2 = p;
+    p1.row_split = p2.row_split = 256;
+    p1.part_mode = 1;
+    p2.part_mode = 2;
+    p2.part = nullptr;
+    // At most two 128-row tiles per group: the grid bound of 128 G rows covers them.
+    const int rows2 = (int)std::min<long long>(rows_max, 128ll * p.G);
+    e = hipSuccess;
+    const bool beside = run_beside(
+        s, [&](hipStream_t side) { return launch_cfg(p2, rows2, epi, false, side); },
+        [&](hipStream_t main) { return launch_cfg(p1, rows_max, epi, true, main); }, e);
+    if (!beside) {
+      if ((e = launch_cfg(p1, rows_max, epi, true, s)) != hipSuccess) return e;
+      e = launch_cfg(p2, rows2, epi, false, s);
+    }
+  } else {
+    e = launch_cfg(p, rows_max, epi, big, s);
   }
   if (e != hipSuccess) return e;
   if (p.ksplit > 1) launch_splitk_finish(p, rows_max, epi, s);

@@ -51,6 +51,11 @@ struct GemmParams {
   // k - bt_k1 of B1 (two matrices stacked along K).
   int bt;
   int bt_k1;
+  // Row parts of a grouped product run as two launches (part 1 in tall tiles, part 2 in short
+  // ones): part_mode 1 takes the first floor(n_g / row_split) * row_split rows of every group,
+  // part_mode 2 the rest; 0 takes all rows.
+  int row_split;
+  int part_mode;
 };
 
 enum { EPI_SWIGLU = 0, EPI_STORE = 1, EPI_STORE_F32_BIAS = 2, EPI_SWIGLU_BWD = 3 };
@@ -80,6 +85,16 @@ struct TileScan {
   int incl;     // tiles up to and including this lane's groups
 };
 
+// Rows [rs, re) of group g that this launch covers.
+__device__ __forceinline__ void group_range(const GemmParams& p, int g, int& rs, int& re) {
+  rs = p.offsets[g];
+  re = p.offsets[g + 1];
+  if (p.part_mode != 0) {
+    const int cut = rs + (re - rs) / p.row_split * p.row_split;
+    if (p.part_mode == 1) re = cut; else rs = cut;
+  }
+}
+
 template <int BM>
 __device__ __forceinline__ TileScan scan_tiles(const GemmParams& p, int NT) {
   TileScan s;
@@ -94,8 +109,9 @@ __device__ __forceinline__ TileScan scan_tiles(const GemmParams& p, int NT) {
   s.g1 = min(p.G, s.g0 + per);
   int mine = 0;
   for (int g = s.g0; g < s.g1; ++g) {
-    const int n = p.offsets[g + 1] - p.offsets[g];
-    mine += ((n + BM - 1) / BM) * NT;
+    int rs, re;
+    group_range(p, g, rs, re);
+    mine += ((re - rs + BM - 1) / BM) * NT;
   }
   int incl = mine;
 #pragma unroll
@@ -129,8 +145,9 @@ __device__ __forceinline__ void tile_at(const GemmParams& p, int NT, const TileS
   if (lane == owner) {
     base = excl;
     for (int g = s.g0; g < s.g1; ++g) {
-      const int n = p.offsets[g + 1] - p.offsets[g];
-      const int c = ((n + BM - 1) / BM) * NT;
+      int rs, re;
+      group_range(p, g, rs, re);
+      const int c = ((re - rs + BM - 1) / BM) * NT;
       if (t < base + c) {
         g_found = g;
         break;
@@ -140,7 +157,8 @@ __device__ __forceinline__ void tile_at(const GemmParams& p, int NT, const TileS
   }
   g_found = __shfl(g_found, owner, 64);
   base = __shfl(base, owner, 64);
-  const int rs = p.offsets[g_found], re = p.offsets[g_found + 1];
+  int rs, re;
+  group_range(p, g_found, rs, re);
   const int tm = (re - rs + BM - 1) / BM;
   const int local = t - base;
   tc.g = g_found;

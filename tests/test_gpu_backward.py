@@ -138,6 +138,9 @@ CASES = [
     (20, 64, 16, 1, 64, "softmax_topk", 0, 0, 1.5),
     (1030, 512, 8, 2, 1024, "softmax_topk", 0, 0, 0.0),
     (2048, 256, 4, 1, 512, "softmax_topk", 0, 1, 0.0),
+    # 256 to 512 rows per expert: 256-row tiles for whole blocks, 128-row tiles for the rest
+    (700, 256, 4, 2, 512, "softmax_topk", 0, 0, 1.1),
+    (1500, 128, 8, 2, 320, "sigmoid_topk", 0, 1, 1.3),
 ]
 
 

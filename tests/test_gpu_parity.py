@@ -219,6 +219,10 @@ SWEEP = [
     # more tiles than one round of blocks: whole rounds plus a K-split last round
     (2048, 512, 8, 2, 2048, "bf16", "softmax_topk", 0, 0, 0.0),
     (2048, 256, 64, 2, 1024, "bf16", "sigmoid_topk", 0, 0, 0.0),
+    # 256 to 512 rows per expert on average: whole 256-row blocks, then the rest in 128-row tiles
+    (700, 256, 4, 2, 512, "bf16", "softmax_topk", 0, 0, 1.1),
+    (1500, 128, 8, 2, 320, "bf16", "sigmoid_topk", 0, 1, 1.3),
+    (300, 136, 2, 2, 264, "bf16", "softmax_all", 0, 0, 0.0),
 ]
 
 
