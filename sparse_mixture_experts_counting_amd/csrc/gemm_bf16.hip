@@ -162,7 +162,7 @@ __device__ __forceinline__ TailPlan tail_plan(int total, int slots, int K) {
 }
 
 template <int BM, int BN, int NMAT, int WGM, int WGN, int BK, int NST, int MINB, int EPI, bool TAIL,
-          bool BT = false>
+          bool BT = false, bool AT = false>
 __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_bf16_kernel(const GemmParams p) {
   constexpr int NTHR = 64 * WGM * WGN;
   constexpr int WM = BM / WGM, WN = BN / WGN;       // WGM x WGN waves
@@ -194,8 +194,13 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_bf16_kernel(const G
                          BN % (DROWS * NW) == 0), "direct loads split evenly");
   // Transposed B: a stage's B block is BK rows of RBT bytes; one direct load fills RPB rows.
   constexpr int RBT = BN * 2, UPB = RBT / 16, RPB = 1024 / RBT;
-  static_assert(!BT || (DMA && NMAT == 1 && BN == 256 && EPI == EPI_STORE && BK * RBT == BN * RB),
+  static_assert(!BT || (DMA && NMAT == 1 && BN == 256 && (EPI == EPI_STORE || AT) &&
+                        BK * RBT == BN * RB),
                 "transposed B: direct loads, one 256-column matrix, bf16 output");
+  // Transposed A (with transposed B: the weight gradients, both operands row-major activations
+  // reduced over their rows): a stage's A block is BK rows of RAT bytes.
+  constexpr int RAT = BM * 2, UPA = RAT / 16, RPA = 1024 / RAT;
+  static_assert(!AT || (BT && BM == 256 && EPI == EPI_STORE_F32_BIAS), "transposed A");
 
   extern __shared__ __align__(16) uint8_t smem[];
 
@@ -231,7 +236,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_bf16_kernel(const G
     tc.row_end = p.M;
     tc.n_tile = in / gm;
     const int o0 = p.offsets[tc.g];
-    kg_beg = __builtin_amdgcn_readfirstlane(kpad(o0, tc.g));
+    kg_beg = __builtin_amdgcn_readfirstlane(o0);
     kg_len = __builtin_amdgcn_readfirstlane(p.offsets[tc.g + 1] - o0);
   } else if (p.ksplit > 1) {                // every tile split over K
     const TileScan ts = scan_tiles<BM>(p, NT);
@@ -327,9 +332,16 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_bf16_kernel(const G
       const int uu = (lane % UPR) ^ swz<BK>(srow);
       d_kmax[j] = 0;   // set below, once the K range is known
       if (j < DPW_A) {
-        const int grow = min(tc.row0 + srow, tc.row_end - 1);
-        const int src = p.gather ? p.gather[grow] / p.gather_div : grow;
-        d_voff[j] = ((uint32_t)src * (uint32_t)lda + 8u * uu) * 2u;
+        if constexpr (AT) {   // row kr of the stage's A block (a K row), columns m
+          const int kr = (wave + NW * j) * RPA + lane / UPA;
+          const int ua = (lane % UPA) ^ swzT(kr);
+          const int m = min(tc.row0 + 8 * ua, tc.row_end - 8);
+          d_voff[j] = ((uint32_t)kr * (uint32_t)lda + (uint32_t)m) * 2u;
+        } else {
+          const int grow = min(tc.row0 + srow, tc.row_end - 1);
+          const int src = p.gather ? p.gather[grow] / p.gather_div : grow;
+          d_voff[j] = ((uint32_t)src * (uint32_t)lda + 8u * uu) * 2u;
+        }
       } else if constexpr (BT) {
         // Row kr of the stage's B block (a K row), physical unit lane % UPB.
         const int kr = (wave + NW * (j - DPW_A)) * RPB + lane / UPB;
@@ -362,6 +374,13 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_bf16_kernel(const G
           const int kr = (wave + NW * (j - DPW_A)) * RPB + lane / UPB;
           const int ub = (lane % UPB) ^ swzT(kr);
           d_kmax[j] = n_base + 8 * ub < N ? kend - kr : INT_MIN;
+        }
+      }
+      if constexpr (AT) {
+        if (j < DPW_A) {    // likewise for A: its 8 columns below the row count M
+          const int kr = (wave + NW * j) * RPA + lane / UPA;
+          const int ua = (lane % UPA) ^ swzT(kr);
+          d_kmax[j] = tc.row0 + 8 * ua < tc.row_end ? kend - kr : INT_MIN;
         }
       }
     }
@@ -401,6 +420,9 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_bf16_kernel(const G
           second = p.bt_k1 > 0 && k0 >= p.bt_k1;
           step_off = (uint32_t)(second ? k0 - p.bt_k1 : k0) * (uint32_t)ldb_t * 2u;
         }
+      }
+      if constexpr (AT) {
+        if (is_a) step_off = (uint32_t)k0 * (uint32_t)lda * 2u;
       }
       const uint32_t voff = k0 < d_kmax[j] ? d_voff[j] + step_off : (is_a ? a_bytes : b_bytes);
       if constexpr (BT) {
@@ -467,10 +489,32 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_bf16_kernel(const G
       bt_rd[j] = B_OFF + r * RBT + (((n >> 3) ^ swzT(r)) << 4) + (n & 7) * 2;
     }
   }
-  auto read_frags2 = [&](int a_off, int b_off, int ks, int buf) {
+  int at_rd[AT ? TM : 1];
+  if constexpr (AT) {   // the same lane pattern over the A block's rows and M columns
+    const int g16 = lane >> 4, s16 = lane & 15, qa = s16 >> 2, aa = s16 & 3;
+    const int kh = g16 >> 1, nh = g16 & 1;
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
-      af[buf][i] = *(const lds_bf16x8_t*)(smem + a_off + a_rd[ks] + i * 32 * RB);
+    for (int i = 0; i < TM; ++i) {
+      const int m = wm0 + 32 * i + 16 * nh + 4 * aa;
+      const int r = 8 * kh + qa;
+      at_rd[i] = r * RAT + (((m >> 3) ^ swzT(r)) << 4) + (m & 7) * 2;
+    }
+  }
+  auto read_frags2 = [&](int a_off, int b_off, int ks, int buf) {
+    if constexpr (AT) {
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const uint8_t* ap = smem + a_off + at_rd[i] + ks * 16 * RAT;
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)ap);
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(ap + 4 * RAT));
+        const i16x8 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        af[buf][i] = __builtin_bit_cast(bf16x8, both);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+        af[buf][i] = *(const lds_bf16x8_t*)(smem + a_off + a_rd[ks] + i * 32 * RB);
+    }
     if constexpr (BT) {
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
@@ -983,9 +1027,9 @@ static bool run_beside(hipStream_t s, FS&& side, FM&& main, hipError_t& err) {
 }
 
 template <int BM, int BN, int NMAT, int WGM, int WGN, int BK, int NST, int MINB, int EPI, bool TAIL,
-          bool BT = false>
+          bool BT = false, bool AT = false>
 static hipError_t launch_t(const GemmParams& p, int rows_max, hipStream_t s) {
-  auto kern = gemm_bf16_kernel<BM, BN, NMAT, WGM, WGN, BK, NST, MINB, EPI, TAIL, BT>;
+  auto kern = gemm_bf16_kernel<BM, BN, NMAT, WGM, WGN, BK, NST, MINB, EPI, TAIL, BT, AT>;
   const size_t lds = (size_t)lds_bytes<BM, BN, NMAT, BK, NST, MINB>();
   static bool attr_set = false;
   if (!attr_set) {
@@ -1128,24 +1172,32 @@ static hipError_t launch_cfg(const GemmParams& p, int rows_max, int epi, bool bi
 hipError_t launch_gemm_bf16(const GemmParams& p_in, int rows_max, int epi, hipStream_t s) {
   const int lda = p_in.lda ? p_in.lda : p_in.K;
   const int ldb = p_in.ldb ? p_in.ldb : (p_in.bt ? p_in.N : p_in.K);
-  if (p_in.K % 8 != 0 || lda % 8 != 0 || ldb % 8 != 0 || p_in.N < 1 || p_in.K < 8)
+  // (With transposed A and B, K counts rows of both: any count.)
+  if ((!p_in.at && p_in.K % 8 != 0) || lda % 8 != 0 || ldb % 8 != 0 || p_in.N < 1 ||
+      p_in.K < (p_in.at ? 1 : 8))
     return hipErrorNotSupported;
   const long long b_rows = p_in.bt ? (p_in.bt_k1 > 0 ? p_in.bt_k1 : p_in.K) : p_in.N;
   if ((long long)p_in.a_rows * lda * 2 >= (1ll << 31) || b_rows * ldb * 2 >= (1ll << 31))
     return hipErrorNotSupported;
-  if (p_in.bt) {
+  if (p_in.at && !(p_in.bt && p_in.kgrouped)) return hipErrorNotSupported;
+  if (p_in.bt && p_in.kgrouped) {
+    // Weight gradients from row-major operands: A [K][M], B [K][N], M and N multiples of 8.
+    if (!p_in.at || epi != EPI_STORE_F32_BIAS || p_in.N % 8 != 0 || p_in.M % 8 != 0 ||
+        ldb < p_in.N || lda < p_in.M || p_in.bt_k1 != 0)
+      return hipErrorNotSupported;
+  } else if (p_in.bt) {
     // Transposed B: bf16 output, N a multiple of 8, the stacked matrices split on a 64-deep step.
-    if (epi != EPI_STORE || p_in.kgrouped || p_in.N % 8 != 0 || ldb < p_in.N ||
+    if (epi != EPI_STORE || p_in.N % 8 != 0 || ldb < p_in.N ||
         (p_in.bt_k1 > 0 && (p_in.bt_k1 % 64 != 0 || p_in.bt_k1 >= p_in.K)))
       return hipErrorNotSupported;
   }
   GemmParams p = p_in;
   const bool grouped = p.offsets != nullptr;
   if (p.kgrouped) {             // weight gradients: fp32 out, 256 x 256 tiles, no split
-    if (!grouped || epi != EPI_STORE_F32_BIAS || p.gather) return hipErrorNotSupported;
+    if (!grouped || epi != EPI_STORE_F32_BIAS || p.gather || !p.at) return hipErrorNotSupported;
     p.ksplit = 1;
     p.part = nullptr;
-    return launch_t<256, 256, 1, 4, 2, 64, 2, 1, EPI_STORE_F32_BIAS, false>(p, 0, s);
+    return launch_t<256, 256, 1, 4, 2, 64, 2, 1, EPI_STORE_F32_BIAS, false, true, true>(p, 0, s);
   }
   if (epi == EPI_SWIGLU_BWD) p.part = nullptr;   // its epilogue runs on whole sums only
   p.ksplit = splitk_factor(rows_max, p.G, grouped, p.N, p.K, epi);

@@ -34,10 +34,10 @@ struct GemmParams {
   int slots;                // blocks resident at once; > 0 enables splitting the last partial
                             // round of tiles over K (set by the launcher)
   int lda, ldb;             // row strides of A and B in elements (0: K)
-  // K-grouped mode (kgrouped = 1): the groups split the reduction instead of the rows.  Group g
-  // reduces over columns [kpad(g), kpad(g) + offsets[g+1] - offsets[g]) of A [M][lda] and
-  // B [N][ldb] (kpad as below) and writes its own C at C + g * c_gstride; every group has all M
-  // rows.  No gather, no split.
+  // K-grouped mode (kgrouped = 1, with at = bt = 1): the groups split the reduction instead of
+  // the rows.  Group g reduces over rows offsets[g] .. offsets[g+1] - 1 of A [K][lda] (M columns)
+  // and B [K][ldb] (N columns) and writes its own C at C + g * c_gstride; every group has all M
+  // output rows.  No gather, no split.
   int kgrouped;
   long long c_gstride;
   // SwiGLU-backward epilogue (EPI_SWIGLU_BWD, two matrices: a = A B0^T, b = A B1^T): reads
@@ -51,6 +51,8 @@ struct GemmParams {
   // k - bt_k1 of B1 (two matrices stacked along K).
   int bt;
   int bt_k1;
+  // Transposed A (at != 0, K-grouped only, with bt): A is stored [K][M] (row stride lda).
+  int at;
   // Row parts of a grouped product run as two launches (part 1 in tall tiles, part 2 in short
   // ones): part_mode 1 takes the first floor(n_g / row_split) * row_split rows of every group,
   // part_mode 2 the rest; 0 takes all rows.
@@ -59,14 +61,6 @@ struct GemmParams {
 };
 
 enum { EPI_SWIGLU = 0, EPI_STORE = 1, EPI_STORE_F32_BIAS = 2, EPI_SWIGLU_BWD = 3 };
-
-// Padded start of group g's columns in a K-grouped operand: each group starts on a multiple of 64
-// columns, so every 64-deep step of a row is one aligned 128-byte line (a step that straddles two
-// lines costs twice the cache requests), and the layout depends on offsets[g] alone.  The padded
-// width of G groups holding R rows is kpad(R, G).
-__host__ __device__ __forceinline__ int kpad(int row_offset, int g) {
-  return ((row_offset + 63) & ~63) + 64 * g;
-}
 
 struct TileCoord {
   int g;        // group

@@ -54,9 +54,8 @@ void launch_transpose_ld(const void* src, int batch, int rows, int cols, int ele
                          void* dst, int ldd, long long dst_bstride, hipStream_t s);
 void launch_transpose16(const void* src, int batch, int rows, int cols, void* dst, int ldd,
                         long long dst_bstride, hipStream_t s);
-void launch_transpose_grouped(const void* src, int src_rows, const int32_t* gather,
-                              int gather_div, const int32_t* offsets, int G, int rows_max,
-                              int cols, void* dst, int ldd, hipStream_t s);
+void launch_gather_rows(const void* src, int cols, const int32_t* gather, int gather_div,
+                        const int32_t* offsets, int G, int rows_max, void* dst, hipStream_t s);
 
 // backward.hip
 void launch_combine_backward(const void* dy, const void* out, const int32_t* inv,

@@ -52,14 +52,12 @@ size_t ffn_workspace_bytes(int rows, bool grouped, int G, int d, int d_ff, moe_d
 bool bwd_weights_in_place(int d_ff) { return d_ff % 64 == 0; }
 
 // moe_expert_backward workspace (bf16): the transposed weights (only without in-place weights),
-// the row-major intermediates, the group-padded transposed operands of the weight-gradient
-// products, two ints of dense offsets and the split-K scratch of the input-gradient products, in
-// this order.
+// the row-major intermediates, the expert-ordered copy of the token rows (grouped only), two ints
+// of dense offsets and the split-K scratch of the input-gradient products, in this order.
 struct BwdLayout {
-  size_t w2t, w13t, dh, h, dab, doT, hT, dabT, xgT, offs, part, total;
+  size_t w2t, w13t, dh, h, dab, xg, offs, part, total;
 };
 BwdLayout bwd_layout(int rows, bool grouped, int G, int d, int d_ff) {
-  const size_t P = (size_t)moe::kpad(rows, G);
   BwdLayout L;
   size_t o = 0;
   auto take = [&](size_t bytes) { const size_t at = o; o += align_up(bytes); return at; };
@@ -69,10 +67,7 @@ BwdLayout bwd_layout(int rows, bool grouped, int G, int d, int d_ff) {
   L.dh = take((size_t)rows * d_ff * 2);
   L.h = take((size_t)rows * d_ff * 2);
   L.dab = take((size_t)rows * 2 * d_ff * 2);
-  L.doT = take((size_t)d * P * 2);
-  L.hT = take((size_t)d_ff * P * 2);
-  L.dabT = take((size_t)2 * d_ff * P * 2);
-  L.xgT = take((size_t)d * P * 2);
+  L.xg = take(grouped ? (size_t)rows * d * 2 : 0);
   L.offs = take(16);
   const size_t p1 = moe::gemm_bf16_partial_bytes(rows, G, grouped, d_ff, d, moe::EPI_STORE);
   const size_t p2 = moe::gemm_bf16_partial_bytes(rows, G, grouped, d, 2 * d_ff, moe::EPI_STORE);
@@ -526,17 +521,16 @@ moe_status moe_expert_backward(const void* x, const int32_t* perm, const int32_t
   if (dt != MOE_BF16) return MOE_ERR_UNSUPPORTED;
   const int G = grouped ? E : 1;
   const int rows = grouped ? T * k : T;
-  const int P = moe::kpad(rows, G);
   // 32-bit element offsets inside one operand (the GEMMs offset each group's weights in 64 bits)
-  if (!fits_i32((long long)rows * 2 * d_ff) || !fits_i32((long long)2 * d_ff * P) ||
-      !fits_i32((long long)d * P) || !fits_i32((long long)d * 2 * d_ff))
+  if (!fits_i32((long long)rows * 2 * d_ff) || !fits_i32((long long)rows * d) ||
+      !fits_i32((long long)d * 2 * d_ff))
     return MOE_ERR_UNSUPPORTED;
   const BwdLayout L = bwd_layout(rows, grouped, G, d, d_ff);
   if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
   hipStream_t s = (hipStream_t)stream;
   char* ws = (char*)workspace;
   void *w2t = ws + L.w2t, *w13t = ws + L.w13t, *dh = ws + L.dh, *h = ws + L.h, *dab = ws + L.dab;
-  void *doT = ws + L.doT, *hT = ws + L.hT, *dabT = ws + L.dabT, *xgT = ws + L.xgT;
+  void* xg = ws + L.xg;
   int32_t* offs = grouped ? (int32_t*)offsets : (int32_t*)(ws + L.offs);
   float* part = (float*)(ws + L.part);
   if (!grouped) moe::launch_dense_offsets(offs, T, s);
@@ -587,22 +581,24 @@ moe_status moe_expert_backward(const void* x, const int32_t* perm, const int32_t
     q.C = dx_rows; q.ldc = d; q.part = part;
     if ((e = moe::launch_gemm_bf16(q, rows, moe::EPI_STORE, s)) != hipSuccess) return MOE_ERR_DEVICE;
   }
-  // Operands of the weight gradients, reduced over each expert's rows.
-  const int32_t* toffs = grouped ? offsets : nullptr;
-  moe::launch_transpose_grouped(d_out, rows, nullptr, 1, toffs, G, rows, d, doT, P, s);
-  moe::launch_transpose_grouped(h, rows, nullptr, 1, toffs, G, rows, d_ff, hT, P, s);
-  moe::launch_transpose_grouped(dab, rows, nullptr, 1, toffs, G, rows, 2 * d_ff, dabT, P, s);
-  moe::launch_transpose_grouped(x, T, perm, k, toffs, G, rows, d, xgT, P, s);
-  struct WG { const void* A; int M; const void* B; int N; float* C; };
-  const WG wg[3] = {{doT, d, hT, d_ff, dw2},                                   // dw2 = d_out^T h
-                    {dabT, d_ff, xgT, d, dw1},                                 // dw1 = da^T x
-                    {(uint16_t*)dabT + (size_t)d_ff * P, d_ff, xgT, d, dw3}};  // dw3 = db^T x
+  // Weight gradients, reduced over each expert's rows of row-major operands (the GEMM reads both
+  // transposed): dw2 = d_out^T h, dw1 = da^T x_e, dw3 = db^T x_e, with x_e the expert-ordered
+  // token rows (gathered once; in dense mode x itself).
+  const void* xe = x;
+  if (grouped) {
+    moe::launch_gather_rows(x, d, perm, k, offsets, G, rows, xg, s);
+    xe = xg;
+  }
+  struct WG { const void* A; int M; int lda; const void* B; int N; float* C; };
+  const WG wg[3] = {{d_out, d, d, h, d_ff, dw2},
+                    {dab, d_ff, 2 * d_ff, xe, d, dw1},
+                    {(const uint16_t*)dab + d_ff, d_ff, 2 * d_ff, xe, d, dw3}};
   for (const WG& w : wg) {
     moe::GemmParams q{};
-    q.A = w.A; q.a_rows = w.M; q.lda = P; q.gather_div = 1;
-    q.offsets = offs; q.G = G; q.M = w.M; q.N = w.N; q.K = P;
-    q.B0 = w.B; q.ldb = P; q.C = w.C; q.ldc = w.N;
-    q.kgrouped = 1; q.c_gstride = (long long)w.M * w.N;
+    q.A = w.A; q.a_rows = rows; q.lda = w.lda; q.gather_div = 1;
+    q.offsets = offs; q.G = G; q.M = w.M; q.N = w.N; q.K = rows;
+    q.B0 = w.B; q.ldb = w.N; q.C = w.C; q.ldc = w.N;
+    q.kgrouped = 1; q.at = 1; q.bt = 1; q.c_gstride = (long long)w.M * w.N;
     if ((e = moe::launch_gemm_bf16(q, rows, moe::EPI_STORE_F32_BIAS, s)) != hipSuccess)
       return MOE_ERR_DEVICE;
   }
