@@ -67,9 +67,10 @@ __device__ __forceinline__ desc_t make_desc(const void* base, uint32_t num_recor
 // One wave-wide 16-byte direct-to-LDS load (lane l to byte lds + 16 l), issued where the compiler
 // does not see it: the transposing LDS reads would otherwise make it wait for every such load in
 // flight (it cannot tell the stages apart) before each of them.  No register is written; the
-// loads are waited for by the explicit vmcnt waits of the main loop.
+// loads are waited for by the explicit vmcnt waits of the main loop.  The load reads M0, which
+// needs one wait state after the scalar write (the compiler inserts it for its own loads).
 __device__ __forceinline__ void dma16(desc_t desc, uint32_t voff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
                :
                : "v"(voff), "s"(desc), "s"(lds)
                : "memory", "m0");
