@@ -1151,9 +1151,9 @@ size_t gemm_bf16_partial_bytes(int rows_max, int G, bool grouped, int N, int K, 
 // tiles (4 waves, two blocks per CU).
 static hipError_t launch_cfg(const GemmParams& p, int rows_max, int epi, bool big, hipStream_t s) {
   switch (epi) {
-    case EPI_SWIGLU:
+    case EPI_SWIGLU:   // short tiles: 64-deep steps (128-byte runs per weight row), one block per CU
       return big ? launch_tail_or_not<256, 128, 2, 4, 2, 64, 2, 1, EPI_SWIGLU>(p, rows_max, s)
-                 : launch_tail_or_not<128, 128, 2, 2, 2, 32, 3, 2, EPI_SWIGLU>(p, rows_max, s);
+                 : launch_tail_or_not<128, 128, 2, 2, 2, 64, 3, 1, EPI_SWIGLU>(p, rows_max, s);
     case EPI_STORE:
       if (p.bt)
         return big ? launch_tail_or_not<256, 256, 1, 2, 4, 64, 2, 1, EPI_STORE, true>(p, rows_max, s)
