@@ -23,6 +23,7 @@
 
 #include <algorithm>
 #include <climits>
+#include <type_traits>
 
 namespace moe {
 
@@ -49,6 +50,14 @@ template <int NMAT, int BITS> constexpr int q_lds() {
 __device__ __forceinline__ int qswz8(int r) { return (r ^ ((r >> 3) & 3)) & 7; }
 __device__ __forceinline__ int qswz16(int r) { return r & 15; }
 __device__ __forceinline__ int qswz4(int r) { return ((r >> 2) ^ (r >> 1)) & 3; }
+
+// Workgroup barrier without the memory fence of __syncthreads: the fence would also wait for the
+// direct loads still in flight for later stages (each wave waits explicitly for the stage it needs).
+__device__ __forceinline__ void q_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
 
 template <int VM>
 constexpr int q_wait() {                                  // s_waitcnt vmcnt(VM) lgkmcnt(0)
@@ -174,36 +183,72 @@ __global__ __launch_bounds__(256, 2) void gemm_q_kernel(const GemmParams p, cons
                                                16, (int)off_, 0, 0, 0);                       \
     }                                                                                         \
   } while (0)
+  // Operand reads of slice ks of a stage: the activation fragment (shared by both matrices) and
+  // each matrix's 8 packed weights of this lane's row.
+  typedef typename std::conditional<BITS == 8, qu32x2, uint32_t>::type wpack_t;
+  auto read_a = [&](const uint8_t* sa, int ks) {
+    return *(const qlds_bf16x8_t*)(sa + a_row_off + (((2 * ks + h) ^ swa) << 4));
+  };
+  auto read_w = [&](const uint8_t* sb, int m, int ks) {
+    const int br = m * kQBN + brow0;
+    if constexpr (BITS == 8)
+      return *(const qlds_u32x2_t*)(sb + br * 64 + ((ks ^ qswz4(br)) << 4) + 8 * h);
+    else
+      return *(const qlds_u32_t*)(sb + br * 64 + (((ks >> 1) ^ qswz4(br)) << 4) + 8 * (ks & 1) +
+                                  4 * h);
+  };
+  auto widen = [&](wpack_t w) {
+    if constexpr (BITS == 8)
+      return widen8_i8(w[0], w[1]);
+    else
+      return widen8_i4(w);
+  };
 #pragma unroll
   for (int s = 0; s < NST - 1; ++s) MOE_Q_ISSUE(s, s);
   __builtin_amdgcn_s_waitcnt(q_wait<DPW * (NST - 2)>());
-  __syncthreads();
+  q_barrier();
+  // Software pipeline: the reads of slice ks + 1 go out before slice ks is widened and multiplied;
+  // the last slice of a stage is multiplied after the barrier, behind the next stage's first reads.
+  bf16x8 a_c = read_a(smem, 0);
+  wpack_t w_c[NMAT];
+#pragma unroll
+  for (int m = 0; m < NMAT; ++m) w_c[m] = read_w(smem + NA * 1024, m, 0);
   int st = 0;
   for (int kt = 0; kt < KT; ++kt) {
     MOE_Q_ISSUE(st == 0 ? NST - 1 : st - 1, kt + NST - 1);   // past the last step: zeros
     const uint8_t* sa = smem + st * STAGE;
     const uint8_t* sb = sa + NA * 1024;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const bf16x8 af = *(const qlds_bf16x8_t*)(sa + a_row_off + (((2 * ks + h) ^ swa) << 4));
+    for (int ks = 0; ks < KS - 1; ++ks) {
+      const bf16x8 a_n = read_a(sa, ks + 1);
+      wpack_t w_n[NMAT];
 #pragma unroll
-      for (int m = 0; m < NMAT; ++m) {
-        const int br = m * kQBN + brow0;
-        bf16x8 bfr;
-        if constexpr (BITS == 8) {
-          const qu32x2 w = *(const qlds_u32x2_t*)(sb + br * 64 + ((ks ^ qswz4(br)) << 4) + 8 * h);
-          bfr = widen8_i8(w[0], w[1]);
-        } else {
-          const uint32_t w = *(const qlds_u32_t*)(sb + br * 64 + (((ks >> 1) ^ qswz4(br)) << 4) +
-                                                  8 * (ks & 1) + 4 * h);
-          bfr = widen8_i4(w);
-        }
-        acc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bfr, acc[m], 0, 0, 0);
-      }
+      for (int m = 0; m < NMAT; ++m) w_n[m] = read_w(sb, m, ks + 1);
+      __builtin_amdgcn_sched_barrier(0);   // keep the reads ahead of this slice's work
+#pragma unroll
+      for (int m = 0; m < NMAT; ++m)
+        acc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_c, widen(w_c[m]), acc[m], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      a_c = a_n;
+#pragma unroll
+      for (int m = 0; m < NMAT; ++m) w_c[m] = w_n[m];
     }
     __builtin_amdgcn_s_waitcnt(q_wait<DPW * (NST - 2)>());
-    __syncthreads();
+    q_barrier();
     st = st + 1 == NST ? 0 : st + 1;
+    const uint8_t* na = smem + st * STAGE;
+    const bf16x8 a_n = read_a(na, 0);
+    wpack_t w_n[NMAT];
+#pragma unroll
+    for (int m = 0; m < NMAT; ++m) w_n[m] = read_w(na + NA * 1024, m, 0);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int m = 0; m < NMAT; ++m)
+      acc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_c, widen(w_c[m]), acc[m], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    a_c = a_n;
+#pragma unroll
+    for (int m = 0; m < NMAT; ++m) w_c[m] = w_n[m];
   }
   __builtin_amdgcn_s_waitcnt(q_wait<0>());                   // no LDS write outlives the block
 #undef MOE_Q_ISSUE
