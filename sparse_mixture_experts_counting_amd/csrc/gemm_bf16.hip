@@ -1,34 +1,37 @@
 // bf16 grouped GEMM on the CDNA4 matrix cores (v_mfma_f32_32x32x16_bf16, fp32 accumulate).
 //
 // Used for the expert FFN (the page "Mixture of experts (MoE)" (tirogla), How it works step 4: one
-// grouped GEMM over the experts' contiguous batches) and for the router product when E is large.
-// C[r, n] = sum_k A[src(r), k] * B_g[n, k]: both operands are K-contiguous (activation rows, and
-// weights in the [out][in] layout of a linear layer), so both travel the same way.
+// grouped GEMM over the experts' contiguous batches), for the router product when E is large, and
+// for the products of the backward pass.
+// C[r, n] = sum_k A[src(r), k] * B_g[n, k]: in the forward both operands are K-contiguous
+// (activation rows, and weights in the [out][in] layout of a linear layer), so both travel the
+// same way.  The transposed modes read B (BT) or A and B (AT, the weight gradients) stored
+// [K][N] / [K][M] instead.
 //
 // Tiling: a block of WGM x WGN waves computes a BM-row tile of C over BN columns (256 x 256 with
 // 8 waves and one block per CU for large groups, 128 x 256 with 4 waves and two blocks per CU
 // otherwise); for the SwiGLU up projection two weight matrices (w1 and w3) of 128 columns each
 // share the tile and the epilogue forms silu(x.w1) * (x.w3) in registers, so the gate and up
-// products never leave the chip.  Each wave owns a 64 x 128 block of accumulators.  K is walked in
-// steps of 32.
+// products never leave the chip.  K is walked in steps of BK = 64 (32 for the short decode tiles).
 //
-// LDS: every operand row holds the step's 32 bf16 (64 bytes, four 16-byte units) with unit u of
-// row r stored at u ^ swz(r).  Each operand read of the matrix instruction is one ds_read_b128 per
-// lane (32 rows x 2 units per wave), and the swizzle puts 16 consecutive rows read at one unit in
-// 16 distinct 4-bank groups; stores are 4-lane quads filling one row, so 16 lanes write 256
-// contiguous bytes.  Global loads are quads reading one row's 64 contiguous bytes.
+// LDS: every operand row holds the step's BK bf16 (BK / 8 16-byte units) with unit u of row r
+// stored at u ^ swz(r); each operand read of the matrix instruction is one ds_read_b128 per lane
+// and the swizzle puts 16 consecutive rows read at one unit in distinct banks.  Transposed
+// operands are stored as K rows (unit u of row r at u ^ swzT(r)) and read with ds_read_b64_tr_b16.
 //
-// Pipeline: two LDS stages and two register sets.  At the top of step kt the registers holding
-// step kt+1 go to the idle stage and are refilled with step kt+3, so a load has two steps of work
-// to land; one barrier per step, issued without the memory fence of __syncthreads so that it does
-// not drain the loads in flight; the operand reads of the next 16-wide k slice are issued before
-// the matrix instructions of the current one.  The loop body is branch-free: when K divides into
-// an even number of steps, prefetches past the end re-read the last step; otherwise (TAIL) each
-// 16-byte load past the end of its K range is sent out of the buffer's range, which reads zeros.
+// Pipeline: direct-to-LDS buffer loads (one wave-wide 16-byte load fills 1 KB of a stage) into a
+// ring of stages, one barrier per step issued without the memory fence of __syncthreads (which
+// would drain the loads in flight), the operand reads of the next 16-wide k slice issued before
+// the matrix instructions of the current one, and the last slice of a step multiplied after the
+// barrier.  256-row tiles split the ring: two A stages and three B stages, so a weight load has
+// two steps to land.  (The fp32-output router product stages through two register sets instead.)
+// Loads past the end of a block's K range, past a group's rows or past N are sent out of the
+// buffer's range and read zeros.
 //
 // Split-K: when the tile grid would leave CUs idle (few rows per expert, e.g. decode), blocks also
 // split K; each writes fp32 partials and splitk_finish_kernel sums them in a fixed order and
-// applies the epilogue (results do not depend on the split).
+// applies the epilogue.  Otherwise the last partial round of tiles may be split over K and summed
+// by tail_finish_kernel, also in a fixed order (results do not depend on either split).
 #include "common.h"
 #include "gemm_common.h"
 #include "kernels.h"
