@@ -7,9 +7,10 @@
 // A is bf16 (gathered activation rows), q holds int8 values or two int4 values per byte (column 2j
 // in the low nibble), s fp32.  The weights are streamed into LDS as stored (a half or a quarter of
 // the bf16 bytes) and widened to bf16 after the LDS read; every |q| <= 127 is exact in bf16, so the
-// matrix instruction (32x32x16 bf16, fp32 accumulate) forms the exact integer-weighted sum and the
-// scale is applied once per output in the epilogue (with K split, to the fp32 partials, whose sum
-// splitk_finish_kernel takes in chunk order).
+// matrix instruction (32x32x16 bf16, fp32 accumulate) forms exact products, and the scale is
+// applied once per output in the epilogue (with K split, to the fp32 partials, whose sum
+// splitk_finish_kernel takes in chunk order).  INT4 values enter as 136 + q (built from bit
+// patterns) and the epilogue removes 136 times the activation row sums.
 //
 // Tiles: 32 activation rows x 128 weight rows per matrix, 4 waves (wave w owns weight rows
 // 32 w .. 32 w + 31 of each matrix), made for decode-sized groups whose GEMMs are bound by the
@@ -80,11 +81,24 @@ __device__ __forceinline__ bf16x8 widen8_i8(uint32_t lo, uint32_t hi) {
   }
   return r;
 }
-__device__ __forceinline__ bf16x8 widen8_i4(uint32_t w) {
-  bf16x8 r;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) r[i] = (__bf16)(float)(((int)(w << (28 - 4 * i))) >> 28);
-  return r;
+// 8 int4 (one dword) -> the bf16 values 136 + q, exactly, by bit patterns: with u = q + 8 in
+// [0, 15] (the nibble with its top bit flipped), 0x4300 | u is the bf16 of 128 + u.  Ten
+// instructions for 8 values (four bytes of the nibbles spread, then byte permutes that insert the
+// 0x43 high bytes) instead of a sign extension and two conversions per value; the kernel subtracts
+// 136 times the activation row sums in the epilogue.
+__device__ __forceinline__ bf16x8 widen8_i4_biased(uint32_t w) {
+  const uint32_t x = w ^ 0x88888888u;
+  const uint32_t t = x & 0x0F0F0F0Fu;                  // u0 u2 u4 u6 (one per byte)
+  const uint32_t s = (x >> 4) & 0x0F0F0F0Fu;           // u1 u3 u5 u7
+  const uint32_t lo = __builtin_amdgcn_perm(s, t, 0x05010400u);   // u0 u1 u2 u3
+  const uint32_t hi = __builtin_amdgcn_perm(s, t, 0x07030602u);   // u4 u5 u6 u7
+  const uint32_t c = 0x43434343u;
+  u32x4 d;
+  d[0] = __builtin_amdgcn_perm(c, lo, 0x04010400u);    // (0x4300 | u0, 0x4300 | u1)
+  d[1] = __builtin_amdgcn_perm(c, lo, 0x04030402u);
+  d[2] = __builtin_amdgcn_perm(c, hi, 0x04010400u);
+  d[3] = __builtin_amdgcn_perm(c, hi, 0x04030402u);
+  return __builtin_bit_cast(bf16x8, d);
 }
 
 template <int NMAT, int EPI, int BITS>
@@ -158,6 +172,14 @@ __global__ __launch_bounds__(256, 2) void gemm_q_kernel(const GemmParams p, cons
   }
 
   f32x16 acc[NMAT];
+  // INT4: the weights enter as 136 + q; acc_s collects the activation row sums (the fragment
+  // against ones), and the epilogue takes acc - 136 acc_s.
+  f32x16 acc_s;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) acc_s[r] = 0.f;
+  bf16x8 ones;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) ones[i] = (__bf16)1.0f;
 #pragma unroll
   for (int m = 0; m < NMAT; ++m)
 #pragma unroll
@@ -201,7 +223,7 @@ __global__ __launch_bounds__(256, 2) void gemm_q_kernel(const GemmParams p, cons
     if constexpr (BITS == 8)
       return widen8_i8(w[0], w[1]);
     else
-      return widen8_i4(w);
+      return widen8_i4_biased(w);
   };
 #pragma unroll
   for (int s = 0; s < NST - 1; ++s) MOE_Q_ISSUE(s, s);
@@ -228,6 +250,8 @@ __global__ __launch_bounds__(256, 2) void gemm_q_kernel(const GemmParams p, cons
 #pragma unroll
       for (int m = 0; m < NMAT; ++m)
         acc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_c, widen(w_c[m]), acc[m], 0, 0, 0);
+      if constexpr (BITS == 4)
+        acc_s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_c, ones, acc_s, 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
       a_c = a_n;
 #pragma unroll
@@ -245,6 +269,8 @@ __global__ __launch_bounds__(256, 2) void gemm_q_kernel(const GemmParams p, cons
 #pragma unroll
     for (int m = 0; m < NMAT; ++m)
       acc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_c, widen(w_c[m]), acc[m], 0, 0, 0);
+    if constexpr (BITS == 4)
+      acc_s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_c, ones, acc_s, 0, 0, 0);
     __builtin_amdgcn_sched_barrier(0);
     a_c = a_n;
 #pragma unroll
@@ -262,8 +288,9 @@ __global__ __launch_bounds__(256, 2) void gemm_q_kernel(const GemmParams p, cons
   for (int r = 0; r < 16; ++r) {
     const int row = tc.row0 + 8 * (r >> 2) + 4 * h + (r & 3);
     if (row >= tc.row_end) continue;
-    const float v0 = acc[0][r] * sc0;
-    const float v1 = NMAT == 2 ? acc[NMAT - 1][r] * sc1 : 0.f;
+    const float bias = BITS == 4 ? 136.0f * acc_s[r] : 0.f;
+    const float v0 = (acc[0][r] - bias) * sc0;
+    const float v1 = NMAT == 2 ? (acc[NMAT - 1][r] - bias) * sc1 : 0.f;
     if (p.ksplit > 1) {
       p.part[((size_t)(kc * NMAT) * p.part_rows + row) * N + col] = v0;
       if (NMAT == 2) p.part[((size_t)(kc * NMAT + 1) * p.part_rows + row) * N + col] = v1;
