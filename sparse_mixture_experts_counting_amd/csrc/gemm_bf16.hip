@@ -1035,12 +1035,14 @@ template <int BM, int BN, int NMAT, int WGM, int WGN, int BK, int NST, int MINB,
 static hipError_t launch_t(const GemmParams& p, int rows_max, hipStream_t s) {
   auto kern = gemm_bf16_kernel<BM, BN, NMAT, WGM, WGN, BK, NST, MINB, EPI, TAIL, BT, AT>;
   const size_t lds = (size_t)lds_bytes<BM, BN, NMAT, BK, NST, MINB>();
-  static bool attr_set = false;
-  if (!attr_set) {
+  static bool attr_set[64] = {};   // per device: the attribute is set on the current device
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  if (!attr_set[dev]) {
     hipError_t e = hipFuncSetAttribute((const void*)kern,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    attr_set = true;
+    attr_set[dev] = true;
   }
   GemmParams q = p;
   // The last partial round of tiles is split over K when the epilogue allows it (bf16 output, 8

@@ -344,12 +344,14 @@ static hipError_t launch_q_t(GemmParams p, int rows_max, const float* s0, const 
                              hipStream_t s) {
   auto kern = gemm_q_kernel<NMAT, EPI, BITS>;
   constexpr int lds = q_lds<NMAT, BITS>();
-  static bool attr_set = false;
-  if (!attr_set) {
+  static bool attr_set[64] = {};   // per device: the attribute is set on the current device
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  if (!attr_set[dev]) {
     hipError_t e =
         hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (e != hipSuccess) return e;
-    attr_set = true;
+    attr_set[dev] = true;
   }
   const bool grouped = p.offsets != nullptr;
   p.ksplit = p.part ? gemm_q_split(rows_max, p.G, grouped, p.N, p.K, BITS) : 1;
