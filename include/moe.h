@@ -12,10 +12,13 @@
  * Conventions shared by every entry point
  *   - Every pointer is a DEVICE pointer (memory the caller allocated on the current HIP device),
  *     unless stated otherwise.  The caller owns every buffer, including the workspace; the
- *     library never allocates, frees or synchronises.  Buffers must stay valid until the work
- *     enqueued on `stream` has finished.
+ *     library never allocates or frees device memory and never synchronises the host.  Buffers
+ *     must stay valid until the work enqueued on `stream` has finished.
  *   - `stream` is a hipStream_t passed as void*; NULL means the default stream.  Every call only
- *     enqueues kernels on that stream and returns.
+ *     enqueues work ordered on that stream and returns.  (The expert products of groups averaging
+ *     256 to 512 rows run part of their tiles on a second stream the library creates once per
+ *     device, forked from `stream` and joined back to it with events inside the same call, so
+ *     the work still completes in `stream` order.)
  *   - Outputs are fully overwritten (no accumulate-into semantics) and must not alias inputs.
  *   - Integers are int32, row-major everywhere.  T tokens, d model width, E routed experts, k
  *     experts per token, d_ff expert width; assignment a = t*k + s for slot s of token t.
