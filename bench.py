@@ -17,7 +17,9 @@ With --pass train a step is the forward followed by the backward pass of the lay
 <dy, y> + aux + z for x, the router and every expert weight: moe_combine_backward,
 moe_expert_backward for the routed and shared experts, moe_route_backward, and moe_combine adding
 each token's input-gradient rows); that line reports training-step tokens/s and the roofline of
-the expert backward.  With --routing expert_choice the forward runs under Expert Choice routing
+the expert backward.  The training step saves the experts' activations in the forward pass
+(moe_expert_ffn_save, moe_expert_backward_saved); --recompute recomputes them in the backward
+pass instead (moe_expert_ffn, moe_expert_backward).  With --routing expert_choice the forward runs under Expert Choice routing
 (moe_expert_choice, C = T*k/E tokens per expert) and reports its own line; with --routing reroute
 the capacity is C = T*k/E and overflowed assignments go to their next-best expert (moe_reroute);
 with --weights int8 / int4 the routed experts are weight-only quantized (moe_expert_ffn_q).
@@ -111,6 +113,9 @@ def main():
     ap.add_argument("--cpu-repeats", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--pass", dest="mode", choices=("forward", "train"), default="forward")
+    ap.add_argument("--recompute", action="store_true",
+                    help="--pass train: recompute the experts' up projection in the backward "
+                         "pass instead of saving its activations in the forward pass")
     ap.add_argument("--weights", choices=("bf16", "int8", "int4"), default="bf16",
                     help="int8 / int4: weight-only quantized routed experts (moe_expert_ffn_q)")
     ap.add_argument("--routing", choices=("topk", "expert_choice", "reroute"), default="topk",
@@ -551,7 +556,8 @@ def train_bench(args, cfg, dev, torch, layer, lm, synth):
     log("bench: workload %s (forward + backward), generating inputs on the device" % cfg.name)
     inp = synth.make_inputs(cfg, seed=args.seed, device=dev)
     dy = synth.make_dy(cfg, seed=args.seed, device=dev)
-    buf = layer.alloc_buffers(cfg, dev)
+    save = not args.recompute
+    buf = layer.alloc_buffers(cfg, dev, save=save)
     g = layer.alloc_grads(cfg, dev)
     stream = torch.cuda.current_stream(dev)
     T, d, E, k, f = cfg.T, cfg.d, cfg.E, cfg.k, cfg.d_ff
@@ -571,14 +577,23 @@ def train_bench(args, cfg, dev, torch, layer, lm, synth):
         lm.combine_backward(dy, buf.expert_out, buf.inv, buf.topk_gate, T, d, k, bf, g.d_out,
                             g.d_gate)
         mark(2)
-        lm.expert_backward(inp.x, buf.perm, buf.offsets, T, d, f, E, k, inp.w1, inp.w3, inp.w2,
-                           g.d_out, bf, g.dx_rows, g.dw1, g.dw3, g.dw2, g.workspace)
+        if save:
+            lm.expert_backward_saved(buf.saved, inp.x, buf.perm, buf.offsets, T, d, f, E, k,
+                                     inp.w1, inp.w3, inp.w2, g.d_out, bf, g.dx_rows, g.dw1,
+                                     g.dw3, g.dw2, g.workspace)
+        else:
+            lm.expert_backward(inp.x, buf.perm, buf.offsets, T, d, f, E, k, inp.w1, inp.w3,
+                               inp.w2, g.d_out, bf, g.dx_rows, g.dw1, g.dw3, g.dw2, g.workspace)
         mark(3)
         i = 3
         if cfg.n_shared:
             w1s, w3s, w2s = inp.shared
-            lm.expert_backward(inp.x, None, None, T, d, f, 1, 1, w1s, w3s, w2s, dy, bf,
-                               g.dx_shared, *g.dshared, g.workspace)
+            if save:
+                lm.expert_backward_saved(buf.saved_shared, inp.x, None, None, T, d, f, 1, 1, w1s,
+                                         w3s, w2s, dy, bf, g.dx_shared, *g.dshared, g.workspace)
+            else:
+                lm.expert_backward(inp.x, None, None, T, d, f, 1, 1, w1s, w3s, w2s, dy, bf,
+                                   g.dx_shared, *g.dshared, g.workspace)
             i += 1
             mark(i)
         lm.route_backward(inp.x, inp.w_r, buf.logits, buf.topk_idx, buf.topk_gate, g.d_gate,
@@ -604,7 +619,7 @@ def train_bench(args, cfg, dev, torch, layer, lm, synth):
     ms_per_step = wall * 1e3 / args.steps
     n_kept = int(buf.offsets[-1].item())
     # Algorithmic FLOPs of the expert backward: dh (2 d d_ff per row), dx (4), dw1 + dw3 (4),
-    # dw2 (2); the recomputed up projection (4 more) is not counted.
+    # dw2 (2); the recomputed up projection (4 more, --recompute) is not counted.
     bwd_flops = 12.0 * d * f * n_kept
     achieved = bwd_flops / (stage_ms["expert_bwd"] * 1e-3) / 1e12
     fwd_flops = 2.0 * T * d * E + 6.0 * d * f * (n_kept + T * cfg.n_shared)
@@ -617,11 +632,16 @@ def train_bench(args, cfg, dev, torch, layer, lm, synth):
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic (seeded randn inputs, upstream gradient and random-init expert "
                 "weights of the workload's shapes, drawn on the device)",
-        "config": {"workload": cfg.name, "pass": "forward+backward", "T": T, "d": d, "E": E,
+        "config": {"workload": cfg.name, "pass": "forward+backward",
+                   "activations": "recomputed" if args.recompute else "saved",
+                   "T": T, "d": d, "E": E,
                    "k": k, "d_ff": f, "gating": cfg.gating, "capacity": cfg.capacity or None,
                    "shared_experts": cfg.n_shared, "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "mfma",
-                     "kernel": "moe_expert_backward (routed): 6 grouped GEMMs + transposes",
+                     "kernel": ("moe_expert_backward (routed): 6 grouped GEMMs + row gather"
+                                if args.recompute else
+                                "moe_expert_backward_saved (routed): 5 grouped GEMMs + row "
+                                "gather"),
                      "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None},
         "layer": {"algorithmic_flops": train_flops,

@@ -388,6 +388,40 @@ moe_status moe_expert_backward(const void* x, const int32_t* perm, const int32_t
                                size_t ws_bytes, void* stream);
 
 /*
+ * Saved activations: the same backward without recomputing a and b.  A training step that can hold
+ * 3 * rows * d_ff bf16 values per expert layer (rows = T*k, or T in dense mode) runs the forward
+ * Compute step as
+ *
+ *   moe_expert_ffn_save(x, perm, offsets, ..., out, saved)  -> out as moe_expert_ffn, and
+ *       saved [rows][3 * d_ff] bf16: row r holds h_r | a_r | b_r (h exactly the values the down
+ *       projection read; a and b rounded to bf16 from the fp32 sums h was computed from)
+ *
+ * and the Compute gradient as
+ *
+ *   moe_expert_backward_saved(saved, x, perm, offsets, ...) -> the outputs of moe_expert_backward
+ *
+ * whose dh product applies the SwiGLU derivative (da = dh * b * silu'(a), db = dh * silu(a), with
+ * the saved bf16 a and b) in its epilogue and whose dw2 reads the saved h.  This removes the
+ * recomputed up projection (a third of the Compute backward's matrix work) at the price of the
+ * stored activations; the results differ from moe_expert_backward only by the bf16 rounding of a
+ * and b (dw2 is the same).  Arguments, layouts and errors otherwise as moe_expert_ffn and
+ * moe_expert_backward; moe_expert_ffn_save's workspace may be smaller than moe_workspace_bytes
+ * (it holds no h) and moe_expert_backward_saved takes moe_backward_workspace_bytes.  bf16 only
+ * (MOE_ERR_UNSUPPORTED for MOE_F32, or when saved exceeds 2 GiB); saved must be 16-byte aligned
+ * (MOE_ERR_ARG).
+ */
+moe_status moe_expert_ffn_save(const void* x, const int32_t* perm, const int32_t* offsets, int T,
+                               int d, int d_ff, int E, int k, const void* w1, const void* w3,
+                               const void* w2, moe_dtype dt, void* out, void* saved,
+                               void* workspace, size_t ws_bytes, void* stream);
+moe_status moe_expert_backward_saved(const void* saved, const void* x, const int32_t* perm,
+                                     const int32_t* offsets, int T, int d, int d_ff, int E, int k,
+                                     const void* w1, const void* w3, const void* w2,
+                                     const void* d_out, moe_dtype dt, void* dx_rows, float* dw1,
+                                     float* dw3, float* dw2, void* workspace, size_t ws_bytes,
+                                     void* stream);
+
+/*
  * moe_route_backward -- gradient of Score and of the two router losses:
  *
  *   d_logits[t,.] = (gating function's derivative) applied to d_gate[t,.]

@@ -198,7 +198,8 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_bf16_kernel(const G
                          BN % (DROWS * NW) == 0), "direct loads split evenly");
   // Transposed B: a stage's B block is BK rows of RBT bytes; one direct load fills RPB rows.
   constexpr int RBT = BN * 2, UPB = RBT / 16, RPB = 1024 / RBT;
-  static_assert(!BT || (DMA && NMAT == 1 && BN == 256 && (EPI == EPI_STORE || AT) &&
+  static_assert(!BT || (DMA && NMAT == 1 && BN == 256 &&
+                        (EPI == EPI_STORE || EPI == EPI_SWIGLU_BWD_SAVED || AT) &&
                         BK * RBT == BN * RB),
                 "transposed B: direct loads, one 256-column matrix, bf16 output");
   // Transposed A (with transposed B: the weight gradients, both operands row-major activations
@@ -706,12 +707,22 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_bf16_kernel(const G
       // Two columns per lane as in the bf16 store below: after the pair exchange the even lane
       // holds row a and the odd lane row b of columns (2c, 2c+1); dh is read and h, da, db are
       // written 4 bytes at a time.
+      // The 8 loads of dh of a 32 x 32 block are issued before its stores (one round trip).
       const bool odd = lane & 1;
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
           const int col0 = n_base + wn0 + j * 32 + (l32 & ~1);
+          uint32_t dhws[8];
+#pragma unroll
+          for (int q = 0; q < 8; ++q) {
+            const int rr = odd ? 2 * q + 1 : 2 * q;
+            const int row = tc.row0 + wm0 + i * 32 + 8 * (rr >> 2) + 4 * h + (rr & 3);
+            dhws[q] = 0;
+            if (row < tc.row_end && col0 < N)
+              dhws[q] = *(const uint32_t*)((const uint16_t*)p.D + (size_t)row * N + col0);
+          }
 #pragma unroll
           for (int r = 0; r < 16; r += 2) {
             const float ga = swap_pair(odd ? acc[0][i][j][r] : acc[0][i][j][r + 1]);
@@ -725,7 +736,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_bf16_kernel(const G
             b[0] = odd ? gb : acc[NMAT - 1][i][j][r];
             b[1] = odd ? acc[NMAT - 1][i][j][r + 1] : gb;
             const size_t o = (size_t)row * N + col0;
-            const uint32_t dhw = *(const uint32_t*)((const uint16_t*)p.D + o);
+            const uint32_t dhw = dhws[r >> 1];
             float hv[2], da[2], db[2];
 #pragma unroll
             for (int q = 0; q < 2; ++q) {
@@ -765,6 +776,78 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_bf16_kernel(const G
           uint16_t* dab = (uint16_t*)p.C + (size_t)row * p.ldc + col;
           dab[0] = f32_to_bf16(dh * b * (sg * (1.0f + a * (1.0f - sg))));
           dab[N] = f32_to_bf16(dh * sa);
+        }
+      }
+    }
+    return;
+  }
+  if constexpr (EPI == EPI_SWIGLU_BWD_SAVED) {   // never split (the launcher passes no workspace)
+    // The accumulator is dh; a and b come from the forward pass's saved bf16 values.  Per 32 x 32
+    // block all 16 loads of a and b are issued before any store, so that one memory round trip
+    // (not one per row pair: the stores may alias the loads) covers the block.
+    if (N % 2 == 0 && p.ldc % 2 == 0 && p.ldd % 2 == 0) {
+      const bool odd = lane & 1;
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          const int col0 = n_base + wn0 + j * 32 + (l32 & ~1);
+          float dh[8][2];
+          uint32_t aw[8], bw[8];
+          int rows[8];
+#pragma unroll
+          for (int q = 0; q < 8; ++q) {
+            const int r = 2 * q;
+            const float g = swap_pair(odd ? acc[0][i][j][r] : acc[0][i][j][r + 1]);
+            const int rr = odd ? r + 1 : r;
+            rows[q] = tc.row0 + wm0 + i * 32 + 8 * (rr >> 2) + 4 * h + (rr & 3);
+            dh[q][0] = odd ? g : acc[0][i][j][r];
+            dh[q][1] = odd ? acc[0][i][j][r + 1] : g;
+            aw[q] = bw[q] = 0;
+            if (rows[q] < tc.row_end && col0 < N) {
+              const uint16_t* ab = (const uint16_t*)p.D + (size_t)rows[q] * p.ldd + col0;
+              aw[q] = *(const uint32_t*)ab;
+              bw[q] = *(const uint32_t*)(ab + N);
+            }
+          }
+#pragma unroll
+          for (int q = 0; q < 8; ++q) {
+            if (rows[q] >= tc.row_end || col0 >= N) continue;
+            float da[2], db[2];
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+              const float a = c ? bf16_hi(aw[q]) : bf16_lo(aw[q]);
+              const float b = c ? bf16_hi(bw[q]) : bf16_lo(bw[q]);
+              const float sg =
+                  __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * a));
+              da[c] = dh[q][c] * b * (sg * (1.0f + a * (1.0f - sg)));
+              db[c] = dh[q][c] * (a * sg);
+            }
+            uint16_t* dab = (uint16_t*)p.C + (size_t)rows[q] * p.ldc + col0;
+            *(uint32_t*)dab = pack_bf16x2(da[0], da[1]);
+            *(uint32_t*)(dab + N) = pack_bf16x2(db[0], db[1]);
+          }
+        }
+      }
+      return;
+    }
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int col = n_base + wn0 + j * 32 + l32;
+        if (col >= N) continue;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = tc.row0 + wm0 + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+          if (row >= tc.row_end) continue;
+          const float dh = acc[0][i][j][r];
+          const uint16_t* ab = (const uint16_t*)p.D + (size_t)row * p.ldd + col;
+          const float a = bf16_to_f32(ab[0]), b = bf16_to_f32(ab[N]);
+          const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * a));
+          uint16_t* dab = (uint16_t*)p.C + (size_t)row * p.ldc + col;
+          dab[0] = f32_to_bf16(dh * b * (sg * (1.0f + a * (1.0f - sg))));
+          dab[N] = f32_to_bf16(dh * (a * sg));
         }
       }
     }
@@ -832,7 +915,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_bf16_kernel(const G
         float v[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          if constexpr (EPI == EPI_SWIGLU)
+          if constexpr (epi_swiglu(EPI))
             v[r] = silu(acc[0][i][j][r]) * acc[NMAT - 1][i][j][r];
           else
             v[r] = acc[0][i][j][r];
@@ -844,6 +927,17 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_bf16_kernel(const G
               float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, send), 0xB1, 0xF, 0xF, false));
           const int rr = odd ? r + 1 : r;
           const int row = tc.row0 + wm0 + i * 32 + 8 * (rr >> 2) + 4 * h + (rr & 3);
+          if constexpr (EPI == EPI_SWIGLU_SAVE) {   // a and b beside h, exchanged the same way
+            const float ga = swap_pair(odd ? acc[0][i][j][r] : acc[0][i][j][r + 1]);
+            const float gb = swap_pair(odd ? acc[NMAT - 1][i][j][r] : acc[NMAT - 1][i][j][r + 1]);
+            if (row < tc.row_end && col0 < N) {
+              uint16_t* dst = (uint16_t*)Cg + (size_t)row * p.ldc + col0;
+              *(uint32_t*)(dst + N) = odd ? pack_bf16x2(ga, acc[0][i][j][r + 1])
+                                          : pack_bf16x2(acc[0][i][j][r], ga);
+              *(uint32_t*)(dst + 2 * N) = odd ? pack_bf16x2(gb, acc[NMAT - 1][i][j][r + 1])
+                                              : pack_bf16x2(acc[NMAT - 1][i][j][r], gb);
+            }
+          }
           if (row < tc.row_end && col0 < N) {
             const uint32_t packed = odd ? pack_bf16x2(got, v[r + 1]) : pack_bf16x2(v[r], got);
             *(uint32_t*)((uint16_t*)Cg + (size_t)row * p.ldc + col0) = packed;
@@ -872,10 +966,15 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_bf16_kernel(const G
           for (int m = 0; m < NMAT; ++m)
             p.part[(((size_t)rtile * nsplit + kc) * NMAT + m) * (BM * BN) + (row - tc.row0) * BN +
                    (col - n_base)] = acc[m][i][j][r];
-        } else if constexpr (EPI == EPI_SWIGLU) {
+        } else if constexpr (epi_swiglu(EPI)) {
           const float g = acc[0][i][j][r];
           const float v = acc[NMAT - 1][i][j][r];
-          ((uint16_t*)Cg)[(size_t)row * p.ldc + col] = f32_to_bf16(silu(g) * v);
+          uint16_t* dst = (uint16_t*)Cg + (size_t)row * p.ldc + col;
+          dst[0] = f32_to_bf16(silu(g) * v);
+          if constexpr (EPI == EPI_SWIGLU_SAVE) {
+            dst[N] = f32_to_bf16(g);
+            dst[2 * N] = f32_to_bf16(v);
+          }
         } else if constexpr (EPI == EPI_STORE) {
           ((uint16_t*)Cg)[(size_t)row * p.ldc + col] = f32_to_bf16(acc[0][i][j][r]);
         } else {
@@ -912,21 +1011,28 @@ __global__ __launch_bounds__(256) void splitk_finish_kernel(const GemmParams p) 
         s[m][4] += b[0]; s[m][5] += b[1]; s[m][6] += b[2]; s[m][7] += b[3];
       }
     }
-    u32x4 o;
+    u32x4 o, oa, ob;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       float v0, v1;
-      if constexpr (EPI == EPI_SWIGLU) {
+      if constexpr (epi_swiglu(EPI)) {
         const float g0 = s[0][2 * q], g1 = s[0][2 * q + 1];
         v0 = silu(g0) * s[NMAT - 1][2 * q];
         v1 = silu(g1) * s[NMAT - 1][2 * q + 1];
+        oa[q] = pack_bf16x2(g0, g1);
+        ob[q] = pack_bf16x2(s[NMAT - 1][2 * q], s[NMAT - 1][2 * q + 1]);
       } else {
         v0 = s[0][2 * q];
         v1 = s[0][2 * q + 1];
       }
       o[q] = pack_bf16x2(v0, v1);
     }
-    *reinterpret_cast<u32x4*>((uint16_t*)p.C + (size_t)row * p.ldc + c0) = o;
+    uint16_t* dst = (uint16_t*)p.C + (size_t)row * p.ldc + c0;
+    *reinterpret_cast<u32x4*>(dst) = o;
+    if constexpr (EPI == EPI_SWIGLU_SAVE) {
+      *reinterpret_cast<u32x4*>(dst + p.N) = oa;
+      *reinterpret_cast<u32x4*>(dst + 2 * p.N) = ob;
+    }
   }
 }
 
@@ -965,21 +1071,28 @@ __global__ __launch_bounds__(256) void tail_finish_kernel(const GemmParams p) {
         s[m][4] += b[0]; s[m][5] += b[1]; s[m][6] += b[2]; s[m][7] += b[3];
       }
     }
-    u32x4 o;
+    u32x4 o, oa, ob;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       float v0, v1;
-      if constexpr (EPI == EPI_SWIGLU) {
+      if constexpr (epi_swiglu(EPI)) {
         const float g0 = s[0][2 * c], g1 = s[0][2 * c + 1];
         v0 = silu(g0) * s[NMAT - 1][2 * c];
         v1 = silu(g1) * s[NMAT - 1][2 * c + 1];
+        oa[c] = pack_bf16x2(g0, g1);
+        ob[c] = pack_bf16x2(s[NMAT - 1][2 * c], s[NMAT - 1][2 * c + 1]);
       } else {
         v0 = s[0][2 * c];
         v1 = s[0][2 * c + 1];
       }
       o[c] = pack_bf16x2(v0, v1);
     }
-    *reinterpret_cast<u32x4*>((uint16_t*)p.C + (size_t)row * p.ldc + col) = o;
+    uint16_t* dst = (uint16_t*)p.C + (size_t)row * p.ldc + col;
+    *reinterpret_cast<u32x4*>(dst) = o;
+    if constexpr (EPI == EPI_SWIGLU_SAVE) {
+      *reinterpret_cast<u32x4*>(dst + p.N) = oa;
+      *reinterpret_cast<u32x4*>(dst + 2 * p.N) = ob;
+    }
   }
 }
 
@@ -1048,7 +1161,8 @@ static hipError_t launch_t(const GemmParams& p, int rows_max, hipStream_t s) {
   // The last partial round of tiles is split over K when the epilogue allows it (bf16 output, 8
   // columns per finishing item) and the caller gave scratch for the partials.
   const bool tail = p.ksplit == 1 && p.part != nullptr && EPI != EPI_STORE_F32_BIAS &&
-                    EPI != EPI_SWIGLU_BWD && !p.kgrouped && p.N % 8 == 0 && p.K % 64 == 0;
+                    EPI != EPI_SWIGLU_BWD && EPI != EPI_SWIGLU_BWD_SAVED && !p.kgrouped &&
+                    p.N % 8 == 0 && p.K % 64 == 0;
   q.slots = tail ? device_cus() * MINB : 0;
   if (p.kgrouped) q.slots = device_cus() / 8 * 8 * MINB;   // blocks per round (tile order only)
   const int NT = (p.N + BN - 1) / BN;
@@ -1058,7 +1172,8 @@ static hipError_t launch_t(const GemmParams& p, int rows_max, hipStream_t s) {
   if (tiles <= 0) return hipSuccess;
   hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * WGM * WGN), lds, s, q);
   if (q.slots > 0 && !p.kgrouped) {
-    if constexpr (EPI != EPI_STORE_F32_BIAS && EPI != EPI_SWIGLU_BWD)
+    if constexpr (EPI != EPI_STORE_F32_BIAS && EPI != EPI_SWIGLU_BWD &&
+                  EPI != EPI_SWIGLU_BWD_SAVED)
       hipLaunchKernelGGL((tail_finish_kernel<BM, BN, NMAT, EPI>), dim3(q.slots * kFinishSplit),
                          dim3(256), 0, s, q);
   }
@@ -1081,6 +1196,9 @@ static void launch_splitk_finish(const GemmParams& p, int rows_max, int epi, hip
   if (fgrid <= 0) return;
   if (epi == EPI_SWIGLU)
     hipLaunchKernelGGL((splitk_finish_kernel<2, EPI_SWIGLU>), dim3(fgrid), dim3(256), 0, s, p);
+  else if (epi == EPI_SWIGLU_SAVE)
+    hipLaunchKernelGGL((splitk_finish_kernel<2, EPI_SWIGLU_SAVE>), dim3(fgrid), dim3(256), 0, s,
+                       p);
   else
     hipLaunchKernelGGL((splitk_finish_kernel<1, EPI_STORE>), dim3(fgrid), dim3(256), 0, s, p);
 }
@@ -1106,7 +1224,7 @@ static bool use_big_tiles(int rows_max, int G, bool grouped, int epi) {
 static int splitk_factor(int rows_max, int G, bool grouped, int N, int K, int epi) {
   if (epi == EPI_STORE_F32_BIAS || K % 64 != 0 || N % 8 != 0) return 1;
   if (use_big_tiles(rows_max, G, grouped, epi)) return 1;
-  const int BM = 128, BN = (epi == EPI_SWIGLU) ? 128 : 256;
+  const int BM = 128, BN = epi_swiglu(epi) ? 128 : 256;
   const int mt = grouped ? std::min(G, rows_max) + rows_max / BM : (rows_max + BM - 1) / BM;
   const long long tiles = (long long)mt * ((N + BN - 1) / BN);
   const int cus = device_cus();
@@ -1143,12 +1261,12 @@ static int splitk_factor(int rows_max, int G, bool grouped, int N, int K, int ep
 // every tile configuration used here).
 size_t gemm_bf16_partial_bytes(int rows_max, int G, bool grouped, int N, int K, int epi) {
   if (epi == EPI_STORE_F32_BIAS) return 0;
-  const int nmat = epi == EPI_SWIGLU ? 2 : 1;
+  const int nmat = epi_swiglu(epi) ? 2 : 1;
   const int ks = splitk_factor(rows_max, G, grouped, N, K, epi);
   if (ks > 1) return (size_t)ks * nmat * rows_max * N * sizeof(float);
   if (N % 8 != 0 || K % 64 != 0) return 0;
   const bool big = use_big_tiles(rows_max, G, grouped, epi);
-  const int BM = big ? 256 : 128, BN = epi == EPI_SWIGLU ? 128 : 256, minb = big ? 1 : 2;
+  const int BM = big ? 256 : 128, BN = epi_swiglu(epi) ? 128 : 256, minb = big ? 1 : 2;
   return (size_t)device_cus() * minb * nmat * BM * BN * sizeof(float);
 }
 
@@ -1159,6 +1277,9 @@ static hipError_t launch_cfg(const GemmParams& p, int rows_max, int epi, bool bi
     case EPI_SWIGLU:   // short tiles: 64-deep steps (128-byte runs per weight row), one block per CU
       return big ? launch_tail_or_not<256, 128, 2, 4, 2, 64, 2, 1, EPI_SWIGLU>(p, rows_max, s)
                  : launch_tail_or_not<128, 128, 2, 2, 2, 64, 3, 1, EPI_SWIGLU>(p, rows_max, s);
+    case EPI_SWIGLU_SAVE:   // the same tiles, storing a and b beside h
+      return big ? launch_tail_or_not<256, 128, 2, 4, 2, 64, 2, 1, EPI_SWIGLU_SAVE>(p, rows_max, s)
+                 : launch_tail_or_not<128, 128, 2, 2, 2, 64, 3, 1, EPI_SWIGLU_SAVE>(p, rows_max, s);
     case EPI_STORE:
       if (p.bt)
         return big ? launch_tail_or_not<256, 256, 1, 2, 4, 64, 2, 1, EPI_STORE, true>(p, rows_max, s)
@@ -1168,6 +1289,16 @@ static hipError_t launch_cfg(const GemmParams& p, int rows_max, int epi, bool bi
     case EPI_SWIGLU_BWD:
       return big ? launch_tail_or_not<256, 128, 2, 4, 2, 64, 2, 1, EPI_SWIGLU_BWD>(p, rows_max, s)
                  : launch_tail_or_not<128, 128, 2, 2, 2, 32, 3, 2, EPI_SWIGLU_BWD>(p, rows_max, s);
+    case EPI_SWIGLU_BWD_SAVED:   // the dh product's tiles (transposed B as stored, or K-contiguous)
+      if (p.bt)
+        return big ? launch_tail_or_not<256, 256, 1, 2, 4, 64, 2, 1, EPI_SWIGLU_BWD_SAVED, true>(
+                         p, rows_max, s)
+                   : launch_tail_or_not<128, 256, 1, 2, 2, 32, 3, 2, EPI_SWIGLU_BWD_SAVED, true>(
+                         p, rows_max, s);
+      return big ? launch_tail_or_not<256, 256, 1, 4, 2, 64, 2, 1, EPI_SWIGLU_BWD_SAVED>(p, rows_max,
+                                                                                      s)
+                 : launch_tail_or_not<128, 256, 1, 2, 2, 32, 3, 2, EPI_SWIGLU_BWD_SAVED>(p, rows_max,
+                                                                                      s);
     default:
       return launch_tail_or_not<128, 256, 1, 2, 2, 32, 0, 1, EPI_STORE_F32_BIAS>(p, rows_max, s);
   }
@@ -1193,7 +1324,7 @@ hipError_t launch_gemm_bf16(const GemmParams& p_in, int rows_max, int epi, hipSt
       return hipErrorNotSupported;
   } else if (p_in.bt) {
     // Transposed B: bf16 output, N a multiple of 8, the stacked matrices split on a 64-deep step.
-    if (epi != EPI_STORE || p_in.N % 8 != 0 || ldb < p_in.N ||
+    if ((epi != EPI_STORE && epi != EPI_SWIGLU_BWD_SAVED) || p_in.N % 8 != 0 || ldb < p_in.N ||
         (p_in.bt_k1 > 0 && (p_in.bt_k1 % 64 != 0 || p_in.bt_k1 >= p_in.K)))
       return hipErrorNotSupported;
   }
@@ -1205,7 +1336,10 @@ hipError_t launch_gemm_bf16(const GemmParams& p_in, int rows_max, int epi, hipSt
     p.part = nullptr;
     return launch_t<256, 256, 1, 4, 2, 64, 2, 1, EPI_STORE_F32_BIAS, false, true, true>(p, 0, s);
   }
-  if (epi == EPI_SWIGLU_BWD) p.part = nullptr;   // its epilogue runs on whole sums only
+  // These epilogues run on whole sums only.
+  if (epi == EPI_SWIGLU_BWD || epi == EPI_SWIGLU_BWD_SAVED) p.part = nullptr;
+  if (epi == EPI_SWIGLU_BWD_SAVED && (!p.D || p.ldd < 2 * p.N)) return hipErrorInvalidValue;
+  if (epi == EPI_SWIGLU_SAVE && p.ldc < 3 * p.N) return hipErrorInvalidValue;
   p.ksplit = splitk_factor(rows_max, p.G, grouped, p.N, p.K, epi);
   p.part_rows = rows_max;
   if (p.ksplit > 1 && p.part == nullptr) p.ksplit = 1;   // no scratch given: no split

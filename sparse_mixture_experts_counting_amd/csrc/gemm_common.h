@@ -45,6 +45,11 @@ struct GemmParams {
   // [0, N) and db in [N, 2N): da = dh * b * silu'(a), db = dh * silu(a).  All bf16.
   const void* D;
   void* H;
+  // Saved-activation epilogues.  EPI_SWIGLU_SAVE: as EPI_SWIGLU, and also stores the bf16 a and b
+  // beside h in the same row of C (ldc >= 3N): h in columns [0, N), a in [N, 2N), b in [2N, 3N).
+  // EPI_SWIGLU_BWD_SAVED (one matrix, the GEMM gives dh): reads a = D[row * ldd + col] and
+  // b = D[row * ldd + N + col] and writes da, db into C as EPI_SWIGLU_BWD does.
+  int ldd;
   // Transposed B (bt != 0; one matrix, bf16 output): B_g is stored [K][N] (row stride ldb, or N),
   // i.e. N-contiguous, as a linear layer's weight is for the products that reduce over its output
   // dimension.  With bt_k1 > 0, rows k < bt_k1 come from B0 and rows k >= bt_k1 from row
@@ -60,7 +65,17 @@ struct GemmParams {
   int part_mode;
 };
 
-enum { EPI_SWIGLU = 0, EPI_STORE = 1, EPI_STORE_F32_BIAS = 2, EPI_SWIGLU_BWD = 3 };
+enum {
+  EPI_SWIGLU = 0,
+  EPI_STORE = 1,
+  EPI_STORE_F32_BIAS = 2,
+  EPI_SWIGLU_BWD = 3,
+  EPI_SWIGLU_SAVE = 4,
+  EPI_SWIGLU_BWD_SAVED = 5
+};
+
+// Epilogues whose GEMM carries two matrices (a and b) and writes h = silu(a) * b.
+constexpr bool epi_swiglu(int epi) { return epi == EPI_SWIGLU || epi == EPI_SWIGLU_SAVE; }
 
 struct TileCoord {
   int g;        // group

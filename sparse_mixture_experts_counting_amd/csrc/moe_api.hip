@@ -237,9 +237,10 @@ static hipError_t run_up(const void* x, const int32_t* perm, const int32_t* offs
 
 static hipError_t run_down_rows(const void* h, const int32_t* offsets, int T, int d, int d_ff,
                                 int E, int rows_max, const void* w2, bool bf16, void* out,
-                                void* part, hipStream_t s) {
+                                void* part, hipStream_t s, int lda = 0) {
   moe::GemmParams dn{};
   dn.A = h;
+  dn.lda = lda;
   dn.a_rows = rows_max;
   dn.gather_div = 1;
   dn.offsets = offsets;
@@ -278,6 +279,46 @@ moe_status moe_expert_ffn(const void* x, const int32_t* perm, const int32_t* off
   if (e != hipSuccess) return MOE_ERR_DEVICE;
   e = run_down(workspace, perm ? offsets : nullptr, T, d, d_ff, E, k, w2, bf16, out, part, s);
   if (e != hipSuccess) return MOE_ERR_DEVICE;
+  return launched();
+}
+
+moe_status moe_expert_ffn_save(const void* x, const int32_t* perm, const int32_t* offsets, int T,
+                               int d, int d_ff, int E, int k, const void* w1, const void* w3,
+                               const void* w2, moe_dtype dt, void* out, void* saved,
+                               void* workspace, size_t ws_bytes, void* stream) {
+  moe_status st = check_ffn_args(x, w1, w3, out, perm != nullptr, offsets, T, d, d_ff, E, k, dt);
+  if (st != MOE_OK) return st;
+  if (!w2 || !aligned16(w2) || !saved || !aligned16(saved)) return MOE_ERR_ARG;
+  if (dt != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  const int rows_max = perm ? T * k : T;
+  const bool grouped = perm != nullptr;
+  if (!fits_i32((long long)rows_max * 6 * d_ff)) return MOE_ERR_UNSUPPORTED;   // bytes of saved
+  const size_t need = ffn_partial_bytes(rows_max, grouped, E, d, d_ff, dt);
+  if (need && (!workspace || !aligned16(workspace))) return MOE_ERR_ARG;
+  if (ws_bytes < need) return MOE_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  void* part = need ? workspace : nullptr;
+  moe::GemmParams up{};   // h | a | b per row of saved
+  up.A = x;
+  up.a_rows = T;
+  up.gather = perm;
+  up.gather_div = k;
+  up.offsets = grouped ? offsets : nullptr;
+  up.G = grouped ? E : 1;
+  up.M = T;
+  up.N = d_ff;
+  up.K = d;
+  up.B0 = w1;
+  up.B1 = w3;
+  up.b_gstride = (long long)d * d_ff;
+  up.C = saved;
+  up.ldc = 3 * d_ff;
+  up.part = (float*)part;
+  if (moe::launch_gemm_bf16(up, rows_max, moe::EPI_SWIGLU_SAVE, s) != hipSuccess)
+    return MOE_ERR_DEVICE;
+  if (run_down_rows(saved, grouped ? offsets : nullptr, T, d, d_ff, E, rows_max, w2, true, out,
+                    part, s, 3 * d_ff) != hipSuccess)
+    return MOE_ERR_DEVICE;
   return launched();
 }
 
@@ -506,14 +547,20 @@ moe_status moe_combine_backward(const void* dy, const void* expert_out, const in
   return launched();
 }
 
-moe_status moe_expert_backward(const void* x, const int32_t* perm, const int32_t* offsets, int T,
-                               int d, int d_ff, int E, int k, const void* w1, const void* w3,
-                               const void* w2, const void* d_out, moe_dtype dt, void* dx_rows,
-                               float* dw1, float* dw3, float* dw2, void* workspace,
-                               size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+// The expert backward chain; saved (or NULL) holds the forward's h | a | b rows
+// (moe_expert_ffn_save), which replace the recomputation of a and b.
+static moe_status expert_backward(const void* saved, const void* x, const int32_t* perm,
+                                  const int32_t* offsets, int T, int d, int d_ff, int E, int k,
+                                  const void* w1, const void* w3, const void* w2,
+                                  const void* d_out, moe_dtype dt, void* dx_rows, float* dw1,
+                                  float* dw3, float* dw2, void* workspace, size_t ws_bytes,
+                                  void* stream) {
   const bool grouped = perm != nullptr;
   moe_status st = check_ffn_args(x, w1, w3, dx_rows, grouped, offsets, T, d, d_ff, E, k, dt);
   if (st != MOE_OK) return st;
+  if (saved && !aligned16(saved)) return MOE_ERR_ARG;
   if (!w2 || !d_out || !dw1 || !dw3 || !dw2 || !workspace) return MOE_ERR_ARG;
   if (!aligned16(w2) || !aligned16(d_out) || !aligned16(dw1) || !aligned16(dw3) ||
       !aligned16(dw2) || !aligned16(workspace))
@@ -522,7 +569,7 @@ moe_status moe_expert_backward(const void* x, const int32_t* perm, const int32_t
   const int G = grouped ? E : 1;
   const int rows = grouped ? T * k : T;
   // 32-bit element offsets inside one operand (the GEMMs offset each group's weights in 64 bits)
-  if (!fits_i32((long long)rows * 2 * d_ff) || !fits_i32((long long)rows * d) ||
+  if (!fits_i32((long long)rows * (saved ? 6 : 2) * d_ff) || !fits_i32((long long)rows * d) ||
       !fits_i32((long long)d * 2 * d_ff))
     return MOE_ERR_UNSUPPORTED;
   const BwdLayout L = bwd_layout(rows, grouped, G, d, d_ff);
@@ -545,7 +592,8 @@ moe_status moe_expert_backward(const void* x, const int32_t* perm, const int32_t
                             (long long)d * 2 * d_ff, s);
   }
   hipError_t e;
-  {   // dh = d_out w2 (rows of each expert); w2[e] is [d][d_ff], i.e. [K][N]
+  {   // dh = d_out w2 (rows of each expert); w2[e] is [d][d_ff], i.e. [K][N].  From saved
+      // activations the epilogue turns dh into da, db at once.
     moe::GemmParams q{};
     q.A = d_out; q.a_rows = rows; q.gather_div = 1;
     q.offsets = grouped ? offsets : nullptr; q.G = G; q.M = T;
@@ -556,9 +604,15 @@ moe_status moe_expert_backward(const void* x, const int32_t* perm, const int32_t
       q.B0 = w2t;
     }
     q.C = dh; q.ldc = d_ff; q.part = part;
-    if ((e = moe::launch_gemm_bf16(q, rows, moe::EPI_STORE, s)) != hipSuccess) return MOE_ERR_DEVICE;
+    int epi = moe::EPI_STORE;
+    if (saved) {
+      q.C = dab; q.ldc = 2 * d_ff;
+      q.D = (const uint16_t*)saved + d_ff; q.ldd = 3 * d_ff;
+      epi = moe::EPI_SWIGLU_BWD_SAVED;
+    }
+    if ((e = moe::launch_gemm_bf16(q, rows, epi, s)) != hipSuccess) return MOE_ERR_DEVICE;
   }
-  {   // a, b recomputed; h, da, db from dh
+  if (!saved) {   // a, b recomputed; h, da, db from dh
     moe::GemmParams q{};
     q.A = x; q.a_rows = T; q.gather = perm; q.gather_div = k;
     q.offsets = grouped ? offsets : nullptr; q.G = G; q.M = T;
@@ -589,20 +643,42 @@ moe_status moe_expert_backward(const void* x, const int32_t* perm, const int32_t
     moe::launch_gather_rows(x, d, perm, k, offsets, G, rows, xg, s);
     xe = xg;
   }
-  struct WG { const void* A; int M; int lda; const void* B; int N; float* C; };
-  const WG wg[3] = {{d_out, d, d, h, d_ff, dw2},
-                    {dab, d_ff, 2 * d_ff, xe, d, dw1},
-                    {(const uint16_t*)dab + d_ff, d_ff, 2 * d_ff, xe, d, dw3}};
+  struct WG { const void* A; int M; int lda; const void* B; int N; int ldb; float* C; };
+  const WG wg[3] = {{d_out, d, d, saved ? saved : h, d_ff, saved ? 3 * d_ff : d_ff, dw2},
+                    {dab, d_ff, 2 * d_ff, xe, d, d, dw1},
+                    {(const uint16_t*)dab + d_ff, d_ff, 2 * d_ff, xe, d, d, dw3}};
   for (const WG& w : wg) {
     moe::GemmParams q{};
     q.A = w.A; q.a_rows = rows; q.lda = w.lda; q.gather_div = 1;
     q.offsets = offs; q.G = G; q.M = w.M; q.N = w.N; q.K = rows;
-    q.B0 = w.B; q.ldb = w.N; q.C = w.C; q.ldc = w.N;
+    q.B0 = w.B; q.ldb = w.ldb; q.C = w.C; q.ldc = w.N;
     q.kgrouped = 1; q.at = 1; q.bt = 1; q.c_gstride = (long long)w.M * w.N;
     if ((e = moe::launch_gemm_bf16(q, rows, moe::EPI_STORE_F32_BIAS, s)) != hipSuccess)
       return MOE_ERR_DEVICE;
   }
   return launched();
+}
+
+extern "C" {
+
+moe_status moe_expert_backward(const void* x, const int32_t* perm, const int32_t* offsets, int T,
+                               int d, int d_ff, int E, int k, const void* w1, const void* w3,
+                               const void* w2, const void* d_out, moe_dtype dt, void* dx_rows,
+                               float* dw1, float* dw3, float* dw2, void* workspace,
+                               size_t ws_bytes, void* stream) {
+  return expert_backward(nullptr, x, perm, offsets, T, d, d_ff, E, k, w1, w3, w2, d_out, dt,
+                         dx_rows, dw1, dw3, dw2, workspace, ws_bytes, stream);
+}
+
+moe_status moe_expert_backward_saved(const void* saved, const void* x, const int32_t* perm,
+                                     const int32_t* offsets, int T, int d, int d_ff, int E, int k,
+                                     const void* w1, const void* w3, const void* w2,
+                                     const void* d_out, moe_dtype dt, void* dx_rows, float* dw1,
+                                     float* dw3, float* dw2, void* workspace, size_t ws_bytes,
+                                     void* stream) {
+  if (!saved) return MOE_ERR_ARG;
+  return expert_backward(saved, x, perm, offsets, T, d, d_ff, E, k, w1, w3, w2, d_out, dt,
+                         dx_rows, dw1, dw3, dw2, workspace, ws_bytes, stream);
 }
 
 moe_status moe_route_backward(const void* x, const void* w_r, const float* logits,

@@ -33,9 +33,15 @@ class MoEBuffers:
     aux: torch.Tensor
     z: torch.Tensor
     workspace: torch.Tensor
+    # Saved activations for the backward pass (h | a | b per expert row, bf16), or None: the
+    # backward then recomputes a and b.
+    saved: torch.Tensor = None
+    saved_shared: torch.Tensor = None
 
 
-def alloc_buffers(cfg, device="cuda"):
+def alloc_buffers(cfg, device="cuda", save=False):
+    """Device buffers of one forward; save=True adds the saved activations of a training step
+    (3 * d_ff bf16 values per expert row and per token of the shared expert)."""
     dev = torch.device(device)
     dt = torch.float32 if cfg.dtype == "fp32" else torch.bfloat16
     code = lm.MOE_F32 if cfg.dtype == "fp32" else lm.MOE_BF16
@@ -52,7 +58,10 @@ def alloc_buffers(cfg, device="cuda"):
         n_dropped=torch.empty(1, **i32), expert_out=torch.empty((A, d), dtype=dt, device=dev),
         shared_out=torch.empty((T, d), dtype=dt, device=dev) if cfg.n_shared else None,
         y=torch.empty((T, d), dtype=dt, device=dev), aux=torch.empty(1, **f32),
-        z=torch.empty(1, **f32), workspace=torch.empty(ws, dtype=torch.uint8, device=dev))
+        z=torch.empty(1, **f32), workspace=torch.empty(ws, dtype=torch.uint8, device=dev),
+        saved=torch.empty((A, 3 * f), dtype=dt, device=dev) if save else None,
+        saved_shared=(torch.empty((T, 3 * f), dtype=dt, device=dev)
+                      if save and cfg.n_shared else None))
 
 
 def route(cfg, inp, b, logits_in=False, stream=None):
@@ -71,12 +80,20 @@ def dispatch(cfg, b, stream=None):
 
 def experts(cfg, inp, b, stream=None):
     code = lm.MOE_F32 if cfg.dtype == "fp32" else lm.MOE_BF16
-    lm.expert_ffn(inp.x, b.perm, b.offsets, cfg.T, cfg.d, cfg.d_ff, cfg.E, cfg.k, inp.w1, inp.w3,
-                  inp.w2, code, b.expert_out, b.workspace, stream)
+    if b.saved is not None:
+        lm.expert_ffn_save(inp.x, b.perm, b.offsets, cfg.T, cfg.d, cfg.d_ff, cfg.E, cfg.k, inp.w1,
+                           inp.w3, inp.w2, code, b.expert_out, b.saved, b.workspace, stream)
+    else:
+        lm.expert_ffn(inp.x, b.perm, b.offsets, cfg.T, cfg.d, cfg.d_ff, cfg.E, cfg.k, inp.w1,
+                      inp.w3, inp.w2, code, b.expert_out, b.workspace, stream)
     if cfg.n_shared:
         w1s, w3s, w2s = inp.shared
-        lm.expert_ffn(inp.x, None, None, cfg.T, cfg.d, cfg.d_ff, 1, 1, w1s, w3s, w2s, code,
-                      b.shared_out, b.workspace, stream)
+        if b.saved_shared is not None:
+            lm.expert_ffn_save(inp.x, None, None, cfg.T, cfg.d, cfg.d_ff, 1, 1, w1s, w3s, w2s,
+                               code, b.shared_out, b.saved_shared, b.workspace, stream)
+        else:
+            lm.expert_ffn(inp.x, None, None, cfg.T, cfg.d, cfg.d_ff, 1, 1, w1s, w3s, w2s, code,
+                          b.shared_out, b.workspace, stream)
 
 
 def combine(cfg, b, stream=None):
@@ -142,17 +159,28 @@ def alloc_grads(cfg, device="cuda"):
 def backward(cfg, inp, b, dy, g, stream=None):
     """Gradient of <dy, y> + aux + z after forward(cfg, inp, b): the steps in reverse order
     (Combine, Compute of the routed and shared experts, Score and Balance), then the input
-    gradient rows added per token.  No host synchronisation inside."""
+    gradient rows added per token.  With saved activations (alloc_buffers(save=True)) the
+    expert gradients read them instead of recomputing the up projection.  No host
+    synchronisation inside."""
     T, d, f, E, k = cfg.T, cfg.d, cfg.d_ff, cfg.E, cfg.k
     bf = lm.MOE_BF16
     lm.combine_backward(dy, b.expert_out, b.inv, b.topk_gate, T, d, k, bf, g.d_out, g.d_gate,
                         stream)
-    lm.expert_backward(inp.x, b.perm, b.offsets, T, d, f, E, k, inp.w1, inp.w3, inp.w2, g.d_out,
-                       bf, g.dx_rows, g.dw1, g.dw3, g.dw2, g.workspace, stream)
+    if b.saved is not None:
+        lm.expert_backward_saved(b.saved, inp.x, b.perm, b.offsets, T, d, f, E, k, inp.w1,
+                                 inp.w3, inp.w2, g.d_out, bf, g.dx_rows, g.dw1, g.dw3, g.dw2,
+                                 g.workspace, stream)
+    else:
+        lm.expert_backward(inp.x, b.perm, b.offsets, T, d, f, E, k, inp.w1, inp.w3, inp.w2,
+                           g.d_out, bf, g.dx_rows, g.dw1, g.dw3, g.dw2, g.workspace, stream)
     if cfg.n_shared:
         w1s, w3s, w2s = inp.shared
-        lm.expert_backward(inp.x, None, None, T, d, f, 1, 1, w1s, w3s, w2s, dy, bf, g.dx_shared,
-                           *g.dshared, g.workspace, stream)
+        if b.saved_shared is not None:
+            lm.expert_backward_saved(b.saved_shared, inp.x, None, None, T, d, f, 1, 1, w1s, w3s,
+                                     w2s, dy, bf, g.dx_shared, *g.dshared, g.workspace, stream)
+        else:
+            lm.expert_backward(inp.x, None, None, T, d, f, 1, 1, w1s, w3s, w2s, dy, bf,
+                               g.dx_shared, *g.dshared, g.workspace, stream)
     lm.route_backward(inp.x, inp.w_r, b.logits, b.topk_idx, b.topk_gate, g.d_gate, b.counts, T, d,
                       E, k, bf, GATING_CODE[cfg.gating], cfg.alpha, cfg.beta, g.dx_shared,
                       g.d_logits, g.dw_r, g.dx_route, g.workspace, stream)

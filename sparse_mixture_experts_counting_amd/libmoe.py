@@ -26,7 +26,8 @@ EXPORTS = ("moe_workspace_bytes", "moe_status_str", "moe_route", "moe_dispatch",
            "moe_update_select_bias", "moe_transpose", "moe_backward_workspace_bytes",
            "moe_combine_backward", "moe_expert_backward", "moe_route_backward",
            "moe_expert_choice", "moe_gathered_workspace_bytes", "moe_expert_ffn_gathered",
-           "moe_reroute", "moe_q_workspace_bytes", "moe_quantize_weights", "moe_expert_ffn_q")
+           "moe_reroute", "moe_q_workspace_bytes", "moe_quantize_weights", "moe_expert_ffn_q",
+           "moe_expert_ffn_save", "moe_expert_backward_saved")
 
 
 class MoEError(RuntimeError):
@@ -49,6 +50,10 @@ _lib.moe_route.argtypes = [_p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _u, _p, _p, _
                           _p]
 _lib.moe_dispatch.argtypes = [_p, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _sz, _p]
 _lib.moe_expert_ffn.argtypes = [_p, _p, _p, _i, _i, _i, _i, _i, _p, _p, _p, _i, _p, _p, _sz, _p]
+_lib.moe_expert_ffn_save.argtypes = [_p, _p, _p, _i, _i, _i, _i, _i, _p, _p, _p, _i, _p, _p, _p,
+                                     _sz, _p]
+_lib.moe_expert_backward_saved.argtypes = [_p, _p, _p, _p, _i, _i, _i, _i, _i, _p, _p, _p, _p, _i,
+                                           _p, _p, _p, _p, _p, _sz, _p]
 _lib.moe_expert_up.argtypes = [_p, _p, _p, _i, _i, _i, _i, _i, _p, _p, _i, _p, _p, _sz, _p]
 _lib.moe_expert_down.argtypes = [_p, _p, _i, _i, _i, _i, _i, _p, _i, _p, _p, _sz, _p]
 _lib.moe_combine.argtypes = [_p, _p, _p, _i, _i, _i, _i, _p, _p, _p]
@@ -149,6 +154,13 @@ def expert_ffn(x, perm, offsets, T, d, d_ff, E, k, w1, w3, w2, dt, out, workspac
         _ptr(out), _ptr(workspace), _nbytes(workspace), _stream(stream)))
 
 
+def expert_ffn_save(x, perm, offsets, T, d, d_ff, E, k, w1, w3, w2, dt, out, saved, workspace,
+                    stream=None):
+    _check("moe_expert_ffn_save", _lib.moe_expert_ffn_save(
+        _ptr(x), _ptr(perm), _ptr(offsets), T, d, d_ff, E, k, _ptr(w1), _ptr(w3), _ptr(w2), dt,
+        _ptr(out), _ptr(saved), _ptr(workspace), _nbytes(workspace), _stream(stream)))
+
+
 def expert_up(x, perm, offsets, T, d, d_ff, E, k, w1, w3, dt, h, workspace, stream=None):
     _check("moe_expert_up", _lib.moe_expert_up(
         _ptr(x), _ptr(perm), _ptr(offsets), T, d, d_ff, E, k, _ptr(w1), _ptr(w3), dt, _ptr(h),
@@ -201,6 +213,14 @@ def expert_backward(x, perm, offsets, T, d, d_ff, E, k, w1, w3, w2, d_out, dt, d
         _ptr(x), _ptr(perm), _ptr(offsets), T, d, d_ff, E, k, _ptr(w1), _ptr(w3), _ptr(w2),
         _ptr(d_out), dt, _ptr(dx_rows), _ptr(dw1), _ptr(dw3), _ptr(dw2), _ptr(workspace),
         _nbytes(workspace), _stream(stream)))
+
+
+def expert_backward_saved(saved, x, perm, offsets, T, d, d_ff, E, k, w1, w3, w2, d_out, dt,
+                          dx_rows, dw1, dw3, dw2, workspace, stream=None):
+    _check("moe_expert_backward_saved", _lib.moe_expert_backward_saved(
+        _ptr(saved), _ptr(x), _ptr(perm), _ptr(offsets), T, d, d_ff, E, k, _ptr(w1), _ptr(w3),
+        _ptr(w2), _ptr(d_out), dt, _ptr(dx_rows), _ptr(dw1), _ptr(dw3), _ptr(dw2),
+        _ptr(workspace), _nbytes(workspace), _stream(stream)))
 
 
 def route_backward(x, w_r, logits, topk_idx, topk_gate, d_gate, counts, T, d, E, k, dt, gating,

@@ -34,7 +34,8 @@ def test_every_declared_symbol_is_exported(lm):
                           "moe_expert_backward", "moe_route_backward", "moe_expert_choice",
                           "moe_gathered_workspace_bytes", "moe_expert_ffn_gathered",
                           "moe_reroute", "moe_q_workspace_bytes", "moe_quantize_weights",
-                          "moe_expert_ffn_q"}
+                          "moe_expert_ffn_q", "moe_expert_ffn_save",
+                          "moe_expert_backward_saved"}
     lib = ctypes.CDLL(lm.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n

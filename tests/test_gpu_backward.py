@@ -50,12 +50,12 @@ def _cuda(inp):
     return type(inp)(**kw)
 
 
-def _run(M, cfg, seed, zero_dy=False):
+def _run(M, cfg, seed, zero_dy=False, save=False):
     inp = _cuda(M["synth"].make_inputs(cfg, seed=seed, device="cpu"))
     dy = M["synth"].make_dy(cfg, seed=seed, device="cpu").cuda()
     if zero_dy:
         dy.zero_()
-    b = M["layer"].alloc_buffers(cfg)
+    b = M["layer"].alloc_buffers(cfg, save=save)
     g = M["layer"].alloc_grads(cfg)
     M["layer"].forward(cfg, inp, b)
     M["layer"].backward(cfg, inp, b, dy, g)
@@ -63,8 +63,8 @@ def _run(M, cfg, seed, zero_dy=False):
     return inp, dy, b, g
 
 
-def _check_case(M, cfg, seed=1, zero_dy=False):
-    inp, dy, b, g = _run(M, cfg, seed, zero_dy)
+def _check_case(M, cfg, seed=1, zero_dy=False, save=False):
+    inp, dy, b, g = _run(M, cfg, seed, zero_dy, save)
     h = P.host_inputs(inp)
     mode = P.GATE_CODE[cfg.gating]
     T, k = cfg.T, cfg.k
@@ -174,3 +174,73 @@ def test_backward_deterministic(M):
     _, _, _, g2 = _run(M, cfg, 3)
     for n, v in snap.items():
         assert torch.equal(v, getattr(g2, n)), n
+
+
+# Saved activations (moe_expert_ffn_save + moe_expert_backward_saved): weights as stored and as
+# transposed copies (d_ff % 64), split-K decode shapes, the two-stream tall/short tiling, shared
+# experts, capacity drops.
+SAVED_CASES = [
+    (37, 64, 4, 2, 96, "softmax_topk", 0, 0, 0.0),
+    (257, 136, 8, 2, 264, "softmax_all", 70, 0, 0.0),
+    (20, 64, 16, 1, 64, "softmax_topk", 0, 0, 1.5),
+    (700, 256, 4, 2, 512, "softmax_topk", 0, 0, 1.1),
+    (1500, 128, 8, 2, 320, "sigmoid_topk", 0, 1, 1.3),
+    (2048, 256, 4, 1, 512, "softmax_topk", 0, 1, 0.0),
+]
+
+
+def _silu(a):
+    return a / (1.0 + np.exp(-a))
+
+
+def _check_saved(saved, x_rows, w1, w3, bounds, f):
+    """saved [n][3f] = h | a | b of each row against float64 products of the same bf16 inputs:
+    a and b within their bf16 rounding, h within the rounding of the fp32 path."""
+    sv = P.np32(saved)[:bounds[-1]].astype(np.float64)
+    a = np.zeros((bounds[-1], f))
+    b = np.zeros((bounds[-1], f))
+    for e in range(len(bounds) - 1):
+        r0, r1 = bounds[e], bounds[e + 1]
+        a[r0:r1] = x_rows[r0:r1] @ w1[e].T
+        b[r0:r1] = x_rows[r0:r1] @ w3[e].T
+    assert P.rel_err(sv[:, f:2 * f], a) <= 4e-3, "saved a"
+    assert P.rel_err(sv[:, 2 * f:], b) <= 4e-3, "saved b"
+    assert P.rel_err(sv[:, :f], _silu(a) * b) <= 4e-3, "saved h"
+
+
+@pytest.mark.parametrize("case", SAVED_CASES, ids=lambda c: "T%d_d%d_E%d_k%d_f%d_%s_C%d_s%d" % c[:8])
+def test_backward_saved_parity(M, case):
+    T, d, E, k, f, gating, C, sh, zipf = case
+    _say("backward from saved activations", case)
+    cfg = M["synth"].tiny_config(T, d, E, k, f, "bf16", gating, capacity=C, n_shared=sh,
+                                 zipf_s=zipf)
+    # Every gradient against the oracle, end to end and per kernel.
+    inp, dy, b, g, ref = _check_case(M, cfg, save=True)
+    # The saving forward gives the same outputs as the plain one, bit for bit.
+    b0 = M["layer"].alloc_buffers(cfg)
+    M["layer"].forward(cfg, inp, b0)
+    torch.cuda.synchronize()
+    n = int(P.npi(b.offsets)[-1])
+    assert torch.equal(b.expert_out[:n], b0.expert_out[:n])
+    assert torch.equal(b.y, b0.y)
+    if sh:
+        assert torch.equal(b.shared_out, b0.shared_out)
+    # The saved rows themselves.
+    h = P.host_inputs(inp)
+    x = h["x"].astype(np.float64)
+    perm = P.npi(b.perm)[:n]
+    bounds = P.npi(b.offsets)
+    _check_saved(b.saved, x[perm // k], h["w1"].astype(np.float64), h["w3"].astype(np.float64),
+                 bounds, f)
+    if sh:
+        w1s, w3s, _ = h["shared"]
+        _check_saved(b.saved_shared, x, w1s[None].astype(np.float64),
+                     w3s[None].astype(np.float64), np.array([0, T]), f)
+    # Against the recomputing backward on the same inputs: only the bf16 rounding of a and b
+    # separates the two.
+    g0 = M["layer"].alloc_grads(cfg)
+    M["layer"].backward(cfg, inp, b0, dy, g0)
+    torch.cuda.synchronize()
+    for name in ("dx", "dw1", "dw3", "dw2", "dw_r", "d_logits"):
+        e_ = P.rel_err(P.np32(getattr(g, name)), P.np32(getattr(g0, name)))
+        assert e_ <= 1e-2, "%s saved vs recomputed %.3e" % (name, e_)

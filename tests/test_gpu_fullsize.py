@@ -98,16 +98,18 @@ def test_full_size_workload(M, name):
 BWD_TOL = 2e-2   # the GPU rounds dh, h, da and db to bf16 (as the small-size backward tests)
 
 
+@pytest.mark.parametrize("save", [False, True], ids=["recomputed", "saved"])
 @pytest.mark.parametrize("name", ["mixtral_decode", "mixtral_prefill", "deepseek_fine"])
-def test_full_size_expert_backward(M, name):
-    """moe_expert_backward at the full sizes, as the training benchmark runs it: the input
+def test_full_size_expert_backward(M, name, save):
+    """moe_expert_backward (save=False) and moe_expert_backward_saved after moe_expert_ffn_save
+    (save=True, as the training benchmark runs it) at the full sizes: the input
     gradient of sampled expert rows (full d_ff) and sampled rows / columns of the weight gradients
     of a few experts (all their rows; SwiGLU acts per d_ff index, so restricting d_ff is exact),
     against the oracle fed the GPU's own d_out.  Experts without rows get zero gradients."""
-    print("full-size backward", name, flush=True)
+    print("full-size backward", name, "saved" if save else "recomputed", flush=True)
     cfg = M["synth"].CONFIGS[name]
     inp = M["synth"].make_inputs(cfg, seed=0, device="cuda")
-    b = M["layer"].alloc_buffers(cfg)
+    b = M["layer"].alloc_buffers(cfg, save=save)
     M["layer"].forward(cfg, inp, b)
     dy = M["synth"].make_dy(cfg, seed=0, device="cuda")
     g = M["layer"].alloc_grads(cfg)

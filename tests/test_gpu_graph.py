@@ -40,15 +40,16 @@ def _snapshot(b, g=None):
     return out
 
 
+@pytest.mark.parametrize("save", [False, True], ids=["recomputed", "saved"])
 @pytest.mark.parametrize("case", CASES, ids=lambda c: "T%d_d%d_E%d_k%d_f%d_%s_C%d_s%d" % c[:8])
-def test_graph_replay_matches_eager(M, case):
+def test_graph_replay_matches_eager(M, case, save):
     T, d, E, k, f, gating, C, sh, zipf = case
-    print("graph", case, flush=True)
+    print("graph", case, "saved" if save else "recomputed", flush=True)
     L, S = M["layer"], M["synth"]
     cfg = S.tiny_config(T, d, E, k, f, "bf16", gating, capacity=C, n_shared=sh, zipf_s=zipf)
     inp = S.make_inputs(cfg, seed=3, device="cuda")
     dy = S.make_dy(cfg, seed=3, device="cuda")
-    b = L.alloc_buffers(cfg)
+    b = L.alloc_buffers(cfg, save=save)
     g = L.alloc_grads(cfg)
 
     def step():
