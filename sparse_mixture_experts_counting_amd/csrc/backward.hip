@@ -209,15 +209,17 @@ void launch_router_wgrad(const void* x, bool bf16, const float* dL, int T, int d
 }
 
 // dx = d_logits W_r (+ add): block (j-tile of 256 columns, 32 tokens); d_logits rows of the
-// tokens staged in LDS 256 experts at a time; fp32 sums, rounded once.
+// tokens staged in LDS 256 experts at a time, expert-major (the 32 tokens' values of one expert
+// contiguous, read as eight 16-byte broadcasts per 32 FMAs; rows padded to 36 floats against bank
+// conflicts of the staging writes); fp32 sums in expert order, rounded once.
 template <bool BF16>
 __global__ __launch_bounds__(256) void router_xgrad_kernel(const float* __restrict__ dL,
                                                            const void* __restrict__ w_r, int T,
                                                            int d, int E,
                                                            const void* __restrict__ add,
                                                            void* __restrict__ dx) {
-  constexpr int TT = 32, EC = 256;
-  __shared__ float sd[TT][EC];
+  constexpr int TT = 32, EC = 256, TP = TT + 4;
+  __shared__ __align__(16) float sd[EC][TP];
   const int j = blockIdx.x * 256 + threadIdx.x;
   const int t0 = blockIdx.y * TT;
   float acc[TT];
@@ -227,7 +229,7 @@ __global__ __launch_bounds__(256) void router_xgrad_kernel(const float* __restri
     __syncthreads();
     for (int q = threadIdx.x; q < TT * EC; q += 256) {
       const int tt = q / EC, ee = q % EC;
-      sd[tt][ee] = (t0 + tt < T && e0 + ee < E) ? dL[(size_t)(t0 + tt) * E + e0 + ee] : 0.f;
+      sd[ee][tt] = (t0 + tt < T && e0 + ee < E) ? dL[(size_t)(t0 + tt) * E + e0 + ee] : 0.f;
     }
     __syncthreads();
     if (j < d) {
@@ -235,8 +237,15 @@ __global__ __launch_bounds__(256) void router_xgrad_kernel(const float* __restri
       for (int ee = 0; ee < ne; ++ee) {
         const size_t o = (size_t)(e0 + ee) * d + j;
         const float w = BF16 ? bf16_to_f32(((const uint16_t*)w_r)[o]) : ((const float*)w_r)[o];
+        const f32x4* col = reinterpret_cast<const f32x4*>(sd[ee]);
 #pragma unroll
-        for (int i = 0; i < TT; ++i) acc[i] = fmaf(sd[i][ee], w, acc[i]);
+        for (int i4 = 0; i4 < TT / 4; ++i4) {
+          const f32x4 v = col[i4];
+          acc[4 * i4 + 0] = fmaf(v[0], w, acc[4 * i4 + 0]);
+          acc[4 * i4 + 1] = fmaf(v[1], w, acc[4 * i4 + 1]);
+          acc[4 * i4 + 2] = fmaf(v[2], w, acc[4 * i4 + 2]);
+          acc[4 * i4 + 3] = fmaf(v[3], w, acc[4 * i4 + 3]);
+        }
       }
     }
   }
