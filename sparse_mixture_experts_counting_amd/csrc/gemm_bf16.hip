@@ -539,6 +539,19 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_bf16_kernel(const G
     }
   };
   auto read_frags = [&](int stage_off, int ks, int buf) { read_frags2(stage_off, stage_off, ks, buf); };
+  // One LDS read after each matrix instruction of a slice (the scheduler otherwise keeps the
+  // slice's reads in one burst ahead of its matrix instructions).
+  constexpr int NRD = (AT ? 2 * TM : TM) + (BT ? 2 * TN : NMAT * TN);
+  constexpr int NMF = TM * NMAT * TN;
+  auto interleave = [&]() {
+#pragma unroll
+    for (int q = 0; q < (NRD < NMF ? NRD : NMF); ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    if constexpr (NMF > NRD) __builtin_amdgcn_sched_group_barrier(0x008, NMF - NRD, 0);
+    if constexpr (NRD > NMF) __builtin_amdgcn_sched_group_barrier(0x100, NRD - NMF, 0);
+  };
   auto mfmas = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < TM; ++i)
@@ -585,8 +598,8 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_bf16_kernel(const G
 #pragma unroll
           for (int ks = 0; ks < KS - 1; ++ks) {
             read_frags2(sa * A_BYTES, b_at(sb), ks + 1, (ks + 1) & 1);
-            __builtin_amdgcn_sched_barrier(0);
             mfmas(ks & 1);
+            interleave();
             __builtin_amdgcn_sched_barrier(0);
           }
         }
@@ -594,8 +607,8 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_bf16_kernel(const G
         barrier_no_fence();
         if constexpr (math) {
           read_frags2(na * A_BYTES, b_at(nb), 0, 0);
-          __builtin_amdgcn_sched_barrier(0);
           mfmas((KS - 1) & 1);
+          interleave();
           __builtin_amdgcn_sched_barrier(0);
         }
         sa = na;
@@ -620,8 +633,8 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_bf16_kernel(const G
 #pragma unroll
           for (int ks = 0; ks < KS - 1; ++ks) {
             read_frags(st * STAGE, ks + 1, (ks + 1) & 1);
-            __builtin_amdgcn_sched_barrier(0);
             mfmas(ks & 1);
+            interleave();
             __builtin_amdgcn_sched_barrier(0);
           }
         }
@@ -629,8 +642,8 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_bf16_kernel(const G
         barrier_no_fence();
         if constexpr (math) {
           read_frags(nx * STAGE, 0, 0);
-          __builtin_amdgcn_sched_barrier(0);
           mfmas((KS - 1) & 1);
+          interleave();
           __builtin_amdgcn_sched_barrier(0);
         }
         st = nx;
@@ -669,8 +682,8 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_bf16_kernel(const G
 #pragma unroll
           for (int ks = 0; ks < KS - 1; ++ks) {
             read_frags(st, ks + 1, (ks + 1) & 1);
-            __builtin_amdgcn_sched_barrier(0);
             mfmas(ks & 1);
+            interleave();
             __builtin_amdgcn_sched_barrier(0);
           }
         }
@@ -678,8 +691,8 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_bf16_kernel(const G
         barrier_no_fence();
         if constexpr (math) {
           read_frags(nx, 0, 0);
-          __builtin_amdgcn_sched_barrier(0);
           mfmas((KS - 1) & 1);
+          interleave();
           __builtin_amdgcn_sched_barrier(0);
         }
       };
