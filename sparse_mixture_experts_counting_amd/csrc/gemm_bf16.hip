@@ -539,18 +539,25 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_bf16_kernel(const G
     }
   };
   auto read_frags = [&](int stage_off, int ks, int buf) { read_frags2(stage_off, stage_off, ks, buf); };
-  // One LDS read after each matrix instruction of a slice (the scheduler otherwise keeps the
-  // slice's reads in one burst ahead of its matrix instructions).
+  // The slice's LDS reads spread over its matrix instructions, ceil(reads / matrix instructions)
+  // after each (one for K-contiguous operands, two for the transposing reads of the weight
+  // gradients), rather than in one burst ahead of them.
   constexpr int NRD = (AT ? 2 * TM : TM) + (BT ? 2 * TN : NMAT * TN);
   constexpr int NMF = TM * NMAT * TN;
   auto interleave = [&]() {
+    constexpr int R = (NRD + NMF - 1) / NMF;
+    constexpr int P = NRD / R;
 #pragma unroll
-    for (int q = 0; q < (NRD < NMF ? NRD : NMF); ++q) {
+    for (int q = 0; q < P; ++q) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, R, 0);
     }
-    if constexpr (NMF > NRD) __builtin_amdgcn_sched_group_barrier(0x008, NMF - NRD, 0);
-    if constexpr (NRD > NMF) __builtin_amdgcn_sched_group_barrier(0x100, NRD - NMF, 0);
+    if constexpr (NRD - P * R > 0) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, NRD - P * R, 0);
+    }
+    constexpr int USED = P + (NRD - P * R > 0 ? 1 : 0);
+    if constexpr (NMF > USED) __builtin_amdgcn_sched_group_barrier(0x008, NMF - USED, 0);
   };
   auto mfmas = [&](int buf) {
 #pragma unroll
