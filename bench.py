@@ -65,13 +65,38 @@ def load_traffic(workload):
     return t.get("hbm_bytes_per_launch")
 
 
+def host_info():
+    """The host the CPU oracle runs on: CPU model, logical CPUs, the CPUs this process may use,
+    and the BLAS library NumPy calls with its thread count."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    from threadpoolctl import threadpool_info
+    blas = [p for p in threadpool_info() if p.get("user_api") == "blas"]
+    b = blas[0] if blas else {}
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        affinity = None
+    return {"cpu_model": model, "host_cpus": os.cpu_count(), "affinity_cpus": affinity,
+            "blas": ("%s %s, %s threading" % (b.get("internal_api"), b.get("version"),
+                                              b.get("threading_layer"))) if b else None,
+            "blas_threads": b.get("num_threads", 1)}
+
+
 def cpu_baseline(cfg, inp, n_tokens, repeats):
-    """The CPU oracle (float64 NumPy, as it stands) on the first n_tokens tokens of the same
-    workload (all of them when n_tokens <= 0), run `repeats` times.  Returns tokens/s, BLAS
-    threads used, a description of the sample and the seconds spent."""
+    """The CPU oracle as it stands on the first n_tokens tokens of the same workload (all of them
+    when n_tokens <= 0): `repeats` timed runs of its float32 pass (the same code with float32
+    working precision), then one float64 pass (the precision every correctness check uses) for
+    reference.  Returns the cpu_baseline object."""
     import numpy as np
     from oracle import moe_oracle as O
-    from threadpoolctl import threadpool_info
 
     n = cfg.T if n_tokens <= 0 else min(n_tokens, cfg.T)
     f = lambda t: t.detach().float().cpu().numpy()
@@ -89,16 +114,67 @@ def cpu_baseline(cfg, inp, n_tokens, repeats):
     cap = cfg.capacity
     if cap > 0:   # same capacity factor on the smaller batch
         cap = max(1, int(math.ceil(cap * n / cfg.T)))
-    t0 = time.perf_counter()
-    for _ in range(repeats):
+
+    def run():
         O.forward(x, w_r, w1, w3, w2, cfg.k, mode, capacity=cap, bias=bias, shared=shared,
                   alpha=cfg.alpha, beta=cfg.beta)
-    dt = time.perf_counter() - t0
-    threads = max([p.get("num_threads", 1) for p in threadpool_info()
-                   if p.get("user_api") == "blas"] or [1])
-    sample = ("first %d of %d tokens of %s, all steps of the layer, float64 NumPy oracle "
-              "(%d experts touched), %d runs" % (n, cfg.T, cfg.name, len(used), repeats))
-    return n * repeats / dt, threads, sample, dt
+
+    with O.working_precision(np.float32):
+        run()                                   # untimed first pass (page-in, BLAS start-up)
+        t0 = time.perf_counter()
+        for _ in range(repeats):
+            run()
+        secs32 = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    run()
+    secs64 = time.perf_counter() - t0
+    hi = host_info()
+    sample = ("first %d of %d tokens of %s, every step of the layer, %d experts touched; "
+              "float32 pass of the NumPy oracle, %d timed runs after one untimed"
+              % (n, cfg.T, cfg.name, len(used), repeats))
+    out = {"value": n * repeats / secs32, "unit": "tokens/s", "cores": hi["blas_threads"],
+           "kind": "oracle", "precision": "float32", "sample": sample, "seconds": secs32,
+           "float64_pass": {"value": n / secs64, "unit": "tokens/s", "seconds": secs64}}
+    out.update(hi)
+    return out
+
+
+def measured_peaks(torch, lm, dev):
+    """The chip's measured ceilings beside its published ones: a loop of bf16 32x32x16 matrix
+    instructions on random register operands (moe_peak_mfma) and a 1 GiB streaming copy
+    (moe_peak_copy), each the best of 10 launches timed with HIP events."""
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    g = torch.Generator(device=dev)
+    g.manual_seed(12345)
+    ops = torch.randn(2048, generator=g, device=dev).to(torch.bfloat16)
+    blocks, iters = 4 * cus, 2000
+    out = torch.empty(blocks * 512, dtype=torch.float32, device=dev)
+    flops = float(blocks) * 8 * iters * 8 * 32768
+    nbytes = 1 << 30
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(3)
+    dst = torch.empty_like(src)
+    stream = torch.cuda.current_stream(dev)
+
+    def best(fn):
+        times = []
+        for _ in range(11):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            b.synchronize()
+            times.append(a.elapsed_time(b))
+        return min(times[1:])
+
+    t_mfma = best(lambda: lm.peak_mfma(ops, blocks, iters, out))
+    t_copy = best(lambda: lm.peak_copy(src, dst, nbytes))
+    del src, dst
+    return {"mfma_bf16_tflops": flops / (t_mfma * 1e-3) / 1e12,
+            "copy_gbs": 2.0 * nbytes / (t_copy * 1e-3) / 1e9,
+            "published_bf16_tflops": PEAK_BF16_TFLOPS, "published_hbm_gbs": PEAK_HBM_GBS,
+            "how": "moe_peak_mfma: %d blocks x 8 waves x %d iterations of 8 independent "
+                   "32x32x16 bf16 instructions on random register operands; moe_peak_copy: 1 GiB "
+                   "copy, 16-byte loads and stores; best of 10 launches" % (blocks, iters)}
 
 
 def main():
@@ -112,6 +188,12 @@ def main():
                     help="tokens of the workload the CPU oracle runs on (0: all)")
     ap.add_argument("--cpu-repeats", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-peaks", action="store_true",
+                    help="skip the measured MFMA-loop and copy ceilings")
+    ap.add_argument("--cold", action="store_true",
+                    help="overwrite a 1 GiB buffer before every timed step (outside the step's "
+                         "events), so the step starts with caches holding none of its data; "
+                         "ms_per_step is then the mean of the steps' event times")
     ap.add_argument("--pass", dest="mode", choices=("forward", "train"), default="forward")
     ap.add_argument("--recompute", action="store_true",
                     help="--pass train: recompute the experts' up projection in the backward "
@@ -193,7 +275,10 @@ def main():
     calib_dst.copy_(calib_src)
     del calib_src, calib_dst
 
-    for _ in range(args.warmup):
+    scrub = torch.empty(1 << 30, dtype=torch.uint8, device=dev) if args.cold else None
+    for w in range(args.warmup):
+        if scrub is not None:
+            scrub.fill_(w & 0xff)
         step()
     torch.cuda.synchronize(dev)
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)]
@@ -201,16 +286,19 @@ def main():
     torch.cuda.synchronize(dev)
     t0 = time.perf_counter()
     for s in range(args.steps):
+        if scrub is not None:
+            scrub.fill_((s + 7) & 0xff)
         step(events[s])
     torch.cuda.synchronize(dev)
     wall = time.perf_counter() - t0
+    del scrub
 
     stage_ms = {}
     for j, name in enumerate(stages):
         stage_ms[name] = sum(events[s][j].elapsed_time(events[s][j + 1])
                              for s in range(args.steps)) / args.steps
     gpu_ms = sum(events[s][0].elapsed_time(events[s][-1]) for s in range(args.steps)) / args.steps
-    ms_per_step = wall * 1e3 / args.steps
+    ms_per_step = gpu_ms if args.cold else wall * 1e3 / args.steps
 
     counts = buf.counts.cpu().tolist()
     n_kept = int(buf.offsets[-1].item())
@@ -223,7 +311,17 @@ def main():
     layer_flops = 2.0 * T * d * E + 6.0 * d * f * (n_kept + T * cfg.n_shared)
     layer_bytes = sb * (3.0 * d * f * (touched + cfg.n_shared) + 2.0 * T * d + d * E)
     up_ms = stage_ms["expert_up"]
-    achieved = up_flops / (up_ms * 1e-3) / 1e12
+    # The up projection's bound: matrix cores when its FLOPs per byte of touched expert weights
+    # (w1 and w3) exceed the chip's ridge point (2.5 PFLOP/s / 8 TB/s), else the weight stream.
+    up_weight_bytes = 2.0 * sb * d * f * touched
+    if up_flops / max(up_weight_bytes, 1.0) >= PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9):
+        roof = {"bound": "mfma", "achieved": up_flops / (up_ms * 1e-3) / 1e12,
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s"}
+    else:   # algorithmic bytes: touched w1 and w3, the token rows read, h written
+        up_bytes = up_weight_bytes + sb * (T * d + n_kept * f)
+        roof = {"bound": "hbm", "achieved": up_bytes / (up_ms * 1e-3) / 1e9,
+                "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
     traffic = load_traffic(cfg.name)
     gg_ms = stage_ms["expert_up"] + stage_ms["expert_down"]
     result = {
@@ -242,11 +340,12 @@ def main():
                 "shapes, drawn on the device)",
         "config": {"workload": cfg.name, "T": T, "d": d, "E": E, "k": k, "d_ff": f,
                    "gating": cfg.gating, "capacity": cfg.capacity or None,
-                   "shared_experts": cfg.n_shared, "parallelism": "none (1 GPU)"},
-        "roofline": {"bound": "mfma",
-                     "kernel": "moe_expert_up: gemm_bf16_kernel (SwiGLU epilogue) + tail_finish_kernel",
-                     "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic},
+                   "shared_experts": cfg.n_shared, "parallelism": "none (1 GPU)",
+                   "cache": ("cold: a 1 GiB buffer overwritten before every step, outside its "
+                             "events" if args.cold else "warm: steps back to back")},
+        "roofline": dict(roof, kernel="moe_expert_up: the grouped GEMM with the SwiGLU epilogue "
+                                      "(and its split-K finish kernel, when launched)",
+                         traffic=traffic),
         "grouped_gemm": {"ms": gg_ms, "tflops": (up_flops + down_flops) / (gg_ms * 1e-3) / 1e12,
                          "frac_bf16_peak": (up_flops + down_flops) / (gg_ms * 1e-3) / 1e12
                          / PEAK_BF16_TFLOPS},
@@ -257,11 +356,12 @@ def main():
         "stage_ms": stage_ms,
     }
     del h
+    if not args.no_peaks:
+        log("bench: measuring the MFMA-loop and copy ceilings")
+        result["measured_peaks"] = measured_peaks(torch, lm, dev)
     if not args.no_cpu_baseline:
         log("bench: timing the CPU oracle on a sample")
-        v, threads, sample, secs = cpu_baseline(cfg, inp, args.cpu_sample_tokens, args.cpu_repeats)
-        result["cpu_baseline"] = {"value": v, "unit": "tokens/s", "cores": threads,
-                                  "kind": "oracle", "sample": sample, "seconds": secs}
+        result["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_sample_tokens, args.cpu_repeats)
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)
@@ -345,7 +445,6 @@ def expert_choice_bench(args, cfg, dev, torch, layer, lm, synth):
     }
     if not args.no_cpu_baseline:
         from oracle import moe_oracle as O
-        from threadpoolctl import threadpool_info
         n = args.cpu_sample_tokens if args.cpu_sample_tokens > 0 else 512
         fl = lambda t: t.detach().float().cpu().numpy()
         x, w_r = fl(inp.x[:n]), fl(inp.w_r)
@@ -355,13 +454,12 @@ def expert_choice_bench(args, cfg, dev, torch, layer, lm, synth):
         for _ in range(args.cpu_repeats):
             O.forward_expert_choice(x, w_r, w1, w3, w2, c_s)
         secs = time.perf_counter() - t1
-        threads = max([q.get("num_threads", 1) for q in threadpool_info()
-                       if q.get("user_api") == "blas"] or [1])
-        result["cpu_baseline"] = {
-            "value": n * args.cpu_repeats / secs, "unit": "tokens/s", "cores": threads,
-            "kind": "oracle", "seconds": secs,
+        hi = host_info()
+        result["cpu_baseline"] = dict({
+            "value": n * args.cpu_repeats / secs, "unit": "tokens/s", "cores": hi["blas_threads"],
+            "kind": "oracle", "precision": "float64", "seconds": secs,
             "sample": "first %d of %d tokens, expert choice with C = %d, float64 NumPy oracle, "
-                      "%d runs" % (n, T, c_s, args.cpu_repeats)}
+                      "%d runs" % (n, T, c_s, args.cpu_repeats)}, **hi)
     print(json.dumps(result), flush=True)
 
 
@@ -528,7 +626,6 @@ def cpu_baseline_train(cfg, inp, dy, n_tokens, repeats):
     """The CPU oracle's forward + backward (float64 NumPy, as it stands) on the first n_tokens
     tokens, `repeats` times.  Returns tokens/s, BLAS threads, the sample and the seconds spent."""
     from oracle import moe_oracle as O
-    from threadpoolctl import threadpool_info
 
     n = min(n_tokens, cfg.T)
     f = lambda t: t.detach().float().cpu().numpy()
@@ -542,11 +639,12 @@ def cpu_baseline_train(cfg, inp, dy, n_tokens, repeats):
         O.backward(x, w_r, w1, w3, w2, dyh, cfg.k, mode, capacity=cfg.capacity or None,
                    bias=bias, shared=shared, alpha=cfg.alpha, beta=cfg.beta)
     secs = time.perf_counter() - t0
-    threads = max([p.get("num_threads", 1) for p in threadpool_info()
-                   if p.get("user_api") == "blas"] or [1])
     sample = ("first %d of %d tokens of %s, forward + backward, float64 NumPy oracle, %d runs"
               % (n, cfg.T, cfg.name, repeats))
-    return n * repeats / secs, threads, sample, secs
+    hi = host_info()
+    return dict({"value": n * repeats / secs, "unit": "tokens/s", "cores": hi["blas_threads"],
+                 "kind": "oracle", "precision": "float64", "sample": sample, "seconds": secs},
+                **hi)
 
 
 def train_bench(args, cfg, dev, torch, layer, lm, synth):
@@ -652,9 +750,7 @@ def train_bench(args, cfg, dev, torch, layer, lm, synth):
     if not args.no_cpu_baseline:
         log("bench: timing the CPU oracle (forward + backward) on a sample")
         n = args.cpu_sample_tokens if args.cpu_sample_tokens > 0 else 256
-        v, threads, sample, secs = cpu_baseline_train(cfg, inp, dy, n, args.cpu_repeats)
-        result["cpu_baseline"] = {"value": v, "unit": "tokens/s", "cores": threads,
-                                  "kind": "oracle", "sample": sample, "seconds": secs}
+        result["cpu_baseline"] = cpu_baseline_train(cfg, inp, dy, n, args.cpu_repeats)
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)

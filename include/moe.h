@@ -16,9 +16,11 @@
  *     must stay valid until the work enqueued on `stream` has finished.
  *   - `stream` is a hipStream_t passed as void*; NULL means the default stream.  Every call only
  *     enqueues work ordered on that stream and returns.  (The expert products of groups averaging
- *     256 to 512 rows run part of their tiles on a second stream the library creates once per
- *     device, forked from `stream` and joined back to it with events inside the same call, so
- *     the work still completes in `stream` order.)
+ *     256 to 512 rows run part of their tiles on a second stream that the library creates for
+ *     each caller stream on that stream's first such call outside stream capture, forked from
+ *     `stream` and joined back to it with events inside the same call, so the work still
+ *     completes in `stream` order; a call on a stream being captured that has no such stream
+ *     yet runs both parts on `stream`.)
  *   - Outputs are fully overwritten (no accumulate-into semantics) and must not alias inputs.
  *   - Integers are int32, row-major everywhere.  T tokens, d model width, E routed experts, k
  *     experts per token, d_ff expert width; assignment a = t*k + s for slot s of token t.
@@ -98,6 +100,12 @@ const char* moe_status_str(moe_status s);
  * fp32; lse_sq_sum [1] fp32.
  * prob_sum and lse_sq_sum may be NULL.  Non-finite logits violate the precondition: routing is then
  * unspecified but memory-safe (indices stay in [0,E) and distinct within a row).
+ * workspace (16-byte aligned, ws_bytes long) is required when prob_sum or lse_sq_sum is given (it
+ * holds the per-block loss partials); it may be NULL otherwise.  When it is as large as
+ * moe_workspace_bytes() for the layer, the matrix-core router product (bf16, E > 16) also splits
+ * its reduction over d into fixed chunks there, summed in a fixed order (more blocks for a few
+ * thousand tokens); a smaller workspace runs it unsplit.  The logits of both forms lie within the
+ * same fp32 dot-product rounding bound; each form is bitwise deterministic.
  * Results are bitwise deterministic run to run.
  */
 moe_status moe_route(const void* x, const void* w_r, const float* logit_bias,
@@ -443,6 +451,23 @@ moe_status moe_route_backward(const void* x, const void* w_r, const float* logit
                               int k, moe_dtype dt, moe_gating gating, float alpha, float beta,
                               const void* dx_add, float* d_logits, float* dw_r, void* dx,
                               void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * Measured ceilings (not part of the layer): the benchmark reports them beside the published
+ * peaks of the chip.
+ *
+ * moe_peak_mfma runs `blocks` blocks of 8 waves; every wave issues iters * 8 bf16 32x32x16 matrix
+ * instructions (8 independent fp32 accumulators, operands held in registers), i.e.
+ * blocks * 8 * iters * 8 * 32768 FLOPs per call.  operands: 2048 bf16 values (16-byte aligned;
+ * two alternating operand sets, 64 lanes x 8 values each for A and B); out: blocks * 512 fp32
+ * sums of the accumulators (written so that no instruction is dead; the values carry no meaning).
+ *
+ * moe_peak_copy copies `bytes` (a multiple of 16, both pointers 16-byte aligned) from src to dst
+ * with 16-byte loads and stores: 2 * bytes of HBM traffic per call for buffers larger than the
+ * caches.  src and dst must not overlap.
+ */
+moe_status moe_peak_mfma(const void* operands, int blocks, int iters, float* out, void* stream);
+moe_status moe_peak_copy(const void* src, void* dst, size_t bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -66,8 +66,31 @@ SOFTMAX_ALL = 1    # softmax over all E logits, keep the selected probabilities 
 SIGMOID_TOPK = 2   # sigmoid affinities renormalised over the selected experts (DeepSeek-V3)
 
 
+# Working precision of the floating-point arithmetic: float64 (the default, what every check
+# uses).  The benchmark's CPU-baseline leg times the same code in float32 (working_precision).
+_WORK = [np.float64]
+
+
+class working_precision:
+    """Context manager: run the oracle's floating-point arithmetic in `dtype` (np.float32 or
+    np.float64) inside the block.  Only the benchmark's timing of a float32 pass uses it."""
+
+    def __init__(self, dtype):
+        self.dtype = np.dtype(dtype).type
+        self.prev = None
+
+    def __enter__(self):
+        self.prev = _WORK[0]
+        _WORK[0] = self.dtype
+        return self
+
+    def __exit__(self, *exc):
+        _WORK[0] = self.prev
+        return False
+
+
 def _f64(a):
-    return np.asarray(a, dtype=np.float64)
+    return np.asarray(a, dtype=_WORK[0])
 
 
 def router_logits(x, w_r, bias=None, exact=False):
@@ -136,7 +159,7 @@ def gate_weights(logits, idx, mode):
     L = _f64(logits)
     T, E = L.shape
     k = idx.shape[1]
-    g = np.empty((T, k), dtype=np.float64)
+    g = np.empty((T, k), dtype=_WORK[0])
     with np.errstate(over="ignore"):
         for t in range(T):
             row = L[t]
@@ -264,7 +287,7 @@ def expert_rows(x, perm, offsets, k, w1, w3, w2):
     """
     x = np.asarray(x)
     E = len(offsets) - 1
-    out = np.zeros((int(offsets[E]), x.shape[1]), dtype=np.float64)
+    out = np.zeros((int(offsets[E]), x.shape[1]), dtype=_WORK[0])
     for e in range(E):
         lo, hi = int(offsets[e]), int(offsets[e + 1])
         if hi > lo:
@@ -285,7 +308,7 @@ def combine(out_rows, inv, gate, T, k, shared_out=None):
         shared_out.shape[1] if shared_out is not None else 0)
     inv = np.asarray(inv).reshape(T, k)
     g = _f64(gate).reshape(T, k)
-    y = np.zeros((T, d), dtype=np.float64)
+    y = np.zeros((T, d), dtype=_WORK[0])
     for s in range(k):
         keep = inv[:, s] >= 0
         y[keep] += g[keep, s, None] * out_rows[inv[keep, s]]
@@ -373,8 +396,8 @@ def combine_backward(dy, out_rows, inv, gate, T, k):
     out_rows = _f64(out_rows)
     inv = np.asarray(inv).reshape(T, k)
     g = _f64(gate).reshape(T, k)
-    d_out = np.zeros(out_rows.shape, dtype=np.float64)
-    d_gate = np.zeros((T, k), dtype=np.float64)
+    d_out = np.zeros(out_rows.shape, dtype=_WORK[0])
+    d_gate = np.zeros((T, k), dtype=_WORK[0])
     for s in range(k):
         keep = inv[:, s] >= 0
         rows = inv[keep, s]
@@ -415,10 +438,10 @@ def expert_rows_backward(x, perm, offsets, k, w1, w3, w2, d_out):
     x = _f64(x)
     E = len(offsets) - 1
     dx = np.zeros_like(x)
-    dx_rows = np.zeros((int(offsets[E]), x.shape[1]), dtype=np.float64)
-    dw1 = np.zeros(np.shape(w1), dtype=np.float64)
-    dw3 = np.zeros(np.shape(w3), dtype=np.float64)
-    dw2 = np.zeros(np.shape(w2), dtype=np.float64)
+    dx_rows = np.zeros((int(offsets[E]), x.shape[1]), dtype=_WORK[0])
+    dw1 = np.zeros(np.shape(w1), dtype=_WORK[0])
+    dw3 = np.zeros(np.shape(w3), dtype=_WORK[0])
+    dw2 = np.zeros(np.shape(w2), dtype=_WORK[0])
     for e in range(E):
         lo, hi = int(offsets[e]), int(offsets[e + 1])
         if hi > lo:
@@ -439,7 +462,7 @@ def gate_backward(logits, idx, mode, d_gate):
     L = _f64(logits)
     T, E = L.shape
     dg_all = _f64(d_gate)
-    dL = np.zeros((T, E), dtype=np.float64)
+    dL = np.zeros((T, E), dtype=_WORK[0])
     with np.errstate(over="ignore"):
         for t in range(T):
             row, sel, dg = L[t], np.asarray(idx[t]), dg_all[t]
@@ -540,7 +563,7 @@ def expert_choice(scores, C):
     T, E = S.shape
     c = min(int(C), T)
     perm = np.empty(E * c, dtype=np.int32)
-    gate = np.empty(E * c, dtype=np.float64)
+    gate = np.empty(E * c, dtype=_WORK[0])
     slot = np.full((T, E), -1, dtype=np.int32)
     for e in range(E):
         col = S[:, e]
@@ -570,7 +593,7 @@ def forward_expert_choice(x, w_r, w1, w3, w2, C, bias=None, shared=None, logits=
     offsets, perm, gate, slot = expert_choice(S, C)
     E = S.shape[1]
     rows = expert_rows(x, perm, offsets, 1, w1, w3, w2)
-    y = np.zeros((T, x.shape[1]), dtype=np.float64)
+    y = np.zeros((T, x.shape[1]), dtype=_WORK[0])
     for e in range(E):
         for r in range(int(offsets[e]), int(offsets[e + 1])):
             y[perm[r]] += gate[r] * rows[r]

@@ -37,6 +37,7 @@
 #include "kernels.h"
 
 #include <algorithm>
+#include <atomic>
 #include <climits>
 #include <mutex>
 #include <type_traits>
@@ -1031,6 +1032,12 @@ __global__ __launch_bounds__(256) void splitk_finish_kernel(const GemmParams p) 
         s[m][4] += b[0]; s[m][5] += b[1]; s[m][6] += b[2]; s[m][7] += b[3];
       }
     }
+    if constexpr (EPI == EPI_STORE_F32_BIAS) {   // the router's fp32 logits (+ bias)
+      float* dst = (float*)p.C + (size_t)row * p.ldc + c0;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) dst[q] = s[0][q] + (p.bias ? p.bias[c0 + q] : 0.f);
+      continue;
+    }
     u32x4 o, oa, ob;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -1116,49 +1123,102 @@ __global__ __launch_bounds__(256) void tail_finish_kernel(const GemmParams p) {
   }
 }
 
+// Compute units of the current device, cached per device (0 when unknown).  Written at most once
+// per device with the same value, so concurrent first calls are harmless; atomics keep the reads
+// well defined.
 static int device_cus() {
-  static int cus[64] = {0};
+  static std::atomic<int> cus[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-  if (cus[dev] == 0) {
+  int c = cus[dev].load(std::memory_order_relaxed);
+  if (c == 0) {
     int n = 0;
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) n = 0;
-    cus[dev] = n > 0 ? n : -1;
+    c = n > 0 ? n : -1;
+    cus[dev].store(c, std::memory_order_relaxed);
   }
-  return cus[dev] > 0 ? cus[dev] : 0;
+  return c > 0 ? c : 0;
 }
 
-// A second stream per device for work that runs beside the caller's stream (created on first use,
-// default priority), and the two events that fork it from and join it back to the caller's stream.
-struct SideStream {
-  hipStream_t stream = nullptr;
-  hipEvent_t fork = nullptr, join = nullptr;
-  bool failed = false;
+// Side streams for work that runs beside a caller's stream.  Each (device, caller stream) pair
+// gets its own side stream (default priority, non-blocking) and a small ring of fork / join event
+// pairs, so two caller streams never share a side stream and a capture on one caller stream never
+// pulls in another caller's work.  Slots are created outside stream capture only (a call made
+// while its stream is capturing and that has no slot yet runs its parts one after the other on the
+// caller's stream) and live until the process ends.  A call whose stream is itself a side stream
+// does not fork again.  The mutex guards only the slot table; the launches run outside it.
+namespace {
+constexpr int kSideRing = 4;
+constexpr int kMaxSideSlots = 64;
+struct SideSlot {
+  int dev = -1;
+  hipStream_t caller = nullptr;
+  hipStream_t side = nullptr;
+  hipEvent_t fork[kSideRing] = {};
+  hipEvent_t join[kSideRing] = {};
+  unsigned next = 0;
 };
-static std::mutex g_side_mutex;
-static SideStream g_side[64];
+std::mutex g_side_mutex;
+SideSlot g_side[kMaxSideSlots];
+int g_side_used = 0;
+}  // namespace
 
-// Queues side(side_stream) after the work already queued on s, then main(s), then makes s wait for
-// the side work.  Returns false (queueing nothing) when no side stream could be made.
-template <typename FS, typename FM>
-static bool run_beside(hipStream_t s, FS&& side, FM&& main, hipError_t& err) {
+// Picks the side stream and the fork / join events for one call on stream s; false when the call
+// must not fork (no slot, a nested call, or creation failed).
+static bool side_slot(hipStream_t s, hipStream_t& side, hipEvent_t& fork, hipEvent_t& join) {
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return false;
+  if (hipGetDevice(&dev) != hipSuccess) return false;
   std::lock_guard<std::mutex> lock(g_side_mutex);
-  SideStream& ss = g_side[dev];
-  if (!ss.stream && !ss.failed) {
-    if (hipStreamCreateWithFlags(&ss.stream, hipStreamNonBlocking) != hipSuccess ||
-        hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming) != hipSuccess ||
-        hipEventCreateWithFlags(&ss.join, hipEventDisableTiming) != hipSuccess)
-      ss.failed = true;
+  SideSlot* slot = nullptr;
+  for (int i = 0; i < g_side_used; ++i) {
+    if (g_side[i].side == s) return false;             // already on a side stream
+    if (g_side[i].dev == dev && g_side[i].caller == s) slot = &g_side[i];
   }
-  if (ss.failed) return false;
-  if ((err = hipEventRecord(ss.fork, s)) != hipSuccess) return true;
-  if ((err = hipStreamWaitEvent(ss.stream, ss.fork, 0)) != hipSuccess) return true;
-  err = side(ss.stream);
-  const hipError_t e1 = hipEventRecord(ss.join, ss.stream);
-  const hipError_t e2 = main(s);
-  const hipError_t e3 = hipStreamWaitEvent(s, ss.join, 0);
+  if (!slot) {
+    if (g_side_used == kMaxSideSlots) return false;
+    // (The legacy default stream, NULL, is never captured.)
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (s != nullptr &&
+        (hipStreamIsCapturing(s, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone))
+      return false;
+    SideSlot fresh;
+    fresh.dev = dev;
+    fresh.caller = s;
+    bool ok = hipStreamCreateWithFlags(&fresh.side, hipStreamNonBlocking) == hipSuccess;
+    for (int i = 0; ok && i < kSideRing; ++i)
+      ok = hipEventCreateWithFlags(&fresh.fork[i], hipEventDisableTiming) == hipSuccess &&
+           hipEventCreateWithFlags(&fresh.join[i], hipEventDisableTiming) == hipSuccess;
+    if (!ok) {
+      for (int i = 0; i < kSideRing; ++i) {
+        if (fresh.fork[i]) (void)hipEventDestroy(fresh.fork[i]);
+        if (fresh.join[i]) (void)hipEventDestroy(fresh.join[i]);
+      }
+      if (fresh.side) (void)hipStreamDestroy(fresh.side);
+      return false;
+    }
+    g_side[g_side_used] = fresh;
+    slot = &g_side[g_side_used++];
+  }
+  const unsigned i = slot->next++ % kSideRing;
+  side = slot->side;
+  fork = slot->fork[i];
+  join = slot->join[i];
+  return true;
+}
+
+// Queues side(side stream) after the work already queued on s, then main(s), then makes s wait for
+// the side work.  Returns false (queueing nothing) when this call does not fork.
+template <typename FS, typename FM>
+static bool run_beside(hipStream_t s, FS&& side_fn, FM&& main_fn, hipError_t& err) {
+  hipStream_t side = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+  if (!side_slot(s, side, fork, join)) return false;
+  if ((err = hipEventRecord(fork, s)) != hipSuccess) return true;
+  if ((err = hipStreamWaitEvent(side, fork, 0)) != hipSuccess) return true;
+  err = side_fn(side);
+  const hipError_t e1 = hipEventRecord(join, side);
+  const hipError_t e2 = main_fn(s);
+  const hipError_t e3 = hipStreamWaitEvent(s, join, 0);
   if (err == hipSuccess) err = e1 != hipSuccess ? e1 : (e2 != hipSuccess ? e2 : e3);
   return true;
 }
@@ -1168,14 +1228,15 @@ template <int BM, int BN, int NMAT, int WGM, int WGN, int BK, int NST, int MINB,
 static hipError_t launch_t(const GemmParams& p, int rows_max, hipStream_t s) {
   auto kern = gemm_bf16_kernel<BM, BN, NMAT, WGM, WGN, BK, NST, MINB, EPI, TAIL, BT, AT>;
   const size_t lds = (size_t)lds_bytes<BM, BN, NMAT, BK, NST, MINB>();
-  static bool attr_set[64] = {};   // per device: the attribute is set on the current device
+  static std::atomic<bool> attr_set[64];   // per device: the attribute is set on that device
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-  if (!attr_set[dev]) {
+  if (!attr_set[dev].load(std::memory_order_acquire)) {
+    // Setting it twice (two threads' first calls) is harmless.
     hipError_t e = hipFuncSetAttribute((const void*)kern,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    attr_set[dev] = true;
+    attr_set[dev].store(true, std::memory_order_release);
   }
   GemmParams q = p;
   // The last partial round of tiles is split over K when the epilogue allows it (bf16 output, 8
@@ -1219,6 +1280,9 @@ static void launch_splitk_finish(const GemmParams& p, int rows_max, int epi, hip
   else if (epi == EPI_SWIGLU_SAVE)
     hipLaunchKernelGGL((splitk_finish_kernel<2, EPI_SWIGLU_SAVE>), dim3(fgrid), dim3(256), 0, s,
                        p);
+  else if (epi == EPI_STORE_F32_BIAS)
+    hipLaunchKernelGGL((splitk_finish_kernel<1, EPI_STORE_F32_BIAS>), dim3(fgrid), dim3(256), 0, s,
+                       p);
   else
     hipLaunchKernelGGL((splitk_finish_kernel<1, EPI_STORE>), dim3(fgrid), dim3(256), 0, s, p);
 }
@@ -1242,7 +1306,19 @@ static bool use_big_tiles(int rows_max, int G, bool grouped, int epi) {
 // least 90% busy on average, else the split that keeps them busiest (or, when no split fills a
 // round, the largest).
 static int splitk_factor(int rows_max, int G, bool grouped, int N, int K, int epi) {
-  if (epi == EPI_STORE_F32_BIAS || K % 64 != 0 || N % 8 != 0) return 1;
+  if (epi == EPI_STORE_F32_BIAS) {
+    // The router product (one dense group, fp32 logits): 128 x 256 tiles, two blocks per CU.  A
+    // few hundred tokens give too few tiles to cover the GPU, so K is split into the smallest
+    // power-of-two number of chunks (whole 64-deep steps, at most 8) whose blocks fill one round.
+    if (grouped || K % 64 != 0 || N % 8 != 0) return 1;
+    const long long tiles = (long long)((rows_max + 127) / 128) * ((N + 255) / 256);
+    const int cus = device_cus();
+    const long long slots = 2ll * (cus > 0 ? cus : 256);
+    int ks = 1;
+    while (ks < 8 && tiles * ks < slots && (K / 64) % (ks * 2) == 0) ks *= 2;
+    return ks;
+  }
+  if (K % 64 != 0 || N % 8 != 0) return 1;
   if (use_big_tiles(rows_max, G, grouped, epi)) return 1;
   const int BM = 128, BN = epi_swiglu(epi) ? 128 : 256;
   const int mt = grouped ? std::min(G, rows_max) + rows_max / BM : (rows_max + BM - 1) / BM;
@@ -1280,7 +1356,10 @@ static int splitk_factor(int rows_max, int G, bool grouped, int N, int K, int ep
 // round (at most one round of blocks, each a BM x BN tile of NMAT partials; 256 KB per CU for
 // every tile configuration used here).
 size_t gemm_bf16_partial_bytes(int rows_max, int G, bool grouped, int N, int K, int epi) {
-  if (epi == EPI_STORE_F32_BIAS) return 0;
+  if (epi == EPI_STORE_F32_BIAS) {
+    const int ks = splitk_factor(rows_max, G, grouped, N, K, epi);
+    return ks > 1 ? (size_t)ks * rows_max * N * sizeof(float) : 0;
+  }
   const int nmat = epi_swiglu(epi) ? 2 : 1;
   const int ks = splitk_factor(rows_max, G, grouped, N, K, epi);
   if (ks > 1) return (size_t)ks * nmat * rows_max * N * sizeof(float);
@@ -1319,8 +1398,8 @@ static hipError_t launch_cfg(const GemmParams& p, int rows_max, int epi, bool bi
                                                                                       s)
                  : launch_tail_or_not<128, 256, 1, 2, 2, 32, 3, 2, EPI_SWIGLU_BWD_SAVED>(p, rows_max,
                                                                                       s);
-    default:
-      return launch_tail_or_not<128, 256, 1, 2, 2, 32, 0, 1, EPI_STORE_F32_BIAS>(p, rows_max, s);
+    default:   // the router product: direct loads, two blocks per CU
+      return launch_tail_or_not<128, 256, 1, 2, 2, 32, 3, 2, EPI_STORE_F32_BIAS>(p, rows_max, s);
   }
 }
 

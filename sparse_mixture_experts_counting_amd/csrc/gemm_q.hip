@@ -23,6 +23,7 @@
 #include "kernels.h"
 
 #include <algorithm>
+#include <atomic>
 #include <climits>
 #include <type_traits>
 
@@ -344,14 +345,15 @@ static hipError_t launch_q_t(GemmParams p, int rows_max, const float* s0, const 
                              hipStream_t s) {
   auto kern = gemm_q_kernel<NMAT, EPI, BITS>;
   constexpr int lds = q_lds<NMAT, BITS>();
-  static bool attr_set[64] = {};   // per device: the attribute is set on the current device
+  static std::atomic<bool> attr_set[64];   // per device: the attribute is set on that device
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-  if (!attr_set[dev]) {
+  if (!attr_set[dev].load(std::memory_order_acquire)) {
+    // Setting it twice (two threads' first calls) is harmless.
     hipError_t e =
         hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (e != hipSuccess) return e;
-    attr_set[dev] = true;
+    attr_set[dev].store(true, std::memory_order_release);
   }
   const bool grouped = p.offsets != nullptr;
   p.ksplit = p.part ? gemm_q_split(rows_max, p.G, grouped, p.N, p.K, BITS) : 1;

@@ -84,4 +84,8 @@ void launch_expert_choice(const float* logits, int T, int E, int C, bool scores_
                           int32_t* offsets, int32_t* perm, float* gate, int32_t* slot,
                           hipStream_t s);
 
+// peak.hip (measurement only)
+void launch_peak_mfma(const void* operands, int blocks, int iters, float* out, hipStream_t s);
+void launch_peak_copy(const void* src, void* dst, size_t bytes, hipStream_t s);
+
 }  // namespace moe

@@ -37,6 +37,13 @@ size_t ffn_partial_bytes(int rows, bool grouped, int G, int d, int d_ff, moe_dty
   return align_up(up > dn ? up : dn);
 }
 
+// Split-K scratch of the router's matrix-core product (E > 16, bf16), placed after the gating
+// partials in moe_route's workspace.
+size_t router_partial_bytes(int T, int d, int E, moe_dtype dt) {
+  if (dt != MOE_BF16 || E <= 16 || E % 8 != 0 || d % 8 != 0) return 0;
+  return align_up(moe::gemm_bf16_partial_bytes(T, 1, false, E, d, moe::EPI_STORE_F32_BIAS));
+}
+
 size_t h_bytes(int rows, int d_ff, moe_dtype dt) {
   return align_up((size_t)rows * d_ff * elem_bytes(dt));
 }
@@ -97,7 +104,7 @@ const char* moe_status_str(moe_status s) {
 
 size_t moe_workspace_bytes(int T, int d, int d_ff, int E, int k, moe_dtype dt) {
   if (T < 1 || E < 1 || k < 1 || d_ff < 1 || d < 1) return 0;
-  size_t r = align_up(moe::route_workspace_bytes(T, E));
+  size_t r = align_up(moe::route_workspace_bytes(T, E)) + router_partial_bytes(T, d, E, dt);
   size_t q = align_up(moe::dispatch_workspace_bytes(T * k, E));
   const size_t rr = align_up(moe::reroute_workspace_bytes(T * k, E));
   q = q > rr ? q : rr;
@@ -134,12 +141,18 @@ moe_status moe_route(const void* x, const void* w_r, const float* logit_bias,
     if (!workspace) return MOE_ERR_ARG;
     if (ws_bytes < moe::route_workspace_bytes(T, E)) return MOE_ERR_WORKSPACE;
   }
+  if (workspace && !aligned16(workspace)) return MOE_ERR_ARG;
   hipStream_t s = (hipStream_t)stream;
   const bool bf16 = dt == MOE_BF16;
   if (!logits_in) {
     if (E <= 16) {
       moe::launch_router_small_e(x, w_r, logit_bias, T, d, E, bf16, logits, s);
     } else if (E % 8 == 0) {
+      // The matrix-core product splits K over the workspace past the gating partials when the
+      // workspace holds them (few tokens: too few tiles to cover the GPU); otherwise it runs
+      // unsplit.  Either way the fp32 sums are within the same rounding bound.
+      const size_t at = align_up(moe::route_workspace_bytes(T, E));
+      const size_t need = router_partial_bytes(T, d, E, dt);
       moe::GemmParams p{};
       p.A = x;
       p.a_rows = T;
@@ -151,6 +164,7 @@ moe_status moe_route(const void* x, const void* w_r, const float* logit_bias,
       p.ldc = E;
       p.bias = logit_bias;
       p.gather_div = 1;
+      if (need && workspace && ws_bytes >= at + need) p.part = (float*)((char*)workspace + at);
       hipError_t e = bf16 ? moe::launch_gemm_bf16(p, T, moe::EPI_STORE_F32_BIAS, s)
                           : moe::launch_gemm_f32(p, T, moe::EPI_STORE_F32_BIAS, s);
       if (e != hipSuccess) return MOE_ERR_DEVICE;
@@ -706,6 +720,24 @@ moe_status moe_route_backward(const void* x, const void* w_r, const float* logit
                             T, E, k, (int)gating, alpha, beta, d_logits, s);
   moe::launch_router_wgrad(x, bf16, d_logits, T, d, E, (float*)workspace, dw_r, s);
   moe::launch_router_xgrad(d_logits, w_r, bf16, T, d, E, dx_add, dx, s);
+  return launched();
+}
+
+}  // extern "C"
+
+extern "C" {
+
+moe_status moe_peak_mfma(const void* operands, int blocks, int iters, float* out, void* stream) {
+  if (!operands || !out || blocks < 1 || iters < 1) return MOE_ERR_ARG;
+  if (!aligned16(operands)) return MOE_ERR_ARG;
+  moe::launch_peak_mfma(operands, blocks, iters, out, (hipStream_t)stream);
+  return launched();
+}
+
+moe_status moe_peak_copy(const void* src, void* dst, size_t bytes, void* stream) {
+  if (!src || !dst || bytes < 16 || bytes % 16 != 0) return MOE_ERR_ARG;
+  if (!aligned16(src) || !aligned16(dst)) return MOE_ERR_ARG;
+  moe::launch_peak_copy(src, dst, bytes, (hipStream_t)stream);
   return launched();
 }
 

@@ -27,7 +27,8 @@ EXPORTS = ("moe_workspace_bytes", "moe_status_str", "moe_route", "moe_dispatch",
            "moe_combine_backward", "moe_expert_backward", "moe_route_backward",
            "moe_expert_choice", "moe_gathered_workspace_bytes", "moe_expert_ffn_gathered",
            "moe_reroute", "moe_q_workspace_bytes", "moe_quantize_weights", "moe_expert_ffn_q",
-           "moe_expert_ffn_save", "moe_expert_backward_saved")
+           "moe_expert_ffn_save", "moe_expert_backward_saved", "moe_peak_mfma",
+           "moe_peak_copy")
 
 
 class MoEError(RuntimeError):
@@ -79,7 +80,9 @@ _lib.moe_gathered_workspace_bytes.argtypes = [_i, _i, _i, _i, _i]
 _lib.moe_gathered_workspace_bytes.restype = _sz
 _lib.moe_expert_ffn_gathered.argtypes = [_p, _p, _p, _i, _i, _i, _i, _i, _p, _p, _p, _i, _p, _p,
                                          _sz, _p]
-for _n in ("moe_route", "moe_dispatch", "moe_expert_ffn", "moe_expert_up", "moe_expert_down",
+_lib.moe_peak_mfma.argtypes = [_p, _i, _i, _p, _p]
+_lib.moe_peak_copy.argtypes = [_p, _p, _sz, _p]
+for _n in ("moe_peak_mfma", "moe_peak_copy", "moe_route", "moe_dispatch", "moe_expert_ffn", "moe_expert_up", "moe_expert_down",
            "moe_combine", "moe_aux_loss", "moe_transpose", "moe_update_select_bias",
            "moe_combine_backward", "moe_expert_backward", "moe_route_backward",
            "moe_expert_choice", "moe_expert_ffn_gathered", "moe_reroute",
@@ -273,3 +276,12 @@ def expert_ffn_q(x, perm, offsets, T, d, d_ff, E, k, bits, q1, s1, q3, s3, q2, s
         _ptr(x), _ptr(perm), _ptr(offsets), T, d, d_ff, E, k, bits, _ptr(q1), _ptr(s1), _ptr(q3),
         _ptr(s3), _ptr(q2), _ptr(s2), dt, _ptr(out), _ptr(workspace), _nbytes(workspace),
         _stream(stream)))
+
+
+def peak_mfma(operands, blocks, iters, out, stream=None):
+    _check("moe_peak_mfma", _lib.moe_peak_mfma(_ptr(operands), blocks, iters, _ptr(out),
+                                               _stream(stream)))
+
+
+def peak_copy(src, dst, nbytes, stream=None):
+    _check("moe_peak_copy", _lib.moe_peak_copy(_ptr(src), _ptr(dst), nbytes, _stream(stream)))

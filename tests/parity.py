@@ -95,3 +95,12 @@ def check_losses(cfg, b, ref):
     z = float(np32(b.z)[0])
     assert math.isclose(aux, ref["aux"], rel_tol=1e-4), (aux, ref["aux"])
     assert math.isclose(z, ref["z"], rel_tol=1e-4, abs_tol=1e-12), (z, ref["z"])
+
+
+# Near-tie flips seen by the end-to-end parity checks: (case, tokens, flipped tokens).  The test
+# session prints them in its summary, so every run reports whether a certified flip occurred.
+FLIP_LOG = []
+
+
+def log_flips(case, T, n_flips):
+    FLIP_LOG.append((str(case), int(T), int(n_flips)))

@@ -35,7 +35,7 @@ def test_every_declared_symbol_is_exported(lm):
                           "moe_gathered_workspace_bytes", "moe_expert_ffn_gathered",
                           "moe_reroute", "moe_q_workspace_bytes", "moe_quantize_weights",
                           "moe_expert_ffn_q", "moe_expert_ffn_save",
-                          "moe_expert_backward_saved"}
+                          "moe_expert_backward_saved", "moe_peak_mfma", "moe_peak_copy"}
     lib = ctypes.CDLL(lm.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -252,3 +252,15 @@ def test_quantized_argument_errors(lm):
     assert L.moe_expert_ffn_q(*q(d=64)) == 2                                     # not 128k
     assert L.moe_expert_ffn_q(*q(wsb=16)) == 3
     assert lm.q_workspace_bytes(8, 128, 256, 4, 2, 8) >= 16 * 256 * 2
+
+
+def test_peak_argument_errors(lm):
+    L = lm.lib()
+    assert L.moe_peak_mfma(None, 4, 10, FAKE, None) == 1
+    assert L.moe_peak_mfma(FAKE, 0, 10, FAKE, None) == 1
+    assert L.moe_peak_mfma(FAKE, 4, 0, FAKE, None) == 1
+    assert L.moe_peak_mfma(FAKE + 4, 4, 10, FAKE, None) == 1      # operands not 16-byte aligned
+    assert L.moe_peak_copy(FAKE, FAKE, 0, None) == 1
+    assert L.moe_peak_copy(FAKE, FAKE, 40, None) == 1             # not a multiple of 16
+    assert L.moe_peak_copy(None, FAKE, 64, None) == 1
+    assert L.moe_peak_copy(FAKE + 8, FAKE, 64, None) == 1

@@ -2,9 +2,11 @@
 
 Serving loops capture a fixed-shape layer once and replay it.  Every entry point only enqueues
 work (no host synchronisation, no allocation, no memset); the grouped products of groups
-averaging 256-512 rows fork part of their tiles onto the library's side stream and join it back,
-which the capture must follow.  Each replay, with eager work and synchronisations in between,
-must reproduce the eager results bit for bit (the kernels are deterministic).
+averaging 256-512 rows fork part of their tiles onto the side stream the library keeps for the
+caller's stream and join it back, which the capture must follow (the warm-up runs on the capture
+stream itself, so that its side stream exists before the capture).  Each replay, with eager work
+and synchronisations in between, must reproduce the eager results bit for bit (the kernels are
+deterministic).
 """
 
 import pytest
@@ -56,19 +58,19 @@ def test_graph_replay_matches_eager(M, case, save):
         L.forward(cfg, inp, b)
         L.backward(cfg, inp, b, dy, g)
 
-    step()                                   # eager (also creates the library's side stream)
+    step()                                   # eager
     torch.cuda.synchronize()
     ref = _snapshot(b, g)
 
-    side = torch.cuda.Stream()
-    side.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(side):
-        step()                               # warm-up on the capture stream's side, as torch asks
-    torch.cuda.current_stream().wait_stream(side)
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap):
+        step()                               # warm-up on the capture stream (off the default
+    torch.cuda.current_stream().wait_stream(cap)   # stream, as torch asks)
     torch.cuda.synchronize()
 
     graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
+    with torch.cuda.graph(graph, stream=cap):
         step()
     torch.cuda.synchronize()
 
@@ -82,3 +84,30 @@ def test_graph_replay_matches_eager(M, case, save):
         got = _snapshot(b, g)
         for n, v in ref.items():
             assert torch.equal(got[n], v), "replay %d: %s differs from the eager run" % (replay, n)
+
+
+def test_two_caller_streams_concurrently(M):
+    """Two streams run the two-part tiling (tall and short tiles on each caller's own side stream)
+    at the same time on different buffers: each result is bit-identical to the same layer run
+    alone on the default stream."""
+    print("two caller streams", flush=True)
+    L, S = M["layer"], M["synth"]
+    cfg = S.tiny_config(700, 256, 4, 2, 512, "bf16", "softmax_topk", n_shared=1, zipf_s=1.1)
+    inps = [S.make_inputs(cfg, seed=s, device="cuda") for s in (5, 6)]
+    refs = []
+    for inp in inps:
+        b = L.alloc_buffers(cfg)
+        L.forward(cfg, inp, b)
+        torch.cuda.synchronize()
+        refs.append(b.y.clone())
+    bufs = [L.alloc_buffers(cfg) for _ in inps]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for st in streams:
+        st.wait_stream(torch.cuda.current_stream())
+    for rep in range(3):
+        for inp, b, st in zip(inps, bufs, streams):
+            with torch.cuda.stream(st):
+                L.forward(cfg, inp, b, stream=st)
+        torch.cuda.synchronize()
+        for b, ref in zip(bufs, refs):
+            assert torch.equal(b.y, ref), "repeat %d differs from the lone run" % rep

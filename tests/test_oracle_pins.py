@@ -581,3 +581,30 @@ def test_int4_pack_round_trip():
     b = O.pack_int4(q)
     assert b.shape == (4, 6, 16) and np.array_equal(O.unpack_int4(b), q)
     assert O.pack_int4(np.array([[-1, 7]], dtype=np.int8)).tolist() == [[0x7F]]
+
+
+def test_working_precision_float32_pass():
+    """The benchmark times the oracle's float32 pass: inside working_precision(float32) the same
+    code computes in float32 (y agrees with the float64 pass to float32 rounding, routing and
+    dispatch are identical on logits without near-ties), and float64 is restored afterwards, also
+    when the block raises."""
+    rng = np.random.default_rng(21)
+    T, d, E, k, f = 40, 24, 6, 2, 32
+    x = rng.normal(size=(T, d)).astype(np.float32)
+    w_r = rng.normal(size=(E, d)).astype(np.float32)
+    w1 = rng.normal(size=(E, f, d)).astype(np.float32) / np.sqrt(d)
+    w3 = rng.normal(size=(E, f, d)).astype(np.float32) / np.sqrt(d)
+    w2 = rng.normal(size=(E, d, f)).astype(np.float32) / np.sqrt(f)
+    ref = O.forward(x, w_r, w1, w3, w2, k, O.SOFTMAX_TOPK, capacity=12)
+    with O.working_precision(np.float32):
+        got = O.forward(x, w_r, w1, w3, w2, k, O.SOFTMAX_TOPK, capacity=12)
+    assert got["y"].dtype == np.float32 and ref["y"].dtype == np.float64
+    for key in ("topk_idx", "counts", "offsets", "perm", "inv"):
+        np.testing.assert_array_equal(got[key], ref[key])
+    assert got["n_dropped"] == ref["n_dropped"] > 0
+    err = np.max(np.abs(got["y"] - ref["y"])) / np.max(np.abs(ref["y"]))
+    assert 0 < err < 1e-5
+    with pytest.raises(ZeroDivisionError):
+        with O.working_precision(np.float32):
+            1 / 0
+    assert O.swiglu_ffn(x, w1[0], w3[0], w2[0]).dtype == np.float64
