@@ -40,11 +40,24 @@ __global__ __launch_bounds__(512) void peak_mfma_kernel(const uint16_t* __restri
   out[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = s;
 }
 
-// 16 bytes per lane per iteration, grid-stride; n16 counts 16-byte units.
+// Each lane copies 8 16-byte units per iteration (all 8 loads issued before the stores, so 128
+// bytes per lane are in flight), blocks striding over the buffer in 256 x 8-unit chunks; n16
+// counts 16-byte units, and a tail shorter than one chunk is copied unit by unit.
 __global__ __launch_bounds__(256) void peak_copy_kernel(const u32x4* __restrict__ src,
                                                         u32x4* __restrict__ dst, size_t n16) {
-  const size_t stride = (size_t)gridDim.x * 256;
-  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += stride) dst[i] = src[i];
+  constexpr int U = 8;
+  const size_t chunk = 256 * U;
+  const size_t full = n16 / chunk;
+  for (size_t c = blockIdx.x; c < full; c += gridDim.x) {
+    const size_t base = c * chunk + threadIdx.x;
+    u32x4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = __builtin_nontemporal_load(src + base + (size_t)u * 256);
+#pragma unroll
+    for (int u = 0; u < U; ++u) __builtin_nontemporal_store(v[u], dst + base + (size_t)u * 256);
+  }
+  if (blockIdx.x == 0)
+    for (size_t i = full * chunk + threadIdx.x; i < n16; i += 256) dst[i] = src[i];
 }
 
 void launch_peak_mfma(const void* operands, int blocks, int iters, float* out, hipStream_t s) {
@@ -59,9 +72,8 @@ void launch_peak_copy(const void* src, void* dst, size_t bytes, hipStream_t s) {
       cus <= 0)
     cus = 256;
   const size_t n16 = bytes / 16;
-  const size_t want = (n16 + 255) / 256;
+  const size_t want = std::max<size_t>(n16 / (256 * 8), 1);
   const int grid = (int)std::min<size_t>(want, (size_t)cus * 8);
-  if (grid > 0)
     hipLaunchKernelGGL(peak_copy_kernel, dim3(grid), dim3(256), 0, s, (const u32x4*)src,
                        (u32x4*)dst, n16);
 }
