@@ -136,6 +136,22 @@ moe_status moe_dispatch(const int32_t* topk_idx, int T, int E, int k, int capaci
                         int32_t* n_dropped, void* workspace, size_t ws_bytes, void* stream);
 
 /*
+ * moe_dispatch_noalloc -- moe_dispatch for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc): the same kernels and
+ * the same outputs, bit for bit, with the per-chunk histogram kept in a fixed 1 MiB device array
+ * inside the library instead of a caller's workspace.  It allocates and frees nothing (the array
+ * is part of the loaded library on every GPU it runs on, until the process ends); the first call
+ * on a device looks up that device's copy.  Limit: ceil(T*k / 2048) * E * 4 + 256 bytes must not
+ * exceed 1 MiB (about 522 k assignments at E = 1024, 2 M at E = 256), else MOE_ERR_UNSUPPORTED.
+ * Every call on one GPU shares that GPU's array: calls that overlap in time on one GPU (two
+ * streams, two threads) race and must be ordered by the caller.  Errors as moe_dispatch;
+ * MOE_ERR_DEVICE also when the array's device address cannot be looked up.
+ */
+moe_status moe_dispatch_noalloc(const int32_t* topk_idx, int T, int E, int k, int capacity,
+                                int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv,
+                                int32_t* n_dropped, void* stream);
+
+/*
  * moe_expert_ffn -- Compute (the tirogla page, How it works step 4: every expert runs its FFN on its
  * contiguous batch, as one grouped GEMM).  The expert is SwiGLU (the dineshblog page, section 1.1):
  *

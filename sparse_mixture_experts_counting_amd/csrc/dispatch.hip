@@ -13,6 +13,8 @@
 #include "common.h"
 #include "kernels.h"
 
+#include <mutex>
+
 namespace moe {
 
 static constexpr int kChunk = 2048;   // assignments per block
@@ -125,6 +127,32 @@ __global__ __launch_bounds__(kThreads) void dispatch_scatter_kernel(
 size_t dispatch_workspace_bytes(int A, int E) {
   const size_t nchunk = (size_t)(A + kChunk - 1) / kChunk;
   return nchunk * E * sizeof(int32_t) + 256;
+}
+
+// Scratch of the entry point that allocates nothing (moe_dispatch_noalloc): the per-chunk
+// histogram lives in this fixed device array instead of a caller's workspace.  Every call on one
+// GPU uses that GPU's copy, so calls that overlap on a GPU race; the histogram pass overwrites
+// every entry a call reads, so nothing needs clearing between calls.
+static constexpr size_t kDispatchScratchBytes = 1u << 20;
+static __device__ __align__(256) int32_t scratch[kDispatchScratchBytes / sizeof(int32_t)];
+
+size_t dispatch_scratch_bytes() { return kDispatchScratchBytes; }
+
+// Device address of this GPU's scratch, looked up on the first call on each device (with that
+// device current) and kept.  In host code `scratch` names a host-side stand-in, never the device
+// memory; only the address looked up here may be handed to kernels.  Returns nullptr when the
+// lookup fails (the next call tries again).
+int32_t* dispatch_scratch() {
+  static std::mutex mu;
+  static int32_t* ptr[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) == hipSuccess) ptr[dev] = (int32_t*)p;
+  }
+  return ptr[dev];
 }
 
 void launch_dispatch(const int32_t* topk_idx, int A, int E, int capacity, int32_t* counts,

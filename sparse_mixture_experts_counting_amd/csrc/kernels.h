@@ -23,6 +23,8 @@ size_t dispatch_workspace_bytes(int A, int E);
 void launch_dispatch(const int32_t* topk_idx, int A, int E, int capacity, int32_t* counts,
                      int32_t* offsets, int32_t* perm, int32_t* inv, int32_t* n_dropped,
                      int32_t* hist, hipStream_t s);
+size_t dispatch_scratch_bytes();
+int32_t* dispatch_scratch();
 
 // gemm_bf16.hip / gemm_f32.hip
 hipError_t launch_gemm_bf16(const GemmParams& p, int rows_max, int epi, hipStream_t s);

@@ -199,6 +199,22 @@ moe_status moe_dispatch(const int32_t* topk_idx, int T, int E, int k, int capaci
   return launched();
 }
 
+moe_status moe_dispatch_noalloc(const int32_t* topk_idx, int T, int E, int k, int capacity,
+                                int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv,
+                                int32_t* n_dropped, void* stream) {
+  if (T < 1 || E < 1 || k < 1 || k > E) return MOE_ERR_ARG;
+  if (!topk_idx || !counts || !offsets || !perm || !inv || !n_dropped) return MOE_ERR_ARG;
+  if (E > kMaxE || k > kMaxK) return MOE_ERR_UNSUPPORTED;
+  if (!fits_i32((long long)T * k)) return MOE_ERR_UNSUPPORTED;
+  if (moe::dispatch_workspace_bytes(T * k, E) > moe::dispatch_scratch_bytes())
+    return MOE_ERR_UNSUPPORTED;
+  int32_t* hist = moe::dispatch_scratch();
+  if (!hist) return MOE_ERR_DEVICE;
+  moe::launch_dispatch(topk_idx, T * k, E, capacity, counts, offsets, perm, inv, n_dropped, hist,
+                       (hipStream_t)stream);
+  return launched();
+}
+
 static moe_status check_ffn_args(const void* x, const void* wa, const void* wb, const void* out,
                                  bool grouped, const int32_t* offsets, int T, int d, int d_ff,
                                  int E, int k, moe_dtype dt) {

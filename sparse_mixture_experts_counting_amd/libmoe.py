@@ -28,7 +28,7 @@ EXPORTS = ("moe_workspace_bytes", "moe_status_str", "moe_route", "moe_dispatch",
            "moe_expert_choice", "moe_gathered_workspace_bytes", "moe_expert_ffn_gathered",
            "moe_reroute", "moe_q_workspace_bytes", "moe_quantize_weights", "moe_expert_ffn_q",
            "moe_expert_ffn_save", "moe_expert_backward_saved", "moe_peak_mfma",
-           "moe_peak_copy")
+           "moe_peak_copy", "moe_dispatch_noalloc")
 
 
 class MoEError(RuntimeError):
@@ -80,9 +80,10 @@ _lib.moe_gathered_workspace_bytes.argtypes = [_i, _i, _i, _i, _i]
 _lib.moe_gathered_workspace_bytes.restype = _sz
 _lib.moe_expert_ffn_gathered.argtypes = [_p, _p, _p, _i, _i, _i, _i, _i, _p, _p, _p, _i, _p, _p,
                                          _sz, _p]
+_lib.moe_dispatch_noalloc.argtypes = [_p, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p]
 _lib.moe_peak_mfma.argtypes = [_p, _i, _i, _p, _p]
 _lib.moe_peak_copy.argtypes = [_p, _p, _sz, _p]
-for _n in ("moe_peak_mfma", "moe_peak_copy", "moe_route", "moe_dispatch", "moe_expert_ffn", "moe_expert_up", "moe_expert_down",
+for _n in ("moe_dispatch_noalloc", "moe_peak_mfma", "moe_peak_copy", "moe_route", "moe_dispatch", "moe_expert_ffn", "moe_expert_up", "moe_expert_down",
            "moe_combine", "moe_aux_loss", "moe_transpose", "moe_update_select_bias",
            "moe_combine_backward", "moe_expert_backward", "moe_route_backward",
            "moe_expert_choice", "moe_expert_ffn_gathered", "moe_reroute",
@@ -149,6 +150,13 @@ def dispatch(topk_idx, T, E, k, capacity, counts, offsets, perm, inv, n_dropped,
     _check("moe_dispatch", _lib.moe_dispatch(
         _ptr(topk_idx), T, E, k, capacity, _ptr(counts), _ptr(offsets), _ptr(perm), _ptr(inv),
         _ptr(n_dropped), _ptr(workspace), _nbytes(workspace), _stream(stream)))
+
+
+def dispatch_noalloc(topk_idx, T, E, k, capacity, counts, offsets, perm, inv, n_dropped,
+                     stream=None):
+    _check("moe_dispatch_noalloc", _lib.moe_dispatch_noalloc(
+        _ptr(topk_idx), T, E, k, capacity, _ptr(counts), _ptr(offsets), _ptr(perm), _ptr(inv),
+        _ptr(n_dropped), _stream(stream)))
 
 
 def expert_ffn(x, perm, offsets, T, d, d_ff, E, k, w1, w3, w2, dt, out, workspace, stream=None):

@@ -35,7 +35,8 @@ def test_every_declared_symbol_is_exported(lm):
                           "moe_gathered_workspace_bytes", "moe_expert_ffn_gathered",
                           "moe_reroute", "moe_q_workspace_bytes", "moe_quantize_weights",
                           "moe_expert_ffn_q", "moe_expert_ffn_save",
-                          "moe_expert_backward_saved", "moe_peak_mfma", "moe_peak_copy"}
+                          "moe_expert_backward_saved", "moe_peak_mfma", "moe_peak_copy",
+                          "moe_dispatch_noalloc"}
     lib = ctypes.CDLL(lm.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -264,3 +265,18 @@ def test_peak_argument_errors(lm):
     assert L.moe_peak_copy(FAKE, FAKE, 40, None) == 1             # not a multiple of 16
     assert L.moe_peak_copy(None, FAKE, 64, None) == 1
     assert L.moe_peak_copy(FAKE + 8, FAKE, 64, None) == 1
+
+
+def test_dispatch_noalloc_argument_errors(lm):
+    """Host-side checks of the entry point that allocates nothing: bad arguments and inputs too
+    large for its fixed 1 MiB histogram array are refused before any device call."""
+    L = lm.lib()
+    f = FAKE
+    assert L.moe_dispatch_noalloc(None, 4, 4, 2, 0, f, f, f, f, f, None) == 1
+    assert L.moe_dispatch_noalloc(f, 0, 4, 2, 0, f, f, f, f, f, None) == 1
+    assert L.moe_dispatch_noalloc(f, 4, 4, 5, 0, f, f, f, f, f, None) == 1
+    assert L.moe_dispatch_noalloc(f, 4, 4, 2, 0, f, f, None, f, f, None) == 1
+    assert L.moe_dispatch_noalloc(f, 4, 2000, 2, 0, f, f, f, f, f, None) == 2
+    # 293 chunks of 2048 assignments x 1024 experts x 4 bytes exceeds 1 MiB
+    assert L.moe_dispatch_noalloc(f, 600000, 1024, 1, 0, f, f, f, f, f, None) == 2
+    assert L.moe_dispatch_noalloc(f, 2 ** 30, 8, 4, 0, f, f, f, f, f, None) == 2
