@@ -166,9 +166,14 @@ __device__ __forceinline__ TailPlan tail_plan(int total, int slots, int K) {
   return tp;
 }
 
+// One output tile: the K loop over the block's range and the epilogue.  tc names the tile; kc /
+// nsplit its K chunk when the tile is split (rtile >= 0: a split tile of the last round, written as
+// tile-local partials); kg_beg / kg_len the reduction rows in the K-grouped mode.  Every thread of
+// the block calls it with the same arguments.
 template <int BM, int BN, int NMAT, int WGM, int WGN, int BK, int NST, int MINB, int EPI, bool TAIL,
           bool BT = false, bool AT = false>
-__global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_bf16_kernel(const GemmParams p) {
+__device__ __forceinline__ void gemm_tile(const GemmParams& p, TileCoord tc, int kc, int nsplit,
+                                          int rtile, int kg_beg, int kg_len) {
   constexpr int NTHR = 64 * WGM * WGN;
   constexpr int WM = BM / WGM, WN = BN / WGN;       // WGM x WGN waves
   constexpr int TM = WM / 32, TN = WN / 32;
@@ -209,65 +214,6 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_bf16_kernel(const G
   static_assert(!AT || (BT && BM == 256 && EPI == EPI_STORE_F32_BIAS), "transposed A");
 
   extern __shared__ __align__(16) uint8_t smem[];
-
-  const int NT = (p.N + BN - 1) / BN;
-  TileCoord tc;
-  int kc = 0, nsplit = p.ksplit, rtile = -1;
-  int kg_beg = 0, kg_len = 0;               // K-grouped mode: this group's reduction columns
-  if (p.kgrouped) {
-    // Tiles group-major; inside a group, bands of 4 m-tiles walked n-tile by n-tile, so 32
-    // consecutive tiles form a 4 x 8 block that reads 4 A and 8 B tiles.  Blocks are dealt to the
-    // 8 XCDs in turn (block b on XCD b % 8); in each whole round of p.slots blocks, XCD x takes
-    // chunk 8 r + x of p.slots / 8 consecutive tiles, so the CUs sharing an L2 share operand
-    // tiles, while consecutive chunks (a group's work, which grows with its row count) still go
-    // to different XCDs.  The last partial round takes tiles in index order.
-    const int MT = (p.M + BM - 1) / BM;
-    const int per = MT * NT;
-    const int total = p.G * per;
-    int t = blockIdx.x;
-    if (t >= total) return;
-    const int round = p.slots >= 8 ? p.slots : 8, chunk = round / 8;
-    if (t < total / round * round) {
-      const int x = t & 7, k = t >> 3;
-      t = ((k / chunk) * 8 + x) * chunk + k % chunk;
-    }
-    tc.g = t / per;
-    const int local = t - tc.g * per;
-    constexpr int GM = 4;
-    const int band = local / (GM * NT);
-    const int m_first = band * GM;
-    const int gm = min(MT - m_first, GM);
-    const int in = local - band * GM * NT;
-    tc.row0 = (m_first + in % gm) * BM;
-    tc.row_end = p.M;
-    tc.n_tile = in / gm;
-    const int o0 = p.offsets[tc.g];
-    kg_beg = __builtin_amdgcn_readfirstlane(o0);
-    kg_len = __builtin_amdgcn_readfirstlane(p.offsets[tc.g + 1] - o0);
-  } else if (p.ksplit > 1) {                // every tile split over K
-    const TileScan ts = scan_tiles<BM>(p, NT);
-    kc = blockIdx.x % p.ksplit;
-    const int bid = blockIdx.x / p.ksplit;
-    if (bid >= ts.total) return;
-    tile_at<BM>(p, NT, ts, xcd_order(bid, ts.total), tc);
-  } else {                                  // whole rounds as is, the last partial round split
-    const TileScan ts = scan_tiles<BM>(p, NT);
-    const TailPlan tp = tail_plan(ts.total, p.slots, p.K);
-    if ((int)blockIdx.x < tp.full) {
-      tile_at<BM>(p, NT, ts, xcd_order(blockIdx.x, tp.full), tc);
-    } else {
-      const int w = blockIdx.x - tp.full;
-      rtile = w / tp.q;
-      kc = w % tp.q;
-      nsplit = tp.q;
-      if (rtile >= tp.rem) return;
-      tile_at<BM>(p, NT, ts, tp.full + rtile, tc);
-    }
-  }
-  tc.g = __builtin_amdgcn_readfirstlane(tc.g);
-  tc.row0 = __builtin_amdgcn_readfirstlane(tc.row0);
-  tc.row_end = __builtin_amdgcn_readfirstlane(tc.row_end);
-  tc.n_tile = __builtin_amdgcn_readfirstlane(tc.n_tile);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -1007,6 +953,202 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_bf16_kernel(const G
   }
 }
 
+// The grouped GEMM kernel: each block finds its tile (K-grouped, every tile split over K, or whole
+// rounds with the last partial round split) and computes it.
+template <int BM, int BN, int NMAT, int WGM, int WGN, int BK, int NST, int MINB, int EPI, bool TAIL,
+          bool BT = false, bool AT = false>
+__global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_bf16_kernel(const GemmParams p) {
+  const int NT = (p.N + BN - 1) / BN;
+  TileCoord tc;
+  int kc = 0, nsplit = p.ksplit, rtile = -1;
+  int kg_beg = 0, kg_len = 0;               // K-grouped mode: this group's reduction columns
+  if (p.kgrouped) {
+    // Tiles group-major; inside a group, bands of 4 m-tiles walked n-tile by n-tile, so 32
+    // consecutive tiles form a 4 x 8 block that reads 4 A and 8 B tiles.  Blocks are dealt to the
+    // 8 XCDs in turn (block b on XCD b % 8); in each whole round of p.slots blocks, XCD x takes
+    // chunk 8 r + x of p.slots / 8 consecutive tiles, so the CUs sharing an L2 share operand
+    // tiles, while consecutive chunks (a group's work, which grows with its row count) still go
+    // to different XCDs.  The last partial round takes tiles in index order.
+    const int MT = (p.M + BM - 1) / BM;
+    const int per = MT * NT;
+    const int total = p.G * per;
+    int t = blockIdx.x;
+    if (t >= total) return;
+    const int round = p.slots >= 8 ? p.slots : 8, chunk = round / 8;
+    if (t < total / round * round) {
+      const int x = t & 7, k = t >> 3;
+      t = ((k / chunk) * 8 + x) * chunk + k % chunk;
+    }
+    tc.g = t / per;
+    const int local = t - tc.g * per;
+    constexpr int GM = 4;
+    const int band = local / (GM * NT);
+    const int m_first = band * GM;
+    const int gm = min(MT - m_first, GM);
+    const int in = local - band * GM * NT;
+    tc.row0 = (m_first + in % gm) * BM;
+    tc.row_end = p.M;
+    tc.n_tile = in / gm;
+    const int o0 = p.offsets[tc.g];
+    kg_beg = __builtin_amdgcn_readfirstlane(o0);
+    kg_len = __builtin_amdgcn_readfirstlane(p.offsets[tc.g + 1] - o0);
+  } else if (p.ksplit > 1) {                // every tile split over K
+    const TileScan ts = scan_tiles<BM>(p, NT);
+    kc = blockIdx.x % p.ksplit;
+    const int bid = blockIdx.x / p.ksplit;
+    if (bid >= ts.total) return;
+    tile_at<BM>(p, NT, ts, xcd_order(bid, ts.total), tc);
+  } else {                                  // whole rounds as is, the last partial round split
+    const TileScan ts = scan_tiles<BM>(p, NT);
+    const TailPlan tp = tail_plan(ts.total, p.slots, p.K);
+    if ((int)blockIdx.x < tp.full) {
+      tile_at<BM>(p, NT, ts,
+                  p.slots >= 8 ? xcd_round_order(blockIdx.x, tp.full, p.slots / 8 * 8)
+                               : xcd_order(blockIdx.x, tp.full),
+                  tc);
+    } else {
+      const int w = blockIdx.x - tp.full;
+      rtile = w / tp.q;
+      kc = w % tp.q;
+      nsplit = tp.q;
+      if (rtile >= tp.rem) return;
+      tile_at<BM>(p, NT, ts, tp.full + rtile, tc);
+    }
+  }
+  tc.g = __builtin_amdgcn_readfirstlane(tc.g);
+  tc.row0 = __builtin_amdgcn_readfirstlane(tc.row0);
+  tc.row_end = __builtin_amdgcn_readfirstlane(tc.row_end);
+  tc.n_tile = __builtin_amdgcn_readfirstlane(tc.n_tile);
+
+  gemm_tile<BM, BN, NMAT, WGM, WGN, BK, NST, MINB, EPI, TAIL, BT, AT>(p, tc, kc, nsplit, rtile,
+                                                                     kg_beg, kg_len);
+}
+
+// ---------------------------------------------------------------------------------------------
+// Block-sparse dropless tiling of a grouped product whose group sizes are skewed (many experts with
+// a few rows beside a few with thousands: the fine-grained, Zipf-routed layer).  The tiles form a
+// block-sparse map over (expert, row block, column block), built on the device from `offsets`:
+//   - a group with at least one whole 256-row block ("big") gets, for every column tile, its whole
+//     256-row tiles followed by one tile for its remainder rows, so the remainder reuses the
+//     column tile's weight panel from L2 instead of streaming the expert's weights a second time;
+//   - a group with fewer than 256 rows ("small") gets one tile per column tile.
+// A tile of at most 64 rows runs as a thin tile (64 x BN, 8 waves in 2 x 4, a 4-stage ring: 96 KB of
+// weights in flight per CU, for the weight-streaming tiles whose speed is set by bytes in flight);
+// any other tile as the tall 256-row tile of the matrix-bound path.  Both kinds are one launch: the
+// small groups' tiles are spread evenly through the big groups' tiles (tile t of the merged order is
+// small when floor((t + 1) S / (S + B)) > floor(t S / (S + B)), S small and B big tiles), so every
+// CU alternates between matrix-bound and weight-streaming work and HBM streams the small experts'
+// weights while the matrix cores work.  Blocks are dealt to the XCDs by rounds (each
+// XCD takes one chunk of every round of resident blocks), so every XCD gets the same mix of tall,
+// thin and remainder tiles.  No K split: every tile sums its full K range.
+// ---------------------------------------------------------------------------------------------
+constexpr int kBsTall = 256;   // rows of a tall tile
+constexpr int kBsThin = 64;    // rows of a thin tile (tiles of at most this many rows run thin)
+
+struct BsScan {
+  int big, small;              // tiles of each sequence in all groups
+  int g0, g1;                  // this lane's groups [g0, g1)
+  int big_mine, big_incl;      // tiles of the big sequence in this lane's groups, and inclusive
+  int small_mine, small_incl;  // likewise for the small sequence
+};
+
+__device__ __forceinline__ BsScan bs_scan(const GemmParams& p, int NT) {
+  BsScan s;
+  const int lane = __lane_id();
+  const int per = (p.G + 63) >> 6;
+  s.g0 = min(p.G, lane * per);
+  s.g1 = min(p.G, s.g0 + per);
+  int big = 0, small = 0;
+  for (int g = s.g0; g < s.g1; ++g) {
+    const int n = p.offsets[g + 1] - p.offsets[g];
+    if (n >= kBsTall)
+      big += (n / kBsTall + (n % kBsTall != 0)) * NT;
+    else if (n > 0)
+      small += NT;
+  }
+  int bi = big, si = small;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int ub = __shfl_up(bi, o, 64), us = __shfl_up(si, o, 64);
+    if (lane >= o) {
+      bi += ub;
+      si += us;
+    }
+  }
+  s.big_mine = big;
+  s.big_incl = bi;
+  s.small_mine = small;
+  s.small_incl = si;
+  s.big = __shfl(bi, 63, 64);
+  s.small = __shfl(si, 63, 64);
+  return s;
+}
+
+// Tile `bid` (block order) of the block-sparse map -> coordinates; false past the last tile.
+__device__ __forceinline__ bool bs_tile(const GemmParams& p, int NT, int bid, TileCoord& tc) {
+  const BsScan s = bs_scan(p, NT);
+  const int total = s.big + s.small;
+  if (bid >= total) return false;
+  const int t = xcd_round_order(bid, total, p.slots);
+  const long long S = s.small, TT = total;
+  const int small_before = (int)((long long)t * S / TT);
+  const bool is_small = (int)((long long)(t + 1) * S / TT) > small_before;
+  const int idx = is_small ? small_before : t - small_before;
+  const int incl = is_small ? s.small_incl : s.big_incl;
+  const int mine = is_small ? s.small_mine : s.big_mine;
+  const int lane = __lane_id();
+  const uint64_t own = __ballot(idx >= incl - mine && idx < incl);
+  const int owner = __ffsll((long long)own) - 1;
+  int g_found = 0, base = 0;
+  if (lane == owner) {
+    base = incl - mine;
+    for (int g = s.g0; g < s.g1; ++g) {
+      const int n = p.offsets[g + 1] - p.offsets[g];
+      const int c = is_small ? (n > 0 && n < kBsTall ? NT : 0)
+                             : (n >= kBsTall ? (n / kBsTall + (n % kBsTall != 0)) * NT : 0);
+      if (idx < base + c) {
+        g_found = g;
+        break;
+      }
+      base += c;
+    }
+  }
+  g_found = __shfl(g_found, owner, 64);
+  base = __shfl(base, owner, 64);
+  const int rs = p.offsets[g_found], re = p.offsets[g_found + 1];
+  const int local = idx - base;
+  tc.g = g_found;
+  if (is_small) {                      // one tile per column tile
+    tc.row0 = rs;
+    tc.row_end = re;
+    tc.n_tile = local;
+  } else {                             // whole 256-row tiles, then the remainder, per column tile
+    const int n = re - rs;
+    const int per_n = n / kBsTall + (n % kBsTall != 0);
+    tc.n_tile = local / per_n;
+    tc.row0 = rs + (local % per_n) * kBsTall;
+    tc.row_end = min(tc.row0 + kBsTall, re);
+  }
+  return true;
+}
+
+template <int EPI>
+__global__ __launch_bounds__(512, 1) void gemm_bs_kernel(const GemmParams p) {
+  constexpr int NMAT = epi_swiglu(EPI) ? 2 : 1;
+  constexpr int BN = epi_swiglu(EPI) ? 128 : 256;   // columns per matrix, both tile kinds
+  const int NT = (p.N + BN - 1) / BN;
+  TileCoord tc;
+  if (!bs_tile(p, NT, blockIdx.x, tc)) return;
+  tc.g = __builtin_amdgcn_readfirstlane(tc.g);
+  tc.row0 = __builtin_amdgcn_readfirstlane(tc.row0);
+  tc.row_end = __builtin_amdgcn_readfirstlane(tc.row_end);
+  tc.n_tile = __builtin_amdgcn_readfirstlane(tc.n_tile);
+  if (tc.row_end - tc.row0 <= kBsThin)
+    gemm_tile<kBsThin, BN, NMAT, 2, 4, 64, 4, 1, EPI, false>(p, tc, 0, 1, -1, 0, 0);
+  else
+    gemm_tile<kBsTall, BN, NMAT, 4, 2, 64, 2, 1, EPI, false>(p, tc, 0, 1, -1, 0, 0);
+}
+
 // Sum the K-chunk partials of every valid row in a fixed order and apply the epilogue.
 // Rows past the valid count (offsets[G], or M for a single group) are untouched.
 template <int NMAT, int EPI>
@@ -1261,6 +1403,44 @@ static hipError_t launch_t(const GemmParams& p, int rows_max, hipStream_t s) {
   return hipGetLastError();
 }
 
+// The block-sparse launch (forward epilogues: SwiGLU, SwiGLU storing a and b, plain bf16 store).
+template <int EPI>
+static hipError_t launch_bs_t(const GemmParams& p, int rows_max, hipStream_t s) {
+  auto kern = gemm_bs_kernel<EPI>;
+  static_assert(lds_bytes<kBsThin, epi_swiglu(EPI) ? 128 : 256, epi_swiglu(EPI) ? 2 : 1, 64, 4,
+                          1>() == kMaxLds &&
+                    lds_bytes<kBsTall, epi_swiglu(EPI) ? 128 : 256, epi_swiglu(EPI) ? 2 : 1, 64,
+                              2, 1>() == kMaxLds,
+                "both tile kinds fill the LDS the launch asks for");
+  static std::atomic<bool> attr_set[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  if (!attr_set[dev].load(std::memory_order_acquire)) {
+    hipError_t e = hipFuncSetAttribute((const void*)kern,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLds);
+    if (e != hipSuccess) return e;
+    attr_set[dev].store(true, std::memory_order_release);
+  }
+  GemmParams q = p;
+  q.ksplit = 1;
+  q.slots = device_cus() / 8 * 8;   // one block per CU: the blocks of one round
+  const int NT = (p.N + (epi_swiglu(EPI) ? 128 : 256) - 1) / (epi_swiglu(EPI) ? 128 : 256);
+  // Every group yields at most floor(n_g / 256) + 1 tiles per column tile.
+  const int grid = tiles_upper_bound(rows_max, p.G, true, kBsTall, NT);
+  if (grid <= 0) return hipSuccess;
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(512), kMaxLds, s, q);
+  return hipGetLastError();
+}
+
+static hipError_t launch_bs(const GemmParams& p, int rows_max, int epi, hipStream_t s) {
+  switch (epi) {
+    case EPI_SWIGLU: return launch_bs_t<EPI_SWIGLU>(p, rows_max, s);
+    case EPI_SWIGLU_SAVE: return launch_bs_t<EPI_SWIGLU_SAVE>(p, rows_max, s);
+    case EPI_STORE: return launch_bs_t<EPI_STORE>(p, rows_max, s);
+    default: return hipErrorNotSupported;
+  }
+}
+
 template <int BM, int BN, int NMAT, int WGM, int WGN, int BK, int NST, int MINB, int EPI,
           bool BT = false>
 static hipError_t launch_tail_or_not(const GemmParams& p, int rows_max, hipStream_t s) {
@@ -1444,14 +1624,22 @@ hipError_t launch_gemm_bf16(const GemmParams& p_in, int rows_max, int epi, hipSt
   if (p.ksplit > 1 && p.part == nullptr) p.ksplit = 1;   // no scratch given: no split
   const bool big = use_big_tiles(rows_max, p.G, grouped, epi);
   hipError_t e;
-  if (big && grouped && p.ksplit == 1 && epi != EPI_STORE_F32_BIAS &&
-      (long long)rows_max < 512ll * p.G) {
-    // Groups of a few hundred rows on average (fine-grained experts, skewed routing): the rows of
-    // every group that fill whole 256-row tiles run in 256-row tiles, the rest (under 256 rows
-    // per group) in 128-row tiles, two blocks per CU, where a short group wastes less.  The short
-    // tiles of the many small groups are bound by streaming those experts' weights, the tall ones
-    // by the matrix cores, so the two launches run side by side on two streams.  Only the tall
-    // launch splits its last round over K (the scratch is not shared).
+  const bool skewed = big && grouped && p.ksplit == 1 && epi != EPI_STORE_F32_BIAS &&
+                     (long long)rows_max < 512ll * p.G;
+  if (big && grouped && p.ksplit == 1 && !p.bt &&
+      (epi_swiglu(epi) || (skewed && epi == EPI_STORE))) {
+    // Forward products: one block-sparse launch of tall and thin tiles.  The SwiGLU up projection
+    // takes it whenever the groups fill 256-row tiles (its few-row remainders run as thin tiles);
+    // the down projection only for skewed groups (with a few hundred rows per group on average:
+    // evenly filled groups give it too few tiles, whose last round the K-split tiling balances).
+    e = launch_bs(p, rows_max, epi, s);
+  } else if (skewed) {
+    // The backward's products of skewed groups (transposed weights, SwiGLU-derivative epilogues):
+    // the rows of every group that fill whole 256-row tiles run in 256-row tiles, the rest (under
+    // 256 rows per group) in 128-row tiles, two blocks per CU, where a short group wastes less.
+    // The short tiles of the many small groups are bound by streaming those experts' weights, the
+    // tall ones by the matrix cores, so the two launches run side by side on two streams.  Only
+    // the tall launch splits its last round over K (the scratch is not shared).
     GemmParams p1 = p, p2 = p;
     p1.row_split = p2.row_split = 256;
     p1.part_mode = 1;

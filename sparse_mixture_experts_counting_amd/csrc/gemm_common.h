@@ -183,6 +183,17 @@ __device__ __forceinline__ int xcd_order(int bid, int n) {
   return (x < r) ? x * (q + 1) + i : r * (q + 1) + (x - r) * q + i;
 }
 
+// Blocks are handed to the 8 XCDs round-robin; in each whole round of `round` blocks (a multiple of
+// 8: the blocks resident at once), XCD x takes the x-th chunk of round / 8 consecutive tiles of that
+// round, so consecutive tiles (those sharing a weight panel) share an L2, and every XCD gets the
+// same share of every part of the tile order (equal work when tile costs vary along the order).
+// Blocks past the last whole round take tiles in index order.
+__device__ __forceinline__ int xcd_round_order(int bid, int n, int round) {
+  if (round < 8 || bid >= n / round * round) return bid;
+  const int chunk = round >> 3, x = bid & 7, k = bid >> 3;
+  return (k / chunk) * round + x * chunk + k % chunk;
+}
+
 // Map block `bid` to a tile in XCD order.  Returns false when bid is past the real tile count.
 template <int BM>
 __device__ __forceinline__ bool find_tile(const GemmParams& p, int NT, int bid, TileCoord& tc) {
