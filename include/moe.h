@@ -41,24 +41,36 @@
 extern "C" {
 #endif
 
+/* Every enum below spans the whole int range (the two range enumerators are not values to pass),
+ * so that any int a caller passes is a representable value that the checks can refuse: an
+ * out-of-range value is MOE_ERR_ARG, never undefined behaviour in the library's C++ code. */
 typedef enum {
   MOE_OK = 0,
   MOE_ERR_ARG = 1,
   MOE_ERR_UNSUPPORTED = 2,
   MOE_ERR_WORKSPACE = 3,
-  MOE_ERR_DEVICE = 4
+  MOE_ERR_DEVICE = 4,
+  MOE_STATUS_RANGE_MIN_ = -0x7fffffff - 1,
+  MOE_STATUS_RANGE_MAX_ = 0x7fffffff
 } moe_status;
 
 /* Element type of x, W_r, the expert weights, expert outputs and y.  Accumulation is always fp32
  * and router logits are always fp32 (the tirogla page, Implementation notes: compute the router in
  * fp32 because small logit differences decide routing). */
-typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+typedef enum {
+  MOE_F32 = 0,
+  MOE_BF16 = 1,
+  MOE_DTYPE_RANGE_MIN_ = -0x7fffffff - 1,
+  MOE_DTYPE_RANGE_MAX_ = 0x7fffffff
+} moe_dtype;
 
 /* Gating (the tirogla page, How it works, step 1). */
 typedef enum {
   MOE_GATE_SOFTMAX_TOPK = 0, /* softmax over the k selected logits (Mixtral)                       */
   MOE_GATE_SOFTMAX_ALL = 1,  /* softmax over all E logits, keep the selected probabilities (Switch) */
-  MOE_GATE_SIGMOID_TOPK = 2  /* sigmoid affinities renormalised over the k selected (DeepSeek-V3)   */
+  MOE_GATE_SIGMOID_TOPK = 2, /* sigmoid affinities renormalised over the k selected (DeepSeek-V3)   */
+  MOE_GATING_RANGE_MIN_ = -0x7fffffff - 1,
+  MOE_GATING_RANGE_MAX_ = 0x7fffffff
 } moe_gating;
 
 /* moe_route flag: skip the router product and read `logits` as an input. */

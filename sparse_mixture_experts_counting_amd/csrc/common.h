@@ -62,3 +62,8 @@ __device__ __forceinline__ uint64_t lanemask_lt() {
 }
 
 __device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + __expf(-z)); }
+
+// log(sigmoid(v)) = min(v, 0) - log1p(exp(-|v|)), finite for every finite v.
+__device__ __forceinline__ float log_sigmoid(float v) {
+  return fminf(v, 0.f) - log1pf(expf(-fabsf(v)));
+}

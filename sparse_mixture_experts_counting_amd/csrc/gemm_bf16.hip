@@ -820,12 +820,17 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, TileCoord tc, int
     }
     return;
   }
-  if (EPI == EPI_STORE_F32_BIAS && !partial && N % 4 == 0 && p.ldc % 4 == 0) {
+  if (EPI == EPI_STORE_F32_BIAS && rtile < 0 && N % 4 == 0 && p.ldc % 4 == 0) {
     // fp32 output, four columns per 16-byte store: the four lanes of a quad hold one column each
     // of four consecutive rows; two DPP exchanges (lane ^ 1, then lane ^ 2) transpose that 4 x 4
     // block, so lane 4c + s holds row s of columns 4c .. 4c + 3.  The stores are non-temporal:
     // the output (the weight gradients, 4 bytes per weight) is not read again by this kernel and
-    // would otherwise push the operand tiles out of the caches.
+    // would otherwise push the operand tiles out of the caches.  A K-split product writes its
+    // chunk's partial sums the same way (no bias, cached stores) into its slice of the scratch.
+    const bool kpart = p.ksplit > 1;
+    float* const Cout = kpart ? p.part + (size_t)kc * p.part_rows * N : (float*)Cg;
+    const int ldo = kpart ? N : p.ldc;
+    const float* const bias = kpart ? nullptr : p.bias;
     const int s4 = lane & 3;
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
@@ -833,7 +838,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, TileCoord tc, int
       for (int j = 0; j < TN; ++j) {
         const int col0 = n_base + wn0 + j * 32 + (l32 & ~3);
         f32x4 bias4 = {0.f, 0.f, 0.f, 0.f};
-        if (p.bias && col0 < N) bias4 = *(const f32x4*)(p.bias + col0);
+        if (bias && col0 < N) bias4 = *(const f32x4*)(bias + col0);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           float a[4], b[4];
@@ -862,7 +867,11 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, TileCoord tc, int
           w[3] = (o2 ? b[3] : r3) + bias4[3];
           const int row = tc.row0 + wm0 + i * 32 + 8 * q + 4 * h + s4;
           if (row < tc.row_end && col0 < N) {
-            __builtin_nontemporal_store(w, (f32x4*)((float*)Cg + (size_t)row * p.ldc + col0));
+            f32x4* dst = (f32x4*)(Cout + (size_t)row * ldo + col0);
+            if (kpart)   // read back soon by the finishing kernel: keep it in the caches
+              *dst = w;
+            else
+              __builtin_nontemporal_store(w, dst);
           }
         }
       }
@@ -1487,13 +1496,13 @@ static bool use_big_tiles(int rows_max, int G, bool grouped, int epi) {
 // round, the largest).
 static int splitk_factor(int rows_max, int G, bool grouped, int N, int K, int epi) {
   if (epi == EPI_STORE_F32_BIAS) {
-    // The router product (one dense group, fp32 logits): 128 x 256 tiles, two blocks per CU.  A
-    // few hundred tokens give too few tiles to cover the GPU, so K is split into the smallest
+    // The router product (one dense group, fp32 logits): 256 x 256 tiles, one block per CU.  A
+    // few thousand tokens give too few tiles to cover the GPU, so K is split into the smallest
     // power-of-two number of chunks (whole 64-deep steps, at most 8) whose blocks fill one round.
     if (grouped || K % 64 != 0 || N % 8 != 0) return 1;
-    const long long tiles = (long long)((rows_max + 127) / 128) * ((N + 255) / 256);
+    const long long tiles = (long long)((rows_max + 255) / 256) * ((N + 255) / 256);
     const int cus = device_cus();
-    const long long slots = 2ll * (cus > 0 ? cus : 256);
+    const long long slots = 1ll * (cus > 0 ? cus : 256);
     int ks = 1;
     while (ks < 8 && tiles * ks < slots && (K / 64) % (ks * 2) == 0) ks *= 2;
     return ks;
@@ -1578,8 +1587,8 @@ static hipError_t launch_cfg(const GemmParams& p, int rows_max, int epi, bool bi
                                                                                       s)
                  : launch_tail_or_not<128, 256, 1, 2, 2, 32, 3, 2, EPI_SWIGLU_BWD_SAVED>(p, rows_max,
                                                                                       s);
-    default:   // the router product: direct loads, two blocks per CU
-      return launch_tail_or_not<128, 256, 1, 2, 2, 32, 3, 2, EPI_STORE_F32_BIAS>(p, rows_max, s);
+    default:   // the router product: the 256 x 256 direct-load tiles, one block per CU
+      return launch_tail_or_not<256, 256, 1, 4, 2, 64, 2, 1, EPI_STORE_F32_BIAS>(p, rows_max, s);
   }
 }
 

@@ -98,6 +98,7 @@ const char* moe_status_str(moe_status s) {
     case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED: shape or mode not supported";
     case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE: workspace too small";
     case MOE_ERR_DEVICE: return "MOE_ERR_DEVICE: kernel launch failed";
+    default: break;
   }
   return "unknown moe_status";
 }

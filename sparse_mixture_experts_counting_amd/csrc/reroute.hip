@@ -87,21 +87,15 @@ __global__ __launch_bounds__(256) void reroute_propose_kernel(
       ++j;
     }
   }
-  // Final selection, and the gates of the gating function over it.
-  float m = -INFINITY;
-  for (int e = lane; e < E; e += 64) m = fmaxf(m, L[e]);
-  m = wave_max(m);
-  float zall = 0.f;
-  if (mode == 1) {
-    for (int e = lane; e < E; e += 64) zall += expf(L[e] - m);
-    zall = wave_sum(zall);
-  }
-  if (lane == 0) {
-    int jj = 0;
-    for (int s = 0; s < k; ++s) {
+  // Final selection: lane 0 walks the slots (an overflowed slot takes its proposal), and slot s's
+  // expert goes to lane s.
+  int my_e = 0, jj = 0;
+  for (int s = 0; s < k; ++s) {
+    int e = 0;
+    if (lane == 0) {
       const int a = t * k + s;
       const int e0 = topk_idx[a];
-      int e = e0;
+      e = e0;
       if (inv[a] < 0 && e0 >= 0 && e0 < E) {
         if (k + jj < E) {
           e = proposal[a];
@@ -115,23 +109,30 @@ __global__ __launch_bounds__(256) void reroute_propose_kernel(
       idx2[a] = e;
       r2rank[a] = -1;
     }
-    float sum = 0.f;
-    for (int s = 0; s < k; ++s) {
-      const float v = L[idx2[t * k + s]];
-      sum += mode == 2 ? 1.0f / (1.0f + expf(-v)) : expf(v - m);
-    }
-    for (int s = 0; s < k; ++s) {
-      const float v = L[idx2[t * k + s]];
-      float g;
-      if (mode == 0)
-        g = expf(v - m) / sum;
-      else if (mode == 1)
-        g = expf(v - m) / zall;
-      else
-        g = (1.0f / (1.0f + expf(-v))) / sum;
-      gate2[t * k + s] = g;
-    }
+    e = __shfl(e, 0, 64);
+    if (lane == s) my_e = e;
   }
+  // The gates of the final selection, with the numerics of moe_route's gating: softmax over the
+  // selected and the renormalised sigmoids are shifted by the largest selected logit v0 (in
+  // log-sigmoid form for the latter), so they stay finite however far the selected logits lie
+  // below the row maximum or below zero; softmax over all E uses the row maximum and its sum.
+  const float my_v = lane < k ? L[my_e] : -INFINITY;
+  float g;
+  if (mode == 1) {
+    float m = -INFINITY;
+    for (int e = lane; e < E; e += 64) m = fmaxf(m, L[e]);
+    m = wave_max(m);
+    float zall = 0.f;
+    for (int e = lane; e < E; e += 64) zall += expf(L[e] - m);
+    zall = wave_sum(zall);
+    g = expf(my_v - m) * (1.0f / zall);
+  } else {
+    const float v0 = wave_max(my_v);
+    float w = 0.f;
+    if (lane < k) w = mode == 0 ? expf(my_v - v0) : expf(log_sigmoid(my_v) - log_sigmoid(v0));
+    g = w / wave_sum(w);
+  }
+  if (lane < k) gate2[t * k + lane] = g;
 }
 
 constexpr int kRrThreads = 1024;

@@ -184,10 +184,6 @@ __device__ __forceinline__ uint32_t ordered_bits(float v) {
 __device__ __forceinline__ float from_ordered_bits(uint32_t o) {
   return __uint_as_float((o & 0x80000000u) ? (o ^ 0x80000000u) : ~o);
 }
-// log(sigmoid(v)) = min(v, 0) - log1p(exp(-|v|)), finite for every finite v.
-__device__ __forceinline__ float log_sigmoid(float v) {
-  return fminf(v, 0.f) - log1pf(expf(-fabsf(v)));
-}
 
 template <int EPL>
 __global__ __launch_bounds__(256) void gate_topk_kernel(const float* __restrict__ logits,
@@ -321,10 +317,11 @@ __global__ __launch_bounds__(256) void route_finalize_kernel(const float* __rest
 }
 
 int gate_rows_per_block(int T) {
-  // Enough blocks to cover the chip for large T, few partials for small T.
-  if (T >= 8192) return 32;
-  if (T >= 1024) return 16;
-  return 8;
+  // A wave per row at a time, four waves per block: at least four blocks per CU for large T (the
+  // row's k arg-max rounds are chains of cross-lane exchanges whose latency other waves hide),
+  // few partials for small T.
+  if (T >= 8192) return 8;
+  return 4;
 }
 
 void launch_gate_topk(const float* logits, const float* select_bias, int T, int E, int k, int mode,

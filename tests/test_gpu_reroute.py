@@ -67,6 +67,42 @@ def test_reroute_from_given_logits(M, T, E, k, C, mode):
                                rtol=0)
 
 
+@pytest.mark.parametrize("mode", [0, 1, 2])
+def test_reroute_gates_with_a_large_logit_gap(M, mode):
+    """Every token's first choice (expert 0) sits 300 above the rest, or every other logit lies far
+    below zero (sigmoid mode), and expert 0 overflows: the rerouted tokens' selected logits all lie
+    far below the row maximum.  Their gates must stay finite and match the oracle's float64 gates
+    of the final selection within 1e-6 (the gating of moe_route shifts by the largest selected
+    logit; shifting by the row maximum would underflow every term to 0)."""
+    _say("reroute large gap, mode", mode)
+    lm, layer, synth = M["lm"], M["layer"], M["synth"]
+    T, E, k, C = 64, 8, 2, 4
+    rng = np.random.default_rng(77 + mode)
+    L = rng.normal(0, 1, size=(T, E)).astype(np.float32)
+    if mode == 2:
+        L[:, 1:] -= 200.0
+        L[:, 0] = 5.0
+    else:
+        L[:, 0] = 300.0
+    cfg = synth.tiny_config(T, 8, E, k, 8, "fp32", ["softmax_topk", "softmax_all",
+                                                      "sigmoid_topk"][mode], capacity=C)
+    b = layer.alloc_buffers(cfg)
+    b.logits.copy_(torch.from_numpy(L))
+    inp = synth.make_inputs(cfg, seed=0, device="cpu")
+    layer.route(cfg, inp, b, logits_in=True)
+    layer.dispatch(cfg, b)
+    r = layer.alloc_reroute_buffers(cfg)
+    lm.reroute(b.logits, None, b.topk_idx, b.topk_gate, b.offsets, b.inv, T, E, k, C, mode,
+               r.topk_idx, r.topk_gate, r.offsets, r.perm, r.inv, r.n_dropped, b.workspace)
+    torch.cuda.synchronize()
+    idx = O.select_topk(L, k)
+    ref = O.dispatch_reroute(L, idx, E, C)
+    _check_layout(r, *ref)
+    got = P.np32(r.topk_gate)
+    assert np.all(np.isfinite(got))
+    np.testing.assert_allclose(got, O.gate_weights(L, ref[0], mode), atol=1e-6, rtol=0)
+
+
 REROUTE_LAYER = [
     # T, d, E, k, d_ff, dtype, gating, C, shared, zipf
     (300, 128, 8, 2, 192, "bf16", "softmax_topk", 60, 0, 0.0),
