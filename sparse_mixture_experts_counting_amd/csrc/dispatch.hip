@@ -124,6 +124,92 @@ __global__ __launch_bounds__(kThreads) void dispatch_scatter_kernel(
   }
 }
 
+// The three passes in one block of 1024 threads for at most one chunk of assignments (A <= 2048,
+// decode-sized batches), where the launches, not the work, would set the time: the histogram and
+// the scan as above with a single chunk (its first assignment to e is e's first), then the
+// stable scatter by the first four waves exactly as dispatch_scatter_kernel ranks them (the other
+// waves only take part in the barriers).  The same integers as the three-kernel path.
+__global__ __launch_bounds__(1024) void dispatch_one_chunk_kernel(
+    const int32_t* __restrict__ idx, int A, int E, int nbits, int capacity,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ perm,
+    int32_t* __restrict__ inv, int32_t* __restrict__ n_dropped) {
+  __shared__ int32_t h[1024];
+  __shared__ int32_t sc[1024];
+  __shared__ int32_t run[1024];
+  const int tid = threadIdx.x;
+  h[tid] = 0;
+  run[tid] = 0;
+  __syncthreads();
+  for (int a = tid; a < A; a += 1024) {
+    const int e = idx[a];
+    if (e >= 0 && e < E) atomicAdd(&h[e], 1);
+  }
+  __syncthreads();
+  int kept = 0;
+  if (tid < E) {
+    counts[tid] = h[tid];
+    kept = (capacity > 0 && h[tid] > capacity) ? capacity : h[tid];
+  }
+  sc[tid] = kept;
+  __syncthreads();
+  for (int o = 1; o < 1024; o <<= 1) {
+    const int v = (tid >= o) ? sc[tid - o] : 0;
+    __syncthreads();
+    sc[tid] += v;
+    __syncthreads();
+  }
+  const int off = sc[tid] - kept;   // exclusive prefix of kept at expert tid
+  if (tid < E) offsets[tid] = off;
+  if (tid == 0) {
+    offsets[E] = sc[1023];
+    n_dropped[0] = A - sc[1023];
+  }
+  __syncthreads();
+  h[tid] = off;                     // h now holds each expert's first row
+  __syncthreads();
+  const bool scatter = tid < kThreads;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  for (int r0 = 0; r0 < A; r0 += kThreads) {
+    const int a = r0 + tid;
+    int e = -1;
+    if (scatter && a < A) {
+      e = idx[a];
+      if (e < 0 || e >= E) {
+        inv[a] = -1;
+        e = -1;
+      }
+    }
+    const bool valid = e >= 0;
+    uint64_t peers = __ballot(valid);
+    for (int b = 0; b < nbits; ++b) {
+      const bool bit = valid && ((e >> b) & 1);
+      const uint64_t m = __ballot(bit);
+      peers &= bit ? m : ~m;
+    }
+    const int below = __popcll(peers & lanemask_lt());
+    const int total = __popcll(peers);
+    int rank = 0;
+    for (int w = 0; w < kThreads / 64; ++w) {
+      if (wave == w && valid) {
+        const int b = run[e];
+        rank = b + below;
+        if (below == 0) run[e] = b + total;
+      }
+      __syncthreads();
+    }
+    if (valid) {
+      if (capacity <= 0 || rank < capacity) {
+        const int pos = h[e] + rank;
+        perm[pos] = a;
+        inv[a] = pos;
+      } else {
+        inv[a] = -1;
+      }
+    }
+  }
+}
+
 size_t dispatch_workspace_bytes(int A, int E) {
   const size_t nchunk = (size_t)(A + kChunk - 1) / kChunk;
   return nchunk * E * sizeof(int32_t) + 256;
@@ -161,6 +247,11 @@ void launch_dispatch(const int32_t* topk_idx, int A, int E, int capacity, int32_
   const int nchunk = (A + kChunk - 1) / kChunk;
   int nbits = 0;
   while ((1 << nbits) < E) ++nbits;
+  if (nchunk == 1) {
+    hipLaunchKernelGGL(dispatch_one_chunk_kernel, dim3(1), dim3(1024), 0, s, topk_idx, A, E,
+                       nbits, capacity, counts, offsets, perm, inv, n_dropped);
+    return;
+  }
   hipLaunchKernelGGL(dispatch_hist_kernel, dim3(nchunk), dim3(kThreads), 0, s, topk_idx, A, E,
                      nchunk, hist);
   hipLaunchKernelGGL(dispatch_scan_kernel, dim3(1), dim3(1024), 0, s, hist, E, nchunk, A, capacity,

@@ -1011,10 +1011,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_bf16_kernel(const G
     const TileScan ts = scan_tiles<BM>(p, NT);
     const TailPlan tp = tail_plan(ts.total, p.slots, p.K);
     if ((int)blockIdx.x < tp.full) {
-      tile_at<BM>(p, NT, ts,
-                  p.slots >= 8 ? xcd_round_order(blockIdx.x, tp.full, p.slots / 8 * 8)
-                               : xcd_order(blockIdx.x, tp.full),
-                  tc);
+      tile_at<BM>(p, NT, ts, xcd_order(blockIdx.x, tp.full), tc);
     } else {
       const int w = blockIdx.x - tp.full;
       rtile = w / tp.q;

@@ -16,6 +16,7 @@ void launch_gate_topk(const float* logits, const float* select_bias, int T, int 
                       int32_t* topk_idx, float* topk_gate, float* part_p, float* part_l,
                       float* prob_sum, float* lse_sq_sum, hipStream_t s);
 size_t route_workspace_bytes(int T, int E);
+
 int gate_rows_per_block(int T);
 
 // dispatch.hip

@@ -11,8 +11,8 @@ namespace moe {
 // ---------------------------------------------------------------------------------------------
 // Router product for E <= 16 experts: logits[t, e] = sum_j x[t, j] w_r[e, j] (+ bias[e]), W_r in
 // the [E][d] layout of a linear layer.  Memory bound on x.  A block of 4 waves takes TPB = 64 / EP
-// tokens (EP = E rounded up to a power of two, at least 4), so that its TPB x EP (token, expert)
-// sums are one per lane; the waves split d in four, and lanes stride over 8-wide slices of their
+// tokens (EP = E rounded up to a power of two, at least 4; or 64 for one token per block when the
+// batch is small), so that its TPB x EP (token, expert) sums are one per lane; the waves split d in four, and lanes stride over 8-wide slices of their
 // quarter (16-byte loads of x and of every W_r row; d is a multiple of 8).  Each lane's 64 partial
 // sums are reduced across the wave by a butterfly that halves the values a lane carries at every
 // step (63 lane exchanges in all), leaving lane l with the total of sum l; the four waves' totals
@@ -34,12 +34,12 @@ __device__ __forceinline__ void load8(const TIn* p, float* f) {
   }
 }
 
-template <typename TIn, int E>
+template <typename TIn, int E, int EP>
 __global__ __launch_bounds__(256) void router_small_e_kernel(const TIn* __restrict__ x,
                                                              const TIn* __restrict__ w_r,
                                                              const float* __restrict__ bias, int T,
                                                              int d, float* __restrict__ logits) {
-  constexpr int EP = pow2_at_least<E>();
+  static_assert(EP >= E && EP <= 64 && (EP & (EP - 1)) == 0, "expert slots per token");
   constexpr int TPB = 64 / EP;
   __shared__ float part[4][64];
   const int lane = threadIdx.x & 63;
@@ -90,12 +90,20 @@ __global__ __launch_bounds__(256) void router_small_e_kernel(const TIn* __restri
   }
 }
 
+// A few hundred tokens or fewer: one token per block (64 expert slots, most of them idle), so
+// that the blocks spread over many CUs; otherwise TPB tokens per block as above.
 template <typename TIn, int E>
 static void launch_router_small_e_t(const void* x, const void* w_r, const float* bias, int T,
                                     int d, float* logits, hipStream_t s) {
-  constexpr int TPB = 64 / pow2_at_least<E>();
+  constexpr int EP = pow2_at_least<E>();
+  constexpr int TPB = 64 / EP;
+  if (T < 1024) {
+    hipLaunchKernelGGL((router_small_e_kernel<TIn, E, 64>), dim3(T), dim3(256), 0, s,
+                       (const TIn*)x, (const TIn*)w_r, bias, T, d, logits);
+    return;
+  }
   const int blocks = (T + TPB - 1) / TPB;
-  hipLaunchKernelGGL((router_small_e_kernel<TIn, E>), dim3(blocks), dim3(256), 0, s,
+  hipLaunchKernelGGL((router_small_e_kernel<TIn, E, EP>), dim3(blocks), dim3(256), 0, s,
                      (const TIn*)x, (const TIn*)w_r, bias, T, d, logits);
 }
 
@@ -185,6 +193,86 @@ __device__ __forceinline__ float from_ordered_bits(uint32_t o) {
   return __uint_as_float((o & 0x80000000u) ? (o ^ 0x80000000u) : ~o);
 }
 
+// Gating, top-k and the loss terms of one row t, by one wave.  `row` holds the row's E logits
+// (global memory or LDS); acc_p[i] (expert lane + 64 i) and acc_l accumulate the row's softmax
+// probabilities and squared logsumexp.
+template <int EPL>
+__device__ __forceinline__ void gate_row(const float* row, const float* __restrict__ select_bias,
+                                         int t, int E, int k, int mode,
+                                         int32_t* __restrict__ topk_idx,
+                                         float* __restrict__ topk_gate, float* acc_p,
+                                         float& acc_l) {
+  const int lane = threadIdx.x & 63;
+  float v[EPL];
+  uint64_t key[EPL];
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    const int e = lane + 64 * i;
+    if (e < E) {
+      v[i] = row[e];
+      const float score = select_bias ? v[i] + select_bias[e] : v[i];
+      key[i] = ((uint64_t)ordered_bits(score) << 32) | (uint32_t)(~e);
+    } else {
+      v[i] = -INFINITY;
+      key[i] = 0ull;
+    }
+  }
+  // Full-row softmax (for P_e) and logsumexp (for the z-loss).
+  float m = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) m = fmaxf(m, v[i]);
+  m = wave_max(m);
+  float ex[EPL];
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    ex[i] = (lane + 64 * i < E) ? expf(v[i] - m) : 0.f;
+    s += ex[i];
+  }
+  s = wave_sum(s);
+  const float inv_s = 1.0f / s;
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) acc_p[i] += ex[i] * inv_s;
+  const float lse = m + logf(s);
+  acc_l += lse * lse;
+
+  // Top-k by repeated wave arg-max over the keys.  v0 is the largest selected logit (the first
+  // one selected when there is no selection bias), the shift that keeps the gates finite.
+  int my_e = 0;
+  float my_v = -INFINITY;
+  for (int j = 0; j < k; ++j) {
+    uint64_t best = key[0];
+#pragma unroll
+    for (int i = 1; i < EPL; ++i) best = key[i] > best ? key[i] : best;
+    best = wave_max_u64(best);
+    const int e_j = (int)(~(uint32_t)best);
+    const float v_j = select_bias ? row[e_j] : from_ordered_bits((uint32_t)(best >> 32));
+#pragma unroll
+    for (int i = 0; i < EPL; ++i)
+      if (lane + 64 * i == e_j) key[i] = 0ull;
+    if (lane == j) {
+      my_e = e_j;
+      my_v = v_j;
+    }
+  }
+  const float v0 = wave_max(my_v);
+  float w = 0.f;
+  if (lane < k) {
+    if (mode == 0)
+      w = expf(my_v - v0);
+    else if (mode == 1)
+      w = expf(my_v - m) * inv_s;
+    else
+      w = expf(log_sigmoid(my_v) - log_sigmoid(v0));
+  }
+  float g = w;
+  if (mode != 1) g = w / wave_sum(w);
+  if (lane < k) {
+    topk_idx[(size_t)t * k + lane] = my_e;
+    topk_gate[(size_t)t * k + lane] = g;
+  }
+}
+
 template <int EPL>
 __global__ __launch_bounds__(256) void gate_topk_kernel(const float* __restrict__ logits,
                                                         const float* __restrict__ select_bias,
@@ -205,78 +293,9 @@ __global__ __launch_bounds__(256) void gate_topk_kernel(const float* __restrict_
 #pragma unroll
   for (int i = 0; i < EPL; ++i) acc_p[i] = 0.f;
   float acc_l = 0.f;
-
-  for (int t = row0 + wave; t < row1; t += 4) {
-    const float* row = logits + (size_t)t * E;
-    float v[EPL];
-    uint64_t key[EPL];
-#pragma unroll
-    for (int i = 0; i < EPL; ++i) {
-      const int e = lane + 64 * i;
-      if (e < E) {
-        v[i] = row[e];
-        const float score = select_bias ? v[i] + select_bias[e] : v[i];
-        key[i] = ((uint64_t)ordered_bits(score) << 32) | (uint32_t)(~e);
-      } else {
-        v[i] = -INFINITY;
-        key[i] = 0ull;
-      }
-    }
-    // Full-row softmax (for P_e) and logsumexp (for the z-loss).
-    float m = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < EPL; ++i) m = fmaxf(m, v[i]);
-    m = wave_max(m);
-    float ex[EPL];
-    float s = 0.f;
-#pragma unroll
-    for (int i = 0; i < EPL; ++i) {
-      ex[i] = (lane + 64 * i < E) ? expf(v[i] - m) : 0.f;
-      s += ex[i];
-    }
-    s = wave_sum(s);
-    const float inv_s = 1.0f / s;
-#pragma unroll
-    for (int i = 0; i < EPL; ++i) acc_p[i] += ex[i] * inv_s;
-    const float lse = m + logf(s);
-    acc_l += lse * lse;
-
-    // Top-k by repeated wave arg-max over the keys.  v0 is the largest selected logit (the first
-    // one selected when there is no selection bias), the shift that keeps the gates finite.
-    int my_e = 0;
-    float my_v = -INFINITY;
-    for (int j = 0; j < k; ++j) {
-      uint64_t best = key[0];
-#pragma unroll
-      for (int i = 1; i < EPL; ++i) best = key[i] > best ? key[i] : best;
-      best = wave_max_u64(best);
-      const int e_j = (int)(~(uint32_t)best);
-      const float v_j = select_bias ? row[e_j] : from_ordered_bits((uint32_t)(best >> 32));
-#pragma unroll
-      for (int i = 0; i < EPL; ++i)
-        if (lane + 64 * i == e_j) key[i] = 0ull;
-      if (lane == j) {
-        my_e = e_j;
-        my_v = v_j;
-      }
-    }
-    const float v0 = wave_max(my_v);
-    float w = 0.f;
-    if (lane < k) {
-      if (mode == 0)
-        w = expf(my_v - v0);
-      else if (mode == 1)
-        w = expf(my_v - m) * inv_s;
-      else
-        w = expf(log_sigmoid(my_v) - log_sigmoid(v0));
-    }
-    float g = w;
-    if (mode != 1) g = w / wave_sum(w);
-    if (lane < k) {
-      topk_idx[(size_t)t * k + lane] = my_e;
-      topk_gate[(size_t)t * k + lane] = g;
-    }
-  }
+  for (int t = row0 + wave; t < row1; t += 4)
+    gate_row<EPL>(logits + (size_t)t * E, select_bias, t, E, k, mode, topk_idx, topk_gate, acc_p,
+                  acc_l);
 
   if (part_p) {
 #pragma unroll

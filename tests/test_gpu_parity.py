@@ -217,6 +217,11 @@ SWEEP = [
     (7, 512, 3, 2, 1024, "bf16", "softmax_all", 3, 0, 0.0),
     # decode-sized groups (weight-streaming kernel): N not a multiple of 32, groups past 32 rows
     (24, 192, 8, 2, 200, "bf16", "softmax_topk", 0, 1, 0.0),
+    # decode-sized batches (one token per router block, the one-block dispatch of at most 2048
+    # assignments): logit bias, all three gating modes, drops, k = E, fp32
+    (50, 64, 8, 3, 64, "bf16", "sigmoid_topk", 0, 0, 1.1),
+    (64, 72, 5, 5, 48, "bf16", "softmax_all", 20, 0, 0.0),
+    (61, 40, 7, 2, 56, "fp32", "softmax_topk", 9, 1, 0.0),
     (128, 128, 32, 2, 192, "bf16", "softmax_topk", 0, 0, 1.2),
     # at least 512 rows per expert: 256-row tiles (8 waves), ragged and even K, N past one tile
     (2600, 136, 2, 2, 264, "bf16", "softmax_all", 0, 0, 0.0),
@@ -361,15 +366,16 @@ def test_update_select_bias_exact(M):
                                                                           1e-3))
 
 
+@pytest.mark.parametrize("T,E", [(300, 16), (40, 8)])
 @pytest.mark.parametrize("mode", ["softmax_topk", "sigmoid_topk"])
-def test_layer_with_select_bias(M, mode):
+def test_layer_with_select_bias(M, mode, T, E):
     """A whole layer whose expert selection is biased; routing, dispatch, gates, y and losses
-    against the oracle given the same bias."""
+    against the oracle given the same bias (T = 40: the small-batch router and dispatch)."""
     import dataclasses
-    _say("layer with select bias", mode)
-    cfg = M["synth"].tiny_config(300, 128, 16, 2, 192, "bf16", mode)
+    _say("layer with select bias", mode, T, E)
+    cfg = M["synth"].tiny_config(T, 128, E, 2, 192, "bf16", mode)
     inp = M["synth"].make_inputs(cfg, seed=12, device="cpu")
-    sb = torch.from_numpy(np.random.default_rng(5).normal(0, 0.5, size=16).astype(np.float32))
+    sb = torch.from_numpy(np.random.default_rng(5).normal(0, 0.5, size=E).astype(np.float32))
     inp = _to_cuda(dataclasses.replace(inp, select_bias=sb))
     run_and_compare(M, cfg, inp)
 
