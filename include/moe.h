@@ -15,12 +15,9 @@
  *     library never allocates or frees device memory and never synchronises the host.  Buffers
  *     must stay valid until the work enqueued on `stream` has finished.
  *   - `stream` is a hipStream_t passed as void*; NULL means the default stream.  Every call only
- *     enqueues work ordered on that stream and returns.  (The expert products of groups averaging
- *     256 to 512 rows run part of their tiles on a second stream that the library creates for
- *     each caller stream on that stream's first such call outside stream capture, forked from
- *     `stream` and joined back to it with events inside the same call, so the work still
- *     completes in `stream` order; a call on a stream being captured that has no such stream
- *     yet runs both parts on `stream`.)
+ *     enqueues work ordered on that stream and returns.  The library creates no streams or
+ *     events of its own, so calls on different streams are independent and any call can be
+ *     captured into a HIP graph.
  *   - Outputs are fully overwritten (no accumulate-into semantics) and must not alias inputs.
  *   - Integers are int32, row-major everywhere.  T tokens, d model width, E routed experts, k
  *     experts per token, d_ff expert width; assignment a = t*k + s for slot s of token t.

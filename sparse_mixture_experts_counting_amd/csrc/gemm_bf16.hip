@@ -39,7 +39,6 @@
 #include <algorithm>
 #include <atomic>
 #include <climits>
-#include <mutex>
 #include <type_traits>
 
 namespace moe {
@@ -1138,10 +1137,16 @@ __device__ __forceinline__ bool bs_tile(const GemmParams& p, int NT, int bid, Ti
   return true;
 }
 
-template <int EPI>
+// Tile shapes of the block-sparse launch per epilogue: two weight matrices of 128 columns each
+// (SwiGLU forward, SwiGLU backward), else one of 256; the tall tile's wave layout is that of the
+// ordinary launch (4 x 2, or 2 x 4 for weights read transposed).
+constexpr int bs_nmat(int epi) { return epi_swiglu(epi) || epi == EPI_SWIGLU_BWD ? 2 : 1; }
+constexpr int bs_bn(int epi) { return bs_nmat(epi) == 2 ? 128 : 256; }
+
+template <int EPI, bool BT>
 __global__ __launch_bounds__(512, 1) void gemm_bs_kernel(const GemmParams p) {
-  constexpr int NMAT = epi_swiglu(EPI) ? 2 : 1;
-  constexpr int BN = epi_swiglu(EPI) ? 128 : 256;   // columns per matrix, both tile kinds
+  constexpr int NMAT = bs_nmat(EPI);
+  constexpr int BN = bs_bn(EPI);                     // columns per matrix, both tile kinds
   const int NT = (p.N + BN - 1) / BN;
   TileCoord tc;
   if (!bs_tile(p, NT, blockIdx.x, tc)) return;
@@ -1150,9 +1155,10 @@ __global__ __launch_bounds__(512, 1) void gemm_bs_kernel(const GemmParams p) {
   tc.row_end = __builtin_amdgcn_readfirstlane(tc.row_end);
   tc.n_tile = __builtin_amdgcn_readfirstlane(tc.n_tile);
   if (tc.row_end - tc.row0 <= kBsThin)
-    gemm_tile<kBsThin, BN, NMAT, 2, 4, 64, 4, 1, EPI, false>(p, tc, 0, 1, -1, 0, 0);
+    gemm_tile<kBsThin, BN, NMAT, 2, 4, 64, 4, 1, EPI, false, BT>(p, tc, 0, 1, -1, 0, 0);
   else
-    gemm_tile<kBsTall, BN, NMAT, 4, 2, 64, 2, 1, EPI, false>(p, tc, 0, 1, -1, 0, 0);
+    gemm_tile<kBsTall, BN, NMAT, BT ? 2 : 4, BT ? 4 : 2, 64, 2, 1, EPI, false, BT>(p, tc, 0, 1,
+                                                                                    -1, 0, 0);
 }
 
 // Sum the K-chunk partials of every valid row in a fixed order and apply the epilogue.
@@ -1288,89 +1294,6 @@ static int device_cus() {
   return c > 0 ? c : 0;
 }
 
-// Side streams for work that runs beside a caller's stream.  Each (device, caller stream) pair
-// gets its own side stream (default priority, non-blocking) and a small ring of fork / join event
-// pairs, so two caller streams never share a side stream and a capture on one caller stream never
-// pulls in another caller's work.  Slots are created outside stream capture only (a call made
-// while its stream is capturing and that has no slot yet runs its parts one after the other on the
-// caller's stream) and live until the process ends.  A call whose stream is itself a side stream
-// does not fork again.  The mutex guards only the slot table; the launches run outside it.
-namespace {
-constexpr int kSideRing = 4;
-constexpr int kMaxSideSlots = 64;
-struct SideSlot {
-  int dev = -1;
-  hipStream_t caller = nullptr;
-  hipStream_t side = nullptr;
-  hipEvent_t fork[kSideRing] = {};
-  hipEvent_t join[kSideRing] = {};
-  unsigned next = 0;
-};
-std::mutex g_side_mutex;
-SideSlot g_side[kMaxSideSlots];
-int g_side_used = 0;
-}  // namespace
-
-// Picks the side stream and the fork / join events for one call on stream s; false when the call
-// must not fork (no slot, a nested call, or creation failed).
-static bool side_slot(hipStream_t s, hipStream_t& side, hipEvent_t& fork, hipEvent_t& join) {
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return false;
-  std::lock_guard<std::mutex> lock(g_side_mutex);
-  SideSlot* slot = nullptr;
-  for (int i = 0; i < g_side_used; ++i) {
-    if (g_side[i].side == s) return false;             // already on a side stream
-    if (g_side[i].dev == dev && g_side[i].caller == s) slot = &g_side[i];
-  }
-  if (!slot) {
-    if (g_side_used == kMaxSideSlots) return false;
-    // (The legacy default stream, NULL, is never captured.)
-    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-    if (s != nullptr &&
-        (hipStreamIsCapturing(s, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone))
-      return false;
-    SideSlot fresh;
-    fresh.dev = dev;
-    fresh.caller = s;
-    bool ok = hipStreamCreateWithFlags(&fresh.side, hipStreamNonBlocking) == hipSuccess;
-    for (int i = 0; ok && i < kSideRing; ++i)
-      ok = hipEventCreateWithFlags(&fresh.fork[i], hipEventDisableTiming) == hipSuccess &&
-           hipEventCreateWithFlags(&fresh.join[i], hipEventDisableTiming) == hipSuccess;
-    if (!ok) {
-      for (int i = 0; i < kSideRing; ++i) {
-        if (fresh.fork[i]) (void)hipEventDestroy(fresh.fork[i]);
-        if (fresh.join[i]) (void)hipEventDestroy(fresh.join[i]);
-      }
-      if (fresh.side) (void)hipStreamDestroy(fresh.side);
-      return false;
-    }
-    g_side[g_side_used] = fresh;
-    slot = &g_side[g_side_used++];
-  }
-  const unsigned i = slot->next++ % kSideRing;
-  side = slot->side;
-  fork = slot->fork[i];
-  join = slot->join[i];
-  return true;
-}
-
-// Queues side(side stream) after the work already queued on s, then main(s), then makes s wait for
-// the side work.  Returns false (queueing nothing) when this call does not fork.
-template <typename FS, typename FM>
-static bool run_beside(hipStream_t s, FS&& side_fn, FM&& main_fn, hipError_t& err) {
-  hipStream_t side = nullptr;
-  hipEvent_t fork = nullptr, join = nullptr;
-  if (!side_slot(s, side, fork, join)) return false;
-  if ((err = hipEventRecord(fork, s)) != hipSuccess) return true;
-  if ((err = hipStreamWaitEvent(side, fork, 0)) != hipSuccess) return true;
-  err = side_fn(side);
-  const hipError_t e1 = hipEventRecord(join, side);
-  const hipError_t e2 = main_fn(s);
-  const hipError_t e3 = hipStreamWaitEvent(s, join, 0);
-  if (err == hipSuccess) err = e1 != hipSuccess ? e1 : (e2 != hipSuccess ? e2 : e3);
-  return true;
-}
-
 template <int BM, int BN, int NMAT, int WGM, int WGN, int BK, int NST, int MINB, int EPI, bool TAIL,
           bool BT = false, bool AT = false>
 static hipError_t launch_t(const GemmParams& p, int rows_max, hipStream_t s) {
@@ -1409,14 +1332,12 @@ static hipError_t launch_t(const GemmParams& p, int rows_max, hipStream_t s) {
   return hipGetLastError();
 }
 
-// The block-sparse launch (forward epilogues: SwiGLU, SwiGLU storing a and b, plain bf16 store).
-template <int EPI>
+// The block-sparse launch (every bf16-output epilogue, weights K-contiguous or transposed).
+template <int EPI, bool BT>
 static hipError_t launch_bs_t(const GemmParams& p, int rows_max, hipStream_t s) {
-  auto kern = gemm_bs_kernel<EPI>;
-  static_assert(lds_bytes<kBsThin, epi_swiglu(EPI) ? 128 : 256, epi_swiglu(EPI) ? 2 : 1, 64, 4,
-                          1>() == kMaxLds &&
-                    lds_bytes<kBsTall, epi_swiglu(EPI) ? 128 : 256, epi_swiglu(EPI) ? 2 : 1, 64,
-                              2, 1>() == kMaxLds,
+  auto kern = gemm_bs_kernel<EPI, BT>;
+  static_assert(lds_bytes<kBsThin, bs_bn(EPI), bs_nmat(EPI), 64, 4, 1>() == kMaxLds &&
+                    lds_bytes<kBsTall, bs_bn(EPI), bs_nmat(EPI), 64, 2, 1>() == kMaxLds,
                 "both tile kinds fill the LDS the launch asks for");
   static std::atomic<bool> attr_set[64];
   int dev = 0;
@@ -1430,7 +1351,7 @@ static hipError_t launch_bs_t(const GemmParams& p, int rows_max, hipStream_t s) 
   GemmParams q = p;
   q.ksplit = 1;
   q.slots = device_cus() / 8 * 8;   // one block per CU: the blocks of one round
-  const int NT = (p.N + (epi_swiglu(EPI) ? 128 : 256) - 1) / (epi_swiglu(EPI) ? 128 : 256);
+  const int NT = (p.N + bs_bn(EPI) - 1) / bs_bn(EPI);
   // Every group yields at most floor(n_g / 256) + 1 tiles per column tile.
   const int grid = tiles_upper_bound(rows_max, p.G, true, kBsTall, NT);
   if (grid <= 0) return hipSuccess;
@@ -1440,9 +1361,15 @@ static hipError_t launch_bs_t(const GemmParams& p, int rows_max, hipStream_t s) 
 
 static hipError_t launch_bs(const GemmParams& p, int rows_max, int epi, hipStream_t s) {
   switch (epi) {
-    case EPI_SWIGLU: return launch_bs_t<EPI_SWIGLU>(p, rows_max, s);
-    case EPI_SWIGLU_SAVE: return launch_bs_t<EPI_SWIGLU_SAVE>(p, rows_max, s);
-    case EPI_STORE: return launch_bs_t<EPI_STORE>(p, rows_max, s);
+    case EPI_SWIGLU: return launch_bs_t<EPI_SWIGLU, false>(p, rows_max, s);
+    case EPI_SWIGLU_SAVE: return launch_bs_t<EPI_SWIGLU_SAVE, false>(p, rows_max, s);
+    case EPI_SWIGLU_BWD: return launch_bs_t<EPI_SWIGLU_BWD, false>(p, rows_max, s);
+    case EPI_STORE:
+      return p.bt ? launch_bs_t<EPI_STORE, true>(p, rows_max, s)
+                  : launch_bs_t<EPI_STORE, false>(p, rows_max, s);
+    case EPI_SWIGLU_BWD_SAVED:
+      return p.bt ? launch_bs_t<EPI_SWIGLU_BWD_SAVED, true>(p, rows_max, s)
+                  : launch_bs_t<EPI_SWIGLU_BWD_SAVED, false>(p, rows_max, s);
     default: return hipErrorNotSupported;
   }
 }
@@ -1632,35 +1559,13 @@ hipError_t launch_gemm_bf16(const GemmParams& p_in, int rows_max, int epi, hipSt
   hipError_t e;
   const bool skewed = big && grouped && p.ksplit == 1 && epi != EPI_STORE_F32_BIAS &&
                      (long long)rows_max < 512ll * p.G;
-  if (big && grouped && p.ksplit == 1 && !p.bt &&
-      (epi_swiglu(epi) || (skewed && epi == EPI_STORE))) {
-    // Forward products: one block-sparse launch of tall and thin tiles.  The SwiGLU up projection
-    // takes it whenever the groups fill 256-row tiles (its few-row remainders run as thin tiles);
-    // the down projection only for skewed groups (with a few hundred rows per group on average:
-    // evenly filled groups give it too few tiles, whose last round the K-split tiling balances).
+  if (big && grouped && p.ksplit == 1 && epi != EPI_STORE_F32_BIAS &&
+      (skewed || epi_swiglu(epi))) {
+    // One block-sparse launch of tall and thin tiles: every product of skewed groups (a few
+    // hundred rows per group on average), and the SwiGLU up projection whenever the groups fill
+    // 256-row tiles (its few-row remainders run as thin tiles).  Evenly filled groups give the
+    // other products too few tiles, whose last round the K-split tiling balances.
     e = launch_bs(p, rows_max, epi, s);
-  } else if (skewed) {
-    // The backward's products of skewed groups (transposed weights, SwiGLU-derivative epilogues):
-    // the rows of every group that fill whole 256-row tiles run in 256-row tiles, the rest (under
-    // 256 rows per group) in 128-row tiles, two blocks per CU, where a short group wastes less.
-    // The short tiles of the many small groups are bound by streaming those experts' weights, the
-    // tall ones by the matrix cores, so the two launches run side by side on two streams.  Only
-    // the tall launch splits its last round over K (the scratch is not shared).
-    GemmParams p1 = p, p2 = p;
-    p1.row_split = p2.row_split = 256;
-    p1.part_mode = 1;
-    p2.part_mode = 2;
-    p2.part = nullptr;
-    // At most two 128-row tiles per group: the grid bound of 128 G rows covers them.
-    const int rows2 = (int)std::min<long long>(rows_max, 128ll * p.G);
-    e = hipSuccess;
-    const bool beside = run_beside(
-        s, [&](hipStream_t side) { return launch_cfg(p2, rows2, epi, false, side); },
-        [&](hipStream_t main) { return launch_cfg(p1, rows_max, epi, true, main); }, e);
-    if (!beside) {
-      if ((e = launch_cfg(p1, rows_max, epi, true, s)) != hipSuccess) return e;
-      e = launch_cfg(p2, rows2, epi, false, s);
-    }
   } else {
     e = launch_cfg(p, rows_max, epi, big, s);
   }

@@ -58,11 +58,6 @@ struct GemmParams {
   int bt_k1;
   // Transposed A (at != 0, K-grouped only, with bt): A is stored [K][M] (row stride lda).
   int at;
-  // Row parts of a grouped product run as two launches (part 1 in tall tiles, part 2 in short
-  // ones): part_mode 1 takes the first floor(n_g / row_split) * row_split rows of every group,
-  // part_mode 2 the rest; 0 takes all rows.
-  int row_split;
-  int part_mode;
 };
 
 enum {
@@ -94,14 +89,10 @@ struct TileScan {
   int incl;     // tiles up to and including this lane's groups
 };
 
-// Rows [rs, re) of group g that this launch covers.
+// Rows [rs, re) of group g.
 __device__ __forceinline__ void group_range(const GemmParams& p, int g, int& rs, int& re) {
   rs = p.offsets[g];
   re = p.offsets[g + 1];
-  if (p.part_mode != 0) {
-    const int cut = rs + (re - rs) / p.row_split * p.row_split;
-    if (p.part_mode == 1) re = cut; else rs = cut;
-  }
 }
 
 template <int BM>

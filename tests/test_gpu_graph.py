@@ -1,12 +1,10 @@
 """The layer's forward and backward captured into a HIP graph and replayed (needs an MI355X).
 
 Serving loops capture a fixed-shape layer once and replay it.  Every entry point only enqueues
-work (no host synchronisation, no allocation, no memset); the grouped products of groups
-averaging 256-512 rows fork part of their tiles onto the side stream the library keeps for the
-caller's stream and join it back, which the capture must follow (the warm-up runs on the capture
-stream itself, so that its side stream exists before the capture).  Each replay, with eager work
-and synchronisations in between, must reproduce the eager results bit for bit (the kernels are
-deterministic).
+work on the caller's stream (no host synchronisation, no allocation, no memset, no stream of the
+library's own); the warm-up runs on the capture stream itself, as torch asks.  Each replay, with
+eager work and synchronisations in between, must reproduce the eager results bit for bit (the
+kernels are deterministic).
 """
 
 import pytest
@@ -28,7 +26,7 @@ def M():
 CASES = [
     # T, d, E, k, d_ff, gating, C, shared, zipf
     (300, 128, 8, 2, 192, "softmax_topk", 0, 0, 0.0),        # 128-row tiles
-    (700, 256, 4, 2, 512, "softmax_topk", 0, 1, 1.1),        # tall + short tiles on two streams
+    (700, 256, 4, 2, 512, "softmax_topk", 0, 1, 1.1),        # block-sparse tall and thin tiles
     (257, 136, 8, 2, 264, "sigmoid_topk", 70, 0, 0.0),       # capacity drops, ragged shapes
 ]
 
@@ -87,9 +85,9 @@ def test_graph_replay_matches_eager(M, case, save):
 
 
 def test_two_caller_streams_concurrently(M):
-    """Two streams run the two-part tiling (tall and short tiles on each caller's own side stream)
-    at the same time on different buffers: each result is bit-identical to the same layer run
-    alone on the default stream."""
+    """Two streams run the block-sparse tiling (skewed groups of a few hundred rows) at the same
+    time on different buffers: each result is bit-identical to the same layer run alone on the
+    default stream."""
     print("two caller streams", flush=True)
     L, S = M["layer"], M["synth"]
     cfg = S.tiny_config(700, 256, 4, 2, 512, "bf16", "softmax_topk", n_shared=1, zipf_s=1.1)
