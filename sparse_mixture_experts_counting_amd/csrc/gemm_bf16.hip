@@ -826,7 +826,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, TileCoord tc, int
     // the output (the weight gradients, 4 bytes per weight) is not read again by this kernel and
     // would otherwise push the operand tiles out of the caches.  A K-split product writes its
     // chunk's partial sums the same way (no bias, cached stores) into its slice of the scratch.
-    const bool kpart = p.ksplit > 1;
+    const bool kpart = !AT && p.ksplit > 1;   // (the weight gradients never split)
     float* const Cout = kpart ? p.part + (size_t)kc * p.part_rows * N : (float*)Cg;
     const int ldo = kpart ? N : p.ldc;
     const float* const bias = kpart ? nullptr : p.bias;
@@ -1437,7 +1437,9 @@ static int splitk_factor(int rows_max, int G, bool grouped, int N, int K, int ep
   const int mt = grouped ? std::min(G, rows_max) + rows_max / BM : (rows_max + BM - 1) / BM;
   const long long tiles = (long long)mt * ((N + BN - 1) / BN);
   const int cus = device_cus();
-  const long long slots = 2ll * (cus > 0 ? cus : 256);   // two 128-row blocks per CU
+  // Two work items per CU: the transposed-weight short tiles run two blocks per CU, the others
+  // one block per CU over two rounds (measured no slower on the weight stream than one round).
+  const long long slots = 2ll * (cus > 0 ? cus : 256);
   if (tiles >= 2 * slots) return 1;
   // Fewer rows than a tile per group: weight streaming, bound by HBM; any full round keeps HBM
   // busy, so split only as far as one round needs (fewer partial sums to add).
@@ -1492,12 +1494,12 @@ static hipError_t launch_cfg(const GemmParams& p, int rows_max, int epi, bool bi
     case EPI_SWIGLU_SAVE:   // the same tiles, storing a and b beside h
       return big ? launch_tail_or_not<256, 128, 2, 4, 2, 64, 2, 1, EPI_SWIGLU_SAVE>(p, rows_max, s)
                  : launch_tail_or_not<128, 128, 2, 2, 2, 64, 3, 1, EPI_SWIGLU_SAVE>(p, rows_max, s);
-    case EPI_STORE:
+    case EPI_STORE:   // short tiles: 64-deep steps (128-byte runs per weight row), one block per CU
       if (p.bt)
         return big ? launch_tail_or_not<256, 256, 1, 2, 4, 64, 2, 1, EPI_STORE, true>(p, rows_max, s)
                    : launch_tail_or_not<128, 256, 1, 2, 2, 32, 3, 2, EPI_STORE, true>(p, rows_max, s);
       return big ? launch_tail_or_not<256, 256, 1, 4, 2, 64, 2, 1, EPI_STORE>(p, rows_max, s)
-                 : launch_tail_or_not<128, 256, 1, 2, 2, 32, 3, 2, EPI_STORE>(p, rows_max, s);
+                 : launch_tail_or_not<128, 256, 1, 2, 2, 64, 3, 1, EPI_STORE>(p, rows_max, s);
     case EPI_SWIGLU_BWD:
       return big ? launch_tail_or_not<256, 128, 2, 4, 2, 64, 2, 1, EPI_SWIGLU_BWD>(p, rows_max, s)
                  : launch_tail_or_not<128, 128, 2, 2, 2, 32, 3, 2, EPI_SWIGLU_BWD>(p, rows_max, s);
