@@ -322,6 +322,16 @@ def main():
         roof = {"bound": "hbm", "achieved": up_bytes / (up_ms * 1e-3) / 1e9,
                 "peak": PEAK_HBM_GBS, "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
+    # The up projection's launch: the block-sparse tall/thin tiling when the groups fill 256-row
+    # tiles (gemm_bs_kernel), else the grouped tiles (gemm_bf16_kernel, with a finish kernel for
+    # split partial sums); the fp32 layers run gemm_f32_kernel.
+    if cfg.dtype == "fp32":
+        up_kernel = "moe_expert_up: gemm_f32_kernel (SwiGLU epilogue)"
+    elif T * k >= 256 * E:
+        up_kernel = "moe_expert_up: gemm_bs_kernel (block-sparse tall/thin tiles, SwiGLU epilogue)"
+    else:
+        up_kernel = ("moe_expert_up: gemm_bf16_kernel (SwiGLU epilogue) + its split-K finish "
+                     "kernel")
     traffic = load_traffic(cfg.name)
     gg_ms = stage_ms["expert_up"] + stage_ms["expert_down"]
     result = {
@@ -343,9 +353,7 @@ def main():
                    "shared_experts": cfg.n_shared, "parallelism": "none (1 GPU)",
                    "cache": ("cold: a 1 GiB buffer overwritten before every step, outside its "
                              "events" if args.cold else "warm: steps back to back")},
-        "roofline": dict(roof, kernel="moe_expert_up: the grouped GEMM with the SwiGLU epilogue "
-                                      "(and its split-K finish kernel, when launched)",
-                         traffic=traffic),
+        "roofline": dict(roof, kernel=up_kernel, traffic=traffic),
         "grouped_gemm": {"ms": gg_ms, "tflops": (up_flops + down_flops) / (gg_ms * 1e-3) / 1e12,
                          "frac_bf16_peak": (up_flops + down_flops) / (gg_ms * 1e-3) / 1e12
                          / PEAK_BF16_TFLOPS},
