@@ -1037,6 +1037,8 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_bf16_kernel(const G
 //     256-row tiles followed by one tile for its remainder rows, so the remainder reuses the
 //     column tile's weight panel from L2 instead of streaming the expert's weights a second time;
 //   - a group with fewer than 256 rows ("small") gets one tile per column tile.
+// Inside a big group, row tiles go in bands (below) so that an XCD's chunk of a round shares
+// both its activation and its weight panels in L2.
 // A tile of at most 64 rows runs as a thin tile (64 x BN, 8 waves in 2 x 4, a 4-stage ring: 96 KB of
 // weights in flight per CU, for the weight-streaming tiles whose speed is set by bytes in flight);
 // any other tile as the tall 256-row tile of the matrix-bound path.  Both kinds are one launch: the
@@ -1127,11 +1129,21 @@ __device__ __forceinline__ bool bs_tile(const GemmParams& p, int NT, int bid, Ti
     tc.row0 = rs;
     tc.row_end = re;
     tc.n_tile = local;
-  } else {                             // whole 256-row tiles, then the remainder, per column tile
+  } else {
+    // A group's row tiles (whole 256-row tiles, then the remainder) in bands of GM, each band
+    // walked column tile by column tile: 32 consecutive tiles (one XCD's chunk of a round) then
+    // read GM activation panels and 32 / GM weight panels.  A group of at most 8 row tiles is
+    // one band (its remainder stays beside the whole tiles that share its weight panel); larger
+    // groups take bands of 4 (a 4 x 8 block: 12 panels instead of up to 33).
     const int n = re - rs;
     const int per_n = n / kBsTall + (n % kBsTall != 0);
-    tc.n_tile = local / per_n;
-    tc.row0 = rs + (local % per_n) * kBsTall;
+    const int GM = per_n <= 8 ? per_n : 4;
+    const int band = local / (GM * NT);
+    const int m_first = band * GM;
+    const int gm = min(per_n - m_first, GM);
+    const int in = local - band * GM * NT;
+    tc.n_tile = in / gm;
+    tc.row0 = rs + (m_first + in % gm) * kBsTall;
     tc.row_end = min(tc.row0 + kBsTall, re);
   }
   return true;
