@@ -72,11 +72,18 @@ __device__ __forceinline__ desc_t make_desc(const void* base, uint32_t num_recor
 // flight (it cannot tell the stages apart) before each of them.  No register is written; the
 // loads are waited for by the explicit vmcnt waits of the main loop.  The load reads M0, which
 // needs one wait state after the scalar write (the compiler inserts it for its own loads).
+template <bool NTL>
 __device__ __forceinline__ void dma16(desc_t desc, uint32_t voff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
-               :
-               : "v"(voff), "s"(desc), "s"(lds)
-               : "memory", "m0");
+  if constexpr (NTL)
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen nt lds"
+                 :
+                 : "v"(voff), "s"(desc), "s"(lds)
+                 : "memory", "m0");
+  else
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+                 :
+                 : "v"(voff), "s"(desc), "s"(lds)
+                 : "memory", "m0");
 }
 
 // Physical 16-byte unit of logical unit u in LDS row r is u ^ swz(r).  Both forms depend on r % 32
@@ -168,9 +175,12 @@ __device__ __forceinline__ TailPlan tail_plan(int total, int slots, int K) {
 // One output tile: the K loop over the block's range and the epilogue.  tc names the tile; kc /
 // nsplit its K chunk when the tile is split (rtile >= 0: a split tile of the last round, written as
 // tile-local partials); kg_beg / kg_len the reduction rows in the K-grouped mode.  Every thread of
-// the block calls it with the same arguments.
+// the block calls it with the same arguments.  NTB: the weight (B) loads carry the non-temporal
+// hint (bit 1 of a buffer load's cache-policy operand), for launches that read every weight panel
+// once (the decode-sized products, bound by the weight stream: HBM serves such reads about 10%
+// faster); otherwise the default policy keeps panels that several row tiles share in the caches.
 template <int BM, int BN, int NMAT, int WGM, int WGN, int BK, int NST, int MINB, int EPI, bool TAIL,
-          bool BT = false, bool AT = false>
+          bool BT = false, bool AT = false, bool NTB = false>
 __device__ __forceinline__ void gemm_tile(const GemmParams& p, TileCoord tc, int kc, int nsplit,
                                           int rtile, int kg_beg, int kg_len) {
   constexpr int NTHR = 64 * WGM * WGN;
@@ -199,6 +209,14 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, TileCoord tc, int
   constexpr int DROWS = 1024 / RB;
   constexpr int DPW = (BM + NMAT * BN) / (DROWS * NW);   // direct loads per wave per step
   constexpr int DPW_A = BM / (DROWS * NW);                // the first DPW_A of them are A rows
+  // The 256-row tiles with split rings (K-contiguous operands): only the first half of the waves
+  // (one per SIMD) issue the direct loads, twice as many each, so the other wave of every SIMD
+  // never stalls behind the loads' address processing and keeps the matrix core busy.
+  constexpr bool LSPLIT = DMA && NST == 2 && MINB == 1 && !BT && !AT &&
+                          2 * BM * BK * 2 + 3 * NMAT * BN * BK * 2 <= kMaxLds;
+  constexpr int NWL = LSPLIT ? NW / 2 : NW;               // waves that issue direct loads
+  constexpr int DPWL = LSPLIT ? 2 * DPW : DPW;             // direct loads per loading wave
+  constexpr int DPWL_A = LSPLIT ? 2 * DPW_A : DPW_A;
   static_assert(!DMA || (DPW_A * DROWS * NW == BM && DPW * DROWS * NW == BM + NMAT * BN &&
                          BN % (DROWS * NW) == 0), "direct loads split evenly");
   // Transposed B: a stage's B block is BK rows of RBT bytes; one direct load fills RPB rows.
@@ -274,15 +292,15 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, TileCoord tc, int
 
   // Direct loads: lane l of the load for stage block b = wave + NW j covers stage row
   // DROWS b + l / UPR at physical unit l % UPR, so it fetches the logical unit stored there.
-  uint32_t d_voff[DMA ? DPW : 1];
-  int d_kmax[DMA ? DPW : 1];            // the load reads zeros for steps starting at k0 >= d_kmax
+  uint32_t d_voff[DMA ? DPWL : 1];
+  int d_kmax[DMA ? DPWL : 1];           // the load reads zeros for steps starting at k0 >= d_kmax
   if constexpr (DMA) {
 #pragma unroll
-    for (int j = 0; j < DPW; ++j) {
-      const int srow = (wave + NW * j) * DROWS + lane / UPR;
+    for (int j = 0; j < DPWL; ++j) {
+      const int srow = (wave + NWL * j) * DROWS + lane / UPR;
       const int uu = (lane % UPR) ^ swz<BK>(srow);
       d_kmax[j] = 0;   // set below, once the K range is known
-      if (j < DPW_A) {
+      if (j < DPWL_A) {
         if constexpr (AT) {   // row kr of the stage's A block (a K row), columns m
           const int kr = (wave + NW * j) * RPA + lane / UPA;
           const int ua = (lane % UPA) ^ swzT(kr);
@@ -314,11 +332,11 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, TileCoord tc, int
   const int k_last = kbeg + (KT - 1) * BK;
   if constexpr (DMA) {
 #pragma unroll
-    for (int j = 0; j < DPW; ++j) {
-      const int srow = (wave + NW * j) * DROWS + lane / UPR;
+    for (int j = 0; j < DPWL; ++j) {
+      const int srow = (wave + NWL * j) * DROWS + lane / UPR;
       // Rows past the group's end (A) or past N (B) feed only results that are never stored:
       // they read zeros without touching memory.
-      const bool live = j < DPW_A ? tc.row0 + srow < tc.row_end : n_base + (srow - BM) % BN < N;
+      const bool live = j < DPWL_A ? tc.row0 + srow < tc.row_end : n_base + (srow - BM) % BN < N;
       d_kmax[j] = live ? kend - 8 * ((lane % UPR) ^ swz<BK>(srow)) : INT_MIN;
       if constexpr (BT) {
         if (j >= DPW_A) {   // a K row: live while k0 + kr < kend and its 8 columns lie below N
@@ -351,7 +369,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, TileCoord tc, int
     for (int i = 0; i < B_UNITS; ++i) {
       const bool second = NMAT == 2 && (ROWS_PER_LOAD * i) / BN == 1;   // static per i
       b_reg[set][i] = __builtin_amdgcn_raw_buffer_load_b128(
-          second ? rB1 : rB0, in_range ? b_voff[i] + koff : b_bytes, 0, 0);
+          second ? rB1 : rB0, in_range ? b_voff[i] + koff : b_bytes, 0, NTB ? 2 : 0);
     }
   };
   // Direct loads of the step starting at k0 into the stage at stage_off.  Units at or past the end
@@ -361,10 +379,11 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, TileCoord tc, int
   // stage, a B block to b_off + its offset (b_off is the B stage's address minus B_OFF).
   auto issue_dma_range = [&](int a_off, int b_off, int k0, auto J0, auto J1) {
     const uint32_t koff = (uint32_t)k0 * 2u;
+    if (LSPLIT && wave >= NWL) return;
 #pragma unroll
     for (int j = decltype(J0)::value; j < decltype(J1)::value; ++j) {
-      const bool is_a = j < DPW_A;
-      bool second = NMAT == 2 && !is_a && ((j - DPW_A) * DROWS * NW) / BN == 1;
+      const bool is_a = j < DPWL_A;
+      bool second = NMAT == 2 && !is_a && ((j - DPWL_A) * DROWS * NWL) / BN == 1;
       uint32_t step_off = koff;
       if constexpr (BT) {
         if (!is_a) {   // K rows: k0 moves along rows; past bt_k1 they come from B1
@@ -377,14 +396,20 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, TileCoord tc, int
       }
       const uint32_t voff = k0 < d_kmax[j] ? d_voff[j] + step_off : (is_a ? a_bytes : b_bytes);
       if constexpr (BT) {
-        dma16(is_a ? dA : (second ? dB1 : dB0), voff,
-              (uint32_t)(size_t)(lds_void_t*)(smem + (is_a ? a_off : b_off) +
-                                              (wave + NW * j) * 1024));
+        const uint32_t lds_at = (uint32_t)(size_t)(lds_void_t*)(smem + (is_a ? a_off : b_off) +
+                                                                (wave + NWL * j) * 1024);
+        if (is_a)
+          dma16<false>(dA, voff, lds_at);
+        else
+          dma16<NTB>(second ? dB1 : dB0, voff, lds_at);
       } else {
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(is_a ? rA : (second ? rB1 : rB0),
-                                                 (lds_void_t*)(smem + (is_a ? a_off : b_off) +
-                                                               (wave + NW * j) * 1024),
-                                                 16, (int)voff, 0, 0, 0);
+        lds_void_t* const lds_at =
+            (lds_void_t*)(smem + (is_a ? a_off : b_off) + (wave + NWL * j) * 1024);
+        if (is_a)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, lds_at, 16, (int)voff, 0, 0, 0);
+        else
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(second ? rB1 : rB0, lds_at, 16, (int)voff, 0, 0,
+                                                   NTB ? 2 : 0);
       }
     }
   };
@@ -529,10 +554,10 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, TileCoord tc, int
     // are in flight (vmcnt counts in issue order) leaves A(kt + 1) and B(kt + 1) landed.
     auto run_split = [&](auto MATH) {
       constexpr bool math = decltype(MATH)::value;
-      constexpr int DPW_B = DPW - DPW_A;
+      constexpr int DPW_B = DPWL - DPWL_A;
       const std::integral_constant<int, 0> j0;
-      const std::integral_constant<int, DPW_A> ja;
-      const std::integral_constant<int, DPW> j1;
+      const std::integral_constant<int, DPWL_A> ja;
+      const std::integral_constant<int, DPWL> j1;
       auto b_at = [&](int sb) { return NST * A_BYTES + sb * B_BYTES - B_OFF; };
       issue_dma_range(0, 0, kbeg, j0, ja);
       issue_dma_range(0, b_at(0), kbeg, ja, j1);
@@ -964,7 +989,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, TileCoord tc, int
 // The grouped GEMM kernel: each block finds its tile (K-grouped, every tile split over K, or whole
 // rounds with the last partial round split) and computes it.
 template <int BM, int BN, int NMAT, int WGM, int WGN, int BK, int NST, int MINB, int EPI, bool TAIL,
-          bool BT = false, bool AT = false>
+          bool BT = false, bool AT = false, bool NTB = false>
 __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_bf16_kernel(const GemmParams p) {
   const int NT = (p.N + BN - 1) / BN;
   TileCoord tc;
@@ -1025,8 +1050,8 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_bf16_kernel(const G
   tc.row_end = __builtin_amdgcn_readfirstlane(tc.row_end);
   tc.n_tile = __builtin_amdgcn_readfirstlane(tc.n_tile);
 
-  gemm_tile<BM, BN, NMAT, WGM, WGN, BK, NST, MINB, EPI, TAIL, BT, AT>(p, tc, kc, nsplit, rtile,
-                                                                     kg_beg, kg_len);
+  gemm_tile<BM, BN, NMAT, WGM, WGN, BK, NST, MINB, EPI, TAIL, BT, AT, NTB>(p, tc, kc, nsplit,
+                                                                          rtile, kg_beg, kg_len);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -1166,9 +1191,16 @@ __global__ __launch_bounds__(512, 1) void gemm_bs_kernel(const GemmParams p) {
   tc.row0 = __builtin_amdgcn_readfirstlane(tc.row0);
   tc.row_end = __builtin_amdgcn_readfirstlane(tc.row_end);
   tc.n_tile = __builtin_amdgcn_readfirstlane(tc.n_tile);
-  if (tc.row_end - tc.row0 <= kBsThin)
-    gemm_tile<kBsThin, BN, NMAT, 2, 4, 64, 4, 1, EPI, false, BT>(p, tc, 0, 1, -1, 0, 0);
-  else
+  if (tc.row_end - tc.row0 <= kBsThin) {
+    // A thin tile that starts its group is the whole of a small group, the only reader of its
+    // weight panel (non-temporal weight loads); else it is a big group's remainder, which shares
+    // the panel with the group's whole tiles.
+    if (tc.row0 == p.offsets[tc.g])
+      gemm_tile<kBsThin, BN, NMAT, 2, 4, 64, 4, 1, EPI, false, BT, false, true>(p, tc, 0, 1, -1, 0,
+                                                                               0);
+    else
+      gemm_tile<kBsThin, BN, NMAT, 2, 4, 64, 4, 1, EPI, false, BT>(p, tc, 0, 1, -1, 0, 0);
+  } else
     gemm_tile<kBsTall, BN, NMAT, BT ? 2 : 4, BT ? 4 : 2, 64, 2, 1, EPI, false, BT>(p, tc, 0, 1,
                                                                                     -1, 0, 0);
 }
@@ -1188,15 +1220,33 @@ __global__ __launch_bounds__(256) void splitk_finish_kernel(const GemmParams p) 
     for (int m = 0; m < NMAT; ++m)
 #pragma unroll
       for (int q = 0; q < 8; ++q) s[m][q] = 0.f;
-    for (int kc = 0; kc < p.ksplit; ++kc) {
+    // Chunks in groups of four: the group's loads are all issued before any of them is added, and
+    // the additions keep chunk order (the same sums as one chunk at a time).
+    constexpr int KG = 4;
+    for (int kc0 = 0; kc0 < p.ksplit; kc0 += KG) {
+      f32x4 a[KG][NMAT], b[KG][NMAT];
 #pragma unroll
-      for (int m = 0; m < NMAT; ++m) {
-        const f32x4* src = reinterpret_cast<const f32x4*>(
-            p.part + ((size_t)(kc * NMAT + m) * p.part_rows + row) * p.N + c0);
-        const f32x4 a = src[0], b = src[1];
-        s[m][0] += a[0]; s[m][1] += a[1]; s[m][2] += a[2]; s[m][3] += a[3];
-        s[m][4] += b[0]; s[m][5] += b[1]; s[m][6] += b[2]; s[m][7] += b[3];
-      }
+      for (int j = 0; j < KG; ++j)
+#pragma unroll
+        for (int m = 0; m < NMAT; ++m) {
+          if (kc0 + j < p.ksplit) {
+            const f32x4* src = reinterpret_cast<const f32x4*>(
+                p.part + ((size_t)((kc0 + j) * NMAT + m) * p.part_rows + row) * p.N + c0);
+            a[j][m] = src[0];
+            b[j][m] = src[1];
+          }
+        }
+#pragma unroll
+      for (int j = 0; j < KG; ++j)
+#pragma unroll
+        for (int m = 0; m < NMAT; ++m) {
+          if (kc0 + j < p.ksplit) {
+            s[m][0] += a[j][m][0]; s[m][1] += a[j][m][1];
+            s[m][2] += a[j][m][2]; s[m][3] += a[j][m][3];
+            s[m][4] += b[j][m][0]; s[m][5] += b[j][m][1];
+            s[m][6] += b[j][m][2]; s[m][7] += b[j][m][3];
+          }
+        }
     }
     if constexpr (EPI == EPI_STORE_F32_BIAS) {   // the router's fp32 logits (+ bias)
       float* dst = (float*)p.C + (size_t)row * p.ldc + c0;
@@ -1307,9 +1357,9 @@ static int device_cus() {
 }
 
 template <int BM, int BN, int NMAT, int WGM, int WGN, int BK, int NST, int MINB, int EPI, bool TAIL,
-          bool BT = false, bool AT = false>
+          bool BT = false, bool AT = false, bool NTB = false>
 static hipError_t launch_t(const GemmParams& p, int rows_max, hipStream_t s) {
-  auto kern = gemm_bf16_kernel<BM, BN, NMAT, WGM, WGN, BK, NST, MINB, EPI, TAIL, BT, AT>;
+  auto kern = gemm_bf16_kernel<BM, BN, NMAT, WGM, WGN, BK, NST, MINB, EPI, TAIL, BT, AT, NTB>;
   const size_t lds = (size_t)lds_bytes<BM, BN, NMAT, BK, NST, MINB>();
   static std::atomic<bool> attr_set[64];   // per device: the attribute is set on that device
   int dev = 0;
@@ -1387,13 +1437,13 @@ static hipError_t launch_bs(const GemmParams& p, int rows_max, int epi, hipStrea
 }
 
 template <int BM, int BN, int NMAT, int WGM, int WGN, int BK, int NST, int MINB, int EPI,
-          bool BT = false>
+          bool BT = false, bool NTB = false>
 static hipError_t launch_tail_or_not(const GemmParams& p, int rows_max, hipStream_t s) {
   // The direct-load path handles any K range; the register path needs an even step count.
   const bool even_steps = NST > 0 || (p.K / p.ksplit) % (2 * BK) == 0;
   return even_steps
-             ? launch_t<BM, BN, NMAT, WGM, WGN, BK, NST, MINB, EPI, false, BT>(p, rows_max, s)
-             : launch_t<BM, BN, NMAT, WGM, WGN, BK, NST, MINB, EPI, true, BT>(p, rows_max, s);
+             ? launch_t<BM, BN, NMAT, WGM, WGN, BK, NST, MINB, EPI, false, BT, false, NTB>(p, rows_max, s)
+             : launch_t<BM, BN, NMAT, WGM, WGN, BK, NST, MINB, EPI, true, BT, false, NTB>(p, rows_max, s);
 }
 
 static void launch_splitk_finish(const GemmParams& p, int rows_max, int epi, hipStream_t s) {
@@ -1498,10 +1548,16 @@ size_t gemm_bf16_partial_bytes(int rows_max, int G, bool grouped, int N, int K, 
 
 // The tile configuration of each epilogue: 256-row tiles (8 waves, one block per CU) or 128-row
 // tiles (4 waves, two blocks per CU).
-static hipError_t launch_cfg(const GemmParams& p, int rows_max, int epi, bool big, hipStream_t s) {
+// `streams`: the short tiles read every weight panel once (fewer rows per group than a tile), so
+// the forward products load their weights with the non-temporal hint.
+static hipError_t launch_cfg(const GemmParams& p, int rows_max, int epi, bool big, bool streams,
+                             hipStream_t s) {
   switch (epi) {
     case EPI_SWIGLU:   // short tiles: 64-deep steps (128-byte runs per weight row), one block per CU
-      return big ? launch_tail_or_not<256, 128, 2, 4, 2, 64, 2, 1, EPI_SWIGLU>(p, rows_max, s)
+      if (big) return launch_tail_or_not<256, 128, 2, 4, 2, 64, 2, 1, EPI_SWIGLU>(p, rows_max, s);
+      return streams
+                 ? launch_tail_or_not<128, 128, 2, 2, 2, 64, 3, 1, EPI_SWIGLU, false, true>(p, rows_max,
+                                                                                          s)
                  : launch_tail_or_not<128, 128, 2, 2, 2, 64, 3, 1, EPI_SWIGLU>(p, rows_max, s);
     case EPI_SWIGLU_SAVE:   // the same tiles, storing a and b beside h
       return big ? launch_tail_or_not<256, 128, 2, 4, 2, 64, 2, 1, EPI_SWIGLU_SAVE>(p, rows_max, s)
@@ -1510,7 +1566,10 @@ static hipError_t launch_cfg(const GemmParams& p, int rows_max, int epi, bool bi
       if (p.bt)
         return big ? launch_tail_or_not<256, 256, 1, 2, 4, 64, 2, 1, EPI_STORE, true>(p, rows_max, s)
                    : launch_tail_or_not<128, 256, 1, 2, 2, 32, 3, 2, EPI_STORE, true>(p, rows_max, s);
-      return big ? launch_tail_or_not<256, 256, 1, 4, 2, 64, 2, 1, EPI_STORE>(p, rows_max, s)
+      if (big) return launch_tail_or_not<256, 256, 1, 4, 2, 64, 2, 1, EPI_STORE>(p, rows_max, s);
+      return streams
+                 ? launch_tail_or_not<128, 256, 1, 2, 2, 64, 3, 1, EPI_STORE, false, true>(p, rows_max,
+                                                                                         s)
                  : launch_tail_or_not<128, 256, 1, 2, 2, 64, 3, 1, EPI_STORE>(p, rows_max, s);
     case EPI_SWIGLU_BWD:
       return big ? launch_tail_or_not<256, 128, 2, 4, 2, 64, 2, 1, EPI_SWIGLU_BWD>(p, rows_max, s)
@@ -1581,7 +1640,8 @@ hipError_t launch_gemm_bf16(const GemmParams& p_in, int rows_max, int epi, hipSt
     // other products too few tiles, whose last round the K-split tiling balances.
     e = launch_bs(p, rows_max, epi, s);
   } else {
-    e = launch_cfg(p, rows_max, epi, big, s);
+    const int per_group = grouped ? rows_max / std::max(p.G, 1) : rows_max;
+    e = launch_cfg(p, rows_max, epi, big, !big && per_group < 128, s);
   }
   if (e != hipSuccess) return e;
   if (p.ksplit > 1) launch_splitk_finish(p, rows_max, epi, s);
