@@ -1548,13 +1548,19 @@ size_t gemm_bf16_partial_bytes(int rows_max, int G, bool grouped, int N, int K, 
 
 // The tile configuration of each epilogue: 256-row tiles (8 waves, one block per CU) or 128-row
 // tiles (4 waves, two blocks per CU).
-// `streams`: the short tiles read every weight panel once (fewer rows per group than a tile), so
-// the forward products load their weights with the non-temporal hint.
-static hipError_t launch_cfg(const GemmParams& p, int rows_max, int epi, bool big, bool streams,
+// `per_group`: rows per group on average.  With fewer rows than a short tile, the short tiles read
+// every weight panel once, so the forward products load their weights with the non-temporal hint;
+// with at most 64 rows they take 64-row tiles (8 waves in 2 x 4, a 4-stage ring: 96 KB of weights
+// in flight per CU instead of 64 KB, the decode-sized products being bound by the weight stream).
+static hipError_t launch_cfg(const GemmParams& p, int rows_max, int epi, bool big, int per_group,
                              hipStream_t s) {
+  const bool streams = !big && per_group < 128;
+  const bool thin = streams && per_group <= 64;
   switch (epi) {
     case EPI_SWIGLU:   // short tiles: 64-deep steps (128-byte runs per weight row), one block per CU
       if (big) return launch_tail_or_not<256, 128, 2, 4, 2, 64, 2, 1, EPI_SWIGLU>(p, rows_max, s);
+      if (thin)
+        return launch_tail_or_not<64, 128, 2, 2, 4, 64, 4, 1, EPI_SWIGLU, false, true>(p, rows_max, s);
       return streams
                  ? launch_tail_or_not<128, 128, 2, 2, 2, 64, 3, 1, EPI_SWIGLU, false, true>(p, rows_max,
                                                                                           s)
@@ -1567,6 +1573,8 @@ static hipError_t launch_cfg(const GemmParams& p, int rows_max, int epi, bool bi
         return big ? launch_tail_or_not<256, 256, 1, 2, 4, 64, 2, 1, EPI_STORE, true>(p, rows_max, s)
                    : launch_tail_or_not<128, 256, 1, 2, 2, 32, 3, 2, EPI_STORE, true>(p, rows_max, s);
       if (big) return launch_tail_or_not<256, 256, 1, 4, 2, 64, 2, 1, EPI_STORE>(p, rows_max, s);
+      if (thin)
+        return launch_tail_or_not<64, 256, 1, 2, 4, 64, 4, 1, EPI_STORE, false, true>(p, rows_max, s);
       return streams
                  ? launch_tail_or_not<128, 256, 1, 2, 2, 64, 3, 1, EPI_STORE, false, true>(p, rows_max,
                                                                                          s)
@@ -1640,8 +1648,7 @@ hipError_t launch_gemm_bf16(const GemmParams& p_in, int rows_max, int epi, hipSt
     // other products too few tiles, whose last round the K-split tiling balances.
     e = launch_bs(p, rows_max, epi, s);
   } else {
-    const int per_group = grouped ? rows_max / std::max(p.G, 1) : rows_max;
-    e = launch_cfg(p, rows_max, epi, big, !big && per_group < 128, s);
+    e = launch_cfg(p, rows_max, epi, big, grouped ? rows_max / std::max(p.G, 1) : rows_max, s);
   }
   if (e != hipSuccess) return e;
   if (p.ksplit > 1) launch_splitk_finish(p, rows_max, epi, s);
