@@ -376,10 +376,10 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, TileCoord tc, int
   // of this block's K range (a ragged K, or a step past the last one) are sent out of the buffer's
   // range: they read zeros and touch no memory.
   // Loads j in [J0, J1) (A blocks first, then B): an A block goes to a_off + its offset in a
-  // stage, a B block to b_off + its offset (b_off is the B stage's address minus B_OFF).
+  // stage, a B block to b_off + its offset (b_off is the B stage's address minus B_OFF).  With
+  // LSPLIT only the loading waves call it.
   auto issue_dma_range = [&](int a_off, int b_off, int k0, auto J0, auto J1) {
     const uint32_t koff = (uint32_t)k0 * 2u;
-    if (LSPLIT && wave >= NWL) return;
 #pragma unroll
     for (int j = decltype(J0)::value; j < decltype(J1)::value; ++j) {
       const bool is_a = j < DPWL_A;
@@ -530,6 +530,20 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, TileCoord tc, int
     constexpr int USED = P + (NRD - P * R > 0 ? 1 : 0);
     if constexpr (NMF > USED) __builtin_amdgcn_sched_group_barrier(0x008, NMF - USED, 0);
   };
+  // As interleave(), with NV direct loads placed too, one after each of the first NV matrix
+  // instructions, so that a wave's load issue never holds back a run of its matrix instructions.
+  auto interleave_v = [&](auto NVc) {
+    constexpr int NV = decltype(NVc)::value;
+    constexpr int R = (NRD + NMF - 1) / NMF;
+#pragma unroll
+    for (int q = 0; q < NMF; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+        if (q * R + r < NRD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      if (q < NV) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    }
+  };
   auto mfmas = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < TM; ++i)
@@ -552,16 +566,33 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, TileCoord tc, int
     // Split rings: A stage s at s * A_BYTES, B stage s at NST * A_BYTES + s * B_BYTES.  In step kt
     // the loads of A(kt + 1) go out before those of B(kt + 2), so waiting until only the latter
     // are in flight (vmcnt counts in issue order) leaves A(kt + 1) and B(kt + 1) landed.
-    auto run_split = [&](auto MATH) {
+    auto run_split = [&](auto MATH, auto LOADER) {
       constexpr bool math = decltype(MATH)::value;
+      constexpr bool loader = decltype(LOADER)::value;
       constexpr int DPW_B = DPWL - DPWL_A;
+      auto dma_range = [&](int a_off, int b_off, int k0, auto J0, auto J1) {
+        if constexpr (loader) issue_dma_range(a_off, b_off, k0, J0, J1);
+      };
       const std::integral_constant<int, 0> j0;
       const std::integral_constant<int, DPWL_A> ja;
       const std::integral_constant<int, DPWL> j1;
       auto b_at = [&](int sb) { return NST * A_BYTES + sb * B_BYTES - B_OFF; };
-      issue_dma_range(0, 0, kbeg, j0, ja);
-      issue_dma_range(0, b_at(0), kbeg, ja, j1);
-      issue_dma_range(0, b_at(1), kbeg + BK, ja, j1);
+      // Part Q (of the KS - 1 slices before the barrier) of step kt's loads, in issue order: the
+      // A(kt + 1) blocks, then the B(kt + 2) blocks, cut into equal runs.
+      auto dma_part = [&](auto Q, int kt, int na, int fb) {
+        constexpr int q = decltype(Q)::value;
+        constexpr int lo = DPWL * q / (KS - 1), hi = DPWL * (q + 1) / (KS - 1);
+        constexpr int alo = lo < DPWL_A ? lo : DPWL_A, ahi = hi < DPWL_A ? hi : DPWL_A;
+        constexpr int blo = lo > DPWL_A ? lo : DPWL_A, bhi = hi > DPWL_A ? hi : DPWL_A;
+        dma_range(na * A_BYTES, 0, kbeg + (kt + 1) * BK, std::integral_constant<int, alo>(),
+                  std::integral_constant<int, ahi>());
+        dma_range(0, b_at(fb), kbeg + (kt + 2) * BK, std::integral_constant<int, blo>(),
+                  std::integral_constant<int, bhi>());
+        return std::integral_constant<int, loader ? hi - lo : 0>();
+      };
+      dma_range(0, 0, kbeg, j0, ja);
+      dma_range(0, b_at(0), kbeg, ja, j1);
+      dma_range(0, b_at(1), kbeg + BK, ja, j1);
       __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0<DPW_B>());
       barrier_no_fence();
       if constexpr (math) read_frags2(0, b_at(0), 0, 0);
@@ -570,16 +601,38 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, TileCoord tc, int
         const int na = sa ^ 1;
         const int nb = sb + 1 == NSB ? 0 : sb + 1;
         const int fb = sb == 0 ? NSB - 1 : sb - 1;  // stage of step kt + 2
-        issue_dma_range(na * A_BYTES, 0, kbeg + (kt + 1) * BK, j0, ja);
-        issue_dma_range(0, b_at(fb), kbeg + (kt + 2) * BK, ja, j1);
+        // K-contiguous operands: the step's loads spread over the slices (the transposing tiles of
+        // the backward products, whose loads are inline assembly, issue them all first: measured
+        // faster there).
+        constexpr bool spread = !BT && !AT;
         if constexpr (math) {
-#pragma unroll
-          for (int ks = 0; ks < KS - 1; ++ks) {
-            read_frags2(sa * A_BYTES, b_at(sb), ks + 1, (ks + 1) & 1);
-            mfmas(ks & 1);
-            interleave();
-            __builtin_amdgcn_sched_barrier(0);
+          if constexpr (!spread) {
+            dma_range(na * A_BYTES, 0, kbeg + (kt + 1) * BK, j0, ja);
+            dma_range(0, b_at(fb), kbeg + (kt + 2) * BK, ja, j1);
           }
+          // Slice ks: a part of the step's loads, the reads of slice ks + 1 and the matrix
+          // instructions of slice ks, interleaved.
+          auto slice = [&](auto KSc) {
+            constexpr int ks = decltype(KSc)::value;
+            if constexpr (spread) {
+              const auto nv = dma_part(KSc, kt, na, fb);
+              read_frags2(sa * A_BYTES, b_at(sb), ks + 1, (ks + 1) & 1);
+              mfmas(ks & 1);
+              interleave_v(nv);
+            } else {
+              read_frags2(sa * A_BYTES, b_at(sb), ks + 1, (ks + 1) & 1);
+              mfmas(ks & 1);
+              interleave();
+            }
+            __builtin_amdgcn_sched_barrier(0);
+          };
+          static_assert(KS == 4, "64-deep steps: three slices before the barrier");
+          slice(std::integral_constant<int, 0>());
+          slice(std::integral_constant<int, 1>());
+          slice(std::integral_constant<int, 2>());
+        } else {
+          dma_range(na * A_BYTES, 0, kbeg + (kt + 1) * BK, j0, ja);
+          dma_range(0, b_at(fb), kbeg + (kt + 2) * BK, ja, j1);
         }
         __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0<DPW_B>());
         barrier_no_fence();
@@ -629,10 +682,19 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, TileCoord tc, int
     };
     if constexpr (NSB > NST) {
       static_assert(NST == 2, "split rings take a 2-stage A ring");
-      if (active)
-        run_split(std::true_type());
-      else
-        run_split(std::false_type());
+      // (LSPLIT: the other waves issue no loads; each kind runs its own copy of the loop.)
+      const bool loader = !LSPLIT || wave < NWL;
+      if (active) {
+        if (loader)
+          run_split(std::true_type(), std::true_type());
+        else
+          run_split(std::true_type(), std::false_type());
+      } else {
+        if (loader)
+          run_split(std::false_type(), std::true_type());
+        else
+          run_split(std::false_type(), std::false_type());
+      }
     } else {
       if (active)
         run(std::true_type());
