@@ -6,6 +6,8 @@
 #include "common.h"
 #include "kernels.h"
 
+#include <type_traits>
+
 namespace moe {
 
 // One block per token row; each thread owns 16-byte column chunks.  k is at most kCombineMaxK (the
@@ -27,23 +29,36 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ e
   __syncthreads();
   constexpr int VEC = BF16 ? 8 : 4;  // elements per 16-byte chunk
   const int nchunk = d / VEC;
+  // Slots in groups of eight: a group's row loads are all issued before any of them is added,
+  // and the sums keep slot order.
+  constexpr int KG = 8;
+  typedef typename std::conditional<BF16, u32x4, f32x4>::type chunk_t;
   for (int c = threadIdx.x; c < nchunk; c += blockDim.x) {
     float acc[VEC];
 #pragma unroll
     for (int i = 0; i < VEC; ++i) acc[i] = 0.f;
-    for (int s = 0; s < k; ++s) {
-      const int pos = s_pos[s];
-      if (pos < 0) continue;
-      const float g = s_g[s];
-      float v[VEC];
-      if constexpr (BF16) {
-        unpack8(*reinterpret_cast<const u32x4*>((const uint16_t*)expert_out + (size_t)pos * d + c * 8), v);
-      } else {
-        const f32x4 q = *reinterpret_cast<const f32x4*>((const float*)expert_out + (size_t)pos * d + c * 4);
-        v[0] = q[0]; v[1] = q[1]; v[2] = q[2]; v[3] = q[3];
+    for (int s0 = 0; s0 < k; s0 += KG) {
+      chunk_t raw[KG];
+#pragma unroll
+      for (int j = 0; j < KG; ++j) {
+        const int pos = s0 + j < k ? s_pos[s0 + j] : -1;
+        if (pos >= 0)   // every expert row is read once: non-temporal loads
+          raw[j] = __builtin_nontemporal_load(reinterpret_cast<const chunk_t*>(
+              (const char*)expert_out + ((size_t)pos * d + (size_t)c * VEC) * (BF16 ? 2 : 4)));
       }
 #pragma unroll
-      for (int i = 0; i < VEC; ++i) acc[i] = fmaf(g, v[i], acc[i]);
+      for (int j = 0; j < KG; ++j) {
+        if (s0 + j >= k || s_pos[s0 + j] < 0) continue;
+        const float g = s_g[s0 + j];
+        float v[VEC];
+        if constexpr (BF16) {
+          unpack8(raw[j], v);
+        } else {
+          v[0] = raw[j][0]; v[1] = raw[j][1]; v[2] = raw[j][2]; v[3] = raw[j][3];
+        }
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) acc[i] = fmaf(g, v[i], acc[i]);
+      }
     }
     if (shared_out) {
       float v[VEC];

@@ -48,10 +48,17 @@ __global__ __launch_bounds__(1024) void dispatch_scan_kernel(int32_t* __restrict
   if (e < E) {
     int32_t* h = hist + (size_t)e * nchunk;
     int run = 0;
-    for (int c = 0; c < nchunk; ++c) {
-      const int v = h[c];
-      h[c] = run;  // position of chunk c's first assignment to e in e's stream
-      run += v;
+    // Chunks in groups of eight: the group's counts are loaded before any is replaced.
+    constexpr int G8 = 8;
+    for (int c0 = 0; c0 < nchunk; c0 += G8) {
+      int v[G8];
+#pragma unroll
+      for (int j = 0; j < G8; ++j) v[j] = c0 + j < nchunk ? h[c0 + j] : 0;
+#pragma unroll
+      for (int j = 0; j < G8; ++j) {
+        if (c0 + j < nchunk) h[c0 + j] = run;  // position of the chunk's first assignment to e
+        run += v[j];
+      }
     }
     counts[e] = run;
     kept = (capacity > 0 && run > capacity) ? capacity : run;
