@@ -468,7 +468,10 @@ moe_status moe_expert_backward_saved(const void* saved, const void* x, const int
  * renormalised over the selected).  logits [T,E] fp32, topk_idx, topk_gate from moe_route; d_gate
  * from moe_combine_backward; counts from moe_dispatch (may be NULL when alpha == 0); dx_add [T][d]
  * or NULL.  d_logits [T,E] fp32 is an output.  fp32 sums throughout; dw_r is added over token
- * chunks in a fixed order.
+ * chunks in a fixed order.  For bf16 with E a multiple of 64 the two products run on the matrix
+ * cores: d_logits enters as three bf16 terms (hi, mid, lo: their sum is d_logits to within
+ * 2^-24 relative), dw_r takes all three and dx the first two (2^-16 relative, below the bf16
+ * rounding of dx); dx_add is added before dx is rounded.  Workspace: moe_backward_workspace_bytes.
  */
 moe_status moe_route_backward(const void* x, const void* w_r, const float* logits,
                               const int32_t* topk_idx, const float* topk_gate,

@@ -275,6 +275,62 @@ void launch_router_xgrad(const float* dL, const void* w_r, bool bf16, int T, int
                        dx);
 }
 
+// Matrix-core form of the two router products (bf16 activations and weights, E a multiple of 64).
+// d_logits (fp32) enters as three bf16 terms, hi = bf16(v), mid = bf16(v - hi),
+// lo = bf16(v - hi - mid) (round to nearest even; each difference is exact in fp32), whose sum
+// is v to within 2^-24 |v|; the products of bf16 terms with bf16 x or w_r are exact in the fp32
+// accumulators.  Row t of `terms` holds [hi | mid | lo], 3E values.  Block 0 also writes the
+// token-chunk boundaries of the weight-gradient product: offs[g] = min(g * chunk, T), g <= G.
+__global__ __launch_bounds__(256) void split_terms_kernel(const float* __restrict__ dL, int T,
+                                                          int E, uint16_t* __restrict__ terms,
+                                                          int32_t* __restrict__ offs, int G,
+                                                          int chunk) {
+  if (blockIdx.x == 0)
+    for (int g = threadIdx.x; g <= G; g += 256) offs[g] = (int)min((long long)g * chunk, (long long)T);
+  const size_t n = (size_t)T * E;
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) {
+    const size_t t = i / E, e = i % E;
+    const float v = dL[i];
+    const uint16_t hi = f32_to_bf16(v);
+    const float r1 = v - bf16_to_f32(hi);
+    const uint16_t mid = f32_to_bf16(r1);
+    const uint16_t lo = f32_to_bf16(r1 - bf16_to_f32(mid));
+    uint16_t* row = terms + t * 3 * E;
+    row[e] = hi;
+    row[E + e] = mid;
+    row[2 * E + e] = lo;
+  }
+}
+
+// dW[e][j] = sum over chunks g in order of (part[g][e][j] + part[g][E + e][j]) + part[g][2E + e][j]
+// (the hi, mid and lo terms' products of chunk g).
+__global__ __launch_bounds__(256) void sum_terms_kernel(const float* __restrict__ part, int G,
+                                                        int E, int d, float* __restrict__ dw) {
+  const size_t n = (size_t)E * d, per = 3 * n;
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) {
+    float v = 0.f;
+    for (int g = 0; g < G; ++g) {
+      const float* q = part + (size_t)g * per + i;
+      v += (q[0] + q[n]) + q[2 * n];
+    }
+    dw[i] = v;
+  }
+}
+
+void launch_split_terms(const float* dL, int T, int E, void* terms, int32_t* offs, int G,
+                        int chunk, hipStream_t s) {
+  const size_t n = (size_t)T * E;
+  const int grid = (int)std::min<size_t>((n + 255) / 256, 4096);
+  hipLaunchKernelGGL(split_terms_kernel, dim3(grid), dim3(256), 0, s, dL, T, E, (uint16_t*)terms,
+                     offs, G, chunk);
+}
+
+void launch_sum_terms(const float* part, int G, int E, int d, float* dw, hipStream_t s) {
+  const size_t n = (size_t)E * d;
+  const int grid = (int)std::min<size_t>((n + 255) / 256, 4096);
+  hipLaunchKernelGGL(sum_terms_kernel, dim3(grid), dim3(256), 0, s, part, G, E, d, dw);
+}
+
 __global__ void dense_offsets_kernel(int32_t* o, int T) {
   if (threadIdx.x == 0) {
     o[0] = 0;

@@ -1001,8 +1001,14 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, TileCoord tc, int
             }
           }
           if (row < tc.row_end && col0 < N) {
-            const uint32_t packed = odd ? pack_bf16x2(got, v[r + 1]) : pack_bf16x2(v[r], got);
-            *(uint32_t*)((uint16_t*)Cg + (size_t)row * p.ldc + col0) = packed;
+            float lo = odd ? got : v[r], hi = odd ? v[r + 1] : got;
+            if (EPI == EPI_STORE && p.D) {   // the addend, rounded with the sum
+              const uint32_t add =
+                  *(const uint32_t*)((const uint16_t*)p.D + (size_t)row * p.ldd + col0);
+              lo += __builtin_bit_cast(float, add << 16);
+              hi += __builtin_bit_cast(float, add & 0xffff0000u);
+            }
+            *(uint32_t*)((uint16_t*)Cg + (size_t)row * p.ldc + col0) = pack_bf16x2(lo, hi);
           }
         }
       }
@@ -1038,7 +1044,9 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, TileCoord tc, int
             dst[2 * N] = f32_to_bf16(v);
           }
         } else if constexpr (EPI == EPI_STORE) {
-          ((uint16_t*)Cg)[(size_t)row * p.ldc + col] = f32_to_bf16(acc[0][i][j][r]);
+          const float add =
+              p.D ? bf16_to_f32(((const uint16_t*)p.D)[(size_t)row * p.ldd + col]) : 0.f;
+          ((uint16_t*)Cg)[(size_t)row * p.ldc + col] = f32_to_bf16(acc[0][i][j][r] + add);
         } else {
           ((float*)Cg)[(size_t)row * p.ldc + col] =
               acc[0][i][j][r] + (p.bias ? p.bias[col] : 0.f);
@@ -1693,6 +1701,10 @@ hipError_t launch_gemm_bf16(const GemmParams& p_in, int rows_max, int epi, hipSt
   }
   // These epilogues run on whole sums only.
   if (epi == EPI_SWIGLU_BWD || epi == EPI_SWIGLU_BWD_SAVED) p.part = nullptr;
+  if (epi == EPI_STORE && p.D) {   // the addend: one group, no split
+    if (grouped) return hipErrorNotSupported;
+    p.part = nullptr;
+  }
   if (epi == EPI_SWIGLU_BWD_SAVED && (!p.D || p.ldd < 2 * p.N)) return hipErrorInvalidValue;
   if (epi == EPI_SWIGLU_SAVE && p.ldc < 3 * p.N) return hipErrorInvalidValue;
   p.ksplit = splitk_factor(rows_max, p.G, grouped, p.N, p.K, epi);

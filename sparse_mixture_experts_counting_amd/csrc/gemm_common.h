@@ -45,6 +45,8 @@ struct GemmParams {
   // [0, N) and db in [N, 2N): da = dh * b * silu'(a), db = dh * silu(a).  All bf16.
   const void* D;
   void* H;
+  // EPI_STORE with D set (one group, no split): C = A B^T + D, D a bf16 [rows][ldd] addend, the
+  // sum rounded to bf16 once.
   // Saved-activation epilogues.  EPI_SWIGLU_SAVE: as EPI_SWIGLU, and also stores the bf16 a and b
   // beside h in the same row of C (ldc >= 3N): h in columns [0, N), a in [N, 2N), b in [2N, 3N).
   // EPI_SWIGLU_BWD_SAVED (one matrix, the GEMM gives dh): reads a = D[row * ldd + col] and

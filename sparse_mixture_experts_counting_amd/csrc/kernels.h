@@ -73,6 +73,12 @@ void launch_router_wgrad(const void* x, bool bf16, const float* dL, int T, int d
 void launch_router_xgrad(const float* dL, const void* w_r, bool bf16, int T, int d, int E,
                          const void* add, void* dx, hipStream_t s);
 void launch_dense_offsets(int32_t* o, int T, hipStream_t s);
+// Matrix-core router backward: d_logits as three bf16 terms [T][3E] (and the token-chunk offsets
+// [G+1] of the weight-gradient product), and the fixed-order sum of its per-chunk, per-term
+// partials [G][3E][d] into dW [E][d].
+void launch_split_terms(const float* dL, int T, int E, void* terms, int32_t* offs, int G,
+                        int chunk, hipStream_t s);
+void launch_sum_terms(const float* part, int G, int E, int d, float* dw, hipStream_t s);
 
 // reroute.hip
 size_t reroute_workspace_bytes(int A, int E);

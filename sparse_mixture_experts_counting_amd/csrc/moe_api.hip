@@ -83,8 +83,36 @@ BwdLayout bwd_layout(int rows, bool grouped, int G, int d, int d_ff) {
   return L;
 }
 
+// The router products run on the matrix cores for bf16 operands with E a multiple of 64 (the
+// stacked-K weight reads split on a 64-deep step); otherwise on the vector units.
+bool route_bwd_mfma(int E, moe_dtype dt) { return dt == MOE_BF16 && E % 64 == 0; }
+
+// Token chunks of the matrix-core weight-gradient product: enough 256 x 256 tiles for a round of
+// the CUs (3E x d outputs per chunk), at most 16.
+int route_bwd_chunks(int T, int d, int E) {
+  const long long tiles = (long long)((3 * E + 255) / 256) * ((d + 255) / 256);
+  int G = (int)std::min<long long>(16, std::max<long long>(1, (256 + tiles - 1) / tiles));
+  return std::max(1, std::min(G, T));
+}
+
+struct RouteBwdLayout {
+  size_t terms, offs, part, total;
+};
+
+RouteBwdLayout route_bwd_layout(int T, int d, int E) {
+  RouteBwdLayout L{};
+  const int G = route_bwd_chunks(T, d, E);
+  L.terms = 0;
+  L.offs = align_up((size_t)T * 3 * E * sizeof(uint16_t));
+  L.part = L.offs + align_up((size_t)(G + 1) * sizeof(int32_t));
+  L.total = L.part + align_up((size_t)G * 3 * E * d * sizeof(float));
+  return L;
+}
+
 size_t route_bwd_bytes(int T, int d, int E) {
-  return align_up((size_t)moe::router_wgrad_chunks(T) * E * d * sizeof(float));
+  const size_t valu = align_up((size_t)moe::router_wgrad_chunks(T) * E * d * sizeof(float));
+  const size_t mfma = route_bwd_layout(T, d, E).total;
+  return valu > mfma ? valu : mfma;
 }
 
 }  // namespace
@@ -735,8 +763,41 @@ moe_status moe_route_backward(const void* x, const void* w_r, const float* logit
   const bool bf16 = dt == MOE_BF16;
   moe::launch_gate_backward(logits, topk_idx, topk_gate, d_gate, alpha != 0.0f ? counts : nullptr,
                             T, E, k, (int)gating, alpha, beta, d_logits, s);
-  moe::launch_router_wgrad(x, bf16, d_logits, T, d, E, (float*)workspace, dw_r, s);
-  moe::launch_router_xgrad(d_logits, w_r, bf16, T, d, E, dx_add, dx, s);
+  if (!route_bwd_mfma(E, dt)) {
+    moe::launch_router_wgrad(x, bf16, d_logits, T, d, E, (float*)workspace, dw_r, s);
+    moe::launch_router_xgrad(d_logits, w_r, bf16, T, d, E, dx_add, dx, s);
+    return launched();
+  }
+  // Matrix cores: d_logits as three bf16 terms (hi, mid, lo) of fp32 accuracy.
+  const RouteBwdLayout L = route_bwd_layout(T, d, E);
+  const int G = route_bwd_chunks(T, d, E);
+  const int chunk = (T + G - 1) / G;
+  char* ws = (char*)workspace;
+  void* terms = ws + L.terms;
+  int32_t* offs = (int32_t*)(ws + L.offs);
+  float* part = (float*)(ws + L.part);
+  moe::launch_split_terms(d_logits, T, E, terms, offs, G, chunk, s);
+  hipError_t e;
+  {   // dW_r partials: chunk g, term q -> rows q E .. q E + E - 1 of part[g] = terms^T x over the
+      // chunk's tokens (both operands row-major, read transposed)
+    moe::GemmParams q{};
+    q.A = terms; q.a_rows = T; q.lda = 3 * E; q.gather_div = 1;
+    q.offsets = offs; q.G = G; q.M = 3 * E; q.N = d; q.K = T;
+    q.B0 = x; q.ldb = d; q.C = part; q.ldc = d;
+    q.kgrouped = 1; q.at = 1; q.bt = 1; q.c_gstride = (long long)3 * E * d;
+    if ((e = moe::launch_gemm_bf16(q, T, moe::EPI_STORE_F32_BIAS, s)) != hipSuccess)
+      return MOE_ERR_DEVICE;
+  }
+  moe::launch_sum_terms(part, G, E, d, dw_r, s);
+  {   // dx = [hi | mid] [w_r; w_r] (+ dx_add): K = 2E, w_r read as stored ([E][d], [K][N])
+    moe::GemmParams q{};
+    q.A = terms; q.a_rows = T; q.lda = 3 * E; q.gather_div = 1;
+    q.M = T; q.N = d; q.K = 2 * E;
+    q.B0 = w_r; q.B1 = w_r; q.bt = 1; q.bt_k1 = E; q.ldb = d;
+    q.C = dx; q.ldc = d;
+    q.D = dx_add; q.ldd = d;
+    if ((e = moe::launch_gemm_bf16(q, T, moe::EPI_STORE, s)) != hipSuccess) return MOE_ERR_DEVICE;
+  }
   return launched();
 }
 
