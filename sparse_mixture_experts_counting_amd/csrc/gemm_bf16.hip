@@ -405,8 +405,11 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, TileCoord tc, int
       } else {
         lds_void_t* const lds_at =
             (lds_void_t*)(smem + (is_a ? a_off : b_off) + (wave + NWL * j) * 1024);
+        // (The router product streams its activations: with at most 256 experts, one column
+        // tile, every x element is read once; non-temporal.)
         if (is_a)
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, lds_at, 16, (int)voff, 0, 0, 0);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, lds_at, 16, (int)voff, 0, 0,
+                                                   (EPI == EPI_STORE_F32_BIAS && !AT) ? 2 : 0);
         else
           __builtin_amdgcn_raw_ptr_buffer_load_lds(second ? rB1 : rB0, lds_at, 16, (int)voff, 0, 0,
                                                    NTB ? 2 : 0);
