@@ -21,12 +21,36 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ e
                                                       void* __restrict__ y) {
   __shared__ int32_t s_pos[kCombineMaxK];
   __shared__ float s_g[kCombineMaxK];
+  __shared__ int s_n;
   const int t = blockIdx.x;
   for (int i = threadIdx.x; i < k; i += blockDim.x) {
     s_pos[i] = inv[(size_t)t * k + i];
     s_g[i] = gate ? gate[(size_t)t * k + i] : 1.0f;
   }
   __syncthreads();
+  // The first wave packs the kept slots to the front, in slot order (a dropped or empty slot
+  // adds nothing; the Expert Choice layout has one slot per expert, most of them empty).  Each
+  // 64-slot window is read by all lanes before any lane writes, and no write lands past its slot.
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    int base = 0;
+    for (int s0 = 0; s0 < k; s0 += 64) {
+      const int sl = s0 + lane;
+      const int pos = sl < k ? s_pos[sl] : -1;
+      const float g = sl < k ? s_g[sl] : 0.f;
+      const bool ok = pos >= 0;
+      const uint64_t m = __ballot(ok);
+      if (ok) {
+        const int at = base + __popcll(m & lanemask_lt());
+        s_pos[at] = pos;
+        s_g[at] = g;
+      }
+      base += __popcll(m);
+    }
+    if (lane == 0) s_n = base;
+  }
+  __syncthreads();
+  const int nk = s_n;                 // kept slots, packed
   constexpr int VEC = BF16 ? 8 : 4;  // elements per 16-byte chunk
   const int nchunk = d / VEC;
   // Slots in groups of eight: a group's row loads are all issued before any of them is added,
@@ -37,18 +61,18 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ e
     float acc[VEC];
 #pragma unroll
     for (int i = 0; i < VEC; ++i) acc[i] = 0.f;
-    for (int s0 = 0; s0 < k; s0 += KG) {
+    for (int s0 = 0; s0 < nk; s0 += KG) {
       chunk_t raw[KG];
 #pragma unroll
       for (int j = 0; j < KG; ++j) {
-        const int pos = s0 + j < k ? s_pos[s0 + j] : -1;
+        const int pos = s0 + j < nk ? s_pos[s0 + j] : -1;
         if (pos >= 0)   // every expert row is read once: non-temporal loads
           raw[j] = __builtin_nontemporal_load(reinterpret_cast<const chunk_t*>(
               (const char*)expert_out + ((size_t)pos * d + (size_t)c * VEC) * (BF16 ? 2 : 4)));
       }
 #pragma unroll
       for (int j = 0; j < KG; ++j) {
-        if (s0 + j >= k || s_pos[s0 + j] < 0) continue;
+        if (s0 + j >= nk) continue;
         const float g = s_g[s0 + j];
         float v[VEC];
         if constexpr (BF16) {

@@ -5,9 +5,10 @@
         `rocprofv3 --kernel-trace --stats` run.
 
     python -m sparse_mixture_experts_counting_amd.profsum kernels FETCH_CSV WRITE_CSV STATS_CSV TITLE \
-            COMMAND
+            PMC_COMMAND ;; STATS_COMMAND
         Markdown table of every library kernel's HBM bytes read and written per dispatch and the
-        rate over its average duration.
+        rate over its average duration (PMC_COMMAND names the counter COUNTER; STATS_COMMAND is
+        the kernel-trace run the durations come from).
 
     python -m sparse_mixture_experts_counting_amd.profsum mfma PMC_CSV[,PMC_CSV] STATS_CSV KERNEL \
             TITLE COMMANDS
@@ -127,7 +128,10 @@ def _stats_us(stats_csv):
 
 def kernels(fetch_csv, write_csv, stats_csv, title, command):
     """Per-kernel HBM bytes (FETCH_SIZE and WRITE_SIZE per dispatch, scaled by the calibration
-    copy) and the rate they imply over each kernel's average duration, for the library's kernels."""
+    copy) and the rate they imply over each kernel's average duration, for the library's kernels.
+    `command` is the counter runs' command (COUNTER for the counter name), then " ;; " and the
+    kernel-trace run's command."""
+    pmc_cmd, _, stats_cmd = command.partition(" ;; ")
     fetch, write = _per_kernel(fetch_csv), _per_kernel(write_csv)
     f_cal = max((max(v) for k, v in fetch.items() if "copyBuffer" in k or "copy_kernel" in k))
     w_cal = max((max(v) for k, v in write.items() if "copyBuffer" in k or "copy_kernel" in k))
@@ -135,12 +139,12 @@ def kernels(fetch_csv, write_csv, stats_csv, title, command):
     st = _stats_us(stats_csv)
     out = ["# HBM traffic per kernel: %s" % title, "",
            "Commands (run from /tmp with TMPDIR=/tmp on one MI355X; repository at $R):", "",
-           "    " + command.replace("COUNTER", "FETCH_SIZE"),
-           "    " + command.replace("COUNTER", "WRITE_SIZE"),
-           "    " + command.replace("--pmc COUNTER", "--kernel-trace --stats"), "",
+           "    " + pmc_cmd.replace("COUNTER", "FETCH_SIZE"),
+           "    " + pmc_cmd.replace("COUNTER", "WRITE_SIZE"),
+           "    " + (stats_cmd or pmc_cmd.replace("--pmc COUNTER", "--kernel-trace --stats")), "",
            "FETCH_SIZE and WRITE_SIZE are KiB per dispatch between L2 and the memory fabric; each is "
            "scaled by what it reads for the benchmark's untimed 256 MiB device copy (fetch x%.3f, "
-           "write x%.3f). Durations are the kernel-trace averages of the same command." %
+           "write x%.3f). Durations are the kernel-trace averages of the last command." %
            (f_scale, w_scale), "",
            "| kernel | dispatches | avg us | read MB | written MB | GB/s |", "|---|---|---|---|---|---|"]
     rows = []
