@@ -141,6 +141,12 @@ CASES = [
     # 256 to 512 rows per expert: 256-row tiles for whole blocks, 128-row tiles for the rest
     (700, 256, 4, 2, 512, "softmax_topk", 0, 0, 1.1),
     (1500, 128, 8, 2, 320, "sigmoid_topk", 0, 1, 1.3),
+    # E a multiple of 64: the router products on the matrix cores (three-term split of d_logits;
+    # token chunks not dividing T; dx with and without the shared expert's addend)
+    (300, 128, 64, 4, 192, "sigmoid_topk", 0, 1, 1.1),
+    (1030, 256, 128, 2, 256, "softmax_topk", 0, 0, 0.0),
+    (96, 64, 256, 8, 64, "sigmoid_topk", 0, 1, 1.1),
+    (5, 512, 64, 2, 128, "softmax_all", 0, 0, 0.0),
 ]
 
 
