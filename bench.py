@@ -13,6 +13,11 @@ grouped GEMM) against the bf16 matrix-core peak, and the CPU oracle timed on a b
 
     python bench.py [--steps K] [--warmup W] [--workload mixtral_prefill]
 
+The timed steps replay the forward step captured once into a HIP graph (the serving form of a
+fixed-shape layer: the same kernels, without the per-kernel launch gaps); --eager times them as
+launched one by one.  The per-stage breakdown always comes from eager steps with events between
+the stages, and the line also carries the eager step time.
+
 With --pass train a step is the forward followed by the backward pass of the layer (gradients of
 <dy, y> + aux + z for x, the router and every expert weight: moe_combine_backward,
 moe_expert_backward for the routed and shared experts, moe_route_backward, and moe_combine adding
@@ -194,6 +199,9 @@ def main():
                     help="overwrite a 1 GiB buffer before every timed step (outside the step's "
                          "events), so the step starts with caches holding none of its data; "
                          "ms_per_step is then the mean of the steps' event times")
+    ap.add_argument("--eager", action="store_true",
+                    help="time the forward steps as launched one by one instead of replaying the "
+                         "step captured in a HIP graph (the stage breakdown is eager either way)")
     ap.add_argument("--pass", dest="mode", choices=("forward", "train"), default="forward")
     ap.add_argument("--recompute", action="store_true",
                     help="--pass train: recompute the experts' up projection in the backward "
@@ -299,6 +307,43 @@ def main():
                              for s in range(args.steps)) / args.steps
     gpu_ms = sum(events[s][0].elapsed_time(events[s][-1]) for s in range(args.steps)) / args.steps
     ms_per_step = gpu_ms if args.cold else wall * 1e3 / args.steps
+    eager = {"ms_per_step": ms_per_step, "gpu_event_ms": gpu_ms}
+    launch = "eager: every kernel launched per step"
+    if not args.eager:
+        # The step captured once into a HIP graph (warm-up on the capture stream itself) and
+        # replayed: the serving form of a fixed-shape layer.  The same kernels run; only the
+        # per-kernel launch gaps go.  The stage breakdown above stays the eager one.
+        cap = torch.cuda.Stream(dev)
+        cap.wait_stream(stream)
+        with torch.cuda.stream(cap):
+            step()
+        torch.cuda.synchronize(dev)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=cap):
+            step()
+        torch.cuda.synchronize(dev)
+        scrub = torch.empty(1 << 30, dtype=torch.uint8, device=dev) if args.cold else None
+        for w in range(args.warmup):
+            if scrub is not None:
+                scrub.fill_(w & 0xff)
+            graph.replay()
+        torch.cuda.synchronize(dev)
+        gev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+        torch.cuda.synchronize(dev)
+        t0 = time.perf_counter()
+        for s in range(args.steps):
+            if scrub is not None:
+                scrub.fill_((s + 7) & 0xff)
+            gev[s][0].record(stream)
+            graph.replay()
+            gev[s][1].record(stream)
+        torch.cuda.synchronize(dev)
+        wall = time.perf_counter() - t0
+        del scrub, graph
+        gpu_ms = sum(a.elapsed_time(b) for a, b in gev) / args.steps
+        ms_per_step = gpu_ms if args.cold else wall * 1e3 / args.steps
+        launch = "hip graph: the step captured once and replayed"
 
     counts = buf.counts.cpu().tolist()
     n_kept = int(buf.offsets[-1].item())
@@ -352,11 +397,13 @@ def main():
                    "gating": cfg.gating, "capacity": cfg.capacity or None,
                    "shared_experts": cfg.n_shared, "parallelism": "none (1 GPU)",
                    "cache": ("cold: a 1 GiB buffer overwritten before every step, outside its "
-                             "events" if args.cold else "warm: steps back to back")},
+                             "events" if args.cold else "warm: steps back to back"),
+                   "launch": launch},
         "roofline": dict(roof, kernel=up_kernel, traffic=traffic),
         "grouped_gemm": {"ms": gg_ms, "tflops": (up_flops + down_flops) / (gg_ms * 1e-3) / 1e12,
                          "frac_bf16_peak": (up_flops + down_flops) / (gg_ms * 1e-3) / 1e12
                          / PEAK_BF16_TFLOPS},
+        "eager": eager,
         "layer": {"gpu_event_ms": gpu_ms, "tflops": layer_flops / (ms_per_step * 1e-3) / 1e12,
                   "hbm_gbs_algorithmic": layer_bytes / (ms_per_step * 1e-3) / 1e9,
                   "algorithmic_flops": layer_flops, "algorithmic_bytes": layer_bytes,
