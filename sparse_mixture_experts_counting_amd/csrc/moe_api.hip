@@ -84,8 +84,14 @@ BwdLayout bwd_layout(int rows, bool grouped, int G, int d, int d_ff) {
 }
 
 // The router products run on the matrix cores for bf16 operands with E a multiple of 64 (the
-// stacked-K weight reads split on a 64-deep step); otherwise on the vector units.
-bool route_bwd_mfma(int E, moe_dtype dt) { return dt == MOE_BF16 && E % 64 == 0; }
+// stacked-K weight reads split on a 64-deep step) while every operand stays under 2 GiB (32-bit
+// buffer offsets); otherwise on the vector units.
+bool route_bwd_mfma(int T, int d, int E, moe_dtype dt) {
+  const long long two_gib = 1ll << 31;
+  return dt == MOE_BF16 && E % 64 == 0 && (long long)T * 3 * E * 2 < two_gib &&
+         (long long)T * d * 2 < two_gib &&
+         (long long)E * d * 2 < two_gib;
+}
 
 // Token chunks of the matrix-core weight-gradient product: enough 256 x 256 tiles for a round of
 // the CUs (3E x d outputs per chunk), at most 16.
@@ -763,7 +769,7 @@ moe_status moe_route_backward(const void* x, const void* w_r, const float* logit
   const bool bf16 = dt == MOE_BF16;
   moe::launch_gate_backward(logits, topk_idx, topk_gate, d_gate, alpha != 0.0f ? counts : nullptr,
                             T, E, k, (int)gating, alpha, beta, d_logits, s);
-  if (!route_bwd_mfma(E, dt)) {
+  if (!route_bwd_mfma(T, d, E, dt)) {
     moe::launch_router_wgrad(x, bf16, d_logits, T, d, E, (float*)workspace, dw_r, s);
     moe::launch_router_xgrad(d_logits, w_r, bf16, T, d, E, dx_add, dx, s);
     return launched();
