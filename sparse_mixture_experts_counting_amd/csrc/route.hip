@@ -121,8 +121,87 @@ static void launch_router_small_e_d(const void* x, const void* w_r, const float*
   }
 }
 
+// The same product on the matrix cores for batches of at least 1024 bf16 tokens with d a multiple of
+// 2048: a block of 16 waves takes 16 tokens; wave w reduces over its sixteenth of d with
+// v_mfma_f32_32x32x16_bf16 (A: the 16 token rows, padded to 32; B: the E expert rows of W_r,
+// padded to 32), every lane loading 16-byte pieces that cover 256 contiguous bytes of a row per
+// batch of eight instructions; the waves' fp32 partial sums are added in wave order through
+// LDS.  The products of bf16 values are exact in the fp32 accumulators, so the logits lie within
+// the same rounding bound as the vector form's.  Memory bound on x, which every lane streams
+// with the non-temporal hint (read once).
+constexpr int kRouterMfmaTok = 16, kRouterMfmaWaves = 16, kRouterMfmaU = 8;
+
+template <int E>
+__global__ __launch_bounds__(1024) void router_mfma_kernel(const uint16_t* __restrict__ x,
+                                                          const uint16_t* __restrict__ w_r,
+                                                          const float* __restrict__ bias, int T,
+                                                          int d, float* __restrict__ logits) {
+  __shared__ float part[kRouterMfmaWaves][kRouterMfmaTok][E];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int l32 = lane & 31, h = lane >> 5;
+  const int t0 = blockIdx.x * kRouterMfmaTok;
+  const int kw = d / kRouterMfmaWaves;               // this wave's K range: [wave kw, +kw)
+  const bool row_ok = l32 < kRouterMfmaTok && t0 + l32 < T;
+  const bool col_ok = l32 < E;
+  const u32x4* xr = reinterpret_cast<const u32x4*>(
+      x + (size_t)(row_ok ? t0 + l32 : 0) * d + (size_t)wave * kw + 8 * h);
+  const u32x4* wr = reinterpret_cast<const u32x4*>(
+      w_r + (size_t)(col_ok ? l32 : 0) * d + (size_t)wave * kw + 8 * h);
+  f32x16 acc;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+  const u32x4 zero = {0u, 0u, 0u, 0u};
+  for (int k = 0; k < kw; k += 16 * kRouterMfmaU) {
+    u32x4 a[kRouterMfmaU], b[kRouterMfmaU];
+#pragma unroll
+    for (int u = 0; u < kRouterMfmaU; ++u) {
+      a[u] = row_ok ? __builtin_nontemporal_load(xr + (k + 16 * u) / 8) : zero;
+      b[u] = col_ok ? wr[(k + 16 * u) / 8] : zero;
+    }
+#pragma unroll
+    for (int u = 0; u < kRouterMfmaU; ++u)
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[u]),
+                                                    __builtin_bit_cast(bf16x8, b[u]), acc, 0, 0,
+                                                    0);
+  }
+  // Register r holds token row 8 (r / 4) + 4 h + r % 4 and expert column l32.
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int row = 8 * (r >> 2) + 4 * h + (r & 3);
+    if (row < kRouterMfmaTok && col_ok) part[wave][row][l32] = acc[r];
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < kRouterMfmaTok * E; i += 1024) {
+    const int row = i / E, e = i % E, t = t0 + row;
+    if (t >= T) continue;
+    float v = 0.f;
+#pragma unroll
+    for (int w = 0; w < kRouterMfmaWaves; ++w) v += part[w][row][e];
+    logits[(size_t)t * E + e] = v + (bias ? bias[e] : 0.f);
+  }
+}
+
+template <int E>
+static void launch_router_mfma_t(const void* x, const void* w_r, const float* bias, int T, int d,
+                                 float* logits, hipStream_t s) {
+  const int blocks = (T + kRouterMfmaTok - 1) / kRouterMfmaTok;
+  hipLaunchKernelGGL((router_mfma_kernel<E>), dim3(blocks), dim3(1024), 0, s, (const uint16_t*)x,
+                     (const uint16_t*)w_r, bias, T, d, logits);
+}
+
 void launch_router_small_e(const void* x, const void* w_r, const float* bias, int T, int d, int E,
                            bool bf16, float* logits, hipStream_t s) {
+  if (bf16 && T >= 1024 && d % (kRouterMfmaWaves * 16 * kRouterMfmaU) == 0) {
+    switch (E) {
+#define MOE_CASE(n) \
+  case n: launch_router_mfma_t<n>(x, w_r, bias, T, d, logits, s); return;
+      MOE_CASE(1) MOE_CASE(2) MOE_CASE(3) MOE_CASE(4) MOE_CASE(5) MOE_CASE(6) MOE_CASE(7)
+      MOE_CASE(8) MOE_CASE(9) MOE_CASE(10) MOE_CASE(11) MOE_CASE(12) MOE_CASE(13) MOE_CASE(14)
+      MOE_CASE(15) MOE_CASE(16)
+#undef MOE_CASE
+      default: break;
+    }
+  }
   if (bf16)
     launch_router_small_e_d<uint16_t>(x, w_r, bias, T, d, E, logits, s);
   else

@@ -380,6 +380,37 @@ def test_layer_with_select_bias(M, mode, T, E):
     run_and_compare(M, cfg, inp)
 
 
+@pytest.mark.parametrize("T,d,E", [(1024, 2048, 8), (1500, 2048, 13), (4096, 4096, 1),
+                                   (1030, 6144, 16)])
+def test_router_few_experts_matrix_cores(M, T, d, E):
+    """The few-expert router product on the matrix cores (at least 1024 bf16 tokens, d a multiple
+    of 2048, E <= 16; a ragged last block of tokens): logits within the float32 rounding bound of
+    the exact product and bitwise repeatable."""
+    _say("router few experts T=%d d=%d E=%d" % (T, d, E))
+    lm, synth, layer = M["lm"], M["synth"], M["layer"]
+    cfg = synth.tiny_config(T, d, E, 1, 64, "bf16", "softmax_topk")
+    inp = _to_cuda(synth.make_inputs(cfg, seed=6, device="cpu"))
+    h = P.host_inputs(inp)
+    bound, exact = P.logit_error_bound(h["x"], h["w_r"], h["bias"])
+    b = layer.alloc_buffers(cfg)
+    got = []
+    for _ in range(2):
+        lm.route(inp.x, inp.w_r, inp.bias, T, d, E, cfg.k, lm.MOE_BF16, 0, 0, b.logits,
+                 b.topk_idx, b.topk_gate, None, None, b.workspace)
+        torch.cuda.synchronize()
+        got.append(P.np32(b.logits).copy())
+        assert np.all(np.abs(got[-1] - exact) <= bound)
+    assert np.array_equal(got[0].view(np.int32), got[1].view(np.int32))
+
+
+def test_layer_few_experts_matrix_router(M):
+    """A whole layer whose router product takes the matrix-core form (T = 1024, d = 2048, E = 8)."""
+    synth = M["synth"]
+    cfg = synth.tiny_config(1024, 2048, 8, 2, 128, "bf16", "softmax_topk")
+    inp = _to_cuda(synth.make_inputs(cfg, seed=7, device="cpu"))
+    run_and_compare(M, cfg, inp)
+
+
 @pytest.mark.parametrize("T,d,E", [(700, 1024, 256), (8192, 512, 64), (33, 7168, 24)])
 def test_router_split_and_unsplit(M, T, d, E):
     """The matrix-core router product with the full workspace (K split into fixed chunks, summed
