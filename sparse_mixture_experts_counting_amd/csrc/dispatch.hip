@@ -217,6 +217,104 @@ __global__ __launch_bounds__(1024) void dispatch_one_chunk_kernel(
   }
 }
 
+// Up to kBlockA assignments (a prefill-sized batch) in one block of 16 waves, no workspace: wave w
+// ranks the assignments of its contiguous segment (64 at a time, in order) among the segment's
+// earlier ones to the same expert, counting per expert in its own LDS row; one thread per expert
+// then turns the 16 rows into exclusive prefixes over the waves (so an assignment's rank in its
+// expert's stream is its wave's prefix plus its rank in the segment), the counts, kept and
+// offsets follow as in dispatch_scan_kernel, and every assignment is placed.  The same integers
+// as the chunked path, in one launch instead of three.
+static constexpr int kBlockA = 16384, kBlockWaves = 16, kBlockPer = kBlockA / (64 * kBlockWaves);
+
+__global__ __launch_bounds__(1024) void dispatch_block_kernel(
+    const int32_t* __restrict__ idx, int A, int E, int nbits, int capacity,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ perm,
+    int32_t* __restrict__ inv, int32_t* __restrict__ n_dropped) {
+  __shared__ int32_t cnt[kBlockWaves][1024];   // per wave, then the waves' exclusive prefixes
+  __shared__ int32_t sc[1024];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int e = tid; e < kBlockWaves * 1024; e += 1024) (&cnt[0][0])[e] = 0;
+  __syncthreads();
+  // The wave's segment: whole 64-assignment windows, in assignment order.
+  const int per_wave = ((A + 63) / 64 + kBlockWaves - 1) / kBlockWaves;   // windows per wave
+  const int a_beg = wave * per_wave * 64;
+  int my_e[kBlockPer], my_rank[kBlockPer];
+#pragma unroll
+  for (int i = 0; i < kBlockPer; ++i) {
+    my_e[i] = -1;
+    my_rank[i] = 0;
+    if (i >= per_wave) continue;                 // uniform over the wave
+    const int a = a_beg + i * 64 + lane;
+    int e = -1;
+    if (a < A) {
+      e = idx[a];
+      if (e < 0 || e >= E) e = -1;
+    }
+    const bool valid = e >= 0;
+    uint64_t peers = __ballot(valid);
+    for (int b = 0; b < nbits; ++b) {
+      const bool bit = valid && ((e >> b) & 1);
+      const uint64_t m = __ballot(bit);
+      peers &= bit ? m : ~m;
+    }
+    const int below = __popcll(peers & lanemask_lt());
+    const int total = __popcll(peers);
+    if (valid) {
+      const int run = cnt[wave][e];              // every lane reads before the leader writes
+      my_rank[i] = run + below;
+      if (below == 0) cnt[wave][e] = run + total;
+    }
+    my_e[i] = e;
+  }
+  __syncthreads();
+  int kept = 0;
+  if (tid < E) {
+    int run = 0;
+    for (int w = 0; w < kBlockWaves; ++w) {
+      const int v = cnt[w][tid];
+      cnt[w][tid] = run;
+      run += v;
+    }
+    counts[tid] = run;
+    kept = (capacity > 0 && run > capacity) ? capacity : run;
+  }
+  sc[tid] = kept;
+  __syncthreads();
+  for (int o = 1; o < 1024; o <<= 1) {
+    const int v = (tid >= o) ? sc[tid - o] : 0;
+    __syncthreads();
+    sc[tid] += v;
+    __syncthreads();
+  }
+  if (tid < E) offsets[tid] = sc[tid] - kept;
+  if (tid == 0) {
+    offsets[E] = sc[1023];
+    n_dropped[0] = A - sc[1023];
+  }
+  __syncthreads();
+  if (tid < E) sc[tid] -= kept;                  // each expert's first row
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < kBlockPer; ++i) {
+    if (i >= per_wave) continue;
+    const int a = a_beg + i * 64 + lane;
+    if (a >= A) continue;
+    const int e = my_e[i];
+    if (e < 0) {
+      inv[a] = -1;
+      continue;
+    }
+    const int g = cnt[wave][e] + my_rank[i];
+    if (capacity <= 0 || g < capacity) {
+      const int pos = sc[e] + g;
+      perm[pos] = a;
+      inv[a] = pos;
+    } else {
+      inv[a] = -1;
+    }
+  }
+}
+
 size_t dispatch_workspace_bytes(int A, int E) {
   const size_t nchunk = (size_t)(A + kChunk - 1) / kChunk;
   return nchunk * E * sizeof(int32_t) + 256;
@@ -257,6 +355,11 @@ void launch_dispatch(const int32_t* topk_idx, int A, int E, int capacity, int32_
   if (nchunk == 1) {
     hipLaunchKernelGGL(dispatch_one_chunk_kernel, dim3(1), dim3(1024), 0, s, topk_idx, A, E,
                        nbits, capacity, counts, offsets, perm, inv, n_dropped);
+    return;
+  }
+  if (A <= kBlockA) {
+    hipLaunchKernelGGL(dispatch_block_kernel, dim3(1), dim3(1024), 0, s, topk_idx, A, E, nbits,
+                       capacity, counts, offsets, perm, inv, n_dropped);
     return;
   }
   hipLaunchKernelGGL(dispatch_hist_kernel, dim3(nchunk), dim3(kThreads), 0, s, topk_idx, A, E,

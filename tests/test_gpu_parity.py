@@ -96,7 +96,8 @@ def test_route_from_given_logits(M, E, k, mode):
 
 @pytest.mark.parametrize("T,E,k,C", [(1, 1, 1, 0), (5, 3, 2, 1), (300, 8, 2, 40), (2048, 8, 1, 256),
                                      (4096, 8, 2, 0), (3000, 64, 6, 200), (8192, 256, 8, 0),
-                                     (1500, 1024, 3, 2), (777, 17, 4, 0), (2500, 4, 1, 100)])
+                                     (1500, 1024, 3, 2), (777, 17, 4, 0), (2500, 4, 1, 100),
+                                     (2049, 8, 1, 0), (4096, 64, 4, 300), (4097, 64, 4, 0)])
 def test_dispatch_from_given_topk(M, T, E, k, C):
     _say("dispatch T=%d E=%d k=%d C=%d" % (T, E, k, C))
     rng = np.random.default_rng(T + E + k + C)
