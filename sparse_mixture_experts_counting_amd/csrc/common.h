@@ -53,6 +53,63 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
   return v;
 }
 
+// The same reductions on the vector unit's lane exchanges (DPP) instead of the LDS crossbar, for
+// the chains of reductions on one row (the gating's k arg-max rounds): exchanges with lane ^ 1 and
+// lane ^ 2, then with the mirrored lane of each 8 and of each 16 leave every lane of a 16-lane row
+// with that row's result; the four row results are read as uniform values and combined in a fixed
+// order.  Each exchange pairs two lanes that combine the same two operands, so every lane ends with
+// the same bits.  The whole wave must be active.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __builtin_bit_cast(float,
+                            __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)v, CTRL, 0xF, 0xF, false);
+  const uint32_t hi =
+      (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)(v >> 32), CTRL, 0xF, 0xF, false);
+  return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ float readlane_f32(float v, int l) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
+}
+__device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int l) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, l);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), l);
+  return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+  v += dpp_f32<0xB1>(v);    // lane ^ 1
+  v += dpp_f32<0x4E>(v);    // lane ^ 2
+  v += dpp_f32<0x141>(v);   // mirrored within 8
+  v += dpp_f32<0x140>(v);   // mirrored within 16
+  return (readlane_f32(v, 0) + readlane_f32(v, 16)) + (readlane_f32(v, 32) + readlane_f32(v, 48));
+}
+__device__ __forceinline__ float wave_max_dpp(float v) {
+  v = fmaxf(v, dpp_f32<0xB1>(v));
+  v = fmaxf(v, dpp_f32<0x4E>(v));
+  v = fmaxf(v, dpp_f32<0x141>(v));
+  v = fmaxf(v, dpp_f32<0x140>(v));
+  return fmaxf(fmaxf(readlane_f32(v, 0), readlane_f32(v, 16)),
+               fmaxf(readlane_f32(v, 32), readlane_f32(v, 48)));
+}
+__device__ __forceinline__ uint64_t wave_max_u64_dpp(uint64_t v) {
+  uint64_t w;
+  w = dpp_u64<0xB1>(v);
+  v = w > v ? w : v;
+  w = dpp_u64<0x4E>(v);
+  v = w > v ? w : v;
+  w = dpp_u64<0x141>(v);
+  v = w > v ? w : v;
+  w = dpp_u64<0x140>(v);
+  v = w > v ? w : v;
+  const uint64_t a = readlane_u64(v, 0), b = readlane_u64(v, 16);
+  const uint64_t c = readlane_u64(v, 32), d = readlane_u64(v, 48);
+  const uint64_t ab = a > b ? a : b, cd = c > d ? c : d;
+  return ab > cd ? ab : cd;
+}
+
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
 // Bits below this lane in a 64-bit ballot.

@@ -1285,6 +1285,9 @@ __global__ __launch_bounds__(256) void splitk_finish_kernel(const GemmParams p) 
   const int rows = p.offsets ? p.offsets[p.G] : p.M;
   const int nv = p.N / 8;                              // 8 columns per thread
   const size_t total = (size_t)rows * nv;
+  // fp32 output rows (and the bias) on 16-byte boundaries: vector stores.
+  const bool vec_out = EPI == EPI_STORE_F32_BIAS && p.ldc % 4 == 0 &&
+                       ((uintptr_t)p.C & 15) == 0 && ((uintptr_t)p.bias & 15) == 0;
   for (size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x; idx < total;
        idx += (size_t)gridDim.x * 256) {
     const int row = (int)(idx / nv), c0 = (int)(idx % nv) * 8;
@@ -1323,8 +1326,24 @@ __global__ __launch_bounds__(256) void splitk_finish_kernel(const GemmParams p) 
     }
     if constexpr (EPI == EPI_STORE_F32_BIAS) {   // the router's fp32 logits (+ bias)
       float* dst = (float*)p.C + (size_t)row * p.ldc + c0;
+      if (vec_out) {   // two 16-byte stores (and bias loads)
+        f32x4 b0 = {0.f, 0.f, 0.f, 0.f}, b1 = b0;
+        if (p.bias) {
+          b0 = *reinterpret_cast<const f32x4*>(p.bias + c0);
+          b1 = *reinterpret_cast<const f32x4*>(p.bias + c0 + 4);
+        }
+        f32x4 o0, o1;
 #pragma unroll
-      for (int q = 0; q < 8; ++q) dst[q] = s[0][q] + (p.bias ? p.bias[c0 + q] : 0.f);
+        for (int q = 0; q < 4; ++q) {
+          o0[q] = s[0][q] + b0[q];
+          o1[q] = s[0][4 + q] + b1[q];
+        }
+        *reinterpret_cast<f32x4*>(dst) = o0;
+        *reinterpret_cast<f32x4*>(dst + 4) = o1;
+      } else {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) dst[q] = s[0][q] + (p.bias ? p.bias[c0 + q] : 0.f);
+      }
       continue;
     }
     u32x4 o, oa, ob;

@@ -300,7 +300,7 @@ __device__ __forceinline__ void gate_row(const float* row, const float* __restri
   float m = -INFINITY;
 #pragma unroll
   for (int i = 0; i < EPL; ++i) m = fmaxf(m, v[i]);
-  m = wave_max(m);
+  m = wave_max_dpp(m);
   float ex[EPL];
   float s = 0.f;
 #pragma unroll
@@ -308,7 +308,7 @@ __device__ __forceinline__ void gate_row(const float* row, const float* __restri
     ex[i] = (lane + 64 * i < E) ? expf(v[i] - m) : 0.f;
     s += ex[i];
   }
-  s = wave_sum(s);
+  s = wave_sum_dpp(s);
   const float inv_s = 1.0f / s;
 #pragma unroll
   for (int i = 0; i < EPL; ++i) acc_p[i] += ex[i] * inv_s;
@@ -323,9 +323,16 @@ __device__ __forceinline__ void gate_row(const float* row, const float* __restri
     uint64_t best = key[0];
 #pragma unroll
     for (int i = 1; i < EPL; ++i) best = key[i] > best ? key[i] : best;
-    best = wave_max_u64(best);
+    best = wave_max_u64_dpp(best);
     const int e_j = (int)(~(uint32_t)best);
-    const float v_j = select_bias ? row[e_j] : from_ordered_bits((uint32_t)(best >> 32));
+    float v_j = from_ordered_bits((uint32_t)(best >> 32));
+    if (select_bias) {   // the score is biased: take the logit from the lane that holds it
+      float own = v[0];
+#pragma unroll
+      for (int i = 1; i < EPL; ++i)
+        if ((e_j >> 6) == i) own = v[i];
+      v_j = readlane_f32(own, e_j & 63);
+    }
 #pragma unroll
     for (int i = 0; i < EPL; ++i)
       if (lane + 64 * i == e_j) key[i] = 0ull;
@@ -334,7 +341,7 @@ __device__ __forceinline__ void gate_row(const float* row, const float* __restri
       my_v = v_j;
     }
   }
-  const float v0 = wave_max(my_v);
+  const float v0 = wave_max_dpp(my_v);
   float w = 0.f;
   if (lane < k) {
     if (mode == 0)
@@ -345,24 +352,24 @@ __device__ __forceinline__ void gate_row(const float* row, const float* __restri
       w = expf(log_sigmoid(my_v) - log_sigmoid(v0));
   }
   float g = w;
-  if (mode != 1) g = w / wave_sum(w);
+  if (mode != 1) g = w / wave_sum_dpp(w);
   if (lane < k) {
     topk_idx[(size_t)t * k + lane] = my_e;
     topk_gate[(size_t)t * k + lane] = g;
   }
 }
 
+// kGateWaves waves per block, a wave per row at a time; the waves' P and lse partials are added in
+// wave order, one partial per block.
+static constexpr int kGateWaves = 16;
+
 template <int EPL>
-__global__ __launch_bounds__(256) void gate_topk_kernel(const float* __restrict__ logits,
-                                                        const float* __restrict__ select_bias,
-                                                        int T, int E, int k, int mode,
-                                                        int rows_per_block,
-                                                        int32_t* __restrict__ topk_idx,
-                                                        float* __restrict__ topk_gate,
-                                                        float* __restrict__ part_p,
-                                                        float* __restrict__ part_l) {
-  __shared__ float red_p[4][1024];
-  __shared__ float red_l[4];
+__global__ __launch_bounds__(64 * kGateWaves) void gate_topk_kernel(
+    const float* __restrict__ logits, const float* __restrict__ select_bias, int T, int E, int k,
+    int mode, int rows_per_block, int32_t* __restrict__ topk_idx, float* __restrict__ topk_gate,
+    float* __restrict__ part_p, float* __restrict__ part_l) {
+  __shared__ float red_p[kGateWaves][64 * EPL];
+  __shared__ float red_l[kGateWaves];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int row0 = blockIdx.x * rows_per_block;
@@ -372,21 +379,27 @@ __global__ __launch_bounds__(256) void gate_topk_kernel(const float* __restrict_
 #pragma unroll
   for (int i = 0; i < EPL; ++i) acc_p[i] = 0.f;
   float acc_l = 0.f;
-  for (int t = row0 + wave; t < row1; t += 4)
+  for (int t = row0 + wave; t < row1; t += kGateWaves)
     gate_row<EPL>(logits + (size_t)t * E, select_bias, t, E, k, mode, topk_idx, topk_gate, acc_p,
                   acc_l);
 
   if (part_p) {
 #pragma unroll
-    for (int i = 0; i < EPL; ++i) {
-      const int e = lane + 64 * i;
-      if (e < E) red_p[wave][e] = acc_p[i];
-    }
+    for (int i = 0; i < EPL; ++i) red_p[wave][lane + 64 * i] = acc_p[i];
     if (lane == 0) red_l[wave] = acc_l;
     __syncthreads();
-    for (int e = threadIdx.x; e < E; e += 256)
-      part_p[(size_t)blockIdx.x * E + e] = ((red_p[0][e] + red_p[1][e]) + red_p[2][e]) + red_p[3][e];
-    if (threadIdx.x == 0) part_l[blockIdx.x] = ((red_l[0] + red_l[1]) + red_l[2]) + red_l[3];
+    for (int e = threadIdx.x; e < E; e += 64 * kGateWaves) {
+      float v = red_p[0][e];
+#pragma unroll
+      for (int w = 1; w < kGateWaves; ++w) v += red_p[w][e];
+      part_p[(size_t)blockIdx.x * E + e] = v;
+    }
+    if (threadIdx.x == 0) {
+      float v = red_l[0];
+#pragma unroll
+      for (int w = 1; w < kGateWaves; ++w) v += red_l[w];
+      part_l[blockIdx.x] = v;
+    }
   }
 }
 
@@ -415,11 +428,9 @@ __global__ __launch_bounds__(256) void route_finalize_kernel(const float* __rest
 }
 
 int gate_rows_per_block(int T) {
-  // A wave per row at a time, four waves per block: at least four blocks per CU for large T (the
-  // row's k arg-max rounds are chains of cross-lane exchanges whose latency other waves hide),
-  // few partials for small T.
-  if (T >= 8192) return 8;
-  return 4;
+  // One row per wave up to 4096 rows (each wave's rows are a chain of dependent reductions), two
+  // from 8192 rows (fewer partials for the finalizing pass to add).
+  return T >= 8192 ? 2 * kGateWaves : kGateWaves;
 }
 
 void launch_gate_topk(const float* logits, const float* select_bias, int T, int E, int k, int mode,
@@ -430,8 +441,8 @@ void launch_gate_topk(const float* logits, const float* select_bias, int T, int 
   float* pp = (prob_sum || lse_sq_sum) ? part_p : nullptr;
   const int epl = (E + 63) / 64;
 #define MOE_GATE(n)                                                                          \
-  hipLaunchKernelGGL((gate_topk_kernel<n>), dim3(nblk), dim3(256), 0, s, logits, select_bias, T, \
-                     E, k, mode, rpb, topk_idx, topk_gate, pp, part_l)
+  hipLaunchKernelGGL((gate_topk_kernel<n>), dim3(nblk), dim3(64 * kGateWaves), 0, s, logits,     \
+                     select_bias, T, E, k, mode, rpb, topk_idx, topk_gate, pp, part_l)
   if (epl <= 1) MOE_GATE(1);
   else if (epl <= 2) MOE_GATE(2);
   else if (epl <= 4) MOE_GATE(4);
