@@ -144,10 +144,12 @@ def cpu_baseline(cfg, inp, n_tokens, repeats):
     return out
 
 
-def measured_peaks(torch, lm, dev):
+def measured_peaks(torch, lm, dev, gemm_shape=None):
     """The chip's measured ceilings beside its published ones: a loop of bf16 32x32x16 matrix
     instructions on random register operands (moe_peak_mfma) and a 1 GiB streaming copy
-    (moe_peak_copy), each the best of 10 launches timed with HIP events."""
+    (moe_peak_copy), each the best of 10 launches timed with HIP events.  With `gemm_shape`
+    (M, N, K), also PyTorch's library GEMM (torch.nn.functional.linear in bf16, weights [N][K]) on
+    that dense shape, a reference for what the vendor library reaches at the same size."""
     cus = torch.cuda.get_device_properties(dev).multi_processor_count
     g = torch.Generator(device=dev)
     g.manual_seed(12345)
@@ -174,7 +176,19 @@ def measured_peaks(torch, lm, dev):
     t_mfma = best(lambda: lm.peak_mfma(ops, blocks, iters, out))
     t_copy = best(lambda: lm.peak_copy(src, dst, nbytes))
     del src, dst
+    lib = None
+    if gemm_shape is not None:
+        M, N, K = gemm_shape
+        a = torch.randn(M, K, generator=g, device=dev).to(torch.bfloat16)
+        w = torch.randn(N, K, generator=g, device=dev).to(torch.bfloat16)
+        c = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+        t_lib = best(lambda: torch.matmul(a, w.t(), out=c))
+        lib = {"shape_mnk": [M, N, K], "tflops": 2.0 * M * N * K / (t_lib * 1e-3) / 1e12,
+               "ms": t_lib, "how": "torch.matmul(a [M][K], w[N][K].t()) in bf16 (the vendor "
+                                   "GEMM library), best of 10"}
+        del a, w, c
     return {"mfma_bf16_tflops": flops / (t_mfma * 1e-3) / 1e12,
+            "library_gemm_bf16": lib,
             "copy_gbs": 2.0 * nbytes / (t_copy * 1e-3) / 1e9,
             "published_bf16_tflops": PEAK_BF16_TFLOPS, "published_hbm_gbs": PEAK_HBM_GBS,
             "how": "moe_peak_mfma: %d blocks x 8 waves x %d iterations of 8 independent "
@@ -413,7 +427,10 @@ def main():
     del h
     if not args.no_peaks:
         log("bench: measuring the MFMA-loop and copy ceilings")
-        result["measured_peaks"] = measured_peaks(torch, lm, dev)
+        # The library reference: the up projection's kept rows as one dense GEMM against both
+        # stacked weight matrices of one expert (the same FLOPs, none of the grouping or gather).
+        shape = (n_kept, 2 * f, d) if roof["bound"] == "mfma" and sb == 2 else None
+        result["measured_peaks"] = measured_peaks(torch, lm, dev, shape)
     if not args.no_cpu_baseline:
         log("bench: timing the CPU oracle on a sample")
         result["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_sample_tokens, args.cpu_repeats)

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #define MOE_WAVE 64
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -93,6 +95,20 @@ __device__ __forceinline__ float wave_max_dpp(float v) {
   v = fmaxf(v, dpp_f32<0x140>(v));
   return fmaxf(fmaxf(readlane_f32(v, 0), readlane_f32(v, 16)),
                fmaxf(readlane_f32(v, 32), readlane_f32(v, 48)));
+}
+__device__ __forceinline__ uint32_t wave_max_u32_dpp(uint32_t v) {
+  auto ex = [](uint32_t x, auto ctrl) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, decltype(ctrl)::value, 0xF, 0xF, false);
+  };
+  v = max(v, ex(v, std::integral_constant<int, 0xB1>()));
+  v = max(v, ex(v, std::integral_constant<int, 0x4E>()));
+  v = max(v, ex(v, std::integral_constant<int, 0x141>()));
+  v = max(v, ex(v, std::integral_constant<int, 0x140>()));
+  const uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)v, 0);
+  const uint32_t b = (uint32_t)__builtin_amdgcn_readlane((int)v, 16);
+  const uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)v, 32);
+  const uint32_t d = (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
+  return max(max(a, b), max(c, d));
 }
 __device__ __forceinline__ uint64_t wave_max_u64_dpp(uint64_t v) {
   uint64_t w;

@@ -272,28 +272,40 @@ __device__ __forceinline__ float from_ordered_bits(uint32_t o) {
   return __uint_as_float((o & 0x80000000u) ? (o ^ 0x80000000u) : ~o);
 }
 
-// Gating, top-k and the loss terms of one row t, by one wave.  `row` holds the row's E logits
-// (global memory or LDS); acc_p[i] (expert lane + 64 i) and acc_l accumulate the row's softmax
-// probabilities and squared logsumexp.
+// Lane l's logits of one row (experts l, l + 64, ...), every load issued before any is used (lanes
+// past E read expert E - 1; gate_row masks them).
 template <int EPL>
-__device__ __forceinline__ void gate_row(const float* row, const float* __restrict__ select_bias,
+__device__ __forceinline__ void load_row(const float* row, int E, float (&v)[EPL]) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    const int e = lane + 64 * i;
+    v[i] = row[e < E ? e : E - 1];
+  }
+}
+
+// Gating, top-k and the loss terms of one row t, by one wave.  `v` holds the lane's logits of the
+// row as load_row reads them; acc_p[i] (expert lane + 64 i) and acc_l accumulate the row's softmax
+// probabilities and squared logsumexp.
+// `sb` holds the lane's selection biases (as load_row reads them) when `biased`.
+template <int EPL>
+__device__ __forceinline__ void gate_row(float (&v)[EPL], bool biased, const float (&sb)[EPL],
                                          int t, int E, int k, int mode,
                                          int32_t* __restrict__ topk_idx,
                                          float* __restrict__ topk_gate, float* acc_p,
                                          float& acc_l) {
   const int lane = threadIdx.x & 63;
-  float v[EPL];
-  uint64_t key[EPL];
+  uint32_t key[EPL];   // order-preserving bits of the score
+  uint32_t live = 0;   // bit i: expert lane + 64 i exists and is not selected yet
 #pragma unroll
   for (int i = 0; i < EPL; ++i) {
     const int e = lane + 64 * i;
     if (e < E) {
-      v[i] = row[e];
-      const float score = select_bias ? v[i] + select_bias[e] : v[i];
-      key[i] = ((uint64_t)ordered_bits(score) << 32) | (uint32_t)(~e);
+      key[i] = ordered_bits(biased ? v[i] + sb[i] : v[i]);
+      live |= 1u << i;
     } else {
       v[i] = -INFINITY;
-      key[i] = 0ull;
+      key[i] = 0u;
     }
   }
   // Full-row softmax (for P_e) and logsumexp (for the z-loss).
@@ -315,27 +327,32 @@ __device__ __forceinline__ void gate_row(const float* row, const float* __restri
   const float lse = m + logf(s);
   acc_l += lse * lse;
 
-  // Top-k by repeated wave arg-max over the keys.  v0 is the largest selected logit (the first
-  // one selected when there is no selection bias), the shift that keeps the gates finite.
+  // Top-k by repeated wave arg-max: the largest live score, then among the live experts holding
+  // it the lowest index (the first nonzero ballot over i, its lowest lane), which leaves the
+  // selection.  v0 is the largest selected logit (the first one selected when there is no
+  // selection bias), the shift that keeps the gates finite.
   int my_e = 0;
   float my_v = -INFINITY;
   for (int j = 0; j < k; ++j) {
-    uint64_t best = key[0];
+    uint32_t best = 0u;
 #pragma unroll
-    for (int i = 1; i < EPL; ++i) best = key[i] > best ? key[i] : best;
-    best = wave_max_u64_dpp(best);
-    const int e_j = (int)(~(uint32_t)best);
-    float v_j = from_ordered_bits((uint32_t)(best >> 32));
-    if (select_bias) {   // the score is biased: take the logit from the lane that holds it
+    for (int i = 0; i < EPL; ++i) best = max(best, ((live >> i) & 1u) ? key[i] : 0u);
+    best = wave_max_u32_dpp(best);
+    int e_j = -1;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+      const uint64_t b = __ballot(((live >> i) & 1u) && key[i] == best);
+      if (e_j < 0 && b != 0ull) e_j = 64 * i + (int)__builtin_ctzll(b);
+    }
+    if (lane == (e_j & 63)) live &= ~(1u << (e_j >> 6));
+    float v_j = from_ordered_bits(best);
+    if (biased) {   // the score is biased: take the logit from the lane that holds it
       float own = v[0];
 #pragma unroll
       for (int i = 1; i < EPL; ++i)
         if ((e_j >> 6) == i) own = v[i];
       v_j = readlane_f32(own, e_j & 63);
     }
-#pragma unroll
-    for (int i = 0; i < EPL; ++i)
-      if (lane + 64 * i == e_j) key[i] = 0ull;
     if (lane == j) {
       my_e = e_j;
       my_v = v_j;
@@ -379,9 +396,20 @@ __global__ __launch_bounds__(64 * kGateWaves) void gate_topk_kernel(
 #pragma unroll
   for (int i = 0; i < EPL; ++i) acc_p[i] = 0.f;
   float acc_l = 0.f;
-  for (int t = row0 + wave; t < row1; t += kGateWaves)
-    gate_row<EPL>(logits + (size_t)t * E, select_bias, t, E, k, mode, topk_idx, topk_gate, acc_p,
-                  acc_l);
+  // The selection biases are the same for every row; the next row's logits are loaded while this
+  // row is gated.
+  float sb[EPL] = {}, nxt[EPL];
+  const bool biased = select_bias != nullptr;
+  if (biased) load_row<EPL>(select_bias, E, sb);
+  int t = row0 + wave;
+  if (t < row1) load_row<EPL>(logits + (size_t)t * E, E, nxt);
+  for (; t < row1; t += kGateWaves) {
+    float v[EPL];
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) v[i] = nxt[i];
+    if (t + kGateWaves < row1) load_row<EPL>(logits + (size_t)(t + kGateWaves) * E, E, nxt);
+    gate_row<EPL>(v, biased, sb, t, E, k, mode, topk_idx, topk_gate, acc_p, acc_l);
+  }
 
   if (part_p) {
 #pragma unroll
