@@ -352,6 +352,47 @@ def test_route_select_bias_from_given_logits(M, E, k, mode):
     assert not np.array_equal(want, O.select_topk(L, k)), "the bias should change some choices"
 
 
+_MANY_ROWS = {}
+
+
+def _many_rows_case(T, E, k, biased):
+    """Logits, selection bias and the oracle's selection, P and lse (shared by the gating modes)."""
+    key = (T, E, k, biased)
+    if key not in _MANY_ROWS:
+        rng = np.random.default_rng(T + 31 * E + 7 * k + biased)
+        L = rng.normal(0, 2, size=(T, E)).astype(np.float32)
+        L[::3] = np.round(L[::3] * 4) / 4
+        sb = rng.normal(0, 1.0, size=E).astype(np.float32) if biased else None
+        p, lse = O.row_softmax_lse(L)
+        _MANY_ROWS[key] = (L, sb, O.select_topk(L, k, sb), p, lse)
+    return _MANY_ROWS[key]
+
+
+@pytest.mark.parametrize("T", [4101, 8229])
+@pytest.mark.parametrize("E,k", [(8, 2), (256, 8), (1024, 4)])
+@pytest.mark.parametrize("biased", [False, True])
+@pytest.mark.parametrize("mode", ["softmax_topk", "sigmoid_topk"])
+def test_route_many_rows(M, T, E, k, biased, mode):
+    """Gating at the row counts where each wave takes one row (T < 8192) or two (the second one's
+    logits loaded while the first is gated), with a ragged last block; a third of the rows hold
+    quarter-step values (many ties).  Selection bit-exact, gates, P and lse sums to tolerance."""
+    import types
+    _say("route many rows T=%d E=%d k=%d biased=%d mode=%s" % (T, E, k, biased, mode))
+    L, sb, want, p, lse = _many_rows_case(T, E, k, biased)
+    cfg = M["synth"].tiny_config(T, 8, E, k, 8, "fp32", mode)
+    b = M["layer"].alloc_buffers(cfg)
+    b.logits.copy_(torch.from_numpy(L))
+    inp = types.SimpleNamespace(select_bias=torch.from_numpy(sb).cuda()) if biased else None
+    M["layer"].route(cfg, inp, b, logits_in=True)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(P.npi(b.topk_idx), want)
+    g_ref = O.gate_weights(L, want, P.GATE_CODE[mode])
+    np.testing.assert_allclose(P.np32(b.topk_gate), g_ref, atol=1e-6, rtol=0)
+    np.testing.assert_allclose(P.np32(b.prob_sum), p.sum(axis=0), rtol=2e-5, atol=1e-5)
+    want_l = float(np.sum(lse * lse))
+    assert abs(float(P.np32(b.lse_sq_sum)[0]) - want_l) <= 2e-5 * max(1.0, want_l)
+
+
 def test_update_select_bias_exact(M):
     _say("update select bias")
     lm = M["lm"]
