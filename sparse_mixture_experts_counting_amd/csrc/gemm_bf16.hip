@@ -1595,11 +1595,14 @@ static int splitk_factor(int rows_max, int G, bool grouped, int N, int K, int ep
   // one block per CU over two rounds (measured no slower on the weight stream than one round).
   const long long slots = 2ll * (cus > 0 ? cus : 256);
   if (tiles >= 2 * slots) return 1;
-  // Fewer rows than a tile per group: weight streaming, bound by HBM; any full round keeps HBM
-  // busy, so split only as far as one round needs (fewer partial sums to add).
+  // Fewer rows than a tile per group: weight streaming, bound by HBM; one round of one block per
+  // CU keeps HBM busy, so split only as far as that round needs (fewer partial sums to add, and
+  // each block's stream long enough to hide its ring's fill: measured 6% faster on the decode down
+  // projection than splitting for two blocks per CU).
   if ((grouped ? rows_max / std::max(G, 1) : rows_max) < BM) {
+    const long long round1 = cus > 0 ? cus : 256;
     int ks = 1;
-    while (ks < 16 && tiles * ks < slots && (K / 64) % (ks * 2) == 0) ks *= 2;
+    while (ks < 16 && tiles * ks < round1 && (K / 64) % (ks * 2) == 0) ks *= 2;
     return ks;
   }
   auto busy = [&](long long items) {                    // mean occupancy of the rounds
