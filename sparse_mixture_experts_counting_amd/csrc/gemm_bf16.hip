@@ -682,6 +682,9 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, TileCoord tc, int
         }
         st = nx;
       }
+      // The loads of the steps past the end (zeros) land in LDS before the block may exit or
+      // take another tile.
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0<0>());
     };
     if constexpr (NSB > NST) {
       static_assert(NST == 2, "split rings take a 2-stage A ring");
@@ -1189,12 +1192,10 @@ __device__ __forceinline__ BsScan bs_scan(const GemmParams& p, int NT) {
   return s;
 }
 
-// Tile `bid` (block order) of the block-sparse map -> coordinates; false past the last tile.
-__device__ __forceinline__ bool bs_tile(const GemmParams& p, int NT, int bid, TileCoord& tc) {
-  const BsScan s = bs_scan(p, NT);
+// Tile t of the merged order of the block-sparse map -> coordinates (s from bs_scan).
+__device__ __forceinline__ void bs_tile_at(const GemmParams& p, int NT, const BsScan& s, int t,
+                                           TileCoord& tc) {
   const int total = s.big + s.small;
-  if (bid >= total) return false;
-  const int t = xcd_round_order(bid, total, p.slots);
   const long long S = s.small, TT = total;
   const int small_before = (int)((long long)t * S / TT);
   const bool is_small = (int)((long long)(t + 1) * S / TT) > small_before;
@@ -1244,7 +1245,27 @@ __device__ __forceinline__ bool bs_tile(const GemmParams& p, int NT, int bid, Ti
     tc.row0 = rs + (m_first + in % gm) * kBsTall;
     tc.row_end = min(tc.row0 + kBsTall, re);
   }
+}
+
+// Tile `bid` (block order) of the block-sparse map -> coordinates; false past the last tile.
+__device__ __forceinline__ bool bs_tile(const GemmParams& p, int NT, int bid, TileCoord& tc) {
+  const BsScan s = bs_scan(p, NT);
+  const int total = s.big + s.small;
+  if (bid >= total) return false;
+  bs_tile_at(p, NT, s, xcd_round_order(bid, total, p.slots), tc);
   return true;
+}
+
+// Ticket j of XCD x -> tile of the merged order, or -1 past XCD x's share.  The same tiles the
+// hardware's round-robin dealing of blocks (block b on XCD b % 8) gives XCD x under
+// xcd_round_order: in each whole round of `round` tiles its chunk of round / 8 consecutive tiles,
+// then every eighth tile of the last partial round.
+__device__ __forceinline__ int bs_ticket_tile(int x, int j, int total, int round) {
+  const int chunk = round >> 3;
+  const int whole = round >= 8 ? total / round : 0;
+  if (j < whole * chunk) return (j / chunk) * round + x * chunk + j % chunk;
+  const int t = whole * round + x + 8 * (j - whole * chunk);
+  return t < total ? t : -1;
 }
 
 // Tile shapes of the block-sparse launch per epilogue: two weight matrices of 128 columns each
@@ -1254,12 +1275,9 @@ constexpr int bs_nmat(int epi) { return epi_swiglu(epi) || epi == EPI_SWIGLU_BWD
 constexpr int bs_bn(int epi) { return bs_nmat(epi) == 2 ? 128 : 256; }
 
 template <int EPI, bool BT>
-__global__ __launch_bounds__(512, 1) void gemm_bs_kernel(const GemmParams p) {
+__device__ __forceinline__ void bs_run_tile(const GemmParams& p, TileCoord tc) {
   constexpr int NMAT = bs_nmat(EPI);
   constexpr int BN = bs_bn(EPI);                     // columns per matrix, both tile kinds
-  const int NT = (p.N + BN - 1) / BN;
-  TileCoord tc;
-  if (!bs_tile(p, NT, blockIdx.x, tc)) return;
   tc.g = __builtin_amdgcn_readfirstlane(tc.g);
   tc.row0 = __builtin_amdgcn_readfirstlane(tc.row0);
   tc.row_end = __builtin_amdgcn_readfirstlane(tc.row_end);
@@ -1276,6 +1294,56 @@ __global__ __launch_bounds__(512, 1) void gemm_bs_kernel(const GemmParams p) {
   } else
     gemm_tile<kBsTall, BN, NMAT, BT ? 2 : 4, BT ? 4 : 2, 64, 2, 1, EPI, false, BT>(p, tc, 0, 1,
                                                                                     -1, 0, 0);
+}
+
+// One block per tile: the hardware deals the blocks to the CUs.
+template <int EPI, bool BT>
+__global__ __launch_bounds__(512, 1) void gemm_bs_kernel(const GemmParams p) {
+  const int NT = (p.N + bs_bn(EPI) - 1) / bs_bn(EPI);
+  TileCoord tc;
+  if (!bs_tile(p, NT, blockIdx.x, tc)) return;
+  bs_run_tile<EPI, BT>(p, tc);
+}
+
+// One block per CU taking tiles from counters.  The hardware hands a CU the next block of its
+// dealing order only when that block's turn comes, so with tiles of unequal length (thin and
+// tall) CUs wait between blocks; here each block takes the next tile of its XCD's share as soon
+// as it is done (the same tiles per XCD, so the L2 sharing is unchanged), then helps the other
+// XCDs once its own share is gone.  The map scan runs once per block.  Every block ends when all
+// eight counters are past their shares, so the grid always drains.
+template <int EPI, bool BT>
+__global__ __launch_bounds__(512, 1) void gemm_bs_persistent_kernel(const GemmParams p) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  const int NT = (p.N + bs_bn(EPI) - 1) / bs_bn(EPI);
+  const BsScan s = bs_scan(p, NT);
+  const int total = s.big + s.small;
+  // HW_REG_XCC_ID: the XCD this block runs on.
+  const int x0 = (int)(__builtin_amdgcn_s_getreg(20 | (31 << 11)) & 7);
+  int tried = 0;   // thread 0: XCD shares found empty so far
+  for (;;) {
+    if (threadIdx.x == 0) {
+      int t = -1;
+      while (tried < 8) {
+        const int x = (x0 + tried) & 7;
+        t = bs_ticket_tile(x, atomicAdd(p.tickets + x, 1), total, p.slots);
+        if (t >= 0) break;
+        ++tried;
+      }
+      *(volatile int*)smem = t;
+    }
+    __syncthreads();
+    const int t = __builtin_amdgcn_readfirstlane(*(volatile int*)smem);
+    __syncthreads();   // read by every wave before the tile's loads overwrite it
+    if (t < 0) break;
+    TileCoord tc;
+    bs_tile_at(p, NT, s, t, tc);
+    bs_run_tile<EPI, BT>(p, tc);
+    __syncthreads();   // every wave is done with the LDS stages before the next tile's loads
+  }
+}
+
+__global__ void zero_tickets_kernel(int* tickets) {
+  if (threadIdx.x < 8) tickets[threadIdx.x] = 0;
 }
 
 // Sum the K-chunk partials of every valid row in a fixed order and apply the epilogue.
@@ -1487,29 +1555,47 @@ static hipError_t launch_t(const GemmParams& p, int rows_max, hipStream_t s) {
 }
 
 // The block-sparse launch (every bf16-output epilogue, weights K-contiguous or transposed).
+size_t gemm_bf16_partial_bytes(int rows_max, int G, bool grouped, int N, int K, int epi);
+
 template <int EPI, bool BT>
 static hipError_t launch_bs_t(const GemmParams& p, int rows_max, hipStream_t s) {
-  auto kern = gemm_bs_kernel<EPI, BT>;
   static_assert(lds_bytes<kBsThin, bs_bn(EPI), bs_nmat(EPI), 64, 4, 1>() == kMaxLds &&
                     lds_bytes<kBsTall, bs_bn(EPI), bs_nmat(EPI), 64, 2, 1>() == kMaxLds,
                 "both tile kinds fill the LDS the launch asks for");
-  static std::atomic<bool> attr_set[64];
+  // One block per CU taking tiles from counters when the caller's split-K scratch (which this
+  // launch does not otherwise use) can hold them; else one block per tile.
+  // (The SwiGLU-backward epilogues never get scratch: they run on whole sums only.)
+  constexpr bool can_persist = EPI == EPI_SWIGLU || EPI == EPI_SWIGLU_SAVE || EPI == EPI_STORE;
+  const bool persistent = can_persist && p.part != nullptr && device_cus() >= 8 &&
+                          gemm_bf16_partial_bytes(rows_max, p.G, true, p.N, p.K, EPI) >= 64;
+  void (*kern)(GemmParams) = gemm_bs_kernel<EPI, BT>;
+  if constexpr (can_persist) {
+    if (persistent) kern = gemm_bs_persistent_kernel<EPI, BT>;
+  }
+  static std::atomic<bool> attr_set[64][2];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-  if (!attr_set[dev].load(std::memory_order_acquire)) {
+  if (!attr_set[dev][persistent].load(std::memory_order_acquire)) {
     hipError_t e = hipFuncSetAttribute((const void*)kern,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLds);
     if (e != hipSuccess) return e;
-    attr_set[dev].store(true, std::memory_order_release);
+    attr_set[dev][persistent].store(true, std::memory_order_release);
   }
   GemmParams q = p;
   q.ksplit = 1;
   q.slots = device_cus() / 8 * 8;   // one block per CU: the blocks of one round
   const int NT = (p.N + bs_bn(EPI) - 1) / bs_bn(EPI);
   // Every group yields at most floor(n_g / 256) + 1 tiles per column tile.
-  const int grid = tiles_upper_bound(rows_max, p.G, true, kBsTall, NT);
-  if (grid <= 0) return hipSuccess;
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(512), kMaxLds, s, q);
+  const int tiles = tiles_upper_bound(rows_max, p.G, true, kBsTall, NT);
+  if (tiles <= 0) return hipSuccess;
+  if (persistent) {
+    q.tickets = (int*)p.part;
+    hipLaunchKernelGGL(zero_tickets_kernel, dim3(1), dim3(64), 0, s, q.tickets);
+    hipLaunchKernelGGL(kern, dim3(std::min(tiles, q.slots)), dim3(512), kMaxLds, s, q);
+  } else {
+    q.tickets = nullptr;
+    hipLaunchKernelGGL(kern, dim3(tiles), dim3(512), kMaxLds, s, q);
+  }
   return hipGetLastError();
 }
 

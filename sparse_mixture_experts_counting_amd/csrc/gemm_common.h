@@ -60,6 +60,9 @@ struct GemmParams {
   int bt_k1;
   // Transposed A (at != 0, K-grouped only, with bt): A is stored [K][M] (row stride lda).
   int at;
+  // Block-sparse launch with one block per CU (set by the launcher): 8 tile counters, one per
+  // XCD, zeroed on the stream before the launch; NULL for one block per tile.
+  int* tickets;
 };
 
 enum {
