@@ -179,10 +179,16 @@ __device__ __forceinline__ TailPlan tail_plan(int total, int slots, int K) {
 // hint (bit 1 of a buffer load's cache-policy operand), for launches that read every weight panel
 // once (the decode-sized products, bound by the weight stream: HBM serves such reads about 10%
 // faster); otherwise the default policy keeps panels that several row tiles share in the caches.
+struct NoHook {
+  __device__ void operator()() const {}
+};
+
+// `after_loop` runs in every wave once the K loop is done, before the epilogue.
 template <int BM, int BN, int NMAT, int WGM, int WGN, int BK, int NST, int MINB, int EPI, bool TAIL,
-          bool BT = false, bool AT = false, bool NTB = false>
+          bool BT = false, bool AT = false, bool NTB = false, class Hook = NoHook>
 __device__ __forceinline__ void gemm_tile(const GemmParams& p, TileCoord tc, int kc, int nsplit,
-                                          int rtile, int kg_beg, int kg_len) {
+                                          int rtile, int kg_beg, int kg_len,
+                                          Hook after_loop = Hook()) {
   constexpr int NTHR = 64 * WGM * WGN;
   constexpr int WM = BM / WGM, WN = BN / WGN;       // WGM x WGN waves
   constexpr int TM = WM / 32, TN = WN / 32;
@@ -753,6 +759,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, TileCoord tc, int
     else
       run(std::false_type());
   }
+  after_loop();
   if (!active) return;
 
   // Epilogue.  Accumulator register r of a 32x32 tile holds row 8 (r / 4) + 4 (lane / 32) + r % 4
@@ -1192,13 +1199,27 @@ __device__ __forceinline__ BsScan bs_scan(const GemmParams& p, int NT) {
   return s;
 }
 
+// Whether the small groups' tiles follow all of the big groups' (bs_tile_at): a 256-row bf16
+// panel of K columns over 2 MB.
+__host__ __device__ constexpr bool bs_small_last(int K) { return K > 4096; }
+
 // Tile t of the merged order of the block-sparse map -> coordinates (s from bs_scan).
 __device__ __forceinline__ void bs_tile_at(const GemmParams& p, int NT, const BsScan& s, int t,
                                            TileCoord& tc) {
   const int total = s.big + s.small;
-  const long long S = s.small, TT = total;
-  const int small_before = (int)((long long)t * S / TT);
-  const bool is_small = (int)((long long)(t + 1) * S / TT) > small_before;
+  // Small groups' tiles spread evenly through the big groups' (so that their weight streams run
+  // beside matrix-bound tiles), unless a tall tile's operand panels (256 rows x K) are larger than
+  // half an XCD's L2: then the big groups' tiles go first, in near lock step, so that the tiles of
+  // a chunk still share their panels in L2, and the small groups' streams follow.
+  int small_before, is_small;
+  if (bs_small_last(p.K)) {
+    is_small = t >= s.big;
+    small_before = is_small ? t - s.big : 0;
+  } else {
+    const long long S = s.small, TT = total;
+    small_before = (int)((long long)t * S / TT);
+    is_small = (int)((long long)(t + 1) * S / TT) > small_before;
+  }
   const int idx = is_small ? small_before : t - small_before;
   const int incl = is_small ? s.small_incl : s.big_incl;
   const int mine = is_small ? s.small_mine : s.big_mine;
@@ -1274,8 +1295,9 @@ __device__ __forceinline__ int bs_ticket_tile(int x, int j, int total, int round
 constexpr int bs_nmat(int epi) { return epi_swiglu(epi) || epi == EPI_SWIGLU_BWD ? 2 : 1; }
 constexpr int bs_bn(int epi) { return bs_nmat(epi) == 2 ? 128 : 256; }
 
-template <int EPI, bool BT>
-__device__ __forceinline__ void bs_run_tile(const GemmParams& p, TileCoord tc) {
+template <int EPI, bool BT, class Hook = NoHook>
+__device__ __forceinline__ void bs_run_tile(const GemmParams& p, TileCoord tc,
+                                            Hook after_loop = Hook()) {
   constexpr int NMAT = bs_nmat(EPI);
   constexpr int BN = bs_bn(EPI);                     // columns per matrix, both tile kinds
   tc.g = __builtin_amdgcn_readfirstlane(tc.g);
@@ -1287,13 +1309,14 @@ __device__ __forceinline__ void bs_run_tile(const GemmParams& p, TileCoord tc) {
     // weight panel (non-temporal weight loads); else it is a big group's remainder, which shares
     // the panel with the group's whole tiles.
     if (tc.row0 == p.offsets[tc.g])
-      gemm_tile<kBsThin, BN, NMAT, 2, 4, 64, 4, 1, EPI, false, BT, false, true>(p, tc, 0, 1, -1, 0,
-                                                                               0);
+      gemm_tile<kBsThin, BN, NMAT, 2, 4, 64, 4, 1, EPI, false, BT, false, true>(
+          p, tc, 0, 1, -1, 0, 0, after_loop);
     else
-      gemm_tile<kBsThin, BN, NMAT, 2, 4, 64, 4, 1, EPI, false, BT>(p, tc, 0, 1, -1, 0, 0);
+      gemm_tile<kBsThin, BN, NMAT, 2, 4, 64, 4, 1, EPI, false, BT, false, false>(
+          p, tc, 0, 1, -1, 0, 0, after_loop);
   } else
-    gemm_tile<kBsTall, BN, NMAT, BT ? 2 : 4, BT ? 4 : 2, 64, 2, 1, EPI, false, BT>(p, tc, 0, 1,
-                                                                                    -1, 0, 0);
+    gemm_tile<kBsTall, BN, NMAT, BT ? 2 : 4, BT ? 4 : 2, 64, 2, 1, EPI, false, BT, false, false>(
+        p, tc, 0, 1, -1, 0, 0, after_loop);
 }
 
 // One block per tile: the hardware deals the blocks to the CUs.
@@ -1316,29 +1339,46 @@ __global__ __launch_bounds__(512, 1) void gemm_bs_persistent_kernel(const GemmPa
   extern __shared__ __align__(16) uint8_t smem[];
   const int NT = (p.N + bs_bn(EPI) - 1) / bs_bn(EPI);
   const BsScan s = bs_scan(p, NT);
-  const int total = s.big + s.small;
+  const int total = __builtin_amdgcn_readfirstlane(s.big + s.small);
   // HW_REG_XCC_ID: the XCD this block runs on.
   const int x0 = (int)(__builtin_amdgcn_s_getreg(20 | (31 << 11)) & 7);
-  int tried = 0;   // thread 0: XCD shares found empty so far
+  const bool wave0 = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) == 0;
+  int tried = 0;   // wave 0: XCD shares found empty so far
+  // Wave 0 takes the next tile (-1 when every share is gone); its lane 0 does the atomics, and
+  // every value stays wave-uniform.
+  auto take = [&]() {
+    int t = -1;
+    while (tried < 8) {
+      const int x = (x0 + tried) & 7;
+      int j = 0;
+      if (__lane_id() == 0) j = atomicAdd(p.tickets + x, 1);
+      t = bs_ticket_tile(x, __builtin_amdgcn_readfirstlane(j), total, p.slots);
+      if (t >= 0) break;
+      ++tried;
+    }
+    return t;
+  };
+  int next = wave0 ? take() : -1;
   for (;;) {
     if (threadIdx.x == 0) {
-      int t = -1;
-      while (tried < 8) {
-        const int x = (x0 + tried) & 7;
-        t = bs_ticket_tile(x, atomicAdd(p.tickets + x, 1), total, p.slots);
-        if (t >= 0) break;
-        ++tried;
-      }
-      *(volatile int*)smem = t;
+      *(volatile int*)smem = next;
+      __builtin_amdgcn_s_waitcnt(waitcnt_lgkm0());
     }
-    __syncthreads();
+    // Bare barriers: they order the LDS only.  (A fenced barrier would also wait for the
+    // previous tile's output stores, which may drain while the next tile starts.)
+    barrier_no_fence();
     const int t = __builtin_amdgcn_readfirstlane(*(volatile int*)smem);
-    __syncthreads();   // read by every wave before the tile's loads overwrite it
+    barrier_no_fence();   // read by every wave before the tile's loads overwrite it
     if (t < 0) break;
     TileCoord tc;
     bs_tile_at(p, NT, s, t, tc);
-    bs_run_tile<EPI, BT>(p, tc);
-    __syncthreads();   // every wave is done with the LDS stages before the next tile's loads
+    // The next tile is taken once the K loop is done, before this tile's output stores (whose
+    // completion a later wait on the atomic's result would otherwise include).
+    bs_run_tile<EPI, BT>(p, tc, [&]() {
+      if (wave0) next = take();
+    });
+    // Every wave has waited for its LDS reads and its direct loads at the end of the K loop.
+    barrier_no_fence();
   }
 }
 
