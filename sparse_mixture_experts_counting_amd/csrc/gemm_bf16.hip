@@ -49,6 +49,7 @@ typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8_t;
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4_t;
+typedef __attribute__((address_space(3))) int lds_int_t;
 
 // Transposed-B stages hold K rows of BN columns (2 BN bytes); unit u of row r is stored at
 // u ^ swzT(r).  A transposing read takes 4 consecutive rows of 32 bytes at one unit pair; the
@@ -280,13 +281,30 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, TileCoord tc, int
   uint32_t a_voff[A_UNITS], b_voff[B_UNITS];
   int a_lds[A_UNITS], b_lds[B_UNITS];
   const int u = tid % UPR;
+  // Source rows of the gathered operand rows: every index load is issued before any is used (a
+  // load and its wait per row would serialise their latencies at the start of every tile).
+  auto gather_rows = [&](auto NRc, auto row_of, int* src) {
+    constexpr int NR = decltype(NRc)::value;
+    if (p.gather) {
 #pragma unroll
-  for (int i = 0; i < A_UNITS; ++i) {
-    const int row = tid / UPR + ROWS_PER_LOAD * i;
-    const int grow = min(tc.row0 + row, tc.row_end - 1);
-    const int src = p.gather ? p.gather[grow] / p.gather_div : grow;
-    a_voff[i] = ((uint32_t)src * (uint32_t)lda + 8u * u) * 2u;
-    a_lds[i] = row * RB + ((u ^ swz<BK>(row)) << 4);
+      for (int i = 0; i < NR; ++i) src[i] = p.gather[min(tc.row0 + row_of(i), tc.row_end - 1)];
+#pragma unroll
+      for (int i = 0; i < NR; ++i) src[i] = src[i] / p.gather_div;
+    } else {
+#pragma unroll
+      for (int i = 0; i < NR; ++i) src[i] = min(tc.row0 + row_of(i), tc.row_end - 1);
+    }
+  };
+  if constexpr (!DMA) {
+    int src[A_UNITS];
+    gather_rows(std::integral_constant<int, A_UNITS>(),
+                [&](int i) { return tid / UPR + ROWS_PER_LOAD * i; }, src);
+#pragma unroll
+    for (int i = 0; i < A_UNITS; ++i) {
+      const int row = tid / UPR + ROWS_PER_LOAD * i;
+      a_voff[i] = ((uint32_t)src[i] * (uint32_t)lda + 8u * u) * 2u;
+      a_lds[i] = row * RB + ((u ^ swz<BK>(row)) << 4);
+    }
   }
 #pragma unroll
   for (int i = 0; i < B_UNITS; ++i) {
@@ -301,6 +319,10 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, TileCoord tc, int
   uint32_t d_voff[DMA ? DPWL : 1];
   int d_kmax[DMA ? DPWL : 1];           // the load reads zeros for steps starting at k0 >= d_kmax
   if constexpr (DMA) {
+    int dsrc[AT ? 1 : DPWL_A];
+    if constexpr (!AT)
+      gather_rows(std::integral_constant<int, DPWL_A>(),
+                  [&](int j) { return (wave + NWL * j) * DROWS + lane / UPR; }, dsrc);
 #pragma unroll
     for (int j = 0; j < DPWL; ++j) {
       const int srow = (wave + NWL * j) * DROWS + lane / UPR;
@@ -313,9 +335,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, TileCoord tc, int
           const int m = min(tc.row0 + 8 * ua, tc.row_end - 8);
           d_voff[j] = ((uint32_t)kr * (uint32_t)lda + (uint32_t)m) * 2u;
         } else {
-          const int grow = min(tc.row0 + srow, tc.row_end - 1);
-          const int src = p.gather ? p.gather[grow] / p.gather_div : grow;
-          d_voff[j] = ((uint32_t)src * (uint32_t)lda + 8u * uu) * 2u;
+          d_voff[j] = ((uint32_t)dsrc[j] * (uint32_t)lda + 8u * uu) * 2u;
         }
       } else if constexpr (BT) {
         // Row kr of the stage's B block (a K row), physical unit lane % UPB.
@@ -1361,13 +1381,13 @@ __global__ __launch_bounds__(512, 1) void gemm_bs_persistent_kernel(const GemmPa
   int next = wave0 ? take() : -1;
   for (;;) {
     if (threadIdx.x == 0) {
-      *(volatile int*)smem = next;
+      *(lds_int_t*)smem = next;   // an LDS store (a generic one would also count as a memory op)
       __builtin_amdgcn_s_waitcnt(waitcnt_lgkm0());
     }
     // Bare barriers: they order the LDS only.  (A fenced barrier would also wait for the
     // previous tile's output stores, which may drain while the next tile starts.)
     barrier_no_fence();
-    const int t = __builtin_amdgcn_readfirstlane(*(volatile int*)smem);
+    const int t = __builtin_amdgcn_readfirstlane(*(lds_int_t*)smem);
     barrier_no_fence();   // read by every wave before the tile's loads overwrite it
     if (t < 0) break;
     TileCoord tc;
