@@ -382,12 +382,14 @@ def main():
                 "peak": PEAK_HBM_GBS, "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
     # The up projection's launch: the block-sparse tall/thin tiling when the groups fill 256-row
-    # tiles (gemm_bs_kernel), else the grouped tiles (gemm_bf16_kernel, with a finish kernel for
-    # split partial sums); the fp32 layers run gemm_f32_kernel.
+    # tiles (gemm_bs_persistent_kernel: one block per CU taking tiles from per-XCD counters, which
+    # zero_tickets_kernel clears in the workspace first), else the grouped tiles (gemm_bf16_kernel,
+    # with a finish kernel for split partial sums); the fp32 layers run gemm_f32_kernel.
     if cfg.dtype == "fp32":
         up_kernel = "moe_expert_up: gemm_f32_kernel (SwiGLU epilogue)"
     elif T * k >= 256 * E:
-        up_kernel = "moe_expert_up: gemm_bs_kernel (block-sparse tall/thin tiles, SwiGLU epilogue)"
+        up_kernel = ("moe_expert_up: gemm_bs_persistent_kernel (block-sparse tall/thin tiles, one "
+                     "block per CU, SwiGLU epilogue) + zero_tickets_kernel")
     else:
         up_kernel = ("moe_expert_up: gemm_bf16_kernel (SwiGLU epilogue) + its split-K finish "
                      "kernel")

@@ -1622,11 +1622,18 @@ static hipError_t launch_bs_t(const GemmParams& p, int rows_max, hipStream_t s) 
   static_assert(lds_bytes<kBsThin, bs_bn(EPI), bs_nmat(EPI), 64, 4, 1>() == kMaxLds &&
                     lds_bytes<kBsTall, bs_bn(EPI), bs_nmat(EPI), 64, 2, 1>() == kMaxLds,
                 "both tile kinds fill the LDS the launch asks for");
-  // One block per CU taking tiles from counters when the caller's split-K scratch (which this
-  // launch does not otherwise use) can hold them; else one block per tile.
-  // (The SwiGLU-backward epilogues never get scratch: they run on whole sums only.)
+  const int NT = (p.N + bs_bn(EPI) - 1) / bs_bn(EPI);
+  // Every group yields at most floor(n_g / 256) + 1 tiles per column tile.
+  const int tiles = tiles_upper_bound(rows_max, p.G, true, kBsTall, NT);
+  if (tiles <= 0) return hipSuccess;
+  // One block per CU taking tiles from counters when there can be more than two rounds of tiles
+  // (with fewer, a block has at most a tile or two and the counters only add their latency) and
+  // the caller's split-K scratch (which this launch does not otherwise use) can hold them; else
+  // one block per tile.  (The SwiGLU-backward epilogues never get scratch: they run on whole sums
+  // only.)
   constexpr bool can_persist = EPI == EPI_SWIGLU || EPI == EPI_SWIGLU_SAVE || EPI == EPI_STORE;
-  const bool persistent = can_persist && p.part != nullptr && device_cus() >= 8 &&
+  const int round = device_cus() / 8 * 8;
+  const bool persistent = can_persist && p.part != nullptr && round >= 8 && tiles > 2 * round &&
                           gemm_bf16_partial_bytes(rows_max, p.G, true, p.N, p.K, EPI) >= 64;
   void (*kern)(GemmParams) = gemm_bs_kernel<EPI, BT>;
   if constexpr (can_persist) {
@@ -1643,11 +1650,7 @@ static hipError_t launch_bs_t(const GemmParams& p, int rows_max, hipStream_t s) 
   }
   GemmParams q = p;
   q.ksplit = 1;
-  q.slots = device_cus() / 8 * 8;   // one block per CU: the blocks of one round
-  const int NT = (p.N + bs_bn(EPI) - 1) / bs_bn(EPI);
-  // Every group yields at most floor(n_g / 256) + 1 tiles per column tile.
-  const int tiles = tiles_upper_bound(rows_max, p.G, true, kBsTall, NT);
-  if (tiles <= 0) return hipSuccess;
+  q.slots = round;   // one block per CU: the blocks of one round
   if (persistent) {
     q.tickets = (int*)p.part;
     hipLaunchKernelGGL(zero_tickets_kernel, dim3(1), dim3(64), 0, s, q.tickets);

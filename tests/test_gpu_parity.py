@@ -234,6 +234,13 @@ SWEEP = [
     (700, 256, 4, 2, 512, "bf16", "softmax_topk", 0, 0, 1.1),
     (1500, 128, 8, 2, 320, "bf16", "sigmoid_topk", 0, 1, 1.3),
     (300, 136, 2, 2, 264, "bf16", "softmax_all", 0, 0, 0.0),
+    # more than two rounds of block-sparse tiles (one block per CU taking tiles from per-XCD
+    # counters, shares running out and taken over): skewed groups with tall and thin tiles, the
+    # small groups' tiles spread through the big groups' (K <= 4096) or after them (ragged
+    # K = 4160), and the down projection's store epilogue on the same path
+    (2048, 256, 16, 2, 4096, "bf16", "softmax_topk", 0, 0, 1.2),
+    (1024, 4160, 8, 2, 4224, "bf16", "sigmoid_topk", 0, 0, 1.3),
+    (2048, 4352, 16, 2, 256, "bf16", "softmax_topk", 0, 1, 1.2),
 ]
 
 
