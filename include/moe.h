@@ -13,7 +13,9 @@
  *   - Every pointer is a DEVICE pointer (memory the caller allocated on the current HIP device),
  *     unless stated otherwise.  The caller owns every buffer, including the workspace; the
  *     library never allocates or frees device memory and never synchronises the host.  Buffers
- *     must stay valid until the work enqueued on `stream` has finished.
+ *     must stay valid until the work enqueued on `stream` has finished.  A workspace holds the
+     call's scratch (partial sums, tile counters) while its work runs, so calls that may overlap
+     (on different streams) need workspaces of their own.
  *   - `stream` is a hipStream_t passed as void*; NULL means the default stream.  Every call only
  *     enqueues work ordered on that stream and returns.  The library creates no streams or
  *     events of its own, so calls on different streams are independent and any call can be
@@ -199,8 +201,10 @@ moe_status moe_expert_ffn(const void* x, const int32_t* perm, const int32_t* off
  * fp32 partial sums of K-split tiles: every tile when few rows leave the GPU under-filled
  * (decode-sized batches), else the tiles of a last, partial round of tiles.  Partials are added in
  * a fixed order, so results are bitwise deterministic run to run; a split changes only the order of
- * the fp32 sums.  The workspace may be NULL: the GEMMs then run unsplit (equal up to that rounding
- * order).  Same errors as moe_expert_ffn.
+ * the fp32 sums.  Products of groups that fill 256-row tiles with more than two rounds of tiles
+ * keep 8 tile counters there instead (one block per compute unit taking tiles; each tile is still
+ * summed whole, in the same order).  The workspace may be NULL: the GEMMs then run unsplit and one
+ * block per tile (equal up to the split's rounding order).  Same errors as moe_expert_ffn.
  */
 moe_status moe_expert_up(const void* x, const int32_t* perm, const int32_t* offsets, int T, int d,
                          int d_ff, int E, int k, const void* w1, const void* w3, moe_dtype dt,
