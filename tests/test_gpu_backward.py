@@ -147,6 +147,10 @@ CASES = [
     (1030, 256, 128, 2, 256, "softmax_topk", 0, 0, 0.0),
     (96, 64, 256, 8, 64, "sigmoid_topk", 0, 1, 1.1),
     (5, 512, 64, 2, 128, "softmax_all", 0, 0, 0.0),
+    # skewed groups with more than two rounds of 256-column tiles (d = 8448): the input-gradient
+    # product (weights read transposed) and the forward down projection take the block-sparse
+    # launch with one block per CU taking tiles from counters
+    (1024, 8448, 8, 2, 128, "softmax_topk", 0, 0, 1.2),
 ]
 
 

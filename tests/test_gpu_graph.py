@@ -28,6 +28,9 @@ CASES = [
     (300, 128, 8, 2, 192, "softmax_topk", 0, 0, 0.0),        # 128-row tiles
     (700, 256, 4, 2, 512, "softmax_topk", 0, 1, 1.1),        # block-sparse tall and thin tiles
     (257, 136, 8, 2, 264, "sigmoid_topk", 70, 0, 0.0),       # capacity drops, ragged shapes
+    # more than two rounds of block-sparse tiles: one block per CU taking tiles from counters that
+    # a kernel zeroes in the workspace before every launch, replays included
+    (2048, 256, 16, 2, 4096, "softmax_topk", 0, 0, 1.2),
 ]
 
 
@@ -84,13 +87,17 @@ def test_graph_replay_matches_eager(M, case, save):
             assert torch.equal(got[n], v), "replay %d: %s differs from the eager run" % (replay, n)
 
 
-def test_two_caller_streams_concurrently(M):
-    """Two streams run the block-sparse tiling (skewed groups of a few hundred rows) at the same
-    time on different buffers: each result is bit-identical to the same layer run alone on the
-    default stream."""
-    print("two caller streams", flush=True)
+@pytest.mark.parametrize("shape", [(700, 256, 4, 2, 512, 1, 1.1), (2048, 256, 16, 2, 4096, 0, 1.2)],
+                         ids=["one_block_per_tile", "counters"])
+def test_two_caller_streams_concurrently(M, shape):
+    """Two streams run the block-sparse tiling (skewed groups) at the same time on different
+    buffers (each with its own workspace, which holds the tile counters when there are more than
+    two rounds of tiles): each result is bit-identical to the same layer run alone on the default
+    stream."""
+    print("two caller streams", shape, flush=True)
     L, S = M["layer"], M["synth"]
-    cfg = S.tiny_config(700, 256, 4, 2, 512, "bf16", "softmax_topk", n_shared=1, zipf_s=1.1)
+    T, d, E, k, f, sh, zipf = shape
+    cfg = S.tiny_config(T, d, E, k, f, "bf16", "softmax_topk", n_shared=sh, zipf_s=zipf)
     inps = [S.make_inputs(cfg, seed=s, device="cuda") for s in (5, 6)]
     refs = []
     for inp in inps:
