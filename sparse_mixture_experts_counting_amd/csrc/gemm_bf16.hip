@@ -1002,6 +1002,49 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, TileCoord tc, int
     // rows (a DPP quad permute), so the even lane holds row a and the odd lane row b of columns
     // (2c, 2c+1).
     const bool odd = lane & 1;
+    // A wave whose whole WM x WN block lies inside the output (no addend, no saved a and b) stores
+    // through a buffer descriptor based at its block: the lane's row pair and column go into one
+    // 32-bit offset computed once, and each register's row step into a wave-uniform offset, so the
+    // stores need no per-store address arithmetic or bounds checks.
+    if constexpr (EPI == EPI_SWIGLU || EPI == EPI_STORE) {
+      const bool whole = __builtin_amdgcn_readfirstlane(
+          (int)(tc.row0 + wm0 + WM <= tc.row_end && n_base + wn0 + WN <= N && !p.D));
+      if (whole) {
+        const int ldc2 = __builtin_amdgcn_readfirstlane(p.ldc * 2);   // row stride in bytes
+        const int row_base = __builtin_amdgcn_readfirstlane(tc.row0 + wm0);
+        const __amdgpu_buffer_rsrc_t rC = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)((char*)Cg + (size_t)row_base * ldc2 + (size_t)(n_base + wn0) * 2), (short)0,
+            0x7fffffff, 0x00020000);
+        const int voff = (4 * h + (odd ? 1 : 0)) * ldc2 + (l32 & ~1) * 2;
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+#pragma unroll
+          for (int j = 0; j < TN; ++j) {
+            float v[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              if constexpr (epi_swiglu(EPI))
+                v[r] = silu(acc[0][i][j][r]) * acc[NMAT - 1][i][j][r];
+              else
+                v[r] = acc[0][i][j][r];
+            }
+#pragma unroll
+            for (int r = 0; r < 16; r += 2) {
+              const float send = odd ? v[r] : v[r + 1];
+              const float got = __builtin_bit_cast(
+                  float,
+                  __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, send), 0xB1, 0xF, 0xF, false));
+              const float lo = odd ? got : v[r], hi = odd ? v[r + 1] : got;
+              // Row i * 32 + 8 (r / 4) + (r % 4) of the block (plus the lane's 4 h + odd), columns
+              // j * 32 + the lane's pair.
+              const int soff = (i * 32 + 8 * (r >> 2) + (r & 3)) * ldc2 + j * 64;
+              __builtin_amdgcn_raw_buffer_store_b32(pack_bf16x2(lo, hi), rC, voff, soff, 0);
+            }
+          }
+        }
+        return;
+      }
+    }
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
 #pragma unroll
