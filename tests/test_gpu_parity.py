@@ -241,6 +241,11 @@ SWEEP = [
     (2048, 256, 16, 2, 4096, "bf16", "softmax_topk", 0, 0, 1.2),
     (1024, 4160, 8, 2, 4224, "bf16", "sigmoid_topk", 0, 0, 1.3),
     (2048, 4352, 16, 2, 256, "bf16", "softmax_topk", 0, 1, 1.2),
+    # the same launch under extreme skew: empty experts and one-row experts (Zipf 3), and capacity
+    # drops leaving fewer tiles than one round of CUs, so every XCD's share is short and blocks
+    # take tiles from the other XCDs' counters (Zipf 5, C = 512)
+    (2048, 256, 16, 2, 4096, "bf16", "softmax_topk", 0, 0, 3.0),
+    (2048, 256, 16, 2, 4096, "bf16", "sigmoid_topk", 512, 0, 5.0),
 ]
 
 
