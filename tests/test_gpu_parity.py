@@ -249,7 +249,7 @@ SWEEP = [
 ]
 
 
-@pytest.mark.parametrize("case", SWEEP, ids=lambda c: "T%d_d%d_E%d_k%d_f%d_%s_%s_C%d_s%d" % c[:9])
+@pytest.mark.parametrize("case", SWEEP, ids=lambda c: "T%d_d%d_E%d_k%d_f%d_%s_%s_C%d_s%d_z%g" % c)
 def test_layer_property_sweep(M, case):
     T, d, E, k, f, dt, g, C, sh, zipf = case
     _say("sweep", case)
